@@ -1,0 +1,30 @@
+"""Build the CPU oracle (test infrastructure only) into oracle/liboracle.so.
+
+Plain gcc, no fused multiply-add, no fast-math: the encoder's fp32 steps are
+the definition the GPU encoder is checked against bit for bit.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    src = os.path.join(HERE, "kvq_oracle.c")
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-std=c11", "-D_GNU_SOURCE", "-O2", "-fPIC", "-shared",
+           "-ffp-contract=off", "-fno-fast-math", "-fno-strict-aliasing", "-pthread",
+           "-Wall", "-Wextra", "-Wno-unused-parameter",
+           src, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

@@ -1,0 +1,471 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check compares the oracle with something other than itself: a library
+routine (numpy float16, torch bfloat16, scipy's Hadamard matrix, scipy's
+incomplete beta function), a closed form, a textbook table, an invariant, or
+brute force on tiny inputs.  No GPU is involved.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy import linalg, special, stats
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def unpack_codes(rec: np.ndarray, d: int, bits: int) -> np.ndarray:
+    """Read codes back following the documented record layout."""
+    out = np.zeros(d, np.int64)
+    for i in range(d):
+        if bits == 3:
+            lo = (rec[(2 * i) // 8] >> ((2 * i) % 8)) & 3
+            hi = (rec[d // 4 + i // 8] >> (i % 8)) & 1
+            out[i] = lo | (hi << 2)
+        else:
+            out[i] = (rec[(i * bits) // 8] >> ((i * bits) % 8)) & ((1 << bits) - 1)
+    return out
+
+
+def unpack_signs(rec: np.ndarray, m: int) -> np.ndarray:
+    return np.array([(rec[k // 8] >> (k % 8)) & 1 for k in range(m)], np.int64)
+
+
+# --------------------------------------------------------------------------- formats
+def test_f16_conversion_matches_numpy(orc):
+    rng = np.random.default_rng(0)
+    vals = list(rng.standard_normal(4000) * np.exp(rng.uniform(-25, 12, 4000)))
+    # edge values: zeros, limits, ties, subnormal range
+    vals += [0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 1e6, 2.0 ** -24, 2.0 ** -25,
+             3 * 2.0 ** -26, 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -11), 1 + 2 ** -11,
+             1 + 3 * 2 ** -11, 1e-30, float("inf"), -float("inf")]
+    for v in vals:
+        f = np.float32(v)
+        with np.errstate(over="ignore"):
+            want = int(np.array([f], np.float32).astype(np.float16).view(np.uint16)[0])
+        assert orc.f32_to_f16_bits(f) == want, (v, hex(want))
+    for h in [0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xFBFF]:
+        assert orc.f16_bits_to_f64(h) == float(np.array([h], np.uint16).view(np.float16)[0])
+
+
+def test_bf16_conversion_matches_torch(orc):
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 4000),
+                        np.array([0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 3.3895314e38, 1e-40],
+                                 np.float32)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.f32_to_bf16_bits(v) for v in x], np.uint16)
+    assert np.array_equal(got, want)
+    assert orc.bf16_bits_to_f32(0x3F80) == 1.0
+
+
+# --------------------------------------------------------------------------- codebook
+def _beta_cell(d, a, b):
+    """Mass and first moment of f(t) ~ (1-t^2)^((d-3)/2) on [a,b] (scipy incomplete beta +
+    the closed-form antiderivative of t (1-t^2)^alpha)."""
+    p = (d - 1) / 2.0
+    mass = special.betainc(p, p, (1 + b) / 2) - special.betainc(p, p, (1 + a) / 2)
+    alpha = (d - 3) / 2.0
+    logZ = 0.5 * math.log(math.pi) + special.gammaln(alpha + 1) - special.gammaln(alpha + 1.5)
+    F = lambda t: -(max(1 - t * t, 0.0) ** (alpha + 1)) / (2 * (alpha + 1)) / math.exp(logZ)
+    return mass, F(b) - F(a)
+
+
+@pytest.mark.parametrize("d", [8, 16, 64, 128])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_is_lloyd_max_fixed_point(orc, d, bits):
+    c, t, c64 = orc.codebook(d, bits)
+    K = 1 << bits
+    # exact symmetry, order, zero middle threshold
+    assert np.array_equal(c[: K // 2], -c[K // 2:][::-1])
+    assert np.array_equal(t[: K // 2 - 1], -t[K // 2:][::-1])
+    assert t[K // 2 - 1] == 0.0
+    assert np.all(np.diff(c) > 0) and np.all(np.diff(t) > 0)
+    # centroid condition: each level is the conditional mean of its cell
+    edges = np.concatenate([[0.0], 0.5 * (c64[1:] + c64[:-1]), [1.0]])
+    for i in range(K // 2):
+        mass, mom = _beta_cell(d, edges[i], edges[i + 1])
+        assert abs(c64[i] - mom / mass) < 1e-12 * max(1.0, abs(c64[i]) * math.sqrt(d)), (i, c64[i], mom / mass)
+    # thresholds are the fp32-rounded fp64 midpoints; levels are fp32-rounded fp64 levels
+    assert np.array_equal(c[K // 2:], c64.astype(np.float32))
+    assert np.array_equal(t[K // 2:], (0.5 * (c64[1:] + c64[:-1])).astype(np.float32))
+    # total mass 1 and E[t^2] = 1/d (closed forms) via the same cells
+    tot = sum(_beta_cell(d, edges[i], edges[i + 1])[0] for i in range(K // 2))
+    assert abs(2 * tot - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("d", [8, 64, 128, 1000])
+def test_codebook_one_bit_closed_form(orc, d):
+    c, t, c64 = orc.codebook(d, 1)
+    # Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)) = B(d/2, 1/2) / pi
+    want = special.beta(d / 2, 0.5) / math.pi
+    assert abs(c64[0] - want) < 1e-12 * want
+    assert list(t) == [0.0]
+
+
+def test_codebook_one_bit_values():
+    # E|t| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)): 0.100126 at d=64, 0.070662 at d=128
+    from oracle import ref
+    assert abs(ref.codebook(64, 1)[2][0] - 0.100126) < 1e-6
+    assert abs(ref.codebook(128, 1)[2][0] - 0.070662) < 1e-6
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_d3_is_uniform_quantizer(orc, bits):
+    # d = 3: f(t) ~ (1-t^2)^0 is uniform on [-1,1]; Lloyd-Max = uniform quantiser
+    c, t, c64 = orc.codebook(3, bits)
+    K = 1 << bits
+    want = -1 + (2 * np.arange(K) + 1) / K
+    assert np.max(np.abs(c.astype(np.float64) - want)) < 1e-7
+    assert np.max(np.abs(c64 - want[K // 2:])) < 1e-12
+
+
+def _gauss_lloyd_max(bits):
+    K = 1 << bits
+    c = np.linspace(0.1, 2.5, K // 2)
+    for _ in range(20000):
+        e = np.concatenate([[0.0], 0.5 * (c[1:] + c[:-1]), [np.inf]])
+        mass = stats.norm.cdf(e[1:]) - stats.norm.cdf(e[:-1])
+        mom = stats.norm.pdf(e[:-1]) - stats.norm.pdf(e[1:])
+        cn = mom / mass
+        if np.max(np.abs(cn - c)) < 1e-15:
+            break
+        c = cn
+    return cn
+
+
+# Max (1960) / textbook Gaussian Lloyd-Max levels (positive half)
+MAX_1960 = {1: [0.7979], 2: [0.4528, 1.510], 3: [0.2451, 0.7560, 1.344, 2.152],
+            4: [0.1284, 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733]}
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_gaussian_limit(orc, bits):
+    """As d grows, sqrt(d) * t tends to N(0,1), so sqrt(d) * levels tend to the
+    Gaussian Lloyd-Max levels (sphere-marginal -> Gaussian, D'Alberto summary,
+    'Theoretical framework')."""
+    g = _gauss_lloyd_max(bits)
+    assert np.max(np.abs(g - np.array(MAX_1960[bits]))) < 1.5e-3
+    err = {}
+    for d in (256, 4096):
+        c64 = orc.codebook(d, bits)[2]
+        err[d] = np.max(np.abs(np.sqrt(d) * c64 - g))
+    assert err[4096] < 2e-3
+    assert err[4096] < err[256] / 8  # O(1/d) convergence
+
+
+def _distortion(d, bits, c64):
+    """D_b = E||u - Q(u)||^2 for u uniform on S^{d-1} = 1 - d * sum_i P_i c_i^2."""
+    K = 1 << bits
+    edges = np.concatenate([[0.0], 0.5 * (c64[1:] + c64[:-1]), [1.0]])
+    s = sum(2 * _beta_cell(d, edges[i], edges[i + 1])[0] * c64[i] ** 2 for i in range(K // 2))
+    return 1.0 - d * s
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_mse_bound(orc, d, bits):
+    """KVQuant++ thread, 'Rate-distortion performance': per-element MSE under
+    sqrt(3*pi/2) * 4^-b.  Literal reading (per coordinate of a unit vector) must
+    hold; the TurboQuant form (sqrt(3)*pi/2) * 4^-b bounds the whole-vector D_b."""
+    with open(os.path.join(GOLDEN, "pages_constants.json")) as f:
+        pages = json.load(f)
+    cst = pages["mse_bound_constant_as_printed"]["value"]
+    c64 = orc.codebook(d, bits)[2]
+    D = _distortion(d, bits, c64)
+    assert D / d <= cst * 4.0 ** -bits
+    assert D <= (math.sqrt(3) * math.pi / 2) * 4.0 ** -bits
+    # Monte-Carlo through the oracle encoder (no rotation; unit-norm inputs)
+    rng = np.random.default_rng(10 + bits)
+    side = orc.Side(0, bits, 0)
+    c = orc.codebook(d, bits)[0].astype(np.float64)
+    errs = []
+    for _ in range(1500):
+        x = rng.standard_normal(d)
+        u = x / np.linalg.norm(x)
+        codes, _, _, _ = orc.encode(u.astype(np.float32), side)
+        errs.append(np.sum((u - c[unpack_codes(codes, d, bits)]) ** 2))
+    errs = np.array(errs)
+    assert abs(errs.mean() - D) < 4 * errs.std() / math.sqrt(len(errs)) + 1e-5
+
+
+# --------------------------------------------------------------------------- WHT, sums
+@pytest.mark.parametrize("d", [8, 64, 128, 256])
+def test_wht_equals_sylvester_matrix(orc, d):
+    H = linalg.hadamard(d)                       # Sylvester construction
+    assert np.array_equal(H @ H.T, d * np.eye(d, dtype=H.dtype))
+    rng = np.random.default_rng(d)
+    xi = rng.integers(-1000, 1000, d).astype(np.float32)   # exact in fp32
+    y = orc.wht_f32(xi)
+    assert np.array_equal(y.astype(np.float64), H @ xi.astype(np.float64))
+    assert np.array_equal(orc.wht_f32(y), d * xi)          # H H x = d x
+    x = rng.standard_normal(d).astype(np.float32)
+    y = orc.wht_f32(x).astype(np.float64)
+    ref = H @ x.astype(np.float64)
+    assert np.max(np.abs(y - ref)) <= math.log2(d) * 2 ** -23 * np.sum(np.abs(x)) * math.sqrt(d)
+    assert abs(np.linalg.norm(y) - math.sqrt(d) * np.linalg.norm(x.astype(np.float64))) < 1e-5 * np.linalg.norm(y)
+
+
+def test_sumsq_pairwise_order(orc):
+    rng = np.random.default_rng(3)
+    xi = rng.integers(-300, 300, 128).astype(np.float32)
+    assert float(orc.sumsq_f32(xi)) == float(np.sum(xi.astype(np.float64) ** 2))
+    # adjacent pairs first: (1 + 2^-24) + (2^-24 + 2^-24) = 1 + 2^-23, whereas a
+    # left-to-right sum would stay at 1.
+    y = np.array([1.0, 2.0 ** -12, 2.0 ** -12, 2.0 ** -12], np.float32)
+    assert float(orc.sumsq_f32(y)) == 1.0 + 2.0 ** -23
+    x = rng.standard_normal(128).astype(np.float32)
+    assert abs(float(orc.sumsq_f32(x)) - np.sum(x.astype(np.float64) ** 2)) < 1e-6 * np.sum(x.astype(np.float64) ** 2)
+
+
+# --------------------------------------------------------------------------- bucketize
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_bucketize_is_nearest_centroid(orc, bits):
+    """KVQuant++ thread, 'Fast codebook lookup': bucketize against sorted
+    thresholds replaces the argmin nearest-centroid search; same answer."""
+    c, t, _ = orc.codebook(8, bits)
+    rng = np.random.default_rng(bits)
+    us = np.concatenate([rng.uniform(-1, 1, 3000), rng.normal(0, 0.35, 3000),
+                         c + rng.normal(0, 1e-3, c.shape)]).astype(np.float32)
+    c64 = c.astype(np.float64)
+    for u in us:
+        if np.any(np.abs(np.float64(u) - t.astype(np.float64)) <= np.spacing(np.float32(abs(u) + 1e-30))):
+            continue
+        want = int(np.argmin(np.abs(np.float64(u) - c64)))
+        assert orc.bucketize(u, t) == want
+    for i, th in enumerate(t):                                     # ties go to the lower cell
+        assert orc.bucketize(th, t) == i
+    assert orc.bucketize(0.0, t) == (1 << (bits - 1)) - 1
+
+
+# --------------------------------------------------------------------------- encoder
+def _unit_with_prefix(orc, d, bits, prefix_codes):
+    """A unit-norm fp32 vector whose first entries sit exactly on the given
+    centroids; the remaining entries share one filler value that makes the norm 1."""
+    c = orc.codebook(d, bits)[0].astype(np.float64)
+    head = c[np.asarray(prefix_codes)]
+    rest = d - len(head)
+    f = math.sqrt((1.0 - np.sum(head ** 2)) / rest)
+    return np.concatenate([head, np.full(rest, f)]).astype(np.float32)
+
+
+def test_record_layout_hand_computed(orc):
+    """Codes 0..K-1 in the first coordinates -> bytes fixed by the documented layout."""
+    x3 = _unit_with_prefix(orc, 64, 3, range(8))
+    codes, _, _, _ = orc.encode(x3, orc.Side(0, 3, 0))
+    # 2-bit plane: low bits 0,1,2,3,0,1,2,3; 1-bit plane (offset d/4): high bits 0,0,0,0,1,1,1,1
+    assert list(codes[:2]) == [0xE4, 0xE4] and codes[16] == 0xF0
+    x4 = _unit_with_prefix(orc, 64, 4, range(16))
+    codes4, _, _, _ = orc.encode(x4, orc.Side(0, 4, 0))
+    assert list(codes4[:8]) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    x2 = _unit_with_prefix(orc, 64, 2, [0, 1, 2, 3, 3, 2, 1, 0])
+    codes2, _, _, _ = orc.encode(x2, orc.Side(0, 2, 0))
+    assert list(codes2[:2]) == [0xE4, 0x1B]
+    x1 = _unit_with_prefix(orc, 64, 1, [1, 0, 1, 1, 0, 0, 0, 1])
+    codes1, _, _, _ = orc.encode(x1, orc.Side(0, 1, 0))
+    assert codes1[0] == 0x8D
+
+
+@pytest.mark.parametrize("rotate", [0, 1])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codes_and_norm_against_fp64_direction(orc, rotate, bits):
+    d = 64
+    H = linalg.hadamard(d).astype(np.float64)
+    c, t, _ = orc.codebook(d, bits)
+    rng = np.random.default_rng(100 + bits + 10 * rotate)
+    checked = 0
+    for _ in range(200):
+        x = (rng.standard_normal(d) * rng.uniform(0.1, 30)).astype(np.float32)
+        y = H @ x.astype(np.float64) if rotate else x.astype(np.float64)
+        u = y / np.linalg.norm(y)
+        codes, _, nb, _ = orc.encode(x, orc.Side(rotate, bits, 0))
+        got = unpack_codes(codes, d, bits)
+        near = np.min(np.abs(u[:, None] - t.astype(np.float64)[None, :]), axis=1) < 1e-5 * (np.abs(u) + 1e-3)
+        want = np.argmin(np.abs(u[:, None] - c.astype(np.float64)[None, :]), axis=1)
+        assert np.array_equal(got[~near], want[~near])
+        checked += int((~near).sum())
+        n = np.linalg.norm(x.astype(np.float64))
+        assert abs(orc.f16_bits_to_f64(nb) - n) <= n * 2 ** -11 * 1.01
+    assert checked > 200 * d * 0.98
+
+
+def test_zero_vector_and_overflow(orc):
+    S = np.asarray(torch.randn(32, 32, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+                   .view(torch.int16).numpy().view(np.uint16))
+    for bits in (1, 2, 3, 4):
+        codes, signs, nb, rb = orc.encode(np.zeros(32, np.float32), orc.Side(1, bits, 1), S)
+        assert np.array_equal(unpack_codes(codes, 32, bits), np.full(32, (1 << (bits - 1)) - 1))
+        assert nb == 0
+        x = orc.decode(codes, signs, nb, rb, 32, orc.Side(1, bits, 1), S)
+        assert np.all(x == 0)
+    big = np.full(32, 20000.0, np.float32)
+    _, _, nb, _ = orc.encode(big, orc.Side(1, 4, 0))
+    assert nb == 0x7C00  # ||x|| = 113137 > 65504 -> +inf in binary16
+
+
+def test_sign_bits_match_fp64_projection(orc):
+    d = m = 64
+    rng = np.random.default_rng(7)
+    S16 = torch.from_numpy(rng.standard_normal((m, d)).astype(np.float32)).to(torch.bfloat16)
+    S = S16.view(torch.int16).numpy().view(np.uint16)
+    Sf = S16.to(torch.float64).numpy()
+    H = linalg.hadamard(d).astype(np.float64)
+    c, _, _ = orc.codebook(d, 3)
+    tested = 0
+    for _ in range(100):
+        x = rng.standard_normal(d).astype(np.float32)
+        codes, signs, _, rb = orc.encode(x, orc.Side(1, 3, 1), S)
+        y = H @ x.astype(np.float64)
+        u = y / np.linalg.norm(y)
+        r = u - c.astype(np.float64)[unpack_codes(codes, d, 3)]
+        z = Sf @ r
+        ok = np.abs(z) > 1e-2 * np.linalg.norm(Sf, axis=1) * np.linalg.norm(r)
+        assert np.array_equal(unpack_signs(signs, m)[ok], (z[ok] >= 0).astype(np.int64))
+        assert abs(orc.f16_bits_to_f64(rb) - np.linalg.norm(r)) < 2e-3 * np.linalg.norm(r) + 1e-7
+        tested += ok.sum()
+    assert tested > 100 * m * 0.9
+
+
+# --------------------------------------------------------------------------- QJL
+def test_qjl_estimator_unbiased_with_stated_variance(orc):
+    """D'Alberto summary, 'Contribution 1': the 1-bit sketch gives an unbiased
+    estimate of the residual's inner products; per-row variance
+    (pi/2)||r||^2||y||^2 - <r,y>^2, averaged over m rows.  The decoder's sketch
+    term is checked here against that law over many independent S."""
+    d = m = 16
+    side = orc.Side(0, 2, 1)
+    c, _, _ = orc.codebook(d, 2)
+    rng = np.random.default_rng(11)
+    codes = np.array([0x1B, 0xE4, 0x4E, 0xB1], np.uint8)          # fixed code pattern
+    base = c.astype(np.float64)[unpack_codes(codes, d, 2)]
+    r = np.array([(-1) ** i * (i + 1) / 64.0 for i in range(d)])   # exact in bf16
+    rho = np.linalg.norm(r)
+    rho16 = orc.f32_to_f16_bits(np.float32(rho))
+    rho_h = orc.f16_bits_to_f64(rho16)
+    y = rng.standard_normal(d)
+    ests = []
+    for _ in range(20000):
+        S16 = torch.from_numpy(rng.standard_normal((m, d)).astype(np.float32)).to(torch.bfloat16)
+        Sf = S16.to(torch.float64).numpy()
+        sg = (Sf @ r >= 0).astype(np.uint8)
+        signs = np.packbits(sg, bitorder="little")
+        xh = orc.decode(codes, signs, 0x3C00, rho16, d, side, S16.view(torch.int16).numpy().view(np.uint16))
+        ests.append(y @ (xh - base))
+    ests = np.array(ests)
+    mean_want = rho_h * (y @ r) / rho
+    var_want = rho_h ** 2 * ((math.pi / 2) * (y @ y) - (y @ r) ** 2 / rho ** 2) / m
+    n = len(ests)
+    assert abs(ests.mean() - mean_want) < 4 * math.sqrt(var_want / n)
+    assert abs(ests.var() / var_want - 1) < 0.05
+    # the pages' bound (pi/2) ||r||^2 / d at m = d and ||y|| = 1
+    yn = y / np.linalg.norm(y)
+    v1 = ((math.pi / 2) - (yn @ r) ** 2 / rho ** 2) * rho ** 2 / m
+    assert v1 <= (math.pi / 2) * rho ** 2 / d
+
+
+def test_qjl_end_to_end_unbiased(orc):
+    """Encoder + decoder: over independent sketches, <y, x^> averages to <y, x>
+    (up to the fp16/bf16 rounding of the stored norms and residual)."""
+    d = m = 32
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(d).astype(np.float32)
+    y = rng.standard_normal(d)
+    side = orc.Side(1, 2, 1)
+    vals = []
+    for _ in range(4000):
+        S = torch.from_numpy(rng.standard_normal((m, d)).astype(np.float32)).to(torch.bfloat16) \
+            .view(torch.int16).numpy().view(np.uint16)
+        codes, signs, nb, rb = orc.encode(x, side, S)
+        vals.append(y @ orc.decode(codes, signs, nb, rb, d, side, S))
+    vals = np.array(vals)
+    se = vals.std() / math.sqrt(len(vals))
+    assert abs(vals.mean() - y @ x.astype(np.float64)) < 4 * se + 5e-3 * np.linalg.norm(y) * np.linalg.norm(x)
+
+
+# --------------------------------------------------------------------------- attention
+def _np_attention(q, K, V):
+    s = K @ q / math.sqrt(q.shape[0])
+    p = np.exp(s - s.max())
+    return (p[:, None] * V).sum(0) / p.sum()
+
+
+def test_attention_dense_invariants(orc):
+    rng = np.random.default_rng(20)
+    d, n = 8, 9
+    q, K, V = rng.standard_normal(d), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    o = orc.attention_dense(q, K, V)
+    assert np.allclose(o, _np_attention(q, K, V), rtol=1e-13, atol=1e-14)
+    # HeadQ 2.1: a token-shared key shift is softmax-null
+    mu = rng.standard_normal(d) * 3
+    assert np.allclose(orc.attention_dense(q, K + mu, V), o, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(orc.attention_dense(q, K[:1], V[:1]), V[0])
+    assert np.allclose(orc.attention_dense(q, K, np.tile(V[3], (n, 1))), V[3], rtol=1e-14)
+    assert np.allclose(orc.attention_dense(np.zeros(d), K, V), V.mean(0), rtol=1e-13)
+
+
+@pytest.mark.parametrize("scheme", ["KV", "KQV", "QKQV"])
+def test_attention_over_cache_matches_numpy(orc, scheme):
+    """Cache attention = plain softmax attention over the dequantised cache,
+    with G = Hq / Hkv query heads per KV head."""
+    B, Hkv, Hq, d, n, cap = 2, 2, 4, 8, 11, 13
+    rng = np.random.default_rng(21)
+    S = torch.from_numpy(rng.standard_normal((d, d)).astype(np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+    ks, vs = orc.scheme_sides(scheme, 3)
+    kc = orc.OracleCache(B, Hkv, cap, d, ks, d)
+    vc = orc.OracleCache(B, Hkv, cap, d, vs, d)
+    K = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    kc.quantize(K, 0, S)
+    vc.quantize(V, 0, S)
+    Kh, Vh = kc.dequantize(0, n, S), vc.dequantize(0, n, S)
+    out = orc.attention(kc, vc, q, n, S, nthreads=2)
+    for b in range(B):
+        for h in range(Hq):
+            want = _np_attention(q[b, h].astype(np.float64), Kh[b, h // 2], Vh[b, h // 2])
+            assert np.allclose(out[b, h], want, rtol=1e-12, atol=1e-12)
+    rows = [1, 6]
+    part = orc.attention(kc, vc, q, n, S, rows=rows)
+    for r in rows:
+        assert np.array_equal(part[r // Hq, r % Hq], out[r // Hq, r % Hq])
+
+
+def test_quantize_cache_strides_and_offset(orc):
+    """Any token stride, cache slots t0..t0+T-1, bf16 widened exactly."""
+    B, H, T, d, cap = 2, 3, 5, 16, 9
+    rng = np.random.default_rng(22)
+    Xbt = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    X = Xbt.transpose(0, 2, 1, 3)                       # [B][H][T][d] view, token stride H*d
+    side = orc.Side(1, 4, 0)
+    a = orc.OracleCache(B, H, cap, d, side, 0)
+    a.quantize(X, 3, None)
+    bc = orc.OracleCache(B, H, cap, d, side, 0)
+    bc.quantize(np.ascontiguousarray(X), 3, None)
+    assert np.array_equal(a.codes, bc.codes) and np.array_equal(a.norm, bc.norm)
+    assert not a.codes[:, :, :3].any() and not a.codes[:, :, 8:].any()
+    for bb in range(B):
+        for h in range(H):
+            for t in range(T):
+                codes, _, nb, _ = orc.encode(X[bb, h, t], side)
+                assert np.array_equal(a.codes[bb, h, 3 + t], codes) and a.norm[bb, h, 3 + t] == nb
+    Xb = torch.from_numpy(np.ascontiguousarray(X)).to(torch.bfloat16)
+    c16 = orc.OracleCache(B, H, cap, d, side, 0)
+    c16.quantize(Xb.view(torch.int16).numpy().view(np.uint16), 0, None)
+    c32 = orc.OracleCache(B, H, cap, d, side, 0)
+    c32.quantize(Xb.to(torch.float32).numpy(), 0, None)
+    assert np.array_equal(c16.codes, c32.codes) and np.array_equal(c16.norm, c32.norm)
+
+
+def test_codebook_golden_regression(orc):
+    """Stored tables (written by tests/golden/make_golden.py from the oracle)."""
+    with open(os.path.join(GOLDEN, "codebooks.json")) as f:
+        g = json.load(f)
+    for key, ent in g["tables"].items():
+        d, bits = map(int, key.split(","))
+        c, t, _ = orc.codebook(d, bits)
+        assert [int(v) for v in c.view(np.uint32)] == ent["centroid_bits"]
+        assert [int(v) for v in t.view(np.uint32)] == ent["threshold_bits"]
