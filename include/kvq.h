@@ -1,0 +1,187 @@
+/*
+ * kvq.h -- C ABI of libkvq: KQV KV-cache quantisation and decode attention
+ * over the compressed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages, cited by title and section):
+ *  - D'Alberto, "Statistical Inference and Quality Measures of KV Cache
+ *    Quantisations Inspired by TurboQuant" (gist.science technical summary),
+ *    "Quantization schemes": three schemes at a budget of n bits/coordinate
+ *      KV   : scalar Lloyd-Max on K and V, no rotation, no sketch
+ *      KQV  : Walsh-Hadamard transform (WHT) on both; K n-bit scalar;
+ *             V (n-1)-bit scalar + 1-bit QJL sketch of the residual
+ *      QKQV : WHT on both; K and V each (n-1)-bit scalar + 1-bit QJL sketch
+ *    "Theoretical framework": a coordinate of a uniform point on S^{d-1}
+ *    follows Beta((d-1)/2,(d-1)/2) on (1+t)/2; "Contribution 1": the sign
+ *    sketch is unbiased with variance (pi/2)||r||^2/d.
+ *  - "KVQuant++" forum thread (zingnex.cn): "Codebook design" -- the codebook
+ *    is fitted to f(t) ~ (1-t^2)^((d-3)/2); "Fast codebook lookup" --
+ *    bucketize against sorted thresholds; "Deployment and usage" --
+ *    construct(head_dim, num_bits) / compress / decompress.
+ *  - "Your KV cache is not a bit problem but a geometry problem": "Why the
+ *    KV cache is the pain point" -- every generated token reads the whole
+ *    cache; "Systems tax" -- per-token quantisation appends along the token
+ *    axis and nothing else moves.
+ *  - "HeadQ" explanation (gist.science), 2.1 score q.k/sqrt(d) and softmax;
+ *    2.2 the value readout is linear in the values.
+ *
+ * Conventions for every entry point
+ *  - Returns kvq_status; never throws; never synchronises a stream.
+ *  - Device pointers are caller-owned (allocate with torch / hipMalloc).  The
+ *    library allocates no device memory and keeps no pointer after return.
+ *  - All validation happens on the host before any launch: a call that fails
+ *    validation launches nothing.  A failed launch returns KVQ_ERR_HIP.
+ *    Asynchronous device faults surface at the caller's next synchronisation.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Entry points are reentrant; calls that write the same cache region
+ *    concurrently on different streams race.
+ *  - Inputs must be finite; NaN/Inf inputs give unspecified codes.  A norm
+ *    that overflows binary16 is stored as +Inf.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,       /* a required pointer is NULL */
+  KVQ_ERR_ALIGN = 2,      /* a pointer or stride breaks the 16-byte alignment rule */
+  KVQ_ERR_DIM = 3,        /* head dimension not in {16, 32, 64, 128} */
+  KVQ_ERR_BITS = 4,       /* bit width out of range for the scheme */
+  KVQ_ERR_SCHEME = 5,     /* unknown scheme */
+  KVQ_ERR_CAPACITY = 6,   /* t0 + T or n_ctx exceeds the cache capacity */
+  KVQ_ERR_WORKSPACE = 7,  /* workspace missing or too small */
+  KVQ_ERR_DTYPE = 8,      /* unknown element type */
+  KVQ_ERR_HEADS = 9,      /* q_heads not a supported multiple of kv_heads */
+  KVQ_ERR_RANGE = 10,     /* a size is zero/negative or a count overflows */
+  KVQ_ERR_HIP = 11        /* the HIP runtime reported an error on launch */
+} kvq_status;
+
+typedef enum { KVQ_SCHEME_KV = 0, KVQ_SCHEME_KQV = 1, KVQ_SCHEME_QKQV = 2 } kvq_scheme;
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+/* Scalar codebook for one (d, bits): 2^bits ascending fp32 centroids and the
+ * 2^bits - 1 midpoint thresholds (unused entries are zero).  Host POD; it is
+ * copied by value into kernel arguments. */
+typedef struct {
+  int32_t d, bits;
+  float centroid[16];
+  float threshold[15];
+} kvq_codebook;
+
+/* Lloyd-Max codebook on the sphere-marginal density f(t) ~ (1-t^2)^((d-3)/2)
+ * over [-1, 1] ("KVQuant++" thread, "Codebook design"; D'Alberto summary,
+ * "Theoretical framework"; Lloyd-Max: "Quantization schemes").  Host only.
+ * Iterated in fp64 to its fixed point (unique: the density is log-concave),
+ * then rounded once to fp32; the table is exactly symmetric and the middle
+ * threshold is 0.  d in [3, 4096], bits in [1, 4].
+ * Errors: KVQ_ERR_NULL (out NULL), KVQ_ERR_DIM, KVQ_ERR_BITS. */
+kvq_status kvq_codebook_init(int d, int bits, kvq_codebook *out);
+
+/* Gaussian sketch S (m x d, row-major, bfloat16 bit patterns) for the 1-bit
+ * QJL residual sketch (D'Alberto summary, "Problem statement" and
+ * "Contribution 1").  Host only; fills a caller-owned host buffer of m*d
+ * uint16.  Generator: SplitMix64 counter stream from `seed`, 53-bit uniforms,
+ * Box-Muller in fp64, rounded to fp32 then to bf16 (nearest even).
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_RANGE (m or d < 1). */
+kvq_status kvq_sketch_init(uint64_t seed, int m, int d, uint16_t *S_bf16_host);
+
+/* A compressed cache: caller-owned device buffers plus codec parameters.
+ * Buffer shapes (record per (batch b, KV head h, slot t), slot-major):
+ *   k_codes [B][Hkv][cap][d*kb/8]  k_norm  [B][Hkv][cap] binary16
+ *   k_signs [B][Hkv][cap][m/8]     k_rnorm [B][Hkv][cap] binary16  (K sketch only)
+ *   v_codes [B][Hkv][cap][d*vb/8]  v_norm  [B][Hkv][cap] binary16
+ *   v_signs [B][Hkv][cap][m/8]     v_rnorm [B][Hkv][cap] binary16  (V sketch only)
+ * kb, vb = per-side code widths of the scheme (see kvq_cache_init); m = d.
+ * Code layout inside a record: widths 1, 2, 4 -- code i at bit offset i*w,
+ * little-endian bytes; width 3 -- a 2-bit plane of the low bits (d/4 bytes)
+ * followed by a 1-bit plane of the high bits (d/8 bytes).  Sign bit k at byte
+ * k/8, bit k%8; bit = 1 means the sketch row is >= 0.  The stored norm is
+ * ||x||; the residual norm is ||r|| of the rotated unit direction.
+ * Pointers not used by the scheme must be NULL.  All pointers 16-B aligned. */
+typedef struct {
+  int32_t scheme, n_bits, d, m, batch, kv_heads, capacity;
+  int32_t k_bits, v_bits, k_qjl, v_qjl, rotate;  /* derived by kvq_cache_init */
+  kvq_codebook cb_k, cb_v;                       /* host copies, by value */
+  const uint16_t *S;                             /* device, m*d bf16, NULL if no sketch */
+  uint8_t *k_codes, *k_signs, *v_codes, *v_signs;
+  uint16_t *k_norm, *k_rnorm, *v_norm, *v_rnorm;
+} kvq_cache;
+
+/* Fill the scalar fields and codebooks of `c` for a scheme at n_bits per
+ * coordinate (KV: n in 1..4; KQV, QKQV: n in 2..4); leaves the pointers
+ * NULL.  Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME, KVQ_ERR_BITS, KVQ_ERR_DIM,
+ * KVQ_ERR_RANGE. */
+kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch,
+                          int kv_heads, int capacity);
+
+/* Byte sizes of the eight buffers, in the order k_codes, k_signs, k_norm,
+ * k_rnorm, v_codes, v_signs, v_norm, v_rnorm (0 = buffer unused).
+ * Errors: as kvq_cache_init. */
+kvq_status kvq_cache_layout(int scheme, int n_bits, int d, int batch, int kv_heads,
+                            int capacity, size_t bytes_out[8]);
+
+/* Quantize-on-write of T new tokens of K (resp. V) into slots t0..t0+T-1 of
+ * every (b, h) ("Systems tax": per-token append along the token axis).
+ * src element (b, h, t, i) is at src + (b*stride_b + h*stride_h + t*stride_t
+ * + i) elements of `dtype` (fp32 or bf16); strides are in elements, rows must
+ * be 16-B aligned.  Per vector: y = WHT(x) (rotated schemes), nu = ||y||,
+ * u = y/nu, code_i = #{thresholds < u_i} (bucketize), norm = ||x|| in fp16;
+ * sketch sides add r = u - C[code], ||r|| in fp16 and sign(S bf16(r)).
+ * fp32 arithmetic in a fixed order (ascending butterfly stages, adjacent-pair
+ * sums, correctly rounded sqrt and division, no contraction) so codes and
+ * sign bits are reproducible bit for bit.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_CAPACITY,
+ * KVQ_ERR_RANGE, KVQ_ERR_HIP. */
+kvq_status kvq_quantize_k(const kvq_cache *c, const void *src, int dtype, int t0, int T,
+                          int64_t stride_b, int64_t stride_h, int64_t stride_t, void *stream);
+kvq_status kvq_quantize_v(const kvq_cache *c, const void *src, int dtype, int t0, int T,
+                          int64_t stride_b, int64_t stride_h, int64_t stride_t, void *stream);
+
+/* Reconstruct slots t0..t0+T-1 of one side (which: 0 = K, 1 = V) into out
+ * [B][Hkv][T][d] fp32 (device):
+ *   x^ = ||x|| (H/sqrt(d)) (C[code] + sqrt(pi/2)/m ||r|| S^T (2 sigma - 1))
+ * (no H for the unrotated scheme, no sketch term for scalar-only sides).
+ * ("KVQuant++" thread, "Deployment and usage": decompress.)
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_CAPACITY, KVQ_ERR_RANGE, KVQ_ERR_HIP. */
+kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *out, void *stream);
+
+/* One decode step over the first n_ctx slots ("Why the KV cache is the pain
+ * point": every generated token reads the whole cache):
+ *   out[b][hq] = sum_j softmax_j(q[b][hq] . k^_j / sqrt(d)) v^_j
+ * with KV head hq / (q_heads / kv_heads) (grouped-query attention; q_heads a
+ * multiple of kv_heads with ratio 1, 2, 4 or a multiple of 4), no mask.
+ * q: [B][q_heads][d] fp32 or bf16 (device, contiguous); out: [B][q_heads][d]
+ * fp32 (device).  splits: number of token splits per (b, KV head); 0 picks
+ * one for the GPU.  workspace: device scratch of kvq_decode_workspace bytes.
+ * Keys are scored in rotated space (q is rotated once instead of each key);
+ * values and the V sketch term are accumulated in rotated and sketch space and
+ * mapped back with one S^T product and one WHT per query head.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_HEADS,
+ * KVQ_ERR_CAPACITY, KVQ_ERR_RANGE, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
+kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
+                                int n_ctx, int splits, float *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kvq_decode_attention needs for these arguments. */
+kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int splits,
+                                size_t *bytes);
+
+/* The split count kvq_decode_attention uses when splits == 0. */
+int kvq_decode_auto_splits(const kvq_cache *c, int q_heads, int n_ctx);
+
+/* Static text for a status code. */
+const char *kvq_status_str(kvq_status s);
+
+/* Library version string. */
+const char *kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,432 @@
+// kvq_host.cpp -- host half of libkvq: codebook construction, sketch
+// generation, cache layout, argument validation and the extern "C" entry
+// points that launch the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <type_traits>
+
+#include "kvq_internal.hpp"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Codebook: Lloyd-Max on f(t) ~ (1 - t^2)^((d-3)/2) over [-1, 1].
+// ("KVQuant++" thread, "Codebook design"; D'Alberto summary, "Theoretical
+// framework".)  With t = sin(theta) the weight becomes cos^(d-2)(theta), whose
+// integral from 0 follows the Wallis reduction
+//   W_n(x) = cos^(n-1)(x) sin(x) / n + (n-1)/n * W_(n-2)(x),  W_0 = x, W_1 = sin x,
+// and the first moment has the antiderivative -(1 - t^2)^((d-1)/2) / (d-1).
+// Only the positive half is iterated; the table is mirrored, so it is exactly
+// symmetric and the middle threshold is 0.
+// ---------------------------------------------------------------------------
+double wallis(int n, double x) {
+  double s = std::sin(x), c = std::cos(x);
+  double w = (n & 1) ? s : x;
+  double cp = (n & 1) ? 1.0 : c;  // cos^(k-1) for the next k
+  for (int k = (n & 1) ? 3 : 2; k <= n; k += 2) {
+    w = cp * s / k + (double)(k - 1) / k * w;
+    cp *= c * c;
+  }
+  return w;
+}
+
+double cell_mass(int d, double a, double b) {
+  return wallis(d - 2, std::asin(b)) - wallis(d - 2, std::asin(a));
+}
+
+double cell_moment(int d, double a, double b) {
+  double e = 0.5 * (d - 1);
+  return (std::pow(1.0 - a * a, e) - std::pow(1.0 - b * b, e)) / (d - 1);
+}
+
+void lloyd_max_positive(int d, int half, double *c) {
+  for (int i = 0; i < half; ++i) c[i] = std::fmin(0.95, 2.0 * (i + 0.5) / (half * std::sqrt((double)d)));
+  double edge[9];
+  int still = 0;
+  for (int it = 0; it < 400000; ++it) {
+    edge[0] = 0.0;
+    edge[half] = 1.0;
+    for (int i = 1; i < half; ++i) edge[i] = 0.5 * (c[i - 1] + c[i]);
+    double delta = 0.0, top = 0.0;
+    for (int i = 0; i < half; ++i) {
+      double nc = cell_moment(d, edge[i], edge[i + 1]) / cell_mass(d, edge[i], edge[i + 1]);
+      delta = std::fmax(delta, std::fabs(nc - c[i]));
+      top = std::fmax(top, std::fabs(nc));
+      c[i] = nc;
+    }
+    if (delta <= 4.0 * 2.220446049250313e-16 * top) break;
+    still = delta < 1e-13 * top ? still + 1 : 0;
+    if (still >= 64) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sketch generator: SplitMix64 (Steele, Lea & Flood 2014) counter stream,
+// 53-bit uniforms in (0, 1], Box-Muller pairs in fp64, fp32 then bf16 RNE.
+// ---------------------------------------------------------------------------
+uint64_t splitmix64(uint64_t &state) {
+  uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+uint16_t to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Sides {
+  int kb, vb, kq, vq, rot;
+};
+
+kvq_status scheme_sides(int scheme, int n, Sides *s) {
+  switch (scheme) {
+    case KVQ_SCHEME_KV:
+      if (n < 1 || n > 4) return KVQ_ERR_BITS;
+      *s = {n, n, 0, 0, 0};
+      return KVQ_OK;
+    case KVQ_SCHEME_KQV:
+      if (n < 2 || n > 4) return KVQ_ERR_BITS;
+      *s = {n, n - 1, 0, 1, 1};
+      return KVQ_OK;
+    case KVQ_SCHEME_QKQV:
+      if (n < 2 || n > 4) return KVQ_ERR_BITS;
+      *s = {n - 1, n - 1, 1, 1, 1};
+      return KVQ_OK;
+    default:
+      return KVQ_ERR_SCHEME;
+  }
+}
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Structural checks shared by every device entry point.
+kvq_status check_cache(const kvq_cache *c) {
+  if (!c) return KVQ_ERR_NULL;
+  Sides s;
+  kvq_status st = scheme_sides(c->scheme, c->n_bits, &s);
+  if (st != KVQ_OK) return st;
+  if (!supported_dim(c->d)) return KVQ_ERR_DIM;
+  if (c->m != c->d) return KVQ_ERR_DIM;
+  if (c->k_bits != s.kb || c->v_bits != s.vb || c->k_qjl != s.kq || c->v_qjl != s.vq ||
+      c->rotate != s.rot)
+    return KVQ_ERR_SCHEME;
+  if (c->cb_k.d != c->d || c->cb_k.bits != s.kb || c->cb_v.d != c->d || c->cb_v.bits != s.vb)
+    return KVQ_ERR_BITS;
+  if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 1) return KVQ_ERR_RANGE;
+  if ((long long)c->batch * c->kv_heads * c->capacity > (1ll << 40)) return KVQ_ERR_RANGE;
+  if (!c->k_codes || !c->k_norm || !c->v_codes || !c->v_norm) return KVQ_ERR_NULL;
+  if (s.kq && (!c->k_signs || !c->k_rnorm)) return KVQ_ERR_NULL;
+  if (s.vq && (!c->v_signs || !c->v_rnorm)) return KVQ_ERR_NULL;
+  if ((s.kq || s.vq) && !c->S) return KVQ_ERR_NULL;
+  const void *ptrs[] = {c->k_codes, c->k_norm, c->v_codes, c->v_norm, c->k_signs, c->k_rnorm,
+                        c->v_signs, c->v_rnorm, c->S};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+template <typename F>
+hipError_t by_dim(int d, F &&f) {
+  switch (d) {
+    case 16: return f(std::integral_constant<int, 16>{});
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    default: return f(std::integral_constant<int, 128>{});
+  }
+}
+
+const float kLog2e = 1.4426950408889634f;
+
+kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtype, int t0, int T,
+                         int64_t sb, int64_t sh, int64_t st, void *stream) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!src) return KVQ_ERR_NULL;
+  if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+  if (T < 1 || t0 < 0) return KVQ_ERR_RANGE;
+  if ((long long)t0 + T > c->capacity) return KVQ_ERR_CAPACITY;
+  const int esz = dtype == KVQ_F32 ? 4 : 2;
+  if (!aligned16(src) || ((sb * esz) & 15) || ((sh * esz) & 15) || ((st * esz) & 15))
+    return KVQ_ERR_ALIGN;
+  kvq::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.src = src;
+  a.sb = sb; a.sh = sh; a.st = st;
+  a.B = c->batch; a.H = c->kv_heads; a.T = T; a.t0 = t0; a.cap = c->capacity;
+  const int vt = c->d > 64 ? 32 : 64;  // tokens per quantize tile
+  a.tiles_per_bh = (T + vt - 1) / vt;
+  long long tiles = (long long)a.tiles_per_bh * a.B * a.H;
+  if (tiles > (1ll << 31) - 1) return KVQ_ERR_RANGE;
+  a.total_tiles = (int)tiles;
+  a.scale = c->rotate ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
+  const kvq_codebook &cb = side == 0 ? c->cb_k : c->cb_v;
+  for (int i = 0; i < 16; ++i) a.cent[i] = cb.centroid[i];
+  for (int i = 0; i < 15; ++i) a.thr[i] = cb.threshold[i];
+  a.S = c->S;
+  const bool qjl = side == 0 ? c->k_qjl : c->v_qjl;
+  a.codes = side == 0 ? c->k_codes : c->v_codes;
+  a.signs = side == 0 ? c->k_signs : c->v_signs;
+  a.norm = side == 0 ? c->k_norm : c->v_norm;
+  a.rnorm = side == 0 ? c->k_rnorm : c->v_rnorm;
+  const int bits = side == 0 ? c->k_bits : c->v_bits;
+  hipStream_t hs = (hipStream_t)stream;
+  return hip_status(by_dim(c->d, [&](auto D) {
+    return kvq::launch_quantize<decltype(D)::value>(a, bits, c->rotate != 0, qjl,
+                                                    dtype == KVQ_BF16, hs);
+  }));
+}
+
+int heads_per_block(int G) { return G >= 4 ? 4 : G; }
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || (G > 4 && G % 4 == 0); }
+
+int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
+  int G = q_heads / c->kv_heads;
+  int HG = G / heads_per_block(G);
+  long long units = (long long)c->batch * c->kv_heads * HG;
+  long long want = (2048 + units - 1) / units;
+  long long maxs = (n_ctx + 255) / 256;
+  long long s = want < maxs ? want : maxs;
+  if (s < 1) s = 1;
+  if (s > 1024) s = 1024;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_version(void) { return "libkvq 0.1 (gfx950)"; }
+
+const char *kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer";
+    case KVQ_ERR_ALIGN: return "misaligned pointer or stride (16-byte rule)";
+    case KVQ_ERR_DIM: return "unsupported head dimension";
+    case KVQ_ERR_BITS: return "bit width out of range for the scheme";
+    case KVQ_ERR_SCHEME: return "unknown or inconsistent scheme";
+    case KVQ_ERR_CAPACITY: return "token range exceeds cache capacity";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_DTYPE: return "unsupported element type";
+    case KVQ_ERR_HEADS: return "unsupported query/KV head ratio";
+    case KVQ_ERR_RANGE: return "size out of range";
+    case KVQ_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_codebook_init(int d, int bits, kvq_codebook *out) {
+  if (!out) return KVQ_ERR_NULL;
+  if (d < 3 || d > 4096) return KVQ_ERR_DIM;
+  if (bits < 1 || bits > 4) return KVQ_ERR_BITS;
+  std::memset(out, 0, sizeof(*out));
+  out->d = d;
+  out->bits = bits;
+  const int K = 1 << bits, half = K / 2;
+  double c[8];
+  lloyd_max_positive(d, half, c);
+  for (int i = 0; i < half; ++i) {
+    out->centroid[half + i] = (float)c[i];
+    out->centroid[half - 1 - i] = -(float)c[i];
+  }
+  out->threshold[half - 1] = 0.0f;
+  for (int i = 0; i + 1 < half; ++i) {
+    float t = (float)(0.5 * (c[i] + c[i + 1]));
+    out->threshold[half + i] = t;
+    out->threshold[half - 2 - i] = -t;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_sketch_init(uint64_t seed, int m, int d, uint16_t *S) {
+  if (!S) return KVQ_ERR_NULL;
+  if (m < 1 || d < 1) return KVQ_ERR_RANGE;
+  uint64_t state = seed;
+  const size_t n = (size_t)m * d;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (size_t i = 0; i < n; i += 2) {
+    double u1 = (double)((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+    double u2 = (double)((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+    double r = std::sqrt(-2.0 * std::log(u1));
+    S[i] = to_bf16((float)(r * std::cos(two_pi * u2)));
+    if (i + 1 < n) S[i + 1] = to_bf16((float)(r * std::sin(two_pi * u2)));
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch, int kv_heads,
+                          int capacity) {
+  if (!c) return KVQ_ERR_NULL;
+  Sides s;
+  kvq_status st = scheme_sides(scheme, n_bits, &s);
+  if (st != KVQ_OK) return st;
+  if (!supported_dim(d)) return KVQ_ERR_DIM;
+  if (batch < 1 || kv_heads < 1 || capacity < 1) return KVQ_ERR_RANGE;
+  std::memset(c, 0, sizeof(*c));
+  c->scheme = scheme; c->n_bits = n_bits; c->d = d; c->m = d;
+  c->batch = batch; c->kv_heads = kv_heads; c->capacity = capacity;
+  c->k_bits = s.kb; c->v_bits = s.vb; c->k_qjl = s.kq; c->v_qjl = s.vq; c->rotate = s.rot;
+  st = kvq_codebook_init(d, s.kb, &c->cb_k);
+  if (st != KVQ_OK) return st;
+  return kvq_codebook_init(d, s.vb, &c->cb_v);
+}
+
+kvq_status kvq_cache_layout(int scheme, int n_bits, int d, int batch, int kv_heads, int capacity,
+                            size_t bytes_out[8]) {
+  if (!bytes_out) return KVQ_ERR_NULL;
+  Sides s;
+  kvq_status st = scheme_sides(scheme, n_bits, &s);
+  if (st != KVQ_OK) return st;
+  if (!supported_dim(d)) return KVQ_ERR_DIM;
+  if (batch < 1 || kv_heads < 1 || capacity < 1) return KVQ_ERR_RANGE;
+  size_t rec = (size_t)batch * kv_heads * capacity;
+  bytes_out[0] = rec * d * s.kb / 8;
+  bytes_out[1] = s.kq ? rec * d / 8 : 0;
+  bytes_out[2] = rec * 2;
+  bytes_out[3] = s.kq ? rec * 2 : 0;
+  bytes_out[4] = rec * d * s.vb / 8;
+  bytes_out[5] = s.vq ? rec * d / 8 : 0;
+  bytes_out[6] = rec * 2;
+  bytes_out[7] = s.vq ? rec * 2 : 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_k(const kvq_cache *c, const void *src, int dtype, int t0, int T,
+                          int64_t stride_b, int64_t stride_h, int64_t stride_t, void *stream) {
+  return quantize_side(c, 0, src, dtype, t0, T, stride_b, stride_h, stride_t, stream);
+}
+
+kvq_status kvq_quantize_v(const kvq_cache *c, const void *src, int dtype, int t0, int T,
+                          int64_t stride_b, int64_t stride_h, int64_t stride_t, void *stream) {
+  return quantize_side(c, 1, src, dtype, t0, T, stride_b, stride_h, stride_t, stream);
+}
+
+kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *out, void *stream) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!out) return KVQ_ERR_NULL;
+  if (!aligned16(out)) return KVQ_ERR_ALIGN;
+  if (which != 0 && which != 1) return KVQ_ERR_RANGE;
+  if (T < 1 || t0 < 0) return KVQ_ERR_RANGE;
+  if ((long long)t0 + T > c->capacity) return KVQ_ERR_CAPACITY;
+  long long nvec = (long long)c->batch * c->kv_heads * T;
+  if (nvec > (1ll << 31) - 1) return KVQ_ERR_RANGE;
+  kvq::DequantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  const bool k = which == 0;
+  a.codes = k ? c->k_codes : c->v_codes;
+  a.signs = k ? c->k_signs : c->v_signs;
+  a.norm = k ? c->k_norm : c->v_norm;
+  a.rnorm = k ? c->k_rnorm : c->v_rnorm;
+  a.S = c->S;
+  a.out = out;
+  a.H = c->kv_heads; a.cap = c->capacity; a.t0 = t0; a.T = T;
+  const kvq_codebook &cb = k ? c->cb_k : c->cb_v;
+  for (int i = 0; i < 16; ++i) a.cent[i] = cb.centroid[i];
+  a.coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
+  a.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
+  const int bits = k ? c->k_bits : c->v_bits;
+  const bool qjl = k ? c->k_qjl : c->v_qjl;
+  hipStream_t hs = (hipStream_t)stream;
+  return hip_status(by_dim(c->d, [&](auto D) {
+    return kvq::launch_dequantize<decltype(D)::value>(a, bits, c->rotate != 0, qjl, (int)nvec, hs);
+  }));
+}
+
+int kvq_decode_auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
+  if (check_cache(c) != KVQ_OK || q_heads < 1 || n_ctx < 1 || q_heads % c->kv_heads) return 0;
+  if (!supported_group(q_heads / c->kv_heads)) return 0;
+  return auto_splits(c, q_heads, n_ctx);
+}
+
+kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int splits,
+                                size_t *bytes) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!bytes) return KVQ_ERR_NULL;
+  if (q_heads < 1 || q_heads % c->kv_heads) return KVQ_ERR_HEADS;
+  if (!supported_group(q_heads / c->kv_heads)) return KVQ_ERR_HEADS;
+  if (n_ctx < 1) return KVQ_ERR_RANGE;
+  if (n_ctx > c->capacity) return KVQ_ERR_CAPACITY;
+  if (splits < 0 || splits > 4096) return KVQ_ERR_RANGE;
+  if (splits == 0) splits = auto_splits(c, q_heads, n_ctx);
+  size_t rows = (size_t)c->batch * q_heads;
+  *bytes = sizeof(float) * (rows * c->d * 2 + rows * (size_t)splits * (2 + 2 * (size_t)c->d));
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
+                                int n_ctx, int splits, float *out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!q || !out) return KVQ_ERR_NULL;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  size_t need = 0;
+  s = kvq_decode_workspace(c, q_heads, n_ctx, splits, &need);
+  if (s != KVQ_OK) return s;
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (splits == 0) splits = auto_splits(c, q_heads, n_ctx);
+  const int d = c->d;
+  const int G = q_heads / c->kv_heads;
+  const int gt = heads_per_block(G);
+  const int rows = c->batch * q_heads;
+  float *ws = (float *)workspace;
+  float *qs = ws;
+  float *sq = ws + (size_t)rows * d;
+  float *part = ws + (size_t)rows * d * 2;
+  hipStream_t hs = (hipStream_t)stream;
+
+  kvq::PrepArgs p;
+  p.q = q; p.qs = qs; p.sq = sq; p.S = c->S; p.rows = rows;
+  p.qscale = c->rotate ? (float)(1.4426950408889634 / d) : (float)(1.4426950408889634 / std::sqrt((double)d));
+  (void)kLog2e;
+  hipError_t e = by_dim(d, [&](auto D) {
+    return kvq::launch_prep<decltype(D)::value>(p, c->rotate != 0, c->k_qjl != 0,
+                                                q_dtype == KVQ_BF16, hs);
+  });
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+
+  kvq::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
+  a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
+  a.qs = qs; a.sq = sq; a.part = part;
+  for (int i = 0; i < 16; ++i) {
+    a.kcent[i] = c->cb_k.centroid[i];
+    a.vcent[i] = c->cb_v.centroid[i];
+  }
+  a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
+  a.Hkv = c->kv_heads; a.Hq = q_heads; a.Gtot = G; a.HG = G / gt; a.cap = c->capacity;
+  a.n_ctx = n_ctx; a.splits = splits; a.tps = (n_ctx + splits - 1) / splits;
+  e = by_dim(d, [&](auto D) {
+    return kvq::launch_decode<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
+                                                  c->v_qjl != 0, gt, c->batch, hs);
+  });
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+
+  kvq::CombineArgs cb;
+  cb.part = part; cb.S = c->S; cb.out = out; cb.splits = splits;
+  cb.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
+  cb.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
+  e = by_dim(d, [&](auto D) {
+    return kvq::launch_combine<decltype(D)::value>(cb, c->rotate != 0, c->v_qjl != 0, rows, hs);
+  });
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// kvq_internal.hpp -- declarations shared by the libkvq translation units.
+// Host-side argument blocks and the per-head-dimension launch dispatchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// Quantize-on-write launch description (one side of the cache).
+struct QuantArgs {
+  const void *src;
+  long long sb, sh, st;      // element strides of the source
+  int B, H, T, t0, cap;
+  int tiles_per_bh, total_tiles;
+  float scale;               // stored norm = ||y|| * scale (1/sqrt(d) when rotated)
+  float cent[16];
+  float thr[15];
+  const uint16_t *S;         // m x d bf16 (sketch sides)
+  uint8_t *codes, *signs;
+  uint16_t *norm, *rnorm;
+};
+
+struct DequantArgs {
+  const uint8_t *codes, *signs;
+  const uint16_t *norm, *rnorm;
+  const uint16_t *S;
+  float *out;
+  int H, cap, t0, T;
+  float cent[16];
+  float coef;                // sqrt(pi/2)/m
+  float oscale;              // 1/sqrt(d) when rotated, else 1
+};
+
+struct PrepArgs {
+  const void *q;             // [B][Hq][d]
+  float *qs;                 // rotated, scaled query [B][Hq][d]
+  float *sq;                 // S qs (K sketch only) [B][Hq][d]
+  const uint16_t *S;
+  int rows;                  // B * Hq
+  float qscale;              // log2(e)/d (rotated) or log2(e)/sqrt(d)
+};
+
+struct DecodeArgs {
+  const uint8_t *kc, *ks, *vc, *vs;
+  const uint16_t *kn, *kr, *vn, *vr;
+  const float *qs, *sq;
+  float *part;               // [B][Hq][splits][2 + 2d]
+  float kcent[16], vcent[16];
+  float kcoef;               // sqrt(pi/2)/m (K sketch)
+  int Hkv, Hq, Gtot, HG, cap, n_ctx, splits, tps;
+};
+
+struct CombineArgs {
+  const float *part;
+  const uint16_t *S;
+  float *out;
+  int splits;
+  float vcoef;               // sqrt(pi/2)/m (V sketch)
+  float oscale;              // 1/sqrt(d) when rotated, else 1
+};
+
+// Dispatchers: one translation unit per head dimension.
+template <int D> hipError_t launch_quantize(const QuantArgs &a, int bits, bool rot, bool qjl,
+                                            bool bf16, hipStream_t s);
+template <int D> hipError_t launch_dequantize(const DequantArgs &a, int bits, bool rot, bool qjl,
+                                              int n_vec, hipStream_t s);
+template <int D> hipError_t launch_prep(const PrepArgs &a, bool rot, bool kqjl, bool bf16,
+                                        hipStream_t s);
+template <int D> hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq,
+                                          int gt, int B, hipStream_t s);
+template <int D> hipError_t launch_combine(const CombineArgs &a, bool rot, bool vq, int rows,
+                                           hipStream_t s);
+
+}  // namespace kvq

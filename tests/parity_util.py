@@ -1,0 +1,68 @@
+"""Shared helpers for the GPU-vs-oracle parity tests (test infrastructure)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from kv_cache_quantization_kqv_amd import synth
+from kv_cache_quantization_kqv_amd.kvq import KVQCache
+from oracle import ref
+
+
+def host_bits(x: torch.Tensor) -> np.ndarray:
+    """CPU numpy view for the oracle: fp32 stays fp32, bf16 becomes uint16 bits."""
+    x = x.detach().cpu()
+    if x.dtype == torch.bfloat16:
+        return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return x.numpy()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy().view(np.uint16)
+
+
+class Pair:
+    """A GPU cache and the oracle's cache of the same scheme and inputs."""
+
+    def __init__(self, scheme, n, d, B, Hkv, cap, S=None, device="cuda"):
+        self.scheme, self.n, self.d, self.B, self.Hkv, self.cap = scheme, n, d, B, Hkv, cap
+        self.S_t = synth.sketch_bf16(d, d, 7) if S is None else S
+        self.S = synth.bits_u16(self.S_t)
+        self.gpu = KVQCache(scheme, n, d, B, Hkv, cap, S_bf16=self.S, device=device)
+        ks, vs = ref.scheme_sides(scheme, n)
+        self.ok = ref.OracleCache(B, Hkv, cap, d, ks, d)
+        self.ov = ref.OracleCache(B, Hkv, cap, d, vs, d)
+
+    def write(self, K: torch.Tensor, V: torch.Tensor, t0: int, dev="cuda", nthreads=8):
+        """K, V: [B][Hkv][T][d] tensors (any strides, innermost contiguous)."""
+        self.gpu.quantize_k(K.to(dev) if K.device.type != "cuda" else K, t0)
+        self.gpu.quantize_v(V.to(dev) if V.device.type != "cuda" else V, t0)
+        self.ok.quantize(host_bits(K), t0, self.S, nthreads)
+        self.ov.quantize(host_bits(V), t0, self.S, nthreads)
+
+    def assert_bit_exact(self, slots=None):
+        sl = slice(None) if slots is None else slots
+        g = self.gpu
+        pairs = [("k_codes", self.ok.codes), ("v_codes", self.ov.codes)]
+        assert np.array_equal(g.view("k_codes").cpu().numpy()[:, :, sl], self.ok.codes[:, :, sl]), "K codes"
+        assert np.array_equal(g.view("v_codes").cpu().numpy()[:, :, sl], self.ov.codes[:, :, sl]), "V codes"
+        assert np.array_equal(u16(g.view("k_norm"))[:, :, sl], self.ok.norm[:, :, sl]), "K norms"
+        assert np.array_equal(u16(g.view("v_norm"))[:, :, sl], self.ov.norm[:, :, sl]), "V norms"
+        if self.ok.side.qjl:
+            assert np.array_equal(g.view("k_signs").cpu().numpy()[:, :, sl], self.ok.signs[:, :, sl]), "K signs"
+            assert np.array_equal(u16(g.view("k_rnorm"))[:, :, sl], self.ok.rnorm[:, :, sl]), "K rnorms"
+        if self.ov.side.qjl:
+            assert np.array_equal(g.view("v_signs").cpu().numpy()[:, :, sl], self.ov.signs[:, :, sl]), "V signs"
+            assert np.array_equal(u16(g.view("v_rnorm"))[:, :, sl], self.ov.rnorm[:, :, sl]), "V rnorms"
+        del pairs
+
+    def attention(self, q: torch.Tensor, n_ctx: int, rows=None, nthreads=8):
+        return ref.attention(self.ok, self.ov, host_bits(q), n_ctx, self.S, rows=rows,
+                             nthreads=nthreads)
+
+
+def rel_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    """Per-row ||got - want|| / ||want|| over the last axis."""
+    num = np.linalg.norm(got.astype(np.float64) - want, axis=-1)
+    den = np.linalg.norm(want, axis=-1)
+    return num / np.maximum(den, 1e-300)

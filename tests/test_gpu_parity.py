@@ -1,0 +1,194 @@
+"""GPU (HIP, through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Codes, norms, residual norms and sign bits: bit for bit.  Reconstructed vectors
+and attention outputs: per vector / per (b, query head) relative error within
+1e-5 for fp32 inputs and 2e-3 * ||o|| for bf16 inputs (the stated tolerances).
+Sizes span several encoder tiles (32 or 64 tokens) with a ragged tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_kqv_amd import synth
+from parity_util import Pair, rel_rows
+
+pytestmark = pytest.mark.gpu
+
+SCHEME_BITS = [("KV", 1), ("KV", 2), ("KV", 3), ("KV", 4), ("KQV", 2), ("KQV", 3), ("KQV", 4),
+               ("QKQV", 2), ("QKQV", 3), ("QKQV", 4)]
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def _inputs(B, H, T, d, dtype, seed, heavy=False):
+    if heavy:
+        K = synth.lowrank_heavytail_keys(B, H, T, d, seed, dtype=dtype)
+    else:
+        K = synth.gaussian((B, H, T, d), seed, dtype) * 3
+    V = synth.gaussian((B, H, T, d), seed + 1, dtype)
+    return K.to(dtype), V.to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("scheme,n", SCHEME_BITS, ids=[f"{s}{n}" for s, n in SCHEME_BITS])
+def test_quantize_bit_exact(scheme, n, d, dtype):
+    print(f"case quantize {scheme}{n} d={d} {dtype}", flush=True)
+    B, H, T, t0, cap = 2, 3, 77, 5, 90
+    P = Pair(scheme, n, d, B, H, cap)
+    K, V = _inputs(B, H, T, d, dtype, 100 + d + n, heavy=(scheme != "KV"))
+    P.write(K, V, t0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scheme,n", [("KV", 4), ("KQV", 4), ("KQV", 2), ("QKQV", 3)])
+def test_dequantize_matches_oracle(scheme, n, d):
+    print(f"case dequantize {scheme}{n} d={d}", flush=True)
+    B, H, T, cap = 2, 2, 70, 70
+    P = Pair(scheme, n, d, B, H, cap)
+    K, V = _inputs(B, H, T, d, torch.float32, 300 + d)
+    P.write(K, V, 0)
+    for which, oc in ((0, P.ok), (1, P.ov)):
+        got = P.gpu.dequantize(which, 3, 60).cpu().numpy()
+        want = oc.dequantize(3, 60, P.S, nthreads=8)
+        err = rel_rows(got, want)
+        assert err.max() < 1e-5, (which, err.max())
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("scheme,n", [("KV", 2), ("KV", 4), ("KQV", 2), ("KQV", 3), ("KQV", 4),
+                                      ("QKQV", 2), ("QKQV", 4)])
+def test_decode_matches_oracle(scheme, n, d, dtype):
+    print(f"case decode {scheme}{n} d={d} {dtype}", flush=True)
+    B, Hkv, G, N = 2, 2, 2, 300
+    P = Pair(scheme, n, d, B, Hkv, N + 3)
+    K, V = _inputs(B, Hkv, N, d, dtype, 500 + d + n, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, Hkv * G, d), 900 + d, dtype)
+    want = P.attention(q, N)
+    for splits in (0, 1, 7):
+        got = P.gpu.decode_attention(q.cuda(), N, splits=splits).cpu().numpy()
+        err = rel_rows(got, want)
+        assert err.max() < TOL[dtype], (splits, err.max())
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_gqa_ratios(G):
+    print(f"case gqa G={G}", flush=True)
+    B, Hkv, d, N = 2, 2, 128, 517
+    P = Pair("KQV", 4, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, torch.bfloat16, 700 + G, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, Hkv * G, d), 800 + G, torch.bfloat16)
+    want = P.attention(q, N)
+    got = P.gpu.decode_attention(q.cuda(), N).cpu().numpy()
+    assert rel_rows(got, want).max() < 2e-3
+    # same cache, fp32 query: tight tolerance
+    qf = q.float()
+    got = P.gpu.decode_attention(qf.cuda(), N).cpu().numpy()
+    assert rel_rows(got, P.attention(qf, N)).max() < 1e-5
+
+
+def test_tiny_single_head_workload():
+    """d=64, N=256, one head, fp32 K, V, q ~ N(0,1); KQV n=4 (K 4-bit after WHT;
+    V 3-bit + 1-bit sketch, S 64x64); quantize both, one decode step."""
+    w = synth.WORKLOADS["tiny_single_head"]
+    K, V, q = synth.make_kvq(w)
+    P = Pair(w.scheme, w.n_bits, w.d, w.B, w.Hkv, w.N)
+    P.write(K, V, 0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+    got = P.gpu.decode_attention(q.cuda(), w.N).cpu().numpy()
+    assert rel_rows(got, P.attention(q, w.N)).max() < 1e-5
+
+
+def test_chunked_and_token_appends_equal_one_shot():
+    """Per-token append ("Systems tax": quantise each arriving token, nothing else
+    moves): chunked and single-token writes give the same bytes as one write."""
+    B, H, d, T = 2, 2, 128, 150
+    K, V = _inputs(B, H, T, d, torch.bfloat16, 41, heavy=True)
+    one = Pair("KQV", 4, d, B, H, T)
+    one.write(K, V, 0)
+    many = Pair("KQV", 4, d, B, H, T)
+    for t0, t1 in [(0, 64), (64, 100), (100, 147)]:
+        many.gpu.quantize_k(K[:, :, t0:t1].cuda(), t0)
+        many.gpu.quantize_v(V[:, :, t0:t1].cuda(), t0)
+    for t in range(147, T):
+        many.gpu.quantize_k(K[:, :, t:t + 1].cuda(), t)
+        many.gpu.quantize_v(V[:, :, t:t + 1].cuda(), t)
+    for name in one.gpu.bufs:
+        assert torch.equal(one.gpu.bufs[name], many.gpu.bufs[name]), name
+    one.assert_bit_exact()
+
+
+def test_strided_and_offset_input():
+    B, H, T, d = 2, 3, 70, 64
+    base = synth.gaussian((B, T, H, d), 51, torch.bfloat16)
+    Kv = base.permute(0, 2, 1, 3)                  # [B][H][T][d] view, token stride H*d
+    V = synth.gaussian((B, H, T, d), 52, torch.bfloat16)
+    P = Pair("QKQV", 4, d, B, H, T + 10)
+    P.gpu.quantize_k(base.cuda().permute(0, 2, 1, 3), 10)
+    P.gpu.quantize_v(V.cuda(), 10)
+    P.ok.quantize(synth.bits_u16(Kv.contiguous()), 10, P.S)
+    P.ov.quantize(synth.bits_u16(V), 10, P.S)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+
+
+def test_sign_fixup_rows():
+    """Sketch rows that are zero give z = 0 exactly: the certified-sign test fails
+    and the fp64 recomputation must set the bit (ties -> 1); negated duplicate
+    rows must give complementary bits."""
+    d = 128
+    S = synth.sketch_bf16(d, d, 9).clone()
+    S[0:8] = 0
+    S[8:16] = -S[16:24]
+    e = torch.zeros(8, d, dtype=torch.bfloat16)
+    for i in range(8):
+        e[i, i] = 1
+    S[24:32] = e                                   # z_k = r~_k exactly
+    B, H, T = 1, 2, 96
+    K, V = _inputs(B, H, T, d, torch.float32, 61)
+    V[0, 0, :5] = 0                                # zero vectors
+    P = Pair("QKQV", 3, d, B, H, T, S=S)
+    P.write(K, V, 0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+    sg = P.gpu.view("v_signs").cpu().numpy()
+    assert np.all(sg[..., 0] == 0xFF)              # rows 0..7 are zero -> bit 1
+
+
+def test_zero_and_large_vectors():
+    B, H, T, d = 1, 1, 40, 128
+    K = torch.zeros(B, H, T, d)
+    K[0, 0, 10:20] = synth.gaussian((10, d), 71, torch.float32) * 1e4   # norms beyond fp16 range
+    V = synth.gaussian((B, H, T, d), 72, torch.float32)
+    V[0, 0, :8] = 0
+    P = Pair("KQV", 4, d, B, H, T)
+    P.write(K, V, 0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+    kn = P.gpu.view("k_norm").cpu().numpy().view(np.uint16)
+    assert np.all(kn[0, 0, :10] == 0) and np.all(kn[0, 0, 10:20] == 0x7C00)
+
+
+def test_single_token_context():
+    B, H, d = 2, 2, 64
+    K, V = _inputs(B, H, 4, d, torch.float32, 81)
+    P = Pair("KQV", 4, d, B, H, 4)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, H, d), 82, torch.float32)
+    got = P.gpu.decode_attention(q.cuda(), 1).cpu().numpy()
+    want = P.attention(q, 1)
+    assert rel_rows(got, want).max() < 1e-5
+    vh = P.gpu.dequantize(1, 0, 1).cpu().numpy()[:, :, 0]
+    assert np.allclose(got, vh, rtol=1e-5, atol=1e-6)   # o = v^_1
