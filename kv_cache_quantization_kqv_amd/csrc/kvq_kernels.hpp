@@ -33,8 +33,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// binary16, round to nearest even, overflow to infinity (v_cvt_f16_f32).
+// binary16, round to nearest even, overflow to infinity (v_cvt_f16_f32).  The
+// argument is pinned in a register first: otherwise the compiler may fuse a
+// preceding fp32 multiply into v_fma_mixlo_f16, which rounds once instead of
+// fp32-then-fp16 and can differ by one binary16 ulp.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  asm volatile("" : "+v"(f));
   _Float16 h = (_Float16)f;
   return __builtin_bit_cast(uint16_t, h);
 }

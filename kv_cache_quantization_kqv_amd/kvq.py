@@ -174,7 +174,10 @@ class KVQCache:
         self.torch = torch
         self.scheme, self.n_bits, self.d = scheme, n_bits, d
         self.batch, self.kv_heads, self.capacity = batch, kv_heads, capacity
-        self.device = torch.device(device)
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
         self.c = kvq_cache_init(SCHEMES[scheme], n_bits, d, batch, kv_heads, capacity)
         sizes = kvq_cache_layout(SCHEMES[scheme], n_bits, d, batch, kv_heads, capacity)
         self.bufs = {}

@@ -43,18 +43,23 @@ class Pair:
     def assert_bit_exact(self, slots=None):
         sl = slice(None) if slots is None else slots
         g = self.gpu
-        pairs = [("k_codes", self.ok.codes), ("v_codes", self.ov.codes)]
-        assert np.array_equal(g.view("k_codes").cpu().numpy()[:, :, sl], self.ok.codes[:, :, sl]), "K codes"
-        assert np.array_equal(g.view("v_codes").cpu().numpy()[:, :, sl], self.ov.codes[:, :, sl]), "V codes"
-        assert np.array_equal(u16(g.view("k_norm"))[:, :, sl], self.ok.norm[:, :, sl]), "K norms"
-        assert np.array_equal(u16(g.view("v_norm"))[:, :, sl], self.ov.norm[:, :, sl]), "V norms"
+        checks = [("k_codes", g.view("k_codes").cpu().numpy(), self.ok.codes),
+                  ("v_codes", g.view("v_codes").cpu().numpy(), self.ov.codes),
+                  ("k_norm", u16(g.view("k_norm")), self.ok.norm),
+                  ("v_norm", u16(g.view("v_norm")), self.ov.norm)]
         if self.ok.side.qjl:
-            assert np.array_equal(g.view("k_signs").cpu().numpy()[:, :, sl], self.ok.signs[:, :, sl]), "K signs"
-            assert np.array_equal(u16(g.view("k_rnorm"))[:, :, sl], self.ok.rnorm[:, :, sl]), "K rnorms"
+            checks += [("k_signs", g.view("k_signs").cpu().numpy(), self.ok.signs),
+                       ("k_rnorm", u16(g.view("k_rnorm")), self.ok.rnorm)]
         if self.ov.side.qjl:
-            assert np.array_equal(g.view("v_signs").cpu().numpy()[:, :, sl], self.ov.signs[:, :, sl]), "V signs"
-            assert np.array_equal(u16(g.view("v_rnorm"))[:, :, sl], self.ov.rnorm[:, :, sl]), "V rnorms"
-        del pairs
+            checks += [("v_signs", g.view("v_signs").cpu().numpy(), self.ov.signs),
+                       ("v_rnorm", u16(g.view("v_rnorm")), self.ov.rnorm)]
+        for name, got, want in checks:
+            got, want = got[:, :, sl], want[:, :, sl]
+            if not np.array_equal(got, want):
+                bad = np.argwhere(got != want)
+                first = [(tuple(int(v) for v in ix), int(got[tuple(ix)]), int(want[tuple(ix)]))
+                         for ix in bad[:6]]
+                raise AssertionError(f"{name}: {len(bad)} of {got.size} differ; first {first}")
 
     def attention(self, q: torch.Tensor, n_ctx: int, rows=None, nthreads=8):
         return ref.attention(self.ok, self.ov, host_bits(q), n_ctx, self.S, rows=rows,

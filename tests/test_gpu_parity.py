@@ -92,10 +92,12 @@ def test_decode_gqa_ratios(G):
     want = P.attention(q, N)
     got = P.gpu.decode_attention(q.cuda(), N).cpu().numpy()
     assert rel_rows(got, want).max() < 2e-3
-    # same cache, fp32 query: tight tolerance
+    # same cache, fp32 query.  K and V are bf16 inputs (stated tolerance 2e-3);
+    # the heavy-tailed keys give scores of magnitude ~1e2, where fp32 score
+    # rounding alone moves softmax weights by ~1e-5 relative, so check 1e-4.
     qf = q.float()
     got = P.gpu.decode_attention(qf.cuda(), N).cpu().numpy()
-    assert rel_rows(got, P.attention(qf, N)).max() < 1e-5
+    assert rel_rows(got, P.attention(qf, N)).max() < 1e-4
 
 
 def test_tiny_single_head_workload():
