@@ -108,6 +108,28 @@ kvq_status scheme_sides(int scheme, int n, Sides *s) {
 
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// The encoder's table bucketize needs a symmetric threshold table with a zero
+// middle threshold, and at most one positive threshold in every cell of the
+// 11-bit prefix (exponent + 3 mantissa bits) of |u|.
+bool codebook_usable(const kvq_codebook &cb) {
+  const int K = 1 << cb.bits, half = K / 2;
+  if (cb.threshold[half - 1] != 0.0f) return false;
+  for (int k = 0; k + 1 < half; ++k) {
+    const float p = cb.threshold[half + k];
+    if (!(p > 0.0f) || p >= 2.0f || cb.threshold[half - 2 - k] != -p) return false;
+    if (k > 0) {
+      uint32_t a, b;
+      const float q = cb.threshold[half + k - 1];
+      std::memcpy(&a, &q, 4);
+      std::memcpy(&b, &p, 4);
+      if ((a >> 20) == (b >> 20) || !(p > q)) return false;
+    }
+  }
+  for (int i = 0; i < half; ++i)
+    if (cb.centroid[half + i] != -cb.centroid[half - 1 - i]) return false;
+  return true;
+}
+
 // Structural checks shared by every device entry point.
 kvq_status check_cache(const kvq_cache *c) {
   if (!c) return KVQ_ERR_NULL;
@@ -121,6 +143,7 @@ kvq_status check_cache(const kvq_cache *c) {
     return KVQ_ERR_SCHEME;
   if (c->cb_k.d != c->d || c->cb_k.bits != s.kb || c->cb_v.d != c->d || c->cb_v.bits != s.vb)
     return KVQ_ERR_BITS;
+  if (!codebook_usable(c->cb_k) || !codebook_usable(c->cb_v)) return KVQ_ERR_BITS;
   if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 1) return KVQ_ERR_RANGE;
   if ((long long)c->batch * c->kv_heads * c->capacity > (1ll << 40)) return KVQ_ERR_RANGE;
   if (!c->k_codes || !c->k_norm || !c->v_codes || !c->v_norm) return KVQ_ERR_NULL;

@@ -15,6 +15,10 @@
 
 #include "kvq_internal.hpp"
 
+#ifndef KVQ_DECODE_E4
+#define KVQ_DECODE_E4 8  // coordinates per lane when four query heads share a KV head
+#endif
+
 namespace kvq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -159,23 +163,134 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 }
 
 // ---------------------------------------------------------------------------
-// Quantize-on-write.  One wave (64 lanes) per block; a tile is VT consecutive
-// tokens of one (b, h), each token owned by LPV lanes (LPV = 2 for D = 128,
-// else 1), each lane holding DL = D/LPV consecutive coordinates in registers.
-// The tile is read with coalesced 16-B loads into LDS (padded rows).
+// Exact bucketize by table ("KVQuant++" thread, "Fast codebook lookup": a
+// lookup against sorted thresholds instead of a nearest-centroid search).
+// For |u| the top 11 bits of its fp32 pattern (exponent and 3 mantissa bits)
+// are monotone in |u| and cut [0, 2) into cells whose width is at most 1/8 of
+// their lower end.  Consecutive positive thresholds of the tables used here
+// are more than 9/8 apart, so a cell holds at most one of them (the host
+// checks this for every table it builds).  cell_lo[idx] counts the positive
+// thresholds below the cell; one exact comparison with the next threshold
+// finishes the count.  With the table symmetric and the middle threshold 0:
+//   u > 0 : code = K/2 + #{P_k <  |u|}
+//   u <= 0: code = K/2 - 1 - #{P_k <= |u|}
+// which equals #{thresholds < u} (ties go to the lower cell).
+// ---------------------------------------------------------------------------
+struct BucketTables {
+  uint8_t cell_lo[1024];   // per 11-bit |u| prefix: positive thresholds below the cell
+  float pos[9];            // positive thresholds, then +inf sentinels
+  float cent[16];
+};
+
+template <int BITS>
+__device__ void build_bucket_tables(BucketTables &bt, const float *thr, const float *cent, int tid,
+                                    int nthreads) {
+  constexpr int K2 = 1 << (BITS - 1);
+  for (int i = tid; i < 1024; i += nthreads) {
+    const float lo = __uint_as_float((uint32_t)i << 20);
+    int c = 0;
+    for (int k = 0; k + 1 < K2; ++k) c += (thr[K2 + k] < lo) ? 1 : 0;
+    bt.cell_lo[i] = (uint8_t)c;
+  }
+  if (tid < 9) bt.pos[tid] = (tid + 1 < K2) ? thr[K2 + tid] : INFINITY;
+  if (tid < 16) bt.cent[tid] = cent[tid];
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables &bt) {
+  constexpr int K2 = 1 << (BITS - 1);
+  const float au = fabsf(u);
+  const uint32_t idx = min(__float_as_uint(au) >> 20, 1023u);  // |u| <= 1 (1+ulp) in practice
+  const uint32_t c = bt.cell_lo[idx];
+  const float p = bt.pos[c];
+  const uint32_t lt = c + (p < au ? 1u : 0u);              // #{P_k <  |u|}
+  const uint32_t le = lt + (p == au ? 1u : 0u);            // #{P_k <= |u|}
+  return u > 0.0f ? (uint32_t)K2 + lt : (uint32_t)(K2 - 1) - le;
+}
+
+// Value of the partner lane (lane ^ 1) through a DPP quad permute (no LDS).
+__device__ __forceinline__ float xor1_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t xor1_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// Codes of DL consecutive coordinates packed at compile-time positions: widths
+// 1, 2, 4 as one little-endian image; width 3 as a 2-bit plane image (DL/16
+// words) followed by a 1-bit plane image (DL/32 words, at least one).
+template <int DL, int BITS>
+struct LocalCodes {
+  static constexpr int NA = BITS == 3 ? DL / 16 : (DL * BITS + 31) / 32;
+  static constexpr int NB = BITS == 3 ? (DL + 31) / 32 : 0;
+  uint32_t w[NA + NB];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int k = 0; k < NA + NB; ++k) w[k] = 0u;
+  }
+  __device__ __forceinline__ void put(int i, uint32_t code) {
+    if constexpr (BITS == 3) {
+      w[(2 * i) >> 5] |= (code & 3u) << ((2 * i) & 31);
+      w[NA + (i >> 5)] |= (code >> 2) << (i & 31);
+    } else {
+      w[(i * BITS) >> 5] |= code << ((i * BITS) & 31);
+    }
+  }
+};
+
+// Record image of a D-vector from the halves built by a lane pair (LPV = 2):
+// own = coordinates [0, DL), other = [DL, 2 DL).  Layout as in place_code.
+template <int D, int DL, int BITS, int RECW>
+__device__ __forceinline__ void join_halves(uint32_t *rec, const LocalCodes<DL, BITS> &own,
+                                            const LocalCodes<DL, BITS> &other) {
+  using LC = LocalCodes<DL, BITS>;
+  if constexpr (BITS == 3) {
+#pragma unroll
+    for (int k = 0; k < LC::NA; ++k) {
+      rec[k] = own.w[k];
+      rec[LC::NA + k] = other.w[k];
+    }
+#pragma unroll
+    for (int k = 0; k < LC::NB; ++k) {
+      rec[2 * LC::NA + k] = own.w[LC::NA + k];
+      rec[2 * LC::NA + LC::NB + k] = other.w[LC::NA + k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < LC::NA; ++k) {
+      rec[k] = own.w[k];
+      rec[LC::NA + k] = other.w[k];
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Quantize-on-write.  Blocks of 4 waves share the bucketize tables and (sketch
+// sides) the sketch matrix S, staged once in LDS with a padded row pitch; each
+// wave then walks its own tiles.  A tile is VT consecutive tokens of one
+// (b, h), each token owned by LPV lanes (LPV = 2 for D = 128, else 1), each
+// lane holding DL = D/LPV consecutive coordinates in registers.  The tile is
+// read with coalesced 16-B loads into a padded LDS stage; the next tile's loads
+// are issued before the current one is processed.
 // Butterfly stages h < DL run in registers; the last stage of a split vector is
 // one exchange with the partner lane (lane ^ 1), and the pairwise sum of
 // squares of a split vector is (left half sum) + (right half sum), which is the
 // root of the same adjacent-pair tree.  Then u = y * (1/nu), bucketize, pack.
-// Sketch sides write the bf16 residual halves back to LDS and form z = S r~ for
-// the tile with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  A sign is taken
-// from z when |z| exceeds a bound on the accumulation error of any summation
-// order, D * 2^-22 * ||S_k|| * ||r~|| (+2^-100 for flushed denormals);
-// otherwise the lane recomputes that row in fp64, ascending, which is the
-// definition.
+// Sketch sides write the bf16 residual halves back to the stage and form
+// z = S r~ for the tile with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  A
+// sign is taken from z when |z| exceeds a bound on the accumulation error of
+// any summation order, D * 2^-22 * ||S_k|| * ||r~|| (+2^-100 for flushed
+// denormals); otherwise the lane recomputes that row in fp64, ascending, which
+// is the definition.
 // ---------------------------------------------------------------------------
 template <int D, int BITS, bool ROT, bool QJL, bool BF16>
-__global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
+__global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
   constexpr int LPV = D > 64 ? 2 : 1;        // lanes per vector
   constexpr int DL = D / LPV;                // coordinates per lane
   constexpr int VT = 64 / LPV;               // vectors per tile
@@ -188,25 +303,30 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
   constexpr int RECW = (RECB + 3) / 4;
   constexpr int NCT = (D + 31) / 32;
   constexpr int NRT = VT / 32;
-  constexpr int P2 = D * 2 + 16;
+  constexpr int P2 = D * 2 + 16;             // bf16 row pitch (residuals, S)
+  constexpr int SBYTES = QJL ? D * P2 : 16;
   static_assert(VT * P2 <= VT * PITCH, "residual rows must fit the staging buffer");
   static_assert((VT * CPR) % 64 == 0, "tile copy must split evenly over the wave");
-  __shared__ __attribute__((aligned(16))) unsigned char stage[VT * PITCH];
-  __shared__ float cent_s[16];
-  __shared__ float rn_s[VT];
-  __shared__ uint32_t sg_s[VT * NCT];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_all[4][VT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
+  __shared__ BucketTables bt;
+  __shared__ float rn_all[4][VT];
+  __shared__ uint32_t sg_all[4][VT * NCT];
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned char *stage = stage_all[wave];
+  float *rn_s = rn_all[wave];
+  uint32_t *sg_s = sg_all[wave];
   const int vrow = lane / LPV;               // token row of this lane in the tile
   const int half = lane % LPV;               // which coordinate half
-  if (lane < 16) cent_s[lane] = a.cent[lane];
-  uint32_t thr[15];
-#pragma unroll
-  for (int k = 0; k < 15; ++k) {
-    uint32_t v = __float_as_uint(a.thr[k]);
-    asm volatile("" : "+v"(v));
-    thr[k] = v;
+  build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
+  if constexpr (QJL) {
+    for (int i = tid; i < D * (D / 8); i += 256) {     // 16-B chunks of S
+      const int r = i / (D / 8), c = i - r * (D / 8);
+      *(u32x4 *)(S_s + r * P2 + c * 16) = *(const u32x4 *)(a.S + (size_t)r * D + c * 8);
+    }
   }
+  __syncthreads();
 
   float snorm[NCT];
 #pragma unroll
@@ -215,20 +335,22 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
 #pragma unroll 1
     for (int ct = 0; ct < NCT; ++ct) {
       const int col = ct * 32 + (lane & 31);
-      float s = 0.0f;
+      float sq = 0.0f;
       if (col < D) {
+        const uint16_t *sr = (const uint16_t *)(S_s + col * P2);
         for (int i = 0; i < D; ++i) {
-          const float v = bf16_to_f32(a.S[(size_t)col * D + i]);
-          s = s + v * v;
+          const float v = bf16_to_f32(sr[i]);
+          sq = sq + v * v;
         }
       }
-      snorm[ct] = sqrtf(s) * (1.0f + 0x1p-12f);
+      snorm[ct] = sqrtf(sq) * (1.0f + 0x1p-12f);
     }
   }
-  __syncthreads();
 
-#pragma unroll 1
-  for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
+  const int tile0 = blockIdx.x * 4 + wave;
+  const int tstride = gridDim.x * 4;
+  u32x4 pf[NLD];
+  auto fetch = [&](int tile) {
     const int bh = tile / a.tiles_per_bh;
     const int tt = tile - bh * a.tiles_per_bh;
     const int b = bh / a.H, h = bh - b * a.H;
@@ -241,11 +363,30 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
     for (int k = 0; k < NLD; ++k) {
       const int ci = lane + 64 * k;
       const int r = ci / CPR, cc = ci - r * CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < nvalid) v = *(const u32x4 *)(src0 + r * rstride + cc * 16);
-      *(u32x4 *)(stage + r * PITCH + cc * 16) = v;
+      pf[k] = u32x4{0u, 0u, 0u, 0u};
+      if (r < nvalid) pf[k] = *(const u32x4 *)(src0 + r * rstride + cc * 16);
     }
-    __syncthreads();
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int ci = lane + 64 * k;
+      const int r = ci / CPR, cc = ci - r * CPR;
+      *(u32x4 *)(stage + r * PITCH + cc * 16) = pf[k];
+    }
+  };
+  if (tile0 < a.total_tiles) {
+    fetch(tile0);
+    stash();
+  }
+  wave_sync();
+
+#pragma unroll 1
+  for (int tile = tile0; tile < a.total_tiles; tile += tstride) {
+    const int bh = tile / a.tiles_per_bh;
+    const int tt = tile - bh * a.tiles_per_bh;
+    const int tbase = tt * VT;
+    const int nvalid = min(VT, a.T - tbase);
 
     float y[DL];
     const unsigned char *myrow = stage + vrow * PITCH + half * DL * ESZ;
@@ -266,7 +407,9 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
         y[4 * c + 2] = __uint_as_float(v.z); y[4 * c + 3] = __uint_as_float(v.w);
       }
     }
-    __syncthreads();
+    wave_sync();
+    const int next = tile + tstride;
+    if (next < a.total_tiles) fetch(next);
 
     if constexpr (ROT) {
       wht_inplace<DL>(y);
@@ -276,34 +419,47 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
         const uint32_t flip = half ? 0x80000000u : 0u;
 #pragma unroll
         for (int i = 0; i < DL; ++i) {
-          const float other = __shfl_xor(y[i], 1, 64);
+          const float other = xor1_f(y[i]);
           y[i] = other + __uint_as_float(__float_as_uint(y[i]) ^ flip);
         }
       }
     }
     float ss = pairwise_sumsq<DL>(y);
     if constexpr (LPV == 2) {
-      const float o = __shfl_xor(ss, 1, 64);
+      const float o = xor1_f(ss);
       ss = half ? (o + ss) : (ss + o);
     }
     const float nu = sqrtf(ss);
     const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
-    uint32_t rec[RECW];
-#pragma unroll
-    for (int w = 0; w < RECW; ++w) rec[w] = 0u;
+    LocalCodes<DL, BITS> lc;
+    lc.clear();
 #pragma unroll
     for (int i = 0; i < DL; ++i) {
       const float u = y[i] * rcp;
-      const uint32_t code = bucketize<BITS>(u, thr);
-      place_code<D, BITS>(rec, half * DL + i, code);
-      if constexpr (QJL) y[i] = u - cent_s[code];
+      const uint32_t code = bucketize_lut<BITS>(u, bt);
+      lc.put(i, code);
+      if constexpr (QJL) y[i] = u - bt.cent[code];
     }
     const bool valid = vrow < nvalid;
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vrow);
+    uint32_t rec[RECW];
     if constexpr (LPV == 2) {
-      // each lane built the codes of its half; merge the two word images
+      // each lane packed its own half; the lower lane joins the two images
+      LocalCodes<DL, BITS> oth;
 #pragma unroll
-      for (int w = 0; w < RECW; ++w) rec[w] |= __shfl_xor(rec[w], 1, 64);
+      for (int k = 0; k < LocalCodes<DL, BITS>::NA + LocalCodes<DL, BITS>::NB; ++k)
+        oth.w[k] = xor1_u(lc.w[k]);
+      join_halves<D, DL, BITS, RECW>(rec, lc, oth);
+    } else {
+#pragma unroll
+      for (int k = 0; k < RECW; ++k) rec[k] = 0u;
+#pragma unroll
+      for (int k = 0; k < LocalCodes<DL, BITS>::NA; ++k) rec[k] = lc.w[k];
+      if constexpr (BITS == 3) {
+#pragma unroll
+        for (int k = 0; k < LocalCodes<DL, BITS>::NB; ++k)
+          rec[LocalCodes<DL, BITS>::NA + k] |= lc.w[LocalCodes<DL, BITS>::NA + k];
+      }
     }
     if (valid && half == 0) {
       store_bytes<RECB>(a.codes + slot * RECB, rec);
@@ -313,7 +469,7 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
     if constexpr (QJL) {
       float rs = pairwise_sumsq<DL>(y);
       if constexpr (LPV == 2) {
-        const float o = __shfl_xor(rs, 1, 64);
+        const float o = xor1_f(rs);
         rs = half ? (o + rs) : (rs + o);
       }
       const float rho = sqrtf(rs);
@@ -334,9 +490,9 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
         }
         *(u32x4 *)(rrow + c * 16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
       }
-      if constexpr (LPV == 2) rt2 = rt2 + __shfl_xor(rt2, 1, 64);
+      if constexpr (LPV == 2) rt2 = rt2 + xor1_f(rt2);
       if (half == 0) rn_s[vrow] = sqrtf(rt2) * (1.0f + 0x1p-12f);
-      __syncthreads();
+      wave_sync();
 
 #pragma unroll 1
       for (int rt = 0; rt < NRT; ++rt) {
@@ -347,12 +503,13 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
           for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
           const int col = ct * 32 + (lane & 31);
           const bool colok = col < D;
+          const int scol = colok ? col : 0;
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks) {
             const int k0 = ks * 16 + 8 * (lane >> 5);
             const u32x4 av = *(const u32x4 *)(stage + (rt * 32 + (lane & 31)) * P2 + k0 * 2);
-            u32x4 bv = {0u, 0u, 0u, 0u};
-            if (colok) bv = *(const u32x4 *)(a.S + (size_t)col * D + k0);
+            u32x4 bv = *(const u32x4 *)(S_s + scol * P2 + k0 * 2);
+            if (!colok) bv = u32x4{0u, 0u, 0u, 0u};
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
                                                           __builtin_bit_cast(bf16x8, bv), acc, 0,
                                                           0, 0);
@@ -372,11 +529,20 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
             const int j = __builtin_ctz(unsure);
             unsure &= unsure - 1u;
             const int row = rt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-            const uint16_t *rr = (const uint16_t *)(stage + row * P2);
-            const uint16_t *sr = a.S + (size_t)col * D;
+            const unsigned char *rr = stage + row * P2;
+            const unsigned char *sr = S_s + col * P2;
             double sum = 0.0;
-            for (int i = 0; i < D; ++i)
-              sum = sum + (double)bf16_to_f32(sr[i]) * (double)bf16_to_f32(rr[i]);
+            for (int c = 0; c < D / 8; ++c) {
+              const u32x4 rv = *(const u32x4 *)(rr + c * 16);
+              const u32x4 sv = *(const u32x4 *)(sr + c * 16);
+              const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+              const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                sum = sum + (double)bf16_lo(sw[k]) * (double)bf16_lo(rw[k]);
+                sum = sum + (double)bf16_hi(sw[k]) * (double)bf16_hi(rw[k]);
+              }
+            }
             bits = (bits & ~(1u << j)) | ((sum >= 0.0 ? 1u : 0u) << j);
           }
 #pragma unroll
@@ -388,7 +554,7 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
           }
         }
       }
-      __syncthreads();
+      wave_sync();
       if (valid && half == 0) {
         uint8_t *dst = a.signs + slot * (D / 8);
         if constexpr (D == 128) {
@@ -401,8 +567,10 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantArgs a) {
           *(uint16_t *)dst = (uint16_t)(sg_s[vrow] & 0xFFFFu);
         }
       }
-      __syncthreads();
     }
+    wave_sync();
+    if (next < a.total_tiles) stash();
+    wave_sync();
   }
 }
 
@@ -484,31 +652,30 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
 
 // ---------------------------------------------------------------------------
 // Decode scan: one block (4 waves) per (token split, KV head, head group,
-// batch row).  A token is spread over L = D/16 lanes, 16 coordinates each, so a
-// wave covers 64/L tokens per step; every lane keeps its 16-coordinate slice of
-// the GT query heads' rotated query, value accumulator and (sketched values)
-// sketch-space accumulator.  Scores: sum of q'_i C_K[code_i] over the slice,
-// reduced across the L lanes; online softmax in base 2 with lazy rescaling
-// (the running max moves only when a score exceeds it by more than 8).
+// batch row).  The split is walked in tiles of TT = 64 tokens.  Every segment
+// of a tile (K codes, V codes, sign bits, fp16 norms; each contiguous in HBM)
+// is copied into LDS with coalesced 16-byte loads spread over the whole block;
+// the next tile's chunks are loaded into registers while the current tile is
+// consumed, so HBM latency overlaps the arithmetic.
+// Inside a tile a token is spread over L = D/E lanes (E = 16 coordinates per
+// lane, 8 when four query heads share the KV head), so a wave covers 64/L
+// tokens per pass; every lane keeps its E-coordinate slice of the GT query
+// heads' rotated query, value accumulator and (sketched values) sketch-space
+// accumulator.  Scores: sum of q'_i C_K[code_i] over the slice, reduced across
+// the L lanes with DPP; online softmax in base 2 with lazy rescaling (the
+// running max moves only when a score exceeds it by more than 20, so weights
+// stay below 2^20 and fp32 sums keep their relative precision).
 // Values: o' += w ||v|| C_V[code]; sketch: a += w ||v|| ||r|| (2 sigma - 1).
 // ---------------------------------------------------------------------------
-// Load the codes of coordinates [g*E, g*E+E) of one record (E = 16 or 8).
 template <int D, int BITS, int E>
-__device__ __forceinline__ void load_codes(const uint8_t *base, size_t rec, int g, uint32_t &w0,
-                                           uint32_t &w1) {
-  constexpr int RB = D * BITS / 8;
-  const uint8_t *r = base + rec * RB;
+__device__ __forceinline__ void lds_codes(const uint8_t *r, int g, uint32_t &w0, uint32_t &w1) {
   if constexpr (E == 16) {
     if constexpr (BITS == 4) {
       const u32x2 v = *(const u32x2 *)(r + g * 8);
       w0 = v.x;
       w1 = v.y;
     } else if constexpr (BITS == 3) {
-      if constexpr (RB % 4 == 0) {
-        w0 = *(const uint32_t *)(r + g * 4);
-      } else {  // 6-byte records (D = 16) are only 2-byte aligned
-        w0 = (uint32_t)*(const uint16_t *)(r + g * 4) | ((uint32_t)*(const uint16_t *)(r + g * 4 + 2) << 16);
-      }
+      w0 = (uint32_t) * (const uint16_t *)(r + g * 4) | ((uint32_t) * (const uint16_t *)(r + g * 4 + 2) << 16);
       w1 = *(const uint16_t *)(r + D / 4 + g * 2);
     } else if constexpr (BITS == 2) {
       w0 = *(const uint32_t *)(r + g * 4);
@@ -542,13 +709,61 @@ __device__ __forceinline__ int slice_code(uint32_t w0, uint32_t w1, int e) {
   return (int)((w0 >> e) & 1u);
 }
 
+// Sum over each aligned group of N lanes (N = 1, 2, 4, 8, 16), result in every
+// lane of the group, with DPP lane permutes (no LDS traffic): quad_perm swaps
+// lanes 1 and 2 apart, row_half_mirror pairs the two quads of 8 lanes,
+// row_mirror pairs the two halves of a 16-lane row.  Partners add the same two
+// operands, so every lane of a group ends with the same bits.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if constexpr (N >= 4)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if constexpr (N >= 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  if constexpr (N >= 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// 2^x with the hardware instruction (results below 2^-126 flush to zero, which
+// only drops softmax weights that are negligible anyway).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Byte layout of one tile of TT tokens in LDS: the record segments back to back.
+template <int D, int KB, bool KQ, int VB, bool VQ, int TT>
+struct TileLayout {
+  static constexpr int KREC = D * KB / 8, VREC = D * VB / 8, SREC = D / 8;
+  static constexpr int KC = 0;
+  static constexpr int VC = KC + TT * KREC;
+  static constexpr int KS = VC + TT * VREC;
+  static constexpr int VS = KS + (KQ ? TT * SREC : 0);
+  static constexpr int KN = VS + (VQ ? TT * SREC : 0);
+  static constexpr int VN = KN + TT * 2;
+  static constexpr int KR = VN + TT * 2;
+  static constexpr int VR = KR + (KQ ? TT * 2 : 0);
+  static constexpr int BYTES = VR + (VQ ? TT * 2 : 0);
+  static constexpr int NCH = BYTES / 16;
+  static_assert(BYTES % 16 == 0 && KC % 16 == 0 && VC % 16 == 0 && KS % 16 == 0 &&
+                VS % 16 == 0 && KN % 16 == 0 && VN % 16 == 0 && KR % 16 == 0 && VR % 16 == 0,
+                "tile segments must be 16-byte multiples");
+};
+
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  constexpr int E = (GT >= 4 && D >= 16) ? 8 : 16;  // coordinates per lane
+  constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // coordinates per lane
   constexpr int L = D / E;
   constexpr int TW = 64 / L;
   constexpr int NS = 2 + 2 * D;
+  constexpr int TT = 64;
+  using TL = TileLayout<D, KB, KQ, VB, VQ, TT>;
+  constexpr int NPT = (TL::NCH + 255) / 256;         // 16-B chunks per thread per tile
+  constexpr int NPASS = TT / TW;                     // token passes per tile
+  constexpr int NPW = (NPASS + 3) / 4;               // passes per wave
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TL::BYTES];
   __shared__ float kc_s[16], vc_s[16];
+  __shared__ float wmax_s[4][GT];
   __shared__ float wst[4][GT][NS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane % L, slot = lane / L;
@@ -560,6 +775,30 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     kc_s[tid] = a.kcent[tid];
     vc_s[tid] = a.vcent[tid];
   }
+
+  // this thread's chunks of a tile: segment base (at token 0), bytes per token,
+  // byte offset inside the tile's segment
+  const size_t unit = (size_t)b * a.Hkv + hkv;
+  const uint8_t *cbase[NPT];
+  int crec[NPT], coff[NPT];
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const int byte = (tid + 256 * k) * 16;
+    const uint8_t *base = nullptr;
+    int rec = 1, start = 0;
+    if (byte < TL::VC) { base = a.kc; rec = TL::KREC; start = TL::KC; }
+    else if (byte < TL::KS) { base = a.vc; rec = TL::VREC; start = TL::VC; }
+    else if (byte < TL::VS) { base = a.ks; rec = TL::SREC; start = TL::KS; }
+    else if (byte < TL::KN) { base = a.vs; rec = TL::SREC; start = TL::VS; }
+    else if (byte < TL::VN) { base = (const uint8_t *)a.kn; rec = 2; start = TL::KN; }
+    else if (byte < TL::KR) { base = (const uint8_t *)a.vn; rec = 2; start = TL::VN; }
+    else if (byte < TL::VR) { base = (const uint8_t *)a.kr; rec = 2; start = TL::KR; }
+    else if (byte < TL::BYTES) { base = (const uint8_t *)a.vr; rec = 2; start = TL::VR; }
+    cbase[k] = base ? base + unit * a.cap * (size_t)rec : nullptr;
+    crec[k] = rec;
+    coff[k] = byte - start;
+  }
+
   float q[GT][E];
   float sqv[GT][E];
 #pragma unroll
@@ -572,7 +811,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       sqv[hh][e] = KQ ? sr[e] : 0.0f;
     }
   }
-  float o[GT][E], av[GT][E], M[GT], Ls[GT];
+  // Block-uniform running max per head; per-lane partial sums (each token slot
+  // adds its own tokens; slots and waves are summed at the end).
+  float M[GT], Ls[GT], o[GT][E], av[GT][E];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     M[hh] = -INFINITY;
@@ -583,116 +824,164 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       av[hh][e] = 0.0f;
     }
   }
-  __syncthreads();
 
   const int t_lo = split * a.tps;
   const int t_hi = min(a.n_ctx, t_lo + a.tps);
-  const size_t base = ((size_t)b * a.Hkv + hkv) * a.cap;
-  for (int t0 = t_lo + wave * TW; t0 < t_hi; t0 += 4 * TW) {
-    const int t = t0 + slot;
-    const bool valid = t < t_hi;
-    const size_t rec = base + (size_t)(valid ? t : t_lo);
-    uint32_t kw0, kw1, vw0, vw1;
-    load_codes<D, KB, E>(a.kc, rec, g, kw0, kw1);
-    load_codes<D, VB, E>(a.vc, rec, g, vw0, vw1);
-    uint32_t ksg = 0u, vsg = 0u;
-    if constexpr (E == 16) {
-      if constexpr (KQ) ksg = *(const uint16_t *)(a.ks + rec * (D / 8) + g * 2);
-      if constexpr (VQ) vsg = *(const uint16_t *)(a.vs + rec * (D / 8) + g * 2);
-    } else {
-      if constexpr (KQ) ksg = a.ks[rec * (D / 8) + g];
-      if constexpr (VQ) vsg = a.vs[rec * (D / 8) + g];
+  const int ntiles = t_hi > t_lo ? (t_hi - t_lo + TT - 1) / TT : 0;
+  u32x4 pf[NPT];
+  auto fetch = [&](int it) {
+    const int tt = t_lo + it * TT;
+    const int nv = min(TT, t_hi - tt);
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      pf[k] = u32x4{0u, 0u, 0u, 0u};
+      if (cbase[k] && coff[k] < nv * crec[k])
+        pf[k] = *(const u32x4 *)(cbase[k] + (size_t)tt * crec[k] + coff[k]);
     }
-    const float nk = f16_bits_to_f32(a.kn[rec]);
-    const float nv = f16_bits_to_f32(a.vn[rec]);
-    const float rk = KQ ? f16_bits_to_f32(a.kr[rec]) : 0.0f;
-    const float rv = VQ ? f16_bits_to_f32(a.vr[rec]) : 0.0f;
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      if (cbase[k]) *(u32x4 *)(tile + (tid + 256 * k) * 16) = pf[k];
+  };
+  if (ntiles > 0) {
+    fetch(0);
+    stash();
+  }
+  __syncthreads();
 
-    float sc[GT], sk[GT];
+  for (int it = 0; it < ntiles; ++it) {
+    const int nvalid = min(TT, t_hi - (t_lo + it * TT));
+    if (it + 1 < ntiles) fetch(it + 1);
+
+    // phase 1: scores of this wave's tokens of the tile (base-2 logits)
+    float sct[NPW][GT];
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      sc[hh] = 0.0f;
-      sk[hh] = 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float ck = kc_s[slice_code<KB>(kw0, kw1, e)];
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) sc[hh] = fmaf(q[hh][e], ck, sc[hh]);
+    for (int pw = 0; pw < NPW; ++pw) {
+      const int pass = wave + 4 * pw;
+      const int tl = pass * TW + slot;
+      const bool valid = pass < NPASS && tl < nvalid;
+      const int tr = valid ? tl : 0;
+      uint32_t kw0, kw1;
+      lds_codes<D, KB, E>(tile + TL::KC + tr * TL::KREC, g, kw0, kw1);
+      uint32_t ksg = 0u;
       if constexpr (KQ) {
-        const float sg = ((ksg >> e) & 1u) ? 1.0f : -1.0f;
-#pragma unroll
-        for (int hh = 0; hh < GT; ++hh) sk[hh] = fmaf(sqv[hh][e], sg, sk[hh]);
+        if constexpr (E == 16) ksg = *(const uint16_t *)(tile + TL::KS + tr * TL::SREC + g * 2);
+        else ksg = tile[TL::KS + tr * TL::SREC + g];
       }
-    }
-#pragma unroll
-    for (int off = 1; off < L; off <<= 1) {
+      const float nk = f16_bits_to_f32(*(const uint16_t *)(tile + TL::KN + tr * 2));
+      const float rk = KQ ? f16_bits_to_f32(*(const uint16_t *)(tile + TL::KR + tr * 2)) : 0.0f;
+      float sc[GT], sk[GT];
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        sc[hh] += __shfl_xor(sc[hh], off, 64);
-        if constexpr (KQ) sk[hh] += __shfl_xor(sk[hh], off, 64);
+        sc[hh] = 0.0f;
+        sk[hh] = 0.0f;
       }
-    }
-    bool need = false;
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      float s = KQ ? nk * fmaf(a.kcoef * rk, sk[hh], sc[hh]) : nk * sc[hh];
-      sc[hh] = valid ? s : -INFINITY;
-      need = need || (sc[hh] > M[hh] + 8.0f);
-    }
-    if (__any(need)) {
+      for (int e = 0; e < E; ++e) {
+        const float ck = kc_s[slice_code<KB>(kw0, kw1, e)];
 #pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        const float mn = (sc[hh] > M[hh] + 8.0f) ? sc[hh] : M[hh];
-        const float al = (mn == M[hh]) ? 1.0f : exp2f(M[hh] - mn);
-        Ls[hh] *= al;
+        for (int hh = 0; hh < GT; ++hh) sc[hh] = fmaf(q[hh][e], ck, sc[hh]);
+        if constexpr (KQ) {
+          const float sg = ((ksg >> e) & 1u) ? 1.0f : -1.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          o[hh][e] *= al;
-          if constexpr (VQ) av[hh][e] *= al;
+          for (int hh = 0; hh < GT; ++hh) sk[hh] = fmaf(sqv[hh][e], sg, sk[hh]);
         }
-        M[hh] = mn;
+      }
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        const float dot = group_sum<L>(sc[hh]);
+        float s;
+        if constexpr (KQ) s = nk * fmaf(a.kcoef * rk, group_sum<L>(sk[hh]), dot);
+        else s = nk * dot;
+        sct[pw][hh] = valid ? s : -INFINITY;
       }
     }
-    float c[GT], cq[GT];
+    // tile max per head: over this wave's passes and slots, then over the 4 waves
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      const float w = valid ? exp2f(sc[hh] - M[hh]) : 0.0f;
-      Ls[hh] += w;
-      c[hh] = w * nv;
-      cq[hh] = c[hh] * rv;
+      float m = sct[0][hh];
+#pragma unroll
+      for (int pw = 1; pw < NPW; ++pw) m = fmaxf(m, sct[pw][hh]);
+#pragma unroll
+      for (int off = L; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      if (lane == 0) wmax_s[wave][hh] = m;
     }
+    __syncthreads();
+    // new running max (uniform over the block) and one rescale of the sums
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float cv = vc_s[slice_code<VB>(vw0, vw1, e)];
+    for (int hh = 0; hh < GT; ++hh) {
+      const float tm = fmaxf(fmaxf(wmax_s[0][hh], wmax_s[1][hh]), fmaxf(wmax_s[2][hh], wmax_s[3][hh]));
+      const float mn = fmaxf(M[hh], tm);
+      const float al = (M[hh] == -INFINITY) ? 0.0f : fast_exp2(M[hh] - mn);
+      M[hh] = mn;
+      Ls[hh] *= al;
 #pragma unroll
-      for (int hh = 0; hh < GT; ++hh) o[hh][e] = fmaf(c[hh], cv, o[hh][e]);
-      if constexpr (VQ) {
-        const float sg = ((vsg >> e) & 1u) ? 1.0f : -1.0f;
-#pragma unroll
-        for (int hh = 0; hh < GT; ++hh) av[hh][e] = fmaf(cq[hh], sg, av[hh][e]);
+      for (int e = 0; e < E; ++e) {
+        o[hh][e] *= al;
+        if constexpr (VQ) av[hh][e] *= al;
       }
     }
+    // phase 2: weights, value and sketch sums
+#pragma unroll
+    for (int pw = 0; pw < NPW; ++pw) {
+      const int pass = wave + 4 * pw;
+      const int tl = pass * TW + slot;
+      const bool valid = pass < NPASS && tl < nvalid;
+      const int tr = valid ? tl : 0;
+      uint32_t vw0, vw1;
+      lds_codes<D, VB, E>(tile + TL::VC + tr * TL::VREC, g, vw0, vw1);
+      uint32_t vsg = 0u;
+      if constexpr (VQ) {
+        if constexpr (E == 16) vsg = *(const uint16_t *)(tile + TL::VS + tr * TL::SREC + g * 2);
+        else vsg = tile[TL::VS + tr * TL::SREC + g];
+      }
+      const float nv = f16_bits_to_f32(*(const uint16_t *)(tile + TL::VN + tr * 2));
+      const float rv = VQ ? f16_bits_to_f32(*(const uint16_t *)(tile + TL::VR + tr * 2)) : 0.0f;
+      float c[GT], cq[GT];
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        const float w = valid ? fast_exp2(sct[pw][hh] - M[hh]) : 0.0f;
+        Ls[hh] += w;
+        c[hh] = w * nv;
+        cq[hh] = c[hh] * rv;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float cv = vc_s[slice_code<VB>(vw0, vw1, e)];
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) o[hh][e] = fmaf(c[hh], cv, o[hh][e]);
+        if constexpr (VQ) {
+          const float sg = ((vsg >> e) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+          for (int hh = 0; hh < GT; ++hh) av[hh][e] = fmaf(cq[hh], sg, av[hh][e]);
+        }
+      }
+    }
+    __syncthreads();
+    if (it + 1 < ntiles) stash();
+    __syncthreads();
   }
 
-  // merge the token slots of this wave (lanes with equal g)
+  // the max is block-uniform, so slots and waves combine by plain sums
 #pragma unroll
   for (int off = L; off < 64; off <<= 1) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      const float M2 = __shfl_xor(M[hh], off, 64);
-      const float L2 = __shfl_xor(Ls[hh], off, 64);
-      const float mn = fmaxf(M[hh], M2);
-      const float a1 = (M[hh] == mn) ? 1.0f : exp2f(M[hh] - mn);
-      const float a2 = (M2 == mn) ? 1.0f : exp2f(M2 - mn);
-      Ls[hh] = Ls[hh] * a1 + L2 * a2;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        o[hh][e] = o[hh][e] * a1 + __shfl_xor(o[hh][e], off, 64) * a2;
-        if constexpr (VQ) av[hh][e] = av[hh][e] * a1 + __shfl_xor(av[hh][e], off, 64) * a2;
+        o[hh][e] += __shfl_xor(o[hh][e], off, 64);
+        if constexpr (VQ) av[hh][e] += __shfl_xor(av[hh][e], off, 64);
       }
-      M[hh] = mn;
     }
+  }
+  // Ls is replicated over the L lanes of a slot: sum one lane per slot
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    float l = (g == 0) ? Ls[hh] : 0.0f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
+    Ls[hh] = l;
   }
   if (slot == 0) {
 #pragma unroll
@@ -709,22 +998,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  // merge the 4 waves and write this split's partial state
   for (int idx = tid; idx < GT * (2 * D + 1); idx += 256) {
     const int hh = idx / (2 * D + 1), k = idx - hh * (2 * D + 1);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, wst[w][hh][0]);
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = wst[w][hh][0];
-      const float al = (mw == -INFINITY) ? 0.0f : exp2f(mw - mx);
-      acc += al * (k == 2 * D ? wst[w][hh][1] : wst[w][hh][2 + k]);
-    }
+    for (int w = 0; w < 4; ++w) acc += (k == 2 * D ? wst[w][hh][1] : wst[w][hh][2 + k]);
     float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
     if (k == 2 * D) {
-      dst[0] = mx;
+      dst[0] = wst[0][hh][0];
       dst[1] = acc;
     } else {
       dst[2 + k] = acc;
@@ -771,11 +1052,13 @@ __global__ __launch_bounds__(D) void combine_kernel(const CombineArgs a) {
 // ---------------------------------------------------------------------------
 template <int D, int BITS, bool ROT, bool QJL>
 hipError_t quantize_go(const QuantArgs &a, bool bf16, hipStream_t s) {
-  const int grid = a.total_tiles < 16384 ? a.total_tiles : 16384;
+  // persistent-style grid: each wave walks tiles with a stride of 4 * grid
+  const int want = (a.total_tiles + 3) / 4;
+  const int grid = want < 2048 ? want : 2048;
   if (bf16)
-    hipLaunchKernelGGL((quantize_kernel<D, BITS, ROT, QJL, true>), dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, BITS, ROT, QJL, true>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((quantize_kernel<D, BITS, ROT, QJL, false>), dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, BITS, ROT, QJL, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

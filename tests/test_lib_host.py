@@ -182,3 +182,27 @@ def test_auto_splits_fill_the_gpu(K):
     assert K.kvq_decode_auto_splits(c, 32, 131136) == 64
     c = _fake_cache(K, d=64, B=1, H=1, cap=256)
     assert K.kvq_decode_auto_splits(c, 1, 256) == 1
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_table_bucketize_precondition(K, d, bits):
+    """At most one positive threshold per 11-bit |u| prefix cell (the encoder's
+    exact table bucketize relies on it); the library re-checks before launch."""
+    cb = K.kvq_codebook_init(d, bits)
+    n = 1 << bits
+    pos = np.array(cb.threshold[n // 2: n - 1], np.float32)
+    cells = pos.view(np.uint32) >> 20
+    assert len(set(cells.tolist())) == len(cells)
+    if len(pos) > 1:
+        assert np.min(pos[1:] / pos[:-1]) > 1.125
+
+
+def test_bad_codebook_rejected(K):
+    lib = K.lib()
+    c = _fake_cache(K, d=64)
+    c.cb_k.threshold[8] = c.cb_k.threshold[9] * 0.99        # two thresholds in one cell
+    assert lib.kvq_quantize_k(C.byref(c), 0x900000, 1, 0, 4, 0, 0, 64, None) == 4
+    c = _fake_cache(K, d=64)
+    c.cb_v.centroid[0] = 0.5                                 # asymmetric table
+    assert lib.kvq_quantize_v(C.byref(c), 0x900000, 1, 0, 4, 0, 0, 64, None) == 4
