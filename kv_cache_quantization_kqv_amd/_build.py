@@ -26,10 +26,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 SOURCES = ["kvq_host.cpp", "kvq_d16.hip", "kvq_d32.hip", "kvq_d64.hip", "kvq_d128.hip"]
 
+# Optional extra compiler flags (tuning macros such as -DKVQ_DECODE_E4=16).
+EXTRA = os.environ.get("KVQ_EXTRA_FLAGS", "").split()
+
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *EXTRA, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,18 +44,19 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, lib_path: str | None = None) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+    out = lib_path or LIB
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -25,6 +25,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -311,12 +313,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
   __shared__ BucketTables bt;
   __shared__ float rn_all[4][VT];
-  __shared__ uint32_t sg_all[4][VT * NCT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned char *stage = stage_all[wave];
   float *rn_s = rn_all[wave];
-  uint32_t *sg_s = sg_all[wave];
   const int vrow = lane / LPV;               // token row of this lane in the tile
   const int half = lane % LPV;               // which coordinate half
   build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
@@ -328,10 +328,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
   }
   __syncthreads();
 
-  float snorm[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) snorm[ct] = 0.0f;
+  // largest sketch row norm (fp32, rounded up), for the sign-certification bound
+  float a_snmax = 0.0f;
   if constexpr (QJL) {
+    float mx = 0.0f;
 #pragma unroll 1
     for (int ct = 0; ct < NCT; ++ct) {
       const int col = ct * 32 + (lane & 31);
@@ -343,8 +343,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
           sq = sq + v * v;
         }
       }
-      snorm[ct] = sqrtf(sq) * (1.0f + 0x1p-12f);
+      mx = fmaxf(mx, sqrtf(sq) * (1.0f + 0x1p-12f));
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    a_snmax = mx;
   }
 
   const int tile0 = blockIdx.x * 4 + wave;
@@ -439,6 +442,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
       const uint32_t code = bucketize_lut<BITS>(u, bt);
       lc.put(i, code);
       if constexpr (QJL) y[i] = u - bt.cent[code];
+      // keep at most 16 coordinates' table lookups in flight (register pressure)
+      if ((i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
     }
     const bool valid = vrow < nvalid;
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vrow);
@@ -474,97 +479,98 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
       }
       const float rho = sqrtf(rs);
       if (valid && half == 0) a.rnorm[slot] = f32_to_f16_bits(rho);
-      float rt2 = 0.0f;
+      // bf16 residual halves into the stage (hardware round-to-nearest-even pack)
       unsigned char *rrow = stage + vrow * P2 + half * DL * 2;
 #pragma unroll
       for (int c = 0; c < DL / 8; ++c) {
         uint32_t wv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t lo = f32_to_bf16_rne(y[8 * c + 2 * k]);
-          const uint32_t hi = f32_to_bf16_rne(y[8 * c + 2 * k + 1]);
-          const float flo = __uint_as_float(lo << 16), fhi = __uint_as_float(hi << 16);
-          rt2 = rt2 + flo * flo;
-          rt2 = rt2 + fhi * fhi;
-          wv[k] = lo | (hi << 16);
+          const f32x2 pr = {y[8 * c + 2 * k], y[8 * c + 2 * k + 1]};
+          wv[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
         }
         *(u32x4 *)(rrow + c * 16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
       }
-      if constexpr (LPV == 2) rt2 = rt2 + xor1_f(rt2);
-      if (half == 0) rn_s[vrow] = sqrtf(rt2) * (1.0f + 0x1p-12f);
+      // ||r~|| <= (1 + 2^-8) ||r|| (bf16 rounding is at most 2^-8 relative per
+      // element); 2^-7 also covers the fp32 error of rho.  Stored pre-scaled by
+      // the accumulation-error factor D * 2^-22.
+      if (half == 0) rn_s[vrow] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
       wave_sync();
 
+      // z^T = S r~^T per 32-token block: A = S rows (sketch rows k), B = r~ rows
+      // (tokens t).  Output register j of lane l is z[k][t] with
+      // k = 32 ct + 8 (j/4) + 4 (l/32) + (j%4) and t = l%32, so a lane holds 16
+      // of its token's sign bits per 32-row block and lane l^32 the other 16.
 #pragma unroll 1
       for (int rt = 0; rt < NRT; ++rt) {
+        const int t = rt * 32 + (lane & 31);                  // token row in the tile
+        const float rbt = rn_s[t];
+        uint32_t sgw[NCT];
 #pragma unroll 1
         for (int ct = 0; ct < NCT; ++ct) {
           f32x16 acc;
 #pragma unroll
           for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-          const int col = ct * 32 + (lane & 31);
-          const bool colok = col < D;
-          const int scol = colok ? col : 0;
+          const int krow = ct * 32 + (lane & 31);             // A row of this lane
+          const bool kok = krow < D;
+          const int ks_row = kok ? krow : 0;
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks) {
             const int k0 = ks * 16 + 8 * (lane >> 5);
-            const u32x4 av = *(const u32x4 *)(stage + (rt * 32 + (lane & 31)) * P2 + k0 * 2);
-            u32x4 bv = *(const u32x4 *)(S_s + scol * P2 + k0 * 2);
-            if (!colok) bv = u32x4{0u, 0u, 0u, 0u};
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0,
+            u32x4 sv = *(const u32x4 *)(S_s + ks_row * P2 + k0 * 2);
+            if (!kok) sv = u32x4{0u, 0u, 0u, 0u};
+            const u32x4 rv = *(const u32x4 *)(stage + t * P2 + k0 * 2);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sv),
+                                                          __builtin_bit_cast(bf16x8, rv), acc, 0,
                                                           0, 0);
           }
-          // sign bits from z where certified; rows left uncertain are redone in fp64
+          // certified signs; uncertain entries are recomputed in fp64, ascending
+          const float bound = fmaf(a_snmax, rbt, 0x1p-100f);
           uint32_t bits = 0u, unsure = 0u;
-          const float sn = snorm[ct];
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int row = rt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);   // bit = sketch row % 32
             const float z = acc[j];
-            const float bound = (float)D * 0x1p-22f * sn * rn_s[row] + 0x1p-100f;
-            bits |= (z > 0.0f ? 1u : 0u) << j;
-            unsure |= ((colok && !(fabsf(z) > bound)) ? 1u : 0u) << j;
+            bits |= (z > 0.0f ? 1u : 0u) << bp;
+            unsure |= (!(fabsf(z) > bound) ? 1u : 0u) << bp;
           }
+          if constexpr (D < 32) unsure &= (1u << D) - 1u;                 // rows >= D do not exist
+          if (t >= nvalid) unsure = 0u;                                    // padding rows of the tile
           while (unsure) {
-            const int j = __builtin_ctz(unsure);
+            const int bp = __builtin_ctz(unsure);
             unsure &= unsure - 1u;
-            const int row = rt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-            const unsigned char *rr = stage + row * P2;
-            const unsigned char *sr = S_s + col * P2;
+            const int k = ct * 32 + bp;
+            const unsigned char *rr = stage + t * P2;
+            const unsigned char *sr = S_s + k * P2;
             double sum = 0.0;
             for (int c = 0; c < D / 8; ++c) {
               const u32x4 rv = *(const u32x4 *)(rr + c * 16);
-              const u32x4 sv = *(const u32x4 *)(sr + c * 16);
+              const u32x4 sw4 = *(const u32x4 *)(sr + c * 16);
               const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
-              const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+              const uint32_t sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                sum = sum + (double)bf16_lo(sw[k]) * (double)bf16_lo(rw[k]);
-                sum = sum + (double)bf16_hi(sw[k]) * (double)bf16_hi(rw[k]);
+              for (int k2 = 0; k2 < 4; ++k2) {
+                sum = sum + (double)bf16_lo(sw[k2]) * (double)bf16_lo(rw[k2]);
+                sum = sum + (double)bf16_hi(sw[k2]) * (double)bf16_hi(rw[k2]);
               }
             }
-            bits = (bits & ~(1u << j)) | ((sum >= 0.0 ? 1u : 0u) << j);
+            bits = (bits & ~(1u << bp)) | ((sum >= 0.0 ? 1u : 0u) << bp);
           }
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int row = rt * 32 + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
-            const unsigned long long m = __ballot((bits >> j) & 1u);
-            if (lane == 0) sg_s[row * NCT + ct] = (uint32_t)m;
-            if (lane == 32) sg_s[row * NCT + ct] = (uint32_t)(m >> 32);
-          }
+          sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
         }
-      }
-      wave_sync();
-      if (valid && half == 0) {
-        uint8_t *dst = a.signs + slot * (D / 8);
-        if constexpr (D == 128) {
-          *(u32x4 *)dst = u32x4{sg_s[vrow * 4], sg_s[vrow * 4 + 1], sg_s[vrow * 4 + 2], sg_s[vrow * 4 + 3]};
-        } else if constexpr (D == 64) {
-          *(u32x2 *)dst = u32x2{sg_s[vrow * 2], sg_s[vrow * 2 + 1]};
-        } else if constexpr (D == 32) {
-          *(uint32_t *)dst = sg_s[vrow];
-        } else {
-          *(uint16_t *)dst = (uint16_t)(sg_s[vrow] & 0xFFFFu);
+        const bool tvalid = t < nvalid && lane < 32;
+        if (tvalid) {
+          const size_t tslot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + t);
+          uint8_t *dst = a.signs + tslot * (D / 8);
+          if constexpr (D == 128) {
+            *(u32x4 *)dst = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
+          } else if constexpr (D == 64) {
+            *(u32x2 *)dst = u32x2{sgw[0], sgw[1]};
+          } else if constexpr (D == 32) {
+            *(uint32_t *)dst = sgw[0];
+          } else {
+            *(uint16_t *)dst = (uint16_t)(sgw[0] & 0xFFFFu);
+          }
         }
       }
     }
