@@ -43,7 +43,10 @@ def main():
     ap.add_argument("--bits", type=int, default=None, help="override n bits/coordinate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=4, help="(b, KV head) units in the CPU sample")
-    ap.add_argument("--roofline-json", default=None, help="optional rocprof-derived traffic file")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gqa_decode_kqv4.md"),
+                    help="profiles/*.md summary holding measured HBM bytes per launch (json block)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
@@ -80,6 +83,13 @@ def main():
     ws = torch.zeros(cache.workspace_bytes(Hq, N), dtype=torch.uint8, device=dev)
     out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb * 1024 * 1024 // 4
+        a_src = torch.ones(n, dtype=torch.float32, device=dev)
+        a_dst = torch.empty_like(a_src)
+        a_dst.copy_(a_src)
+        torch.cuda.synchronize(dev)
+        del a_src, a_dst
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -133,9 +143,8 @@ def main():
             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
             "bytes_per_launch": dec_bytes, "per_record_bytes": rec}
-    if args.roofline_json and os.path.exists(args.roofline_json):
-        with open(args.roofline_json) as f:
-            roof["traffic"] = json.load(f).get("decode_traffic_bytes")
+    if args.traffic and os.path.exists(args.traffic):
+        roof["traffic"] = read_traffic(args.traffic, scheme, n_bits, w.name)
 
     result = {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s",
@@ -164,6 +173,32 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, scheme, n_bits, K, V, q, S, args.cpu_units, rec)
     print(json.dumps(result), flush=True)
+
+
+def kernel_source_digest():
+    """sha256 over the device and host sources of libkvq (counter summaries are
+    only valid for the code they were taken on)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_quantization_kqv_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def read_traffic(path, scheme, n_bits, workload):
+    """Measured HBM bytes per decode launch from a profile summary's json block;
+    None unless it was taken on this workload and on the current sources."""
+    text = open(path).read()
+    if "```json" not in text:
+        return None
+    blk = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if blk.get("workload") != workload or blk.get("scheme") != f"{scheme}{n_bits}":
+        return None
+    if blk.get("source_sha256") != kernel_source_digest():
+        return None
+    return blk.get("decode_bytes_per_launch")
 
 
 def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec):
