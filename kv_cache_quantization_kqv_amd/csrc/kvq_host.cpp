@@ -214,6 +214,12 @@ int heads_per_block(int G) { return G >= 4 ? 4 : G; }
 
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || (G > 4 && G % 4 == 0); }
 
+// Fewest splits that keep every split's logits in LDS.
+long long min_splits(const kvq_cache *c, int q_heads, int n_ctx) {
+  const int tmax = kvq::scan_tokens_max(heads_per_block(q_heads / c->kv_heads));
+  return ((long long)n_ctx + tmax - 1) / tmax;
+}
+
 int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   int G = q_heads / c->kv_heads;
   int HG = G / heads_per_block(G);
@@ -221,8 +227,9 @@ int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   long long want = (2048 + units - 1) / units;
   long long maxs = (n_ctx + 255) / 256;
   long long s = want < maxs ? want : maxs;
+  const long long need = min_splits(c, q_heads, n_ctx);
+  if (s < need) s = need;
   if (s < 1) s = 1;
-  if (s > 1024) s = 1024;
   return (int)s;
 }
 
@@ -383,8 +390,9 @@ kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int 
   if (!supported_group(q_heads / c->kv_heads)) return KVQ_ERR_HEADS;
   if (n_ctx < 1) return KVQ_ERR_RANGE;
   if (n_ctx > c->capacity) return KVQ_ERR_CAPACITY;
-  if (splits < 0 || splits > 4096) return KVQ_ERR_RANGE;
+  if (splits < 0 || splits > 8192) return KVQ_ERR_RANGE;
   if (splits == 0) splits = auto_splits(c, q_heads, n_ctx);
+  if (splits < min_splits(c, q_heads, n_ctx)) return KVQ_ERR_RANGE;
   size_t rows = (size_t)c->batch * q_heads;
   *bytes = sizeof(float) * (rows * c->d * 2 + rows * (size_t)splits * (2 + 2 * (size_t)c->d));
   return KVQ_OK;
@@ -409,13 +417,14 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   const int gt = heads_per_block(G);
   const int rows = c->batch * q_heads;
   float *ws = (float *)workspace;
-  float *qs = ws;
-  float *sq = ws + (size_t)rows * d;
+  float *qt = ws;
+  float *sqt = ws + (size_t)rows * d;
   float *part = ws + (size_t)rows * d * 2;
   hipStream_t hs = (hipStream_t)stream;
 
   kvq::PrepArgs p;
-  p.q = q; p.qs = qs; p.sq = sq; p.S = c->S; p.rows = rows;
+  p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = rows;
+  p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
   p.qscale = c->rotate ? (float)(1.4426950408889634 / d) : (float)(1.4426950408889634 / std::sqrt((double)d));
   (void)kLog2e;
   hipError_t e = by_dim(d, [&](auto D) {
@@ -428,7 +437,7 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   std::memset(&a, 0, sizeof(a));
   a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
   a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
-  a.qs = qs; a.sq = sq; a.part = part;
+  a.qt = qt; a.sqt = sqt; a.part = part;
   for (int i = 0; i < 16; ++i) {
     a.kcent[i] = c->cb_k.centroid[i];
     a.vcent[i] = c->cb_v.centroid[i];

@@ -6,7 +6,16 @@
 
 #include "../../include/kvq.h"
 
+// Logits and weights of one decode split stay in LDS: 2 floats per (token,
+// query head of the block), so a split holds at most KVQ_SCAN_WBUF_FLOATS/(2 GT)
+// tokens.
+#ifndef KVQ_SCAN_WBUF_FLOATS
+#define KVQ_SCAN_WBUF_FLOATS 8192
+#endif
+
 namespace kvq {
+
+inline int scan_tokens_max(int gt) { return KVQ_SCAN_WBUF_FLOATS / (2 * gt); }
 
 // Quantize-on-write launch description (one side of the cache).
 struct QuantArgs {
@@ -35,17 +44,18 @@ struct DequantArgs {
 
 struct PrepArgs {
   const void *q;             // [B][Hq][d]
-  float *qs;                 // rotated, scaled query [B][Hq][d]
-  float *sq;                 // S qs (K sketch only) [B][Hq][d]
+  float *qt;                 // rotated, scaled query [B][Hkv][HG][d][GT]
+  float *sqt;                // S q' (K sketch only), same layout
   const uint16_t *S;
   int rows;                  // B * Hq
+  int Hq, Hkv, G, GT, HG;    // G = Hq / Hkv query heads per KV head, GT per block, HG = G / GT
   float qscale;              // log2(e)/d (rotated) or log2(e)/sqrt(d)
 };
 
 struct DecodeArgs {
   const uint8_t *kc, *ks, *vc, *vs;
   const uint16_t *kn, *kr, *vn, *vr;
-  const float *qs, *sq;
+  const float *qt, *sqt;      // prepared queries, layout of PrepArgs::qt
   float *part;               // [B][Hq][splits][2 + 2d]
   float kcent[16], vcent[16];
   float kcoef;               // sqrt(pi/2)/m (K sketch)

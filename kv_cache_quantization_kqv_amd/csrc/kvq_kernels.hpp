@@ -633,9 +633,12 @@ __global__ __launch_bounds__(D) void dequant_kernel(const DequantArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Query preparation: qs = H q * log2(e)/d (rotated schemes) or q * log2(e)/sqrt(d),
-// and for sketched keys sq = S qs.  Rotating q once replaces rotating every key
-// (H is symmetric and H H = d I); log2(e) lets the scan use exp2.
+// Query preparation, one block per query row: q' = H q * log2(e)/d (rotated
+// schemes) or q * log2(e)/sqrt(d), and for sketched keys S q'.  Rotating q once
+// replaces rotating every key (H is symmetric and H H = d I); log2(e) lets the
+// scan use exp2.  Output layout [b][h_kv][head group][coordinate][GT] puts the
+// GT heads of one coordinate side by side, so the scan reads them with scalar
+// loads.
 // ---------------------------------------------------------------------------
 template <int D, bool ROT, bool KQ, bool BF16>
 __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
@@ -645,34 +648,79 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
                  : ((const float *)a.q)[(size_t)row * D + i];
   if constexpr (ROT) x = wht_block<D>(t_s, x);
   x = x * a.qscale;
-  a.qs[(size_t)row * D + i] = x;
+  const int b = row / a.Hq, hq = row - b * a.Hq;
+  const int hkv = hq / a.G, within = hq - hkv * a.G;
+  const int hg = within / a.GT, hh = within - hg * a.GT;
+  const size_t dst = ((((size_t)b * a.Hkv + hkv) * a.HG + hg) * D + i) * a.GT + hh;
+  a.qt[dst] = x;
   if constexpr (KQ) {
     __syncthreads();
     t_s[i] = x;
     __syncthreads();
     float acc = 0.0f;
     for (int k = 0; k < D; ++k) acc = acc + bf16_to_f32(a.S[(size_t)i * D + k]) * t_s[k];
-    a.sq[(size_t)row * D + i] = acc;
+    a.sqt[dst] = acc;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Decode scan: one block (4 waves) per (token split, KV head, head group,
-// batch row).  The split is walked in tiles of TT = 64 tokens.  Every segment
-// of a tile (K codes, V codes, sign bits, fp16 norms; each contiguous in HBM)
-// is copied into LDS with coalesced 16-byte loads spread over the whole block;
-// the next tile's chunks are loaded into registers while the current tile is
-// consumed, so HBM latency overlaps the arithmetic.
-// Inside a tile a token is spread over L = D/E lanes (E = 16 coordinates per
-// lane, 8 when four query heads share the KV head), so a wave covers 64/L
-// tokens per pass; every lane keeps its E-coordinate slice of the GT query
-// heads' rotated query, value accumulator and (sketched values) sketch-space
-// accumulator.  Scores: sum of q'_i C_K[code_i] over the slice, reduced across
-// the L lanes with DPP; online softmax in base 2 with lazy rescaling (the
-// running max moves only when a score exceeds it by more than 20, so weights
-// stay below 2^20 and fp32 sums keep their relative precision).
-// Values: o' += w ||v|| C_V[code]; sketch: a += w ||v|| ||r|| (2 sigma - 1).
+// Decode scan.  One block (4 waves) per (token split, KV head, group of GT
+// query heads, batch row); every record of the split is read once and serves
+// the GT heads.  Three phases:
+//   A  keys, one token per lane: base-2 logit
+//        s = n_k * (sum_i q'_i C_K[code_i]  [+ sqrt(pi/2)/m rho_k <S q', 2 sigma - 1>])
+//      with q' (and S q') taken from scalar registers; logits stay in LDS.
+//   B  the split's exact max M per head, then once per (token, head) the
+//      weight w = 2^(s - M), the sum L, and c = w n_v, cq = c rho_v in LDS.
+//   C  values: tiles of 64 tokens staged in LDS with coalesced 16-byte loads
+//      (next tile prefetched into registers); a token is spread over D/E
+//      lanes, each with E coordinates: o' += c C_V[code] (codes looked up two
+//      at a time from a pair table) and a += cq (2 sigma - 1).
+// The block writes (M, L, o'[D], a[D]) per head; the merge kernel combines the
+// splits.
 // ---------------------------------------------------------------------------
+template <int BYTES>
+__device__ __forceinline__ void load_rec(const uint8_t *p, uint32_t *w) {
+  if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+    for (int k = 0; k < BYTES / 16; ++k) {
+      const u32x4 v = *(const u32x4 *)(p + 16 * k);
+      w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
+  } else if constexpr (BYTES % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < BYTES / 8; ++k) {
+      const u32x2 v = *(const u32x2 *)(p + 8 * k);
+      w[2 * k] = v.x; w[2 * k + 1] = v.y;
+    }
+  } else if constexpr (BYTES % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < BYTES / 4; ++k) w[k] = *(const uint32_t *)(p + 4 * k);
+  } else if constexpr (BYTES == 6) {
+    const uint16_t *h = (const uint16_t *)p;
+    w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    w[1] = h[2];
+  } else {
+    static_assert(BYTES == 2, "record size");
+    w[0] = *(const uint16_t *)p;
+  }
+}
+
+// Code i of a whole record held as little-endian words (layout as place_code).
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t rec_code(const uint32_t *w, int i) {
+  if constexpr (BITS == 3) {
+    const uint32_t lo = (w[(2 * i) >> 5] >> ((2 * i) & 31)) & 3u;
+    const uint32_t hi = (w[D / 16 + (i >> 5)] >> (i & 31)) & 1u;
+    return lo | (hi << 2);
+  } else {
+    return (w[(i * BITS) >> 5] >> ((i * BITS) & 31)) & ((1u << BITS) - 1u);
+  }
+}
+
+// Codes of one lane's E-coordinate slice g of a record in LDS: w0 holds the
+// low (or only) bits, w1 the 1-bit plane of 3-bit codes or the upper half of
+// 4-bit codes when E = 16.
 template <int D, int BITS, int E>
 __device__ __forceinline__ void lds_codes(const uint8_t *r, int g, uint32_t &w0, uint32_t &w1) {
   if constexpr (E == 16) {
@@ -707,12 +755,27 @@ __device__ __forceinline__ void lds_codes(const uint8_t *r, int g, uint32_t &w0,
   }
 }
 
+// Codes of coordinate pair p of a lane's E-coordinate slice (words from
+// lds_codes), as an index into the pair table.  Widths 1, 2, 4: the two codes'
+// bits are adjacent (index = code_a | code_b << BITS).  Width 3: the pair's
+// nibble of the 2-bit plane, then its two bits of the 1-bit plane.
 template <int BITS>
-__device__ __forceinline__ int slice_code(uint32_t w0, uint32_t w1, int e) {
-  if constexpr (BITS == 4) return (int)(((e < 8 ? w0 : w1) >> (4 * (e & 7))) & 15u);
-  if constexpr (BITS == 3) return (int)(((w0 >> (2 * e)) & 3u) | (((w1 >> e) & 1u) << 2));
-  if constexpr (BITS == 2) return (int)((w0 >> (2 * e)) & 3u);
-  return (int)((w0 >> e) & 1u);
+__device__ __forceinline__ uint32_t pair_index(uint32_t w0, uint32_t w1, int p) {
+  if constexpr (BITS == 4) return ((p < 4 ? w0 : w1) >> (8 * (p & 3))) & 255u;
+  if constexpr (BITS == 3) return ((w0 >> (4 * p)) & 15u) | (((w1 >> (2 * p)) & 3u) << 4);
+  if constexpr (BITS == 2) return (w0 >> (4 * p)) & 15u;
+  return (w0 >> (2 * p)) & 3u;
+}
+// The two codes a pair-table index stands for.
+template <int BITS>
+__device__ __forceinline__ void pair_codes(int idx, int &ca, int &cb) {
+  if constexpr (BITS == 3) {
+    ca = (idx & 3) | (((idx >> 4) & 1) << 2);
+    cb = ((idx >> 2) & 3) | (((idx >> 5) & 1) << 2);
+  } else {
+    ca = idx & ((1 << BITS) - 1);
+    cb = idx >> BITS;
+  }
 }
 
 // Sum over each aligned group of N lanes (N = 1, 2, 4, 8, 16), result in every
@@ -737,54 +800,213 @@ __device__ __forceinline__ float group_sum(float v) {
 // only drops softmax weights that are negligible anyway).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Byte layout of one tile of TT tokens in LDS: the record segments back to back.
-template <int D, int KB, bool KQ, int VB, bool VQ, int TT>
-struct TileLayout {
-  static constexpr int KREC = D * KB / 8, VREC = D * VB / 8, SREC = D / 8;
-  static constexpr int KC = 0;
-  static constexpr int VC = KC + TT * KREC;
-  static constexpr int KS = VC + TT * VREC;
-  static constexpr int VS = KS + (KQ ? TT * SREC : 0);
-  static constexpr int KN = VS + (VQ ? TT * SREC : 0);
-  static constexpr int VN = KN + TT * 2;
-  static constexpr int KR = VN + TT * 2;
-  static constexpr int VR = KR + (KQ ? TT * 2 : 0);
-  static constexpr int BYTES = VR + (VQ ? TT * 2 : 0);
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// A uniform zero the compiler cannot see through: added to the scalar-load
+// offsets inside the token loop, it keeps the query loads in the loop (one
+// chunk of SGPRs live at a time) instead of hoisting all of them.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
+typedef const __attribute__((address_space(4))) float cfloat;
+
+// Byte layout of one value tile of TT tokens in LDS: value codes, then value
+// sign bits (sketched values).
+template <int D, int VB, bool VQ, int TT>
+struct VTile {
+  static constexpr int VREC = D * VB / 8, SREC = D / 8;
+  static constexpr int VC = 0;
+  static constexpr int VS = VC + TT * VREC;
+  static constexpr int BYTES = VS + (VQ ? TT * SREC : 0);
   static constexpr int NCH = BYTES / 16;
-  static_assert(BYTES % 16 == 0 && KC % 16 == 0 && VC % 16 == 0 && KS % 16 == 0 &&
-                VS % 16 == 0 && KN % 16 == 0 && VN % 16 == 0 && KR % 16 == 0 && VR % 16 == 0,
-                "tile segments must be 16-byte multiples");
+  static_assert(BYTES % 16 == 0 && VS % 16 == 0, "tile segments must be 16-byte multiples");
 };
 
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // coordinates per lane
-  constexpr int L = D / E;
-  constexpr int TW = 64 / L;
-  constexpr int NS = 2 + 2 * D;
+  constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // value coordinates per lane
+  constexpr int L = D / E;                           // lanes per token in phase C
+  constexpr int TW = 64 / L;                         // tokens per wave pass
   constexpr int TT = 64;
-  using TL = TileLayout<D, KB, KQ, VB, VQ, TT>;
+  constexpr int NS = 2 + 2 * D;
+  constexpr int WS = 2 * GT;                         // LDS floats per token
+  constexpr int TPS_MAX = KVQ_SCAN_WBUF_FLOATS / WS;
+  constexpr int KBYTES = D * KB / 8, KW = (KBYTES + 3) / 4;
+  constexpr int SBYTES = D / 8, SW = (SBYTES + 3) / 4;
+  constexpr int NPAIR = 1 << (2 * VB);
+  using TL = VTile<D, VB, VQ, TT>;
   constexpr int NPT = (TL::NCH + 255) / 256;         // 16-B chunks per thread per tile
-  constexpr int NPASS = TT / TW;                     // token passes per tile
-  constexpr int NPW = (NPASS + 3) / 4;               // passes per wave
+  constexpr int NPASS = TT / TW;
+  constexpr int NPW = (NPASS + 3) / 4;
+  constexpr int EPI = 4 * GT * NS;                   // epilogue floats (reuses wbuf)
+  static_assert(TPS_MAX % TT == 0, "split budget must be whole tiles");
+  static_assert(EPI <= KVQ_SCAN_WBUF_FLOATS, "epilogue staging must fit the logit buffer");
+
+  __shared__ __attribute__((aligned(16))) float wbuf[KVQ_SCAN_WBUF_FLOATS];
   __shared__ __attribute__((aligned(16))) uint8_t tile[TL::BYTES];
-  __shared__ float kc_s[16], vc_s[16];
-  __shared__ float wmax_s[4][GT];
-  __shared__ float wst[4][GT][NS];
+  __shared__ float kc_s[16];
+  __shared__ __attribute__((aligned(8))) f32x2 vp_s[NPAIR];
+  __shared__ float red_s[4][GT];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane % L, slot = lane / L;
   const int split = blockIdx.x;
   const int hkv = blockIdx.y / a.HG, hg = blockIdx.y - (blockIdx.y / a.HG) * a.HG;
   const int b = blockIdx.z;
   const int hq0 = hkv * a.Gtot + hg * GT;
-  if (tid < 16) {
-    kc_s[tid] = a.kcent[tid];
-    vc_s[tid] = a.vcent[tid];
+  const size_t unit = (size_t)b * a.Hkv + hkv;
+  const size_t unitg = unit * a.HG + hg;
+  if (tid < 16) kc_s[tid] = a.kcent[tid];
+  for (int p = tid; p < NPAIR; p += 256) {
+    int ca, cb;
+    pair_codes<VB>(p, ca, cb);
+    vp_s[p] = f32x2{a.vcent[ca], a.vcent[cb]};
   }
 
-  // this thread's chunks of a tile: segment base (at token 0), bytes per token,
-  // byte offset inside the tile's segment
-  const size_t unit = (size_t)b * a.Hkv + hkv;
+  const int t_lo = split * a.tps;
+  const int t_hi = min(a.n_ctx, t_lo + a.tps);
+  const int nloc = t_hi > t_lo ? t_hi - t_lo : 0;
+  const size_t rec0 = unit * a.cap + t_lo;           // first record of the split
+  __syncthreads();
+
+  // ---- phase A: logits, one token per lane -------------------------------
+  cfloat *qc = (cfloat *)(a.qt + unitg * D * GT);
+  cfloat *sc = (cfloat *)(a.sqt + unitg * D * GT);
+  const uint8_t *kc_p = a.kc + rec0 * KBYTES;
+  const uint8_t *ks_p = KQ ? a.ks + rec0 * SBYTES : nullptr;
+  const uint16_t *kn_p = a.kn + rec0;
+  const uint16_t *kr_p = KQ ? a.kr + rec0 : nullptr;
+  float mx[GT];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) mx[hh] = -INFINITY;
+
+  uint32_t kw[KW], ksw[SW];
+  float nk = 0.0f, rk = 0.0f;
+  auto kload = [&](int tl, uint32_t *w, uint32_t *sw, float &n, float &r) {
+    if (tl < nloc) {
+      load_rec<KBYTES>(kc_p + (size_t)tl * KBYTES, w);
+      n = f16_bits_to_f32(kn_p[tl]);
+      if constexpr (KQ) {
+        load_rec<SBYTES>(ks_p + (size_t)tl * SBYTES, sw);
+        r = f16_bits_to_f32(kr_p[tl]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KW; ++k) w[k] = 0u;
+#pragma unroll
+      for (int k = 0; k < SW; ++k) sw[k] = 0u;
+      n = 0.0f;
+      r = 0.0f;
+    }
+  };
+  kload(wave * 64 + lane, kw, ksw, nk, rk);
+  for (int base = wave * 64; base < nloc; base += 256) {
+    uint32_t nw[KW], nsw[SW];
+    float nnk, nrk;
+    kload(base + 256 + lane, nw, nsw, nnk, nrk);    // prefetch the next round
+    const int z = opaque_zero();
+    float acc[GT], sk[GT];
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+      acc[hh] = 0.0f;
+      sk[hh] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const float ck = kc_s[rec_code<D, KB>(kw, i)];
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) acc[hh] = fmaf(qc[z + i * GT + hh], ck, acc[hh]);
+      if constexpr (KQ) {
+        const float sg = ((ksw[i >> 5] >> (i & 31)) & 1u) ? 1.0f : -1.0f;
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) sk[hh] = fmaf(sc[z + i * GT + hh], sg, sk[hh]);
+      }
+    }
+    const int tl = base + lane;
+    if (tl < nloc) {
+      float s[GT];
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        if constexpr (KQ) s[hh] = nk * fmaf(a.kcoef * rk, sk[hh], acc[hh]);
+        else s[hh] = nk * acc[hh];
+        mx[hh] = fmaxf(mx[hh], s[hh]);
+      }
+      float *dst = wbuf + tl * WS;
+      if constexpr (GT == 4) *(float4 *)dst = float4{s[0], s[1], s[2], s[3]};
+      else if constexpr (GT == 2) *(f32x2 *)dst = f32x2{s[0], s[1]};
+      else dst[0] = s[0];
+    }
+#pragma unroll
+    for (int k = 0; k < KW; ++k) kw[k] = nw[k];
+#pragma unroll
+    for (int k = 0; k < SW; ++k) ksw[k] = nsw[k];
+    nk = nnk;
+    rk = nrk;
+  }
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    const float m = wave_max(mx[hh]);
+    if (lane == 0) red_s[wave][hh] = m;
+  }
+  __syncthreads();
+
+  // ---- phase B: exact split max, weights once per (token, head) ----------
+  float M[GT], Lp[GT];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh) {
+    M[hh] = fmaxf(fmaxf(red_s[0][hh], red_s[1][hh]), fmaxf(red_s[2][hh], red_s[3][hh]));
+    Lp[hh] = 0.0f;
+  }
+  const uint16_t *vn_p = a.vn + rec0;
+  const uint16_t *vr_p = VQ ? a.vr + rec0 : nullptr;
+  const int nround = (nloc + TT - 1) / TT * TT;
+  for (int tl = tid; tl < nround; tl += 256) {
+    float c[GT], cq[GT];
+    if (tl < nloc) {
+      const float nv = f16_bits_to_f32(vn_p[tl]);
+      const float rv = VQ ? f16_bits_to_f32(vr_p[tl]) : 0.0f;
+      const float *src = wbuf + tl * WS;
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        const float w = fast_exp2(src[hh] - M[hh]);
+        Lp[hh] += w;
+        c[hh] = w * nv;
+        cq[hh] = c[hh] * rv;
+      }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        c[hh] = 0.0f;
+        cq[hh] = 0.0f;
+      }
+    }
+    float *dst = wbuf + tl * WS;
+    if constexpr (GT == 4) {
+      *(float4 *)dst = float4{c[0], c[1], c[2], c[3]};
+      *(float4 *)(dst + 4) = float4{cq[0], cq[1], cq[2], cq[3]};
+    } else if constexpr (GT == 2) {
+      *(float4 *)dst = float4{c[0], c[1], cq[0], cq[1]};
+    } else {
+      *(f32x2 *)dst = f32x2{c[0], cq[0]};
+    }
+  }
+
+  // ---- phase C: values ---------------------------------------------------
+  const int lg = lane % L, slot = lane / L;
+  float o[GT][E], av[GT][E];
+#pragma unroll
+  for (int hh = 0; hh < GT; ++hh)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      o[hh][e] = 0.0f;
+      av[hh][e] = 0.0f;
+    }
   const uint8_t *cbase[NPT];
   int crec[NPT], coff[NPT];
 #pragma unroll
@@ -792,57 +1014,21 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     const int byte = (tid + 256 * k) * 16;
     const uint8_t *base = nullptr;
     int rec = 1, start = 0;
-    if (byte < TL::VC) { base = a.kc; rec = TL::KREC; start = TL::KC; }
-    else if (byte < TL::KS) { base = a.vc; rec = TL::VREC; start = TL::VC; }
-    else if (byte < TL::VS) { base = a.ks; rec = TL::SREC; start = TL::KS; }
-    else if (byte < TL::KN) { base = a.vs; rec = TL::SREC; start = TL::VS; }
-    else if (byte < TL::VN) { base = (const uint8_t *)a.kn; rec = 2; start = TL::KN; }
-    else if (byte < TL::KR) { base = (const uint8_t *)a.vn; rec = 2; start = TL::VN; }
-    else if (byte < TL::VR) { base = (const uint8_t *)a.kr; rec = 2; start = TL::KR; }
-    else if (byte < TL::BYTES) { base = (const uint8_t *)a.vr; rec = 2; start = TL::VR; }
-    cbase[k] = base ? base + unit * a.cap * (size_t)rec : nullptr;
+    if (byte < TL::VS) { base = a.vc; rec = TL::VREC; start = TL::VC; }
+    else if (byte < TL::BYTES) { base = a.vs; rec = TL::SREC; start = TL::VS; }
+    cbase[k] = base ? base + rec0 * rec : nullptr;
     crec[k] = rec;
     coff[k] = byte - start;
   }
-
-  float q[GT][E];
-  float sqv[GT][E];
-#pragma unroll
-  for (int hh = 0; hh < GT; ++hh) {
-    const float *qr = a.qs + ((size_t)b * a.Hq + hq0 + hh) * D + g * E;
-    const float *sr = a.sq + ((size_t)b * a.Hq + hq0 + hh) * D + g * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      q[hh][e] = qr[e];
-      sqv[hh][e] = KQ ? sr[e] : 0.0f;
-    }
-  }
-  // Block-uniform running max per head; per-lane partial sums (each token slot
-  // adds its own tokens; slots and waves are summed at the end).
-  float M[GT], Ls[GT], o[GT][E], av[GT][E];
-#pragma unroll
-  for (int hh = 0; hh < GT; ++hh) {
-    M[hh] = -INFINITY;
-    Ls[hh] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      o[hh][e] = 0.0f;
-      av[hh][e] = 0.0f;
-    }
-  }
-
-  const int t_lo = split * a.tps;
-  const int t_hi = min(a.n_ctx, t_lo + a.tps);
-  const int ntiles = t_hi > t_lo ? (t_hi - t_lo + TT - 1) / TT : 0;
+  const int ntiles = nround / TT;
   u32x4 pf[NPT];
   auto fetch = [&](int it) {
-    const int tt = t_lo + it * TT;
-    const int nv = min(TT, t_hi - tt);
+    const int nv = min(TT, nloc - it * TT);
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       pf[k] = u32x4{0u, 0u, 0u, 0u};
       if (cbase[k] && coff[k] < nv * crec[k])
-        pf[k] = *(const u32x4 *)(cbase[k] + (size_t)tt * crec[k] + coff[k]);
+        pf[k] = *(const u32x4 *)(cbase[k] + (size_t)it * TT * crec[k] + coff[k]);
     }
   };
   auto stash = [&]() {
@@ -854,110 +1040,40 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     fetch(0);
     stash();
   }
-  __syncthreads();
-
+  __syncthreads();   // weights and the first tile are in LDS
   for (int it = 0; it < ntiles; ++it) {
-    const int nvalid = min(TT, t_hi - (t_lo + it * TT));
     if (it + 1 < ntiles) fetch(it + 1);
-
-    // phase 1: scores of this wave's tokens of the tile (base-2 logits)
-    float sct[NPW][GT];
 #pragma unroll
     for (int pw = 0; pw < NPW; ++pw) {
       const int pass = wave + 4 * pw;
-      const int tl = pass * TW + slot;
-      const bool valid = pass < NPASS && tl < nvalid;
-      const int tr = valid ? tl : 0;
-      uint32_t kw0, kw1;
-      lds_codes<D, KB, E>(tile + TL::KC + tr * TL::KREC, g, kw0, kw1);
-      uint32_t ksg = 0u;
-      if constexpr (KQ) {
-        if constexpr (E == 16) ksg = *(const uint16_t *)(tile + TL::KS + tr * TL::SREC + g * 2);
-        else ksg = tile[TL::KS + tr * TL::SREC + g];
-      }
-      const float nk = f16_bits_to_f32(*(const uint16_t *)(tile + TL::KN + tr * 2));
-      const float rk = KQ ? f16_bits_to_f32(*(const uint16_t *)(tile + TL::KR + tr * 2)) : 0.0f;
-      float sc[GT], sk[GT];
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        sc[hh] = 0.0f;
-        sk[hh] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float ck = kc_s[slice_code<KB>(kw0, kw1, e)];
-#pragma unroll
-        for (int hh = 0; hh < GT; ++hh) sc[hh] = fmaf(q[hh][e], ck, sc[hh]);
-        if constexpr (KQ) {
-          const float sg = ((ksg >> e) & 1u) ? 1.0f : -1.0f;
-#pragma unroll
-          for (int hh = 0; hh < GT; ++hh) sk[hh] = fmaf(sqv[hh][e], sg, sk[hh]);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        const float dot = group_sum<L>(sc[hh]);
-        float s;
-        if constexpr (KQ) s = nk * fmaf(a.kcoef * rk, group_sum<L>(sk[hh]), dot);
-        else s = nk * dot;
-        sct[pw][hh] = valid ? s : -INFINITY;
-      }
-    }
-    // tile max per head: over this wave's passes and slots, then over the 4 waves
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      float m = sct[0][hh];
-#pragma unroll
-      for (int pw = 1; pw < NPW; ++pw) m = fmaxf(m, sct[pw][hh]);
-#pragma unroll
-      for (int off = L; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-      if (lane == 0) wmax_s[wave][hh] = m;
-    }
-    __syncthreads();
-    // new running max (uniform over the block) and one rescale of the sums
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      const float tm = fmaxf(fmaxf(wmax_s[0][hh], wmax_s[1][hh]), fmaxf(wmax_s[2][hh], wmax_s[3][hh]));
-      const float mn = fmaxf(M[hh], tm);
-      const float al = (M[hh] == -INFINITY) ? 0.0f : fast_exp2(M[hh] - mn);
-      M[hh] = mn;
-      Ls[hh] *= al;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        o[hh][e] *= al;
-        if constexpr (VQ) av[hh][e] *= al;
-      }
-    }
-    // phase 2: weights, value and sketch sums
-#pragma unroll
-    for (int pw = 0; pw < NPW; ++pw) {
-      const int pass = wave + 4 * pw;
-      const int tl = pass * TW + slot;
-      const bool valid = pass < NPASS && tl < nvalid;
-      const int tr = valid ? tl : 0;
-      uint32_t vw0, vw1;
-      lds_codes<D, VB, E>(tile + TL::VC + tr * TL::VREC, g, vw0, vw1);
-      uint32_t vsg = 0u;
-      if constexpr (VQ) {
-        if constexpr (E == 16) vsg = *(const uint16_t *)(tile + TL::VS + tr * TL::SREC + g * 2);
-        else vsg = tile[TL::VS + tr * TL::SREC + g];
-      }
-      const float nv = f16_bits_to_f32(*(const uint16_t *)(tile + TL::VN + tr * 2));
-      const float rv = VQ ? f16_bits_to_f32(*(const uint16_t *)(tile + TL::VR + tr * 2)) : 0.0f;
+      if (pass >= NPASS) break;
+      const int tr = pass * TW + slot;
+      const float *wsrc = wbuf + (it * TT + tr) * WS;
       float c[GT], cq[GT];
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
-        const float w = valid ? fast_exp2(sct[pw][hh] - M[hh]) : 0.0f;
-        Ls[hh] += w;
-        c[hh] = w * nv;
-        cq[hh] = c[hh] * rv;
+        c[hh] = wsrc[hh];
+        cq[hh] = wsrc[GT + hh];
+      }
+      uint32_t vw0, vw1;
+      lds_codes<D, VB, E>(tile + TL::VC + tr * TL::VREC, lg, vw0, vw1);
+      uint32_t vsg = 0u;
+      if constexpr (VQ) {
+        if constexpr (E == 16) vsg = *(const uint16_t *)(tile + TL::VS + tr * TL::SREC + lg * 2);
+        else vsg = tile[TL::VS + tr * TL::SREC + lg];
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float cv = vc_s[slice_code<VB>(vw0, vw1, e)];
+      for (int p = 0; p < E / 2; ++p) {
+        const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh) o[hh][e] = fmaf(c[hh], cv, o[hh][e]);
-        if constexpr (VQ) {
+        for (int hh = 0; hh < GT; ++hh) {
+          o[hh][2 * p] = fmaf(c[hh], cv.x, o[hh][2 * p]);
+          o[hh][2 * p + 1] = fmaf(c[hh], cv.y, o[hh][2 * p + 1]);
+        }
+      }
+      if constexpr (VQ) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
           const float sg = ((vsg >> e) & 1u) ? 1.0f : -1.0f;
 #pragma unroll
           for (int hh = 0; hh < GT; ++hh) av[hh][e] = fmaf(cq[hh], sg, av[hh][e]);
@@ -969,7 +1085,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     __syncthreads();
   }
 
-  // the max is block-uniform, so slots and waves combine by plain sums
+  // ---- epilogue: sum token slots (lanes), then waves; L over threads -------
 #pragma unroll
   for (int off = L; off < 64; off <<= 1) {
 #pragma unroll
@@ -981,37 +1097,35 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       }
     }
   }
-  // Ls is replicated over the L lanes of a slot: sum one lane per slot
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
-    float l = (g == 0) ? Ls[hh] : 0.0f;
+    float l = Lp[hh];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
-    Ls[hh] = l;
+    Lp[hh] = l;
   }
+  float *wst = wbuf;   // [4][GT][NS]; the logit buffer is dead now
   if (slot == 0) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
-      if (g == 0) {
-        wst[wave][hh][0] = M[hh];
-        wst[wave][hh][1] = Ls[hh];
-      }
+      if (lg == 0) wst[(wave * GT + hh) * NS + 1] = Lp[hh];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        wst[wave][hh][2 + g * E + e] = o[hh][e];
-        wst[wave][hh][2 + D + g * E + e] = VQ ? av[hh][e] : 0.0f;
+        wst[(wave * GT + hh) * NS + 2 + lg * E + e] = o[hh][e];
+        wst[(wave * GT + hh) * NS + 2 + D + lg * E + e] = VQ ? av[hh][e] : 0.0f;
       }
     }
   }
   __syncthreads();
   for (int idx = tid; idx < GT * (2 * D + 1); idx += 256) {
     const int hh = idx / (2 * D + 1), k = idx - hh * (2 * D + 1);
+    const int col = (k == 2 * D) ? 1 : 2 + k;
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc += (k == 2 * D ? wst[w][hh][1] : wst[w][hh][2 + k]);
+    for (int w = 0; w < 4; ++w) acc += wst[(w * GT + hh) * NS + col];
     float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
     if (k == 2 * D) {
-      dst[0] = wst[0][hh][0];
+      dst[0] = nloc > 0 ? M[hh] : -INFINITY;
       dst[1] = acc;
     } else {
       dst[2 + k] = acc;
