@@ -817,6 +817,11 @@ __device__ __forceinline__ int opaque_zero() {
 
 typedef const __attribute__((address_space(4))) float cfloat;
 
+// An empty asm the value passes through: the compiler cannot fold the masks
+// that built it into each later byte extract (which would cost two
+// instructions per extract instead of one).
+__device__ __forceinline__ void pin_reg(uint32_t &x) { asm("" : "+v"(x)); }
+
 // Byte layout of one value tile of TT tokens in LDS: value codes, then value
 // sign bits (sketched values).
 template <int D, int VB, bool VQ, int TT>
@@ -832,9 +837,12 @@ struct VTile {
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // value coordinates per lane
-  constexpr int L = D / E;                           // lanes per token in phase C
-  constexpr int TW = 64 / L;                         // tokens per wave pass
-  constexpr int TT = 64;
+  constexpr int L = D / E;                           // lanes sharing a token group in phase C
+  constexpr int GPW = 64 / L;                        // token groups per wave
+  constexpr int TG = 4;                              // tokens per group
+  constexpr int TT = (1024 / L) < 256 ? (1024 / L) : 256;  // tokens per value tile
+  constexpr int NWA = TT / (GPW * TG);               // waves that own groups of a tile
+  constexpr int NGT = TT / TG;                       // groups per tile
   constexpr int NS = 2 + 2 * D;
   constexpr int WS = 2 * GT;                         // LDS floats per token
   constexpr int TPS_MAX = KVQ_SCAN_WBUF_FLOATS / WS;
@@ -843,14 +851,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   constexpr int NPAIR = 1 << (2 * VB);
   using TL = VTile<D, VB, VQ, TT>;
   constexpr int NPT = (TL::NCH + 255) / 256;         // 16-B chunks per thread per tile
-  constexpr int NPASS = TT / TW;
-  constexpr int NPW = (NPASS + 3) / 4;
+  constexpr int TSH = GT == 4 ? 4 : (GT == 2 ? 3 : 2);  // log2 of a table entry's bytes
   constexpr int EPI = 4 * GT * NS;                   // epilogue floats (reuses wbuf)
   static_assert(TPS_MAX % TT == 0, "split budget must be whole tiles");
+  static_assert(NWA >= 1 && NWA <= 4 && E % 8 == 0, "phase C mapping");
   static_assert(EPI <= KVQ_SCAN_WBUF_FLOATS, "epilogue staging must fit the logit buffer");
 
   __shared__ __attribute__((aligned(16))) float wbuf[KVQ_SCAN_WBUF_FLOATS];
   __shared__ __attribute__((aligned(16))) uint8_t tile[TL::BYTES];
+  // sign tables of the tile's token groups: for group g and 4-bit mask m,
+  // sum_i (2 m_i - 1) cq[4g + i] per head
+  __shared__ __attribute__((aligned(16))) float tbl[VQ ? NGT * 16 * GT : 1];
   __shared__ float kc_s[16];
   __shared__ __attribute__((aligned(8))) f32x2 vp_s[NPAIR];
   __shared__ float red_s[4][GT];
@@ -917,9 +928,28 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       acc[hh] = 0.0f;
       sk[hh] = 0.0f;
     }
+    // 4-bit codes: code*4 of even nibbles in the bytes of lo4, odd in hi4, so
+    // each table address is one byte extract
+    uint32_t lo4[KB == 4 ? KW : 1], hi4[KB == 4 ? KW : 1];
+    if constexpr (KB == 4) {
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        lo4[k] = (kw[k] << 2) & 0x3C3C3C3Cu;
+        hi4[k] = (kw[k] >> 2) & 0x3C3C3C3Cu;
+        pin_reg(lo4[k]);
+        pin_reg(hi4[k]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      const float ck = kc_s[rec_code<D, KB>(kw, i)];
+      float ck;
+      if constexpr (KB == 4) {
+        const uint32_t w = (i & 1) ? hi4[i >> 3] : lo4[i >> 3];
+        const uint32_t off = (w >> (8 * ((i & 7) >> 1))) & 0xFFu;
+        ck = *(const float *)((const uint8_t *)kc_s + off);
+      } else {
+        ck = kc_s[rec_code<D, KB>(kw, i)];
+      }
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) acc[hh] = fmaf(qc[z + i * GT + hh], ck, acc[hh]);
       if constexpr (KQ) {
@@ -998,7 +1028,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   }
 
   // ---- phase C: values ---------------------------------------------------
-  const int lg = lane % L, slot = lane / L;
+  // Lane (gs, lg) owns coordinates [lg*E, lg*E + E) of token group
+  // wave*GPW + gs of every tile (4 consecutive tokens).  Sign bits of the 4
+  // tokens are transposed so that each coordinate's 4 bits form a table index.
+  const int lg = lane % L, gs = lane / L;
+  const int grp = wave * GPW + gs;
+  const bool active = wave < NWA;
   float o[GT][E], av[GT][E];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh)
@@ -1036,52 +1071,121 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int k = 0; k < NPT; ++k)
       if (cbase[k]) *(u32x4 *)(tile + (tid + 256 * k) * 16) = pf[k];
   };
+  // tables of tile `it` from the weights cq (zero past the split's end)
+  auto build_tables = [&](int it) {
+    if constexpr (VQ) {
+      for (int idx = tid; idx < NGT * 16; idx += 256) {
+        const int g = idx >> 4, m = idx & 15;
+        const float *cqp = wbuf + (it * TT + g * TG) * WS + GT;
+        float acc[GT];
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) acc[hh] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+          const float sg = ((m >> i) & 1) ? 1.0f : -1.0f;
+#pragma unroll
+          for (int hh = 0; hh < GT; ++hh) acc[hh] = fmaf(sg, cqp[i * WS + hh], acc[hh]);
+        }
+        float *dst = tbl + idx * GT;
+        if constexpr (GT == 4) *(float4 *)dst = float4{acc[0], acc[1], acc[2], acc[3]};
+        else if constexpr (GT == 2) *(f32x2 *)dst = f32x2{acc[0], acc[1]};
+        else dst[0] = acc[0];
+      }
+    }
+  };
+  // add the table entries of 8 coordinates whose 4-token sign bits are in w
+  // (byte i = token i, bit e = coordinate e0 + e)
+  auto sign_terms = [&](uint32_t w, int e0) {
+    // 4x8 bit transpose by four delta swaps: afterwards nibble e holds the
+    // bits of coordinate e for tokens 0..3
+    auto dswap = [](uint32_t x, int sh, uint32_t m) {
+      const uint32_t t = ((x >> sh) ^ x) & m;
+      return x ^ t ^ (t << sh);
+    };
+    uint32_t y = dswap(w, 7, 0x00AA00AAu);
+    y = dswap(y, 14, 0x0000CCCCu);
+    y = dswap(y, 4, 0x00F000F0u);
+    y = dswap(y, 8, 0x0000FF00u);
+    uint32_t lo = (y << TSH) & (0x0F0F0F0Fu << TSH);          // even coordinates
+    uint32_t hi = (y >> (4 - TSH)) & (0x0F0F0F0Fu << TSH);    // odd coordinates
+    pin_reg(lo);
+    pin_reg(hi);
+    const uint8_t *tg = (const uint8_t *)tbl + (size_t)grp * 16 * GT * 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t off = (((e & 1) ? hi : lo) >> (8 * (e >> 1))) & 0xFFu;
+      const float *t = (const float *)(tg + off);
+      if constexpr (GT == 4) {
+        const float4 v = *(const float4 *)t;
+        av[0][e0 + e] += v.x;
+        av[1][e0 + e] += v.y;
+        av[2][e0 + e] += v.z;
+        av[3][e0 + e] += v.w;
+      } else if constexpr (GT == 2) {
+        const f32x2 v = *(const f32x2 *)t;
+        av[0][e0 + e] += v.x;
+        av[1][e0 + e] += v.y;
+      } else {
+        av[0][e0 + e] += t[0];
+      }
+    }
+  };
   if (ntiles > 0) {
     fetch(0);
     stash();
   }
-  __syncthreads();   // weights and the first tile are in LDS
+  __syncthreads();   // weights (phase B) and the first tile are in LDS
+  if constexpr (VQ) {
+    if (ntiles > 0) build_tables(0);
+    __syncthreads();
+  }
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) fetch(it + 1);
+    if (active) {
+      const int tr0 = grp * TG;
+      float c[TG][GT];
 #pragma unroll
-    for (int pw = 0; pw < NPW; ++pw) {
-      const int pass = wave + 4 * pw;
-      if (pass >= NPASS) break;
-      const int tr = pass * TW + slot;
-      const float *wsrc = wbuf + (it * TT + tr) * WS;
-      float c[GT], cq[GT];
+      for (int i = 0; i < TG; ++i) {
+        const float *wsrc = wbuf + (it * TT + tr0 + i) * WS;
 #pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        c[hh] = wsrc[hh];
-        cq[hh] = wsrc[GT + hh];
-      }
-      uint32_t vw0, vw1;
-      lds_codes<D, VB, E>(tile + TL::VC + tr * TL::VREC, lg, vw0, vw1);
-      uint32_t vsg = 0u;
-      if constexpr (VQ) {
-        if constexpr (E == 16) vsg = *(const uint16_t *)(tile + TL::VS + tr * TL::SREC + lg * 2);
-        else vsg = tile[TL::VS + tr * TL::SREC + lg];
+        for (int hh = 0; hh < GT; ++hh) c[i][hh] = wsrc[hh];
       }
 #pragma unroll
-      for (int p = 0; p < E / 2; ++p) {
-        const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
+      for (int i = 0; i < TG; ++i) {
+        uint32_t vw0, vw1;
+        lds_codes<D, VB, E>(tile + TL::VC + (tr0 + i) * TL::VREC, lg, vw0, vw1);
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh) {
-          o[hh][2 * p] = fmaf(c[hh], cv.x, o[hh][2 * p]);
-          o[hh][2 * p + 1] = fmaf(c[hh], cv.y, o[hh][2 * p + 1]);
+        for (int p = 0; p < E / 2; ++p) {
+          const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
+#pragma unroll
+          for (int hh = 0; hh < GT; ++hh) {
+            o[hh][2 * p] = fmaf(c[i][hh], cv.x, o[hh][2 * p]);
+            o[hh][2 * p + 1] = fmaf(c[i][hh], cv.y, o[hh][2 * p + 1]);
+          }
         }
       }
       if constexpr (VQ) {
+        const uint8_t *sb = tile + TL::VS + tr0 * TL::SREC;
+        if constexpr (E == 8) {
+          uint32_t w = 0u;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float sg = ((vsg >> e) & 1u) ? 1.0f : -1.0f;
+          for (int i = 0; i < TG; ++i) w |= (uint32_t)sb[i * TL::SREC + lg] << (8 * i);
+          sign_terms(w, 0);
+        } else {
+          uint32_t h[TG];
 #pragma unroll
-          for (int hh = 0; hh < GT; ++hh) av[hh][e] = fmaf(cq[hh], sg, av[hh][e]);
+          for (int i = 0; i < TG; ++i) h[i] = *(const uint16_t *)(sb + i * TL::SREC + lg * 2);
+          const uint32_t x01 = h[0] | (h[1] << 16), x23 = h[2] | (h[3] << 16);
+          sign_terms(__builtin_amdgcn_perm(x23, x01, 0x06040200u), 0);
+          sign_terms(__builtin_amdgcn_perm(x23, x01, 0x07050301u), 8);
         }
       }
     }
     __syncthreads();
-    if (it + 1 < ntiles) stash();
+    if (it + 1 < ntiles) {
+      stash();
+      build_tables(it + 1);
+    }
     __syncthreads();
   }
 
@@ -1105,7 +1209,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     Lp[hh] = l;
   }
   float *wst = wbuf;   // [4][GT][NS]; the logit buffer is dead now
-  if (slot == 0) {
+  if (gs == 0) {
 #pragma unroll
     for (int hh = 0; hh < GT; ++hh) {
       if (lg == 0) wst[(wave * GT + hh) * NS + 1] = Lp[hh];
