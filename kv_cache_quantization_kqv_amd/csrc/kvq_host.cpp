@@ -212,6 +212,13 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
 
 int heads_per_block(int G) { return G >= 4 ? 4 : G; }
 
+// Split arrival counters, one per (b, KV head, head group), padded to 16 bytes.
+size_t counter_bytes(const kvq_cache *c, int q_heads) {
+  const int G = q_heads / c->kv_heads;
+  const size_t n = (size_t)c->batch * c->kv_heads * (G / heads_per_block(G));
+  return (n * sizeof(unsigned) + 15) / 16 * 16;
+}
+
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || (G > 4 && G % 4 == 0); }
 
 // Fewest splits that keep every split's logits in LDS.
@@ -394,7 +401,8 @@ kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int 
   if (splits == 0) splits = auto_splits(c, q_heads, n_ctx);
   if (splits < min_splits(c, q_heads, n_ctx)) return KVQ_ERR_RANGE;
   size_t rows = (size_t)c->batch * q_heads;
-  *bytes = sizeof(float) * (rows * c->d * 2 + rows * (size_t)splits * (2 + 2 * (size_t)c->d));
+  *bytes = sizeof(float) * (rows * c->d * 2 + rows * (size_t)splits * (2 + 2 * (size_t)c->d)) +
+           counter_bytes(c, q_heads);
   return KVQ_OK;
 }
 
@@ -420,11 +428,14 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   float *qt = ws;
   float *sqt = ws + (size_t)rows * d;
   float *part = ws + (size_t)rows * d * 2;
+  unsigned *cnt = (unsigned *)(part + (size_t)rows * splits * (2 + 2 * (size_t)d));
+  const int units = c->batch * c->kv_heads * (G / gt);
   hipStream_t hs = (hipStream_t)stream;
 
   kvq::PrepArgs p;
   p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = rows;
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
+  p.cnt = cnt; p.ncnt = units;
   p.qscale = c->rotate ? (float)(1.4426950408889634 / d) : (float)(1.4426950408889634 / std::sqrt((double)d));
   (void)kLog2e;
   hipError_t e = by_dim(d, [&](auto D) {
@@ -437,7 +448,10 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   std::memset(&a, 0, sizeof(a));
   a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
   a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
-  a.qt = qt; a.sqt = sqt; a.part = part;
+  a.qt = qt; a.sqt = sqt; a.part = part; a.cnt = cnt; a.S = c->S; a.out = out;
+  a.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
+  a.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
+  a.rot = c->rotate != 0;
   for (int i = 0; i < 16; ++i) {
     a.kcent[i] = c->cb_k.centroid[i];
     a.vcent[i] = c->cb_v.centroid[i];
@@ -448,15 +462,6 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   e = by_dim(d, [&](auto D) {
     return kvq::launch_decode<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
                                                   c->v_qjl != 0, gt, c->batch, hs);
-  });
-  if (e != hipSuccess) return KVQ_ERR_HIP;
-
-  kvq::CombineArgs cb;
-  cb.part = part; cb.S = c->S; cb.out = out; cb.splits = splits;
-  cb.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
-  cb.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
-  e = by_dim(d, [&](auto D) {
-    return kvq::launch_combine<decltype(D)::value>(cb, c->rotate != 0, c->v_qjl != 0, rows, hs);
   });
   return hip_status(e);
 }

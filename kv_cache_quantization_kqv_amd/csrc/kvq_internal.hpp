@@ -50,6 +50,8 @@ struct PrepArgs {
   int rows;                  // B * Hq
   int Hq, Hkv, G, GT, HG;    // G = Hq / Hkv query heads per KV head, GT per block, HG = G / GT
   float qscale;              // log2(e)/d (rotated) or log2(e)/sqrt(d)
+  unsigned *cnt;             // split arrival counters, zeroed here (B * Hkv * HG)
+  int ncnt;
 };
 
 struct DecodeArgs {
@@ -57,19 +59,17 @@ struct DecodeArgs {
   const uint16_t *kn, *kr, *vn, *vr;
   const float *qt, *sqt;      // prepared queries, layout of PrepArgs::qt
   float *part;               // [B][Hq][splits][2 + 2d]
+  unsigned *cnt;             // split arrival counter per (b, KV head, head group)
+  const uint16_t *S;         // sketch (merge: S^T a)
+  float *out;                // [B][Hq][d]
   float kcent[16], vcent[16];
   float kcoef;               // sqrt(pi/2)/m (K sketch)
+  float vcoef;               // sqrt(pi/2)/m (V sketch)
+  float oscale;              // 1/sqrt(d) when rotated, else 1
+  int rot;                   // inverse WHT in the merge
   int Hkv, Hq, Gtot, HG, cap, n_ctx, splits, tps;
 };
 
-struct CombineArgs {
-  const float *part;
-  const uint16_t *S;
-  float *out;
-  int splits;
-  float vcoef;               // sqrt(pi/2)/m (V sketch)
-  float oscale;              // 1/sqrt(d) when rotated, else 1
-};
 
 // Dispatchers: one translation unit per head dimension.
 template <int D> hipError_t launch_quantize(const QuantArgs &a, int bits, bool rot, bool qjl,
@@ -80,7 +80,5 @@ template <int D> hipError_t launch_prep(const PrepArgs &a, bool rot, bool kqjl, 
                                         hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq,
                                           int gt, int B, hipStream_t s);
-template <int D> hipError_t launch_combine(const CombineArgs &a, bool rot, bool vq, int rows,
-                                           hipStream_t s);
 
 }  // namespace kvq

@@ -653,6 +653,7 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
   const int hg = within / a.GT, hh = within - hg * a.GT;
   const size_t dst = ((((size_t)b * a.Hkv + hkv) * a.HG + hg) * D + i) * a.GT + hh;
   a.qt[dst] = x;
+  if (i == 0 && row < a.ncnt) a.cnt[row] = 0u;
   if constexpr (KQ) {
     __syncthreads();
     t_s[i] = x;
@@ -679,42 +680,33 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
 // The block writes (M, L, o'[D], a[D]) per head; the merge kernel combines the
 // splits.
 // ---------------------------------------------------------------------------
+// One cache record into registers.  Records are read once per decode step, so
+// the loads carry the nontemporal hint (streaming; measured to matter a lot on
+// this part for block-contiguous streams).
 template <int BYTES>
 __device__ __forceinline__ void load_rec(const uint8_t *p, uint32_t *w) {
   if constexpr (BYTES % 16 == 0) {
 #pragma unroll
     for (int k = 0; k < BYTES / 16; ++k) {
-      const u32x4 v = *(const u32x4 *)(p + 16 * k);
+      const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(p + 16 * k));
       w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
     }
   } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < BYTES / 8; ++k) {
-      const u32x2 v = *(const u32x2 *)(p + 8 * k);
+      const u32x2 v = __builtin_nontemporal_load((const u32x2 *)(p + 8 * k));
       w[2 * k] = v.x; w[2 * k + 1] = v.y;
     }
   } else if constexpr (BYTES % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < BYTES / 4; ++k) w[k] = *(const uint32_t *)(p + 4 * k);
+    for (int k = 0; k < BYTES / 4; ++k) w[k] = __builtin_nontemporal_load((const uint32_t *)(p + 4 * k));
   } else if constexpr (BYTES == 6) {
     const uint16_t *h = (const uint16_t *)p;
-    w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-    w[1] = h[2];
+    w[0] = (uint32_t)__builtin_nontemporal_load(h) | ((uint32_t)__builtin_nontemporal_load(h + 1) << 16);
+    w[1] = __builtin_nontemporal_load(h + 2);
   } else {
     static_assert(BYTES == 2, "record size");
-    w[0] = *(const uint16_t *)p;
-  }
-}
-
-// Code i of a whole record held as little-endian words (layout as place_code).
-template <int D, int BITS>
-__device__ __forceinline__ uint32_t rec_code(const uint32_t *w, int i) {
-  if constexpr (BITS == 3) {
-    const uint32_t lo = (w[(2 * i) >> 5] >> ((2 * i) & 31)) & 3u;
-    const uint32_t hi = (w[D / 16 + (i >> 5)] >> (i & 31)) & 1u;
-    return lo | (hi << 2);
-  } else {
-    return (w[(i * BITS) >> 5] >> ((i * BITS) & 31)) & ((1u << BITS) - 1u);
+    w[0] = __builtin_nontemporal_load((const uint16_t *)p);
   }
 }
 
@@ -753,6 +745,27 @@ __device__ __forceinline__ void lds_codes(const uint8_t *r, int g, uint32_t &w0,
       w1 = 0u;
     }
   }
+}
+
+// The first nb bytes (even, below 16) of a 16-byte piece, zero-extended: the
+// last piece of a split's value segment may end inside the piece (records of
+// 2, 6, 8, 12 or 24 bytes), and the bytes after it may lie past the end of the
+// caller's buffer.
+__device__ __forceinline__ u32x4 load_piece_tail(const uint8_t *p, int nb) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < nb; i += 2) w[i >> 2] |= (uint32_t)(*(const uint16_t *)(p + i)) << (8 * (i & 2));
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Pair-table index of coordinates (2p, 2p+1) of a whole record held as words
+// (same index convention as pair_index).
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t rec_pair(const uint32_t *w, int p) {
+  if constexpr (BITS == 4) return (w[p >> 2] >> (8 * (p & 3))) & 255u;
+  if constexpr (BITS == 3)
+    return ((w[p >> 3] >> (4 * (p & 7))) & 15u) | (((w[D / 16 + (p >> 4)] >> (2 * (p & 15))) & 3u) << 4);
+  if constexpr (BITS == 2) return (w[p >> 3] >> (4 * (p & 7))) & 15u;
+  return (w[p >> 4] >> (2 * (p & 15))) & 3u;
 }
 
 // Codes of coordinate pair p of a lane's E-coordinate slice (words from
@@ -834,8 +847,121 @@ struct VTile {
   static_assert(BYTES % 16 == 0 && VS % 16 == 0, "tile segments must be 16-byte multiples");
 };
 
+// Device-coherent load of a split partial written by another block.
+__device__ __forceinline__ float ld_part(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge of the splits of GT query heads (run by one block of 256 threads).
+// LDS: `sm` needs GT * (MCH + NS) floats; `mx` GT floats.
+template <int D, bool VQ, int GT>
+__device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, float *mx, int b,
+                                             int hq0) {
+  constexpr int NS = 2 + 2 * D;
+  constexpr int MCH = 256;                           // splits per weight chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int splits = a.splits;
+  const float *pb = a.part + ((size_t)b * a.Hq + hq0) * splits * NS;   // head hh: + hh*splits*NS
+  float *al = sm;                                    // [GT][MCH]
+  float *res = sm + GT * MCH;                        // [GT][NS] merged L, o', a
+  if (wave < GT) {
+    float m = -INFINITY;
+    for (int s = lane; s < splits; s += 64) m = fmaxf(m, ld_part(pb + ((size_t)wave * splits + s) * NS));
+    m = wave_max(m);
+    if (lane == 0) mx[wave] = m;
+  }
+  __syncthreads();
+  constexpr int NIT = (GT * (NS - 1) + 255) / 256;   // (head, column) items per thread
+  float acc[NIT];
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) acc[j] = 0.0f;
+  for (int s0 = 0; s0 < splits; s0 += MCH) {
+    for (int idx = tid; idx < GT * MCH; idx += 256) {
+      const int hh = idx / MCH, s = s0 + idx - hh * MCH;
+      float w = 0.0f;
+      if (s < splits) {
+        const float ms = ld_part(pb + ((size_t)hh * splits + s) * NS);
+        w = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - mx[hh]);
+      }
+      al[idx] = w;
+    }
+    __syncthreads();
+    const int sn = min(MCH, splits - s0);
+    // eight splits per step, all their loads issued before any is used
+    for (int u0 = 0; u0 < sn; u0 += 8) {
+      float v[NIT][8];
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        const int item = tid + 256 * j;
+        const bool ok = item < GT * (NS - 1);
+        const int hh = ok ? item / (NS - 1) : 0, col = ok ? 1 + item - hh * (NS - 1) : 1;
+        const float *src = pb + ((size_t)hh * splits + s0 + u0) * NS + col;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[j][u] = (ok && u0 + u < sn) ? ld_part(src + (size_t)u * NS) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        const int item = tid + 256 * j;
+        const int hh = item < GT * (NS - 1) ? item / (NS - 1) : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[j] = fmaf(al[hh * MCH + u0 + u], v[j][u], acc[j]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < NIT; ++j) {
+    const int item = tid + 256 * j;
+    if (item < GT * (NS - 1)) {
+      const int hh = item / (NS - 1), col = 1 + item - hh * (NS - 1);
+      res[hh * NS + col] = acc[j];
+    }
+  }
+  __syncthreads();
+  // o' (+ sqrt(pi/2)/m S^T a) into al[hh][i] (reused as the WHT buffer)
+  float *wv = al;
+  for (int item = tid; item < GT * D; item += 256) {
+    const int hh = item / D, i = item - hh * D;
+    float v = res[hh * NS + 2 + i];
+    if constexpr (VQ) {
+      const float *av = res + hh * NS + 2 + D;
+      float t = 0.0f;
+      for (int k = 0; k < D; ++k) t = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), av[k], t);
+      v = fmaf(a.vcoef, t, v);
+    }
+    wv[hh * D + i] = v;
+  }
+  __syncthreads();
+  if (a.rot) {
+    for (int h = 1; h < D; h <<= 1) {
+      for (int pi = tid; pi < GT * D / 2; pi += 256) {
+        const int hh = pi / (D / 2), r = pi - hh * (D / 2);
+        const int i = (r / h) * 2 * h + (r % h);     // i has bit h clear
+        const float p = wv[hh * D + i], q = wv[hh * D + i + h];
+        wv[hh * D + i] = p + q;
+        wv[hh * D + i + h] = p - q;
+      }
+      __syncthreads();
+    }
+  }
+  for (int item = tid; item < GT * D; item += 256) {
+    const int hh = item / D, i = item - hh * D;
+    a.out[((size_t)b * a.Hq + hq0 + hh) * D + i] = wv[hh * D + i] * a.oscale / res[hh * NS + 1];
+  }
+}
+
+#ifndef KVQ_SCAN_PD
+#define KVQ_SCAN_PD 3   // value tiles in flight (registers) ahead of the one in LDS
+#endif
+
+#ifdef KVQ_SCAN_WAVES_PER_EU
+#define KVQ_SCAN_OCC __attribute__((amdgpu_waves_per_eu(KVQ_SCAN_WAVES_PER_EU)))
+#else
+#define KVQ_SCAN_OCC
+#endif
+
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeArgs a) {
   constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // value coordinates per lane
   constexpr int L = D / E;                           // lanes sharing a token group in phase C
   constexpr int GPW = 64 / L;                        // token groups per wave
@@ -844,25 +970,26 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   constexpr int NWA = TT / (GPW * TG);               // waves that own groups of a tile
   constexpr int NGT = TT / TG;                       // groups per tile
   constexpr int NS = 2 + 2 * D;
-  constexpr int WS = 2 * GT;                         // LDS floats per token
-  constexpr int TPS_MAX = KVQ_SCAN_WBUF_FLOATS / WS;
+  constexpr int TPS_MAX = KVQ_SCAN_WBUF_FLOATS / (2 * GT);
   constexpr int KBYTES = D * KB / 8, KW = (KBYTES + 3) / 4;
   constexpr int SBYTES = D / 8, SW = (SBYTES + 3) / 4;
   constexpr int NPAIR = 1 << (2 * VB);
+  constexpr int KPAIR = 1 << (2 * KB);
   using TL = VTile<D, VB, VQ, TT>;
   constexpr int NPT = (TL::NCH + 255) / 256;         // 16-B chunks per thread per tile
   constexpr int TSH = GT == 4 ? 4 : (GT == 2 ? 3 : 2);  // log2 of a table entry's bytes
-  constexpr int EPI = 4 * GT * NS;                   // epilogue floats (reuses wbuf)
+  constexpr int EPI = GT * NS;                       // epilogue floats (reuses wbuf)
   static_assert(TPS_MAX % TT == 0, "split budget must be whole tiles");
   static_assert(NWA >= 1 && NWA <= 4 && E % 8 == 0, "phase C mapping");
   static_assert(EPI <= KVQ_SCAN_WBUF_FLOATS, "epilogue staging must fit the logit buffer");
+  static_assert(GT * (256 + NS) <= KVQ_SCAN_WBUF_FLOATS, "merge staging must fit the logit buffer");
 
   __shared__ __attribute__((aligned(16))) float wbuf[KVQ_SCAN_WBUF_FLOATS];
   __shared__ __attribute__((aligned(16))) uint8_t tile[TL::BYTES];
   // sign tables of the tile's token groups: for group g and 4-bit mask m,
   // sum_i (2 m_i - 1) cq[4g + i] per head
   __shared__ __attribute__((aligned(16))) float tbl[VQ ? NGT * 16 * GT : 1];
-  __shared__ float kc_s[16];
+  __shared__ __attribute__((aligned(8))) f32x2 kp_s[KPAIR];
   __shared__ __attribute__((aligned(8))) f32x2 vp_s[NPAIR];
   __shared__ float red_s[4][GT];
 
@@ -873,18 +1000,72 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const int hq0 = hkv * a.Gtot + hg * GT;
   const size_t unit = (size_t)b * a.Hkv + hkv;
   const size_t unitg = unit * a.HG + hg;
-  if (tid < 16) kc_s[tid] = a.kcent[tid];
+  for (int p = tid; p < KPAIR; p += 256) {
+    int ca, cb;
+    pair_codes<KB>(p, ca, cb);
+    kp_s[p] = f32x2{a.kcent[ca], a.kcent[cb]};
+  }
   for (int p = tid; p < NPAIR; p += 256) {
     int ca, cb;
     pair_codes<VB>(p, ca, cb);
     vp_s[p] = f32x2{a.vcent[ca], a.vcent[cb]};
   }
 
+  // logits, then weights c = w n_v per (token, head) in plane wc; cq = c rho_v
+  // in plane wq (16 bytes per token at four heads: linear b128 accesses)
+  float *const wc = wbuf;
+  float *const wq = wbuf + TPS_MAX * GT;
   const int t_lo = split * a.tps;
   const int t_hi = min(a.n_ctx, t_lo + a.tps);
   const int nloc = t_hi > t_lo ? t_hi - t_lo : 0;
   const size_t rec0 = unit * a.cap + t_lo;           // first record of the split
   __syncthreads();
+
+  // value tiles: thread tid copies 16-byte chunks tid + 256k of each tile;
+  // KVQ_SCAN_PD tiles are in flight in registers (the first ones requested
+  // before phase A, so they arrive while the keys are scored)
+  constexpr int PD = KVQ_SCAN_PD;
+  const int nround = (nloc + TT - 1) / TT * TT;
+  const int ntiles = nround / TT;
+  const uint8_t *cbase[NPT];
+  int crec[NPT], coff[NPT];
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const int byte = (tid + 256 * k) * 16;
+    const uint8_t *base = nullptr;
+    int rec = 1, start = 0;
+    if (byte < TL::VS) { base = a.vc; rec = TL::VREC; start = TL::VC; }
+    else if (byte < TL::BYTES) { base = a.vs; rec = TL::SREC; start = TL::VS; }
+    cbase[k] = base ? base + rec0 * rec : nullptr;
+    crec[k] = rec;
+    coff[k] = byte - start;
+  }
+  u32x4 pf[PD][NPT];
+  auto fetch = [&](int it, u32x4 *dst) {
+    const int nv = min(TT, nloc - it * TT);
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      dst[k] = u32x4{0u, 0u, 0u, 0u};
+      if (it < ntiles && cbase[k]) {
+        const uint8_t *src = cbase[k] + (size_t)it * TT * crec[k] + coff[k];
+        const int end = nv * crec[k];
+        if constexpr (TL::VREC % 16 == 0 && TL::SREC % 16 == 0) {
+          // whole records per piece: a piece is either valid or past the end
+          if (coff[k] < end) dst[k] = __builtin_nontemporal_load((const u32x4 *)src);
+        } else {
+          if (coff[k] + 16 <= end) dst[k] = __builtin_nontemporal_load((const u32x4 *)src);
+          else if (coff[k] < end) dst[k] = load_piece_tail(src, end - coff[k]);
+        }
+      }
+    }
+  };
+  auto stash = [&](const u32x4 *src) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k)
+      if (cbase[k]) *(u32x4 *)(tile + (tid + 256 * k) * 16) = src[k];
+  };
+#pragma unroll
+  for (int j = 0; j < PD; ++j) fetch(j, pf[j]);
 
   // ---- phase A: logits, one token per lane -------------------------------
   cfloat *qc = (cfloat *)(a.qt + unitg * D * GT);
@@ -893,19 +1074,24 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const uint8_t *ks_p = KQ ? a.ks + rec0 * SBYTES : nullptr;
   const uint16_t *kn_p = a.kn + rec0;
   const uint16_t *kr_p = KQ ? a.kr + rec0 : nullptr;
+  const uint16_t *vn_p = a.vn + rec0;
+  const uint16_t *vr_p = VQ ? a.vr + rec0 : nullptr;
   float mx[GT];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) mx[hh] = -INFINITY;
 
   uint32_t kw[KW], ksw[SW];
   float nk = 0.0f, rk = 0.0f;
-  auto kload = [&](int tl, uint32_t *w, uint32_t *sw, float &n, float &r) {
+  uint32_t vnr = 0u;   // fp16 bits of the value norm (low) and residual norm (high)
+  auto kload = [&](int tl, uint32_t *w, uint32_t *sw, float &n, float &r, uint32_t &vv) {
     if (tl < nloc) {
       load_rec<KBYTES>(kc_p + (size_t)tl * KBYTES, w);
-      n = f16_bits_to_f32(kn_p[tl]);
+      n = f16_bits_to_f32(__builtin_nontemporal_load(kn_p + tl));
+      vv = (uint32_t)__builtin_nontemporal_load(vn_p + tl) |
+           (VQ ? (uint32_t)__builtin_nontemporal_load(vr_p + tl) << 16 : 0u);
       if constexpr (KQ) {
         load_rec<SBYTES>(ks_p + (size_t)tl * SBYTES, sw);
-        r = f16_bits_to_f32(kr_p[tl]);
+        r = f16_bits_to_f32(__builtin_nontemporal_load(kr_p + tl));
       }
     } else {
 #pragma unroll
@@ -914,13 +1100,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       for (int k = 0; k < SW; ++k) sw[k] = 0u;
       n = 0.0f;
       r = 0.0f;
+      vv = 0u;
     }
   };
-  kload(wave * 64 + lane, kw, ksw, nk, rk);
+  kload(wave * 64 + lane, kw, ksw, nk, rk, vnr);
   for (int base = wave * 64; base < nloc; base += 256) {
     uint32_t nw[KW], nsw[SW];
     float nnk, nrk;
-    kload(base + 256 + lane, nw, nsw, nnk, nrk);    // prefetch the next round
+    uint32_t nvnr;
+    kload(base + 256 + lane, nw, nsw, nnk, nrk, nvnr);    // prefetch the next round
     const int z = opaque_zero();
     float acc[GT], sk[GT];
 #pragma unroll
@@ -928,31 +1116,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       acc[hh] = 0.0f;
       sk[hh] = 0.0f;
     }
-    // 4-bit codes: code*4 of even nibbles in the bytes of lo4, odd in hi4, so
-    // each table address is one byte extract
-    uint32_t lo4[KB == 4 ? KW : 1], hi4[KB == 4 ? KW : 1];
-    if constexpr (KB == 4) {
 #pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        lo4[k] = (kw[k] << 2) & 0x3C3C3C3Cu;
-        hi4[k] = (kw[k] >> 2) & 0x3C3C3C3Cu;
-        pin_reg(lo4[k]);
-        pin_reg(hi4[k]);
+    for (int p = 0; p < D / 2; ++p) {
+      const f32x2 ck = kp_s[rec_pair<D, KB>(kw, p)];
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        acc[hh] = fmaf(qc[z + (2 * p) * GT + hh], ck.x, acc[hh]);
+        acc[hh] = fmaf(qc[z + (2 * p + 1) * GT + hh], ck.y, acc[hh]);
       }
     }
+    if constexpr (KQ) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      float ck;
-      if constexpr (KB == 4) {
-        const uint32_t w = (i & 1) ? hi4[i >> 3] : lo4[i >> 3];
-        const uint32_t off = (w >> (8 * ((i & 7) >> 1))) & 0xFFu;
-        ck = *(const float *)((const uint8_t *)kc_s + off);
-      } else {
-        ck = kc_s[rec_code<D, KB>(kw, i)];
-      }
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) acc[hh] = fmaf(qc[z + i * GT + hh], ck, acc[hh]);
-      if constexpr (KQ) {
+      for (int i = 0; i < D; ++i) {
         const float sg = ((ksw[i >> 5] >> (i & 31)) & 1u) ? 1.0f : -1.0f;
 #pragma unroll
         for (int hh = 0; hh < GT; ++hh) sk[hh] = fmaf(sc[z + i * GT + hh], sg, sk[hh]);
@@ -967,10 +1142,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
         else s[hh] = nk * acc[hh];
         mx[hh] = fmaxf(mx[hh], s[hh]);
       }
-      float *dst = wbuf + tl * WS;
+      float *dst = wc + tl * GT;
       if constexpr (GT == 4) *(float4 *)dst = float4{s[0], s[1], s[2], s[3]};
       else if constexpr (GT == 2) *(f32x2 *)dst = f32x2{s[0], s[1]};
       else dst[0] = s[0];
+      *(uint32_t *)(wq + tl * GT) = vnr;
     }
 #pragma unroll
     for (int k = 0; k < KW; ++k) kw[k] = nw[k];
@@ -978,6 +1154,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int k = 0; k < SW; ++k) ksw[k] = nsw[k];
     nk = nnk;
     rk = nrk;
+    vnr = nvnr;
   }
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
@@ -993,15 +1170,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     M[hh] = fmaxf(fmaxf(red_s[0][hh], red_s[1][hh]), fmaxf(red_s[2][hh], red_s[3][hh]));
     Lp[hh] = 0.0f;
   }
-  const uint16_t *vn_p = a.vn + rec0;
-  const uint16_t *vr_p = VQ ? a.vr + rec0 : nullptr;
-  const int nround = (nloc + TT - 1) / TT * TT;
   for (int tl = tid; tl < nround; tl += 256) {
     float c[GT], cq[GT];
     if (tl < nloc) {
-      const float nv = f16_bits_to_f32(vn_p[tl]);
-      const float rv = VQ ? f16_bits_to_f32(vr_p[tl]) : 0.0f;
-      const float *src = wbuf + tl * WS;
+      const uint32_t nvr = *(const uint32_t *)(wq + tl * GT);   // stored in phase A
+      const float nv = f16_bits_to_f32((uint16_t)(nvr & 0xFFFFu));
+      const float rv = VQ ? f16_bits_to_f32((uint16_t)(nvr >> 16)) : 0.0f;
+      const float *src = wc + tl * GT;
 #pragma unroll
       for (int hh = 0; hh < GT; ++hh) {
         const float w = fast_exp2(src[hh] - M[hh]);
@@ -1016,14 +1191,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
         cq[hh] = 0.0f;
       }
     }
-    float *dst = wbuf + tl * WS;
+    float *dc = wc + tl * GT, *dq = wq + tl * GT;
     if constexpr (GT == 4) {
-      *(float4 *)dst = float4{c[0], c[1], c[2], c[3]};
-      *(float4 *)(dst + 4) = float4{cq[0], cq[1], cq[2], cq[3]};
+      *(float4 *)dc = float4{c[0], c[1], c[2], c[3]};
+      *(float4 *)dq = float4{cq[0], cq[1], cq[2], cq[3]};
     } else if constexpr (GT == 2) {
-      *(float4 *)dst = float4{c[0], c[1], cq[0], cq[1]};
+      *(f32x2 *)dc = f32x2{c[0], c[1]};
+      *(f32x2 *)dq = f32x2{cq[0], cq[1]};
     } else {
-      *(f32x2 *)dst = f32x2{c[0], cq[0]};
+      dc[0] = c[0];
+      dq[0] = cq[0];
     }
   }
 
@@ -1042,41 +1219,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       o[hh][e] = 0.0f;
       av[hh][e] = 0.0f;
     }
-  const uint8_t *cbase[NPT];
-  int crec[NPT], coff[NPT];
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    const int byte = (tid + 256 * k) * 16;
-    const uint8_t *base = nullptr;
-    int rec = 1, start = 0;
-    if (byte < TL::VS) { base = a.vc; rec = TL::VREC; start = TL::VC; }
-    else if (byte < TL::BYTES) { base = a.vs; rec = TL::SREC; start = TL::VS; }
-    cbase[k] = base ? base + rec0 * rec : nullptr;
-    crec[k] = rec;
-    coff[k] = byte - start;
-  }
-  const int ntiles = nround / TT;
-  u32x4 pf[NPT];
-  auto fetch = [&](int it) {
-    const int nv = min(TT, nloc - it * TT);
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      pf[k] = u32x4{0u, 0u, 0u, 0u};
-      if (cbase[k] && coff[k] < nv * crec[k])
-        pf[k] = *(const u32x4 *)(cbase[k] + (size_t)it * TT * crec[k] + coff[k]);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int k = 0; k < NPT; ++k)
-      if (cbase[k]) *(u32x4 *)(tile + (tid + 256 * k) * 16) = pf[k];
-  };
   // tables of tile `it` from the weights cq (zero past the split's end)
   auto build_tables = [&](int it) {
     if constexpr (VQ) {
       for (int idx = tid; idx < NGT * 16; idx += 256) {
         const int g = idx >> 4, m = idx & 15;
-        const float *cqp = wbuf + (it * TT + g * TG) * WS + GT;
+        const float *cqp = wq + (it * TT + g * TG) * GT;
         float acc[GT];
 #pragma unroll
         for (int hh = 0; hh < GT; ++hh) acc[hh] = 0.0f;
@@ -1084,7 +1232,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
         for (int i = 0; i < TG; ++i) {
           const float sg = ((m >> i) & 1) ? 1.0f : -1.0f;
 #pragma unroll
-          for (int hh = 0; hh < GT; ++hh) acc[hh] = fmaf(sg, cqp[i * WS + hh], acc[hh]);
+          for (int hh = 0; hh < GT; ++hh) acc[hh] = fmaf(sg, cqp[i * GT + hh], acc[hh]);
         }
         float *dst = tbl + idx * GT;
         if constexpr (GT == 4) *(float4 *)dst = float4{acc[0], acc[1], acc[2], acc[3]};
@@ -1130,63 +1278,64 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       }
     }
   };
-  if (ntiles > 0) {
-    fetch(0);
-    stash();
-  }
-  __syncthreads();   // weights (phase B) and the first tile are in LDS
+  __syncthreads();   // weights of phase B are in LDS
   if constexpr (VQ) {
     if (ntiles > 0) build_tables(0);
-    __syncthreads();
   }
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) fetch(it + 1);
-    if (active) {
-      const int tr0 = grp * TG;
-      float c[TG][GT];
+  for (int it0 = 0; it0 < ntiles; it0 += PD) {
 #pragma unroll
-      for (int i = 0; i < TG; ++i) {
-        const float *wsrc = wbuf + (it * TT + tr0 + i) * WS;
+    for (int j = 0; j < PD; ++j) {
+      const int it = it0 + j;
+      if (it >= ntiles) break;
+      // tile `it` is in pf[j]; refill pf[j] with tile it + PD
+      stash(pf[j]);
+      fetch(it + PD, pf[j]);
+      __syncthreads();   // tile `it` (and its sign tables) are in LDS
+      if (active) {
+        const int tr0 = grp * TG;
+        float c[TG][GT];
 #pragma unroll
-        for (int hh = 0; hh < GT; ++hh) c[i][hh] = wsrc[hh];
-      }
+        for (int i = 0; i < TG; ++i) {
+          const float *wsrc = wc + (it * TT + tr0 + i) * GT;
 #pragma unroll
-      for (int i = 0; i < TG; ++i) {
-        uint32_t vw0, vw1;
-        lds_codes<D, VB, E>(tile + TL::VC + (tr0 + i) * TL::VREC, lg, vw0, vw1);
+          for (int hh = 0; hh < GT; ++hh) c[i][hh] = wsrc[hh];
+        }
 #pragma unroll
-        for (int p = 0; p < E / 2; ++p) {
-          const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
+        for (int i = 0; i < TG; ++i) {
+          uint32_t vw0, vw1;
+          lds_codes<D, VB, E>(tile + TL::VC + (tr0 + i) * TL::VREC, lg, vw0, vw1);
 #pragma unroll
-          for (int hh = 0; hh < GT; ++hh) {
-            o[hh][2 * p] = fmaf(c[i][hh], cv.x, o[hh][2 * p]);
-            o[hh][2 * p + 1] = fmaf(c[i][hh], cv.y, o[hh][2 * p + 1]);
+          for (int p = 0; p < E / 2; ++p) {
+            const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
+#pragma unroll
+            for (int hh = 0; hh < GT; ++hh) {
+              o[hh][2 * p] = fmaf(c[i][hh], cv.x, o[hh][2 * p]);
+              o[hh][2 * p + 1] = fmaf(c[i][hh], cv.y, o[hh][2 * p + 1]);
+            }
+          }
+        }
+        if constexpr (VQ) {
+          const uint8_t *sb = tile + TL::VS + tr0 * TL::SREC;
+          if constexpr (E == 8) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < TG; ++i) w |= (uint32_t)sb[i * TL::SREC + lg] << (8 * i);
+            sign_terms(w, 0);
+          } else {
+            uint32_t h[TG];
+#pragma unroll
+            for (int i = 0; i < TG; ++i) h[i] = *(const uint16_t *)(sb + i * TL::SREC + lg * 2);
+            const uint32_t x01 = h[0] | (h[1] << 16), x23 = h[2] | (h[3] << 16);
+            sign_terms(__builtin_amdgcn_perm(x23, x01, 0x06040200u), 0);
+            sign_terms(__builtin_amdgcn_perm(x23, x01, 0x07050301u), 8);
           }
         }
       }
+      __syncthreads();
       if constexpr (VQ) {
-        const uint8_t *sb = tile + TL::VS + tr0 * TL::SREC;
-        if constexpr (E == 8) {
-          uint32_t w = 0u;
-#pragma unroll
-          for (int i = 0; i < TG; ++i) w |= (uint32_t)sb[i * TL::SREC + lg] << (8 * i);
-          sign_terms(w, 0);
-        } else {
-          uint32_t h[TG];
-#pragma unroll
-          for (int i = 0; i < TG; ++i) h[i] = *(const uint16_t *)(sb + i * TL::SREC + lg * 2);
-          const uint32_t x01 = h[0] | (h[1] << 16), x23 = h[2] | (h[3] << 16);
-          sign_terms(__builtin_amdgcn_perm(x23, x01, 0x06040200u), 0);
-          sign_terms(__builtin_amdgcn_perm(x23, x01, 0x07050301u), 8);
-        }
+        if (it + 1 < ntiles) build_tables(it + 1);
       }
     }
-    __syncthreads();
-    if (it + 1 < ntiles) {
-      stash();
-      build_tables(it + 1);
-    }
-    __syncthreads();
   }
 
   // ---- epilogue: sum token slots (lanes), then waves; L over threads -------
@@ -1208,66 +1357,54 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
     Lp[hh] = l;
   }
-  float *wst = wbuf;   // [4][GT][NS]; the logit buffer is dead now
-  if (gs == 0) {
+  // waves fold their partial sums into one [GT][NS] buffer in turn (the logit
+  // buffer is dead now); lane 0 of each wave adds its L
+  float *wst = wbuf;
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+      if (gs == 0) {
 #pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      if (lg == 0) wst[(wave * GT + hh) * NS + 1] = Lp[hh];
+        for (int hh = 0; hh < GT; ++hh) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        wst[(wave * GT + hh) * NS + 2 + lg * E + e] = o[hh][e];
-        wst[(wave * GT + hh) * NS + 2 + D + lg * E + e] = VQ ? av[hh][e] : 0.0f;
+          for (int e = 0; e < E; ++e) {
+            float *po = wst + hh * NS + 2 + lg * E + e;
+            float *pa = wst + hh * NS + 2 + D + lg * E + e;
+            const float ov = o[hh][e], avv = VQ ? av[hh][e] : 0.0f;
+            *po = (w == 0) ? ov : *po + ov;
+            *pa = (w == 0) ? avv : *pa + avv;
+          }
+        }
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh) wst[hh * NS + 1] = (w == 0) ? Lp[hh] : wst[hh * NS + 1] + Lp[hh];
       }
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < GT * (2 * D + 1); idx += 256) {
-    const int hh = idx / (2 * D + 1), k = idx - hh * (2 * D + 1);
-    const int col = (k == 2 * D) ? 1 : 2 + k;
-    float acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) acc += wst[(w * GT + hh) * NS + col];
-    float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
-    if (k == 2 * D) {
-      dst[0] = nloc > 0 ? M[hh] : -INFINITY;
-      dst[1] = acc;
-    } else {
-      dst[2 + k] = acc;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Combine: merge the split partials of one (b, hq) (log-sum-exp in base 2),
-// add the sketch term sqrt(pi/2)/m S^T a, rotate back with one WHT, divide by
-// the softmax normaliser.
-// ---------------------------------------------------------------------------
-template <int D, bool ROT, bool VQ>
-__global__ __launch_bounds__(D) void combine_kernel(const CombineArgs a) {
-  constexpr int NS = 2 + 2 * D;
-  __shared__ float a_s[D];
-  __shared__ float t_s[D];
-  const int row = blockIdx.x, i = threadIdx.x;
-  const float *p = a.part + (size_t)row * a.splits * NS;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, p[(size_t)s * NS]);
-  float Lsum = 0.0f, ov = 0.0f, sv = 0.0f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = p[(size_t)s * NS];
-    const float al = (ms == -INFINITY) ? 0.0f : exp2f(ms - mx);
-    Lsum += al * p[(size_t)s * NS + 1];
-    ov += al * p[(size_t)s * NS + 2 + i];
-    if constexpr (VQ) sv += al * p[(size_t)s * NS + 2 + D + i];
-  }
-  if constexpr (VQ) {
-    a_s[i] = sv;
     __syncthreads();
-    float acc = 0.0f;
-    for (int k = 0; k < D; ++k) acc = acc + bf16_to_f32(a.S[(size_t)k * D + i]) * a_s[k];
-    ov = ov + a.vcoef * acc;
   }
-  if constexpr (ROT) ov = wht_block<D>(t_s, ov);
-  a.out[(size_t)row * D + i] = ov * a.oscale / Lsum;
+  // Partials are published with device-coherent (agent-scope) stores and read
+  // back with device-coherent loads, so no cache-wide write-back is needed:
+  // each thread waits for its stores to complete, the block synchronises, and
+  // only then is the arrival counter bumped.
+  for (int idx = tid; idx < GT * NS; idx += 256) {
+    const int hh = idx / NS, k = idx - hh * NS;
+    float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
+    __hip_atomic_store(dst + k, (k == 0) ? (nloc > 0 ? M[hh] : -INFINITY) : wst[idx],
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- merge: the last block of this (b, KV head, head group) to finish
+  // combines the splits: log-sum-exp weights in base 2, o' += sqrt(pi/2)/m S^T a,
+  // one inverse WHT, division by L.
+  __shared__ int last_s;
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0)
+    last_s = __hip_atomic_fetch_add(a.cnt + unitg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(a.splits - 1);
+  __syncthreads();
+  if (!last_s) return;
+  merge_splits<D, VQ, GT>(a, wbuf, red_s[0], b, hq0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1396,26 +1533,12 @@ hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq, 
   return hipErrorInvalidValue;
 }
 
-template <int D>
-hipError_t launch_combine(const CombineArgs &a, bool rot, bool vq, int rows, hipStream_t s) {
-  const dim3 g(rows), blk(D);
-  if (rot) {
-    if (vq) hipLaunchKernelGGL((combine_kernel<D, true, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<D, true, false>), g, blk, 0, s, a);
-  } else {
-    if (vq) hipLaunchKernelGGL((combine_kernel<D, false, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((combine_kernel<D, false, false>), g, blk, 0, s, a);
-  }
-  return hipGetLastError();
-}
-
 #define KVQ_INSTANTIATE(D)                                                                     \
   template hipError_t launch_quantize<D>(const QuantArgs &, int, bool, bool, bool, hipStream_t); \
   template hipError_t launch_dequantize<D>(const DequantArgs &, int, bool, bool, int,           \
                                            hipStream_t);                                        \
   template hipError_t launch_prep<D>(const PrepArgs &, bool, bool, bool, hipStream_t);          \
   template hipError_t launch_decode<D>(const DecodeArgs &, int, bool, int, bool, int, int,      \
-                                       hipStream_t);                                            \
-  template hipError_t launch_combine<D>(const CombineArgs &, bool, bool, int, hipStream_t);
+                                       hipStream_t);
 
 }  // namespace kvq

@@ -194,3 +194,19 @@ def test_single_token_context():
     assert rel_rows(got, want).max() < 1e-5
     vh = P.gpu.dequantize(1, 0, 1).cpu().numpy()[:, :, 0]
     assert np.allclose(got, vh, rtol=1e-5, atol=1e-6)   # o = v^_1
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_decode_full_capacity_ragged_tail(d, splits):
+    """n_ctx equal to the capacity with value records that are not 16-byte
+    multiples (3-bit codes at d <= 64): the last value piece of the last split
+    ends inside a 16-byte piece at the very end of the buffers."""
+    print(f"case full-capacity tail d={d} splits={splits}", flush=True)
+    B, Hkv, G, N = 2, 2, 4, 301
+    P = Pair("KQV", 4, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, torch.float32, 910 + d, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, Hkv * G, d), 920 + d, torch.float32)
+    got = P.gpu.decode_attention(q.cuda(), N, splits=splits).cpu().numpy()
+    assert rel_rows(got, P.attention(q, N)).max() < 1e-5
