@@ -291,8 +291,12 @@ __device__ __forceinline__ void wave_sync() {
 // denormals); otherwise the lane recomputes that row in fp64, ascending, which
 // is the definition.
 // ---------------------------------------------------------------------------
+#ifndef KVQ_QUANT_WPE
+#define KVQ_QUANT_WPE 2  // two waves per SIMD (registers <= 256)
+#endif
 template <int D, int BITS, bool ROT, bool QJL, bool BF16>
-__global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_QUANT_WPE)))
+void quantize_kernel(const QuantArgs a) {
   constexpr int LPV = D > 64 ? 2 : 1;        // lanes per vector
   constexpr int DL = D / LPV;                // coordinates per lane
   constexpr int VT = 64 / LPV;               // vectors per tile
@@ -412,7 +416,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
     }
     wave_sync();
     const int next = tile + tstride;
-    if (next < a.total_tiles) fetch(next);
+    // prefetch the next tile now, or (sketched sides) once the coordinates are
+    // dead, so the prefetch registers overlap the sketch products instead
+    if constexpr (!QJL) {
+      if (next < a.total_tiles) fetch(next);
+    }
 
     if constexpr (ROT) {
       wht_inplace<DL>(y);
@@ -495,6 +503,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QuantArgs a) {
       // element); 2^-7 also covers the fp32 error of rho.  Stored pre-scaled by
       // the accumulation-error factor D * 2^-22.
       if (half == 0) rn_s[vrow] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
+      if (next < a.total_tiles) fetch(next);
       wave_sync();
 
       // z^T = S r~^T per 32-token block: A = S rows (sketch rows k), B = r~ rows
