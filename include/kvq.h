@@ -158,8 +158,8 @@ kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *o
  * multiple of kv_heads with ratio 1, 2, 4 or a multiple of 4), no mask.
  * q: [B][q_heads][d] fp32 or bf16 (device, contiguous); out: [B][q_heads][d]
  * fp32 (device).  splits: number of token splits per (b, KV head); 0 picks
- * one for the GPU.  A split holds at most 1024 tokens when four or more query
- * heads share a KV head (2048 for two, 4096 for one): fewer splits than that
+ * one for the GPU.  A split holds at most 1280 tokens when four or more query
+ * heads share a KV head (2560 for two, 5120 for one): fewer splits than that
  * allows, or more than 8192, give KVQ_ERR_RANGE.  workspace: device scratch of
  * kvq_decode_workspace bytes (contents on entry do not matter).
  * Keys are scored in rotated space (q is rotated once instead of each key);

@@ -10,7 +10,7 @@
 // query head of the block), so a split holds at most KVQ_SCAN_WBUF_FLOATS/(2 GT)
 // tokens.
 #ifndef KVQ_SCAN_WBUF_FLOATS
-#define KVQ_SCAN_WBUF_FLOATS 8192
+#define KVQ_SCAN_WBUF_FLOATS 10240
 #endif
 
 namespace kvq {

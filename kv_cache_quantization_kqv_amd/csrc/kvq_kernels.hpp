@@ -363,15 +363,18 @@ void quantize_kernel(const QuantArgs a) {
     const int b = bh / a.H, h = bh - b * a.H;
     const int tbase = tt * VT;
     const int nvalid = min(VT, a.T - tbase);
-    const unsigned char *src0 = (const unsigned char *)a.src +
-        ((long long)b * a.sb + (long long)h * a.sh + (long long)tbase * a.st) * ESZ;
+    // chunk lane + 64k is row lane/CPR + (64/CPR) k, column lane%CPR: one base
+    // pointer per lane and a fixed row step (few live registers across the loop)
     const long long rstride = a.st * ESZ;
+    const unsigned char *src = (const unsigned char *)a.src +
+        ((long long)b * a.sb + (long long)h * a.sh + (long long)tbase * a.st) * ESZ +
+        (lane / CPR) * rstride + (lane % CPR) * 16;
+    const long long kstep = (64 / CPR) * rstride;
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
-      const int ci = lane + 64 * k;
-      const int r = ci / CPR, cc = ci - r * CPR;
+      const int r = lane / CPR + (64 / CPR) * k;
       pf[k] = u32x4{0u, 0u, 0u, 0u};
-      if (r < nvalid) pf[k] = *(const u32x4 *)(src0 + r * rstride + cc * 16);
+      if (r < nvalid) pf[k] = *(const u32x4 *)(src + k * kstep);
     }
   };
   auto stash = [&]() {
@@ -689,33 +692,34 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
 // The block writes (M, L, o'[D], a[D]) per head; the merge kernel combines the
 // splits.
 // ---------------------------------------------------------------------------
-// One cache record into registers.  Records are read once per decode step, so
-// the loads carry the nontemporal hint (streaming; measured to matter a lot on
-// this part for block-contiguous streams).
+// One cache record into registers (one lane per token).  Plain loads: the
+// record's 16-byte parts are read by separate instructions of the wave, which
+// hit the lines the first part brought into L2 (nontemporal loads here
+// re-fetched them from memory).
 template <int BYTES>
 __device__ __forceinline__ void load_rec(const uint8_t *p, uint32_t *w) {
   if constexpr (BYTES % 16 == 0) {
 #pragma unroll
     for (int k = 0; k < BYTES / 16; ++k) {
-      const u32x4 v = __builtin_nontemporal_load((const u32x4 *)(p + 16 * k));
+      const u32x4 v = *(const u32x4 *)(p + 16 * k);
       w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
     }
   } else if constexpr (BYTES % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < BYTES / 8; ++k) {
-      const u32x2 v = __builtin_nontemporal_load((const u32x2 *)(p + 8 * k));
+      const u32x2 v = *(const u32x2 *)(p + 8 * k);
       w[2 * k] = v.x; w[2 * k + 1] = v.y;
     }
   } else if constexpr (BYTES % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < BYTES / 4; ++k) w[k] = __builtin_nontemporal_load((const uint32_t *)(p + 4 * k));
+    for (int k = 0; k < BYTES / 4; ++k) w[k] = *(const uint32_t *)(p + 4 * k);
   } else if constexpr (BYTES == 6) {
     const uint16_t *h = (const uint16_t *)p;
-    w[0] = (uint32_t)__builtin_nontemporal_load(h) | ((uint32_t)__builtin_nontemporal_load(h + 1) << 16);
-    w[1] = __builtin_nontemporal_load(h + 2);
+    w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    w[1] = h[2];
   } else {
     static_assert(BYTES == 2, "record size");
-    w[0] = __builtin_nontemporal_load((const uint16_t *)p);
+    w[0] = *(const uint16_t *)p;
   }
 }
 

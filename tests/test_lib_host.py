@@ -178,12 +178,12 @@ def test_validation_status_codes(K):
 
 def test_auto_splits_fill_the_gpu(K):
     """At least ~2048 blocks, at most 256-token splits where that suffices, and
-    never more tokens per split than the LDS logit buffer holds (1024 tokens
-    at four heads per block, 2048 at two, 4096 at one)."""
+    never more tokens per split than the LDS logit buffer holds (1280 tokens
+    at four heads per block, 2560 at two, 5120 at one)."""
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)
-    assert K.kvq_decode_auto_splits(c, 32, 32768) == 32       # 1024-token splits
+    assert K.kvq_decode_auto_splits(c, 32, 32768) == 26       # 1261-token splits
     c = _fake_cache(K, d=128, B=4, H=8, cap=131136)
-    assert K.kvq_decode_auto_splits(c, 32, 131136) == 129
+    assert K.kvq_decode_auto_splits(c, 32, 131136) == 103
     c = _fake_cache(K, d=64, B=1, H=1, cap=256)
     assert K.kvq_decode_auto_splits(c, 1, 256) == 1
     c = _fake_cache(K, d=128, B=1, H=32, cap=4096)
@@ -195,15 +195,15 @@ def test_auto_splits_fill_the_gpu(K):
 
 def test_explicit_splits_below_the_lds_budget_rejected(K):
     lib = K.lib()
-    c = _fake_cache(K, d=128, B=1, H=2, cap=5000)
+    c = _fake_cache(K, d=128, B=1, H=2, cap=6000)
     ws = C.c_size_t()
     p = C.byref(c)
-    assert lib.kvq_decode_workspace(p, 8, 4096, 4, C.byref(ws)) == 0      # 1024 per split
-    assert lib.kvq_decode_workspace(p, 8, 4097, 4, C.byref(ws)) == 10
-    assert lib.kvq_decode_workspace(p, 2, 4097, 1, C.byref(ws)) == 10     # one head: 4096
-    assert lib.kvq_decode_workspace(p, 2, 4096, 1, C.byref(ws)) == 0
-    assert lib.kvq_decode_workspace(p, 4, 4096, 2, C.byref(ws)) == 0      # two heads: 2048
-    assert lib.kvq_decode_workspace(p, 4, 4097, 2, C.byref(ws)) == 10
+    assert lib.kvq_decode_workspace(p, 8, 5120, 4, C.byref(ws)) == 0      # 1280 per split
+    assert lib.kvq_decode_workspace(p, 8, 5121, 4, C.byref(ws)) == 10
+    assert lib.kvq_decode_workspace(p, 2, 5121, 1, C.byref(ws)) == 10     # one head: 5120
+    assert lib.kvq_decode_workspace(p, 2, 5120, 1, C.byref(ws)) == 0
+    assert lib.kvq_decode_workspace(p, 4, 5120, 2, C.byref(ws)) == 0      # two heads: 2560
+    assert lib.kvq_decode_workspace(p, 4, 5121, 2, C.byref(ws)) == 10
     assert lib.kvq_decode_workspace(p, 8, 4096, 8193, C.byref(ws)) == 10
 
 
