@@ -139,7 +139,8 @@ def main():
     torch.cuda.synchronize(dev)
     warm_t = e0.elapsed_time(e1) * 1e-3 / 10
 
-    roof = {"kernel": "kvq_decode_attention (prep + split scan + merge)", "bound": "hbm",
+    roof = {"kernel": "kvq_decode_attention: query kernel + decode_kernel (split scan with fused merge)",
+            "bound": "hbm",
             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
             "bytes_per_launch": dec_bytes, "per_record_bytes": rec}
