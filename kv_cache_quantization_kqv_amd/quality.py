@@ -1,0 +1,179 @@
+"""Quality harness: the KV / KQV / QKQV schemes at equal bit budget, measured
+with this library's GPU codec on synthetic caches.
+
+What is measured follows D'Alberto, "Statistical Inference and Quality
+Measures of KV Cache Quantisations Inspired by TurboQuant" (gist.science
+summary): section "Evaluation metrics" (scale and direction error of the key
+cache, the value cache and the attention output; KL divergence between the
+reference and the quantized softmax; top-5 routing recall), and the claims of
+"Contribution 1" (QJL on keys inflates the score variance), "Contribution 2"
+(KQV beats QKQV at n = 4), "Contribution 3" (low-rank keys are the worst case)
+and "Results" (without rotation, heavy tails break the key codec).
+
+Readings where the summary is silent (stated here, used throughout):
+  scale error     SNR in dB, 10 log10(sum ||x||^2 / sum ||x - x^||^2)
+  direction error 1 - cos(x, x^), mean over vectors
+  KL              sum_j p_j log(p_j / p^_j), natural log, mean over queries,
+                  p = softmax(q K^T / sqrt(d)) over all cached tokens
+  top-5 recall    |top5(p) intersect top5(p^)| / 5, mean over queries
+  score variance  variance of q . (k^ - k) / sqrt(d) over (query, token) pairs
+  projection      mean of <x^, x> / ||x||^2: 1 - D_b for a scalar Lloyd-Max side
+                  (centroid condition), 1 in expectation with the QJL sketch
+
+Key distributions (synthetic, seeded): Gaussian; heavy-tailed (per-channel
+scales |t_nu|, outliers in fixed channels); low-rank (rank 8 plus 0.1 noise);
+focused (each query aimed at one cached key, so the softmax is peaked).
+Values are Gaussian.  The reference attention uses the exact keys and values.
+"""
+from __future__ import annotations
+
+import json
+import math
+from dataclasses import asdict, dataclass
+
+import torch
+
+from . import synth
+from .kvq import KVQCache
+
+SCHEMES = ("KV", "KQV", "QKQV")
+
+
+@dataclass
+class Metrics:
+    scheme: str
+    n_bits: int
+    keys: str
+    snr_k: float
+    dir_k: float
+    snr_v: float
+    dir_v: float
+    snr_o: float
+    dir_o: float
+    kl: float
+    top5: float
+    score_var: float
+    proj_k: float
+    proj_v: float
+
+
+def _gen(seed, device):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def make_keys(kind: str, H: int, N: int, d: int, seed: int, nu: float = 3.0) -> torch.Tensor:
+    """[H][N][d] fp32 keys of one synthetic family (CPU)."""
+    g = _gen(seed, "cpu")
+    if kind in ("gaussian", "focused"):
+        return torch.randn(H, N, d, generator=g)
+    if kind == "heavytail":
+        # fixed outlier channels: per-channel scale |t_nu| (Student t drawn as
+        # Z / sqrt(chi2_nu / nu), chi2_nu from a Gamma(nu/2, 2) variate)
+        z = torch.randn(H, 1, d, generator=g)
+        chi2 = torch._standard_gamma(torch.full((H, 1, d), nu / 2.0), generator=g) * 2.0
+        s = (z / torch.sqrt(chi2 / nu)).abs()
+        return torch.randn(H, N, d, generator=g) * s
+    if kind == "lowrank":
+        U = torch.randn(H, N, 8, generator=g)
+        W = torch.randn(H, d, 8, generator=g)
+        return U @ W.transpose(1, 2) + 0.1 * torch.randn(H, N, d, generator=g)
+    raise ValueError(kind)
+
+
+def make_queries(kind: str, keys: torch.Tensor, Q: int, seed: int) -> torch.Tensor:
+    """[H][Q][d] fp32 queries.  'focused': each query is a random cached key
+    scaled up plus noise, so its attention concentrates on that key; otherwise
+    Gaussian with the keys' per-channel spread, normalised to unit mean
+    variance."""
+    g = _gen(seed, "cpu")
+    H, N, d = keys.shape
+    if kind == "focused":
+        # 1.5 x a cached key: its logit is ~1.5 ||k||^2 / sqrt(d), far above
+        # the others, so one token carries most of the weight
+        idx = torch.randint(0, N, (H, Q), generator=g)
+        base = torch.gather(keys, 1, idx[..., None].expand(H, Q, d))
+        return 1.5 * base + 0.3 * torch.randn(H, Q, d, generator=g)
+    # queries on the keys' scale: same marginal spread per channel
+    sd = keys.std(dim=1, keepdim=True)
+    return torch.randn(H, Q, d, generator=g) * sd / sd.pow(2).mean(-1, keepdim=True).sqrt()
+
+
+def _snr_db(x, xh):
+    return float(10.0 * torch.log10(x.pow(2).sum() / (x - xh).pow(2).sum().clamp_min(1e-30)))
+
+
+def _proj(x, xh):
+    x2, xh2 = x.reshape(-1, x.shape[-1]), xh.reshape(-1, x.shape[-1])
+    return float(((x2 * xh2).sum(-1) / x2.pow(2).sum(-1).clamp_min(1e-30)).mean())
+
+
+def _dir_err(x, xh):
+    c = torch.nn.functional.cosine_similarity(x.reshape(-1, x.shape[-1]), xh.reshape(-1, x.shape[-1]),
+                                              dim=-1, eps=1e-30)
+    return float((1.0 - c).mean())
+
+
+def roundtrip(scheme: str, n_bits: int, K: torch.Tensor, V: torch.Tensor, S_bf16, device):
+    """Quantize K and V ([H][N][d] fp32) with the GPU codec and reconstruct them."""
+    H, N, d = K.shape
+    cache = KVQCache(scheme, n_bits, d, 1, H, N, S_bf16=S_bf16, device=device)
+    cache.quantize_k(K[None].to(device), 0)
+    cache.quantize_v(V[None].to(device), 0)
+    Kh = cache.dequantize(0, 0, N)[0]
+    Vh = cache.dequantize(1, 0, N)[0]
+    return Kh, Vh
+
+
+def attention(q, K, V):
+    """Reference softmax attention in fp32: q [H][Q][d], K, V [H][N][d]."""
+    d = q.shape[-1]
+    s = torch.matmul(q, K.transpose(1, 2).contiguous()) / math.sqrt(d)
+    p = torch.softmax(s, dim=-1)
+    return p, torch.matmul(p, V), s
+
+
+def evaluate(scheme, n_bits, keys_kind, K, V, q, S_bf16, device) -> Metrics:
+    Kd, Vd, qd = K.to(device), V.to(device), q.to(device)
+    Kh, Vh = roundtrip(scheme, n_bits, K, V, S_bf16, device)
+    p, o, s = attention(qd, Kd, Vd)
+    ph, oh, sh = attention(qd, Kh, Vh)
+    kl = (p * (torch.log(p.clamp_min(1e-38)) - torch.log(ph.clamp_min(1e-38)))).sum(-1).mean()
+    t5 = torch.topk(p, 5, dim=-1).indices
+    t5h = torch.topk(ph, 5, dim=-1).indices
+    rec = (t5[..., :, None] == t5h[..., None, :]).any(-1).float().sum(-1).mean() / 5.0
+    return Metrics(scheme, n_bits, keys_kind, _snr_db(Kd, Kh), _dir_err(Kd, Kh), _snr_db(Vd, Vh),
+                   _dir_err(Vd, Vh), _snr_db(o, oh), _dir_err(o, oh), float(kl), float(rec),
+                   float((sh - s).var()), _proj(Kd, Kh), _proj(Vd, Vh))
+
+
+def grid(keys_kinds=("gaussian", "heavytail", "lowrank", "focused"), bits=(2, 3, 4), H=8, N=2048,
+         d=128, Q=64, seed=2024, device="cuda", nu=3.0):
+    """All (keys, scheme, n) cells on one set of inputs per key family."""
+    S = synth.bits_u16(synth.sketch_bf16(d, d, 7))
+    out = []
+    for i, kind in enumerate(keys_kinds):
+        K = make_keys(kind, H, N, d, seed + 10 * i, nu=nu)
+        V = torch.randn(H, N, d, generator=_gen(seed + 10 * i + 1, "cpu"))
+        q = make_queries(kind, K, Q, seed + 10 * i + 2)
+        for n in bits:
+            for sc in SCHEMES:
+                out.append(evaluate(sc, n, kind, K, V, q, S, device))
+    return out
+
+
+def main():
+    import argparse
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--N", type=int, default=2048)
+    ap.add_argument("--H", type=int, default=8)
+    ap.add_argument("--Q", type=int, default=64)
+    ap.add_argument("--d", type=int, default=128)
+    args = ap.parse_args()
+    for m in grid(H=args.H, N=args.N, Q=args.Q, d=args.d):
+        print(json.dumps(asdict(m)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
