@@ -171,7 +171,28 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
                                 int n_ctx, int splits, float *out, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
-/* Workspace bytes kvq_decode_attention needs for these arguments. */
+/* One decode step over compressed slots t_begin..t_end-1 plus n_win tokens
+ * the caller keeps at full precision ("Your KV cache is not a bit problem but
+ * a geometry problem", sections "Systems tax" and "What we should do": a
+ * window of the most recent tokens stays unquantized; "Frontier": attention
+ * sink tokens likewise).  The softmax runs over the union of both sets:
+ *   out[b][hq] = sum_{j in cache} p_j v^_j + sum_{j in window} p_j v_j,
+ *   p = softmax over all (q . k / sqrt(d)), exact k, v for window tokens.
+ * wk, wv: [B][kv_heads][n_win][d] of w_dtype (fp32 or bf16), device,
+ * contiguous, 16-B aligned; the window tokens' order does not matter.
+ * 0 <= t_begin <= t_end <= capacity, 0 <= n_win <= 4096, and at least one
+ * token in all (t_end - t_begin + n_win >= 1); wk and wv may be null when
+ * n_win == 0.  Other arguments as kvq_decode_attention; size the workspace
+ * with kvq_decode_workspace(c, q_heads, t_end - t_begin, splits, ...).
+ * Errors: as kvq_decode_attention. */
+kvq_status kvq_decode_attention_window(const kvq_cache *c, const void *q, int q_dtype,
+                                       int q_heads, int t_begin, int t_end, const void *wk,
+                                       const void *wv, int w_dtype, int n_win, int splits,
+                                       float *out, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+/* Workspace bytes kvq_decode_attention (or kvq_decode_attention_window over
+ * n_ctx compressed slots) needs for these arguments; n_ctx may be 0 here. */
 kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int splits,
                                 size_t *bytes);
 

@@ -395,25 +395,40 @@ kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int 
   if (!bytes) return KVQ_ERR_NULL;
   if (q_heads < 1 || q_heads % c->kv_heads) return KVQ_ERR_HEADS;
   if (!supported_group(q_heads / c->kv_heads)) return KVQ_ERR_HEADS;
-  if (n_ctx < 1) return KVQ_ERR_RANGE;
+  if (n_ctx < 0) return KVQ_ERR_RANGE;
   if (n_ctx > c->capacity) return KVQ_ERR_CAPACITY;
   if (splits < 0 || splits > 8192) return KVQ_ERR_RANGE;
   if (splits == 0) splits = auto_splits(c, q_heads, n_ctx);
   if (splits < min_splits(c, q_heads, n_ctx)) return KVQ_ERR_RANGE;
-  size_t rows = (size_t)c->batch * q_heads;
-  *bytes = sizeof(float) * (rows * c->d * 2 + rows * (size_t)splits * (2 + 2 * (size_t)c->d)) +
+  const size_t rows = (size_t)c->batch * q_heads, d = (size_t)c->d;
+  *bytes = sizeof(float) * (rows * d * 2 + rows * (size_t)splits * (2 + 2 * d) + rows * (2 + d)) +
            counter_bytes(c, q_heads);
   return KVQ_OK;
 }
 
-kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
-                                int n_ctx, int splits, float *out, void *workspace,
-                                size_t workspace_bytes, void *stream) {
+namespace {
+
+// One decode step over cache slots [t_begin, t_end) plus n_win full-precision
+// window tokens (both entry points).
+kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_heads, int t_begin,
+                       int t_end, const void *wk, const void *wv, int w_dtype, int n_win,
+                       int splits, float *out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
   kvq_status s = check_cache(c);
   if (s != KVQ_OK) return s;
   if (!q || !out) return KVQ_ERR_NULL;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
   if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (t_begin < 0 || t_end < t_begin || n_win < 0 || n_win > KVQ_WINDOW_MAX)
+    return KVQ_ERR_RANGE;
+  if (t_end > c->capacity) return KVQ_ERR_CAPACITY;
+  if (t_end - t_begin + n_win < 1) return KVQ_ERR_RANGE;
+  if (n_win > 0) {
+    if (!wk || !wv) return KVQ_ERR_NULL;
+    if (w_dtype != KVQ_F32 && w_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (!aligned16(wk) || !aligned16(wv)) return KVQ_ERR_ALIGN;
+  }
+  const int n_ctx = t_end - t_begin;
   size_t need = 0;
   s = kvq_decode_workspace(c, q_heads, n_ctx, splits, &need);
   if (s != KVQ_OK) return s;
@@ -428,7 +443,8 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   float *qt = ws;
   float *sqt = ws + (size_t)rows * d;
   float *part = ws + (size_t)rows * d * 2;
-  unsigned *cnt = (unsigned *)(part + (size_t)rows * splits * (2 + 2 * (size_t)d));
+  float *wpart = part + (size_t)rows * splits * (2 + 2 * (size_t)d);
+  unsigned *cnt = (unsigned *)(wpart + (size_t)rows * (2 + d));
   const int units = c->batch * c->kv_heads * (G / gt);
   hipStream_t hs = (hipStream_t)stream;
 
@@ -436,19 +452,32 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = rows;
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
   p.cnt = cnt; p.ncnt = units;
-  p.qscale = c->rotate ? (float)(1.4426950408889634 / d) : (float)(1.4426950408889634 / std::sqrt((double)d));
-  (void)kLog2e;
+  p.qscale = c->rotate ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
   hipError_t e = by_dim(d, [&](auto D) {
     return kvq::launch_prep<decltype(D)::value>(p, c->rotate != 0, c->k_qjl != 0,
                                                 q_dtype == KVQ_BF16, hs);
   });
   if (e != hipSuccess) return KVQ_ERR_HIP;
 
+  if (n_win > 0) {
+    kvq::WindowArgs w;
+    w.q = q; w.wk = wk; w.wv = wv; w.wpart = wpart;
+    w.Hq = q_heads; w.Hkv = c->kv_heads; w.n_win = n_win;
+    w.qscale = (float)(kLog2e / std::sqrt((double)d));
+    e = by_dim(d, [&](auto D) {
+      return kvq::launch_window<decltype(D)::value>(w, q_dtype == KVQ_BF16, w_dtype == KVQ_BF16,
+                                                    rows, hs);
+    });
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+
   kvq::DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
   a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
   a.qt = qt; a.sqt = sqt; a.part = part; a.cnt = cnt; a.S = c->S; a.out = out;
+  a.wpart = n_win > 0 ? wpart : nullptr;
+  a.t0 = t_begin;
   a.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
   a.rot = c->rotate != 0;
@@ -458,12 +487,31 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   }
   a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.Hkv = c->kv_heads; a.Hq = q_heads; a.Gtot = G; a.HG = G / gt; a.cap = c->capacity;
-  a.n_ctx = n_ctx; a.splits = splits; a.tps = (n_ctx + splits - 1) / splits;
+  a.n_ctx = n_ctx; a.splits = splits; a.tps = n_ctx > 0 ? (n_ctx + splits - 1) / splits : 0;
   e = by_dim(d, [&](auto D) {
     return kvq::launch_decode<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
                                                   c->v_qjl != 0, gt, c->batch, hs);
   });
   return hip_status(e);
+}
+
+}  // namespace
+
+kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
+                                int n_ctx, int splits, float *out, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (n_ctx < 1) return c ? KVQ_ERR_RANGE : KVQ_ERR_NULL;
+  return decode_impl(c, q, q_dtype, q_heads, 0, n_ctx, nullptr, nullptr, KVQ_F32, 0, splits,
+                     out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_window(const kvq_cache *c, const void *q, int q_dtype,
+                                       int q_heads, int t_begin, int t_end, const void *wk,
+                                       const void *wv, int w_dtype, int n_win, int splits,
+                                       float *out, void *workspace, size_t workspace_bytes,
+                                       void *stream) {
+  return decode_impl(c, q, q_dtype, q_heads, t_begin, t_end, wk, wv, w_dtype, n_win, splits, out,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

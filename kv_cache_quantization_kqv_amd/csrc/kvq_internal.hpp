@@ -67,7 +67,20 @@ struct DecodeArgs {
   float vcoef;               // sqrt(pi/2)/m (V sketch)
   float oscale;              // 1/sqrt(d) when rotated, else 1
   int rot;                   // inverse WHT in the merge
+  const float *wpart;        // full-precision window partial [B][Hq][2 + d] or null
+  int t0;                    // first cache slot of the scanned range
   int Hkv, Hq, Gtot, HG, cap, n_ctx, splits, tps;
+};
+
+// Full-precision window (sinks and recent tokens): exact partial softmax sums
+// per query row, merged with the compressed cache's splits.
+#define KVQ_WINDOW_MAX 4096  // window tokens per (batch, KV head): LDS logits of one block
+struct WindowArgs {
+  const void *q;             // [B][Hq][d], q_dtype
+  const void *wk, *wv;       // [B][Hkv][n_win][d], w_dtype
+  float *wpart;              // [B][Hq][2 + d]: max (base 2), sum, unnormalised o
+  int Hq, Hkv, n_win;
+  float qscale;              // log2(e)/sqrt(d)
 };
 
 
@@ -80,5 +93,7 @@ template <int D> hipError_t launch_prep(const PrepArgs &a, bool rot, bool kqjl, 
                                         hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq,
                                           int gt, int B, hipStream_t s);
+template <int D> hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows,
+                                          hipStream_t s);
 
 }  // namespace kvq

@@ -957,9 +957,22 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
       __syncthreads();
     }
   }
+  // with a full-precision window: one more log-sum-exp merge, in the
+  // original space (the window partial is already there)
   for (int item = tid; item < GT * D; item += 256) {
     const int hh = item / D, i = item - hh * D;
-    a.out[((size_t)b * a.Hq + hq0 + hh) * D + i] = wv[hh * D + i] * a.oscale / res[hh * NS + 1];
+    const size_t row = (size_t)b * a.Hq + hq0 + hh;
+    float num = wv[hh * D + i] * a.oscale, den = res[hh * NS + 1];
+    if (a.wpart) {
+      const float *wp = a.wpart + row * (2 + D);
+      const float mc = mx[hh], mu = wp[0];
+      const float m = fmaxf(mc, mu);
+      const float ac = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - m);
+      const float au = (mu == -INFINITY) ? 0.0f : fast_exp2(mu - m);
+      num = ac * num + au * wp[2 + i];
+      den = ac * den + au * wp[1];
+    }
+    a.out[row * D + i] = num / den;
   }
 }
 
@@ -1031,7 +1044,7 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   const int t_lo = split * a.tps;
   const int t_hi = min(a.n_ctx, t_lo + a.tps);
   const int nloc = t_hi > t_lo ? t_hi - t_lo : 0;
-  const size_t rec0 = unit * a.cap + t_lo;           // first record of the split
+  const size_t rec0 = unit * a.cap + a.t0 + t_lo;    // first record of the split
   __syncthreads();
 
   // value tiles: thread tid copies 16-byte chunks tid + 256k of each tile;
@@ -1421,6 +1434,71 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
 }
 
 // ---------------------------------------------------------------------------
+// Full-precision window ("Your KV cache is not a bit problem but a geometry
+// problem": keep the most recent tokens, and attention-sink tokens, at full
+// precision next to the quantized cache).  One block per query row computes
+// the exact partial over the window tokens: base-2 logits s_j = log2(e)
+// q.k_j / sqrt(d), their max M, L = sum 2^(s_j - M) and o = sum 2^(s_j - M) v_j,
+// which the scan's merge combines with the compressed splits.
+// ---------------------------------------------------------------------------
+template <int D, bool QB, bool WB>
+__global__ __launch_bounds__(256) void window_kernel(const WindowArgs a) {
+  __shared__ float qf[D];
+  __shared__ float sj[KVQ_WINDOW_MAX];
+  __shared__ float red[4];
+  __shared__ float po[2][D];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = row / a.Hq, hq = row - b * a.Hq;
+  const int hkv = hq / (a.Hq / a.Hkv);
+  const size_t base = ((size_t)b * a.Hkv + hkv) * a.n_win * D;
+  for (int i = tid; i < D; i += 256) {
+    const float x = QB ? bf16_to_f32(((const uint16_t *)a.q)[(size_t)row * D + i])
+                       : ((const float *)a.q)[(size_t)row * D + i];
+    qf[i] = x * a.qscale;
+  }
+  __syncthreads();
+  auto wval = [&](const void *p, size_t idx) {
+    return WB ? bf16_to_f32(((const uint16_t *)p)[idx]) : ((const float *)p)[idx];
+  };
+  float m = -INFINITY;
+  for (int j = tid; j < a.n_win; j += 256) {
+    float s = 0.0f;
+    for (int i = 0; i < D; ++i) s = fmaf(qf[i], wval(a.wk, base + (size_t)j * D + i), s);
+    sj[j] = s;
+    m = fmaxf(m, s);
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float l = 0.0f;
+  for (int j = tid; j < a.n_win; j += 256) {
+    const float w = fast_exp2(sj[j] - M);
+    sj[j] = w;
+    l += w;
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) l += __shfl_xor(l, off, 64);
+  if (lane == 0) red[wave] = l;
+  __syncthreads();
+  // o: two token halves per coordinate, then summed
+  for (int it = tid; it < 2 * D; it += 256) {
+    const int half = it / D, i = it - half * D;
+    float acc = 0.0f;
+    for (int j = half; j < a.n_win; j += 2) acc = fmaf(sj[j], wval(a.wv, base + (size_t)j * D + i), acc);
+    po[half][i] = acc;
+  }
+  __syncthreads();
+  float *dst = a.wpart + (size_t)row * (2 + D);
+  if (tid == 0) {
+    dst[0] = M;
+    dst[1] = (red[0] + red[1]) + (red[2] + red[3]);
+  }
+  for (int i = tid; i < D; i += 256) dst[2 + i] = po[0][i] + po[1][i];
+}
+
+// ---------------------------------------------------------------------------
 // Dispatchers (host).  Only the (bits, rotation, sketch) combinations that the
 // three schemes produce are instantiated.
 // ---------------------------------------------------------------------------
@@ -1546,12 +1624,26 @@ hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq, 
   return hipErrorInvalidValue;
 }
 
+template <int D>
+hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows, hipStream_t s) {
+  const dim3 g(rows), blk(256);
+  if (q_bf16) {
+    if (w_bf16) hipLaunchKernelGGL((window_kernel<D, true, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((window_kernel<D, true, false>), g, blk, 0, s, a);
+  } else {
+    if (w_bf16) hipLaunchKernelGGL((window_kernel<D, false, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((window_kernel<D, false, false>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 #define KVQ_INSTANTIATE(D)                                                                     \
   template hipError_t launch_quantize<D>(const QuantArgs &, int, bool, bool, bool, hipStream_t); \
   template hipError_t launch_dequantize<D>(const DequantArgs &, int, bool, bool, int,           \
                                            hipStream_t);                                        \
   template hipError_t launch_prep<D>(const PrepArgs &, bool, bool, bool, hipStream_t);          \
   template hipError_t launch_decode<D>(const DecodeArgs &, int, bool, int, bool, int, int,      \
-                                       hipStream_t);
+                                       hipStream_t);                                            \
+  template hipError_t launch_window<D>(const WindowArgs &, bool, bool, int, hipStream_t);
 
 }  // namespace kvq

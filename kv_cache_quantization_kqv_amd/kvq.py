@@ -25,7 +25,7 @@ KVQ_F32, KVQ_BF16 = 0, 1
 
 EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_layout",
            "kvq_quantize_k", "kvq_quantize_v", "kvq_dequantize", "kvq_decode_attention",
-           "kvq_decode_workspace", "kvq_decode_auto_splits", "kvq_status_str", "kvq_version"]
+           "kvq_decode_attention_window", "kvq_decode_workspace", "kvq_decode_auto_splits", "kvq_status_str", "kvq_version"]
 
 
 class KVQError(RuntimeError):
@@ -73,6 +73,8 @@ def lib():
             "kvq_quantize_v": ([cache_p, vp, i32, i32, i32, i64, i64, i64, vp], i32),
             "kvq_dequantize": ([cache_p, i32, i32, i32, vp, vp], i32),
             "kvq_decode_attention": ([cache_p, vp, i32, i32, i32, i32, vp, vp, sz, vp], i32),
+            "kvq_decode_attention_window": ([cache_p, vp, i32, i32, i32, i32, vp, vp, i32, i32,
+                                             i32, vp, vp, sz, vp], i32),
             "kvq_decode_workspace": ([cache_p, i32, i32, i32, C.POINTER(sz)], i32),
             "kvq_decode_auto_splits": ([cache_p, i32, i32], i32),
             "kvq_status_str": ([i32], C.c_char_p),
@@ -154,6 +156,15 @@ def kvq_decode_attention(c: kvq_cache, q: int, q_dtype: int, q_heads: int, n_ctx
                          splits: int, out: int, workspace: int, ws_bytes: int, stream: int = 0):
     _check(lib().kvq_decode_attention(C.byref(c), q, q_dtype, q_heads, n_ctx, splits, out,
                                       workspace, ws_bytes, stream), "kvq_decode_attention")
+
+
+def kvq_decode_attention_window(c: kvq_cache, q: int, q_dtype: int, q_heads: int, t_begin: int,
+                                t_end: int, wk: int, wv: int, w_dtype: int, n_win: int,
+                                splits: int, out: int, workspace: int, ws_bytes: int,
+                                stream: int = 0):
+    _check(lib().kvq_decode_attention_window(C.byref(c), q, q_dtype, q_heads, t_begin, t_end, wk,
+                                             wv, w_dtype, n_win, splits, out, workspace, ws_bytes,
+                                             stream), "kvq_decode_attention_window")
 
 
 # ------------------------------------------------------------------ torch-owned cache
@@ -252,4 +263,37 @@ class KVQCache:
             out = torch.empty(self.batch, Hq, self.d, dtype=torch.float32, device=self.device)
         kvq_decode_attention(self.c, q.data_ptr(), dt, Hq, n_ctx, splits, out.data_ptr(),
                              workspace.data_ptr(), workspace.numel(), self._stream())
+        return out
+
+    def decode_attention_window(self, q, t_begin: int, t_end: int, wk=None, wv=None,
+                                splits: int = 0, out=None, workspace=None):
+        """Decode over cache slots [t_begin, t_end) plus the full-precision
+        tokens wk, wv ([B][kv_heads][n_win][d], fp32 or bf16; None for none)."""
+        torch = self.torch
+        if q.dim() != 3 or q.shape[0] != self.batch or q.shape[2] != self.d or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B][q_heads][d] tensor")
+        dts = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}
+        dt = dts.get(q.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported dtype {q.dtype}")
+        n_win, wdt, pk, pv = 0, KVQ_F32, 0, 0
+        if wk is not None:
+            shape = (self.batch, self.kv_heads, wk.shape[2] if wk.dim() == 4 else -1, self.d)
+            if (wk.dim() != 4 or tuple(wk.shape) != shape or wv is None
+                    or tuple(wv.shape) != shape or wk.dtype != wv.dtype
+                    or not (wk.is_contiguous() and wv.is_contiguous())):
+                raise ValueError("wk, wv must be contiguous [B][kv_heads][n_win][d] tensors")
+            wdt = dts.get(wk.dtype)
+            if wdt is None:
+                raise TypeError(f"unsupported dtype {wk.dtype}")
+            n_win, pk, pv = wk.shape[2], wk.data_ptr(), wv.data_ptr()
+        Hq = q.shape[1]
+        nbytes = self.workspace_bytes(Hq, t_end - t_begin, splits)
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        if out is None:
+            out = torch.empty(self.batch, Hq, self.d, dtype=torch.float32, device=self.device)
+        kvq_decode_attention_window(self.c, q.data_ptr(), dt, Hq, t_begin, t_end, pk, pv, wdt,
+                                    n_win, splits, out.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), self._stream())
         return out

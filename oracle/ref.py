@@ -247,3 +247,42 @@ def attention_dense(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     out = np.zeros(q.shape[0], np.float64)
     lib().orc_attention_dense(_p(q), _p(K), _p(V), K.shape[0], q.shape[0], _p(out))
     return out
+
+
+def _host_f64(x: np.ndarray) -> np.ndarray:
+    """float32 array or uint16 bf16 bit patterns -> float64 (exact)."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_window(kc: OracleCache, vc: OracleCache, q: np.ndarray, t_begin: int, t_end: int,
+                     wk: np.ndarray | None, wv: np.ndarray | None, S: np.ndarray | None,
+                     nthreads: int = 1) -> np.ndarray:
+    """Decode over compressed slots [t_begin, t_end) plus full-precision window
+    tokens wk, wv [B][Hkv][n_win][d] (float32 or bf16 bits; None for none).
+
+    "Your KV cache is not a bit problem but a geometry problem", sections
+    "Systems tax" and "What we should do" (recent tokens kept unquantized) and
+    "Frontier" (attention-sink tokens likewise): one softmax over the union of
+    the reconstructed cache tokens and the exact window tokens, i.e. plain
+    attention over the concatenated key and value lists.  Returns fp64
+    [B][Hq][d]."""
+    qd = _host_f64(np.ascontiguousarray(q))
+    B, Hq, d = qd.shape
+    G = Hq // kc.H
+    T = t_end - t_begin
+    if T > 0:
+        Kh = kc.dequantize(t_begin, T, S, nthreads)
+        Vh = vc.dequantize(t_begin, T, S, nthreads)
+    else:
+        Kh = np.zeros((B, kc.H, 0, d))
+        Vh = np.zeros((B, kc.H, 0, d))
+    if wk is not None:
+        Kh = np.concatenate([Kh, _host_f64(wk)], axis=2)
+        Vh = np.concatenate([Vh, _host_f64(wv)], axis=2)
+    out = np.zeros((B, Hq, d), np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            out[b, hq] = attention_dense(qd[b, hq], Kh[b, hq // G], Vh[b, hq // G])
+    return out

@@ -65,6 +65,12 @@ class Pair:
         return ref.attention(self.ok, self.ov, host_bits(q), n_ctx, self.S, rows=rows,
                              nthreads=nthreads)
 
+    def attention_window(self, q: torch.Tensor, t_begin: int, t_end: int, wk=None, wv=None,
+                         nthreads=8):
+        return ref.attention_window(self.ok, self.ov, host_bits(q), t_begin, t_end,
+                                    None if wk is None else host_bits(wk),
+                                    None if wv is None else host_bits(wv), self.S, nthreads)
+
 
 def rel_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
     """Per-row ||got - want|| / ||want|| over the last axis."""

@@ -210,3 +210,66 @@ def test_decode_full_capacity_ragged_tail(d, splits):
     q = synth.gaussian((B, Hkv * G, d), 920 + d, torch.float32)
     got = P.gpu.decode_attention(q.cuda(), N, splits=splits).cpu().numpy()
     assert rel_rows(got, P.attention(q, N)).max() < 1e-5
+
+
+WINDOW_CASES = {
+    # name: (t_begin, t_end, window = list of (first, count) slices of the inputs)
+    "recent128": (0, 572, [(572, 128)]),
+    "sinks4_recent64": (4, 636, [(0, 4), (636, 64)]),
+    "window_only": (0, 0, [(0, 300)]),
+    "no_window_offset": (7, 700, []),
+}
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("case", list(WINDOW_CASES))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scheme,n", [("KQV", 4), ("KV", 3), ("QKQV", 2)])
+def test_decode_window_matches_oracle(scheme, n, d, case, dtype):
+    """Compressed slots [t_begin, t_end) plus full-precision sink and recent
+    tokens (the exact inputs of those positions) in one softmax."""
+    print(f"case window {scheme}{n} d={d} {case} {dtype}", flush=True)
+    B, Hkv, G, N = 2, 2, 4, 700
+    t_begin, t_end, win = WINDOW_CASES[case]
+    P = Pair(scheme, n, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, dtype, 1100 + d + n, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, Hkv * G, d), 1200 + d, dtype)
+    wk = torch.cat([K[:, :, a:a + c] for a, c in win], 2).contiguous() if win else None
+    wv = torch.cat([V[:, :, a:a + c] for a, c in win], 2).contiguous() if win else None
+    want = P.attention_window(q, t_begin, t_end, wk, wv)
+    for splits in (0, 5):
+        got = P.gpu.decode_attention_window(
+            q.cuda(), t_begin, t_end, None if wk is None else wk.cuda(),
+            None if wv is None else wv.cuda(), splits=splits).cpu().numpy()
+        err = rel_rows(got, want)
+        assert err.max() < TOL[dtype], (splits, err.max())
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_decode_window_gqa_and_largest_window(G):
+    """Largest window (4096 tokens) with a short compressed range, fp32 query
+    over bf16 inputs, every supported head grouping."""
+    print(f"case window-max G={G}", flush=True)
+    B, Hkv, d, N, W = 1, 2, 128, 300, 4096
+    P = Pair("KQV", 4, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, torch.bfloat16, 1300 + G)
+    P.write(K, V, 0)
+    wk = synth.gaussian((B, Hkv, W, d), 1310 + G, torch.bfloat16)
+    wv = synth.gaussian((B, Hkv, W, d), 1320 + G, torch.bfloat16)
+    q = synth.gaussian((B, Hkv * G, d), 1330 + G, torch.float32)
+    got = P.gpu.decode_attention_window(q.cuda(), 11, 290, wk.cuda(), wv.cuda()).cpu().numpy()
+    assert rel_rows(got, P.attention_window(q, 11, 290, wk, wv)).max() < 1e-5
+
+
+def test_decode_window_equals_plain_decode_when_empty():
+    """n_win = 0 over slots [0, n) is the plain decode entry point, bit for bit
+    (same kernels, no window partial)."""
+    B, Hkv, G, d, N = 2, 2, 4, 128, 513
+    P = Pair("KQV", 4, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, torch.float32, 1400, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, Hkv * G, d), 1401, torch.float32).cuda()
+    a = P.gpu.decode_attention(q, N, splits=3)
+    b = P.gpu.decode_attention_window(q, 0, N, splits=3)
+    assert torch.equal(a, b)

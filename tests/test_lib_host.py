@@ -147,14 +147,17 @@ def test_validation_status_codes(K):
     ws = C.c_size_t()
     assert lib.kvq_decode_workspace(p, 3, 8, 0, C.byref(ws)) == 9
     assert lib.kvq_decode_workspace(p, 6, 8, 0, C.byref(ws)) == 9       # G = 3
-    assert lib.kvq_decode_workspace(p, 2, 0, 0, C.byref(ws)) == 10
+    assert lib.kvq_decode_workspace(p, 2, -1, 0, C.byref(ws)) == 10
+    assert lib.kvq_decode_workspace(p, 2, 0, 0, C.byref(ws)) == 0      # window-only sizing
     assert lib.kvq_decode_workspace(p, 2, 33, 0, C.byref(ws)) == 6
     assert lib.kvq_decode_workspace(p, 2, 8, 0, C.byref(ws)) == 0
     need = ws.value
     d, rows, splits = 64, 2, K.kvq_decode_auto_splits(c, 2, 8)
     assert splits >= 1
     units = 1 * 2 * 1                       # (b, KV head, head group) split counters
-    assert need == 4 * (rows * d * 2 + rows * splits * (2 + 2 * d)) + (4 * units + 15) // 16 * 16
+    # prepared queries, split partials, the window partial, split counters
+    assert need == (4 * (rows * d * 2 + rows * splits * (2 + 2 * d) + rows * (2 + d))
+                    + (4 * units + 15) // 16 * 16)
     q, out, w = 0xA00000, 0xB00000, 0xC00000
     assert lib.kvq_decode_attention(p, q, 1, 2, 8, 0, out, w, need - 1, None) == 7
     assert lib.kvq_decode_attention(p, q, 1, 2, 8, 0, out, None, need, None) == 7
@@ -162,6 +165,25 @@ def test_validation_status_codes(K):
     assert lib.kvq_decode_attention(p, q + 4, 1, 2, 8, 0, out, w, need, None) == 2
     assert lib.kvq_decode_attention(p, None, 1, 2, 8, 0, out, w, need, None) == 1
     assert lib.kvq_decode_attention(p, q, 1, 2, 8, -1, out, w, need, None) == 10
+    assert lib.kvq_decode_attention(p, q, 1, 2, 0, 0, out, w, need, None) == 10
+    # decode with a full-precision window: cache slots [t_begin, t_end) + n_win tokens
+    wk, wv = 0xD00000, 0xE00000
+    win = lib.kvq_decode_attention_window
+    assert win(p, q, 1, 2, 5, 4, wk, wv, 1, 4, 0, out, w, need, None) == 10   # t_end < t_begin
+    assert win(p, q, 1, 2, -1, 4, wk, wv, 1, 4, 0, out, w, need, None) == 10
+    assert win(p, q, 1, 2, 0, 33, wk, wv, 1, 4, 0, out, w, need, None) == 6   # beyond capacity
+    assert win(p, q, 1, 2, 3, 3, wk, wv, 1, 0, 0, out, w, need, None) == 10   # no token at all
+    assert win(p, q, 1, 2, 0, 8, wk, wv, 1, 4097, 0, out, w, need, None) == 10
+    assert win(p, q, 1, 2, 0, 8, wk, wv, 1, -1, 0, out, w, need, None) == 10
+    assert win(p, q, 1, 2, 0, 8, None, wv, 1, 4, 0, out, w, need, None) == 1
+    assert win(p, q, 1, 2, 0, 8, wk, None, 1, 4, 0, out, w, need, None) == 1
+    assert win(p, q, 1, 2, 0, 8, wk, wv, 5, 4, 0, out, w, need, None) == 8
+    assert win(p, q, 1, 2, 0, 8, wk + 2, wv, 1, 4, 0, out, w, need, None) == 2
+    assert win(p, q, 1, 2, 0, 8, wk, wv + 8, 1, 4, 0, out, w, need, None) == 2
+    assert win(p, q, 1, 2, 0, 8, wk, wv, 1, 4, 0, out, w, need - 1, None) == 7
+    assert win(p, q, 3, 2, 0, 8, wk, wv, 1, 4, 0, out, w, need, None) == 8
+    assert win(None, q, 1, 2, 0, 8, wk, wv, 1, 4, 0, out, w, need, None) == 1
+    assert win(p, q, 1, 3, 0, 8, wk, wv, 1, 4, 0, out, w, need, None) == 9
     # broken cache structs
     bad = _fake_cache(K)
     bad.v_signs = 0

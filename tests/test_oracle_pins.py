@@ -434,6 +434,85 @@ def test_attention_over_cache_matches_numpy(orc, scheme):
         assert np.array_equal(part[r // Hq, r % Hq], out[r // Hq, r % Hq])
 
 
+def _window_case(scheme, seed, B=2, Hkv=2, Hq=4, d=8, cap=14):
+    from oracle import ref
+    rng = np.random.default_rng(seed)
+    S = torch.from_numpy(rng.standard_normal((d, d)).astype(np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+    ks, vs = ref.scheme_sides(scheme, 3)
+    kc = ref.OracleCache(B, Hkv, cap, d, ks, d)
+    vc = ref.OracleCache(B, Hkv, cap, d, vs, d)
+    K = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32) * 2
+    V = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    kc.quantize(K, 0, S)
+    vc.quantize(V, 0, S)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    return rng, S, kc, vc, q
+
+
+@pytest.mark.parametrize("scheme", ["KV", "KQV", "QKQV"])
+def test_attention_window_reductions(orc, scheme):
+    """Full-precision window next to the compressed cache ("Your KV cache is
+    not a bit problem but a geometry problem", "Systems tax", "What we should
+    do", "Frontier"): one softmax over the union of both token sets.  Checked
+    against (1) the cache-only attention of the C oracle when the window is
+    empty, (2) plain numpy attention over the window alone when the cache
+    range is empty, (3) numpy attention over the explicit union (sinks =
+    slots [0, 2) kept exact, compressed middle, exact recent tokens), and
+    (4) invariance under moving reconstructed tokens from the cache range into
+    the window and under permuting the window."""
+    B, Hkv, Hq, d, cap = 2, 2, 4, 8, 14
+    rng, S, kc, vc, q = _window_case(scheme, 31)
+    G = Hq // Hkv
+    # (1)
+    a = orc.attention_window(kc, vc, q, 0, 11, None, None, S)
+    assert np.allclose(a, orc.attention(kc, vc, q, 11, S), rtol=1e-12, atol=1e-13)
+    # (2)
+    wk = rng.standard_normal((B, Hkv, 5, d)).astype(np.float32)
+    wv = rng.standard_normal((B, Hkv, 5, d)).astype(np.float32)
+    a = orc.attention_window(kc, vc, q, 4, 4, wk, wv, S)
+    for b in range(B):
+        for h in range(Hq):
+            want = _np_attention(q[b, h].astype(np.float64), wk[b, h // G].astype(np.float64),
+                                 wv[b, h // G].astype(np.float64))
+            assert np.allclose(a[b, h], want, rtol=1e-12, atol=1e-13)
+    # (3) sinks [0, 2) exact, compressed [2, 9), plus exact recent tokens
+    sk = rng.standard_normal((B, Hkv, 2, d)).astype(np.float32)
+    sv = rng.standard_normal((B, Hkv, 2, d)).astype(np.float32)
+    wk2, wv2 = np.concatenate([sk, wk], 2), np.concatenate([sv, wv], 2)
+    a = orc.attention_window(kc, vc, q, 2, 9, wk2, wv2, S)
+    Kh, Vh = kc.dequantize(2, 7, S), vc.dequantize(2, 7, S)
+    for b in range(B):
+        for h in range(Hq):
+            Ku = np.concatenate([wk2[b, h // G], Kh[b, h // G]]).astype(np.float64)
+            Vu = np.concatenate([wv2[b, h // G], Vh[b, h // G]]).astype(np.float64)
+            want = _np_attention(q[b, h].astype(np.float64), Ku, Vu)
+            assert np.allclose(a[b, h], want, rtol=1e-12, atol=1e-13)
+    # (4) slots [6, 9) moved into the window as their reconstructions
+    Kh3, Vh3 = kc.dequantize(6, 3, S), vc.dequantize(6, 3, S)
+    moved = orc.attention_window(kc, vc, q, 2, 6, np.concatenate([wk2, Kh3], 2),
+                                 np.concatenate([wv2, Vh3], 2), S)
+    assert np.allclose(moved, a, rtol=1e-12, atol=1e-13)
+    perm = rng.permutation(wk2.shape[2])
+    pa = orc.attention_window(kc, vc, q, 2, 9, wk2[:, :, perm], wv2[:, :, perm], S)
+    assert np.allclose(pa, a, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_window_bf16_inputs_widen_exactly(orc):
+    """bf16 bit patterns for q and the window give the same result as their
+    exact fp32 widening (torch's conversion)."""
+    B, Hkv, Hq, d = 2, 2, 4, 8
+    rng, S, kc, vc, q = _window_case("KQV", 33)
+    wk = torch.randn(B, Hkv, 3, d, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    wv = torch.randn(B, Hkv, 3, d, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    qb = torch.from_numpy(q).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    a = orc.attention_window(kc, vc, bits(qb), 1, 10, bits(wk), bits(wv), S)
+    b = orc.attention_window(kc, vc, qb.float().numpy(), 1, 10, wk.float().numpy(),
+                             wv.float().numpy(), S)
+    assert np.array_equal(a, b)
+
+
 def test_quantize_cache_strides_and_offset(orc):
     """Any token stride, cache slots t0..t0+T-1, bf16 widened exactly."""
     B, H, T, d, cap = 2, 3, 5, 16, 9
