@@ -218,6 +218,20 @@ __device__ __forceinline__ uint32_t xor1_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 
+// Sum over each row of 16 lanes, left in every lane of the row (DPP: partner
+// lane ^1, ^2, then the mirrored lane within 8 and within 16).  Depth 4.
+__device__ __forceinline__ float row_sum16(float v) {
+  v = v + xor1_f(v);
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+// Value of lane l (uniform l).
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Codes of DL consecutive coordinates packed at compile-time positions: widths
 // 1, 2, 4 as one little-endian image; width 3 as a 2-bit plane image (DL/16
 // words) followed by a 1-bit plane image (DL/32 words, at least one).
@@ -517,6 +531,11 @@ void quantize_kernel(const QuantArgs a) {
       for (int rt = 0; rt < NRT; ++rt) {
         const int t = rt * 32 + (lane & 31);                  // token row in the tile
         const float rbt = rn_s[t];
+        // B operands (this block's residual rows), read once for all row blocks
+        u32x4 rv[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          rv[ks] = *(const u32x4 *)(stage + t * P2 + (ks * 16 + 8 * (lane >> 5)) * 2);
         uint32_t sgw[NCT];
 #pragma unroll 1
         for (int ct = 0; ct < NCT; ++ct) {
@@ -531,12 +550,11 @@ void quantize_kernel(const QuantArgs a) {
             const int k0 = ks * 16 + 8 * (lane >> 5);
             u32x4 sv = *(const u32x4 *)(S_s + ks_row * P2 + k0 * 2);
             if (!kok) sv = u32x4{0u, 0u, 0u, 0u};
-            const u32x4 rv = *(const u32x4 *)(stage + t * P2 + k0 * 2);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sv),
-                                                          __builtin_bit_cast(bf16x8, rv), acc, 0,
-                                                          0, 0);
+                                                          __builtin_bit_cast(bf16x8, rv[ks]), acc,
+                                                          0, 0, 0);
           }
-          // certified signs; uncertain entries are recomputed in fp64, ascending
+          // certified signs
           const float bound = fmaf(a_snmax, rbt, 0x1p-100f);
           uint32_t bits = 0u, unsure = 0u;
 #pragma unroll
@@ -548,25 +566,57 @@ void quantize_kernel(const QuantArgs a) {
           }
           if constexpr (D < 32) unsure &= (1u << D) - 1u;                 // rows >= D do not exist
           if (t >= nvalid) unsure = 0u;                                    // padding rows of the tile
-          while (unsure) {
-            const int bp = __builtin_ctz(unsure);
-            unsure &= unsure - 1u;
+          // Uncertain entries, one (lane, row) at a time for the whole wave.  The
+          // products s_i r~_i of two bf16 values are exact in fp32 (16-bit
+          // significands; |s r~| >= 2^-126 unless tiny, covered by 2^-110
+          // below).  The lanes sum them in a tree of depth <= 7, so the sum T
+          // is within 7 2^-24 A of the exact sum E (A = sum |s_i r~_i|), and the
+          // oracle's ascending fp64 sum is within 127 2^-53 A of E: beyond
+          // 2^-20 A + 2^-110 the signs of all three agree.  Otherwise (E = 0
+          // included) the ascending fp64 sum itself is formed, by every lane
+          // alike from uniform addresses.
+          uint64_t pend = __ballot(unsure != 0u);
+          while (pend) {
+            const int src = __builtin_ctzll(pend);
+            const uint32_t um = (uint32_t)__builtin_amdgcn_readlane((int)unsure, src);
+            const int bp = __builtin_ctz(um);
             const int k = ct * 32 + bp;
-            const unsigned char *rr = stage + t * P2;
+            const unsigned char *rr = stage + (rt * 32 + (src & 31)) * P2;
             const unsigned char *sr = S_s + k * P2;
-            double sum = 0.0;
-            for (int c = 0; c < D / 8; ++c) {
-              const u32x4 rv = *(const u32x4 *)(rr + c * 16);
-              const u32x4 sw4 = *(const u32x4 *)(sr + c * 16);
-              const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
-              const uint32_t sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-#pragma unroll
-              for (int k2 = 0; k2 < 4; ++k2) {
-                sum = sum + (double)bf16_lo(sw[k2]) * (double)bf16_lo(rw[k2]);
-                sum = sum + (double)bf16_hi(sw[k2]) * (double)bf16_hi(rw[k2]);
+            float ps = 0.0f, pa = 0.0f;
+            if constexpr (D == 128) {
+              const uint32_t sw = *(const uint32_t *)(sr + 4 * lane);
+              const uint32_t rw = *(const uint32_t *)(rr + 4 * lane);
+              const float p0 = bf16_lo(sw) * bf16_lo(rw), p1 = bf16_hi(sw) * bf16_hi(rw);
+              ps = p0 + p1;
+              pa = fabsf(p0) + fabsf(p1);
+            } else {
+              if (lane < D) {
+                const float p = bf16_to_f32(*(const uint16_t *)(sr + 2 * lane)) *
+                                bf16_to_f32(*(const uint16_t *)(rr + 2 * lane));
+                ps = p;
+                pa = fabsf(p);
               }
             }
-            bits = (bits & ~(1u << bp)) | ((sum >= 0.0 ? 1u : 0u) << bp);
+            ps = row_sum16(ps);
+            pa = row_sum16(pa);
+            const float T = (lane_f(ps, 0) + lane_f(ps, 16)) + (lane_f(ps, 32) + lane_f(ps, 48));
+            const float A = (lane_f(pa, 0) + lane_f(pa, 16)) + (lane_f(pa, 32) + lane_f(pa, 48));
+            uint32_t bit;
+            if (fabsf(T) > fmaf(A, 0x1p-20f, 0x1p-110f)) {
+              bit = T > 0.0f ? 1u : 0u;
+            } else {
+              double sum = 0.0;
+              for (int i = 0; i < D; ++i)
+                sum = sum + (double)bf16_to_f32(*(const uint16_t *)(sr + 2 * i)) *
+                                (double)bf16_to_f32(*(const uint16_t *)(rr + 2 * i));
+              bit = sum >= 0.0 ? 1u : 0u;
+            }
+            if (lane == src) {
+              bits = (bits & ~(1u << bp)) | (bit << bp);
+              unsure &= unsure - 1u;
+            }
+            pend = __ballot(unsure != 0u);
           }
           sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
         }

@@ -169,6 +169,32 @@ def test_sign_fixup_rows():
     assert np.all(sg[..., 0] == 0xFF)              # rows 0..7 are zero -> bit 1
 
 
+def test_sign_exact_cancellation():
+    """Sketch rows e_2j - e_2j+1 against residuals whose coordinates 2j and
+    2j+1 are equal: S r~ is exactly zero, neither the MFMA sum nor the lanes'
+    fp32 sum can decide, and the ascending fp64 sum (+0, bit 1) must."""
+    d, B, H, T = 128, 1, 2, 70
+    Hm = torch.tensor([[1.0]])
+    while Hm.shape[0] < d:
+        Hm = torch.cat([torch.cat([Hm, Hm], 1), torch.cat([Hm, -Hm], 1)], 0)
+    g = torch.Generator().manual_seed(91)
+    y = torch.randint(-40, 41, (B, H, T, d // 2), generator=g).double().repeat_interleave(2, -1)
+    x = (y @ Hm.double()) / d                       # WHT of x is y, exactly, in fp32
+    V = x.float()
+    assert torch.equal(V.double(), x)
+    S = synth.sketch_bf16(d, d, 12).clone()
+    for j in range(d // 2):
+        S[j] = 0
+        S[j, 2 * j], S[j, 2 * j + 1] = 1, -1
+    K = synth.gaussian((B, H, T, d), 92, torch.float32)
+    P = Pair("KQV", 4, d, B, H, T, S=S)
+    P.write(K, V, 0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+    sg = P.gpu.view("v_signs").cpu().numpy()
+    assert np.all(sg[..., : d // 16] == 0xFF)      # rows 0..63: z = 0 exactly -> bit 1
+
+
 def test_zero_and_large_vectors():
     B, H, T, d = 1, 1, 40, 128
     K = torch.zeros(B, H, T, d)
