@@ -41,6 +41,9 @@ def main():
     ap.add_argument("--workload", default="llama_gqa_decode")
     ap.add_argument("--scheme", default=None, help="override the workload's scheme")
     ap.add_argument("--bits", type=int, default=None, help="override n bits/coordinate")
+    ap.add_argument("--rotation", default="wht", choices=["wht", "rht", "qr"],
+                    help="rotation of the rotated schemes (Walsh-Hadamard, randomized "
+                         "Hadamard, dense SO(d))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=4, help="(b, KV head) units in the CPU sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gqa_decode_kqv4.md"),
@@ -69,7 +72,11 @@ def main():
 
     K, V, q = synth.make_kvq(w, device=dev)
     S = synth.bits_u16(synth.sketch_bf16(d, d, 7))
-    cache = KVQCache(scheme, n_bits, d, B, Hkv, N, S_bf16=S, device=dev)
+    rot_param = {"wht": None, "rht": synth.rotation_signs(d, 19),
+                 "qr": synth.rotation_qr(d, 19)}[args.rotation]
+    cache = KVQCache(scheme, n_bits, d, B, Hkv, N, S_bf16=S, device=dev, rotation=args.rotation,
+                     rot_signs=rot_param if args.rotation == "rht" else None,
+                     rot_Q=rot_param if args.rotation == "qr" else None)
     c = cache.c
     rec = record_bytes(d, c.k_bits, c.v_bits, c.k_qjl, c.v_qjl)
     in_b = 2 if w.dtype == torch.bfloat16 else 4
@@ -144,7 +151,7 @@ def main():
             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
             "bytes_per_launch": dec_bytes, "per_record_bytes": rec}
-    if args.traffic and os.path.exists(args.traffic):
+    if args.traffic and os.path.exists(args.traffic) and args.rotation == "wht":
         roof["traffic"] = read_traffic(args.traffic, scheme, n_bits, w.name)
 
     result = {
@@ -156,7 +163,7 @@ def main():
         "config": {"workload": w.name, "scheme": scheme, "n_bits": n_bits, "batch": B,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "context": N,
                    "input_dtype": str(w.dtype).replace("torch.", ""), "keys": w.keys,
-                   "splits": splits},
+                   "splits": splits, "rotation": args.rotation},
         "decode": {"us": round(dec_t * 1e6, 2), "GBps": round(dec_gbps, 1),
                    "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
                    "kv_tokens_per_s": round(B * N / dec_t, 1),
@@ -172,7 +179,8 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, scheme, n_bits, K, V, q, S, args.cpu_units, rec)
+        result["cpu_baseline"] = cpu_baseline(w, scheme, n_bits, K, V, q, S, args.cpu_units, rec,
+                                              args.rotation, rot_param)
     print(json.dumps(result), flush=True)
 
 
@@ -202,7 +210,7 @@ def read_traffic(path, scheme, n_bits, workload):
     return blk.get("decode_bytes_per_launch")
 
 
-def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec):
+def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_param=None):
     """The CPU oracle as it stands, on a bounded sample of the same workload:
     `units` (b=0, KV head h) units, full context, all their query heads."""
     import numpy as np
@@ -221,8 +229,9 @@ def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec):
         return synth_bits(x) if x.dtype == torch.bfloat16 else x.numpy()
 
     ks, vs = ref.scheme_sides(scheme, n_bits)
-    ok = ref.OracleCache(1, units, w.N, w.d, ks, w.d)
-    ov = ref.OracleCache(1, units, w.N, w.d, vs, w.d)
+    rot = ref.Rot(rotation, rot_param)
+    ok = ref.OracleCache(1, units, w.N, w.d, ks, w.d, rot)
+    ov = ref.OracleCache(1, units, w.N, w.d, vs, w.d, rot)
     t0 = time.perf_counter()
     ok.quantize(host(Ks), 0, S, cores)
     ov.quantize(host(Vs), 0, S, cores)

@@ -65,6 +65,16 @@ typedef enum {
 typedef enum { KVQ_SCHEME_KV = 0, KVQ_SCHEME_KQV = 1, KVQ_SCHEME_QKQV = 2 } kvq_scheme;
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
+/* Rotation of the rotated schemes (KQV, QKQV); the KV scheme has none.
+ * "KVQuant++" thread, "Entropy coding" (a random QR or Hadamard rotation makes
+ * the coordinates near-Gaussian), "Rotation invariance guarantee" (the QR
+ * rotation is kept in SO(d), determinant +1) and "Rate-distortion
+ * performance" (either rotation stays under the MSE bound).
+ *   KVQ_ROT_WHT : y = H x, H the Sylvester Walsh-Hadamard matrix (default)
+ *   KVQ_ROT_RHT : y = H D x, D = diag(+-1) (randomized Hadamard)
+ *   KVQ_ROT_QR  : y = Q x, Q in SO(d), fp32 */
+typedef enum { KVQ_ROT_WHT = 0, KVQ_ROT_RHT = 1, KVQ_ROT_QR = 2 } kvq_rotation;
+
 /* Scalar codebook for one (d, bits): 2^bits ascending fp32 centroids and the
  * 2^bits - 1 midpoint thresholds (unused entries are zero).  Host POD; it is
  * copied by value into kernel arguments. */
@@ -102,8 +112,9 @@ kvq_status kvq_sketch_init(uint64_t seed, int m, int d, uint16_t *S_bf16_host);
  * little-endian bytes; width 3 -- a 2-bit plane of the low bits (d/4 bytes)
  * followed by a 1-bit plane of the high bits (d/8 bytes).  Sign bit k at byte
  * k/8, bit k%8; bit = 1 means the sketch row is >= 0.  The stored norm is
- * ||x||; the residual norm is ||r|| of the rotated unit direction.
- * Pointers not used by the scheme must be NULL.  All pointers 16-B aligned. */
+ * ||x|| (||y|| for KVQ_ROT_QR); the residual norm is ||r|| of the rotated unit
+ * direction.  Pointers not used by the scheme must be NULL.  All pointers 16-B
+ * aligned.  The rotation fields are set by kvq_cache_set_rotation. */
 typedef struct {
   int32_t scheme, n_bits, d, m, batch, kv_heads, capacity;
   int32_t k_bits, v_bits, k_qjl, v_qjl, rotate;  /* derived by kvq_cache_init */
@@ -111,14 +122,42 @@ typedef struct {
   const uint16_t *S;                             /* device, m*d bf16, NULL if no sketch */
   uint8_t *k_codes, *k_signs, *v_codes, *v_signs;
   uint16_t *k_norm, *k_rnorm, *v_norm, *v_rnorm;
+  int32_t rot_kind;                              /* kvq_rotation (rotated schemes) */
+  uint32_t rot_signs[4];                         /* RHT: bit i%32 of word i/32 = negate x_i */
+  const float *rot_Q;                            /* QR: device, d*d fp32 row-major, else NULL */
 } kvq_cache;
 
 /* Fill the scalar fields and codebooks of `c` for a scheme at n_bits per
  * coordinate (KV: n in 1..4; KQV, QKQV: n in 2..4); leaves the pointers
- * NULL.  Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME, KVQ_ERR_BITS, KVQ_ERR_DIM,
- * KVQ_ERR_RANGE. */
+ * NULL and the rotation at KVQ_ROT_WHT.  Errors: KVQ_ERR_NULL,
+ * KVQ_ERR_SCHEME, KVQ_ERR_BITS, KVQ_ERR_DIM, KVQ_ERR_RANGE. */
 kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch,
                           int kv_heads, int capacity);
+
+/* Choose the rotation of a rotated-scheme cache (before anything is written
+ * to it; codes written under one rotation do not decode under another).
+ * kind KVQ_ROT_WHT: signs and Q ignored.  KVQ_ROT_RHT: signs = host array of
+ * d bits (d/32 words, at least one; bits at and beyond d must be 0).
+ * KVQ_ROT_QR: Q = device pointer to d*d fp32 (row-major, 16-B aligned),
+ * which must stay valid while the cache is used; its orthogonality is the
+ * caller's (see kvq_rotation_qr).
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME (KV scheme, or unknown kind),
+ * KVQ_ERR_ALIGN, KVQ_ERR_RANGE (sign bits beyond d). */
+kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
+                                  const float *Q_device);
+
+/* Random diagonal of KVQ_ROT_RHT: bit i = SplitMix64 stream from `seed`, one
+ * draw per coordinate, its top bit.  Host; out = 4 words (unused bits 0).
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_DIM (d not in {16, 32, 64, 128}). */
+kvq_status kvq_rotation_signs(uint64_t seed, int d, uint32_t out[4]);
+
+/* Random rotation of KVQ_ROT_QR, Haar-distributed on SO(d) ("Rotation
+ * invariance guarantee"): a d x d standard Gaussian matrix (SplitMix64,
+ * Box-Muller, fp64) factored by Householder QR in fp64; Q is scaled column by
+ * column by sign(R_kk) (Haar on O(d)) and its first column is negated when
+ * det Q = -1; the result is rounded to fp32, row-major.  Host; Q_host holds
+ * d*d floats.  Errors: KVQ_ERR_NULL, KVQ_ERR_DIM. */
+kvq_status kvq_rotation_qr(uint64_t seed, int d, float *Q_host);
 
 /* Byte sizes of the eight buffers, in the order k_codes, k_signs, k_norm,
  * k_rnorm, v_codes, v_signs, v_norm, v_rnorm (0 = buffer unused).
@@ -130,7 +169,8 @@ kvq_status kvq_cache_layout(int scheme, int n_bits, int d, int batch, int kv_hea
  * every (b, h) ("Systems tax": per-token append along the token axis).
  * src element (b, h, t, i) is at src + (b*stride_b + h*stride_h + t*stride_t
  * + i) elements of `dtype` (fp32 or bf16); strides are in elements, rows must
- * be 16-B aligned.  Per vector: y = WHT(x) (rotated schemes), nu = ||y||,
+ * be 16-B aligned.  Per vector: y = R x (rotated schemes: the cache's
+ * rotation, see kvq_rotation; y = x for KV), nu = ||y||,
  * u = y/nu, code_i = #{thresholds < u_i} (bucketize), norm = ||x|| in fp16;
  * sketch sides add r = u - C[code], ||r|| in fp16 and sign(S bf16(r)).
  * fp32 arithmetic in a fixed order (ascending butterfly stages, adjacent-pair
@@ -145,8 +185,9 @@ kvq_status kvq_quantize_v(const kvq_cache *c, const void *src, int dtype, int t0
 
 /* Reconstruct slots t0..t0+T-1 of one side (which: 0 = K, 1 = V) into out
  * [B][Hkv][T][d] fp32 (device):
- *   x^ = ||x|| (H/sqrt(d)) (C[code] + sqrt(pi/2)/m ||r|| S^T (2 sigma - 1))
- * (no H for the unrotated scheme, no sketch term for scalar-only sides).
+ *   x^ = ||x|| R^T (C[code] + sqrt(pi/2)/m ||r|| S^T (2 sigma - 1))
+ * with R^T = H/sqrt(d) (WHT), D H/sqrt(d) (randomized Hadamard), Q^T (dense),
+ * I (KV scheme); no sketch term for scalar-only sides.
  * ("KVQuant++" thread, "Deployment and usage": decompress.)
  * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_CAPACITY, KVQ_ERR_RANGE, KVQ_ERR_HIP. */
 kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *out, void *stream);

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
+#include <vector>
 
 #include "kvq_internal.hpp"
 
@@ -83,6 +84,77 @@ uint16_t to_bf16(float f) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Haar-random rotation in SO(d) ("KVQuant++" thread, "Rotation invariance
+// guarantee"): Householder QR of a standard Gaussian matrix G = Q R in fp64
+// (Golub & Van Loan, Householder QR), Q times diag(sign R_kk) (Haar on O(d)),
+// the first column negated when det Q = -1 (each reflector has determinant -1),
+// rounded to fp32.  Q_out row-major.  False if G is numerically singular.
+bool haar_so(uint64_t seed, int d, float *Q_out) {
+  const int n = d;
+  std::vector<double> Ab((size_t)n * n), Vb((size_t)n * n), Qb((size_t)n * n);
+  double *A = Ab.data(), *V = Vb.data(), *Qd = Qb.data();
+  uint64_t state = seed;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < n * n; i += 2) {
+    double u1 = (double)((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+    double u2 = (double)((splitmix64(state) >> 11) + 1) * 0x1.0p-53;
+    double r = std::sqrt(-2.0 * std::log(u1));
+    A[i] = r * std::cos(two_pi * u2);
+    if (i + 1 < n * n) A[i + 1] = r * std::sin(two_pi * u2);
+  }
+  int det_sign = 1;
+  double rdiag_sign[128];
+  for (int k = 0; k < n; ++k) {
+    // reflector v (stored in V[k][k..n-1]) mapping A[k..n-1][k] onto -sign(a_kk) ||.|| e_k
+    double norm = 0.0;
+    for (int i = k; i < n; ++i) norm += A[i * n + k] * A[i * n + k];
+    norm = std::sqrt(norm);
+    if (!(norm > 0.0)) return false;
+    const double akk = A[k * n + k];
+    const double alpha = akk >= 0.0 ? -norm : norm;
+    double vnorm2 = 0.0;
+    for (int i = k; i < n; ++i) {
+      V[k * n + i] = A[i * n + k] - (i == k ? alpha : 0.0);
+      vnorm2 += V[k * n + i] * V[k * n + i];
+    }
+    if (vnorm2 > 0.0) {
+      det_sign = -det_sign;
+      for (int j = k; j < n; ++j) {
+        double dot = 0.0;
+        for (int i = k; i < n; ++i) dot += V[k * n + i] * A[i * n + j];
+        const double f = 2.0 * dot / vnorm2;
+        for (int i = k; i < n; ++i) A[i * n + j] -= f * V[k * n + i];
+      }
+    }
+    rdiag_sign[k] = A[k * n + k] >= 0.0 ? 1.0 : -1.0;
+    // remember the reflector's squared norm in A's (now zero) subdiagonal slot
+    A[k * n + k] = vnorm2;
+  }
+  // Q = H_0 H_1 ... H_{n-1}: apply the reflectors in reverse to the identity
+  for (int i = 0; i < n * n; ++i) Qd[i] = 0.0;
+  for (int i = 0; i < n; ++i) Qd[i * n + i] = 1.0;
+  for (int k = n - 1; k >= 0; --k) {
+    const double vnorm2 = A[k * n + k];
+    if (!(vnorm2 > 0.0)) continue;
+    for (int j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < n; ++i) dot += V[k * n + i] * Qd[i * n + j];
+      const double f = 2.0 * dot / vnorm2;
+      for (int i = k; i < n; ++i) Qd[i * n + j] -= f * V[k * n + i];
+    }
+  }
+  for (int k = 0; k < n; ++k) {
+    if (rdiag_sign[k] < 0.0) {
+      det_sign = -det_sign;
+      for (int i = 0; i < n; ++i) Qd[i * n + k] = -Qd[i * n + k];
+    }
+  }
+  if (det_sign < 0)
+    for (int i = 0; i < n; ++i) Qd[i * n] = -Qd[i * n];
+  for (int i = 0; i < n * n; ++i) Q_out[i] = (float)Qd[i];
+  return true;
+}
+
 struct Sides {
   int kb, vb, kq, vq, rot;
 };
@@ -130,6 +202,20 @@ bool codebook_usable(const kvq_codebook &cb) {
   return true;
 }
 
+// Sign words of the randomized Hadamard rotation: no bits at or beyond d.
+bool signs_fit(const uint32_t *w, int d) {
+  for (int k = 0; k < 4; ++k) {
+    const int lo = 32 * k;
+    const uint32_t allowed = d >= lo + 32 ? 0xFFFFFFFFu : (d <= lo ? 0u : ((1u << (d - lo)) - 1u));
+    if (w[k] & ~allowed) return false;
+  }
+  return true;
+}
+
+// Rotation kind of the codec (RK_*).
+int rot_code(const kvq_cache *c) { return c->rotate ? kvq::RK_WHT + c->rot_kind : kvq::RK_NONE; }
+bool hadamard_kind(int rk) { return rk == kvq::RK_WHT || rk == kvq::RK_RHT; }
+
 // Structural checks shared by every device entry point.
 kvq_status check_cache(const kvq_cache *c) {
   if (!c) return KVQ_ERR_NULL;
@@ -150,8 +236,13 @@ kvq_status check_cache(const kvq_cache *c) {
   if (s.kq && (!c->k_signs || !c->k_rnorm)) return KVQ_ERR_NULL;
   if (s.vq && (!c->v_signs || !c->v_rnorm)) return KVQ_ERR_NULL;
   if ((s.kq || s.vq) && !c->S) return KVQ_ERR_NULL;
+  if (c->rot_kind < KVQ_ROT_WHT || c->rot_kind > KVQ_ROT_QR) return KVQ_ERR_SCHEME;
+  if (!s.rot && c->rot_kind != KVQ_ROT_WHT) return KVQ_ERR_SCHEME;
+  if (c->rot_kind == KVQ_ROT_QR && !c->rot_Q) return KVQ_ERR_NULL;
+  if (c->rot_kind == KVQ_ROT_RHT && !signs_fit(c->rot_signs, c->d)) return KVQ_ERR_RANGE;
   const void *ptrs[] = {c->k_codes, c->k_norm, c->v_codes, c->v_norm, c->k_signs, c->k_rnorm,
-                        c->v_signs, c->v_rnorm, c->S};
+                        c->v_signs, c->v_rnorm, c->S,
+                        c->rot_kind == KVQ_ROT_QR ? (const void *)c->rot_Q : nullptr};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
   return KVQ_OK;
@@ -187,12 +278,15 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
   a.src = src;
   a.sb = sb; a.sh = sh; a.st = st;
   a.B = c->batch; a.H = c->kv_heads; a.T = T; a.t0 = t0; a.cap = c->capacity;
-  const int vt = c->d > 64 ? 32 : 64;  // tokens per quantize tile
+  const int rk = rot_code(c);
+  const int vt = (rk == kvq::RK_QR || c->d <= 64) ? 64 : 32;  // tokens per quantize tile
   a.tiles_per_bh = (T + vt - 1) / vt;
   long long tiles = (long long)a.tiles_per_bh * a.B * a.H;
   if (tiles > (1ll << 31) - 1) return KVQ_ERR_RANGE;
   a.total_tiles = (int)tiles;
-  a.scale = c->rotate ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
+  a.scale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
+  for (int k = 0; k < 4; ++k) a.rsign[k] = c->rot_signs[k];
+  a.Q = c->rot_Q;
   const kvq_codebook &cb = side == 0 ? c->cb_k : c->cb_v;
   for (int i = 0; i < 16; ++i) a.cent[i] = cb.centroid[i];
   for (int i = 0; i < 15; ++i) a.thr[i] = cb.threshold[i];
@@ -205,8 +299,7 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
   const int bits = side == 0 ? c->k_bits : c->v_bits;
   hipStream_t hs = (hipStream_t)stream;
   return hip_status(by_dim(c->d, [&](auto D) {
-    return kvq::launch_quantize<decltype(D)::value>(a, bits, c->rotate != 0, qjl,
-                                                    dtype == KVQ_BF16, hs);
+    return kvq::launch_quantize<decltype(D)::value>(a, bits, rk, qjl, dtype == KVQ_BF16, hs);
   }));
 }
 
@@ -320,6 +413,44 @@ kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch
   return kvq_codebook_init(d, s.vb, &c->cb_v);
 }
 
+kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
+                                  const float *Q_device) {
+  if (!c) return KVQ_ERR_NULL;
+  if (kind < KVQ_ROT_WHT || kind > KVQ_ROT_QR) return KVQ_ERR_SCHEME;
+  if (!c->rotate && kind != KVQ_ROT_WHT) return KVQ_ERR_SCHEME;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (kind == KVQ_ROT_RHT) {
+    if (!signs) return KVQ_ERR_NULL;
+    const int nw = (c->d + 31) / 32;
+    for (int k = 0; k < nw && k < 4; ++k) w[k] = signs[k];
+    if (!signs_fit(w, c->d)) return KVQ_ERR_RANGE;
+  }
+  if (kind == KVQ_ROT_QR) {
+    if (!Q_device) return KVQ_ERR_NULL;
+    if (!aligned16(Q_device)) return KVQ_ERR_ALIGN;
+  }
+  c->rot_kind = kind;
+  for (int k = 0; k < 4; ++k) c->rot_signs[k] = w[k];
+  c->rot_Q = kind == KVQ_ROT_QR ? Q_device : nullptr;
+  return KVQ_OK;
+}
+
+kvq_status kvq_rotation_signs(uint64_t seed, int d, uint32_t out[4]) {
+  if (!out) return KVQ_ERR_NULL;
+  if (!supported_dim(d)) return KVQ_ERR_DIM;
+  uint64_t state = seed;
+  for (int k = 0; k < 4; ++k) out[k] = 0u;
+  for (int i = 0; i < d; ++i)
+    if (splitmix64(state) >> 63) out[i >> 5] |= 1u << (i & 31);
+  return KVQ_OK;
+}
+
+kvq_status kvq_rotation_qr(uint64_t seed, int d, float *Q) {
+  if (!Q) return KVQ_ERR_NULL;
+  if (!supported_dim(d)) return KVQ_ERR_DIM;
+  return haar_so(seed, d, Q) ? KVQ_OK : KVQ_ERR_RANGE;
+}
+
 kvq_status kvq_cache_layout(int scheme, int n_bits, int d, int batch, int kv_heads, int capacity,
                             size_t bytes_out[8]) {
   if (!bytes_out) return KVQ_ERR_NULL;
@@ -373,12 +504,15 @@ kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *o
   const kvq_codebook &cb = k ? c->cb_k : c->cb_v;
   for (int i = 0; i < 16; ++i) a.cent[i] = cb.centroid[i];
   a.coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
-  a.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
+  const int rk = rot_code(c);
+  a.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
+  for (int r = 0; r < 4; ++r) a.rsign[r] = c->rot_signs[r];
+  a.Q = c->rot_Q;
   const int bits = k ? c->k_bits : c->v_bits;
   const bool qjl = k ? c->k_qjl : c->v_qjl;
   hipStream_t hs = (hipStream_t)stream;
   return hip_status(by_dim(c->d, [&](auto D) {
-    return kvq::launch_dequantize<decltype(D)::value>(a, bits, c->rotate != 0, qjl, (int)nvec, hs);
+    return kvq::launch_dequantize<decltype(D)::value>(a, bits, rk, qjl, (int)nvec, hs);
   }));
 }
 
@@ -452,10 +586,12 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = rows;
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
   p.cnt = cnt; p.ncnt = units;
-  p.qscale = c->rotate ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
+  const int rk = rot_code(c);
+  p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
+  for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
+  p.Q = c->rot_Q;
   hipError_t e = by_dim(d, [&](auto D) {
-    return kvq::launch_prep<decltype(D)::value>(p, c->rotate != 0, c->k_qjl != 0,
-                                                q_dtype == KVQ_BF16, hs);
+    return kvq::launch_prep<decltype(D)::value>(p, rk, c->k_qjl != 0, q_dtype == KVQ_BF16, hs);
   });
   if (e != hipSuccess) return KVQ_ERR_HIP;
 
@@ -479,8 +615,10 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   a.wpart = n_win > 0 ? wpart : nullptr;
   a.t0 = t_begin;
   a.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
-  a.oscale = c->rotate ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
-  a.rot = c->rotate != 0;
+  a.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
+  a.rk = rk;
+  for (int k = 0; k < 4; ++k) a.rsign[k] = c->rot_signs[k];
+  a.Q = c->rot_Q;
   for (int i = 0; i < 16; ++i) {
     a.kcent[i] = c->cb_k.centroid[i];
     a.vcent[i] = c->cb_v.centroid[i];

@@ -17,18 +17,24 @@ namespace kvq {
 
 inline int scan_tokens_max(int gt) { return KVQ_SCAN_WBUF_FLOATS / (2 * gt); }
 
+// Rotation applied by the codec (kernel template / argument code):
+// none, Walsh-Hadamard, randomized Hadamard (signs, then WHT), dense Q.
+enum { RK_NONE = 0, RK_WHT = 1, RK_RHT = 2, RK_QR = 3 };
+
 // Quantize-on-write launch description (one side of the cache).
 struct QuantArgs {
   const void *src;
   long long sb, sh, st;      // element strides of the source
   int B, H, T, t0, cap;
   int tiles_per_bh, total_tiles;
-  float scale;               // stored norm = ||y|| * scale (1/sqrt(d) when rotated)
+  float scale;               // stored norm = ||y|| * scale (1/sqrt(d) for the Hadamard kinds)
   float cent[16];
   float thr[15];
   const uint16_t *S;         // m x d bf16 (sketch sides)
   uint8_t *codes, *signs;
   uint16_t *norm, *rnorm;
+  uint32_t rsign[4];         // RK_RHT: coordinate i negated when bit i is set
+  const float *Q;            // RK_QR: d x d row-major
 };
 
 struct DequantArgs {
@@ -39,7 +45,9 @@ struct DequantArgs {
   int H, cap, t0, T;
   float cent[16];
   float coef;                // sqrt(pi/2)/m
-  float oscale;              // 1/sqrt(d) when rotated, else 1
+  float oscale;              // 1/sqrt(d) for the Hadamard kinds, else 1
+  uint32_t rsign[4];         // RK_RHT
+  const float *Q;            // RK_QR
 };
 
 struct PrepArgs {
@@ -49,9 +57,11 @@ struct PrepArgs {
   const uint16_t *S;
   int rows;                  // B * Hq
   int Hq, Hkv, G, GT, HG;    // G = Hq / Hkv query heads per KV head, GT per block, HG = G / GT
-  float qscale;              // log2(e)/d (rotated) or log2(e)/sqrt(d)
+  float qscale;              // log2(e)/d (Hadamard kinds) or log2(e)/sqrt(d)
   unsigned *cnt;             // split arrival counters, zeroed here (B * Hkv * HG)
   int ncnt;
+  uint32_t rsign[4];         // RK_RHT
+  const float *Q;            // RK_QR
 };
 
 struct DecodeArgs {
@@ -65,8 +75,10 @@ struct DecodeArgs {
   float kcent[16], vcent[16];
   float kcoef;               // sqrt(pi/2)/m (K sketch)
   float vcoef;               // sqrt(pi/2)/m (V sketch)
-  float oscale;              // 1/sqrt(d) when rotated, else 1
-  int rot;                   // inverse WHT in the merge
+  float oscale;              // 1/sqrt(d) for the Hadamard kinds, else 1
+  int rk;                    // rotation kind (RK_*), undone in the merge
+  uint32_t rsign[4];         // RK_RHT
+  const float *Q;            // RK_QR
   const float *wpart;        // full-precision window partial [B][Hq][2 + d] or null
   int t0;                    // first cache slot of the scanned range
   int Hkv, Hq, Gtot, HG, cap, n_ctx, splits, tps;
@@ -85,11 +97,11 @@ struct WindowArgs {
 
 
 // Dispatchers: one translation unit per head dimension.
-template <int D> hipError_t launch_quantize(const QuantArgs &a, int bits, bool rot, bool qjl,
+template <int D> hipError_t launch_quantize(const QuantArgs &a, int bits, int rk, bool qjl,
                                             bool bf16, hipStream_t s);
-template <int D> hipError_t launch_dequantize(const DequantArgs &a, int bits, bool rot, bool qjl,
+template <int D> hipError_t launch_dequantize(const DequantArgs &a, int bits, int rk, bool qjl,
                                               int n_vec, hipStream_t s);
-template <int D> hipError_t launch_prep(const PrepArgs &a, bool rot, bool kqjl, bool bf16,
+template <int D> hipError_t launch_prep(const PrepArgs &a, int rk, bool kqjl, bool bf16,
                                         hipStream_t s);
 template <int D> hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq,
                                           int gt, int B, hipStream_t s);

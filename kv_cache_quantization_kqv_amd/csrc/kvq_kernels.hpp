@@ -286,6 +286,174 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Constant-address-space view of a device buffer that every lane reads at the
+// same address (the loads become scalar loads).
+typedef const __attribute__((address_space(4))) float cfloat;
+
+// ---------------------------------------------------------------------------
+// Sketch-side helpers shared by the encoders.  S is staged in LDS with a padded
+// row pitch P2 = 2D + 16 bytes; residual rows r~ (bf16) use the same pitch.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void stage_sketch(unsigned char *S_s, const uint16_t *S, int tid) {
+  constexpr int P2 = D * 2 + 16;
+  for (int i = tid; i < D * (D / 8); i += 256) {     // 16-B chunks of S
+    const int r = i / (D / 8), c = i - r * (D / 8);
+    *(u32x4 *)(S_s + r * P2 + c * 16) = *(const u32x4 *)(S + (size_t)r * D + c * 8);
+  }
+}
+
+// Largest sketch row norm (fp32, rounded up), for the sign-certification bound.
+template <int D>
+__device__ __forceinline__ float sketch_row_norm_max(const unsigned char *S_s, int lane) {
+  constexpr int P2 = D * 2 + 16;
+  constexpr int NCT = (D + 31) / 32;
+  float mx = 0.0f;
+#pragma unroll 1
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = ct * 32 + (lane & 31);
+    float sq = 0.0f;
+    if (col < D) {
+      const uint16_t *sr = (const uint16_t *)(S_s + col * P2);
+      for (int i = 0; i < D; ++i) {
+        const float v = bf16_to_f32(sr[i]);
+        sq = sq + v * v;
+      }
+    }
+    mx = fmaxf(mx, sqrtf(sq) * (1.0f + 0x1p-12f));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  return mx;
+}
+
+// Sign bits of z = S r~ for the residual rows of one wave's tile (NRT blocks of
+// 32 rows at `stage`, pitch P2), written to signs + (slot0 + t) * D/8 for the
+// valid rows t < nvalid.  rn_s[t] holds D 2^-22 (1 + 2^-7) ||r_t||.
+//
+// z^T = S r~^T per 32-token block with v_mfma_f32_32x32x16_bf16: A = S rows
+// (sketch rows k), B = r~ rows (tokens t).  Output register j of lane l is
+// z[k][t] with k = 32 ct + 8 (j/4) + 4 (l/32) + (j%4) and t = l%32, so a lane
+// holds 16 of its token's sign bits per 32-row block and lane l^32 the other
+// 16.  A sign is taken from z when |z| exceeds a bound on the accumulation
+// error of any summation order, D * 2^-22 * ||S_k|| * ||r~|| (+2^-100 for
+// flushed denormals); the rest are settled exactly (below).
+template <int D, int NRT>
+__device__ __forceinline__ void sketch_signs(const unsigned char *stage, const unsigned char *S_s,
+                                             const float *rn_s, float a_snmax, int nvalid,
+                                             size_t slot0, uint8_t *signs_out, int lane) {
+  constexpr int P2 = D * 2 + 16;
+  constexpr int NCT = (D + 31) / 32;
+#pragma unroll 1
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int t = rt * 32 + (lane & 31);                  // token row in the tile
+    const float rbt = rn_s[t];
+    // B operands (this block's residual rows), read once for all row blocks
+    u32x4 rv[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      rv[ks] = *(const u32x4 *)(stage + t * P2 + (ks * 16 + 8 * (lane >> 5)) * 2);
+    uint32_t sgw[NCT];
+#pragma unroll 1
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x16 acc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+      const int krow = ct * 32 + (lane & 31);             // A row of this lane
+      const bool kok = krow < D;
+      const int ks_row = kok ? krow : 0;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int k0 = ks * 16 + 8 * (lane >> 5);
+        u32x4 sv = *(const u32x4 *)(S_s + ks_row * P2 + k0 * 2);
+        if (!kok) sv = u32x4{0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sv),
+                                                      __builtin_bit_cast(bf16x8, rv[ks]), acc,
+                                                      0, 0, 0);
+      }
+      // certified signs
+      const float bound = fmaf(a_snmax, rbt, 0x1p-100f);
+      uint32_t bits = 0u, unsure = 0u;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);   // bit = sketch row % 32
+        const float z = acc[j];
+        bits |= (z > 0.0f ? 1u : 0u) << bp;
+        unsure |= (!(fabsf(z) > bound) ? 1u : 0u) << bp;
+      }
+      if constexpr (D < 32) unsure &= (1u << D) - 1u;                 // rows >= D do not exist
+      if (t >= nvalid) unsure = 0u;                                    // padding rows of the tile
+      // Uncertain entries, one (lane, row) at a time for the whole wave.  The
+      // products s_i r~_i of two bf16 values are exact in fp32 (16-bit
+      // significands; |s r~| >= 2^-126 unless tiny, covered by 2^-110
+      // below).  The lanes sum them in a tree of depth <= 7, so the sum T
+      // is within 7 2^-24 A of the exact sum E (A = sum |s_i r~_i|), and the
+      // oracle's ascending fp64 sum is within 127 2^-53 A of E: beyond
+      // 2^-20 A + 2^-110 the signs of all three agree.  Otherwise (E = 0
+      // included) the ascending fp64 sum itself is formed, by every lane
+      // alike from uniform addresses.
+      uint64_t pend = __ballot(unsure != 0u);
+      while (pend) {
+        const int src = __builtin_ctzll(pend);
+        const uint32_t um = (uint32_t)__builtin_amdgcn_readlane((int)unsure, src);
+        const int bp = __builtin_ctz(um);
+        const int k = ct * 32 + bp;
+        const unsigned char *rr = stage + (rt * 32 + (src & 31)) * P2;
+        const unsigned char *sr = S_s + k * P2;
+        float ps = 0.0f, pa = 0.0f;
+        if constexpr (D == 128) {
+          const uint32_t sw = *(const uint32_t *)(sr + 4 * lane);
+          const uint32_t rw = *(const uint32_t *)(rr + 4 * lane);
+          const float p0 = bf16_lo(sw) * bf16_lo(rw), p1 = bf16_hi(sw) * bf16_hi(rw);
+          ps = p0 + p1;
+          pa = fabsf(p0) + fabsf(p1);
+        } else {
+          if (lane < D) {
+            const float p = bf16_to_f32(*(const uint16_t *)(sr + 2 * lane)) *
+                            bf16_to_f32(*(const uint16_t *)(rr + 2 * lane));
+            ps = p;
+            pa = fabsf(p);
+          }
+        }
+        ps = row_sum16(ps);
+        pa = row_sum16(pa);
+        const float T = (lane_f(ps, 0) + lane_f(ps, 16)) + (lane_f(ps, 32) + lane_f(ps, 48));
+        const float A = (lane_f(pa, 0) + lane_f(pa, 16)) + (lane_f(pa, 32) + lane_f(pa, 48));
+        uint32_t bit;
+        if (fabsf(T) > fmaf(A, 0x1p-20f, 0x1p-110f)) {
+          bit = T > 0.0f ? 1u : 0u;
+        } else {
+          double sum = 0.0;
+          for (int i = 0; i < D; ++i)
+            sum = sum + (double)bf16_to_f32(*(const uint16_t *)(sr + 2 * i)) *
+                            (double)bf16_to_f32(*(const uint16_t *)(rr + 2 * i));
+          bit = sum >= 0.0 ? 1u : 0u;
+        }
+        if (lane == src) {
+          bits = (bits & ~(1u << bp)) | (bit << bp);
+          unsure &= unsure - 1u;
+        }
+        pend = __ballot(unsure != 0u);
+      }
+      sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
+    }
+    const bool tvalid = t < nvalid && lane < 32;
+    if (tvalid) {
+      const size_t tslot = slot0 + (size_t)t;
+      uint8_t *dst = signs_out + tslot * (D / 8);
+      if constexpr (D == 128) {
+        *(u32x4 *)dst = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
+      } else if constexpr (D == 64) {
+        *(u32x2 *)dst = u32x2{sgw[0], sgw[1]};
+      } else if constexpr (D == 32) {
+        *(uint32_t *)dst = sgw[0];
+      } else {
+        *(uint16_t *)dst = (uint16_t)(sgw[0] & 0xFFFFu);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Quantize-on-write.  Blocks of 4 waves share the bucketize tables and (sketch
 // sides) the sketch matrix S, staged once in LDS with a padded row pitch; each
@@ -294,21 +462,18 @@ __device__ __forceinline__ void wave_sync() {
 // lane holding DL = D/LPV consecutive coordinates in registers.  The tile is
 // read with coalesced 16-B loads into a padded LDS stage; the next tile's loads
 // are issued before the current one is processed.
-// Butterfly stages h < DL run in registers; the last stage of a split vector is
-// one exchange with the partner lane (lane ^ 1), and the pairwise sum of
-// squares of a split vector is (left half sum) + (right half sum), which is the
-// root of the same adjacent-pair tree.  Then u = y * (1/nu), bucketize, pack.
-// Sketch sides write the bf16 residual halves back to the stage and form
-// z = S r~ for the tile with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  A
-// sign is taken from z when |z| exceeds a bound on the accumulation error of
-// any summation order, D * 2^-22 * ||S_k|| * ||r~|| (+2^-100 for flushed
-// denormals); otherwise the lane recomputes that row in fp64, ascending, which
-// is the definition.
+// RK: none, Walsh-Hadamard, or randomized Hadamard (coordinate signs flipped
+// first; a flip is exact).  Butterfly stages h < DL run in registers; the last
+// stage of a split vector is one exchange with the partner lane (lane ^ 1),
+// and the pairwise sum of squares of a split vector is (left half sum) + (right
+// half sum), which is the root of the same adjacent-pair tree.  Then
+// u = y * (1/nu), bucketize, pack.  Sketch sides write the bf16 residual
+// halves back to the stage and take the signs of S r~ (sketch_signs).
 // ---------------------------------------------------------------------------
 #ifndef KVQ_QUANT_WPE
 #define KVQ_QUANT_WPE 2  // two waves per SIMD (registers <= 256)
 #endif
-template <int D, int BITS, bool ROT, bool QJL, bool BF16>
+template <int D, int BITS, int RK, bool QJL, bool BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_QUANT_WPE)))
 void quantize_kernel(const QuantArgs a) {
   constexpr int LPV = D > 64 ? 2 : 1;        // lanes per vector
@@ -321,7 +486,6 @@ void quantize_kernel(const QuantArgs a) {
   constexpr int NLD = VT * CPR / 64;         // chunks per lane
   constexpr int RECB = D * BITS / 8;
   constexpr int RECW = (RECB + 3) / 4;
-  constexpr int NCT = (D + 31) / 32;
   constexpr int NRT = VT / 32;
   constexpr int P2 = D * 2 + 16;             // bf16 row pitch (residuals, S)
   constexpr int SBYTES = QJL ? D * P2 : 16;
@@ -338,34 +502,17 @@ void quantize_kernel(const QuantArgs a) {
   const int vrow = lane / LPV;               // token row of this lane in the tile
   const int half = lane % LPV;               // which coordinate half
   build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
-  if constexpr (QJL) {
-    for (int i = tid; i < D * (D / 8); i += 256) {     // 16-B chunks of S
-      const int r = i / (D / 8), c = i - r * (D / 8);
-      *(u32x4 *)(S_s + r * P2 + c * 16) = *(const u32x4 *)(a.S + (size_t)r * D + c * 8);
-    }
-  }
+  if constexpr (QJL) stage_sketch<D>(S_s, a.S, tid);
   __syncthreads();
-
-  // largest sketch row norm (fp32, rounded up), for the sign-certification bound
   float a_snmax = 0.0f;
-  if constexpr (QJL) {
-    float mx = 0.0f;
-#pragma unroll 1
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int col = ct * 32 + (lane & 31);
-      float sq = 0.0f;
-      if (col < D) {
-        const uint16_t *sr = (const uint16_t *)(S_s + col * P2);
-        for (int i = 0; i < D; ++i) {
-          const float v = bf16_to_f32(sr[i]);
-          sq = sq + v * v;
-        }
-      }
-      mx = fmaxf(mx, sqrtf(sq) * (1.0f + 0x1p-12f));
-    }
+  if constexpr (QJL) a_snmax = sketch_row_norm_max<D>(S_s, lane);
+  // randomized Hadamard: this lane's sign words (coordinates half*DL ...)
+  constexpr int NMW = (DL + 31) / 32;
+  uint32_t mw[NMW];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    a_snmax = mx;
+  for (int w = 0; w < NMW; ++w) {
+    mw[w] = 0u;
+    if constexpr (RK == RK_RHT) mw[w] = (LPV == 2 && half) ? a.rsign[NMW + w] : a.rsign[w];
   }
 
   const int tile0 = blockIdx.x * 4 + wave;
@@ -439,7 +586,20 @@ void quantize_kernel(const QuantArgs a) {
       if (next < a.total_tiles) fetch(next);
     }
 
-    if constexpr (ROT) {
+    if constexpr (RK == RK_RHT) {
+      // passed through an asm tied to the tile: otherwise all DL sign masks
+      // are hoisted out of the tile loop and stay live (register spills)
+      uint32_t m[NMW];
+#pragma unroll
+      for (int w = 0; w < NMW; ++w) {
+        m[w] = mw[w];
+        asm("" : "+v"(m[w]) : "v"(tile));
+      }
+#pragma unroll
+      for (int i = 0; i < DL; ++i)
+        y[i] = __uint_as_float(__float_as_uint(y[i]) ^ ((m[i >> 5] << (31 - (i & 31))) & 0x80000000u));
+    }
+    if constexpr (RK != RK_NONE) {
       wht_inplace<DL>(y);
       if constexpr (LPV == 2) {
         // last stage: (y_i, y_{i+DL}) -> (y_i + y_{i+DL}, y_i - y_{i+DL}); the upper
@@ -523,122 +683,177 @@ void quantize_kernel(const QuantArgs a) {
       if (next < a.total_tiles) fetch(next);
       wave_sync();
 
-      // z^T = S r~^T per 32-token block: A = S rows (sketch rows k), B = r~ rows
-      // (tokens t).  Output register j of lane l is z[k][t] with
-      // k = 32 ct + 8 (j/4) + 4 (l/32) + (j%4) and t = l%32, so a lane holds 16
-      // of its token's sign bits per 32-row block and lane l^32 the other 16.
-#pragma unroll 1
-      for (int rt = 0; rt < NRT; ++rt) {
-        const int t = rt * 32 + (lane & 31);                  // token row in the tile
-        const float rbt = rn_s[t];
-        // B operands (this block's residual rows), read once for all row blocks
-        u32x4 rv[D / 16];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          rv[ks] = *(const u32x4 *)(stage + t * P2 + (ks * 16 + 8 * (lane >> 5)) * 2);
-        uint32_t sgw[NCT];
-#pragma unroll 1
-        for (int ct = 0; ct < NCT; ++ct) {
-          f32x16 acc;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-          const int krow = ct * 32 + (lane & 31);             // A row of this lane
-          const bool kok = krow < D;
-          const int ks_row = kok ? krow : 0;
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            const int k0 = ks * 16 + 8 * (lane >> 5);
-            u32x4 sv = *(const u32x4 *)(S_s + ks_row * P2 + k0 * 2);
-            if (!kok) sv = u32x4{0u, 0u, 0u, 0u};
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sv),
-                                                          __builtin_bit_cast(bf16x8, rv[ks]), acc,
-                                                          0, 0, 0);
-          }
-          // certified signs
-          const float bound = fmaf(a_snmax, rbt, 0x1p-100f);
-          uint32_t bits = 0u, unsure = 0u;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);   // bit = sketch row % 32
-            const float z = acc[j];
-            bits |= (z > 0.0f ? 1u : 0u) << bp;
-            unsure |= (!(fabsf(z) > bound) ? 1u : 0u) << bp;
-          }
-          if constexpr (D < 32) unsure &= (1u << D) - 1u;                 // rows >= D do not exist
-          if (t >= nvalid) unsure = 0u;                                    // padding rows of the tile
-          // Uncertain entries, one (lane, row) at a time for the whole wave.  The
-          // products s_i r~_i of two bf16 values are exact in fp32 (16-bit
-          // significands; |s r~| >= 2^-126 unless tiny, covered by 2^-110
-          // below).  The lanes sum them in a tree of depth <= 7, so the sum T
-          // is within 7 2^-24 A of the exact sum E (A = sum |s_i r~_i|), and the
-          // oracle's ascending fp64 sum is within 127 2^-53 A of E: beyond
-          // 2^-20 A + 2^-110 the signs of all three agree.  Otherwise (E = 0
-          // included) the ascending fp64 sum itself is formed, by every lane
-          // alike from uniform addresses.
-          uint64_t pend = __ballot(unsure != 0u);
-          while (pend) {
-            const int src = __builtin_ctzll(pend);
-            const uint32_t um = (uint32_t)__builtin_amdgcn_readlane((int)unsure, src);
-            const int bp = __builtin_ctz(um);
-            const int k = ct * 32 + bp;
-            const unsigned char *rr = stage + (rt * 32 + (src & 31)) * P2;
-            const unsigned char *sr = S_s + k * P2;
-            float ps = 0.0f, pa = 0.0f;
-            if constexpr (D == 128) {
-              const uint32_t sw = *(const uint32_t *)(sr + 4 * lane);
-              const uint32_t rw = *(const uint32_t *)(rr + 4 * lane);
-              const float p0 = bf16_lo(sw) * bf16_lo(rw), p1 = bf16_hi(sw) * bf16_hi(rw);
-              ps = p0 + p1;
-              pa = fabsf(p0) + fabsf(p1);
-            } else {
-              if (lane < D) {
-                const float p = bf16_to_f32(*(const uint16_t *)(sr + 2 * lane)) *
-                                bf16_to_f32(*(const uint16_t *)(rr + 2 * lane));
-                ps = p;
-                pa = fabsf(p);
-              }
-            }
-            ps = row_sum16(ps);
-            pa = row_sum16(pa);
-            const float T = (lane_f(ps, 0) + lane_f(ps, 16)) + (lane_f(ps, 32) + lane_f(ps, 48));
-            const float A = (lane_f(pa, 0) + lane_f(pa, 16)) + (lane_f(pa, 32) + lane_f(pa, 48));
-            uint32_t bit;
-            if (fabsf(T) > fmaf(A, 0x1p-20f, 0x1p-110f)) {
-              bit = T > 0.0f ? 1u : 0u;
-            } else {
-              double sum = 0.0;
-              for (int i = 0; i < D; ++i)
-                sum = sum + (double)bf16_to_f32(*(const uint16_t *)(sr + 2 * i)) *
-                                (double)bf16_to_f32(*(const uint16_t *)(rr + 2 * i));
-              bit = sum >= 0.0 ? 1u : 0u;
-            }
-            if (lane == src) {
-              bits = (bits & ~(1u << bp)) | (bit << bp);
-              unsure &= unsure - 1u;
-            }
-            pend = __ballot(unsure != 0u);
-          }
-          sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
-        }
-        const bool tvalid = t < nvalid && lane < 32;
-        if (tvalid) {
-          const size_t tslot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + t);
-          uint8_t *dst = a.signs + tslot * (D / 8);
-          if constexpr (D == 128) {
-            *(u32x4 *)dst = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
-          } else if constexpr (D == 64) {
-            *(u32x2 *)dst = u32x2{sgw[0], sgw[1]};
-          } else if constexpr (D == 32) {
-            *(uint32_t *)dst = sgw[0];
-          } else {
-            *(uint16_t *)dst = (uint16_t)(sgw[0] & 0xFFFFu);
-          }
-        }
-      }
+      sketch_signs<D, NRT>(stage, S_s, rn_s, a_snmax, nvalid,
+                           (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs, lane);
     }
     wave_sync();
     if (next < a.total_tiles) stash();
     wave_sync();
+  }
+}
+
+// Adjacent-pair tree over a stream of block sums b_0, b_1, ... (blk uniform):
+// lvl[k] holds a pending left subtree of 2^k blocks.  After the last block of
+// a power-of-two count the return value is the root of the same tree that the
+// pairwise sum over all leaves builds.
+__device__ __forceinline__ float tree_push(float (&lvl)[8], float s, int blk) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (!((blk >> k) & 1)) {
+      lvl[k] = s;
+      return s;
+    }
+    s = lvl[k] + s;
+  }
+  return s;
+}
+
+// RB rows of y = Q x: y_i = fma chain over j = 0 .. D-1 ascending from 0.
+template <int D, int RB>
+__device__ __forceinline__ void dense_rows(cfloat *qb, const float *x, float *yb) {
+#pragma unroll
+  for (int ii = 0; ii < RB; ++ii) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < D; ++j) acc = fmaf(qb[ii * D + j], x[j], acc);
+    yb[ii] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantize-on-write with a dense rotation y = Q x (RK_QR; "KVQuant++" thread,
+// "Rotation invariance guarantee").  One lane per vector, 64 vectors per wave
+// tile, x in registers; Q is read with scalar loads (every lane needs the same
+// row at the same time).  y is formed twice, in blocks of 16 rows: first for
+// the norm, then for the codes, so only x stays live.  A block's pairwise sum
+// of squares is a subtree of the adjacent-pair tree and the block sums are
+// combined in that tree's order (tree_push), so nu and rho equal the pairwise
+// sums over the whole vector.  Codes of a block are stored as soon as they are
+// known; sketch sides stage the bf16 residual rows for sketch_signs.
+// ---------------------------------------------------------------------------
+template <int D, int BITS, bool QJL, bool BF16>
+__global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) {
+  constexpr int VT = 64;                     // vectors per wave tile (one per lane)
+  constexpr int RB = 16;                     // rows of y per block
+  constexpr int NB = D / RB;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int RECB = D * BITS / 8;
+  constexpr int P2 = D * 2 + 16;
+  constexpr int SBYTES = QJL ? D * P2 : 16;
+  constexpr int RBYTES = QJL ? VT * P2 : 16;
+  using LC = LocalCodes<RB, BITS>;
+  __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char res_all[4][RBYTES];
+  __shared__ BucketTables bt;
+  __shared__ float rn_all[4][VT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned char *res = res_all[wave];
+  float *rn_s = rn_all[wave];
+  build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
+  if constexpr (QJL) stage_sketch<D>(S_s, a.S, tid);
+  __syncthreads();
+  float a_snmax = 0.0f;
+  if constexpr (QJL) a_snmax = sketch_row_norm_max<D>(S_s, lane);
+  cfloat *Qc = (cfloat *)a.Q;
+
+#pragma unroll 1
+  for (int tile = blockIdx.x * 4 + wave; tile < a.total_tiles; tile += gridDim.x * 4) {
+    const int bh = tile / a.tiles_per_bh;
+    const int tt = tile - bh * a.tiles_per_bh;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int tbase = tt * VT;
+    const int nvalid = min(VT, a.T - tbase);
+    const bool valid = lane < nvalid;
+    float x[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) x[i] = 0.0f;
+    if (valid) {
+      const unsigned char *src = (const unsigned char *)a.src +
+          ((long long)b * a.sb + (long long)h * a.sh + (long long)(tbase + lane) * a.st) * ESZ;
+      if constexpr (BF16) {
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+          const u32x4 v = *(const u32x4 *)(src + c * 16);
+          x[8 * c + 0] = bf16_lo(v.x); x[8 * c + 1] = bf16_hi(v.x);
+          x[8 * c + 2] = bf16_lo(v.y); x[8 * c + 3] = bf16_hi(v.y);
+          x[8 * c + 4] = bf16_lo(v.z); x[8 * c + 5] = bf16_hi(v.z);
+          x[8 * c + 6] = bf16_lo(v.w); x[8 * c + 7] = bf16_hi(v.w);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+          const u32x4 v = *(const u32x4 *)(src + c * 16);
+          x[4 * c + 0] = __uint_as_float(v.x); x[4 * c + 1] = __uint_as_float(v.y);
+          x[4 * c + 2] = __uint_as_float(v.z); x[4 * c + 3] = __uint_as_float(v.w);
+        }
+      }
+    }
+    // pass 1: nu = ||y||
+    float lvl[8] = {}, ss = 0.0f;
+#pragma unroll 1
+    for (int blk = 0; blk < NB; ++blk) {
+      float yb[RB];
+      dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
+      ss = tree_push(lvl, pairwise_sumsq<RB>(yb), blk);
+    }
+    const float nu = sqrtf(ss);
+    const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
+    const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + lane);
+    uint8_t *crec = a.codes + slot * RECB;
+    // pass 2: codes (and residuals)
+    float rl[8] = {}, rs = 0.0f;
+#pragma unroll 1
+    for (int blk = 0; blk < NB; ++blk) {
+      float yb[RB];
+      dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
+      LC lc;
+      lc.clear();
+#pragma unroll
+      for (int ii = 0; ii < RB; ++ii) {
+        const float u = yb[ii] * rcp;
+        const uint32_t code = bucketize_lut<BITS>(u, bt);
+        lc.put(ii, code);
+        if constexpr (QJL) yb[ii] = u - bt.cent[code];
+      }
+      if (valid) {
+        // records are 2-byte aligned: halfword stores
+        if constexpr (BITS == 3) {
+          uint16_t *p2 = (uint16_t *)(crec + blk * 4);          // 2-bit plane: 4 bytes per block
+          p2[0] = (uint16_t)(lc.w[0] & 0xFFFFu);
+          p2[1] = (uint16_t)(lc.w[0] >> 16);
+          *(uint16_t *)(crec + D / 4 + blk * 2) = (uint16_t)(lc.w[LC::NA] & 0xFFFFu);
+        } else {
+          uint16_t *pc = (uint16_t *)(crec + blk * (RB * BITS / 8));
+#pragma unroll
+          for (int k = 0; k < RB * BITS / 16; ++k)
+            pc[k] = (uint16_t)((lc.w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu);
+        }
+      }
+      if constexpr (QJL) {
+        rs = tree_push(rl, pairwise_sumsq<RB>(yb), blk);
+        unsigned char *rrow = res + lane * P2 + blk * RB * 2;
+#pragma unroll
+        for (int c = 0; c < RB / 8; ++c) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f32x2 pr = {yb[8 * c + 2 * k], yb[8 * c + 2 * k + 1]};
+            wv[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+          }
+          *(u32x4 *)(rrow + c * 16) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        }
+      }
+    }
+    if (valid) a.norm[slot] = f32_to_f16_bits(nu * a.scale);
+    if constexpr (QJL) {
+      const float rho = sqrtf(rs);
+      if (valid) a.rnorm[slot] = f32_to_f16_bits(rho);
+      rn_s[lane] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
+      wave_sync();
+      sketch_signs<D, VT / 32>(res, S_s, rn_s, a_snmax, nvalid,
+                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs, lane);
+      wave_sync();
+    }
   }
 }
 
@@ -670,11 +885,20 @@ __device__ __forceinline__ float wht_block(float *t_s, float x) {
   return t_s[i];
 }
 
+// Coordinate i of R^T t for the dense rotation, t in LDS (all D threads).
+template <int D>
+__device__ __forceinline__ float dense_rotate_back(const float *Q, const float *t_s, int i) {
+  float acc = 0.0f;
+  for (int j = 0; j < D; ++j) acc = fmaf(Q[(size_t)j * D + i], t_s[j], acc);
+  return acc;
+}
+
 // ---------------------------------------------------------------------------
 // Dequantize (parity aid): one block of D threads per record.
-//   x^ = ||x|| (H/sqrt(d)) (C[code] + sqrt(pi/2)/m ||r|| S^T (2 sigma - 1))
+//   x^ = ||x|| R^T (C[code] + sqrt(pi/2)/m ||r|| S^T (2 sigma - 1))
+// with R^T = H/sqrt(d) (WHT), D H/sqrt(d) (randomized Hadamard), Q^T, or I.
 // ---------------------------------------------------------------------------
-template <int D, int BITS, bool ROT, bool QJL>
+template <int D, int BITS, int RK, bool QJL>
 __global__ __launch_bounds__(D) void dequant_kernel(const DequantArgs a) {
   __shared__ float t_s[D];
   __shared__ float sg_s[D];
@@ -690,25 +914,41 @@ __global__ __launch_bounds__(D) void dequant_kernel(const DequantArgs a) {
     for (int k = 0; k < D; ++k) acc = acc + bf16_to_f32(a.S[(size_t)k * D + i]) * sg_s[k];
     val = val + a.coef * f16_bits_to_f32(a.rnorm[slot]) * acc;
   }
-  if constexpr (ROT) val = wht_block<D>(t_s, val) * a.oscale;
+  if constexpr (RK == RK_WHT || RK == RK_RHT) val = wht_block<D>(t_s, val) * a.oscale;
+  if constexpr (RK == RK_RHT) val = ((a.rsign[i >> 5] >> (i & 31)) & 1u) ? -val : val;
+  if constexpr (RK == RK_QR) {
+    t_s[i] = val;
+    __syncthreads();
+    val = dense_rotate_back<D>(a.Q, t_s, i);
+  }
   a.out[((size_t)bh * a.T + t) * D + i] = f16_bits_to_f32(a.norm[slot]) * val;
 }
 
 // ---------------------------------------------------------------------------
-// Query preparation, one block per query row: q' = H q * log2(e)/d (rotated
-// schemes) or q * log2(e)/sqrt(d), and for sketched keys S q'.  Rotating q once
-// replaces rotating every key (H is symmetric and H H = d I); log2(e) lets the
-// scan use exp2.  Output layout [b][h_kv][head group][coordinate][GT] puts the
-// GT heads of one coordinate side by side, so the scan reads them with scalar
-// loads.
+// Query preparation, one block per query row: q' = R q * log2(e)/sqrt(d) with
+// the cache's rotation R (q' = H q * log2(e)/d for the WHT, H (D q) for the
+// randomized Hadamard, Q q for the dense rotation, q unrotated), and for
+// sketched keys S q'.  Rotating q once replaces rotating every key back
+// (q . R^T y = (R q) . y); log2(e) lets the scan use exp2.  Output layout
+// [b][h_kv][head group][coordinate][GT] puts the GT heads of one coordinate
+// side by side, so the scan reads them with scalar loads.
 // ---------------------------------------------------------------------------
-template <int D, bool ROT, bool KQ, bool BF16>
+template <int D, int RK, bool KQ, bool BF16>
 __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
   __shared__ float t_s[D];
   const int row = blockIdx.x, i = threadIdx.x;
   float x = BF16 ? bf16_to_f32(((const uint16_t *)a.q)[(size_t)row * D + i])
                  : ((const float *)a.q)[(size_t)row * D + i];
-  if constexpr (ROT) x = wht_block<D>(t_s, x);
+  if constexpr (RK == RK_RHT) x = ((a.rsign[i >> 5] >> (i & 31)) & 1u) ? -x : x;
+  if constexpr (RK == RK_WHT || RK == RK_RHT) x = wht_block<D>(t_s, x);
+  if constexpr (RK == RK_QR) {
+    t_s[i] = x;
+    __syncthreads();
+    float acc = 0.0f;
+    for (int j = 0; j < D; ++j) acc = fmaf(a.Q[(size_t)i * D + j], t_s[j], acc);
+    x = acc;
+    __syncthreads();
+  }
   x = x * a.qscale;
   const int b = row / a.Hq, hq = row - b * a.Hq;
   const int hkv = hq / a.G, within = hq - hkv * a.G;
@@ -891,7 +1131,6 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
-typedef const __attribute__((address_space(4))) float cfloat;
 
 // An empty asm the value passes through: the compiler cannot fold the masks
 // that built it into each later byte extract (which would cost two
@@ -995,7 +1234,7 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
     wv[hh * D + i] = v;
   }
   __syncthreads();
-  if (a.rot) {
+  if (a.rk == RK_WHT || a.rk == RK_RHT) {
     for (int h = 1; h < D; h <<= 1) {
       for (int pi = tid; pi < GT * D / 2; pi += 256) {
         const int hh = pi / (D / 2), r = pi - hh * (D / 2);
@@ -1013,6 +1252,8 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
     const int hh = item / D, i = item - hh * D;
     const size_t row = (size_t)b * a.Hq + hq0 + hh;
     float num = wv[hh * D + i] * a.oscale, den = res[hh * NS + 1];
+    if (a.rk == RK_RHT && ((a.rsign[i >> 5] >> (i & 31)) & 1u)) num = -num;
+    if (a.rk == RK_QR) num = dense_rotate_back<D>(a.Q, wv + hh * D, i);
     if (a.wpart) {
       const float *wp = a.wpart + row * (2 + D);
       const float mc = mx[hh], mu = wp[0];
@@ -1552,88 +1793,129 @@ __global__ __launch_bounds__(256) void window_kernel(const WindowArgs a) {
 // Dispatchers (host).  Only the (bits, rotation, sketch) combinations that the
 // three schemes produce are instantiated.
 // ---------------------------------------------------------------------------
-template <int D, int BITS, bool ROT, bool QJL>
+template <int D, int BITS, int RK, bool QJL>
 hipError_t quantize_go(const QuantArgs &a, bool bf16, hipStream_t s) {
   // persistent-style grid: each wave walks tiles with a stride of 4 * grid
   const int want = (a.total_tiles + 3) / 4;
   const int grid = want < 2048 ? want : 2048;
-  if (bf16)
-    hipLaunchKernelGGL((quantize_kernel<D, BITS, ROT, QJL, true>), dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((quantize_kernel<D, BITS, ROT, QJL, false>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_quantize(const QuantArgs &a, int bits, bool rot, bool qjl, bool bf16,
-                           hipStream_t s) {
-  if (!rot && !qjl) {
-    switch (bits) {
-      case 1: return quantize_go<D, 1, false, false>(a, bf16, s);
-      case 2: return quantize_go<D, 2, false, false>(a, bf16, s);
-      case 3: return quantize_go<D, 3, false, false>(a, bf16, s);
-      case 4: return quantize_go<D, 4, false, false>(a, bf16, s);
-    }
-  } else if (rot && !qjl) {
-    switch (bits) {
-      case 2: return quantize_go<D, 2, true, false>(a, bf16, s);
-      case 3: return quantize_go<D, 3, true, false>(a, bf16, s);
-      case 4: return quantize_go<D, 4, true, false>(a, bf16, s);
-    }
-  } else if (rot && qjl) {
-    switch (bits) {
-      case 1: return quantize_go<D, 1, true, true>(a, bf16, s);
-      case 2: return quantize_go<D, 2, true, true>(a, bf16, s);
-      case 3: return quantize_go<D, 3, true, true>(a, bf16, s);
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int D, int BITS, bool ROT, bool QJL>
-hipError_t dequant_go(const DequantArgs &a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((dequant_kernel<D, BITS, ROT, QJL>), dim3(n), dim3(D), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_dequantize(const DequantArgs &a, int bits, bool rot, bool qjl, int n,
-                             hipStream_t s) {
-  if (!rot && !qjl) {
-    switch (bits) {
-      case 1: return dequant_go<D, 1, false, false>(a, n, s);
-      case 2: return dequant_go<D, 2, false, false>(a, n, s);
-      case 3: return dequant_go<D, 3, false, false>(a, n, s);
-      case 4: return dequant_go<D, 4, false, false>(a, n, s);
-    }
-  } else if (rot && !qjl) {
-    switch (bits) {
-      case 2: return dequant_go<D, 2, true, false>(a, n, s);
-      case 3: return dequant_go<D, 3, true, false>(a, n, s);
-      case 4: return dequant_go<D, 4, true, false>(a, n, s);
-    }
-  } else if (rot && qjl) {
-    switch (bits) {
-      case 1: return dequant_go<D, 1, true, true>(a, n, s);
-      case 2: return dequant_go<D, 2, true, true>(a, n, s);
-      case 3: return dequant_go<D, 3, true, true>(a, n, s);
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int D>
-hipError_t launch_prep(const PrepArgs &a, bool rot, bool kq, bool bf16, hipStream_t s) {
-  const dim3 g(a.rows), blk(D);
-#define KVQ_PREP(R, K, B) hipLaunchKernelGGL((prep_kernel<D, R, K, B>), g, blk, 0, s, a)
-  if (rot) {
-    if (kq) { if (bf16) KVQ_PREP(true, true, true); else KVQ_PREP(true, true, false); }
-    else { if (bf16) KVQ_PREP(true, false, true); else KVQ_PREP(true, false, false); }
+  if constexpr (RK == RK_QR) {
+    if (bf16)
+      hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, false>), dim3(grid), dim3(256), 0, s, a);
   } else {
-    if (bf16) KVQ_PREP(false, false, true); else KVQ_PREP(false, false, false);
+    if (bf16)
+      hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, false>), dim3(grid), dim3(256), 0, s, a);
   }
-#undef KVQ_PREP
   return hipGetLastError();
+}
+
+template <int D, int RK>
+hipError_t quantize_rot(const QuantArgs &a, int bits, bool qjl, bool bf16, hipStream_t s) {
+  if (!qjl) {
+    switch (bits) {
+      case 2: return quantize_go<D, 2, RK, false>(a, bf16, s);
+      case 3: return quantize_go<D, 3, RK, false>(a, bf16, s);
+      case 4: return quantize_go<D, 4, RK, false>(a, bf16, s);
+    }
+  } else {
+    switch (bits) {
+      case 1: return quantize_go<D, 1, RK, true>(a, bf16, s);
+      case 2: return quantize_go<D, 2, RK, true>(a, bf16, s);
+      case 3: return quantize_go<D, 3, RK, true>(a, bf16, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_quantize(const QuantArgs &a, int bits, int rk, bool qjl, bool bf16,
+                           hipStream_t s) {
+  switch (rk) {
+    case RK_NONE:
+      if (qjl) return hipErrorInvalidValue;
+      switch (bits) {
+        case 1: return quantize_go<D, 1, RK_NONE, false>(a, bf16, s);
+        case 2: return quantize_go<D, 2, RK_NONE, false>(a, bf16, s);
+        case 3: return quantize_go<D, 3, RK_NONE, false>(a, bf16, s);
+        case 4: return quantize_go<D, 4, RK_NONE, false>(a, bf16, s);
+      }
+      return hipErrorInvalidValue;
+    case RK_WHT: return quantize_rot<D, RK_WHT>(a, bits, qjl, bf16, s);
+    case RK_RHT: return quantize_rot<D, RK_RHT>(a, bits, qjl, bf16, s);
+    case RK_QR: return quantize_rot<D, RK_QR>(a, bits, qjl, bf16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, int BITS, int RK, bool QJL>
+hipError_t dequant_go(const DequantArgs &a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((dequant_kernel<D, BITS, RK, QJL>), dim3(n), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int RK>
+hipError_t dequant_rot(const DequantArgs &a, int bits, bool qjl, int n, hipStream_t s) {
+  if (!qjl) {
+    switch (bits) {
+      case 2: return dequant_go<D, 2, RK, false>(a, n, s);
+      case 3: return dequant_go<D, 3, RK, false>(a, n, s);
+      case 4: return dequant_go<D, 4, RK, false>(a, n, s);
+    }
+  } else {
+    switch (bits) {
+      case 1: return dequant_go<D, 1, RK, true>(a, n, s);
+      case 2: return dequant_go<D, 2, RK, true>(a, n, s);
+      case 3: return dequant_go<D, 3, RK, true>(a, n, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_dequantize(const DequantArgs &a, int bits, int rk, bool qjl, int n,
+                             hipStream_t s) {
+  switch (rk) {
+    case RK_NONE:
+      if (qjl) return hipErrorInvalidValue;
+      switch (bits) {
+        case 1: return dequant_go<D, 1, RK_NONE, false>(a, n, s);
+        case 2: return dequant_go<D, 2, RK_NONE, false>(a, n, s);
+        case 3: return dequant_go<D, 3, RK_NONE, false>(a, n, s);
+        case 4: return dequant_go<D, 4, RK_NONE, false>(a, n, s);
+      }
+      return hipErrorInvalidValue;
+    case RK_WHT: return dequant_rot<D, RK_WHT>(a, bits, qjl, n, s);
+    case RK_RHT: return dequant_rot<D, RK_RHT>(a, bits, qjl, n, s);
+    case RK_QR: return dequant_rot<D, RK_QR>(a, bits, qjl, n, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, int RK>
+hipError_t prep_go(const PrepArgs &a, bool kq, bool bf16, hipStream_t s) {
+  const dim3 g(a.rows), blk(D);
+  if (kq) {
+    if (bf16) hipLaunchKernelGGL((prep_kernel<D, RK, true, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((prep_kernel<D, RK, true, false>), g, blk, 0, s, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((prep_kernel<D, RK, false, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((prep_kernel<D, RK, false, false>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prep(const PrepArgs &a, int rk, bool kq, bool bf16, hipStream_t s) {
+  switch (rk) {
+    case RK_NONE: return kq ? hipErrorInvalidValue : prep_go<D, RK_NONE>(a, false, bf16, s);
+    case RK_WHT: return prep_go<D, RK_WHT>(a, kq, bf16, s);
+    case RK_RHT: return prep_go<D, RK_RHT>(a, kq, bf16, s);
+    case RK_QR: return prep_go<D, RK_QR>(a, kq, bf16, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
@@ -1688,10 +1970,10 @@ hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows
 }
 
 #define KVQ_INSTANTIATE(D)                                                                     \
-  template hipError_t launch_quantize<D>(const QuantArgs &, int, bool, bool, bool, hipStream_t); \
-  template hipError_t launch_dequantize<D>(const DequantArgs &, int, bool, bool, int,           \
+  template hipError_t launch_quantize<D>(const QuantArgs &, int, int, bool, bool, hipStream_t); \
+  template hipError_t launch_dequantize<D>(const DequantArgs &, int, int, bool, int,            \
                                            hipStream_t);                                        \
-  template hipError_t launch_prep<D>(const PrepArgs &, bool, bool, bool, hipStream_t);          \
+  template hipError_t launch_prep<D>(const PrepArgs &, int, bool, bool, hipStream_t);           \
   template hipError_t launch_decode<D>(const DecodeArgs &, int, bool, int, bool, int, int,      \
                                        hipStream_t);                                            \
   template hipError_t launch_window<D>(const WindowArgs &, bool, bool, int, hipStream_t);

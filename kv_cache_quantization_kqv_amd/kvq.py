@@ -21,11 +21,14 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_ALIGN", 3: "KVQ_ERR_
                 7: "KVQ_ERR_WORKSPACE", 8: "KVQ_ERR_DTYPE", 9: "KVQ_ERR_HEADS",
                 10: "KVQ_ERR_RANGE", 11: "KVQ_ERR_HIP"}
 SCHEMES = {"KV": 0, "KQV": 1, "QKQV": 2}
+ROTATIONS = {"wht": 0, "rht": 1, "qr": 2}
 KVQ_F32, KVQ_BF16 = 0, 1
 
-EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_layout",
-           "kvq_quantize_k", "kvq_quantize_v", "kvq_dequantize", "kvq_decode_attention",
-           "kvq_decode_attention_window", "kvq_decode_workspace", "kvq_decode_auto_splits", "kvq_status_str", "kvq_version"]
+EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_set_rotation",
+           "kvq_rotation_signs", "kvq_rotation_qr", "kvq_cache_layout", "kvq_quantize_k",
+           "kvq_quantize_v", "kvq_dequantize", "kvq_decode_attention",
+           "kvq_decode_attention_window", "kvq_decode_workspace", "kvq_decode_auto_splits",
+           "kvq_status_str", "kvq_version"]
 
 
 class KVQError(RuntimeError):
@@ -49,7 +52,9 @@ class kvq_cache(C.Structure):
                 ("k_codes", C.c_void_p), ("k_signs", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_signs", C.c_void_p),
                 ("k_norm", C.c_void_p), ("k_rnorm", C.c_void_p),
-                ("v_norm", C.c_void_p), ("v_rnorm", C.c_void_p)]
+                ("v_norm", C.c_void_p), ("v_rnorm", C.c_void_p),
+                ("rot_kind", C.c_int32), ("rot_signs", C.c_uint32 * 4),
+                ("rot_Q", C.c_void_p)]
 
 
 _LIB = None
@@ -68,6 +73,9 @@ def lib():
             "kvq_codebook_init": ([i32, i32, cb_p], i32),
             "kvq_sketch_init": ([C.c_uint64, i32, i32, vp], i32),
             "kvq_cache_init": ([cache_p, i32, i32, i32, i32, i32, i32], i32),
+            "kvq_cache_set_rotation": ([cache_p, i32, vp, vp], i32),
+            "kvq_rotation_signs": ([C.c_uint64, i32, vp], i32),
+            "kvq_rotation_qr": ([C.c_uint64, i32, vp], i32),
             "kvq_cache_layout": ([i32, i32, i32, i32, i32, i32, C.POINTER(sz)], i32),
             "kvq_quantize_k": ([cache_p, vp, i32, i32, i32, i64, i64, i64, vp], i32),
             "kvq_quantize_v": ([cache_p, vp, i32, i32, i32, i64, i64, i64, vp], i32),
@@ -116,6 +124,27 @@ def kvq_cache_init(scheme: int, n_bits: int, d: int, batch: int, kv_heads: int,
     _check(lib().kvq_cache_init(C.byref(c), scheme, n_bits, d, batch, kv_heads, capacity),
            "kvq_cache_init")
     return c
+
+
+def kvq_rotation_signs(seed: int, d: int) -> np.ndarray:
+    out = np.zeros(4, np.uint32)
+    _check(lib().kvq_rotation_signs(seed, d, out.ctypes.data), "kvq_rotation_signs")
+    return out
+
+
+def kvq_rotation_qr(seed: int, d: int) -> np.ndarray:
+    out = np.zeros((d, d), np.float32)
+    _check(lib().kvq_rotation_qr(seed, d, out.ctypes.data), "kvq_rotation_qr")
+    return out
+
+
+def kvq_cache_set_rotation(c: kvq_cache, kind: int, signs=None, Q_device: int = 0):
+    sp = None
+    if signs is not None:
+        signs = np.ascontiguousarray(signs, dtype=np.uint32)
+        sp = signs.ctypes.data
+    _check(lib().kvq_cache_set_rotation(C.byref(c), kind, sp, Q_device or None),
+           "kvq_cache_set_rotation")
 
 
 def kvq_cache_layout(scheme: int, n_bits: int, d: int, batch: int, kv_heads: int,
@@ -180,7 +209,11 @@ class KVQCache:
     BUFS = ["k_codes", "k_signs", "k_norm", "k_rnorm", "v_codes", "v_signs", "v_norm", "v_rnorm"]
 
     def __init__(self, scheme: str, n_bits: int, d: int, batch: int, kv_heads: int,
-                 capacity: int, S_bf16=None, device="cuda"):
+                 capacity: int, S_bf16=None, device="cuda", rotation: str = "wht",
+                 rot_signs=None, rot_Q=None, rot_seed: int = 11):
+        """rotation (rotated schemes): "wht", "rht" (rot_signs: 4 uint32 words,
+        default kvq_rotation_signs(rot_seed)) or "qr" (rot_Q: d x d fp32,
+        default kvq_rotation_qr(rot_seed))."""
         import torch
         self.torch = torch
         self.scheme, self.n_bits, self.d = scheme, n_bits, d
@@ -207,6 +240,15 @@ class KVQCache:
             S_np = np.ascontiguousarray(np.asarray(S_bf16).view(np.uint16))
             self.S = torch.from_numpy(S_np.view(np.int16)).to(self.device)
             self.c.S = self.S.data_ptr()
+        self.rotation, self.rot_Q = rotation, None
+        kind = ROTATIONS[rotation]
+        if kind == 1:
+            signs = kvq_rotation_signs(rot_seed, d) if rot_signs is None else rot_signs
+            kvq_cache_set_rotation(self.c, kind, signs=signs)
+        elif kind == 2:
+            Q = kvq_rotation_qr(rot_seed, d) if rot_Q is None else np.asarray(rot_Q, np.float32)
+            self.rot_Q = torch.from_numpy(np.ascontiguousarray(Q)).to(self.device)
+            kvq_cache_set_rotation(self.c, kind, Q_device=self.rot_Q.data_ptr())
 
     # views of the raw buffers in their documented shapes
     def view(self, name: str):

@@ -24,6 +24,10 @@ Key distributions (synthetic, seeded): Gaussian; heavy-tailed (per-channel
 scales |t_nu|, outliers in fixed channels); low-rank (rank 8 plus 0.1 noise);
 focused (each query aimed at one cached key, so the softmax is peaked).
 Values are Gaussian.  The reference attention uses the exact keys and values.
+
+rotation_mse compares the rotations of the rotated schemes ("KVQuant++"
+thread, "Rate-distortion performance": with the QR or the Hadamard rotation
+the per-element MSE stays under sqrt(3 pi/2) 4^-b).
 """
 from __future__ import annotations
 
@@ -115,10 +119,13 @@ def _dir_err(x, xh):
     return float((1.0 - c).mean())
 
 
-def roundtrip(scheme: str, n_bits: int, K: torch.Tensor, V: torch.Tensor, S_bf16, device):
+def roundtrip(scheme: str, n_bits: int, K: torch.Tensor, V: torch.Tensor, S_bf16, device,
+              rotation: str = "wht", rot_param=None):
     """Quantize K and V ([H][N][d] fp32) with the GPU codec and reconstruct them."""
     H, N, d = K.shape
-    cache = KVQCache(scheme, n_bits, d, 1, H, N, S_bf16=S_bf16, device=device)
+    cache = KVQCache(scheme, n_bits, d, 1, H, N, S_bf16=S_bf16, device=device, rotation=rotation,
+                     rot_signs=rot_param if rotation == "rht" else None,
+                     rot_Q=rot_param if rotation == "qr" else None)
     cache.quantize_k(K[None].to(device), 0)
     cache.quantize_v(V[None].to(device), 0)
     Kh = cache.dequantize(0, 0, N)[0]
@@ -146,6 +153,28 @@ def evaluate(scheme, n_bits, keys_kind, K, V, q, S_bf16, device) -> Metrics:
     return Metrics(scheme, n_bits, keys_kind, _snr_db(Kd, Kh), _dir_err(Kd, Kh), _snr_db(Vd, Vh),
                    _dir_err(Vd, Vh), _snr_db(o, oh), _dir_err(o, oh), float(kl), float(rec),
                    float((sh - s).var()), _proj(Kd, Kh), _proj(Vd, Vh))
+
+
+def rotation_mse(kind: str, bits: int, rotation: str, H=4, N=1024, d=128, seed=2025,
+                 device="cuda"):
+    """Per-element MSE of unit key directions through the K side of KQV at n =
+    bits (n-bit scalar codec after the rotation), for a key family: the pages'
+    families plus "hadamard" (rows of the normalised Hadamard matrix, each a
+    single spike after the plain WHT).  Returns mean ||x - x^||^2 / d."""
+    if kind == "hadamard":
+        Hm = torch.tensor([[1.0]])
+        while Hm.shape[0] < d:
+            Hm = torch.cat([torch.cat([Hm, Hm], 1), torch.cat([Hm, -Hm], 1)], 0)
+        Hm = Hm / math.sqrt(d)
+        K = Hm[torch.arange(H * N) % d].reshape(H, N, d)
+    else:
+        K = make_keys(kind, H, N, d, seed)
+    K = K / K.norm(dim=-1, keepdim=True)
+    param = {"wht": None, "rht": synth.rotation_signs(d, seed + 1),
+             "qr": synth.rotation_qr(d, seed + 2)}[rotation]
+    S = synth.bits_u16(synth.sketch_bf16(d, d, 7))
+    Kh, _ = roundtrip("KQV", bits, K, K, S, device, rotation, param)
+    return float((Kh.float().cpu() - K).pow(2).sum(-1).mean() / d)
 
 
 def grid(keys_kinds=("gaussian", "heavytail", "lowrank", "focused"), bits=(2, 3, 4), H=8, N=2048,

@@ -9,7 +9,8 @@ low-rank keys), and the per-channel outlier structure of real key caches
 live in fixed channels").  No dataset or trained weight is involved.
 
 The sketch matrix S (the random numbers the QJL sketch draws) is also an input:
-iid N(0,1), rounded to bfloat16, row-major [m][d].
+iid N(0,1), rounded to bfloat16, row-major [m][d]; so are the random rotations
+(the sign diagonal of a randomized Hadamard transform, a Haar rotation in SO(d)).
 """
 from __future__ import annotations
 
@@ -52,6 +53,31 @@ def lowrank_heavytail_keys(B, H, N, d, seed: int, rank: int = 8, noise: float = 
 def sketch_bf16(m: int, d: int, seed: int = 7) -> torch.Tensor:
     """Gaussian sketch S [m][d], iid N(0,1) rounded to bf16 (CPU tensor)."""
     return gaussian((m, d), seed, torch.bfloat16, "cpu")
+
+
+def rotation_signs(d: int, seed: int = 13):
+    """Random diagonal of the randomized Hadamard rotation: d fair coin flips
+    as 4 little-endian uint32 words (bit i set: coordinate i negated)."""
+    import numpy as np
+    g = _gen(seed, "cpu")
+    bits = torch.randint(0, 2, (d,), generator=g).numpy().astype(np.uint64)
+    w = np.zeros(4, np.uint32)
+    for i in range(d):
+        w[i // 32] |= np.uint32(int(bits[i]) << (i % 32))
+    return w
+
+
+def rotation_qr(d: int, seed: int = 17):
+    """A random rotation in SO(d) as fp32 [d][d]: QR of a Gaussian matrix
+    (LAPACK via torch, fp64), columns scaled by sign(R_kk), first column
+    negated when the determinant is -1, rounded to fp32."""
+    g = _gen(seed, "cpu")
+    A = torch.randn(d, d, generator=g, dtype=torch.float64)
+    Q, R = torch.linalg.qr(A)
+    Q = Q * torch.sign(torch.diagonal(R))[None, :]
+    if torch.linalg.det(Q) < 0:
+        Q[:, 0] = -Q[:, 0]
+    return Q.to(torch.float32).numpy()
 
 
 def bits_u16(t: torch.Tensor):

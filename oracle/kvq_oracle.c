@@ -227,18 +227,43 @@ static int get_code(const uint8_t *rec, int d, int bits, int i) {
   return (rec[(i * bits) / 8] >> ((i * bits) % 8)) & ((1 << bits) - 1);
 }
 
-/* [DA] "Quantization schemes" / "Problem statement": rotate (WHT), scalar
- * Lloyd-Max quantise the direction, keep the norm; QJL modes add the 1-bit
- * sketch sign(S r) of the scalar residual r and its norm ([DA] Contribution 1).
- *  1. y = H x (skipped when rotate == 0)
+/* Forward rotation y = R x in fp32 (kinds: see the header).  WHT and
+ * randomized Hadamard: sign flips (exact) then the butterflies above.  Dense:
+ * y_i = fma chain over j ascending from 0 ([KPP] "Rotation invariance
+ * guarantee": Q is a rotation in SO(d); the order of the chain is this
+ * library's reading, the pages give none). */
+static void rotate_fwd(float *y, const float *x, int d, int rotate, const void *rparam) {
+  if (rotate == 3) {
+    const float *Q = (const float *)rparam;
+    for (int i = 0; i < d; ++i) {
+      float acc = 0.0f;
+      for (int j = 0; j < d; ++j) acc = fmaf(Q[(size_t)i * d + j], x[j], acc);
+      y[i] = acc;
+    }
+    return;
+  }
+  for (int i = 0; i < d; ++i) y[i] = x[i];
+  if (rotate == 2) {
+    const uint32_t *w = (const uint32_t *)rparam;
+    for (int i = 0; i < d; ++i)
+      if ((w[i / 32] >> (i % 32)) & 1u) y[i] = -y[i];
+  }
+  if (rotate == 1 || rotate == 2) orc_wht_f32(y, d);
+}
+
+/* [DA] "Quantization schemes" / "Problem statement": rotate, scalar Lloyd-Max
+ * quantise the direction, keep the norm; QJL modes add the 1-bit sketch
+ * sign(S r) of the scalar residual r and its norm ([DA] Contribution 1).
+ *  1. y = R x (rotate_fwd; y = x when rotate == 0)
  *  2. nu = sqrtf(pairwise sum of y_i^2); rcp = 1/nu (0 when nu == 0)
  *  3. u_i = y_i * rcp; code_i = bucketize(u_i)
- *  4. stored norm = f16(nu * s), s = fp32(1/sqrt(d)) if rotated else 1, so the
- *     stored value is ||x|| in both cases (||Hx|| = sqrt(d) ||x||)
+ *  4. stored norm = f16(nu * s), s = fp32(1/sqrt(d)) for the Hadamard kinds
+ *     (||Hx|| = sqrt(d) ||x||) else 1, so the stored value is ||x|| (||y||
+ *     for the dense rotation, equal up to rounding)
  *  5. QJL: r_i = u_i - C[code_i]; rnorm = f16(sqrtf(pairwise sum r_i^2));
  *     r~ = bf16(r); sign_k = [sum_i S_ki r~_i >= 0] with the sum taken in fp64,
  *     sequentially over ascending i (every product is exact in fp64). */
-void orc_encode(const float *x, int d, int rotate, int bits,
+void orc_encode(const float *x, int d, int rotate, const void *rparam, int bits,
                 const float *centroid, const float *threshold,
                 int qjl, const uint16_t *S, int m,
                 uint8_t *codes, uint8_t *signs, uint16_t *norm, uint16_t *rnorm) {
@@ -246,11 +271,10 @@ void orc_encode(const float *x, int d, int rotate, int bits,
   uint16_t rt[4096];
   int code[4096];
   const int nthr = (1 << bits) - 1;
-  for (int i = 0; i < d; ++i) y[i] = x[i];
-  if (rotate) orc_wht_f32(y, d);
+  rotate_fwd(y, x, d, rotate, rparam);
   float nu = sqrtf(orc_sumsq_f32(y, d));
   float rcp = (nu == 0.0f) ? 0.0f : 1.0f / nu;
-  float s = rotate ? (float)(1.0 / sqrt((double)d)) : 1.0f;
+  float s = (rotate == 1 || rotate == 2) ? (float)(1.0 / sqrt((double)d)) : 1.0f;
   *norm = orc_f32_to_f16(nu * s);
   memset(codes, 0, (size_t)(d * bits / 8));
   for (int i = 0; i < d; ++i) {
@@ -272,11 +296,12 @@ void orc_encode(const float *x, int d, int rotate, int bits,
 }
 
 /* Reconstruction, fp64, plain definition:
- *   x^ = n^ (H/sqrt(d)) (C[code] + sqrt(pi/2)/m * rho * S^T (2 sigma - 1))
- * (no H when rotate == 0; no sketch term when qjl == 0).  sqrt(pi/2)/m is the
+ *   x^ = n^ R^T (C[code] + sqrt(pi/2)/m * rho * S^T (2 sigma - 1))
+ * with R^T = H/sqrt(d) (WHT), D H/sqrt(d) (randomized Hadamard), Q^T (dense)
+ * or I (no rotation); no sketch term when qjl == 0.  sqrt(pi/2)/m is the
  * scale that makes the sketch estimate unbiased ([DA] Contribution 1). */
 void orc_decode(const uint8_t *codes, const uint8_t *signs, uint16_t norm, uint16_t rnorm,
-                int d, int rotate, int bits, const float *centroid,
+                int d, int rotate, const void *rparam, int bits, const float *centroid,
                 int qjl, const uint16_t *S, int m, double *xhat) {
   double t[4096];
   for (int i = 0; i < d; ++i) t[i] = (double)centroid[get_code(codes, d, bits, i)];
@@ -296,11 +321,21 @@ void orc_decode(const uint8_t *codes, const uint8_t *signs, uint16_t norm, uint1
     for (int i = 0; i < d; ++i) xhat[i] = nh * t[i];
     return;
   }
+  if (rotate == 3) {
+    const float *Q = (const float *)rparam;
+    for (int i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < d; ++j) acc += (double)Q[(size_t)j * d + i] * t[j];
+      xhat[i] = nh * acc;
+    }
+    return;
+  }
   double sc = nh / sqrt((double)d);
   for (int i = 0; i < d; ++i) {
     double acc = 0.0;
     for (int j = 0; j < d; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -t[j] : t[j];
     xhat[i] = sc * acc;
+    if (rotate == 2 && ((((const uint32_t *)rparam)[i / 32] >> (i % 32)) & 1u)) xhat[i] = -xhat[i];
   }
 }
 
@@ -345,7 +380,7 @@ static void run_units(void (*fn)(void *, int), void *ctx, int n, int nthreads) {
 
 typedef struct {
   const void *src; int dtype, H, T, d; long long sb, sh, st; int t0, cap;
-  int rotate, bits; const float *C, *Th; int qjl; const uint16_t *S; int m;
+  int rotate; const void *rparam; int bits; const float *C, *Th; int qjl; const uint16_t *S; int m;
   uint8_t *codes, *signs; uint16_t *norm, *rnorm;
 } qctx_t;
 
@@ -360,7 +395,7 @@ static void quantize_unit(void *vc, int unit) {
       x[i] = c->dtype == 0 ? ((const float *)c->src)[off + i]
                            : orc_bf16_to_f32(((const uint16_t *)c->src)[off + i]);
     size_t slot = ((size_t)unit * c->cap) + (size_t)(c->t0 + t);
-    orc_encode(x, c->d, c->rotate, c->bits, c->C, c->Th, c->qjl, c->S, c->m,
+    orc_encode(x, c->d, c->rotate, c->rparam, c->bits, c->C, c->Th, c->qjl, c->S, c->m,
                c->codes + slot * cb, c->qjl ? c->signs + slot * sbytes : NULL,
                c->norm + slot, c->qjl ? c->rnorm + slot : NULL);
   }
@@ -368,18 +403,19 @@ static void quantize_unit(void *vc, int unit) {
 
 void orc_quantize_cache(const void *src, int dtype, int B, int H, int T, int d,
                         long long sb, long long sh, long long st, int t0, int cap,
-                        int rotate, int bits, const float *centroid, const float *threshold,
-                        int qjl, const uint16_t *S, int m,
+                        int rotate, const void *rparam, int bits, const float *centroid,
+                        const float *threshold, int qjl, const uint16_t *S, int m,
                         uint8_t *codes, uint8_t *signs, uint16_t *norm, uint16_t *rnorm,
                         int nthreads) {
-  qctx_t c = {src, dtype, H, T, d, sb, sh, st, t0, cap, rotate, bits, centroid, threshold,
+  qctx_t c = {src, dtype, H, T, d, sb, sh, st, t0, cap, rotate, rparam, bits, centroid, threshold,
               qjl, S, m, codes, signs, norm, rnorm};
   run_units(quantize_unit, &c, B * H, nthreads);
 }
 
 typedef struct {
   const uint8_t *codes, *signs; const uint16_t *norm, *rnorm;
-  int H, cap, t0, T, d, rotate, bits; const float *C; int qjl; const uint16_t *S; int m;
+  int H, cap, t0, T, d, rotate; const void *rparam; int bits; const float *C; int qjl;
+  const uint16_t *S; int m;
   double *out;
 } dctx_t;
 
@@ -389,7 +425,8 @@ static void dequantize_unit(void *vc, int unit) {
   for (int t = 0; t < c->T; ++t) {
     size_t slot = (size_t)unit * c->cap + (size_t)(c->t0 + t);
     orc_decode(c->codes + slot * cb, c->qjl ? c->signs + slot * sbytes : NULL, c->norm[slot],
-               c->qjl ? c->rnorm[slot] : 0, c->d, c->rotate, c->bits, c->C, c->qjl, c->S, c->m,
+               c->qjl ? c->rnorm[slot] : 0, c->d, c->rotate, c->rparam, c->bits, c->C, c->qjl,
+               c->S, c->m,
                c->out + ((size_t)unit * c->T + t) * c->d);
   }
 }
@@ -397,9 +434,10 @@ static void dequantize_unit(void *vc, int unit) {
 void orc_dequantize_cache(const uint8_t *codes, const uint8_t *signs,
                           const uint16_t *norm, const uint16_t *rnorm,
                           int B, int H, int cap, int t0, int T, int d,
-                          int rotate, int bits, const float *centroid,
+                          int rotate, const void *rparam, int bits, const float *centroid,
                           int qjl, const uint16_t *S, int m, double *out, int nthreads) {
-  dctx_t c = {codes, signs, norm, rnorm, H, cap, t0, T, d, rotate, bits, centroid, qjl, S, m, out};
+  dctx_t c = {codes, signs, norm, rnorm, H, cap, t0, T, d, rotate, rparam, bits, centroid, qjl,
+              S, m, out};
   run_units(dequantize_unit, &c, B * H, nthreads);
 }
 
@@ -420,7 +458,8 @@ static void side_decode(const orc_side *sd, size_t slot, int d, const uint16_t *
                         double *x) {
   size_t cb = (size_t)d * sd->bits / 8, sbytes = (size_t)m / 8;
   orc_decode(sd->codes + slot * cb, sd->qjl ? sd->signs + slot * sbytes : NULL, sd->norm[slot],
-             sd->qjl ? sd->rnorm[slot] : 0, d, sd->rotate, sd->bits, sd->centroid, sd->qjl, S, m, x);
+             sd->qjl ? sd->rnorm[slot] : 0, d, sd->rotate, sd->rparam, sd->bits, sd->centroid,
+             sd->qjl, S, m, x);
 }
 
 /* Plain attention over explicit fp64 keys and values (n tokens, row-major):

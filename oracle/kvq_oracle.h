@@ -19,7 +19,9 @@
  *        per generated token), "Systems tax" (per-token append).
  *  [KPP] "KVQuant++" forum thread (zingnex.cn): "Codebook design: the true
  *        sphere marginal" f(t) ~ (1-t^2)^((d-3)/2), "Fast codebook lookup"
- *        (bucketize), "Rate-distortion performance" (MSE bound).
+ *        (bucketize), "Entropy coding" (QR or Hadamard random rotation),
+ *        "Rotation invariance guarantee" (QR rotation in SO(d)),
+ *        "Rate-distortion performance" (MSE bound).
  *
  * Readings where the pages are silent are listed in the repository's design
  * notes; each function below states the one it implements.
@@ -51,17 +53,23 @@ float orc_sumsq_f32(const float *y, int d);
 /* Bucketize: number of thresholds strictly below u. */
 int orc_bucketize(float u, const float *threshold, int nthr);
 
-/* Encode one d-vector (fp32).  rotate: WHT first.  bits: code width.
- * qjl: also write m sign bits of S.bf16(r) and the fp16 residual norm.
- * S: m x d bf16 bit patterns, row-major.  Packed layout: see the .c file. */
-void orc_encode(const float *x, int d, int rotate, int bits,
+/* Rotation kinds ("rotate" arguments below):
+ *   0 none; 1 WHT y = H x; 2 randomized Hadamard y = H (D x), rparam = sign
+ *   words (uint32, bit i set: x_i negated); 3 dense y = Q x, rparam = Q
+ *   (fp32, d x d, row-major). */
+
+/* Encode one d-vector (fp32).  rotate, rparam: rotation (above).  bits: code
+ * width.  qjl: also write m sign bits of S.bf16(r) and the fp16 residual
+ * norm.  S: m x d bf16 bit patterns, row-major.  Packed layout: see the .c
+ * file. */
+void orc_encode(const float *x, int d, int rotate, const void *rparam, int bits,
                 const float *centroid, const float *threshold,
                 int qjl, const uint16_t *S, int m,
                 uint8_t *codes, uint8_t *signs, uint16_t *norm, uint16_t *rnorm);
 
 /* Reconstruct one vector in fp64 from its record. */
 void orc_decode(const uint8_t *codes, const uint8_t *signs, uint16_t norm, uint16_t rnorm,
-                int d, int rotate, int bits, const float *centroid,
+                int d, int rotate, const void *rparam, int bits, const float *centroid,
                 int qjl, const uint16_t *S, int m, double *xhat);
 
 /* Quantize-on-write of T tokens into a cache laid out [B][H][cap][record].
@@ -70,7 +78,8 @@ void orc_decode(const uint8_t *codes, const uint8_t *signs, uint16_t norm, uint1
  * signs / rnorm may be NULL when qjl == 0.  nthreads >= 1. */
 void orc_quantize_cache(const void *src, int dtype, int B, int H, int T, int d,
                         long long sb, long long sh, long long st, int t0, int cap,
-                        int rotate, int bits, const float *centroid, const float *threshold,
+                        int rotate, const void *rparam, int bits, const float *centroid,
+                        const float *threshold,
                         int qjl, const uint16_t *S, int m,
                         uint8_t *codes, uint8_t *signs, uint16_t *norm, uint16_t *rnorm,
                         int nthreads);
@@ -79,7 +88,7 @@ void orc_quantize_cache(const void *src, int dtype, int B, int H, int T, int d,
 void orc_dequantize_cache(const uint8_t *codes, const uint8_t *signs,
                           const uint16_t *norm, const uint16_t *rnorm,
                           int B, int H, int cap, int t0, int T, int d,
-                          int rotate, int bits, const float *centroid,
+                          int rotate, const void *rparam, int bits, const float *centroid,
                           int qjl, const uint16_t *S, int m, double *out, int nthreads);
 
 /* Plain attention over explicit fp64 keys K [n][d] and values V [n][d]. */
@@ -92,6 +101,7 @@ typedef struct {
   const uint16_t *norm, *rnorm;
   int rotate, bits, qjl;
   const float *centroid;
+  const void *rparam;
 } orc_side;
 
 /* Decode attention over the reconstructed cache, fp64, plain definition:

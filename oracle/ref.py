@@ -16,7 +16,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import numpy as np
 
@@ -50,12 +50,13 @@ def lib():
         L.orc_sumsq_f32.restype = C.c_float
         L.orc_bucketize.argtypes = [C.c_float, vp, i32]
         L.orc_bucketize.restype = i32
-        L.orc_encode.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, vp, vp]
-        L.orc_decode.argtypes = [vp, vp, C.c_uint16, C.c_uint16, i32, i32, i32, vp, i32, vp, i32, vp]
+        L.orc_encode.argtypes = [vp, i32, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, vp]
+        L.orc_decode.argtypes = [vp, vp, C.c_uint16, C.c_uint16, i32, i32, vp, i32, vp, i32, vp,
+                                 i32, vp]
         L.orc_quantize_cache.argtypes = [vp, i32, i32, i32, i32, i32, i64, i64, i64, i32, i32,
-                                         i32, i32, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32]
+                                         i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32]
         L.orc_dequantize_cache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                           i32, i32, vp, i32, vp, i32, vp, i32]
+                                           i32, vp, i32, vp, i32, vp, i32, vp, i32]
         L.orc_attention_dense.argtypes = [vp, vp, vp, i32, i32, vp]
         L.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
                                     vp, vp, i32, i32]
@@ -128,6 +129,30 @@ class Side:
     qjl: int
 
 
+@dataclass(frozen=True)
+class Rot:
+    """Rotation of the rotated sides ("KVQuant++" thread, "Entropy coding",
+    "Rotation invariance guarantee"): "wht" (y = H x), "rht" (y = H D x,
+    param = 4 uint32 sign words) or "qr" (y = Q x, param = fp32 [d][d])."""
+    kind: str = "wht"
+    param: object = field(default=None, compare=False)
+
+    def code(self, side: "Side") -> int:
+        if not side.rotate:
+            return 0
+        return {"wht": 1, "rht": 2, "qr": 3}[self.kind]
+
+    def array(self):
+        if self.kind == "rht":
+            return np.ascontiguousarray(self.param, dtype=np.uint32)
+        if self.kind == "qr":
+            return np.ascontiguousarray(self.param, dtype=np.float32)
+        return None
+
+
+WHT = Rot()
+
+
 def scheme_sides(scheme: str, n: int):
     """(K side, V side) of a scheme at n bits per coordinate."""
     if scheme == "KV":
@@ -140,7 +165,7 @@ def scheme_sides(scheme: str, n: int):
 
 
 # ---------------------------------------------------------------- single vectors
-def encode(x: np.ndarray, side: Side, S: np.ndarray | None = None):
+def encode(x: np.ndarray, side: Side, S: np.ndarray | None = None, rot: Rot = WHT):
     """Encode one vector -> (codes bytes, sign bytes or None, norm f16 bits, rnorm f16 bits)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     d = x.shape[0]
@@ -151,19 +176,21 @@ def encode(x: np.ndarray, side: Side, S: np.ndarray | None = None):
     norm = np.zeros(1, np.uint16)
     rnorm = np.zeros(1, np.uint16)
     Sc = None if S is None else np.ascontiguousarray(S, dtype=np.uint16)
-    lib().orc_encode(_p(x), d, side.rotate, side.bits, _p(c), _p(t), side.qjl, _p(Sc), m,
-                     _p(codes), _p(signs), _p(norm), _p(rnorm))
+    rp = rot.array()
+    lib().orc_encode(_p(x), d, rot.code(side), _p(rp), side.bits, _p(c), _p(t), side.qjl, _p(Sc),
+                     m, _p(codes), _p(signs), _p(norm), _p(rnorm))
     return codes, (signs[: m // 8] if side.qjl else None), int(norm[0]), int(rnorm[0])
 
 
-def decode(codes, signs, norm, rnorm, d, side: Side, S=None) -> np.ndarray:
+def decode(codes, signs, norm, rnorm, d, side: Side, S=None, rot: Rot = WHT) -> np.ndarray:
     c, _, _ = codebook(d, side.bits)
     out = np.zeros(d, np.float64)
     m = 0 if S is None else S.shape[0]
     Sc = None if S is None else np.ascontiguousarray(S, dtype=np.uint16)
     sg = None if signs is None else np.ascontiguousarray(signs, dtype=np.uint8)
+    rp = rot.array()
     lib().orc_decode(_p(np.ascontiguousarray(codes, dtype=np.uint8)), _p(sg), int(norm), int(rnorm),
-                     d, side.rotate, side.bits, _p(c), side.qjl, _p(Sc), m, _p(out))
+                     d, rot.code(side), _p(rp), side.bits, _p(c), side.qjl, _p(Sc), m, _p(out))
     return out
 
 
@@ -171,8 +198,9 @@ def decode(codes, signs, norm, rnorm, d, side: Side, S=None) -> np.ndarray:
 class OracleCache:
     """Host arrays of one side (K or V) of a cache, laid out [B][H][cap][...]."""
 
-    def __init__(self, B, H, cap, d, side: Side, m: int):
+    def __init__(self, B, H, cap, d, side: Side, m: int, rot: Rot = WHT):
         self.B, self.H, self.cap, self.d, self.side, self.m = B, H, cap, d, side, m
+        self.rot, self.rp = rot, rot.array()
         self.codes = np.zeros((B, H, cap, d * side.bits // 8), np.uint8)
         self.signs = np.zeros((B, H, cap, m // 8), np.uint8) if side.qjl else None
         self.norm = np.zeros((B, H, cap), np.uint16)
@@ -193,7 +221,8 @@ class OracleCache:
         assert si == 1
         Sc = None if S is None else np.ascontiguousarray(S, dtype=np.uint16)
         lib().orc_quantize_cache(C.c_void_p(src.ctypes.data), dtype, B, H, T, d, sb, sh, st, t0,
-                                 self.cap, self.side.rotate, self.side.bits, _p(self.centroid),
+                                 self.cap, self.rot.code(self.side), _p(self.rp), self.side.bits,
+                                 _p(self.centroid),
                                  _p(self.threshold), self.side.qjl, _p(Sc), self.m,
                                  _p(self.codes), _p(self.signs), _p(self.norm), _p(self.rnorm),
                                  nthreads)
@@ -202,20 +231,22 @@ class OracleCache:
         out = np.zeros((self.B, self.H, T, self.d), np.float64)
         Sc = None if S is None else np.ascontiguousarray(S, dtype=np.uint16)
         lib().orc_dequantize_cache(_p(self.codes), _p(self.signs), _p(self.norm), _p(self.rnorm),
-                                   self.B, self.H, self.cap, t0, T, self.d, self.side.rotate,
-                                   self.side.bits, _p(self.centroid), self.side.qjl, _p(Sc),
+                                   self.B, self.H, self.cap, t0, T, self.d,
+                                   self.rot.code(self.side), _p(self.rp), self.side.bits,
+                                   _p(self.centroid), self.side.qjl, _p(Sc),
                                    self.m, _p(out), nthreads)
         return out
 
     def _side_struct(self):
         return _OrcSide(_p(self.codes), _p(self.signs), _p(self.norm), _p(self.rnorm),
-                        self.side.rotate, self.side.bits, self.side.qjl, _p(self.centroid))
+                        self.rot.code(self.side), self.side.bits, self.side.qjl,
+                        _p(self.centroid), _p(self.rp))
 
 
 class _OrcSide(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("signs", C.c_void_p), ("norm", C.c_void_p),
                 ("rnorm", C.c_void_p), ("rotate", C.c_int), ("bits", C.c_int),
-                ("qjl", C.c_int), ("centroid", C.c_void_p)]
+                ("qjl", C.c_int), ("centroid", C.c_void_p), ("rparam", C.c_void_p)]
 
 
 def attention(kc: OracleCache, vc: OracleCache, q: np.ndarray, n_ctx: int,

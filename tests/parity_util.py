@@ -24,14 +24,21 @@ def u16(t: torch.Tensor) -> np.ndarray:
 class Pair:
     """A GPU cache and the oracle's cache of the same scheme and inputs."""
 
-    def __init__(self, scheme, n, d, B, Hkv, cap, S=None, device="cuda"):
+    def __init__(self, scheme, n, d, B, Hkv, cap, S=None, device="cuda", rotation="wht",
+                 rot_seed=19):
         self.scheme, self.n, self.d, self.B, self.Hkv, self.cap = scheme, n, d, B, Hkv, cap
         self.S_t = synth.sketch_bf16(d, d, 7) if S is None else S
         self.S = synth.bits_u16(self.S_t)
-        self.gpu = KVQCache(scheme, n, d, B, Hkv, cap, S_bf16=self.S, device=device)
+        param = {"wht": None, "rht": synth.rotation_signs(d, rot_seed),
+                 "qr": synth.rotation_qr(d, rot_seed)}[rotation]
+        self.gpu = KVQCache(scheme, n, d, B, Hkv, cap, S_bf16=self.S, device=device,
+                            rotation=rotation,
+                            rot_signs=param if rotation == "rht" else None,
+                            rot_Q=param if rotation == "qr" else None)
         ks, vs = ref.scheme_sides(scheme, n)
-        self.ok = ref.OracleCache(B, Hkv, cap, d, ks, d)
-        self.ov = ref.OracleCache(B, Hkv, cap, d, vs, d)
+        rot = ref.Rot(rotation, param)
+        self.ok = ref.OracleCache(B, Hkv, cap, d, ks, d, rot)
+        self.ov = ref.OracleCache(B, Hkv, cap, d, vs, d, rot)
 
     def write(self, K: torch.Tensor, V: torch.Tensor, t0: int, dev="cuda", nthreads=8):
         """K, V: [B][Hkv][T][d] tensors (any strides, innermost contiguous)."""

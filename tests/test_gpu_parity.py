@@ -299,3 +299,49 @@ def test_decode_window_equals_plain_decode_when_empty():
     a = P.gpu.decode_attention(q, N, splits=3)
     b = P.gpu.decode_attention_window(q, 0, N, splits=3)
     assert torch.equal(a, b)
+
+
+ROT_SCHEMES = [("KQV", 4), ("KQV", 2), ("QKQV", 3), ("QKQV", 2)]
+
+
+@pytest.mark.parametrize("rotation", ["rht", "qr"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("scheme,n", ROT_SCHEMES, ids=[f"{s}{n}" for s, n in ROT_SCHEMES])
+def test_quantize_bit_exact_rotations(scheme, n, d, dtype, rotation):
+    """Randomized Hadamard and dense SO(d) rotations ("KVQuant++" thread,
+    "Entropy coding", "Rotation invariance guarantee"): codes, norms and sign
+    bits bit for bit, over several tiles with a ragged tail."""
+    print(f"case quantize-rot {rotation} {scheme}{n} d={d} {dtype}", flush=True)
+    B, H, T, t0, cap = 2, 3, 141, 5, 150
+    P = Pair(scheme, n, d, B, H, cap, rotation=rotation)
+    K, V = _inputs(B, H, T, d, dtype, 1500 + d + n, heavy=True)
+    P.write(K, V, t0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+
+
+@pytest.mark.parametrize("rotation", ["rht", "qr"])
+@pytest.mark.parametrize("d", [32, 128])
+def test_dequantize_and_decode_rotations(rotation, d):
+    print(f"case decode-rot {rotation} d={d}", flush=True)
+    B, Hkv, G, N = 2, 2, 4, 333
+    for scheme, n in (("KQV", 4), ("QKQV", 3)):
+        P = Pair(scheme, n, d, B, Hkv, N, rotation=rotation)
+        K, V = _inputs(B, Hkv, N, d, torch.float32, 1600 + d, heavy=True)
+        P.write(K, V, 0)
+        for which, oc in ((0, P.ok), (1, P.ov)):
+            got = P.gpu.dequantize(which, 2, 300).cpu().numpy()
+            assert rel_rows(got, oc.dequantize(2, 300, P.S, nthreads=8)).max() < 1e-5
+        q = synth.gaussian((B, Hkv * G, d), 1700 + d, torch.float32)
+        want = P.attention(q, N)
+        for splits in (0, 3):
+            got = P.gpu.decode_attention(q.cuda(), N, splits=splits).cpu().numpy()
+            assert rel_rows(got, want).max() < 1e-5, (scheme, splits)
+        qb = q.to(torch.bfloat16)
+        got = P.gpu.decode_attention(qb.cuda(), N).cpu().numpy()
+        assert rel_rows(got, P.attention(qb, N)).max() < 1e-5
+        # with a full-precision window as well
+        wk, wv = K[:, :, 300:].contiguous(), V[:, :, 300:].contiguous()
+        got = P.gpu.decode_attention_window(q.cuda(), 0, 300, wk.cuda(), wv.cuda()).cpu().numpy()
+        assert rel_rows(got, P.attention_window(q, 0, 300, wk, wv)).max() < 1e-5

@@ -251,3 +251,72 @@ def test_bad_codebook_rejected(K):
     c = _fake_cache(K, d=64)
     c.cb_v.centroid[0] = 0.5                                 # asymmetric table
     assert lib.kvq_quantize_v(C.byref(c), 0x900000, 1, 0, 4, 0, 0, 64, None) == 4
+
+
+# --------------------------------------------------------------------------- rotations
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_rotation_signs_generator(K, d):
+    """Randomized Hadamard diagonal: deterministic per seed, no bits at or
+    beyond d, about half the coordinates flipped over many draws."""
+    a, b = K.kvq_rotation_signs(5, d), K.kvq_rotation_signs(5, d)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, K.kvq_rotation_signs(6, d))
+    bits = np.array([[(int(K.kvq_rotation_signs(s, d)[i // 32]) >> (i % 32)) & 1
+                      for i in range(128)] for s in range(64)])
+    assert not bits[:, d:].any()
+    p = bits[:, :d].mean()
+    assert abs(p - 0.5) < 4 * math.sqrt(0.25 / (64 * d))
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_rotation_qr_generator_is_haar_on_SO_d(K, d):
+    """Dense rotation ("KVQuant++" thread, "Rotation invariance guarantee"):
+    orthogonal to fp32 rounding, determinant +1 for every seed (about half of
+    the raw QR factors have determinant -1), entries with mean 0 and variance
+    1/d, and the first column uniform on the sphere (its first coordinate has
+    the sphere-marginal variance 1/d, checked by a chi-square on d * q^2)."""
+    Qs = [K.kvq_rotation_qr(s, d).astype(np.float64) for s in range(40)]
+    for Q in Qs:
+        assert np.abs(Q @ Q.T - np.eye(d)).max() < 4e-6
+        assert abs(np.linalg.det(Q) - 1.0) < 1e-4
+    assert np.array_equal(K.kvq_rotation_qr(3, d), K.kvq_rotation_qr(3, d))
+    E = np.stack(Qs)
+    assert abs(E.mean()) < 4 / math.sqrt(E.size * d)
+    assert abs((E ** 2).mean() * d - 1.0) < 1e-5
+    q00 = E[:, :, 0].ravel() ** 2 * d                # many coordinates of first columns
+    assert abs(q00.mean() - 1.0) < 0.15
+
+
+def test_cache_set_rotation_validation(K):
+    lib = K.lib()
+    kv = _fake_cache(K, scheme="KV", n=4)
+    assert lib.kvq_cache_set_rotation(C.byref(kv), 1, np.zeros(4, np.uint32).ctypes.data, None) == 5
+    assert lib.kvq_cache_set_rotation(C.byref(kv), 0, None, None) == 0
+    c = _fake_cache(K, d=64)
+    w = np.zeros(4, np.uint32)
+    assert lib.kvq_cache_set_rotation(C.byref(c), 3, None, None) == 5
+    assert lib.kvq_cache_set_rotation(C.byref(c), 1, None, None) == 1
+    assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, None) == 1
+    assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, 0x10008) == 2
+    w[2] = 1                                         # beyond the d/32 words read at d = 64
+    assert lib.kvq_cache_set_rotation(C.byref(c), 1, w.ctypes.data, None) == 0
+    assert list(c.rot_signs) == [0, 0, 0, 0]
+    c16 = _fake_cache(K, d=16)
+    w16 = np.array([1 << 16, 0, 0, 0], np.uint32)    # coordinate 16 of a d = 16 cache
+    assert lib.kvq_cache_set_rotation(C.byref(c16), 1, w16.ctypes.data, None) == 10
+    w[:] = [0xFFFFFFFF, 0x80000001, 0, 0]
+    assert lib.kvq_cache_set_rotation(C.byref(c), 1, w.ctypes.data, None) == 0
+    assert c.rot_kind == 1 and list(c.rot_signs) == [0xFFFFFFFF, 0x80000001, 0, 0]
+    assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, 0x900000) == 0
+    assert c.rot_kind == 2 and c.rot_Q == 0x900000 and list(c.rot_signs) == [0, 0, 0, 0]
+    # the struct is validated again by every entry point
+    bad = _fake_cache(K, d=64)
+    bad.rot_kind = 2                                 # dense rotation without Q
+    assert lib.kvq_dequantize(C.byref(bad), 0, 0, 4, 0x800000, None) == 1
+    bad.rot_kind = 7
+    assert lib.kvq_dequantize(C.byref(bad), 0, 0, 4, 0x800000, None) == 5
+    bad = _fake_cache(K, d=32)
+    bad.rot_kind, bad.rot_signs[1] = 1, 1            # coordinate 32 of a d = 32 cache
+    assert lib.kvq_quantize_k(C.byref(bad), 0x900000, 1, 0, 4, 0, 0, 32, None) == 10
+    kv.rot_kind = 1
+    assert lib.kvq_quantize_k(C.byref(kv), 0x900000, 1, 0, 4, 0, 0, 64, None) == 5

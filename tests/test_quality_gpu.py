@@ -84,3 +84,30 @@ def test_sketch_removes_the_scalar_shrinkage(table, n):
     assert abs(kv.proj_v - (1 - d_b)) < 0.01 * d_b + 2e-4
     assert abs(kqv.proj_v - 1.0) < 3e-3
     assert abs(kqv.proj_v - 1.0) < abs(kv.proj_v - 1.0)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_rotations_stay_under_the_rate_distortion_bound(bits):
+    """KVQuant++ thread, 'Rate-distortion performance': whether the rotation
+    is the (randomized) Hadamard or a Haar QR rotation, the per-element MSE of
+    unit keys stays under sqrt(3 pi/2) 4^-b (the literal reading) and, on
+    generic keys, under the whole-vector form (sqrt(3) pi/2) 4^-b / d.  On keys
+    that the plain WHT maps to single spikes the plain WHT breaks the
+    whole-vector form, while the randomized rotations do not."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_quantization_kqv_amd import quality
+    print(f"case rotation mse bits={bits}", flush=True)
+    lit = math.sqrt(3 * math.pi / 2) * 4.0 ** -bits
+    tq = (math.sqrt(3) * math.pi / 2) * 4.0 ** -bits / 128
+    for kind in ("gaussian", "heavytail", "lowrank"):
+        for rot in ("wht", "rht", "qr"):
+            e = quality.rotation_mse(kind, bits, rot)
+            assert e <= lit and e <= tq, (kind, rot, e, tq)
+    assert quality.rotation_mse("hadamard", bits, "wht") > tq
+    assert quality.rotation_mse("hadamard", bits, "qr") <= tq
+    # one sign draw maps every Hadamard row to the same magnitudes (a permuted
+    # Walsh transform of the signs): average 32 draws
+    e = sum(quality.rotation_mse("hadamard", bits, "rht", H=1, N=64, seed=3000 + 7 * k)
+            for k in range(32)) / 32
+    assert e <= tq, e
