@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "4-bit KQV decode-attn HBM GB/s (% of peak) + KV tokens/s; quantize GB/s"
 HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK = 157.3  # TFLOP/s, dense fp32 matrix (MI355X)
 
 
 def record_bytes(d, kb, vb, kq, vq):
@@ -44,6 +45,9 @@ def main():
     ap.add_argument("--rotation", default="wht", choices=["wht", "rht", "qr"],
                     help="rotation of the rotated schemes (Walsh-Hadamard, randomized "
                          "Hadamard, dense SO(d))")
+    ap.add_argument("--prefill-chunk", type=int, default=256,
+                    help="also time multi-query attention of a chunk of this many query tokens "
+                         "at the end of the context (causal); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=4, help="(b, KV head) units in the CPU sample")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gqa_decode_kqv4.md"),
@@ -146,6 +150,35 @@ def main():
     torch.cuda.synchronize(dev)
     warm_t = e0.elapsed_time(e1) * 1e-3 / 10
 
+    prefill = None
+    if args.prefill_chunk > 0:
+        C = min(args.prefill_chunk, N)
+        qp = synth.gaussian((B, C, Hq, d), 31, w.dtype, device=dev)
+        from kv_cache_quantization_kqv_amd import kvq as _kq
+        wsp = torch.empty(_kq.kvq_prefill_workspace(c, Hq, C), dtype=torch.uint8, device=dev)
+        outp = torch.empty(B, C, Hq, d, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            cache.prefill_attention(qp, N - C, N, causal=True, out=outp, workspace=wsp)
+        reps = max(1, min(args.steps, 5))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        e0.record(stream)
+        for _ in range(reps):
+            cache.prefill_attention(qp, N - C, N, causal=True, out=outp, workspace=wsp)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        pt = e0.elapsed_time(e1) * 1e-3 / reps
+        # MFMA work per (row, visible token): q'.k (d), the K sketch (m, QKQV),
+        # P V (d) and the V sketch (m)
+        per = 2 * (d + d + d * c.k_qjl + d * c.v_qjl)
+        vis = sum(N - C + i + 1 for i in range(C))
+        flops = B * Hq * vis * per
+        prefill = {"chunk": C, "q_pos0": N - C, "causal": True, "us": round(pt * 1e6, 2),
+                   "TFLOPs": round(flops / pt / 1e12, 2), "peak_TFLOPs": FP32_MFMA_PEAK,
+                   "pct_fp32_mfma_peak": round(100 * flops / pt / 1e12 / FP32_MFMA_PEAK, 2),
+                   "kernel": "prep_kernel + prefill_kernel (fp32 MFMA 16x16x4) + finish_kernel"}
+        del qp, wsp, outp
+
     roof = {"kernel": "kvq_decode_attention: query kernel + decode_kernel (split scan with fused merge)",
             "bound": "hbm",
             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -177,6 +210,8 @@ def main():
                      "GBps_v": round(qv_bytes / float(tv.mean()) / 1e9, 1)},
         "roofline": roof,
     }
+    if prefill is not None:
+        result["prefill"] = prefill
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, scheme, n_bits, K, V, q, S, args.cpu_units, rec,

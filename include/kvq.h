@@ -240,6 +240,29 @@ kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int 
 /* The split count kvq_decode_attention uses when splits == 0. */
 int kvq_decode_auto_splits(const kvq_cache *c, int q_heads, int n_ctx);
 
+/* Multi-query (chunked-prefill) attention over the compressed cache ("Your
+ * KV cache is not a bit problem but a geometry problem", "Systems tax": a
+ * prompt chunk is quantised into the cache along the token axis, then its
+ * queries attend over the cache):
+ *   out[b][i][hq] = sum_{t < T_i} softmax_t(q[b][i][hq] . k^_t / sqrt(d)) v^_t
+ * with T_i = n_ctx, or min(n_ctx, q_pos0 + i + 1) when causal (query token i
+ * sits at absolute position q_pos0 + i; its own token must already be in the
+ * cache).  q: [B][n_q][q_heads][d] fp32 or bf16 (device, contiguous); out:
+ * [B][n_q][q_heads][d] fp32 (device); q_heads any multiple of kv_heads.
+ * Same decoded-vector semantics as kvq_decode_attention (rotated-space
+ * scoring, sketch-space value term, one S^T product per row).  workspace:
+ * kvq_prefill_workspace bytes.  1 <= n_ctx <= capacity, n_q >= 1,
+ * q_pos0 >= 0, causal in {0, 1}.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_HEADS,
+ * KVQ_ERR_CAPACITY, KVQ_ERR_RANGE, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
+kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
+                                 int n_q, int q_pos0, int causal, int n_ctx, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kvq_prefill_attention needs:
+ * 4 * B * q_heads * n_q * d * (3 + [K sketched]). */
+kvq_status kvq_prefill_workspace(const kvq_cache *c, int q_heads, int n_q, size_t *bytes);
+
 /* Static text for a status code. */
 const char *kvq_status_str(kvq_status s);
 

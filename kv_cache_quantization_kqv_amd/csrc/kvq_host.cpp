@@ -583,6 +583,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   hipStream_t hs = (hipStream_t)stream;
 
   kvq::PrepArgs p;
+  std::memset(&p, 0, sizeof(p));       // nq = 0: decode layout
   p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = rows;
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
   p.cnt = cnt; p.ncnt = units;
@@ -597,6 +598,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
 
   if (n_win > 0) {
     kvq::WindowArgs w;
+    std::memset(&w, 0, sizeof(w));
     w.q = q; w.wk = wk; w.wv = wv; w.wpart = wpart;
     w.Hq = q_heads; w.Hkv = c->kv_heads; w.n_win = n_win;
     w.qscale = (float)(kLog2e / std::sqrt((double)d));
@@ -650,6 +652,90 @@ kvq_status kvq_decode_attention_window(const kvq_cache *c, const void *q, int q_
                                        void *stream) {
   return decode_impl(c, q, q_dtype, q_heads, t_begin, t_end, wk, wv, w_dtype, n_win, splits, out,
                      workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_prefill_workspace(const kvq_cache *c, int q_heads, int n_q, size_t *bytes) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!bytes) return KVQ_ERR_NULL;
+  if (q_heads < 1 || q_heads % c->kv_heads) return KVQ_ERR_HEADS;
+  if (n_q < 1) return KVQ_ERR_RANGE;
+  const size_t rows = (size_t)c->batch * q_heads * n_q;
+  if (rows > ((size_t)1 << 31) - 1) return KVQ_ERR_RANGE;
+  // prepared q' (and S q'), then o' and a per row
+  *bytes = sizeof(float) * rows * c->d * (1 + (c->k_qjl ? 1 : 0) + 2);
+  return KVQ_OK;
+}
+
+kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
+                                 int n_q, int q_pos0, int causal, int n_ctx, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!q || !out) return KVQ_ERR_NULL;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (causal != 0 && causal != 1) return KVQ_ERR_RANGE;
+  if (n_q < 1 || n_ctx < 1 || q_pos0 < 0) return KVQ_ERR_RANGE;
+  if (n_ctx > c->capacity) return KVQ_ERR_CAPACITY;
+  size_t need = 0;
+  s = kvq_prefill_workspace(c, q_heads, n_q, &need);
+  if (s != KVQ_OK) return s;
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  const int d = c->d;
+  const int G = q_heads / c->kv_heads;
+  const size_t rows = (size_t)c->batch * q_heads * n_q;
+  float *qt = (float *)workspace;
+  float *sqt = qt + rows * d;
+  float *part = sqt + (c->k_qjl ? rows * d : 0);
+  hipStream_t hs = (hipStream_t)stream;
+  const int rk = rot_code(c);
+
+  kvq::PrepArgs p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = (int)rows;
+  p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = 1; p.HG = G;
+  p.cnt = nullptr; p.ncnt = 0; p.nq = n_q;
+  p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
+  for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
+  p.Q = c->rot_Q;
+  hipError_t e = by_dim(d, [&](auto D) {
+    return kvq::launch_prep<decltype(D)::value>(p, rk, c->k_qjl != 0, q_dtype == KVQ_BF16, hs);
+  });
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+
+  kvq::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
+  a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
+  a.qt = qt; a.sqt = sqt; a.part = part;
+  for (int i = 0; i < 16; ++i) {
+    a.kcent[i] = c->cb_k.centroid[i];
+    a.vcent[i] = c->cb_v.centroid[i];
+  }
+  a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
+  a.Hkv = c->kv_heads; a.G = G; a.cap = c->capacity; a.nq = n_q; a.q_pos0 = q_pos0;
+  a.n_ctx = n_ctx; a.causal = causal;
+  e = by_dim(d, [&](auto D) {
+    return kvq::launch_prefill<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
+                                                   c->v_qjl != 0, c->batch, hs);
+  });
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+
+  kvq::FinishArgs f;
+  std::memset(&f, 0, sizeof(f));
+  f.part = part; f.S = c->S; f.out = out;
+  f.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
+  f.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
+  f.rk = rk;
+  for (int k = 0; k < 4; ++k) f.rsign[k] = c->rot_signs[k];
+  f.Q = c->rot_Q;
+  f.Hkv = c->kv_heads; f.Hq = q_heads; f.G = G; f.nq = n_q;
+  e = by_dim(d, [&](auto D) {
+    return kvq::launch_finish<decltype(D)::value>(f, c->v_qjl != 0, (int)rows, hs);
+  });
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -62,6 +62,8 @@ struct PrepArgs {
   int ncnt;
   uint32_t rsign[4];         // RK_RHT
   const float *Q;            // RK_QR
+  int nq;                    // > 0: multi-query layout (rows (b, i, hq) of [B][nq][Hq][d];
+                             // output [B][Hkv][nq * G][d], row i * G + g)
 };
 
 struct DecodeArgs {
@@ -82,6 +84,31 @@ struct DecodeArgs {
   const float *wpart;        // full-precision window partial [B][Hq][2 + d] or null
   int t0;                    // first cache slot of the scanned range
   int Hkv, Hq, Gtot, HG, cap, n_ctx, splits, tps;
+};
+
+// Multi-query (chunked-prefill) attention over the compressed cache: nq query
+// tokens x G heads per KV head attend to cache slots [0, n_ctx), causally to
+// slot q_pos0 + i for query token i when `causal`.
+struct PrefillArgs {
+  const uint8_t *kc, *ks, *vc, *vs;
+  const uint16_t *kn, *kr, *vn, *vr;
+  const float *qt, *sqt;     // prepared queries [B][Hkv][NR][d], NR = nq * G (row i * G + g)
+  float *part;               // [B][Hkv][NR][2d]: o' / L, a / L
+  float kcent[16], vcent[16];
+  float kcoef;               // sqrt(pi/2)/m (K sketch)
+  int Hkv, G, cap, nq, q_pos0, n_ctx, causal;
+};
+
+// Finish of a multi-query call, one block per output row: o = R^T (o' + c S^T a).
+struct FinishArgs {
+  const float *part;         // as PrefillArgs::part
+  const uint16_t *S;
+  float *out;                // [B][nq][Hq][d]
+  float vcoef, oscale;
+  int rk;
+  uint32_t rsign[4];
+  const float *Q;
+  int Hkv, Hq, G, nq;
 };
 
 // Full-precision window (sinks and recent tokens): exact partial softmax sums
@@ -107,5 +134,8 @@ template <int D> hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, 
                                           int gt, int B, hipStream_t s);
 template <int D> hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows,
                                           hipStream_t s);
+template <int D> hipError_t launch_prefill(const PrefillArgs &a, int kb, bool kq, int vb, bool vq,
+                                           int B, hipStream_t s);
+template <int D> hipError_t launch_finish(const FinishArgs &a, bool vq, int rows, hipStream_t s);
 
 }  // namespace kvq

@@ -23,6 +23,7 @@ namespace kvq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -950,10 +951,18 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
     __syncthreads();
   }
   x = x * a.qscale;
-  const int b = row / a.Hq, hq = row - b * a.Hq;
-  const int hkv = hq / a.G, within = hq - hkv * a.G;
-  const int hg = within / a.GT, hh = within - hg * a.GT;
-  const size_t dst = ((((size_t)b * a.Hkv + hkv) * a.HG + hg) * D + i) * a.GT + hh;
+  size_t dst;
+  if (a.nq > 0) {            // multi-query: row = (b * nq + t) * Hq + hq
+    const int hq = row % a.Hq, bt = row / a.Hq;
+    const int b = bt / a.nq, t = bt - b * a.nq;
+    const int hkv = hq / a.G, g = hq - hkv * a.G;
+    dst = ((((size_t)b * a.Hkv + hkv) * a.nq + t) * a.G + g) * D + i;
+  } else {
+    const int b = row / a.Hq, hq = row - b * a.Hq;
+    const int hkv = hq / a.G, within = hq - hkv * a.G;
+    const int hg = within / a.GT, hh = within - hg * a.GT;
+    dst = ((((size_t)b * a.Hkv + hkv) * a.HG + hg) * D + i) * a.GT + hh;
+  }
   a.qt[dst] = x;
   if (i == 0 && row < a.ncnt) a.cnt[row] = 0u;
   if constexpr (KQ) {
@@ -1790,6 +1799,301 @@ __global__ __launch_bounds__(256) void window_kernel(const WindowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Multi-query (chunked-prefill) attention over the compressed cache ("Your KV
+// cache is not a bit problem but a geometry problem", "Systems tax": a prompt
+// chunk is appended along the token axis, then its queries read the cache).
+// Each query row (query token i, head g of a KV head) attends to slots
+// [0, n_ctx), or [0, min(n_ctx, q_pos0 + i + 1)) when causal.  The scan is a
+// tile contraction on fp32 MFMA (v_mfma_f32_16x16x4_f32: exact fp32 products,
+// fp32 sums).  A block owns 64 rows of one (b, KV head); each wave 16 rows.
+// Per 16-token block a wave forms S^T = K^ Q'^T (M = tokens, N = rows, K =
+// coordinates; A = centroids looked up from the LDS-staged codes, B = q' held
+// in registers), so lane l holds the base-2 logits of row l%16 for tokens
+// 4 (l/16) .. 4 (l/16) + 3; the online softmax runs on those registers, and the
+// same registers are the A operand of O' += P V^ (one MFMA per token of the
+// four: the contraction index of MFMA r is token 4 (l/16) + r), with
+// c = p n_v folded into A and B = C_V[code].  The V sketch term accumulates
+// a += (c rho_v) (2 sigma - 1) the same way.  Rows are finished by
+// finish_kernel (S^T a, inverse rotation).
+// ---------------------------------------------------------------------------
+template <int BITS>
+__device__ __forceinline__ uint32_t kcode_at(const uint32_t *w, int kk, int g, int dwords2) {
+  // coordinate c = 4 kk + g of a record image (layout as in place_code)
+  if constexpr (BITS == 4) return (w[kk >> 1] >> (16 * (kk & 1) + 4 * g)) & 15u;
+  if constexpr (BITS == 2) return (w[kk >> 2] >> (8 * (kk & 3) + 2 * g)) & 3u;
+  if constexpr (BITS == 1) return (w[kk >> 3] >> (4 * (kk & 7) + g)) & 1u;
+  const uint32_t lo = (w[kk >> 2] >> (8 * (kk & 3) + 2 * g)) & 3u;
+  const uint32_t hi = (w[dwords2 + (kk >> 3)] >> (4 * (kk & 7) + g)) & 1u;
+  return lo | (hi << 2);
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t vcode_at(const uint32_t *w, int cb, int j, int dwords2) {
+  // coordinate c = 16 cb + j
+  if constexpr (BITS == 4) {
+    // word 2 cb + (j >= 8), chosen by a mask (a selected array index would
+    // send the record image to scratch)
+    const uint32_t m = 0u - (uint32_t)(j >> 3);
+    const uint32_t x = (w[2 * cb + 1] & m) | (w[2 * cb] & ~m);
+    return (x >> (4 * (j & 7))) & 15u;
+  }
+  if constexpr (BITS == 2) return (w[cb] >> (2 * j)) & 3u;
+  if constexpr (BITS == 1) return (w[cb >> 1] >> (16 * (cb & 1) + j)) & 1u;
+  const uint32_t lo = (w[cb] >> (2 * j)) & 3u;
+  const uint32_t hi = (w[dwords2 + (cb >> 1)] >> (16 * (cb & 1) + j)) & 1u;
+  return lo | (hi << 2);
+}
+
+// Copy ntok records of rb bytes (2-byte multiples, contiguous in memory) into
+// LDS rows of pitch `pitch` bytes, with halfword accesses (records are 2-byte
+// aligned); all 256 threads.
+__device__ __forceinline__ void stage_records(unsigned char *dst, int pitch, const uint8_t *src,
+                                              int rb, int ntok, int tid) {
+  const int nh = ntok * rb / 2;
+  const uint16_t *s16 = (const uint16_t *)src;
+  for (int k = tid; k < nh; k += 256) {
+    const int t = (2 * k) / rb, off = 2 * k - t * rb;
+    *(uint16_t *)(dst + t * pitch + off) = s16[k];
+  }
+}
+
+template <int D, int KB, bool KQ, int VB, bool VQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(const PrefillArgs a) {
+  constexpr int TT = 64;                              // tokens per staged tile
+  constexpr int KBYTES = D * KB / 8, VBYTES = D * VB / 8, SBYTES = D / 8;
+  constexpr int KP = (KBYTES + 15) / 16 * 16, VP = (VBYTES + 15) / 16 * 16;
+  constexpr int SP = (SBYTES + 15) / 16 * 16;
+  constexpr int KW = KP / 4, VW = VP / 4, SW = SP / 4;
+  constexpr int NKK = D / 4, NCB = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char kc_s[TT * KP];
+  __shared__ __attribute__((aligned(16))) unsigned char vc_s[TT * VP];
+  __shared__ __attribute__((aligned(16))) unsigned char ks_s[KQ ? TT * SP : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char vs_s[VQ ? TT * SP : 16];
+  __shared__ __attribute__((aligned(16))) float kn_s[TT], kr_s[TT], vn_s[TT], vr_s[TT];
+  __shared__ float kct_s[16], vct_s[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, j = lane & 15;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  const size_t unit = (size_t)b * a.Hkv + hkv;
+  const int NR = a.nq * a.G;
+  const int R0 = blockIdx.x * 64 + wave * 16;         // first row of this wave
+  if (tid < 16) {
+    kct_s[tid] = a.kcent[tid];
+    vct_s[tid] = a.vcent[tid];
+  }
+  // visible tokens of this lane's row (row j), of the wave and of the block
+  auto t_limit = [&](int R) {
+    if (!a.causal) return a.n_ctx;
+    const int lim = a.q_pos0 + R / a.G + 1;
+    return lim < a.n_ctx ? lim : a.n_ctx;
+  };
+  const int Rj = R0 + j;
+  const int tl = Rj < NR ? t_limit(Rj) : 0;
+  const int tl_w = R0 < NR ? t_limit(min(R0 + 15, NR - 1)) : 0;
+  const int tl_b = t_limit(min((int)blockIdx.x * 64 + 63, NR - 1));
+
+  // B operands of the score MFMAs: q'[row j][4 kk + g4]
+  float qB[NKK], sqB[KQ ? NKK : 1];
+  {
+    const float *qrow = a.qt + (unit * NR + (Rj < NR ? Rj : 0)) * D;
+    const float *sqrow = KQ ? a.sqt + (unit * NR + (Rj < NR ? Rj : 0)) * D : nullptr;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qB[kk] = Rj < NR ? qrow[4 * kk + g4] : 0.0f;
+      if constexpr (KQ) sqB[kk] = Rj < NR ? sqrow[4 * kk + g4] : 0.0f;
+    }
+  }
+  f32x4v acc_o[NCB], acc_a[VQ ? NCB : 1];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    acc_o[cb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (VQ) acc_a[cb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float M = -INFINITY, L = 0.0f;                      // row j (replicated over g4)
+
+  for (int tbase = 0; tbase < tl_b; tbase += TT) {
+    const int ntok = min(TT, tl_b - tbase);
+    const size_t rec0 = unit * a.cap + tbase;
+    __syncthreads();                                  // previous tile consumed
+    stage_records(kc_s, KP, a.kc + rec0 * KBYTES, KBYTES, ntok, tid);
+    stage_records(vc_s, VP, a.vc + rec0 * VBYTES, VBYTES, ntok, tid);
+    if constexpr (KQ) stage_records(ks_s, SP, a.ks + rec0 * SBYTES, SBYTES, ntok, tid);
+    if constexpr (VQ) stage_records(vs_s, SP, a.vs + rec0 * SBYTES, SBYTES, ntok, tid);
+    if (tid < TT) {
+      const bool ok = tid < ntok;
+      kn_s[tid] = ok ? f16_bits_to_f32(a.kn[rec0 + tid]) : 0.0f;
+      vn_s[tid] = ok ? f16_bits_to_f32(a.vn[rec0 + tid]) : 0.0f;
+      kr_s[tid] = (KQ && ok) ? f16_bits_to_f32(a.kr[rec0 + tid]) : 0.0f;
+      vr_s[tid] = (VQ && ok) ? f16_bits_to_f32(a.vr[rec0 + tid]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int tb = 0; tb < TT / 16; ++tb) {
+      const int t16 = tbase + 16 * tb;
+      if (t16 >= tl_w) break;                         // past every row of this wave
+      // ---- scores S^T[token 4 g4 + r][row j] ----
+      f32x4v sc = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4v sk = {0.0f, 0.0f, 0.0f, 0.0f};
+      {
+        const int ta = 16 * tb + j;                   // A-operand token (local index)
+        uint32_t kw[KW];
+#pragma unroll
+        for (int q = 0; q < KW / 4; ++q) {
+          const u32x4 v = *(const u32x4 *)(kc_s + ta * KP + 16 * q);
+          kw[4 * q] = v.x; kw[4 * q + 1] = v.y; kw[4 * q + 2] = v.z; kw[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const float av = kct_s[kcode_at<KB>(kw, kk, g4, D / 16)];
+          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qB[kk], sc, 0, 0, 0);
+        }
+        if constexpr (KQ) {
+          uint32_t sw[SW];
+#pragma unroll
+          for (int q = 0; q < SW / 4; ++q) {
+            const u32x4 v = *(const u32x4 *)(ks_s + ta * SP + 16 * q);
+            sw[4 * q] = v.x; sw[4 * q + 1] = v.y; sw[4 * q + 2] = v.z; sw[4 * q + 3] = v.w;
+          }
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const float sg = ((sw[kk >> 3] >> (4 * (kk & 7) + g4)) & 1u) ? 1.0f : -1.0f;
+            sk = __builtin_amdgcn_mfma_f32_16x16x4f32(sg, sqB[kk], sk, 0, 0, 0);
+          }
+        }
+      }
+      const int tr0 = 16 * tb + 4 * g4;               // local token of register r = 0
+      const float4 knv = *(const float4 *)(kn_s + tr0);
+      const float4 vnv = *(const float4 *)(vn_s + tr0);
+      const float kn4[4] = {knv.x, knv.y, knv.z, knv.w};
+      const float vn4[4] = {vnv.x, vnv.y, vnv.z, vnv.w};
+      float kr4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, vr4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (KQ) {
+        const float4 v = *(const float4 *)(kr_s + tr0);
+        kr4[0] = v.x; kr4[1] = v.y; kr4[2] = v.z; kr4[3] = v.w;
+      }
+      if constexpr (VQ) {
+        const float4 v = *(const float4 *)(vr_s + tr0);
+        vr4[0] = v.x; vr4[1] = v.y; vr4[2] = v.z; vr4[3] = v.w;
+      }
+      // ---- online softmax (base 2) over the 16 tokens, row j ----
+      float s[4], p[4];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = sc[r];
+        if constexpr (KQ) v = fmaf(a.kcoef * kr4[r], sk[r], v);
+        v = kn4[r] * v;
+        s[r] = (tbase + tr0 + r < tl) ? v : -INFINITY;
+        mloc = fmaxf(mloc, s[r]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float Mn = fmaxf(M, mloc);
+      const float alpha = (Mn == -INFINITY) ? 1.0f : fast_exp2(M - Mn);
+      float ps = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = (s[r] == -INFINITY) ? 0.0f : fast_exp2(s[r] - Mn);
+        ps += p[r];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      L = fmaf(alpha, L, ps);
+      M = Mn;
+      // rescale the accumulators: their rows are 4 g4 + rr
+      float al[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) al[rr] = __shfl(alpha, 4 * g4 + rr, 64);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          acc_o[cb][rr] *= al[rr];
+          if constexpr (VQ) acc_a[cb][rr] *= al[rr];
+        }
+      // ---- O' += P V^, a += P (rho_v sign) ----
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tv = tr0 + r;                       // this lane's token for MFMA r
+        const float c = p[r] * vn4[r];
+        uint32_t vw[VW];
+#pragma unroll
+        for (int q = 0; q < VW / 4; ++q) {
+          const u32x4 v = *(const u32x4 *)(vc_s + tv * VP + 16 * q);
+          vw[4 * q] = v.x; vw[4 * q + 1] = v.y; vw[4 * q + 2] = v.z; vw[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const float bv = vct_s[vcode_at<VB>(vw, cb, j, D / 16)];
+          acc_o[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv, acc_o[cb], 0, 0, 0);
+        }
+        if constexpr (VQ) {
+          const float cq = c * vr4[r];
+          uint32_t sw[SW];
+#pragma unroll
+          for (int q = 0; q < SW / 4; ++q) {
+            const u32x4 v = *(const u32x4 *)(vs_s + tv * SP + 16 * q);
+            sw[4 * q] = v.x; sw[4 * q + 1] = v.y; sw[4 * q + 2] = v.z; sw[4 * q + 3] = v.w;
+          }
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const float sg = ((sw[cb >> 1] >> (16 * (cb & 1) + j)) & 1u) ? 1.0f : -1.0f;
+            acc_a[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(cq, sg, acc_a[cb], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // rows 4 g4 + rr: o' / L and a / L
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int R = R0 + 4 * g4 + rr;
+    const float Lr = __shfl(L, 4 * g4 + rr, 64);
+    if (R < NR) {
+      float *dst = a.part + (unit * NR + R) * (2 * D);
+      const float inv = 1.0f / Lr;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        dst[16 * cb + j] = acc_o[cb][rr] * inv;
+        if constexpr (VQ) dst[D + 16 * cb + j] = acc_a[cb][rr] * inv;
+      }
+    }
+  }
+}
+
+// Finish of multi-query rows (one block of D threads per row):
+//   o = R^T (o' + sqrt(pi/2)/m S^T a)   (o', a already divided by L)
+template <int D, int RK, bool VQ>
+__global__ __launch_bounds__(D) void finish_kernel(const FinishArgs a) {
+  __shared__ float t_s[D];
+  __shared__ float a_s[D];
+  const int i = threadIdx.x;
+  const int NR = a.nq * a.G;
+  const size_t ridx = blockIdx.x;
+  const size_t unit = ridx / NR;
+  const int R = (int)(ridx - unit * NR);
+  const int b = (int)(unit / a.Hkv), hkv = (int)(unit - (size_t)b * a.Hkv);
+  const int tq = R / a.G, g = R - tq * a.G;
+  const float *src = a.part + ridx * (2 * D);
+  float v = src[i];
+  if constexpr (VQ) {
+    a_s[i] = src[D + i];
+    __syncthreads();
+    float acc = 0.0f;
+    for (int k = 0; k < D; ++k) acc = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), a_s[k], acc);
+    v = fmaf(a.vcoef, acc, v);
+  }
+  if constexpr (RK == RK_WHT || RK == RK_RHT) v = wht_block<D>(t_s, v) * a.oscale;
+  if constexpr (RK == RK_RHT) v = ((a.rsign[i >> 5] >> (i & 31)) & 1u) ? -v : v;
+  if constexpr (RK == RK_QR) {
+    t_s[i] = v;
+    __syncthreads();
+    v = dense_rotate_back<D>(a.Q, t_s, i);
+  }
+  a.out[(((size_t)b * a.nq + tq) * a.Hq + hkv * a.G + g) * D + i] = v;
+}
+
+// ---------------------------------------------------------------------------
 // Dispatchers (host).  Only the (bits, rotation, sketch) combinations that the
 // three schemes produce are instantiated.
 // ---------------------------------------------------------------------------
@@ -1969,6 +2273,55 @@ hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows
   return hipGetLastError();
 }
 
+template <int D, int KB, bool KQ, int VB, bool VQ>
+hipError_t prefill_go(const PrefillArgs &a, int B, hipStream_t s) {
+  const int NR = a.nq * a.G;
+  const dim3 grid((NR + 63) / 64, a.Hkv, B), blk(256);
+  hipLaunchKernelGGL((prefill_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill(const PrefillArgs &a, int kb, bool kq, int vb, bool vq, int B,
+                          hipStream_t s) {
+  if (!kq && !vq && kb == vb) {  // KV
+    switch (kb) {
+      case 1: return prefill_go<D, 1, false, 1, false>(a, B, s);
+      case 2: return prefill_go<D, 2, false, 2, false>(a, B, s);
+      case 3: return prefill_go<D, 3, false, 3, false>(a, B, s);
+      case 4: return prefill_go<D, 4, false, 4, false>(a, B, s);
+    }
+  } else if (!kq && vq && vb == kb - 1) {  // KQV
+    switch (kb) {
+      case 2: return prefill_go<D, 2, false, 1, true>(a, B, s);
+      case 3: return prefill_go<D, 3, false, 2, true>(a, B, s);
+      case 4: return prefill_go<D, 4, false, 3, true>(a, B, s);
+    }
+  } else if (kq && vq && kb == vb) {  // QKQV
+    switch (kb) {
+      case 1: return prefill_go<D, 1, true, 1, true>(a, B, s);
+      case 2: return prefill_go<D, 2, true, 2, true>(a, B, s);
+      case 3: return prefill_go<D, 3, true, 3, true>(a, B, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_finish(const FinishArgs &a, bool vq, int rows, hipStream_t s) {
+  const dim3 g(rows), blk(D);
+#define KVQ_FIN(R, V) hipLaunchKernelGGL((finish_kernel<D, R, V>), g, blk, 0, s, a)
+  switch (a.rk) {
+    case RK_NONE: if (vq) return hipErrorInvalidValue; KVQ_FIN(RK_NONE, false); break;
+    case RK_WHT: if (vq) KVQ_FIN(RK_WHT, true); else KVQ_FIN(RK_WHT, false); break;
+    case RK_RHT: if (vq) KVQ_FIN(RK_RHT, true); else KVQ_FIN(RK_RHT, false); break;
+    case RK_QR: if (vq) KVQ_FIN(RK_QR, true); else KVQ_FIN(RK_QR, false); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KVQ_FIN
+  return hipGetLastError();
+}
+
 #define KVQ_INSTANTIATE(D)                                                                     \
   template hipError_t launch_quantize<D>(const QuantArgs &, int, int, bool, bool, hipStream_t); \
   template hipError_t launch_dequantize<D>(const DequantArgs &, int, int, bool, int,            \
@@ -1976,6 +2329,9 @@ hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows
   template hipError_t launch_prep<D>(const PrepArgs &, int, bool, bool, hipStream_t);           \
   template hipError_t launch_decode<D>(const DecodeArgs &, int, bool, int, bool, int, int,      \
                                        hipStream_t);                                            \
-  template hipError_t launch_window<D>(const WindowArgs &, bool, bool, int, hipStream_t);
+  template hipError_t launch_window<D>(const WindowArgs &, bool, bool, int, hipStream_t);     \
+  template hipError_t launch_prefill<D>(const PrefillArgs &, int, bool, int, bool, int,        \
+                                        hipStream_t);                                           \
+  template hipError_t launch_finish<D>(const FinishArgs &, bool, int, hipStream_t);
 
 }  // namespace kvq

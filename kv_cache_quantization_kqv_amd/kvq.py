@@ -28,7 +28,7 @@ EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_
            "kvq_rotation_signs", "kvq_rotation_qr", "kvq_cache_layout", "kvq_quantize_k",
            "kvq_quantize_v", "kvq_dequantize", "kvq_decode_attention",
            "kvq_decode_attention_window", "kvq_decode_workspace", "kvq_decode_auto_splits",
-           "kvq_status_str", "kvq_version"]
+           "kvq_prefill_attention", "kvq_prefill_workspace", "kvq_status_str", "kvq_version"]
 
 
 class KVQError(RuntimeError):
@@ -85,6 +85,9 @@ def lib():
                                              i32, vp, vp, sz, vp], i32),
             "kvq_decode_workspace": ([cache_p, i32, i32, i32, C.POINTER(sz)], i32),
             "kvq_decode_auto_splits": ([cache_p, i32, i32], i32),
+            "kvq_prefill_attention": ([cache_p, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp],
+                                      i32),
+            "kvq_prefill_workspace": ([cache_p, i32, i32, C.POINTER(sz)], i32),
             "kvq_status_str": ([i32], C.c_char_p),
             "kvq_version": ([], C.c_char_p),
         }
@@ -196,6 +199,21 @@ def kvq_decode_attention_window(c: kvq_cache, q: int, q_dtype: int, q_heads: int
                                              stream), "kvq_decode_attention_window")
 
 
+def kvq_prefill_workspace(c: kvq_cache, q_heads: int, n_q: int) -> int:
+    n = C.c_size_t()
+    _check(lib().kvq_prefill_workspace(C.byref(c), q_heads, n_q, C.byref(n)),
+           "kvq_prefill_workspace")
+    return n.value
+
+
+def kvq_prefill_attention(c: kvq_cache, q: int, q_dtype: int, q_heads: int, n_q: int,
+                          q_pos0: int, causal: int, n_ctx: int, out: int, workspace: int,
+                          ws_bytes: int, stream: int = 0):
+    _check(lib().kvq_prefill_attention(C.byref(c), q, q_dtype, q_heads, n_q, q_pos0, causal,
+                                       n_ctx, out, workspace, ws_bytes, stream),
+           "kvq_prefill_attention")
+
+
 # ------------------------------------------------------------------ torch-owned cache
 class KVQCache:
     """A compressed KV cache whose buffers are torch device tensors.
@@ -305,6 +323,27 @@ class KVQCache:
             out = torch.empty(self.batch, Hq, self.d, dtype=torch.float32, device=self.device)
         kvq_decode_attention(self.c, q.data_ptr(), dt, Hq, n_ctx, splits, out.data_ptr(),
                              workspace.data_ptr(), workspace.numel(), self._stream())
+        return out
+
+    def prefill_attention(self, q, q_pos0: int, n_ctx: int, causal: bool = True, out=None,
+                          workspace=None):
+        """Multi-query attention of q [B][n_q][q_heads][d] (query token i at
+        position q_pos0 + i) over cache slots [0, n_ctx); out [B][n_q][q_heads][d]."""
+        torch = self.torch
+        if q.dim() != 4 or q.shape[0] != self.batch or q.shape[3] != self.d or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B][n_q][q_heads][d] tensor")
+        dt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}.get(q.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported dtype {q.dtype}")
+        n_q, Hq = q.shape[1], q.shape[2]
+        nbytes = kvq_prefill_workspace(self.c, Hq, n_q)
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        if out is None:
+            out = torch.empty(self.batch, n_q, Hq, self.d, dtype=torch.float32, device=self.device)
+        kvq_prefill_attention(self.c, q.data_ptr(), dt, Hq, n_q, q_pos0, int(bool(causal)), n_ctx,
+                              out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                              self._stream())
         return out
 
     def decode_attention_window(self, q, t_begin: int, t_end: int, wk=None, wv=None,

@@ -317,3 +317,25 @@ def attention_window(kc: OracleCache, vc: OracleCache, q: np.ndarray, t_begin: i
         for hq in range(Hq):
             out[b, hq] = attention_dense(qd[b, hq], Kh[b, hq // G], Vh[b, hq // G])
     return out
+
+
+def prefill_attention(kc: OracleCache, vc: OracleCache, q: np.ndarray, q_pos0: int, causal: bool,
+                      n_ctx: int, S: np.ndarray | None, nthreads: int = 1) -> np.ndarray:
+    """Multi-query attention of q [B][n_q][Hq][d] (float32 or bf16 bits) over
+    the reconstructed cache slots [0, n_ctx); query token i sits at position
+    q_pos0 + i and, when causal, sees slots t <= q_pos0 + i ("Your KV cache is
+    not a bit problem but a geometry problem", "Systems tax": a prompt chunk
+    is appended, then attends).  Plain fp64 attention per row.  Returns fp64
+    [B][n_q][Hq][d]."""
+    qd = _host_f64(np.ascontiguousarray(q))
+    B, nq, Hq, d = qd.shape
+    G = Hq // kc.H
+    Kh = kc.dequantize(0, n_ctx, S, nthreads)
+    Vh = vc.dequantize(0, n_ctx, S, nthreads)
+    out = np.zeros((B, nq, Hq, d), np.float64)
+    for b in range(B):
+        for i in range(nq):
+            T = min(n_ctx, q_pos0 + i + 1) if causal else n_ctx
+            for hq in range(Hq):
+                out[b, i, hq] = attention_dense(qd[b, i, hq], Kh[b, hq // G, :T], Vh[b, hq // G, :T])
+    return out

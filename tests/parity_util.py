@@ -72,6 +72,10 @@ class Pair:
         return ref.attention(self.ok, self.ov, host_bits(q), n_ctx, self.S, rows=rows,
                              nthreads=nthreads)
 
+    def prefill(self, q: torch.Tensor, q_pos0: int, causal: bool, n_ctx: int, nthreads=8):
+        return ref.prefill_attention(self.ok, self.ov, host_bits(q), q_pos0, causal, n_ctx, self.S,
+                                     nthreads)
+
     def attention_window(self, q: torch.Tensor, t_begin: int, t_end: int, wk=None, wv=None,
                          nthreads=8):
         return ref.attention_window(self.ok, self.ov, host_bits(q), t_begin, t_end,

@@ -345,3 +345,46 @@ def test_dequantize_and_decode_rotations(rotation, d):
         wk, wv = K[:, :, 300:].contiguous(), V[:, :, 300:].contiguous()
         got = P.gpu.decode_attention_window(q.cuda(), 0, 300, wk.cuda(), wv.cuda()).cpu().numpy()
         assert rel_rows(got, P.attention_window(q, 0, 300, wk, wv)).max() < 1e-5
+
+
+PREFILL_SCHEMES = [("KV", 4), ("KV", 2), ("KQV", 4), ("KQV", 3), ("KQV", 2), ("QKQV", 3),
+                   ("QKQV", 2)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("d,G", [(16, 2), (32, 4), (64, 1), (128, 4), (128, 8)])
+@pytest.mark.parametrize("scheme,n", PREFILL_SCHEMES, ids=[f"{s}{n}" for s, n in PREFILL_SCHEMES])
+def test_prefill_matches_oracle(scheme, n, d, G, dtype):
+    """Chunked prefill: a chunk of 37 query tokens at positions 150..186 over a
+    cache of 187 slots, causal; and the same queries non-causally over every
+    slot.  Rows span several 64-row tiles and the token range several 64-token
+    tiles with ragged ends."""
+    print(f"case prefill {scheme}{n} d={d} G={G} {dtype}", flush=True)
+    B, Hkv, nq, p0 = 2, 2, 37, 150
+    N = p0 + nq
+    P = Pair(scheme, n, d, B, Hkv, N + 5)
+    K, V = _inputs(B, Hkv, N, d, dtype, 1800 + d + n, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, nq, Hkv * G, d), 1900 + d + G, dtype)
+    for causal in (True, False):
+        got = P.gpu.prefill_attention(q.cuda(), p0, N, causal=causal).cpu().numpy()
+        err = rel_rows(got, P.prefill(q, p0, causal, N))
+        assert err.max() < TOL[dtype], (causal, err.max())
+
+
+@pytest.mark.parametrize("rotation", ["rht", "qr"])
+def test_prefill_rotations_and_short_chunks(rotation):
+    """Rotation variants; a single-token chunk (equals decode over the same
+    slots); a chunk at the start of the cache (first row sees one slot)."""
+    print(f"case prefill-rot {rotation}", flush=True)
+    B, Hkv, G, d, N = 1, 2, 4, 128, 200
+    P = Pair("KQV", 4, d, B, Hkv, N, rotation=rotation)
+    K, V = _inputs(B, Hkv, N, d, torch.float32, 2000, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, 70, Hkv * G, d), 2001, torch.float32)
+    got = P.gpu.prefill_attention(q.cuda(), 0, N, causal=True).cpu().numpy()
+    assert rel_rows(got, P.prefill(q, 0, True, N)).max() < 1e-5
+    q1 = q[:, :1].contiguous()
+    one = P.gpu.prefill_attention(q1.cuda(), N - 1, N, causal=True)[:, 0]
+    dec = P.gpu.decode_attention(q1[:, 0].contiguous().cuda(), N)
+    assert rel_rows(one.cpu().numpy(), dec.cpu().numpy().astype(np.float64)).max() < 1e-5

@@ -320,3 +320,31 @@ def test_cache_set_rotation_validation(K):
     assert lib.kvq_quantize_k(C.byref(bad), 0x900000, 1, 0, 4, 0, 0, 32, None) == 10
     kv.rot_kind = 1
     assert lib.kvq_quantize_k(C.byref(kv), 0x900000, 1, 0, 4, 0, 0, 64, None) == 5
+
+
+def test_prefill_validation_status_codes(K):
+    lib = K.lib()
+    c = _fake_cache(K)                               # KQV-4, d = 64, B = 1, Hkv = 2, cap = 32
+    p = C.byref(c)
+    ws = C.c_size_t()
+    assert lib.kvq_prefill_workspace(p, 3, 5, C.byref(ws)) == 9
+    assert lib.kvq_prefill_workspace(p, 6, 0, C.byref(ws)) == 10
+    assert lib.kvq_prefill_workspace(p, 6, 5, C.byref(ws)) == 0   # G = 3 is fine here
+    assert ws.value == 4 * 1 * 6 * 5 * 64 * 3                     # q', o', a (no K sketch)
+    need = ws.value
+    q, out, w = 0xA00000, 0xB00000, 0xC00000
+    f = lib.kvq_prefill_attention
+    assert f(p, q, 1, 6, 5, 0, 1, 8, out, w, need - 1, None) == 7
+    assert f(p, q, 1, 6, 5, 0, 1, 8, out, None, need, None) == 7
+    assert f(p, q, 3, 6, 5, 0, 1, 8, out, w, need, None) == 8
+    assert f(p, q + 4, 1, 6, 5, 0, 1, 8, out, w, need, None) == 2
+    assert f(p, None, 1, 6, 5, 0, 1, 8, out, w, need, None) == 1
+    assert f(p, q, 1, 6, 5, -1, 1, 8, out, w, need, None) == 10
+    assert f(p, q, 1, 6, 5, 0, 2, 8, out, w, need, None) == 10
+    assert f(p, q, 1, 6, 5, 0, 1, 0, out, w, need, None) == 10
+    assert f(p, q, 1, 6, 5, 0, 1, 33, out, w, need, None) == 6
+    assert f(p, q, 1, 6, 0, 0, 1, 8, out, w, need, None) == 10
+    assert f(p, q, 1, 5, 5, 0, 1, 8, out, w, need, None) == 9
+    q3 = _fake_cache(K, scheme="QKQV", n=3)
+    assert lib.kvq_prefill_workspace(C.byref(q3), 2, 7, C.byref(ws)) == 0
+    assert ws.value == 4 * 1 * 2 * 7 * 64 * 4                     # + S q'

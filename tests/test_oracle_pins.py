@@ -682,3 +682,32 @@ def test_rotations_under_the_mse_bound(orc, bits):
     for name in ("rht", "qr"):
         assert err[name] <= tq and err[name] / d <= cst * 4.0 ** -bits, (name, err[name], tq)
         assert abs(err[name] - Db) < 0.1 * Db, (name, err[name], Db)
+
+
+@pytest.mark.parametrize("scheme", ["KV", "KQV", "QKQV"])
+def test_prefill_attention_reductions(orc, scheme):
+    """Multi-query attention ("Your KV cache is not a bit problem but a
+    geometry problem", "Systems tax": a chunk is appended, then its queries
+    attend).  Checked against (1) a masked score matrix and a numpy softmax
+    over the dequantised cache (causal mask t <= q_pos0 + i), (2) the C
+    oracle's decode attention for the last query of a causal chunk that ends
+    at the cache end, and for every query of a non-causal chunk."""
+    B, Hkv, Hq, d, n_ctx, nq, p0 = 2, 2, 4, 8, 13, 5, 8
+    rng, S, kc, vc, _ = _window_case(scheme, 41)
+    q = rng.standard_normal((B, nq, Hq, d)).astype(np.float32)
+    out = orc.prefill_attention(kc, vc, q, p0, True, n_ctx, S)
+    Kh, Vh = kc.dequantize(0, n_ctx, S), vc.dequantize(0, n_ctx, S)
+    for b in range(B):
+        for hq in range(Hq):
+            s = q[b, :, hq].astype(np.float64) @ Kh[b, hq // 2].T / math.sqrt(d)   # [nq][n_ctx]
+            mask = np.arange(n_ctx)[None, :] <= (p0 + np.arange(nq))[:, None]
+            s = np.where(mask, s, -np.inf)
+            pr = np.exp(s - s.max(1, keepdims=True))
+            want = (pr / pr.sum(1, keepdims=True)) @ Vh[b, hq // 2]
+            assert np.allclose(out[b, :, hq], want, rtol=1e-12, atol=1e-13)
+    last = orc.prefill_attention(kc, vc, q, n_ctx - nq, True, n_ctx, S)[:, -1]
+    assert np.allclose(last, orc.attention(kc, vc, q[:, -1], n_ctx, S), rtol=1e-12, atol=1e-13)
+    full = orc.prefill_attention(kc, vc, q, 0, False, n_ctx, S)
+    for i in range(nq):
+        assert np.allclose(full[:, i], orc.attention(kc, vc, q[:, i], n_ctx, S), rtol=1e-12,
+                           atol=1e-13)
