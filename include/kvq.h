@@ -260,7 +260,9 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes kvq_prefill_attention needs:
- * 4 * B * q_heads * n_q * d * (3 + [K sketched]). */
+ * 4 * B * q_heads * n_q * (d * (1 + [K sketched]) + S * (2 + 2 d)), S the
+ * token splits the library uses for this shape (more when the rows alone do
+ * not fill the GPU; at most 64). */
 kvq_status kvq_prefill_workspace(const kvq_cache *c, int q_heads, int n_q, size_t *bytes);
 
 /* Static text for a status code. */

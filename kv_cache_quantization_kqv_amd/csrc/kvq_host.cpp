@@ -305,6 +305,18 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
 
 int heads_per_block(int G) { return G >= 4 ? 4 : G; }
 
+// Token splits of a multi-query call: enough blocks to fill the GPU (about
+// 1024) when the rows alone do not, at least 256 slots per split.
+int prefill_splits(const kvq_cache *c, int q_heads, int n_q) {
+  const long long NR = (long long)n_q * (q_heads / c->kv_heads);
+  const long long blocks = (NR + 63) / 64 * c->kv_heads * c->batch;
+  long long sp = (1024 + blocks - 1) / blocks;
+  const long long cap_sp = (c->capacity + 255) / 256;
+  if (sp > cap_sp) sp = cap_sp;
+  if (sp > 64) sp = 64;
+  return sp < 1 ? 1 : (int)sp;
+}
+
 // Split arrival counters, one per (b, KV head, head group), padded to 16 bytes.
 size_t counter_bytes(const kvq_cache *c, int q_heads) {
   const int G = q_heads / c->kv_heads;
@@ -662,8 +674,9 @@ kvq_status kvq_prefill_workspace(const kvq_cache *c, int q_heads, int n_q, size_
   if (n_q < 1) return KVQ_ERR_RANGE;
   const size_t rows = (size_t)c->batch * q_heads * n_q;
   if (rows > ((size_t)1 << 31) - 1) return KVQ_ERR_RANGE;
-  // prepared q' (and S q'), then o' and a per row
-  *bytes = sizeof(float) * rows * c->d * (1 + (c->k_qjl ? 1 : 0) + 2);
+  const size_t S = (size_t)prefill_splits(c, q_heads, n_q);
+  // prepared q' (and S q'), then per row and token split (M, L, o', a)
+  *bytes = sizeof(float) * rows * ((size_t)c->d * (1 + (c->k_qjl ? 1 : 0)) + S * (2 + 2 * (size_t)c->d));
   return KVQ_OK;
 }
 
@@ -717,6 +730,12 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.Hkv = c->kv_heads; a.G = G; a.cap = c->capacity; a.nq = n_q; a.q_pos0 = q_pos0;
   a.n_ctx = n_ctx; a.causal = causal;
+  {
+    const int smax = prefill_splits(c, q_heads, n_q);
+    const int per = (n_ctx + smax - 1) / smax;
+    a.tps = (per + 63) / 64 * 64;
+    a.splits = (n_ctx + a.tps - 1) / a.tps;
+  }
   e = by_dim(d, [&](auto D) {
     return kvq::launch_prefill<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
                                                    c->v_qjl != 0, c->batch, hs);
@@ -731,7 +750,8 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   f.rk = rk;
   for (int k = 0; k < 4; ++k) f.rsign[k] = c->rot_signs[k];
   f.Q = c->rot_Q;
-  f.Hkv = c->kv_heads; f.Hq = q_heads; f.G = G; f.nq = n_q;
+  f.Hkv = c->kv_heads; f.Hq = q_heads; f.G = G; f.nq = n_q; f.rows = (int)rows;
+  f.splits = a.splits;
   e = by_dim(d, [&](auto D) {
     return kvq::launch_finish<decltype(D)::value>(f, c->v_qjl != 0, (int)rows, hs);
   });

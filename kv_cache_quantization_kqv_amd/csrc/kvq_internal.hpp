@@ -93,15 +93,16 @@ struct PrefillArgs {
   const uint8_t *kc, *ks, *vc, *vs;
   const uint16_t *kn, *kr, *vn, *vr;
   const float *qt, *sqt;     // prepared queries [B][Hkv][NR][d], NR = nq * G (row i * G + g)
-  float *part;               // [B][Hkv][NR][2d]: o' / L, a / L
+  float *part;               // [B][Hkv][NR][splits][2 + 2d]: M (base 2), L, o', a
   float kcent[16], vcent[16];
   float kcoef;               // sqrt(pi/2)/m (K sketch)
   int Hkv, G, cap, nq, q_pos0, n_ctx, causal;
+  int splits, tps;           // token splits per row tile, tokens per split (multiple of 64)
 };
 
 // Finish of a multi-query call, one block per output row: o = R^T (o' + c S^T a).
 struct FinishArgs {
-  const float *part;         // as PrefillArgs::part
+  const float *part;         // as PrefillArgs::part (merged here)
   const uint16_t *S;
   float *out;                // [B][nq][Hq][d]
   float vcoef, oscale;
@@ -109,6 +110,8 @@ struct FinishArgs {
   uint32_t rsign[4];
   const float *Q;
   int Hkv, Hq, G, nq;
+  int rows;                  // B * Hkv * nq * G
+  int splits;
 };
 
 // Full-precision window (sinks and recent tokens): exact partial softmax sums

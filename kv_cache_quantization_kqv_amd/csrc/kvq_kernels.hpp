@@ -1857,15 +1857,19 @@ __device__ __forceinline__ void stage_records(unsigned char *dst, int pitch, con
 }
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(const PrefillArgs a) {
   constexpr int TT = 64;                              // tokens per staged tile
   constexpr int KBYTES = D * KB / 8, VBYTES = D * VB / 8, SBYTES = D / 8;
-  constexpr int KP = (KBYTES + 15) / 16 * 16, VP = (VBYTES + 15) / 16 * 16;
-  constexpr int SP = (SBYTES + 15) / 16 * 16;
-  constexpr int KW = KP / 4, VW = VP / 4, SW = SP / 4;
+  constexpr int SP = (SBYTES + 15) / 16 * 16, SW = SP / 4;
+  constexpr int KWR = (KBYTES + 3) / 4, VWR = (VBYTES + 3) / 4;
   constexpr int NKK = D / 4, NCB = D / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char kc_s[TT * KP];
-  __shared__ __attribute__((aligned(16))) unsigned char vc_s[TT * VP];
+  constexpr int KROW = NKK + 4;                       // padded row of the K tile
+  // Dequantised tiles, laid out for the MFMA operand reads:
+  //   kh_s[t][g][kk] = C_K[code_t(4 kk + g)]   (A of S^T: lane reads 4 kk at once)
+  //   vh_s[t][j][cb] = C_V[code_t(16 cb + j)]  (B of P V: lane reads 4 cb at once)
+  __shared__ __attribute__((aligned(16))) float kh_s[TT * 4 * KROW];
+  __shared__ __attribute__((aligned(16))) float vh_s[TT * 16 * NCB];
   __shared__ __attribute__((aligned(16))) unsigned char ks_s[KQ ? TT * SP : 16];
   __shared__ __attribute__((aligned(16))) unsigned char vs_s[VQ ? TT * SP : 16];
   __shared__ __attribute__((aligned(16))) float kn_s[TT], kr_s[TT], vn_s[TT], vr_s[TT];
@@ -1876,23 +1880,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hkv = blockIdx.y, b = blockIdx.z;
   const size_t unit = (size_t)b * a.Hkv + hkv;
   const int NR = a.nq * a.G;
-  const int R0 = blockIdx.x * 64 + wave * 16;         // first row of this wave
+  const int rt = blockIdx.x / a.splits, split = blockIdx.x - rt * a.splits;
+  const int R0 = rt * 64 + wave * 16;                 // first row of this wave
+  const int t_lo = split * a.tps;                     // this block's slots [t_lo, t_lo + tps)
   if (tid < 16) {
     kct_s[tid] = a.kcent[tid];
     vct_s[tid] = a.vcent[tid];
   }
-  // visible tokens of this lane's row (row j), of the wave and of the block
   auto t_limit = [&](int R) {
     if (!a.causal) return a.n_ctx;
     const int lim = a.q_pos0 + R / a.G + 1;
     return lim < a.n_ctx ? lim : a.n_ctx;
   };
   const int Rj = R0 + j;
-  const int tl = Rj < NR ? t_limit(Rj) : 0;
-  const int tl_w = R0 < NR ? t_limit(min(R0 + 15, NR - 1)) : 0;
-  const int tl_b = t_limit(min((int)blockIdx.x * 64 + 63, NR - 1));
+  // visible slots end at the row's limit and at this split's end
+  const int tl = Rj < NR ? min(t_limit(Rj), t_lo + a.tps) : 0;
+  const int tl_w = min(t_lo + a.tps, R0 < NR ? t_limit(min(R0 + 15, NR - 1)) : 0);
+  const int tl_b = min(t_lo + a.tps, t_limit(min(rt * 64 + 63, NR - 1)));
 
-  // B operands of the score MFMAs: q'[row j][4 kk + g4]
   float qB[NKK], sqB[KQ ? NKK : 1];
   {
     const float *qrow = a.qt + (unit * NR + (Rj < NR ? Rj : 0)) * D;
@@ -1910,13 +1915,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (VQ) acc_a[cb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
   float M = -INFINITY, L = 0.0f;                      // row j (replicated over g4)
+  // dequantisation role of this thread: token dt, quarter dq
+  const int dt = tid & (TT - 1), dq = tid >> 6;
 
-  for (int tbase = 0; tbase < tl_b; tbase += TT) {
+  __syncthreads();                                    // centroid tables
+  for (int tbase = t_lo; tbase < tl_b; tbase += TT) {
     const int ntok = min(TT, tl_b - tbase);
     const size_t rec0 = unit * a.cap + tbase;
     __syncthreads();                                  // previous tile consumed
-    stage_records(kc_s, KP, a.kc + rec0 * KBYTES, KBYTES, ntok, tid);
-    stage_records(vc_s, VP, a.vc + rec0 * VBYTES, VBYTES, ntok, tid);
+    {
+      // K: this thread's quarter g = dq of token dt, every kk
+      const bool ok = dt < ntok;
+      uint32_t kw[KWR + 1];
+      kw[KWR] = 0u;
+      if (ok) load_rec<KBYTES>(a.kc + (rec0 + dt) * KBYTES, kw);
+      float *kd = kh_s + (dt * 4 + dq) * KROW;
+#pragma unroll
+      for (int q4 = 0; q4 < NKK / 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ok ? kct_s[kcode_at<KB>(kw, 4 * q4 + e, dq, D / 16)] : 0.0f;
+        *(float4 *)(kd + 4 * q4) = float4{v[0], v[1], v[2], v[3]};
+      }
+      // V: lanes j = 4 dq .. 4 dq + 3 of token dt, every cb
+      uint32_t vw[VWR + 1];
+      vw[VWR] = 0u;
+      if (ok) load_rec<VBYTES>(a.vc + (rec0 + dt) * VBYTES, vw);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jv = 4 * dq + jj;
+        float *vd = vh_s + (dt * 16 + jv) * NCB;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) vd[cb] = ok ? vct_s[vcode_at<VB>(vw, cb, jv, D / 16)] : 0.0f;
+      }
+    }
     if constexpr (KQ) stage_records(ks_s, SP, a.ks + rec0 * SBYTES, SBYTES, ntok, tid);
     if constexpr (VQ) stage_records(vs_s, SP, a.vs + rec0 * SBYTES, SBYTES, ntok, tid);
     if (tid < TT) {
@@ -1927,26 +1959,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       vr_s[tid] = (VQ && ok) ? f16_bits_to_f32(a.vr[rec0 + tid]) : 0.0f;
     }
     __syncthreads();
-#pragma unroll 1
-    for (int tb = 0; tb < TT / 16; ++tb) {
-      const int t16 = tbase + 16 * tb;
-      if (t16 >= tl_w) break;                         // past every row of this wave
-      // ---- scores S^T[token 4 g4 + r][row j] ----
-      f32x4v sc = {0.0f, 0.0f, 0.0f, 0.0f};
-      f32x4v sk = {0.0f, 0.0f, 0.0f, 0.0f};
+    // scores S^T[token 4 g4 + r][row j] of token block tb (and QKQV's sketch term)
+    auto scores = [&](int tb, f32x4v &sc, f32x4v &sk) {
+      sk = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
       {
         const int ta = 16 * tb + j;                   // A-operand token (local index)
-        uint32_t kw[KW];
+        const float *kr = kh_s + (ta * 4 + g4) * KROW;
+        // four independent accumulation chains (dependent MFMAs would wait
+        // for each other's results)
+        f32x4v c4[4];
 #pragma unroll
-        for (int q = 0; q < KW / 4; ++q) {
-          const u32x4 v = *(const u32x4 *)(kc_s + ta * KP + 16 * q);
-          kw[4 * q] = v.x; kw[4 * q + 1] = v.y; kw[4 * q + 2] = v.z; kw[4 * q + 3] = v.w;
-        }
+        for (int u = 0; u < 4; ++u) c4[u] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const float av = kct_s[kcode_at<KB>(kw, kk, g4, D / 16)];
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qB[kk], sc, 0, 0, 0);
+        for (int q4 = 0; q4 < NKK / 4; ++q4) {
+          const float4 av = *(const float4 *)(kr + 4 * q4);
+          c4[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, qB[4 * q4], c4[0], 0, 0, 0);
+          c4[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, qB[4 * q4 + 1], c4[1], 0, 0, 0);
+          c4[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, qB[4 * q4 + 2], c4[2], 0, 0, 0);
+          c4[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, qB[4 * q4 + 3], c4[3], 0, 0, 0);
         }
+        sc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
         if constexpr (KQ) {
           uint32_t sw[SW];
 #pragma unroll
@@ -1954,13 +1986,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const u32x4 v = *(const u32x4 *)(ks_s + ta * SP + 16 * q);
             sw[4 * q] = v.x; sw[4 * q + 1] = v.y; sw[4 * q + 2] = v.z; sw[4 * q + 3] = v.w;
           }
+          f32x4v k2[2] = {f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4v{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk) {
             const float sg = ((sw[kk >> 3] >> (4 * (kk & 7) + g4)) & 1u) ? 1.0f : -1.0f;
-            sk = __builtin_amdgcn_mfma_f32_16x16x4f32(sg, sqB[kk], sk, 0, 0, 0);
+            k2[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(sg, sqB[kk], k2[kk & 1], 0, 0, 0);
           }
+          sk = k2[0] + k2[1];
         }
       }
+    };
+    // blocks of this tile that some row of the wave can see
+    const int nb = tl_w > tbase ? min(TT / 16, (tl_w - tbase + 15) / 16) : 0;
+#pragma unroll 1
+    for (int tb = 0; tb < nb; ++tb) {
+      f32x4v sc, sk;
+      scores(tb, sc, sk);
       const int tr0 = 16 * tb + 4 * g4;               // local token of register r = 0
       const float4 knv = *(const float4 *)(kn_s + tr0);
       const float4 vnv = *(const float4 *)(vn_s + tr0);
@@ -2000,33 +2041,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ps += __shfl_xor(ps, 32, 64);
       L = fmaf(alpha, L, ps);
       M = Mn;
-      // rescale the accumulators: their rows are 4 g4 + rr
-      float al[4];
+      // rescale the accumulators (rows 4 g4 + rr) unless no row's max moved
+      if (__ballot(alpha != 1.0f)) {
+        float al[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) al[rr] = __shfl(alpha, 4 * g4 + rr, 64);
+        for (int rr = 0; rr < 4; ++rr) al[rr] = __shfl(alpha, 4 * g4 + rr, 64);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          acc_o[cb][rr] *= al[rr];
-          if constexpr (VQ) acc_a[cb][rr] *= al[rr];
-        }
+          for (int rr = 0; rr < 4; ++rr) {
+            acc_o[cb][rr] *= al[rr];
+            if constexpr (VQ) acc_a[cb][rr] *= al[rr];
+          }
+      }
       // ---- O' += P V^, a += P (rho_v sign) ----
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tv = tr0 + r;                       // this lane's token for MFMA r
         const float c = p[r] * vn4[r];
-        uint32_t vw[VW];
+        const float *vr = vh_s + (tv * 16 + j) * NCB;
+        float bv[NCB];
+        if constexpr (NCB >= 4) {
 #pragma unroll
-        for (int q = 0; q < VW / 4; ++q) {
-          const u32x4 v = *(const u32x4 *)(vc_s + tv * VP + 16 * q);
-          vw[4 * q] = v.x; vw[4 * q + 1] = v.y; vw[4 * q + 2] = v.z; vw[4 * q + 3] = v.w;
+          for (int q4 = 0; q4 < NCB / 4; ++q4) {
+            const float4 v = *(const float4 *)(vr + 4 * q4);
+            bv[4 * q4] = v.x; bv[4 * q4 + 1] = v.y; bv[4 * q4 + 2] = v.z; bv[4 * q4 + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) bv[cb] = vr[cb];
         }
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const float bv = vct_s[vcode_at<VB>(vw, cb, j, D / 16)];
-          acc_o[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv, acc_o[cb], 0, 0, 0);
-        }
+        for (int cb = 0; cb < NCB; ++cb)
+          acc_o[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(c, bv[cb], acc_o[cb], 0, 0, 0);
         if constexpr (VQ) {
           const float cq = c * vr4[r];
           uint32_t sw[SW];
@@ -2044,53 +2091,130 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  // rows 4 g4 + rr: o' / L and a / L
+  // partials of rows 4 g4 + rr: M, L, o', a (a split that sees no slot of a
+  // row leaves M = -inf, L = 0 and zero sums)
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int R = R0 + 4 * g4 + rr;
+    const float Mr = __shfl(M, 4 * g4 + rr, 64);
     const float Lr = __shfl(L, 4 * g4 + rr, 64);
     if (R < NR) {
-      float *dst = a.part + (unit * NR + R) * (2 * D);
-      const float inv = 1.0f / Lr;
+      float *dst = a.part + ((unit * NR + R) * a.splits + split) * (2 + 2 * D);
+      if (j == 0) {
+        dst[0] = Mr;
+        dst[1] = Lr;
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        dst[16 * cb + j] = acc_o[cb][rr] * inv;
-        if constexpr (VQ) dst[D + 16 * cb + j] = acc_a[cb][rr] * inv;
+        dst[2 + 16 * cb + j] = acc_o[cb][rr];
+        if constexpr (VQ) dst[2 + D + 16 * cb + j] = acc_a[cb][rr];
       }
     }
   }
 }
 
-// Finish of multi-query rows (one block of D threads per row):
-//   o = R^T (o' + sqrt(pi/2)/m S^T a)   (o', a already divided by L)
+// Finish of multi-query rows, FR rows per block of 256 threads (S staged once
+// per block in LDS):  o = R^T (o' + sqrt(pi/2)/m S^T a)  (o', a already / L).
+// Thread t owns row t / (D/8) and coordinates 8 (t % (D/8)) .. + 7.
+template <int D>
+struct FinishShape {
+  static constexpr int TPR = D / 8;                 // threads per row
+  static constexpr int FR = 256 / TPR;              // rows per block
+};
+
 template <int D, int RK, bool VQ>
-__global__ __launch_bounds__(D) void finish_kernel(const FinishArgs a) {
-  __shared__ float t_s[D];
-  __shared__ float a_s[D];
-  const int i = threadIdx.x;
+__global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
+  constexpr int TPR = FinishShape<D>::TPR, FR = FinishShape<D>::FR;
+  __shared__ __attribute__((aligned(16))) uint16_t S_s[VQ ? D * D : 8];
+  __shared__ __attribute__((aligned(16))) float a_s[FR][D];
+  __shared__ __attribute__((aligned(16))) float v_s[FR][D];
+  const int tid = threadIdx.x;
+  const int r = tid / TPR, i0 = 8 * (tid % TPR);
   const int NR = a.nq * a.G;
-  const size_t ridx = blockIdx.x;
-  const size_t unit = ridx / NR;
-  const int R = (int)(ridx - unit * NR);
-  const int b = (int)(unit / a.Hkv), hkv = (int)(unit - (size_t)b * a.Hkv);
-  const int tq = R / a.G, g = R - tq * a.G;
-  const float *src = a.part + ridx * (2 * D);
-  float v = src[i];
+  const size_t ridx = (size_t)blockIdx.x * FR + r;
+  const bool ok = ridx < (size_t)a.rows;
   if constexpr (VQ) {
-    a_s[i] = src[D + i];
-    __syncthreads();
-    float acc = 0.0f;
-    for (int k = 0; k < D; ++k) acc = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), a_s[k], acc);
-    v = fmaf(a.vcoef, acc, v);
+    for (int k = tid; k < D * D / 8; k += 256)
+      *(u32x4 *)(S_s + 8 * k) = *(const u32x4 *)(a.S + 8 * (size_t)k);
   }
-  if constexpr (RK == RK_WHT || RK == RK_RHT) v = wht_block<D>(t_s, v) * a.oscale;
-  if constexpr (RK == RK_RHT) v = ((a.rsign[i >> 5] >> (i & 31)) & 1u) ? -v : v;
-  if constexpr (RK == RK_QR) {
-    t_s[i] = v;
-    __syncthreads();
-    v = dense_rotate_back<D>(a.Q, t_s, i);
+  // log-sum-exp merge of the row's token splits (base 2), then / L
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    constexpr int NS = 2 + 2 * D;
+    const float *src = a.part + (ok ? ridx : 0) * a.splits * NS;
+    float Mx = -INFINITY;
+    for (int sp = 0; sp < a.splits; ++sp) Mx = fmaxf(Mx, src[sp * NS]);
+    float Ls = 0.0f;
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float *ps = src + sp * NS;
+      const float w = ps[0] == -INFINITY ? 0.0f : fast_exp2(ps[0] - Mx);
+      Ls = fmaf(w, ps[1], Ls);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = fmaf(w, ps[2 + i0 + e], v[e]);
+        if constexpr (VQ) av[e] = fmaf(w, ps[2 + D + i0 + e], av[e]);
+      }
+    }
+    const float inv = ok ? 1.0f / Ls : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] *= inv;
+      av[e] *= inv;
+    }
   }
-  a.out[(((size_t)b * a.nq + tq) * a.Hq + hkv * a.G + g) * D + i] = v;
+  if constexpr (VQ) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a_s[r][i0 + e] = av[e];
+    __syncthreads();
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < D; ++k) {
+      const u32x4 sw = *(const u32x4 *)(S_s + k * D + i0);
+      const float ak = a_s[r][k];
+      acc[0] = fmaf(bf16_lo(sw.x), ak, acc[0]); acc[1] = fmaf(bf16_hi(sw.x), ak, acc[1]);
+      acc[2] = fmaf(bf16_lo(sw.y), ak, acc[2]); acc[3] = fmaf(bf16_hi(sw.y), ak, acc[3]);
+      acc[4] = fmaf(bf16_lo(sw.z), ak, acc[4]); acc[5] = fmaf(bf16_hi(sw.z), ak, acc[5]);
+      acc[6] = fmaf(bf16_lo(sw.w), ak, acc[6]); acc[7] = fmaf(bf16_hi(sw.w), ak, acc[7]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaf(a.vcoef, acc[e], v[e]);
+  }
+  if constexpr (RK != RK_NONE) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v_s[r][i0 + e] = v[e];
+    __syncthreads();
+    if constexpr (RK == RK_WHT || RK == RK_RHT) {
+      // butterflies over each row: D/2 pairs per row, FR rows, 256 threads
+      for (int h = 1; h < D; h <<= 1) {
+        for (int pi = tid; pi < FR * D / 2; pi += 256) {
+          const int rr = pi / (D / 2), q = pi - rr * (D / 2);
+          const int ii = (q / h) * 2 * h + (q % h);
+          const float x = v_s[rr][ii], y = v_s[rr][ii + h];
+          v_s[rr][ii] = x + y;
+          v_s[rr][ii + h] = x - y;
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = i0 + e;
+        float x = v_s[r][i] * a.oscale;
+        if constexpr (RK == RK_RHT) x = ((a.rsign[i >> 5] >> (i & 31)) & 1u) ? -x : x;
+        v[e] = x;
+      }
+    } else {                                            // RK_QR: o = Q^T v
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = dense_rotate_back<D>(a.Q, v_s[r], i0 + e);
+    }
+  }
+  if (ok) {
+    const size_t unit = ridx / NR;
+    const int R = (int)(ridx - unit * NR);
+    const int b = (int)(unit / a.Hkv), hkv = (int)(unit - (size_t)b * a.Hkv);
+    const int tq = R / a.G, g = R - tq * a.G;
+    float *dst = a.out + (((size_t)b * a.nq + tq) * a.Hq + hkv * a.G + g) * D + i0;
+    *(float4 *)dst = float4{v[0], v[1], v[2], v[3]};
+    *(float4 *)(dst + 4) = float4{v[4], v[5], v[6], v[7]};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2276,7 +2400,7 @@ hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows
 template <int D, int KB, bool KQ, int VB, bool VQ>
 hipError_t prefill_go(const PrefillArgs &a, int B, hipStream_t s) {
   const int NR = a.nq * a.G;
-  const dim3 grid((NR + 63) / 64, a.Hkv, B), blk(256);
+  const dim3 grid((NR + 63) / 64 * a.splits, a.Hkv, B), blk(256);
   hipLaunchKernelGGL((prefill_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
   return hipGetLastError();
 }
@@ -2309,7 +2433,8 @@ hipError_t launch_prefill(const PrefillArgs &a, int kb, bool kq, int vb, bool vq
 
 template <int D>
 hipError_t launch_finish(const FinishArgs &a, bool vq, int rows, hipStream_t s) {
-  const dim3 g(rows), blk(D);
+  constexpr int FR = FinishShape<D>::FR;
+  const dim3 g((rows + FR - 1) / FR), blk(256);
 #define KVQ_FIN(R, V) hipLaunchKernelGGL((finish_kernel<D, R, V>), g, blk, 0, s, a)
   switch (a.rk) {
     case RK_NONE: if (vq) return hipErrorInvalidValue; KVQ_FIN(RK_NONE, false); break;

@@ -388,3 +388,21 @@ def test_prefill_rotations_and_short_chunks(rotation):
     one = P.gpu.prefill_attention(q1.cuda(), N - 1, N, causal=True)[:, 0]
     dec = P.gpu.decode_attention(q1[:, 0].contiguous().cuda(), N)
     assert rel_rows(one.cpu().numpy(), dec.cpu().numpy().astype(np.float64)).max() < 1e-5
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("scheme,n", [("KQV", 4), ("QKQV", 2), ("KV", 3)])
+def test_prefill_token_splits(scheme, n, causal):
+    """Few query rows over a long cache: the library splits the slots (here
+    several splits of a multiple of 64 slots with a ragged last split), and
+    the finish merges them; rows whose causal limit ends inside an early split
+    leave later splits empty."""
+    print(f"case prefill-splits {scheme}{n} causal={causal}", flush=True)
+    B, Hkv, G, d, N, nq = 1, 2, 2, 64, 1900, 9
+    P = Pair(scheme, n, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, torch.float32, 2100 + n, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, nq, Hkv * G, d), 2101, torch.float32)
+    for p0 in (0, 700, N - nq):
+        got = P.gpu.prefill_attention(q.cuda(), p0, N, causal=causal).cpu().numpy()
+        assert rel_rows(got, P.prefill(q, p0, causal, N)).max() < 1e-5, p0

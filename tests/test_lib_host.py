@@ -330,7 +330,9 @@ def test_prefill_validation_status_codes(K):
     assert lib.kvq_prefill_workspace(p, 3, 5, C.byref(ws)) == 9
     assert lib.kvq_prefill_workspace(p, 6, 0, C.byref(ws)) == 10
     assert lib.kvq_prefill_workspace(p, 6, 5, C.byref(ws)) == 0   # G = 3 is fine here
-    assert ws.value == 4 * 1 * 6 * 5 * 64 * 3                     # q', o', a (no K sketch)
+    # q' (no K sketch), then (M, L, o', a) per row and split: one split here
+    # (a 32-slot cache caps the splits at ceil(32 / 256) = 1)
+    assert ws.value == 4 * 1 * 6 * 5 * (64 + 1 * (2 + 2 * 64))
     need = ws.value
     q, out, w = 0xA00000, 0xB00000, 0xC00000
     f = lib.kvq_prefill_attention
@@ -347,4 +349,19 @@ def test_prefill_validation_status_codes(K):
     assert f(p, q, 1, 5, 5, 0, 1, 8, out, w, need, None) == 9
     q3 = _fake_cache(K, scheme="QKQV", n=3)
     assert lib.kvq_prefill_workspace(C.byref(q3), 2, 7, C.byref(ws)) == 0
-    assert ws.value == 4 * 1 * 2 * 7 * 64 * 4                     # + S q'
+    assert ws.value == 4 * 1 * 2 * 7 * (2 * 64 + 1 * (2 + 2 * 64))  # + S q'
+
+
+def test_prefill_splits_fill_the_gpu(K):
+    """Few query rows over a long cache are split along the tokens (at least
+    256 slots per split, at most 64 splits); many rows are not."""
+    ws = C.c_size_t()
+    lib = K.lib()
+    c = _fake_cache(K, d=128, B=1, H=32, cap=4096)   # 32 KV heads, G = 1
+    assert lib.kvq_prefill_workspace(C.byref(c), 32, 256, C.byref(ws)) == 0
+    rows = 32 * 256
+    # 4 row tiles x 32 heads = 128 blocks -> 8 splits
+    assert ws.value == 4 * rows * (128 + 8 * (2 + 256))
+    c = _fake_cache(K, d=128, B=16, H=8, cap=32768)  # GQA chunk: 2048 blocks, 1 split
+    assert lib.kvq_prefill_workspace(C.byref(c), 32, 256, C.byref(ws)) == 0
+    assert ws.value == 4 * 16 * 32 * 256 * (128 + 1 * (2 + 256))
