@@ -375,12 +375,22 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       // certified signs
       const float bound = fmaf(a_snmax, rbt, 0x1p-100f);
       uint32_t bits = 0u, unsure = 0u;
+      float zmin = INFINITY;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);   // bit = sketch row % 32
         const float z = acc[j];
         bits |= (z > 0.0f ? 1u : 0u) << bp;
-        unsure |= (!(fabsf(z) > bound) ? 1u : 0u) << bp;
+        zmin = fminf(zmin, fabsf(z));
+      }
+      // the per-bit mask only where some entry of the wave is uncertain (rare);
+      // !(zmin > bound) also catches NaN
+      if (__ballot(!(zmin > bound) && t < nvalid)) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+          unsure |= (!(fabsf(acc[j]) > bound) ? 1u : 0u) << bp;
+        }
       }
       if constexpr (D < 32) unsure &= (1u << D) - 1u;                 // rows >= D do not exist
       if (t >= nvalid) unsure = 0u;                                    // padding rows of the tile
