@@ -49,7 +49,8 @@ def main():
                     help="also time multi-query attention of a chunk of this many query tokens "
                          "at the end of the context (causal); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=4, help="(b, KV head) units in the CPU sample")
+    ap.add_argument("--cpu-units", type=int, default=16,
+                    help="(b, KV head) units in the CPU sample (about 10 s of oracle work)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gqa_decode_kqv4.md"),
                     help="profiles/*.md summary holding measured HBM bytes per launch (json block)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -254,19 +255,24 @@ def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_
     from oracle import ref
 
     cores = len(os.sched_getaffinity(0))
-    units = max(1, min(units, w.Hkv))
+    units = max(1, min(units, w.B * w.Hkv))
     G = w.Hq // w.Hkv
-    Ks = K[0:1, :units].detach().cpu()
-    Vs = V[0:1, :units].detach().cpu()
-    qs = q[0:1, : units * G].detach().cpu()
+    # the first `units` (b, KV head) units in batch-major order, as whole batch
+    # rows of KV heads (nb rows x hk heads)
+    hk = min(units, w.Hkv)
+    nb = max(1, units // hk)
+    units = nb * hk
+    Ks = K[0:nb, :hk].detach().cpu()
+    Vs = V[0:nb, :hk].detach().cpu()
+    qs = q[0:nb, : hk * G].detach().cpu()
 
     def host(x):
         return synth_bits(x) if x.dtype == torch.bfloat16 else x.numpy()
 
     ks, vs = ref.scheme_sides(scheme, n_bits)
     rot = ref.Rot(rotation, rot_param)
-    ok = ref.OracleCache(1, units, w.N, w.d, ks, w.d, rot)
-    ov = ref.OracleCache(1, units, w.N, w.d, vs, w.d, rot)
+    ok = ref.OracleCache(nb, hk, w.N, w.d, ks, w.d, rot)
+    ov = ref.OracleCache(nb, hk, w.N, w.d, vs, w.d, rot)
     t0 = time.perf_counter()
     ok.quantize(host(Ks), 0, S, cores)
     ov.quantize(host(Vs), 0, S, cores)
@@ -280,7 +286,8 @@ def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_
     del np
     return {"value": round(dec_bytes / ta / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"b=0, {units} of {w.Hkv} KV heads x {G} query heads, full context {w.N}: "
+            "sample": f"b < {nb}, {hk} of {w.Hkv} KV heads x {G} query heads ({units} units), "
+                      f"full context {w.N}: "
                       f"oracle quantize {tq:.2f}s, fp64 decode attention {ta:.2f}s",
             "quantize_GBps": round(q_bytes / tq / 1e9, 4),
             "decode_kv_tokens_per_s": round(w.N * units / w.Hkv / ta, 1)}

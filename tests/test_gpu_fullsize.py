@@ -128,3 +128,36 @@ def test_long_context_full():
     _check_unit_bytes(cache, ok, ov, b, h, cap)
     for s, o in outs.items():
         _check_unit_attention(o, ok, ov, qs[s], b, h, G, w.N + s + 1, S)
+
+
+def test_llama_gqa_prefill_chunk_full():
+    """The bench's multi-query configuration at full size: GQA cache (batch 16,
+    32 query / 8 KV heads, d = 128, 32768 slots), a causal chunk of 256 query
+    tokens at positions 32512..32767 (auto token splits).  Sampled rows of two
+    units against plain fp64 attention over the oracle's reconstruction."""
+    w = synth.WORKLOADS["llama_gqa_decode"]
+    C = 256
+    print("case full-size prefill chunk", flush=True)
+    K, V, _ = synth.make_kvq(w, device=DEV)
+    S = synth.bits_u16(synth.sketch_bf16(w.d, w.d, 7))
+    cache = KVQCache(w.scheme, w.n_bits, w.d, w.B, w.Hkv, w.N, S_bf16=S, device=DEV)
+    cache.quantize_k(K, 0)
+    cache.quantize_v(V, 0)
+    qp = synth.gaussian((w.B, C, w.Hq, w.d), 31, w.dtype, DEV)
+    out = cache.prefill_attention(qp, w.N - C, w.N, causal=True).cpu().numpy()
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    qh = host_bits(qp)
+    q64 = (qh.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for (b, h) in ((0, 0), (15, 7)):
+        ok, ov = _unit_oracle(w.scheme, w.n_bits, w.d, K, V, b, h, S, w.N, w.N)
+        _check_unit_bytes(cache, ok, ov, b, h, w.N)
+        Kh = ok.dequantize(0, w.N, S, 16)[0, 0]
+        Vh = ov.dequantize(0, w.N, S, 16)[0, 0]
+        for i in (0, 131, C - 1):
+            T = w.N - C + i + 1
+            for g in range(G):
+                hq = h * G + g
+                want = ref.attention_dense(q64[b, i, hq], Kh[:T], Vh[:T])
+                err = rel_rows(out[b, i, hq][None], want[None]).max()
+                assert err < 2e-3, (b, h, i, g, err)
