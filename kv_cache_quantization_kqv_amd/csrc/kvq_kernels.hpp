@@ -1287,14 +1287,14 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
 }
 
 #ifndef KVQ_SCAN_PD
-#define KVQ_SCAN_PD 3   // value tiles in flight (registers) ahead of the one in LDS
+#define KVQ_SCAN_PD 2   // value tiles in flight (registers) ahead of the one in LDS
 #endif
 
-#ifdef KVQ_SCAN_WAVES_PER_EU
-#define KVQ_SCAN_OCC __attribute__((amdgpu_waves_per_eu(KVQ_SCAN_WAVES_PER_EU)))
-#else
-#define KVQ_SCAN_OCC
+// Three blocks per CU (LDS allows three at about 52 KB each): registers <= 168.
+#ifndef KVQ_SCAN_WAVES_PER_EU
+#define KVQ_SCAN_WAVES_PER_EU 3
 #endif
+#define KVQ_SCAN_OCC __attribute__((amdgpu_waves_per_eu(KVQ_SCAN_WAVES_PER_EU)))
 
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeArgs a) {
