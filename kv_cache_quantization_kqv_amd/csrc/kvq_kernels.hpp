@@ -180,7 +180,7 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 // which equals #{thresholds < u} (ties go to the lower cell).
 // ---------------------------------------------------------------------------
 struct BucketTables {
-  uint8_t cell_lo[1024];   // per 11-bit |u| prefix: positive thresholds below the cell
+  uint8_t cell_lo[2048];   // per 11-bit |u| prefix: positive thresholds below the cell
   float pos[9];            // positive thresholds, then +inf sentinels
   float cent[16];
 };
@@ -189,11 +189,13 @@ template <int BITS>
 __device__ void build_bucket_tables(BucketTables &bt, const float *thr, const float *cent, int tid,
                                     int nthreads) {
   constexpr int K2 = 1 << (BITS - 1);
-  for (int i = tid; i < 1024; i += nthreads) {
-    const float lo = __uint_as_float((uint32_t)i << 20);
+  for (int i = tid; i < 2048; i += nthreads) {
+    // prefixes from 1024 up are |u| >= 2 (and non-finite patterns): every
+    // positive threshold lies below them
+    const float lo = __uint_as_float((uint32_t)(i < 1024 ? i : 1023) << 20);
     int c = 0;
     for (int k = 0; k + 1 < K2; ++k) c += (thr[K2 + k] < lo) ? 1 : 0;
-    bt.cell_lo[i] = (uint8_t)c;
+    bt.cell_lo[i] = (uint8_t)(i < 1024 ? c : K2 - 1);
   }
   if (tid < 9) bt.pos[tid] = (tid + 1 < K2) ? thr[K2 + tid] : INFINITY;
   if (tid < 16) bt.cent[tid] = cent[tid];
@@ -203,7 +205,7 @@ template <int BITS>
 __device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables &bt) {
   constexpr int K2 = 1 << (BITS - 1);
   const float au = fabsf(u);
-  const uint32_t idx = min(__float_as_uint(au) >> 20, 1023u);  // |u| <= 1 (1+ulp) in practice
+  const uint32_t idx = __builtin_amdgcn_ubfe(__float_as_uint(u), 20, 11);  // bits 20..30 of |u|
   const uint32_t c = bt.cell_lo[idx];
   const float p = bt.pos[c];
   const uint32_t lt = c + (p < au ? 1u : 0u);              // #{P_k <  |u|}
