@@ -213,6 +213,32 @@ __device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables &b
   return u > 0.0f ? (uint32_t)K2 + lt : (uint32_t)(K2 - 1) - le;
 }
 
+// The same count by comparisons against the positive thresholds held in
+// scalar registers (for narrow codes, where K/2 - 1 compares cost no more than
+// the two table reads).  Bit patterns of non-negative floats order like the
+// floats, so  P < |u|  is  bits(P) < bits(|u|)  and  P <= |u|  is
+// bits(P) < bits(|u|) + 1;  u <= 0 (both zeros included) takes the second
+// form, and its code K/2 - 1 - le is the complement of K/2 + le in BITS bits.
+#ifndef KVQ_BUCKETIZE_CMP_MAXBITS
+#define KVQ_BUCKETIZE_CMP_MAXBITS 3
+#endif
+template <int BITS>
+__device__ __forceinline__ uint32_t bucketize_cmp(float u, const float *thr) {
+  constexpr uint32_t K2 = 1u << (BITS - 1);
+  const uint32_t neg = (u <= 0.0f) ? 1u : 0u;
+  const uint32_t key = (__float_as_uint(u) & 0x7FFFFFFFu) + neg;
+  uint32_t n = K2;
+#pragma unroll
+  for (uint32_t k = 0; k + 1 < K2; ++k) n += (__float_as_uint(thr[K2 + k]) < key) ? 1u : 0u;
+  return n ^ (neg ? 2u * K2 - 1u : 0u);
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables &bt, const float *thr) {
+  if constexpr (BITS <= KVQ_BUCKETIZE_CMP_MAXBITS) return bucketize_cmp<BITS>(u, thr);
+  else return bucketize_lut<BITS>(u, bt);
+}
+
 // Value of the partner lane (lane ^ 1) through a DPP quad permute (no LDS).
 __device__ __forceinline__ float xor1_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -637,7 +663,7 @@ void quantize_kernel(const QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < DL; ++i) {
       const float u = y[i] * rcp;
-      const uint32_t code = bucketize_lut<BITS>(u, bt);
+      const uint32_t code = bucketize_code<BITS>(u, bt, a.thr);
       lc.put(i, code);
       if constexpr (QJL) y[i] = u - bt.cent[code];
       // keep at most 16 coordinates' table lookups in flight (register pressure)
@@ -824,7 +850,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
 #pragma unroll
       for (int ii = 0; ii < RB; ++ii) {
         const float u = yb[ii] * rcp;
-        const uint32_t code = bucketize_lut<BITS>(u, bt);
+        const uint32_t code = bucketize_code<BITS>(u, bt, a.thr);
         lc.put(ii, code);
         if constexpr (QJL) yb[ii] = u - bt.cent[code];
       }
