@@ -49,8 +49,9 @@ def main():
                     help="also time multi-query attention of a chunk of this many query tokens "
                          "at the end of the context (causal); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=16,
-                    help="(b, KV head) units in the CPU sample (about 10 s of oracle work)")
+    ap.add_argument("--cpu-units", type=int, default=32,
+                    help="(b, KV head) units in the CPU sample (about 20 s of oracle work "
+                         "on 16 host threads)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gqa_decode_kqv4.md"),
                     help="profiles/*.md summary holding measured HBM bytes per launch (json block)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
