@@ -332,17 +332,28 @@ long long min_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   return ((long long)n_ctx + tmax - 1) / tmax;
 }
 
+// About KVQ_SCAN_BLOCKS scan blocks: the split length is rounded up to whole
+// 256-token rounds of the key phase (at least 256), but stays within the LDS
+// logit buffer.
 int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
-  int G = q_heads / c->kv_heads;
-  int HG = G / heads_per_block(G);
-  long long units = (long long)c->batch * c->kv_heads * HG;
-  long long want = (2048 + units - 1) / units;
-  long long maxs = (n_ctx + 255) / 256;
-  long long s = want < maxs ? want : maxs;
-  const long long need = min_splits(c, q_heads, n_ctx);
-  if (s < need) s = need;
-  if (s < 1) s = 1;
-  return (int)s;
+  const int G = q_heads / c->kv_heads;
+  const int HG = G / heads_per_block(G);
+  const long long units = (long long)c->batch * c->kv_heads * HG;
+  const long long want = (KVQ_SCAN_BLOCKS + units - 1) / units;
+  const long long tmax = kvq::scan_tokens_max(heads_per_block(G));
+  if (n_ctx <= 0) return 1;
+  long long tps = ((long long)n_ctx + want - 1) / want;
+  tps = tps < 256 ? 256 : (tps + 255) / 256 * 256;
+  if (tps > tmax) tps = tmax;
+  const long long s = ((long long)n_ctx + tps - 1) / tps;
+  return s < 1 ? 1 : (int)s;
+}
+
+// Tokens per split for a split count: whole 64-token value tiles (trailing
+// splits may be empty; they contribute nothing to the merge).
+int split_tokens(int n_ctx, int splits) {
+  const int t = (n_ctx + splits - 1) / splits;
+  return (t + 63) / 64 * 64;
 }
 
 }  // namespace
@@ -639,7 +650,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   }
   a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.Hkv = c->kv_heads; a.Hq = q_heads; a.Gtot = G; a.HG = G / gt; a.cap = c->capacity;
-  a.n_ctx = n_ctx; a.splits = splits; a.tps = n_ctx > 0 ? (n_ctx + splits - 1) / splits : 0;
+  a.n_ctx = n_ctx; a.splits = splits; a.tps = n_ctx > 0 ? split_tokens(n_ctx, splits) : 0;
   e = by_dim(d, [&](auto D) {
     return kvq::launch_decode<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
                                                   c->v_qjl != 0, gt, c->batch, hs);

@@ -17,6 +17,11 @@ namespace kvq {
 
 inline int scan_tokens_max(int gt) { return KVQ_SCAN_WBUF_FLOATS / (2 * gt); }
 
+// Target block count of the automatic decode split choice.
+#ifndef KVQ_SCAN_BLOCKS
+#define KVQ_SCAN_BLOCKS 4096
+#endif
+
 // Rotation applied by the codec (kernel template / argument code):
 // none, Walsh-Hadamard, randomized Hadamard (signs, then WHT), dense Q.
 enum { RK_NONE = 0, RK_WHT = 1, RK_RHT = 2, RK_QR = 3 };

@@ -1324,8 +1324,84 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
 #endif
 #define KVQ_SCAN_OCC __attribute__((amdgpu_waves_per_eu(KVQ_SCAN_WAVES_PER_EU)))
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Split merge in the scan's last block (1) or in a kernel of its own that
+// follows the scan on the stream, one block per query row (0).
+#ifndef KVQ_SCAN_FUSED_MERGE
+#define KVQ_SCAN_FUSED_MERGE 0
+#endif
+
+// Split merge of one query row (b, hq): log-sum-exp weights, S^T a, inverse
+// rotation, division by L (and the full-precision window, if any).
+template <int D, bool VQ>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float sm[256 + 2 + 2 * D];
+  __shared__ float mx[1];
+  const int row = blockIdx.x;
+  const int b = row / a.Hq, hq = row - (row / a.Hq) * a.Hq;
+  merge_splits<D, VQ, 1>(a, sm, mx, b, hq);
+}
+
+// Key scores on the matrix cores (4-bit keys, d = 128, four query heads per
+// block).  A wave scores 16 tokens per step with v_mfma_f32_16x16x32_f16:
+// row = token (lane % 16), 32 K slots (lane group g = lane / 16 holds 8 of
+// them), column = output column.  fp16 carries 11 significant bits, so both
+// operands are split: C = Ch + 2^-11 Cl (one pair-table entry holds the fp16
+// pair Ch and the fp16 pair Cl of two coordinates) and q' 2^k = qh + 2^-11 ql,
+// with k a per-head power of two that keeps q' 2^k inside fp16's range.
+// Column h < 4 collects sum Ch qh of head h, column 7 - h the sum
+// (Ch ql + Cl qh); the dropped Cl ql term is 2^-22 relative, so a score
+// carries about fp32 precision.  Lane group g covers coordinates
+// [32 g, 32 g + 32): step j (0..7) takes the code bytes 2j and 2j + 1, i.e.
+// coordinates 32 g + 4 j + {0, 1, 2, 3}, in the slot order
+// (Ch, Ch, Cl, Cl) of the first pair, then of the second.
+#ifndef KVQ_SCAN_MFMA_KEYS
+#define KVQ_SCAN_MFMA_KEYS 1
+#endif
+template <int D, int KB, bool KQ, int GT>
+struct MfmaKeys {
+  static constexpr bool on = KVQ_SCAN_MFMA_KEYS && D == 128 && KB == 4 && !KQ && GT == 4;
+};
+
+// B operands of lane (n = lane % 16, g = lane / 16) for the eight steps, from
+// the prepared query qv ([coordinate][4 heads]).  Column n serves head n
+// (n < 4) or head 7 - n (4 <= n < 8); other columns are zero.  `unscale` =
+// 2^-k of the lane's head.
+__device__ __forceinline__ void mfma_key_operands(const float *qv, int lane, f16x8 (&bq)[8],
+                                                  float &unscale) {
+  const int n = lane & 15, g = lane >> 4, h = n < 4 ? n : 7 - (n & 7);
+  float v[32];
+  float m = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    v[c] = qv[(32 * g + c) * 4 + (h & 3)];
+    m = fmaxf(m, fabsf(v[c]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  int ex = 0;
+  const bool fin = m > 0.0f && m <= 3.0e38f;
+  if (fin) (void)frexpf(m, &ex);                      // m < 2^ex
+  const int k = fin ? 14 - ex : 0;
+  unscale = ldexpf(1.0f, -k);
+  const _Float16 z = (_Float16)0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = 4 * j + 2 * (e >> 2) + (e & 1);
+      const bool lo_slot = (e & 2) != 0;
+      const float x = ldexpf(v[c], k);
+      const _Float16 hi = (_Float16)x;
+      const _Float16 lo = (_Float16)((x - (float)hi) * 2048.0f);
+      bq[j][e] = n < 4 ? (lo_slot ? z : hi) : (n < 8 ? (lo_slot ? hi : lo) : z);
+    }
+}
+
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeArgs a) {
+  constexpr bool MFA = MfmaKeys<D, KB, KQ, GT>::on;  // key scores on the matrix cores
   constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // value coordinates per lane
   constexpr int L = D / E;                           // lanes sharing a token group in phase C
   constexpr int GPW = 64 / L;                        // token groups per wave
@@ -1367,7 +1443,20 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   for (int p = tid; p < KPAIR; p += 256) {
     int ca, cb;
     pair_codes<KB>(p, ca, cb);
-    kp_s[p] = f32x2{a.kcent[ca], a.kcent[cb]};
+    if constexpr (MFA) {
+      // fp16 pair (Ch[a], Ch[b]) and pair of scaled remainders 2^11 (C - Ch)
+      const float xa = a.kcent[ca], xb = a.kcent[cb];
+      const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
+      const _Float16 la = (_Float16)((xa - (float)ha) * 2048.0f);
+      const _Float16 lb = (_Float16)((xb - (float)hb) * 2048.0f);
+      const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+      const uint32_t lw = (uint32_t)__builtin_bit_cast(uint16_t, la) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+      kp_s[p] = f32x2{__uint_as_float(hw), __uint_as_float(lw)};
+    } else {
+      kp_s[p] = f32x2{a.kcent[ca], a.kcent[cb]};
+    }
   }
   for (int p = tid; p < NPAIR; p += 256) {
     int ca, cb;
@@ -1444,6 +1533,80 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) mx[hh] = -INFINITY;
 
+  if constexpr (MFA) {
+    // Lane (n, g) loads bytes [16 g, 16 g + 16) of the records of tokens
+    // base + 16 blk + n (blk < 4); lane l loads the norms of token base + l.
+    const int n = lane & 15, g = lane >> 4;
+    f16x8 bq[8];
+    float unscale;
+    mfma_key_operands((const float *)(a.qt + unitg * D * GT), lane, bq, unscale);
+    u32x4 kw4[4];
+    uint32_t kn2 = 0u, vnr2 = 0u;
+    auto kload4 = [&](int base, u32x4 (&w)[4], uint32_t &nkb, uint32_t &vv) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int tl = base + 16 * blk + n;
+        w[blk] = tl < nloc ? *(const u32x4 *)(kc_p + (size_t)tl * KBYTES + 16 * g) : u32x4{0u, 0u, 0u, 0u};
+      }
+      const int tl = base + lane;
+      if (tl < nloc) {
+        nkb = __builtin_nontemporal_load(kn_p + tl);
+        vv = (uint32_t)__builtin_nontemporal_load(vn_p + tl) |
+             (VQ ? (uint32_t)__builtin_nontemporal_load(vr_p + tl) << 16 : 0u);
+      } else {
+        nkb = 0u;
+        vv = 0u;
+      }
+    };
+    kload4(wave * 64, kw4, kn2, vnr2);
+    for (int base = wave * 64; base < nloc; base += 256) {
+      u32x4 nw4[4];
+      uint32_t nkn, nvv;
+      kload4(base + 256, nw4, nkn, nvv);   // prefetch the next round
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = kw4[blk][j >> 1] >> (16 * (j & 1));
+          const f32x2 t0 = kp_s[w & 255u], t1 = kp_s[(w >> 8) & 255u];
+          const u32x4 av = {__float_as_uint(t0.x), __float_as_uint(t0.y), __float_as_uint(t1.x),
+                            __float_as_uint(t1.y)};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), bq[j], acc, 0, 0, 0);
+        }
+        // acc[r] = column n of token row 4 g + r; column 7 - h holds the
+        // remainder sum of head h (row_half_mirror: lane i <- lane 7 - i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float lo = __int_as_float(
+              __builtin_amdgcn_update_dpp(0, __float_as_int(acc[r]), 0x141, 0xF, 0xF, false));
+          const int tl = base + 16 * blk + 4 * g + r;
+          if (n < 4 && tl < nloc) wc[tl * GT + n] = fmaf(lo, 1.0f / 2048.0f, acc[r]) * unscale;
+        }
+      }
+      const int tl = base + lane;
+      if (tl < nloc) *(u32x2 *)(wq + tl * GT) = u32x2{vnr2, kn2};
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) kw4[blk] = nw4[blk];
+      kn2 = nkn;
+      vnr2 = nvv;
+    }
+    // scale by the key norms; the split's max per head
+    __syncthreads();
+    for (int tl = tid; tl < nloc; tl += 256) {
+      const float nkf = f16_bits_to_f32((uint16_t)(*(const uint32_t *)(wq + tl * GT + 1) & 0xFFFFu));
+      float4 s4 = *(const float4 *)(wc + tl * GT);
+      s4.x *= nkf;
+      s4.y *= nkf;
+      s4.z *= nkf;
+      s4.w *= nkf;
+      *(float4 *)(wc + tl * GT) = s4;
+      mx[0] = fmaxf(mx[0], s4.x);
+      mx[1] = fmaxf(mx[1], s4.y);
+      mx[2] = fmaxf(mx[2], s4.z);
+      mx[3] = fmaxf(mx[3], s4.w);
+    }
+  } else {
   uint32_t kw[KW], ksw[SW];
   float nk = 0.0f, rk = 0.0f;
   uint32_t vnr = 0u;   // fp16 bits of the value norm (low) and residual norm (high)
@@ -1520,6 +1683,7 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     rk = nrk;
     vnr = nvnr;
   }
+  }  // key scores on the vector units
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     const float m = wave_max(mx[hh]);
@@ -1750,6 +1914,15 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   // back with device-coherent loads, so no cache-wide write-back is needed:
   // each thread waits for its stores to complete, the block synchronises, and
   // only then is the arrival counter bumped.
+  if constexpr (!KVQ_SCAN_FUSED_MERGE) {
+    // the merge kernel that follows on the stream combines the splits
+    for (int idx = tid; idx < GT * NS; idx += 256) {
+      const int hh = idx / NS, k = idx - hh * NS;
+      float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
+      dst[k] = (k == 0) ? (nloc > 0 ? M[hh] : -INFINITY) : wst[idx];
+    }
+    return;
+  }
   for (int idx = tid; idx < GT * NS; idx += 256) {
     const int hh = idx / NS, k = idx - hh * NS;
     float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
@@ -2393,6 +2566,7 @@ hipError_t decode_go(const DecodeArgs &a, int gt, int B, hipStream_t s) {
     case 4: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 4>), grid, blk, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  if (!KVQ_SCAN_FUSED_MERGE) hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
   return hipGetLastError();
 }
 

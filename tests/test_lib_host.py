@@ -199,11 +199,11 @@ def test_validation_status_codes(K):
 
 
 def test_auto_splits_fill_the_gpu(K):
-    """At least ~2048 blocks, at most 256-token splits where that suffices, and
-    never more tokens per split than the LDS logit buffer holds (1280 tokens
-    at four heads per block, 2560 at two, 5120 at one)."""
+    """About 4096 blocks, split lengths rounded up to whole 256-token rounds
+    (at least 256), and never more tokens per split than the LDS logit buffer
+    holds (1280 tokens at four heads per block, 2560 at two, 5120 at one)."""
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)
-    assert K.kvq_decode_auto_splits(c, 32, 32768) == 26       # 1261-token splits
+    assert K.kvq_decode_auto_splits(c, 32, 32768) == 32       # 1024-token splits
     c = _fake_cache(K, d=128, B=4, H=8, cap=131136)
     assert K.kvq_decode_auto_splits(c, 32, 131136) == 103
     c = _fake_cache(K, d=64, B=1, H=1, cap=256)
