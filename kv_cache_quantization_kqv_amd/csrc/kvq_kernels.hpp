@@ -1317,6 +1317,9 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
 #ifndef KVQ_SCAN_PD
 #define KVQ_SCAN_PD 2   // value tiles in flight (registers) ahead of the one in LDS
 #endif
+#ifndef KVQ_SCAN_WPF
+#define KVQ_SCAN_WPF 4  // wave-private value slices in flight (registers)
+#endif
 
 // Three blocks per CU (LDS allows three at about 52 KB each): registers <= 168.
 #ifndef KVQ_SCAN_WAVES_PER_EU
@@ -1517,8 +1520,34 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     for (int k = 0; k < NPT; ++k)
       if (cbase[k]) *(u32x4 *)(tile + (tid + 256 * k) * 16) = src[k];
   };
+  // Wave-private value slices (d = 128, one 16-byte piece per lane): wave w
+  // takes tokens [16 w, 16 w + 16) of every 64-token tile itself, with
+  // KVQ_SCAN_WPF slices in flight, so phase C needs no block barrier.
+  using TW = VTile<D, VB, VQ, 16>;
+  constexpr bool WPC = D == 128 && E == 8 && TT == 64 && TW::BYTES == 1024;
+  constexpr int WPF = WPC ? KVQ_SCAN_WPF : 1;
+  u32x4 pw[WPF];
+  auto wfetch = [&](int it, u32x4 &dst) {
+    dst = u32x4{0u, 0u, 0u, 0u};
+    if (it < ntiles) {
+      const int tb = it * TT + 16 * wave;                  // first token of the slice
+      const int byte = lane * 16;
+      if (byte < TW::VS) {
+        if (tb + byte / TW::VREC < nloc)
+          dst = __builtin_nontemporal_load((const u32x4 *)(a.vc + (rec0 + tb) * TW::VREC + byte));
+      } else if constexpr (VQ) {
+        if (tb + (byte - TW::VS) / TW::SREC < nloc)
+          dst = __builtin_nontemporal_load((const u32x4 *)(a.vs + (rec0 + tb) * TW::SREC + byte - TW::VS));
+      }
+    }
+  };
+  if constexpr (WPC) {
 #pragma unroll
-  for (int j = 0; j < PD; ++j) fetch(j, pf[j]);
+    for (int j = 0; j < WPF; ++j) wfetch(j, pw[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < PD; ++j) fetch(j, pf[j]);
+  }
 
   // ---- phase A: logits, one token per lane -------------------------------
   cfloat *qc = (cfloat *)(a.qt + unitg * D * GT);
@@ -1807,6 +1836,63 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     }
   };
   __syncthreads();   // weights of phase B are in LDS
+  if constexpr (WPC) {
+    uint8_t *wt = tile + wave * 1024;                     // this wave's slice in LDS
+    for (int it0 = 0; it0 < ntiles; it0 += WPF) {
+#pragma unroll
+      for (int j = 0; j < WPF; ++j) {
+        const int it = it0 + j;
+        if (it >= ntiles) break;
+        *(u32x4 *)(wt + lane * 16) = pw[j];
+        wfetch(it + WPF, pw[j]);
+        if constexpr (VQ) {
+          // sign table of group grp, mask lg (tokens past the split have cq = 0)
+          const float *cqp = wq + (it * TT + grp * TG) * GT;
+          float t4[GT];
+#pragma unroll
+          for (int hh = 0; hh < GT; ++hh) t4[hh] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < TG; ++i) {
+            const float sg = ((lg >> i) & 1) ? 1.0f : -1.0f;
+#pragma unroll
+            for (int hh = 0; hh < GT; ++hh) t4[hh] = fmaf(sg, cqp[i * GT + hh], t4[hh]);
+          }
+          *(float4 *)(tbl + (grp * 16 + lg) * GT) = float4{t4[0], t4[1], t4[2], t4[3]};
+        }
+        wave_sync();
+        const int tr0 = grp * TG;
+        float c[TG][GT];
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+          const float *wsrc = wc + (it * TT + tr0 + i) * GT;
+#pragma unroll
+          for (int hh = 0; hh < GT; ++hh) c[i][hh] = wsrc[hh];
+        }
+#pragma unroll
+        for (int i = 0; i < TG; ++i) {
+          uint32_t vw0, vw1;
+          lds_codes<D, VB, E>(wt + TW::VC + (4 * gs + i) * TW::VREC, lg, vw0, vw1);
+#pragma unroll
+          for (int p = 0; p < E / 2; ++p) {
+            const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
+#pragma unroll
+            for (int hh = 0; hh < GT; ++hh) {
+              o[hh][2 * p] = fmaf(c[i][hh], cv.x, o[hh][2 * p]);
+              o[hh][2 * p + 1] = fmaf(c[i][hh], cv.y, o[hh][2 * p + 1]);
+            }
+          }
+        }
+        if constexpr (VQ) {
+          const uint8_t *sb = wt + TW::VS + 4 * gs * TW::SREC;
+          uint32_t w = 0u;
+#pragma unroll
+          for (int i = 0; i < TG; ++i) w |= (uint32_t)sb[i * TW::SREC + lg] << (8 * i);
+          sign_terms(w, 0);
+        }
+        wave_sync();   // the slice area and the tables are rewritten next
+      }
+    }
+  } else {
   if constexpr (VQ) {
     if (ntiles > 0) build_tables(0);
   }
@@ -1865,6 +1951,7 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
       }
     }
   }
+  }  // block-staged value tiles
 
   // ---- epilogue: sum token slots (lanes), then waves; L over threads -------
 #pragma unroll
