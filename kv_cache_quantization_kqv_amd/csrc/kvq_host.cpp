@@ -181,14 +181,21 @@ kvq_status scheme_sides(int scheme, int n, Sides *s) {
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // The encoder's table bucketize needs a symmetric threshold table with a zero
-// middle threshold, and at most one positive threshold in every cell of the
-// 11-bit prefix (exponent + 3 mantissa bits) of |u|.
+// middle threshold, and at most one threshold in every cell of the 12-bit
+// prefix (sign, exponent, 3 mantissa bits) of u: positive thresholds with
+// distinct prefixes, the smallest one above the prefix-0 cell (which holds the
+// zero threshold).
 bool codebook_usable(const kvq_codebook &cb) {
   const int K = 1 << cb.bits, half = K / 2;
   if (cb.threshold[half - 1] != 0.0f) return false;
   for (int k = 0; k + 1 < half; ++k) {
     const float p = cb.threshold[half + k];
     if (!(p > 0.0f) || p >= 2.0f || cb.threshold[half - 2 - k] != -p) return false;
+    if (k == 0) {
+      uint32_t a;
+      std::memcpy(&a, &p, 4);
+      if ((a >> 20) == 0) return false;
+    }
     if (k > 0) {
       uint32_t a, b;
       const float q = cb.threshold[half + k - 1];

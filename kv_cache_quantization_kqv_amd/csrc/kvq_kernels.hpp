@@ -168,49 +168,56 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 // ---------------------------------------------------------------------------
 // Exact bucketize by table ("KVQuant++" thread, "Fast codebook lookup": a
 // lookup against sorted thresholds instead of a nearest-centroid search).
-// For |u| the top 11 bits of its fp32 pattern (exponent and 3 mantissa bits)
-// are monotone in |u| and cut [0, 2) into cells whose width is at most 1/8 of
-// their lower end.  Consecutive positive thresholds of the tables used here
-// are more than 9/8 apart, so a cell holds at most one of them (the host
-// checks this for every table it builds).  cell_lo[idx] counts the positive
-// thresholds below the cell; one exact comparison with the next threshold
-// finishes the count.  With the table symmetric and the middle threshold 0:
-//   u > 0 : code = K/2 + #{P_k <  |u|}
-//   u <= 0: code = K/2 - 1 - #{P_k <= |u|}
-// which equals #{thresholds < u} (ties go to the lower cell).
+// The top 12 bits of u's fp32 pattern (sign, exponent, 3 mantissa bits) cut
+// the line into cells: a cell of non-negative patterns holds [lo, hi), one of
+// negative patterns (-hi, -lo], with hi <= 9/8 lo (and the cells of prefix 0
+// reaching down to +0 and -0).  Consecutive positive thresholds of the tables
+// used here fall in different cells and the smallest is above the prefix-0
+// cell (the host checks this for every table it builds), so a cell holds at
+// most one threshold: the entry of a cell is (that threshold or +inf, the
+// number of thresholds below the cell), and
+//   code = count + (threshold < u)
+// equals #{thresholds < u} (ties go to the lower cell; -0 and +0 against the
+// zero threshold compare as IEEE floats do).
 // ---------------------------------------------------------------------------
+#ifndef KVQ_BUCKETIZE_CMP_MAXBITS
+#define KVQ_BUCKETIZE_CMP_MAXBITS 3
+#endif
+template <int BITS>
 struct BucketTables {
-  uint8_t cell_lo[2048];   // per 11-bit |u| prefix: positive thresholds below the cell
-  float pos[9];            // positive thresholds, then +inf sentinels
+  static constexpr bool LUT = BITS > KVQ_BUCKETIZE_CMP_MAXBITS;
+  f32x2 cell[LUT ? 4096 : 1];   // (threshold inside the cell or +inf, count below as bits)
   float cent[16];
 };
 
 template <int BITS>
-__device__ void build_bucket_tables(BucketTables &bt, const float *thr, const float *cent, int tid,
-                                    int nthreads) {
-  constexpr int K2 = 1 << (BITS - 1);
-  for (int i = tid; i < 2048; i += nthreads) {
-    // prefixes from 1024 up are |u| >= 2 (and non-finite patterns): every
-    // positive threshold lies below them
-    const float lo = __uint_as_float((uint32_t)(i < 1024 ? i : 1023) << 20);
-    int c = 0;
-    for (int k = 0; k + 1 < K2; ++k) c += (thr[K2 + k] < lo) ? 1 : 0;
-    bt.cell_lo[i] = (uint8_t)(i < 1024 ? c : K2 - 1);
+__device__ void build_bucket_tables(BucketTables<BITS> &bt, const float *thr, const float *cent,
+                                    int tid, int nthreads) {
+  constexpr int K = 1 << BITS;
+  if constexpr (BucketTables<BITS>::LUT) {
+    for (int i = tid; i < 4096; i += nthreads) {
+      // the cell's range as (lower, upper) end points in the order of floats
+      const uint32_t a = (uint32_t)(i & 2047) << 20, b = a | 0xFFFFFu;
+      const float m0 = __uint_as_float(a), m1 = __uint_as_float(b);
+      const bool neg = i >= 2048;
+      const float lo = neg ? -m1 : m0, hi = neg ? -m0 : m1;   // cell = [lo, hi] up to end points
+      uint32_t below = 0;
+      float inside = INFINITY;
+      for (int k = 0; k + 1 < K; ++k) {
+        const float t = thr[k];
+        if (t < lo) ++below;
+        else if (t <= hi) inside = t;
+      }
+      bt.cell[i] = f32x2{inside, __uint_as_float(below)};
+    }
   }
-  if (tid < 9) bt.pos[tid] = (tid + 1 < K2) ? thr[K2 + tid] : INFINITY;
   if (tid < 16) bt.cent[tid] = cent[tid];
 }
 
 template <int BITS>
-__device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables &bt) {
-  constexpr int K2 = 1 << (BITS - 1);
-  const float au = fabsf(u);
-  const uint32_t idx = __builtin_amdgcn_ubfe(__float_as_uint(u), 20, 11);  // bits 20..30 of |u|
-  const uint32_t c = bt.cell_lo[idx];
-  const float p = bt.pos[c];
-  const uint32_t lt = c + (p < au ? 1u : 0u);              // #{P_k <  |u|}
-  const uint32_t le = lt + (p == au ? 1u : 0u);            // #{P_k <= |u|}
-  return u > 0.0f ? (uint32_t)K2 + lt : (uint32_t)(K2 - 1) - le;
+__device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables<BITS> &bt) {
+  const f32x2 e = bt.cell[__float_as_uint(u) >> 20];
+  return __float_as_uint(e.y) + (e.x < u ? 1u : 0u);
 }
 
 // The same count by comparisons against the positive thresholds held in
@@ -219,9 +226,6 @@ __device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables &b
 // floats, so  P < |u|  is  bits(P) < bits(|u|)  and  P <= |u|  is
 // bits(P) < bits(|u|) + 1;  u <= 0 (both zeros included) takes the second
 // form, and its code K/2 - 1 - le is the complement of K/2 + le in BITS bits.
-#ifndef KVQ_BUCKETIZE_CMP_MAXBITS
-#define KVQ_BUCKETIZE_CMP_MAXBITS 3
-#endif
 template <int BITS>
 __device__ __forceinline__ uint32_t bucketize_cmp(float u, const float *thr) {
   constexpr uint32_t K2 = 1u << (BITS - 1);
@@ -234,7 +238,7 @@ __device__ __forceinline__ uint32_t bucketize_cmp(float u, const float *thr) {
 }
 
 template <int BITS>
-__device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables &bt, const float *thr) {
+__device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables<BITS> &bt, const float *thr) {
   if constexpr (BITS <= KVQ_BUCKETIZE_CMP_MAXBITS) return bucketize_cmp<BITS>(u, thr);
   else return bucketize_lut<BITS>(u, bt);
 }
@@ -532,7 +536,7 @@ void quantize_kernel(const QuantArgs a) {
   static_assert((VT * CPR) % 64 == 0, "tile copy must split evenly over the wave");
   __shared__ __attribute__((aligned(16))) unsigned char stage_all[4][VT * PITCH];
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
-  __shared__ BucketTables bt;
+  __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -783,7 +787,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
   using LC = LocalCodes<RB, BITS>;
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
   __shared__ __attribute__((aligned(16))) unsigned char res_all[4][RBYTES];
-  __shared__ BucketTables bt;
+  __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned char *res = res_all[wave];
