@@ -181,12 +181,13 @@ kvq_status scheme_sides(int scheme, int n, Sides *s) {
 bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // The encoder's table bucketize needs a symmetric threshold table with a zero
-// middle threshold, and at most one threshold in every cell of the 12-bit
-// prefix (sign, exponent, 3 mantissa bits) of u: positive thresholds with
-// distinct prefixes, the smallest one above the prefix-0 cell (which holds the
-// zero threshold).
+// middle threshold, and at most one threshold in every cell of the prefix
+// (sign, exponent, MB mantissa bits; MB = 3 for 4-bit codes, else 1) of u:
+// positive thresholds with distinct prefixes, the smallest one above the
+// prefix-0 cell (which holds the zero threshold).
 bool codebook_usable(const kvq_codebook &cb) {
   const int K = 1 << cb.bits, half = K / 2;
+  const int shift = 23 - (cb.bits >= 4 ? 3 : 1);
   if (cb.threshold[half - 1] != 0.0f) return false;
   for (int k = 0; k + 1 < half; ++k) {
     const float p = cb.threshold[half + k];
@@ -194,14 +195,14 @@ bool codebook_usable(const kvq_codebook &cb) {
     if (k == 0) {
       uint32_t a;
       std::memcpy(&a, &p, 4);
-      if ((a >> 20) == 0) return false;
+      if ((a >> shift) == 0) return false;
     }
     if (k > 0) {
       uint32_t a, b;
       const float q = cb.threshold[half + k - 1];
       std::memcpy(&a, &q, 4);
       std::memcpy(&b, &p, 4);
-      if ((a >> 20) == (b >> 20) || !(p > q)) return false;
+      if ((a >> shift) == (b >> shift) || !(p > q)) return false;
     }
   }
   for (int i = 0; i < half; ++i)

@@ -168,39 +168,45 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 // ---------------------------------------------------------------------------
 // Exact bucketize by table ("KVQuant++" thread, "Fast codebook lookup": a
 // lookup against sorted thresholds instead of a nearest-centroid search).
-// The top 12 bits of u's fp32 pattern (sign, exponent, 3 mantissa bits) cut
-// the line into cells: a cell of non-negative patterns holds [lo, hi), one of
-// negative patterns (-hi, -lo], with hi <= 9/8 lo (and the cells of prefix 0
-// reaching down to +0 and -0).  Consecutive positive thresholds of the tables
-// used here fall in different cells and the smallest is above the prefix-0
-// cell (the host checks this for every table it builds), so a cell holds at
-// most one threshold: the entry of a cell is (that threshold or +inf, the
-// number of thresholds below the cell), and
+// The top 9 + MB bits of u's fp32 pattern (sign, exponent, MB mantissa bits;
+// MB = 3 for 4-bit codes, 1 for 3-bit codes) cut the line into cells: a cell
+// of non-negative patterns holds [lo, hi], one of negative patterns
+// [-hi, -lo], with hi < (1 + 2^-MB) lo (and the cells of prefix 0 reaching
+// down to +0 and -0).  Consecutive positive thresholds of the tables used
+// here fall in different cells and the smallest is above the prefix-0 cell
+// (the host checks this for every table it builds), so a cell holds at most
+// one threshold: the entry of a cell is (that threshold or +inf, the number
+// of thresholds below the cell), and
 //   code = count + (threshold < u)
 // equals #{thresholds < u} (ties go to the lower cell; -0 and +0 against the
 // zero threshold compare as IEEE floats do).
 // ---------------------------------------------------------------------------
 #ifndef KVQ_BUCKETIZE_CMP_MAXBITS
-#define KVQ_BUCKETIZE_CMP_MAXBITS 3
+#define KVQ_BUCKETIZE_CMP_MAXBITS 2
 #endif
 template <int BITS>
 struct BucketTables {
   static constexpr bool LUT = BITS > KVQ_BUCKETIZE_CMP_MAXBITS;
-  f32x2 cell[LUT ? 4096 : 1];   // (threshold inside the cell or +inf, count below as bits)
+  static constexpr int MB = BITS >= 4 ? 3 : 1;       // mantissa bits of the cell prefix
+  static constexpr int SHIFT = 23 - MB;
+  static constexpr int NCELL = 1 << (9 + MB);
+  f32x2 cell[LUT ? NCELL : 1];  // (threshold inside the cell or +inf, count below as bits)
   float cent[16];
 };
 
 template <int BITS>
 __device__ void build_bucket_tables(BucketTables<BITS> &bt, const float *thr, const float *cent,
                                     int tid, int nthreads) {
+  using BT = BucketTables<BITS>;
   constexpr int K = 1 << BITS;
-  if constexpr (BucketTables<BITS>::LUT) {
-    for (int i = tid; i < 4096; i += nthreads) {
+  if constexpr (BT::LUT) {
+    for (int i = tid; i < BT::NCELL; i += nthreads) {
       // the cell's range as (lower, upper) end points in the order of floats
-      const uint32_t a = (uint32_t)(i & 2047) << 20, b = a | 0xFFFFFu;
+      const uint32_t a = (uint32_t)(i & (BT::NCELL / 2 - 1)) << BT::SHIFT;
+      const uint32_t b = a | ((1u << BT::SHIFT) - 1u);
       const float m0 = __uint_as_float(a), m1 = __uint_as_float(b);
-      const bool neg = i >= 2048;
-      const float lo = neg ? -m1 : m0, hi = neg ? -m0 : m1;   // cell = [lo, hi] up to end points
+      const bool neg = i >= BT::NCELL / 2;
+      const float lo = neg ? -m1 : m0, hi = neg ? -m0 : m1;
       uint32_t below = 0;
       float inside = INFINITY;
       for (int k = 0; k + 1 < K; ++k) {
@@ -216,7 +222,7 @@ __device__ void build_bucket_tables(BucketTables<BITS> &bt, const float *thr, co
 
 template <int BITS>
 __device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables<BITS> &bt) {
-  const f32x2 e = bt.cell[__float_as_uint(u) >> 20];
+  const f32x2 e = bt.cell[__float_as_uint(u) >> BucketTables<BITS>::SHIFT];
   return __float_as_uint(e.y) + (e.x < u ? 1u : 0u);
 }
 
