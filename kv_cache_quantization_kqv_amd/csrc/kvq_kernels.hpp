@@ -1279,16 +1279,37 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
   __syncthreads();
   // o' (+ sqrt(pi/2)/m S^T a) into al[hh][i] (reused as the WHT buffer)
   float *wv = al;
-  for (int item = tid; item < GT * D; item += 256) {
+  if constexpr (VQ && GT * D < 256) {
+    // KS threads per output coordinate, each over D / KS rows of S, partial
+    // sums added in thread order
+    constexpr int NI = GT * D, KS = 256 / NI, KL = D / KS;
+    const int item = tid % NI, part = tid / NI;
     const int hh = item / D, i = item - hh * D;
-    float v = res[hh * NS + 2 + i];
-    if constexpr (VQ) {
-      const float *av = res + hh * NS + 2 + D;
-      float t = 0.0f;
-      for (int k = 0; k < D; ++k) t = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), av[k], t);
-      v = fmaf(a.vcoef, t, v);
+    const float *av = res + hh * NS + 2 + D;
+    float t = 0.0f;
+#pragma unroll 16
+    for (int k = part * KL; k < part * KL + KL; ++k) t = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), av[k], t);
+    al[tid] = t;
+    __syncthreads();
+    if (tid < NI) {
+      float u = 0.0f;
+#pragma unroll
+      for (int p = 0; p < KS; ++p) u += al[p * NI + item];
+      wv[item] = fmaf(a.vcoef, u, res[hh * NS + 2 + i]);
     }
-    wv[hh * D + i] = v;
+  } else {
+    for (int item = tid; item < GT * D; item += 256) {
+      const int hh = item / D, i = item - hh * D;
+      float v = res[hh * NS + 2 + i];
+      if constexpr (VQ) {
+        const float *av = res + hh * NS + 2 + D;
+        float t = 0.0f;
+#pragma unroll 16
+        for (int k = 0; k < D; ++k) t = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), av[k], t);
+        v = fmaf(a.vcoef, t, v);
+      }
+      wv[hh * D + i] = v;
+    }
   }
   __syncthreads();
   if (a.rk == RK_WHT || a.rk == RK_RHT) {
