@@ -181,7 +181,7 @@ def main():
                    "kernel": "prep_kernel + prefill_kernel (fp32 MFMA 16x16x4) + finish_kernel"}
         del qp, wsp, outp
 
-    roof = {"kernel": "kvq_decode_attention: query kernel + decode_kernel (split scan with fused merge)",
+    roof = {"kernel": "kvq_decode_attention: query kernel + decode_kernel (split scan, key scores on fp16 MFMA) + merge_kernel (split merge)",
             "bound": "hbm",
             "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,

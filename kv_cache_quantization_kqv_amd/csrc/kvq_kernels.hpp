@@ -207,13 +207,13 @@ __device__ void build_bucket_tables(BucketTables<BITS> &bt, const float *thr, co
       const float m0 = __uint_as_float(a), m1 = __uint_as_float(b);
       const bool neg = i >= BT::NCELL / 2;
       const float lo = neg ? -m1 : m0, hi = neg ? -m0 : m1;
+      // thresholds ascend: count those below lo by binary search; the next one
+      // is the cell's threshold if it does not exceed hi
       uint32_t below = 0;
-      float inside = INFINITY;
-      for (int k = 0; k + 1 < K; ++k) {
-        const float t = thr[k];
-        if (t < lo) ++below;
-        else if (t <= hi) inside = t;
-      }
+#pragma unroll
+      for (int step = K / 2; step >= 1; step >>= 1)
+        if (below + step <= (uint32_t)(K - 1) && thr[below + step - 1] < lo) below += step;
+      const float inside = (below < (uint32_t)(K - 1) && thr[below] <= hi) ? thr[below] : INFINITY;
       bt.cell[i] = f32x2{inside, __uint_as_float(below)};
     }
   }
@@ -2553,8 +2553,11 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 template <int D, int BITS, int RK, bool QJL>
 hipError_t quantize_go(const QuantArgs &a, bool bf16, hipStream_t s) {
   // persistent-style grid: each wave walks tiles with a stride of 4 * grid
+  // (encoders with a bucketize table: at most two blocks per CU, so each block
+  // builds its table once for many tiles)
   const int want = (a.total_tiles + 3) / 4;
-  const int grid = want < 2048 ? want : 2048;
+  const int gmax = BucketTables<BITS>::LUT ? 512 : 2048;
+  const int grid = want < gmax ? want : gmax;
   if constexpr (RK == RK_QR) {
     if (bf16)
       hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, true>), dim3(grid), dim3(256), 0, s, a);
