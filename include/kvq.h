@@ -201,8 +201,11 @@ kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *o
  * fp32 (device).  splits: number of token splits per (b, KV head); 0 picks
  * one for the GPU.  A split holds at most 1280 tokens when four or more query
  * heads share a KV head (2560 for two, 5120 for one): fewer splits than that
- * allows, or more than 8192, give KVQ_ERR_RANGE.  workspace: device scratch of
- * kvq_decode_workspace bytes (contents on entry do not matter).
+ * allows, or more than 8192, give KVQ_ERR_RANGE.  Each split covers
+ * ceil(n_ctx / splits) tokens rounded up to a multiple of 64, so trailing
+ * splits may be empty.  workspace: device scratch of kvq_decode_workspace
+ * bytes (contents on entry do not matter).  Three kernels run on the stream:
+ * query preparation, the split scan, the split merge.
  * Keys are scored in rotated space (q is rotated once instead of each key);
  * values and the V sketch term are accumulated in rotated and sketch space and
  * mapped back with one S^T product and one WHT per query head.
