@@ -182,12 +182,12 @@ bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // The encoder's table bucketize needs a symmetric threshold table with a zero
 // middle threshold, and at most one threshold in every cell of the prefix
-// (sign, exponent, MB mantissa bits; MB = 3 for 4-bit codes, else 1) of u:
+// (sign, exponent, MB mantissa bits; MB = 2 for 4-bit codes, else 1) of u:
 // positive thresholds with distinct prefixes, the smallest one above the
 // prefix-0 cell (which holds the zero threshold).
 bool codebook_usable(const kvq_codebook &cb) {
   const int K = 1 << cb.bits, half = K / 2;
-  const int shift = 23 - (cb.bits >= 4 ? 3 : 1);
+  const int shift = 23 - (cb.bits >= 4 ? 2 : 1);
   if (cb.threshold[half - 1] != 0.0f) return false;
   for (int k = 0; k + 1 < half; ++k) {
     const float p = cb.threshold[half + k];

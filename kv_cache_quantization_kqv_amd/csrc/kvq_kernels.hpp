@@ -169,7 +169,7 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 // Exact bucketize by table ("KVQuant++" thread, "Fast codebook lookup": a
 // lookup against sorted thresholds instead of a nearest-centroid search).
 // The top 9 + MB bits of u's fp32 pattern (sign, exponent, MB mantissa bits;
-// MB = 3 for 4-bit codes, 1 for 3-bit codes) cut the line into cells: a cell
+// MB = 2 for 4-bit codes, 1 for 3-bit codes) cut the line into cells: a cell
 // of non-negative patterns holds [lo, hi], one of negative patterns
 // [-hi, -lo], with hi < (1 + 2^-MB) lo (and the cells of prefix 0 reaching
 // down to +0 and -0).  Consecutive positive thresholds of the tables used
@@ -187,7 +187,7 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 template <int BITS>
 struct BucketTables {
   static constexpr bool LUT = BITS > KVQ_BUCKETIZE_CMP_MAXBITS;
-  static constexpr int MB = BITS >= 4 ? 3 : 1;       // mantissa bits of the cell prefix
+  static constexpr int MB = BITS >= 4 ? 2 : 1;       // mantissa bits of the cell prefix
   static constexpr int SHIFT = 23 - MB;
   static constexpr int NCELL = 1 << (9 + MB);
   f32x2 cell[LUT ? NCELL : 1];  // (threshold inside the cell or +inf, count below as bits)
@@ -2553,10 +2553,11 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 template <int D, int BITS, int RK, bool QJL>
 hipError_t quantize_go(const QuantArgs &a, bool bf16, hipStream_t s) {
   // persistent-style grid: each wave walks tiles with a stride of 4 * grid
-  // (encoders with a bucketize table: at most two blocks per CU, so each block
-  // builds its table once for many tiles)
+  // (encoders with a bucketize table: one round of resident blocks, three per
+  // CU, or two with the sketch staged as well, so each block builds its table
+  // once for many tiles)
   const int want = (a.total_tiles + 3) / 4;
-  const int gmax = BucketTables<BITS>::LUT ? 512 : 2048;
+  const int gmax = BucketTables<BITS>::LUT ? (QJL ? 512 : 768) : 2048;
   const int grid = want < gmax ? want : gmax;
   if constexpr (RK == RK_QR) {
     if (bf16)
