@@ -229,18 +229,72 @@ def test_explicit_splits_below_the_lds_budget_rejected(K):
     assert lib.kvq_decode_workspace(p, 8, 4096, 8193, C.byref(ws)) == 10
 
 
+def _cell_bits(bits):
+    """Mantissa bits of the encoder's bucketize cells (sign, exponent and MB
+    mantissa bits of u's fp32 pattern): 2 for 4-bit codes, 1 for 3-bit codes."""
+    return 2 if bits >= 4 else 1
+
+
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_table_bucketize_precondition(K, d, bits):
-    """At most one positive threshold per 11-bit |u| prefix cell (the encoder's
-    exact table bucketize relies on it); the library re-checks before launch."""
+    """At most one threshold per prefix cell and the smallest positive one
+    above the prefix-0 cell (the encoder's exact table bucketize relies on it;
+    the library re-checks before launch)."""
     cb = K.kvq_codebook_init(d, bits)
     n = 1 << bits
     pos = np.array(cb.threshold[n // 2: n - 1], np.float32)
-    cells = pos.view(np.uint32) >> 20
+    cells = pos.view(np.uint32) >> (23 - _cell_bits(bits))
     assert len(set(cells.tolist())) == len(cells)
+    if len(cells):
+        assert cells[0] != 0
     if len(pos) > 1:
-        assert np.min(pos[1:] / pos[:-1]) > 1.125
+        assert np.min(pos[1:] / pos[:-1]) > 1 + 2.0 ** -_cell_bits(bits)
+
+
+def _cell_table(thr, mb):
+    """The encoder's cell table, built as the kernel builds it: for each
+    prefix (sign, exponent, mb mantissa bits) the count of thresholds below the
+    cell and the threshold inside it (+inf if none)."""
+    n, shift = 1 << (9 + mb), 23 - mb
+    i = np.arange(n, dtype=np.uint64)
+    a = ((i & (n // 2 - 1)) << shift).astype(np.uint32)
+    b = (a | np.uint32((1 << shift) - 1)).astype(np.uint32)
+    m0, m1 = a.view(np.float32), b.view(np.float32)
+    neg = i >= n // 2
+    lo = np.where(neg, -m1, m0)
+    hi = np.where(neg, -m0, m1)
+    below = np.array([np.sum(thr < l) for l in lo])
+    inside = np.full(n, np.inf, np.float32)
+    for k, t in enumerate(thr):
+        sel = (t >= lo) & (t <= hi)
+        inside[sel] = t
+    return below, inside, shift
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_cell_table_bucketize_counts_thresholds(K, d, bits):
+    """count + (threshold < u) from the cell of u's bit pattern equals the
+    plain count #{thresholds < u} (ties lower, -0 and +0 as IEEE floats), on
+    random coordinates, on every threshold and its two fp32 neighbours, on
+    both zeros and on the ends of every cell."""
+    cb = K.kvq_codebook_init(d, bits)
+    thr = np.array(cb.threshold[: (1 << bits) - 1], np.float32)
+    below, inside, shift = _cell_table(thr, _cell_bits(bits))
+    rng = np.random.default_rng(3)
+    u = [rng.standard_normal(20000).astype(np.float32) / np.float32(np.sqrt(d)),
+         thr, np.nextafter(thr, np.float32(np.inf)), np.nextafter(thr, np.float32(-np.inf)),
+         np.array([0.0, -0.0, 1e-30, -1e-30, 1.0, -1.0, 1.999, -1.999], np.float32)]
+    n = 1 << (9 + _cell_bits(bits))
+    ends = (np.arange(n, dtype=np.uint64) << shift).astype(np.uint32)
+    u += [ends.view(np.float32), (ends | np.uint32((1 << shift) - 1)).view(np.float32)]
+    u = np.concatenate(u)
+    u = u[np.isfinite(u)]
+    idx = u.view(np.uint32) >> shift
+    got = below[idx] + (inside[idx] < u)
+    want = np.sum(thr[None, :] < u[:, None], axis=1)
+    assert np.array_equal(got, want)
 
 
 def test_bad_codebook_rejected(K):
@@ -251,6 +305,9 @@ def test_bad_codebook_rejected(K):
     c = _fake_cache(K, d=64)
     c.cb_v.centroid[0] = 0.5                                 # asymmetric table
     assert lib.kvq_quantize_v(C.byref(c), 0x900000, 1, 0, 4, 0, 0, 64, None) == 4
+    c = _fake_cache(K, d=64)
+    c.cb_k.threshold[8], c.cb_k.threshold[6] = 1e-39, -1e-39  # in the zero threshold's cell
+    assert lib.kvq_quantize_k(C.byref(c), 0x900000, 1, 0, 4, 0, 0, 64, None) == 4
 
 
 # --------------------------------------------------------------------------- rotations
