@@ -26,13 +26,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 SOURCES = ["kvq_host.cpp", "kvq_d16.hip", "kvq_d32.hip", "kvq_d64.hip", "kvq_d128.hip"]
 
-# Optional extra compiler flags (tuning macros such as -DKVQ_DECODE_E4=16).
-EXTRA = os.environ.get("KVQ_EXTRA_FLAGS", "").split()
-
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, *EXTRA, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

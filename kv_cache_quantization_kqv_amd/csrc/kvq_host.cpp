@@ -325,13 +325,6 @@ int prefill_splits(const kvq_cache *c, int q_heads, int n_q) {
   return sp < 1 ? 1 : (int)sp;
 }
 
-// Split arrival counters, one per (b, KV head, head group), padded to 16 bytes.
-size_t counter_bytes(const kvq_cache *c, int q_heads) {
-  const int G = q_heads / c->kv_heads;
-  const size_t n = (size_t)c->batch * c->kv_heads * (G / heads_per_block(G));
-  return (n * sizeof(unsigned) + 15) / 16 * 16;
-}
-
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || (G > 4 && G % 4 == 0); }
 
 // Fewest splits that keep every split's logits in LDS.
@@ -566,8 +559,7 @@ kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int 
   if (splits == 0) splits = auto_splits(c, q_heads, n_ctx);
   if (splits < min_splits(c, q_heads, n_ctx)) return KVQ_ERR_RANGE;
   const size_t rows = (size_t)c->batch * q_heads, d = (size_t)c->d;
-  *bytes = sizeof(float) * (rows * d * 2 + rows * (size_t)splits * (2 + 2 * d) + rows * (2 + d)) +
-           counter_bytes(c, q_heads);
+  *bytes = sizeof(float) * (rows * d * 2 + rows * (size_t)splits * (2 + 2 * d) + rows * (2 + d));
   return KVQ_OK;
 }
 
@@ -609,15 +601,12 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   float *sqt = ws + (size_t)rows * d;
   float *part = ws + (size_t)rows * d * 2;
   float *wpart = part + (size_t)rows * splits * (2 + 2 * (size_t)d);
-  unsigned *cnt = (unsigned *)(wpart + (size_t)rows * (2 + d));
-  const int units = c->batch * c->kv_heads * (G / gt);
   hipStream_t hs = (hipStream_t)stream;
 
   kvq::PrepArgs p;
   std::memset(&p, 0, sizeof(p));       // nq = 0: decode layout
   p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = rows;
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
-  p.cnt = cnt; p.ncnt = units;
   const int rk = rot_code(c);
   p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
   for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
@@ -644,7 +633,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   std::memset(&a, 0, sizeof(a));
   a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
   a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
-  a.qt = qt; a.sqt = sqt; a.part = part; a.cnt = cnt; a.S = c->S; a.out = out;
+  a.qt = qt; a.sqt = sqt; a.part = part; a.S = c->S; a.out = out;
   a.wpart = n_win > 0 ? wpart : nullptr;
   a.t0 = t_begin;
   a.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
@@ -728,7 +717,7 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   std::memset(&p, 0, sizeof(p));
   p.q = q; p.qt = qt; p.sqt = sqt; p.S = c->S; p.rows = (int)rows;
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = 1; p.HG = G;
-  p.cnt = nullptr; p.ncnt = 0; p.nq = n_q;
+  p.nq = n_q;
   p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
   for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
   p.Q = c->rot_Q;

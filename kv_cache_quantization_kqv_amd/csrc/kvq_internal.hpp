@@ -63,8 +63,6 @@ struct PrepArgs {
   int rows;                  // B * Hq
   int Hq, Hkv, G, GT, HG;    // G = Hq / Hkv query heads per KV head, GT per block, HG = G / GT
   float qscale;              // log2(e)/d (Hadamard kinds) or log2(e)/sqrt(d)
-  unsigned *cnt;             // split arrival counters, zeroed here (B * Hkv * HG)
-  int ncnt;
   uint32_t rsign[4];         // RK_RHT
   const float *Q;            // RK_QR
   int nq;                    // > 0: multi-query layout (rows (b, i, hq) of [B][nq][Hq][d];
@@ -76,7 +74,6 @@ struct DecodeArgs {
   const uint16_t *kn, *kr, *vn, *vr;
   const float *qt, *sqt;      // prepared queries, layout of PrepArgs::qt
   float *part;               // [B][Hq][splits][2 + 2d]
-  unsigned *cnt;             // split arrival counter per (b, KV head, head group)
   const uint16_t *S;         // sketch (merge: S^T a)
   float *out;                // [B][Hq][d]
   float kcent[16], vcent[16];

@@ -1012,7 +1012,6 @@ __global__ __launch_bounds__(D) void prep_kernel(const PrepArgs a) {
     dst = ((((size_t)b * a.Hkv + hkv) * a.HG + hg) * D + i) * a.GT + hh;
   }
   a.qt[dst] = x;
-  if (i == 0 && row < a.ncnt) a.cnt[row] = 0u;
   if constexpr (KQ) {
     __syncthreads();
     t_s[i] = x;
@@ -1206,10 +1205,9 @@ struct VTile {
   static_assert(BYTES % 16 == 0 && VS % 16 == 0, "tile segments must be 16-byte multiples");
 };
 
-// Device-coherent load of a split partial written by another block.
-__device__ __forceinline__ float ld_part(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Load of a split partial (written by the scan kernel, which completed before
+// the merge kernel started on the same stream).
+__device__ __forceinline__ float ld_part(const float *p) { return *p; }
 
 // Merge of the splits of GT query heads (run by one block of 256 threads).
 // LDS: `sm` needs GT * (MCH + NS) floats; `mx` GT floats.
@@ -1359,12 +1357,6 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
 #define KVQ_SCAN_OCC __attribute__((amdgpu_waves_per_eu(KVQ_SCAN_WAVES_PER_EU)))
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-// Split merge in the scan's last block (1) or in a kernel of its own that
-// follows the scan on the stream, one block per query row (0).
-#ifndef KVQ_SCAN_FUSED_MERGE
-#define KVQ_SCAN_FUSED_MERGE 0
-#endif
 
 // Split merge of one query row (b, hq): log-sum-exp weights, S^T a, inverse
 // rotation, division by L (and the full-precision window, if any).
@@ -2028,38 +2020,12 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     }
     __syncthreads();
   }
-  // Partials are published with device-coherent (agent-scope) stores and read
-  // back with device-coherent loads, so no cache-wide write-back is needed:
-  // each thread waits for its stores to complete, the block synchronises, and
-  // only then is the arrival counter bumped.
-  if constexpr (!KVQ_SCAN_FUSED_MERGE) {
-    // the merge kernel that follows on the stream combines the splits
-    for (int idx = tid; idx < GT * NS; idx += 256) {
-      const int hh = idx / NS, k = idx - hh * NS;
-      float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
-      dst[k] = (k == 0) ? (nloc > 0 ? M[hh] : -INFINITY) : wst[idx];
-    }
-    return;
-  }
+  // the merge kernel that follows on the stream combines the splits
   for (int idx = tid; idx < GT * NS; idx += 256) {
     const int hh = idx / NS, k = idx - hh * NS;
     float *dst = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.splits + split) * NS;
-    __hip_atomic_store(dst + k, (k == 0) ? (nloc > 0 ? M[hh] : -INFINITY) : wst[idx],
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    dst[k] = (k == 0) ? (nloc > 0 ? M[hh] : -INFINITY) : wst[idx];
   }
-
-  // ---- merge: the last block of this (b, KV head, head group) to finish
-  // combines the splits: log-sum-exp weights in base 2, o' += sqrt(pi/2)/m S^T a,
-  // one inverse WHT, division by L.
-  __shared__ int last_s;
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
-  __syncthreads();
-  if (tid == 0)
-    last_s = __hip_atomic_fetch_add(a.cnt + unitg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(a.splits - 1);
-  __syncthreads();
-  if (!last_s) return;
-  merge_splits<D, VQ, GT>(a, wbuf, red_s[0], b, hq0);
 }
 
 // ---------------------------------------------------------------------------
@@ -2688,7 +2654,7 @@ hipError_t decode_go(const DecodeArgs &a, int gt, int B, hipStream_t s) {
     case 4: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 4>), grid, blk, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  if (!KVQ_SCAN_FUSED_MERGE) hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
   return hipGetLastError();
 }
 

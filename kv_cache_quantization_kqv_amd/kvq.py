@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("KVQ_LIB_PATH") or os.path.join(HERE, "libkvq.so")
+LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_ERR_NULL", 2: "KVQ_ERR_ALIGN", 3: "KVQ_ERR_DIM",

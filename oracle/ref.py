@@ -237,6 +237,23 @@ class OracleCache:
                                    self.m, _p(out), nthreads)
         return out
 
+    def view(self, b0: int, b1: int, h0: int = 0, h1: int | None = None) -> "OracleCache":
+        """The same arrays restricted to batch rows [b0, b1) and KV heads
+        [h0, h1) (shared memory; a partial head range needs a single batch
+        row, so the view stays contiguous)."""
+        h1 = self.H if h1 is None else h1
+        if (h0, h1) != (0, self.H) and b1 != b0 + 1:
+            raise ValueError("a partial head range needs a single batch row")
+        v = OracleCache.__new__(OracleCache)
+        v.__dict__.update(self.__dict__)
+        v.B, v.H = b1 - b0, h1 - h0
+        sl = (slice(b0, b1), slice(h0, h1))
+        v.codes = self.codes[sl]
+        v.signs = None if self.signs is None else self.signs[sl]
+        v.norm = self.norm[sl]
+        v.rnorm = None if self.rnorm is None else self.rnorm[sl]
+        return v
+
     def _side_struct(self):
         return _OrcSide(_p(self.codes), _p(self.signs), _p(self.norm), _p(self.rnorm),
                         self.rot.code(self.side), self.side.bits, self.side.qjl,

@@ -154,10 +154,8 @@ def test_validation_status_codes(K):
     need = ws.value
     d, rows, splits = 64, 2, K.kvq_decode_auto_splits(c, 2, 8)
     assert splits >= 1
-    units = 1 * 2 * 1                       # (b, KV head, head group) split counters
-    # prepared queries, split partials, the window partial, split counters
-    assert need == (4 * (rows * d * 2 + rows * splits * (2 + 2 * d) + rows * (2 + d))
-                    + (4 * units + 15) // 16 * 16)
+    # prepared queries, split partials, the window partial
+    assert need == 4 * (rows * d * 2 + rows * splits * (2 + 2 * d) + rows * (2 + d))
     q, out, w = 0xA00000, 0xB00000, 0xC00000
     assert lib.kvq_decode_attention(p, q, 1, 2, 8, 0, out, w, need - 1, None) == 7
     assert lib.kvq_decode_attention(p, q, 1, 2, 8, 0, out, None, need, None) == 7
