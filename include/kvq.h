@@ -27,7 +27,9 @@
  * Conventions for every entry point
  *  - Returns kvq_status; never throws; never synchronises a stream.
  *  - Device pointers are caller-owned (allocate with torch / hipMalloc).  The
- *    library allocates no device memory and keeps no pointer after return.
+ *    library allocates no device memory and keeps no pointer after return;
+ *    its only device storage is the fixed scratch array that
+ *    kvq_decode_attention_noalloc uses.
  *  - All validation happens on the host before any launch: a call that fails
  *    validation launches nothing.  A failed launch returns KVQ_ERR_HIP.
  *    Asynchronous device faults surface at the caller's next synchronisation.
@@ -234,6 +236,24 @@ kvq_status kvq_decode_attention_window(const kvq_cache *c, const void *q, int q_
                                        const void *wv, int w_dtype, int n_win, int splits,
                                        float *out, void *workspace, size_t workspace_bytes,
                                        void *stream);
+
+/* kvq_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace comes from a fixed device array inside the
+ * library, KVQ_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on (held until
+ * the process ends; its address is looked up once per device on the first
+ * call).  The call allocates nothing; the caller still passes q and out.
+ * Arguments and results as kvq_decode_attention, on the current device (the
+ * stream must belong to it).  Nothing in the array needs to start at zero.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or host threads) race and give undefined results.
+ * Errors: as kvq_decode_attention; KVQ_ERR_WORKSPACE when the call needs more
+ * than KVQ_NOALLOC_SCRATCH_BYTES of workspace (kvq_decode_workspace tells);
+ * KVQ_ERR_HIP when the array's device address cannot be obtained. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_cache *c, const void *q, int q_dtype,
+                                        int q_heads, int n_ctx, int splits, float *out,
+                                        void *stream);
 
 /* Workspace bytes kvq_decode_attention (or kvq_decode_attention_window over
  * n_ctx compressed slots) needs for these arguments; n_ctx may be 0 here. */

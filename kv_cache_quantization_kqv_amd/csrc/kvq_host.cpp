@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -359,6 +360,35 @@ int split_tokens(int n_ctx, int splits) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Fixed device scratch for kvq_decode_attention_noalloc: a file-scope device
+// array (each GPU the library runs on holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel: the device
+// address is looked up once per device with hipGetSymbolAddress and cached.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *kvq_version(void) { return "libkvq 0.1 (gfx950)"; }
@@ -663,6 +693,20 @@ kvq_status kvq_decode_attention(const kvq_cache *c, const void *q, int q_dtype, 
   if (n_ctx < 1) return c ? KVQ_ERR_RANGE : KVQ_ERR_NULL;
   return decode_impl(c, q, q_dtype, q_heads, 0, n_ctx, nullptr, nullptr, KVQ_F32, 0, splits,
                      out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache *c, const void *q, int q_dtype,
+                                        int q_heads, int n_ctx, int splits, float *out,
+                                        void *stream) {
+  if (n_ctx < 1) return c ? KVQ_ERR_RANGE : KVQ_ERR_NULL;
+  size_t need = 0;
+  kvq_status s = kvq_decode_workspace(c, q_heads, n_ctx, splits, &need);
+  if (s != KVQ_OK) return s;
+  if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  void *ws = scratch_address();
+  if (!ws) return KVQ_ERR_HIP;
+  return decode_impl(c, q, q_dtype, q_heads, 0, n_ctx, nullptr, nullptr, KVQ_F32, 0, splits, out,
+                     ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kvq_status kvq_decode_attention_window(const kvq_cache *c, const void *q, int q_dtype,

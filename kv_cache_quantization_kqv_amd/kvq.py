@@ -27,7 +27,8 @@ KVQ_F32, KVQ_BF16 = 0, 1
 EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_set_rotation",
            "kvq_rotation_signs", "kvq_rotation_qr", "kvq_cache_layout", "kvq_quantize_k",
            "kvq_quantize_v", "kvq_dequantize", "kvq_decode_attention",
-           "kvq_decode_attention_window", "kvq_decode_workspace", "kvq_decode_auto_splits",
+           "kvq_decode_attention_window", "kvq_decode_attention_noalloc",
+           "kvq_decode_workspace", "kvq_decode_auto_splits",
            "kvq_prefill_attention", "kvq_prefill_workspace", "kvq_status_str", "kvq_version"]
 
 
@@ -83,6 +84,7 @@ def lib():
             "kvq_decode_attention": ([cache_p, vp, i32, i32, i32, i32, vp, vp, sz, vp], i32),
             "kvq_decode_attention_window": ([cache_p, vp, i32, i32, i32, i32, vp, vp, i32, i32,
                                              i32, vp, vp, sz, vp], i32),
+            "kvq_decode_attention_noalloc": ([cache_p, vp, i32, i32, i32, i32, vp, vp], i32),
             "kvq_decode_workspace": ([cache_p, i32, i32, i32, C.POINTER(sz)], i32),
             "kvq_decode_auto_splits": ([cache_p, i32, i32], i32),
             "kvq_prefill_attention": ([cache_p, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp],
@@ -197,6 +199,12 @@ def kvq_decode_attention_window(c: kvq_cache, q: int, q_dtype: int, q_heads: int
     _check(lib().kvq_decode_attention_window(C.byref(c), q, q_dtype, q_heads, t_begin, t_end, wk,
                                              wv, w_dtype, n_win, splits, out, workspace, ws_bytes,
                                              stream), "kvq_decode_attention_window")
+
+
+def kvq_decode_attention_noalloc(c: kvq_cache, q: int, q_dtype: int, q_heads: int, n_ctx: int,
+                                 splits: int, out: int, stream: int = 0):
+    _check(lib().kvq_decode_attention_noalloc(C.byref(c), q, q_dtype, q_heads, n_ctx, splits,
+                                              out, stream), "kvq_decode_attention_noalloc")
 
 
 def kvq_prefill_workspace(c: kvq_cache, q_heads: int, n_q: int) -> int:

@@ -1,0 +1,78 @@
+"""kvq_decode_attention_noalloc (workspace from the library's fixed device
+array) against kvq_decode_attention (caller workspace), through the C ABI, on
+two calls in a row, the second with a smaller input.  Same kernels, same
+inputs and split counts: the outputs must be identical bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_kqv_amd import kvq, synth
+from kv_cache_quantization_kqv_amd.kvq import KVQCache
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _decode_both(cache: KVQCache, q: torch.Tensor, n_ctx: int):
+    dev = cache.device
+    Hq = q.shape[1]
+    splits = kvq.kvq_decode_auto_splits(cache.c, Hq, n_ctx)
+    need = kvq.kvq_decode_workspace(cache.c, Hq, n_ctx, splits)
+    assert need <= 64 << 20
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ref = torch.empty(cache.batch, Hq, cache.d, dtype=torch.float32, device=dev)
+    got = torch.full_like(ref, float("nan"))
+    dt = kvq.KVQ_BF16 if q.dtype == torch.bfloat16 else kvq.KVQ_F32
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    kvq.kvq_decode_attention(cache.c, q.data_ptr(), dt, Hq, n_ctx, splits, ref.data_ptr(),
+                             ws.data_ptr(), need, stream)
+    kvq.kvq_decode_attention_noalloc(cache.c, q.data_ptr(), dt, Hq, n_ctx, splits,
+                                     got.data_ptr(), stream)
+    torch.cuda.synchronize(dev)
+    return ref.cpu().numpy(), got.cpu().numpy()
+
+
+@pytest.mark.parametrize("scheme,n,d,B,Hkv,G,N,dtype", [
+    ("KQV", 4, 128, 2, 4, 4, 3000, torch.bfloat16),
+    ("QKQV", 3, 64, 3, 2, 2, 777, torch.float32),
+    ("KV", 2, 128, 1, 8, 1, 5000, torch.bfloat16),
+])
+def test_noalloc_equals_workspace_entry(scheme, n, d, B, Hkv, G, N, dtype):
+    dev = torch.device("cuda", torch.cuda.current_device())
+    print(f"case noalloc {scheme}{n} d={d} B={B} Hkv={Hkv} G={G} N={N} {dtype}", flush=True)
+    cache = KVQCache(scheme, n, d, B, Hkv, N, device=dev)
+    K = synth.gaussian((B, Hkv, N, d), 501, dtype, dev)
+    V = synth.gaussian((B, Hkv, N, d), 502, dtype, dev)
+    cache.quantize_k(K, 0)
+    cache.quantize_v(V, 0)
+    q1 = synth.gaussian((B, Hkv * G, d), 503, dtype, dev)
+    q2 = synth.gaussian((B, Hkv * G, d), 504, dtype, dev)
+    # first call over the whole context, then a smaller one (fewer tokens)
+    for q, n_ctx in ((q1, N), (q2, N // 3 + 1)):
+        ref, got = _decode_both(cache, q, n_ctx)
+        assert np.isfinite(ref).all()
+        assert np.array_equal(ref, got), f"n_ctx={n_ctx}: max |diff| {np.abs(ref - got).max()}"
+
+
+def test_noalloc_rejects_oversize():
+    """A call needing more than the fixed array returns KVQ_ERR_WORKSPACE and
+    launches nothing."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    # the prepared queries alone (B * Hq * d * 8 bytes) exceed the array
+    B, Hkv, G, N, d = 256, 64, 8, 64, 128
+    c = kvq.kvq_cache_init(kvq.SCHEMES["KQV"], 4, d, B, Hkv, N)
+    # plausible non-null, aligned pointers; validation fails before any launch
+    dummy = torch.empty(64, dtype=torch.uint8, device=dev)
+    for name in ("k_codes", "k_norm", "v_codes", "v_norm", "v_signs", "v_rnorm", "S"):
+        setattr(c, name, dummy.data_ptr())
+    need = kvq.kvq_decode_workspace(c, Hkv * G, N, 0)
+    assert need > 64 << 20
+    out = torch.empty(16, dtype=torch.float32, device=dev)
+    st = kvq.lib().kvq_decode_attention_noalloc(kvq.C.byref(c), dummy.data_ptr(), kvq.KVQ_BF16,
+                                                Hkv * G, N, 0, out.data_ptr(), None)
+    assert st == 7
