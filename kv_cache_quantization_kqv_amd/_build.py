@@ -21,6 +21,9 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-ffp-contract=off", "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in ordinary VGPRs (gfx950 supports both forms):
+         # avoids accumulator copies between the register files in loops
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
          "-I", os.path.join(ROOT, "include")]
 

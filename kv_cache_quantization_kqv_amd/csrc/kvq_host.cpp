@@ -328,25 +328,33 @@ int prefill_splits(const kvq_cache *c, int q_heads, int n_q) {
 
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || (G > 4 && G % 4 == 0); }
 
-// Fewest splits that keep every split's logits in LDS.
+// The matrix-core scan (head dimension 128) streams any number of tokens per
+// split; the vector-unit scan keeps a split's logits in LDS.
+bool scan_mfma(const kvq_cache *c) { return c->d == 128; }
+
+// Fewest splits that keep every split's logits in LDS (vector-unit scan).
 long long min_splits(const kvq_cache *c, int q_heads, int n_ctx) {
+  if (scan_mfma(c)) return 1;
   const int tmax = kvq::scan_tokens_max(heads_per_block(q_heads / c->kv_heads));
   return ((long long)n_ctx + tmax - 1) / tmax;
 }
 
-// About KVQ_SCAN_BLOCKS scan blocks: the split length is rounded up to whole
-// 256-token rounds of the key phase (at least 256), but stays within the LDS
-// logit buffer.
+// About KVQ_SCAN_BLOCKS scan blocks (KVQ_SCAN_BLOCKS_MFMA for the matrix-core
+// scan): the split length is rounded up to whole 256-token rounds (at least
+// 256), and for the vector-unit scan stays within the LDS logit buffer.
 int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   const int G = q_heads / c->kv_heads;
   const int HG = G / heads_per_block(G);
   const long long units = (long long)c->batch * c->kv_heads * HG;
-  const long long want = (KVQ_SCAN_BLOCKS + units - 1) / units;
-  const long long tmax = kvq::scan_tokens_max(heads_per_block(G));
+  const long long target = scan_mfma(c) ? KVQ_SCAN_BLOCKS_MFMA : KVQ_SCAN_BLOCKS;
+  const long long want = (target + units - 1) / units;
   if (n_ctx <= 0) return 1;
   long long tps = ((long long)n_ctx + want - 1) / want;
   tps = tps < 256 ? 256 : (tps + 255) / 256 * 256;
-  if (tps > tmax) tps = tmax;
+  if (!scan_mfma(c)) {
+    const long long tmax = kvq::scan_tokens_max(heads_per_block(G));
+    if (tps > tmax) tps = tmax;
+  }
   const long long s = ((long long)n_ctx + tps - 1) / tps;
   return s < 1 ? 1 : (int)s;
 }
@@ -610,6 +618,8 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
     return KVQ_ERR_RANGE;
   if (t_end > c->capacity) return KVQ_ERR_CAPACITY;
   if (t_end - t_begin + n_win < 1) return KVQ_ERR_RANGE;
+  // the matrix-core scan addresses a unit's records with 32-bit byte offsets
+  if (scan_mfma(c) && (uint64_t)t_end * 64u >= (1ull << 32)) return KVQ_ERR_RANGE;
   if (n_win > 0) {
     if (!wk || !wv) return KVQ_ERR_NULL;
     if (w_dtype != KVQ_F32 && w_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;

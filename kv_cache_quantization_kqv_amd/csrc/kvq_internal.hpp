@@ -17,9 +17,13 @@ namespace kvq {
 
 inline int scan_tokens_max(int gt) { return KVQ_SCAN_WBUF_FLOATS / (2 * gt); }
 
-// Target block count of the automatic decode split choice.
+// Target block count of the automatic decode split choice (vector-unit scan,
+// matrix-core scan).
 #ifndef KVQ_SCAN_BLOCKS
 #define KVQ_SCAN_BLOCKS 4096
+#endif
+#ifndef KVQ_SCAN_BLOCKS_MFMA
+#define KVQ_SCAN_BLOCKS_MFMA 2048
 #endif
 
 // Rotation applied by the codec (kernel template / argument code):

@@ -2512,6 +2512,12 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
   }
 }
 
+}  // namespace kvq
+
+#include "kvq_scan.hpp"
+
+namespace kvq {
+
 // ---------------------------------------------------------------------------
 // Dispatchers (host).  Only the (bits, rotation, sketch) combinations that the
 // three schemes produce are instantiated.
@@ -2648,6 +2654,12 @@ hipError_t launch_prep(const PrepArgs &a, int rk, bool kq, bool bf16, hipStream_
 template <int D, int KB, bool KQ, int VB, bool VQ>
 hipError_t decode_go(const DecodeArgs &a, int gt, int B, hipStream_t s) {
   const dim3 grid(a.splits, a.Hkv * a.HG, B), blk(256);
+  if constexpr (D == 128) {
+    // matrix-core scan (every scheme and head grouping at d = 128)
+    hipLaunchKernelGGL((scan_kernel<KB, KQ, VB, VQ>), grid, blk, 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
+    return hipGetLastError();
+  }
   switch (gt) {
     case 1: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 1>), grid, blk, 0, s, a); break;
     case 2: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 2>), grid, blk, 0, s, a); break;

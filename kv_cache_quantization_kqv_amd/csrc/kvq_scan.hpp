@@ -1,0 +1,632 @@
+// kvq_scan.hpp -- the decode scan on the matrix cores (head dimension 128).
+// Included by kvq_kernels.hpp.
+//
+// One block (4 waves) per (token split, KV head, group of GT <= 4 query
+// heads, batch row), as the merge kernel expects; each wave streams its own
+// quarter of the split in blocks of 16 tokens and keeps a running softmax,
+// so the main loop has no block barrier.  All three contractions of a token
+// block run on v_mfma_f32_16x16x32_f16 (16 x 16 output, 32-deep):
+//
+//   scores  S[row][t] = sum_k Q[row][k] K^[k][t]     rows 4h + kind, t = token
+//   values  O[c][col] = sum_k V^[c][k] W[k][col]     c = coordinate, k = (token, part)
+//   sketch  A[m][col] = sum_k Sg[m][k] W'[k][col]    m = sketch row, k = token
+//
+// fp16 has 11 significant bits, so every operand that must carry fp32-level
+// precision is split x = xh + 2^-11 xl (xh = fp16(x), xl = fp16((x - xh) 2^11)):
+// the centroids of both tables, the prepared query and S q', the softmax
+// weights c = w n_v and cq = c rho_v.  Two output columns per quantity collect
+// sum xh yh and sum (xh yl + xl yh); the dropped xl yl term is 2^-22 relative.
+// Sign bits enter as exact fp16 +-1.
+//
+// Lane roles (lane = 16 g + n):
+//   scores / softmax : token n of the block, query head g (one pair per lane);
+//                      the running max is updated once per pair of blocks
+//   value A operand  : coordinate 8 n + j of value block j, tokens 4 g .. 4 g + 3
+//   sketch A operand : sketch row 8 n + j, tokens 4 g .. 4 g + 3 of two blocks
+//   weight operands  : column 4 h + kind (kind 0/1: value hh/cross, 2/3:
+//                      sketch hi/lo) of head h, tokens of lane group g
+// The softmax lane layout is turned into the weight-operand layout through a
+// small per-wave LDS buffer (one dword per (token, head) and quantity).
+//
+// Records are read in their stored layout with raw buffer loads (one
+// descriptor per array and unit; slots past the scanned range read as zero,
+// so the loads need no branch): each lane loads the bytes its operand needs (the 16-byte key quarter of its token, the value-code bytes of
+// its eight coordinates for four tokens, the sign byte of its eight sketch
+// rows), and the value codes of two tokens are merged per coordinate by
+// in-register bit shuffles into pair-table indices.
+#pragma once
+
+namespace kvq {
+
+// 8 fp16 lanes of an MFMA operand from four dwords.
+__device__ __forceinline__ f16x8 op8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(f16x8, u32x4{a, b, c, d});
+}
+
+// Delta swap: exchange the bit groups selected by m with those s bits above.
+__device__ __forceinline__ uint32_t dswap(uint32_t x, int s, uint32_t m) {
+  const uint32_t t = ((x >> s) ^ x) & m;
+  return x ^ t ^ (t << s);
+}
+
+// Maximum / sum over each row of 16 lanes (DPP), result in every lane of the row.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Value of lane 4 q + 1 (resp. + 3) in lane 4 q (resp. 4 q + 2): quad_perm [1, 1, 3, 3].
+__device__ __forceinline__ float quad_next(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xF5, 0xF, 0xF, false));
+}
+
+// fp16 hi/lo split of two non-negative floats: (hi(a), hi(b)) and (lo(a), lo(b)),
+// lo = fp16((x - hi) 2^11), packed low half first.  Conversions truncate; the
+// remainder captures what the high part drops.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  const float ah = (float)__builtin_bit_cast(_Float16, (uint16_t)(hi & 0xFFFFu));
+  const float bh = (float)__builtin_bit_cast(_Float16, (uint16_t)(hi >> 16));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz((a - ah) * 2048.0f, (b - bh) * 2048.0f));
+}
+
+// fp16 split of one float (any sign): hi | lo << 16.
+__device__ __forceinline__ void split1(float x, _Float16 &h, _Float16 &l) {
+  h = (_Float16)x;
+  l = (_Float16)((x - (float)h) * 2048.0f);
+}
+
+template <int KB, bool KQ, int VB, bool VQ>
+struct ScanShape {
+  static constexpr int D = 128;
+  static constexpr int KREC = D * KB / 8, VREC = D * VB / 8, SREC = D / 8;
+  // key operand table: byte (KB 4) or 6-bit index (KB 3) of two codes -> 8
+  // bytes; byte (KB 2) or nibble (KB 1) of four codes -> 16 bytes
+  static constexpr bool KPAIR = KB >= 3;
+  static constexpr int KENT = KB == 4 ? 256 : KB == 3 ? 64 : KB == 2 ? 256 : 16;
+  static constexpr int KW = KB == 4 ? 4 : KB == 3 ? 3 : KB == 2 ? 2 : 1;   // key dwords per lane
+  static constexpr int VENT = 1 << (2 * VB);                                // value token-pair table
+  static constexpr bool SPIN = KQ || VQ;
+  static constexpr int NS = 2 + 2 * D;                                      // partial floats per head
+};
+
+// One token block's raw data in registers.  Keys and norms are loaded per
+// scored token (lane role above); the block's value records and value sign
+// records are contiguous (16 x VREC and 16 x 16 bytes) and are loaded as
+// 16-byte pieces (lane l: piece l), then staged in LDS, from where each lane
+// picks the bytes of its operand role.
+template <int KB, bool KQ, int VB, bool VQ>
+struct ScanBlock {
+  using SS = ScanShape<KB, KQ, VB, VQ>;
+  uint32_t k[SS::KW];    // key bytes of token n for coordinates 32 g .. 32 g + 31
+  uint32_t ks;           // key sign bytes 4 g .. 4 g + 3 of token n (rows 32 g .. 32 g + 31)
+  uint32_t nk, rk, nv, rv;   // fp16 bits of the key norm, key residual norm, value norm, value residual norm
+  u32x4 vp;              // piece l of the block's value records (lanes l < VREC)
+  u32x4 sp;              // piece l of the block's value sign records (lanes l < 16)
+};
+
+// Buffer descriptors of one (batch row, KV head) unit: each covers the unit's
+// slots [0, t0 + n_ctx) of one array, so a load past the scanned range reads
+// zero (hardware range check) and needs no branch.
+struct ScanRsrc {
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs, kn, kr, vn, vr;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, size_t unit_off,
+                                                           uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)((const uint8_t *)base + unit_off), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+template <int KB, bool KQ, int VB, bool VQ>
+__device__ __forceinline__ void scan_load(ScanBlock<KB, KQ, VB, VQ> &R, const ScanRsrc &rs, int slot0,
+                                          int tb, int n, int g) {
+  using SS = ScanShape<KB, KQ, VB, VQ>;
+  const uint32_t tk = (uint32_t)(slot0 + tb + n);       // slot of this lane's scored token
+  const uint32_t ko = tk * SS::KREC;
+  if constexpr (KB == 4) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs.kc, ko + 16 * g, 0, 0);
+    R.k[0] = w.x; R.k[1] = w.y; R.k[2] = w.z; R.k[3] = w.w;
+  } else if constexpr (KB == 3) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.kc, ko + 8 * g, 0, 0);
+    R.k[0] = w.x; R.k[1] = w.y;
+    R.k[2] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, ko + SS::D / 4 + 4 * g, 0, 0);
+  } else if constexpr (KB == 2) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.kc, ko + 8 * g, 0, 0);
+    R.k[0] = w.x; R.k[1] = w.y;
+  } else {
+    R.k[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, ko + 4 * g, 0, 0);
+  }
+  R.ks = KQ ? __builtin_amdgcn_raw_buffer_load_b32(rs.ks, tk * SS::SREC + 4 * g, 0, 0) : 0u;
+  R.nk = __builtin_amdgcn_raw_buffer_load_b16(rs.kn, 2 * tk, 0, 0);
+  R.rk = KQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.kr, 2 * tk, 0, 0) : 0u;
+  R.nv = __builtin_amdgcn_raw_buffer_load_b16(rs.vn, 2 * tk, 0, 0);
+  R.rv = VQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.vr, 2 * tk, 0, 0) : 0u;
+  const int lane = 16 * g + n;
+  const uint32_t t16 = (uint32_t)(slot0 + tb);
+  // lanes without a piece read at an offset past every descriptor's range (zero)
+  const uint32_t oor = 0xFFFFFFF0u;
+  R.vp = __builtin_amdgcn_raw_buffer_load_b128(rs.vc, lane < SS::VREC ? t16 * SS::VREC + 16 * lane : oor, 0, 0);
+  R.sp = u32x4{0u, 0u, 0u, 0u};
+  if constexpr (VQ) R.sp = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, lane < 16 ? t16 * SS::SREC + 16 * lane : oor, 0, 0);
+}
+
+// The value bytes of operand lane (n, g) for tokens 4 g + r from a staged tile:
+// v[r] = code bytes of coordinates 8 n .. 8 n + 7, vh[r] = the 1-bit plane byte
+// of width-3 codes; s[r] = value sign byte n (rows 8 n .. 8 n + 7).
+template <int VB, bool VQ>
+__device__ __forceinline__ void stage_bytes(const uint8_t *vt, const uint8_t *st, int n, int g,
+                                            uint32_t (&v)[4], uint32_t (&vh)[4], uint32_t (&sg)[4]) {
+  constexpr int D = 128, VREC = D * VB / 8;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint8_t *rec = vt + (4 * g + r) * VREC;
+    vh[r] = 0u;
+    if constexpr (VB == 4) {
+      v[r] = *(const uint32_t *)(rec + 4 * n);
+    } else if constexpr (VB == 3) {
+      v[r] = *(const uint16_t *)(rec + 2 * n);
+      vh[r] = rec[D / 4 + n];
+    } else if constexpr (VB == 2) {
+      v[r] = *(const uint16_t *)(rec + 2 * n);
+    } else {
+      v[r] = rec[n];
+    }
+    sg[r] = VQ ? st[(4 * g + r) * (D / 8) + n] : 0u;
+  }
+}
+
+// B operand of the score product for step j: key centroids of coordinates
+// 32 g + 4 j .. + 3 of token n in the slot order (Ch c0, Ch c1, Cl c0, Cl c1,
+// Ch c2, Ch c3, Cl c2, Cl c3).
+template <int KB>
+__device__ __forceinline__ f16x8 key_operand(const uint32_t *k, int j, const uint8_t *tab) {
+  if constexpr (KB == 4) {
+    const uint32_t w = k[j >> 1] >> (16 * (j & 1));
+    const u32x2 t0 = *(const u32x2 *)(tab + 8 * (w & 255u));
+    const u32x2 t1 = *(const u32x2 *)(tab + 8 * ((w >> 8) & 255u));
+    return op8(t0.x, t0.y, t1.x, t1.y);
+  } else if constexpr (KB == 3) {
+    const uint32_t by = (k[j >> 2] >> (8 * (j & 3))) & 255u;
+    const uint32_t hb = (k[2] >> (4 * j)) & 15u;
+    const uint32_t i0 = (by & 15u) | ((hb & 3u) << 4);
+    const uint32_t i1 = (by >> 4) | ((hb >> 2) << 4);
+    const u32x2 t0 = *(const u32x2 *)(tab + 8 * i0);
+    const u32x2 t1 = *(const u32x2 *)(tab + 8 * i1);
+    return op8(t0.x, t0.y, t1.x, t1.y);
+  } else if constexpr (KB == 2) {
+    const uint32_t by = (k[j >> 2] >> (8 * (j & 3))) & 255u;
+    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * by));
+  } else {
+    const uint32_t nb = (k[0] >> (4 * j)) & 15u;
+    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * nb));
+  }
+}
+
+// Token-pair table indices of the value codes: for coordinate 8 n + j, idx01[j]
+// covers tokens 4 g, 4 g + 1 and idx23[j] tokens 4 g + 2, 4 g + 3 (index
+// convention of pair_codes: first token's code in the low field).
+template <int VB>
+__device__ __forceinline__ void value_indices(const uint32_t *v, const uint32_t *vh, uint32_t (&i01)[8],
+                                              uint32_t (&i23)[8]) {
+  if constexpr (VB == 4) {
+    // bytes (t0 nib, t1 nib) per coordinate: interleave nibbles of two tokens
+    const uint32_t a0 = dswap(__builtin_amdgcn_perm(v[1], v[0], 0x05010400u), 4, 0x00F000F0u);
+    const uint32_t a1 = dswap(__builtin_amdgcn_perm(v[1], v[0], 0x07030602u), 4, 0x00F000F0u);
+    const uint32_t b0 = dswap(__builtin_amdgcn_perm(v[3], v[2], 0x05010400u), 4, 0x00F000F0u);
+    const uint32_t b1 = dswap(__builtin_amdgcn_perm(v[3], v[2], 0x07030602u), 4, 0x00F000F0u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      i01[j] = ((j < 4 ? a0 : a1) >> (8 * (j & 3))) & 255u;
+      i23[j] = ((j < 4 ? b0 : b1) >> (8 * (j & 3))) & 255u;
+    }
+  } else if constexpr (VB == 3 || VB == 2) {
+    // nibble j = (t0 low pair, t1 low pair): interleave 2-bit units of two tokens
+    uint32_t w01 = __builtin_amdgcn_perm(v[1], v[0], 0x05010400u);
+    w01 = dswap(dswap(w01, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu);
+    uint32_t w23 = __builtin_amdgcn_perm(v[3], v[2], 0x05010400u);
+    w23 = dswap(dswap(w23, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu);
+    uint32_t h = 0u;
+    if constexpr (VB == 3) {
+      // 2-bit unit j of each half = (t0 high bit, t1 high bit) of coordinate j
+      h = vh[0] | (vh[1] << 8) | (vh[2] << 16) | (vh[3] << 24);
+      h = dswap(dswap(dswap(h, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu), 1, 0x22222222u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      i01[j] = (w01 >> (4 * j)) & 15u;
+      i23[j] = (w23 >> (4 * j)) & 15u;
+      if constexpr (VB == 3) {
+        i01[j] |= ((h >> (2 * j)) & 3u) << 4;
+        i23[j] |= ((h >> (16 + 2 * j)) & 3u) << 4;
+      }
+    }
+  } else {
+    // 1-bit codes: 2-bit unit j = (t0 bit, t1 bit)
+    uint32_t h = v[0] | (v[1] << 8) | (v[2] << 16) | (v[3] << 24);
+    h = dswap(dswap(dswap(h, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu), 1, 0x22222222u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      i01[j] = (h >> (2 * j)) & 3u;
+      i23[j] = (h >> (16 + 2 * j)) & 3u;
+    }
+  }
+}
+
+template <int KB, bool KQ, int VB, bool VQ>
+__global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
+  using SS = ScanShape<KB, KQ, VB, VQ>;
+  using SB = ScanBlock<KB, KQ, VB, VQ>;
+  constexpr int D = SS::D, NS = SS::NS;
+  constexpr int KTB = SS::KENT * (SS::KPAIR ? 8 : 16);
+  __shared__ __attribute__((aligned(16))) uint8_t kt_s[KTB];
+  __shared__ __attribute__((aligned(16))) u32x2 vt_s[SS::VENT];
+  __shared__ __attribute__((aligned(16))) u32x4 sp_s[SS::SPIN ? 256 : 1];
+  // per wave: X = (ch, cl) and Z = (cqh, cql) of [block parity][head][token]
+  __shared__ __attribute__((aligned(16))) uint32_t wx_s[4][2][4][16];
+  __shared__ __attribute__((aligned(16))) uint32_t wz_s[4][2][4][16];
+  __shared__ __attribute__((aligned(16))) float ep_s[4][4][NS];
+  // per wave: the value and sign tiles of the two blocks of a pair, one
+  // 16-byte slot per lane (slots past the records hold the zero pieces)
+  constexpr int VT = 1024, STB = VQ ? 1024 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t tile_s[4][2][VT + STB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: a scalar loop below
+  const int n = lane & 15, g = lane >> 4;
+  const int GT = a.Gtot < 4 ? a.Gtot : 4;
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y / a.HG, hgrp = blockIdx.y - (blockIdx.y / a.HG) * a.HG;
+  const int b = blockIdx.z;
+  const int hq0 = hkv * a.Gtot + hgrp * GT;
+  const size_t unit = (size_t)b * a.Hkv + hkv;
+  const size_t unitg = unit * a.HG + hgrp;
+  // per-unit buffer descriptors over slots [0, t0 + n_ctx)
+  const uint32_t nslot = (uint32_t)(a.t0 + a.n_ctx);
+  const size_t us = unit * (size_t)a.cap;
+  ScanRsrc rs;
+  rs.kc = unit_rsrc(a.kc, us * SS::KREC, nslot * SS::KREC);
+  rs.vc = unit_rsrc(a.vc, us * SS::VREC, nslot * SS::VREC);
+  rs.kn = unit_rsrc(a.kn, us * 2, nslot * 2);
+  rs.vn = unit_rsrc(a.vn, us * 2, nslot * 2);
+  rs.ks = rs.kr = rs.vs = rs.vr = rs.kc;
+  if constexpr (KQ) {
+    rs.ks = unit_rsrc(a.ks, us * SS::SREC, nslot * SS::SREC);
+    rs.kr = unit_rsrc(a.kr, us * 2, nslot * 2);
+  }
+  if constexpr (VQ) {
+    rs.vs = unit_rsrc(a.vs, us * SS::SREC, nslot * SS::SREC);
+    rs.vr = unit_rsrc(a.vr, us * 2, nslot * 2);
+  }
+
+  // ---- tables (shared by the block) ----------------------------------------
+  for (int p = tid; p < SS::KENT; p += 256) {
+    if constexpr (SS::KPAIR) {
+      int ca, cb;
+      pair_codes<KB>(p, ca, cb);
+      _Float16 ha, la, hb, lb;
+      split1(a.kcent[ca], ha, la);
+      split1(a.kcent[cb], hb, lb);
+      const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+      const uint32_t lw = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+      *(u32x2 *)(kt_s + 8 * p) = u32x2{hw, lw};
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c0 = (p >> (KB * 2 * q)) & ((1 << KB) - 1);
+        const int c1 = (p >> (KB * (2 * q + 1))) & ((1 << KB) - 1);
+        _Float16 h0, l0, h1, l1;
+        split1(a.kcent[c0], h0, l0);
+        split1(a.kcent[c1], h1, l1);
+        w[2 * q] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        w[2 * q + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      *(u32x4 *)(kt_s + 16 * p) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+  for (int p = tid; p < SS::VENT; p += 256) {
+    int ca, cb;
+    pair_codes<VB>(p, ca, cb);
+    _Float16 ha, la, hb, lb;
+    split1(a.vcent[ca], ha, la);
+    split1(a.vcent[cb], hb, lb);
+    vt_s[p] = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, la) << 16),
+                    (uint32_t)__builtin_bit_cast(uint16_t, hb) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16)};
+  }
+  if constexpr (SS::SPIN) {
+    // byte x -> 8 fp16 spins, element e = +1 when bit e is set, else -1
+    for (int p = tid; p < 256; p += 256) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = (((p >> (2 * q)) & 1) ? 0x3C00u : 0xBC00u) | ((((p >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+      sp_s[p] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+
+  // ---- prepared query as the A operand of the score product -------------------
+  // lane (row = 4 h + kind, g); step j slot e <-> coordinate 32 g + 4 j +
+  // 2 (e / 4) + (e % 2), part (e / 2) % 2 (0: centroid hi slot, 1: lo slot).
+  const int qrow = n, qh_ = qrow >> 2, qkind = qrow & 3;
+  f16x8 qa[8];
+  float unsc_q;
+  {
+    const float *qv = a.qt + unitg * D * GT;
+    float v[32];
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      v[c] = qh_ < GT ? qv[(32 * g + c) * GT + qh_] : 0.0f;
+      m = fmaxf(m, fabsf(v[c]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    int ex = 0;
+    const bool fin = m > 0.0f && m <= 3.0e38f;
+    if (fin) (void)frexpf(m, &ex);
+    const int k = fin ? 14 - ex : 0;
+    unsc_q = ldexpf(1.0f, -k);
+    const _Float16 z = (_Float16)0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 4 * j + 2 * (e >> 2) + (e & 1);
+        const bool lo_slot = (e & 2) != 0;
+        _Float16 hi, lo;
+        split1(ldexpf(v[c], k), hi, lo);
+        o[e] = qkind == 0 ? (lo_slot ? z : hi) : (qkind == 1 ? (lo_slot ? hi : lo) : z);
+      }
+      qa[j] = o;
+    }
+  }
+  // K sketch (QKQV): rows 4 h + 2 / 4 h + 3 carry S q' hi / lo, slot e of step
+  // j <-> sketch row 32 g + 8 j + e
+  f16x8 qs[KQ ? 4 : 1];
+  float unsc_s = 0.0f;
+  if constexpr (KQ) {
+    const float *sv = a.sqt + unitg * D * GT;
+    float v[32];
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      v[c] = qh_ < GT ? sv[(32 * g + c) * GT + qh_] : 0.0f;
+      m = fmaxf(m, fabsf(v[c]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    int ex = 0;
+    const bool fin = m > 0.0f && m <= 3.0e38f;
+    if (fin) (void)frexpf(m, &ex);
+    const int k = fin ? 14 - ex : 0;
+    unsc_s = ldexpf(1.0f, -k);
+    const _Float16 z = (_Float16)0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        _Float16 hi, lo;
+        split1(ldexpf(v[8 * j + e], k), hi, lo);
+        o[e] = qkind == 2 ? hi : (qkind == 3 ? lo : z);
+      }
+      qs[j] = o;
+    }
+  }
+  // scale factors of the softmax lane's head g (row 4 g of the operand lanes)
+  const float unscale = __shfl(unsc_q, 4 * g, 64);
+  const float unscale_s = KQ ? __shfl(unsc_s, 4 * g, 64) : 0.0f;
+  const bool head_ok = g < GT;
+
+  // weight-operand lane role: column 4 hc + kind
+  const int hc = n >> 2, wkind = n & 3;
+  const uint32_t selV = wkind == 0 ? 0x0C0C0100u : (wkind == 1 ? 0x01000302u : 0x0C0C0C0Cu);
+  const uint32_t selS = wkind == 2 ? 0x05040100u : (wkind == 3 ? 0x07060302u : 0x0C0C0C0Cu);
+
+  // ---- this wave's token range ------------------------------------------------
+  const int t_split = split * a.tps;
+  const int q4 = a.tps >> 2;
+  const int t_lo = min(a.n_ctx, t_split + wave * q4);
+  const int t_hi = min(a.n_ctx, t_split + (wave + 1) * q4);
+  const int nblk = (t_hi - t_lo + 15) >> 4;
+  const int npair = (nblk + 1) >> 1;
+
+  f32x4v acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  float M = -3.0e38f, L = 0.0f;
+  __syncthreads();   // tables
+
+  uint32_t(*wx)[4][16] = wx_s[wave];
+  uint32_t(*wz)[4][16] = wz_s[wave];
+  const uint8_t *vtab = (const uint8_t *)vt_s;
+
+  // base-2 logit of (token n, head g) of one block, -inf past the range
+  auto score = [&](const SB &R, int tb) {
+    // two independent accumulation chains (a chain waits for each result)
+    f32x4v sc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], key_operand<KB>(R.k, j, kt_s), sc0, 0, 0, 0);
+      sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j + 1], key_operand<KB>(R.k, j + 1, kt_s), sc1, 0, 0, 0);
+    }
+    if constexpr (KQ) {
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const f16x8 sg0 = __builtin_bit_cast(f16x8, sp_s[(R.ks >> (8 * j)) & 255u]);
+        const f16x8 sg1 = __builtin_bit_cast(f16x8, sp_s[(R.ks >> (8 * j + 8)) & 255u]);
+        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qs[j], sg0, sc0, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qs[j + 1], sg1, sc1, 0, 0, 0);
+      }
+    }
+    const f32x4v sc = sc0 + sc1;
+    float s = fmaf(sc[1], 1.0f / 2048.0f, sc[0]) * unscale;
+    if constexpr (KQ) {
+      const float sk = fmaf(sc[3], 1.0f / 2048.0f, sc[2]) * unscale_s;
+      s = fmaf(a.kcoef * f16_bits_to_f32((uint16_t)R.rk), sk, s);
+    }
+    s *= f16_bits_to_f32((uint16_t)R.nk);
+    return (head_ok && tb + n < t_hi) ? s : -INFINITY;
+  };
+  // weights of one block into the exchange buffers of parity par
+  auto weights = [&](const SB &R, float s, int par) {
+    const float w = fast_exp2(s - M);
+    L += w;
+    // masked tokens contribute exactly nothing (their stored norm may be +Inf)
+    const float c = s == -INFINITY ? 0.0f : w * f16_bits_to_f32((uint16_t)R.nv);
+    const float cq = VQ ? c * f16_bits_to_f32((uint16_t)R.rv) : 0.0f;
+    uint32_t hi, lo;
+    split2(c, cq, hi, lo);
+    wx[par][g][n] = __builtin_amdgcn_perm(lo, hi, 0x05040100u);   // (ch, cl)
+    if constexpr (VQ) wz[par][g][n] = __builtin_amdgcn_perm(lo, hi, 0x07060302u);   // (cqh, cql)
+  };
+  // value product of one block: B = weights of head hc for tokens 4 g .. 4 g + 3
+  auto values = [&](const uint32_t (&v)[4], const uint32_t (&vh)[4], int par) {
+    const u32x4 X = *(const u32x4 *)&wx[par][hc][4 * g];
+    const f16x8 bv = op8(__builtin_amdgcn_perm(X.x, X.x, selV), __builtin_amdgcn_perm(X.y, X.y, selV),
+                         __builtin_amdgcn_perm(X.z, X.z, selV), __builtin_amdgcn_perm(X.w, X.w, selV));
+    uint32_t i01[8], i23[8];
+    value_indices<VB>(v, vh, i01, i23);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x2 t0 = *(const u32x2 *)(vtab + 8 * i01[j]);
+      const u32x2 t1 = *(const u32x2 *)(vtab + 8 * i23[j]);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(op8(t0.x, t0.y, t1.x, t1.y), bv, acc[j], 0, 0, 0);
+    }
+  };
+  // sketch product of a block pair: slots 0..3 <- tokens 4 g + e of the first
+  // block, 4..7 <- tokens 4 g + e - 4 of the second
+  auto sketch = [&](const uint32_t (&sa)[4], const uint32_t (&sb)[4]) {
+    const u32x4 ZA = *(const u32x4 *)&wz[0][hc][4 * g];
+    const u32x4 ZB = *(const u32x4 *)&wz[1][hc][4 * g];
+    const f16x8 bz = op8(__builtin_amdgcn_perm(ZA.y, ZA.x, selS), __builtin_amdgcn_perm(ZA.w, ZA.z, selS),
+                         __builtin_amdgcn_perm(ZB.y, ZB.x, selS), __builtin_amdgcn_perm(ZB.w, ZB.z, selS));
+    // 8 x 8 bit transpose: byte e = token e's sign byte (bit j = row 8 n + j)
+    // -> byte j = row 8 n + j (bit e = token e)
+    uint32_t lo8 = sa[0] | (sa[1] << 8) | (sa[2] << 16) | (sa[3] << 24);
+    uint32_t hi8 = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+    lo8 = dswap(dswap(lo8, 7, 0x00AA00AAu), 14, 0x0000CCCCu);
+    hi8 = dswap(dswap(hi8, 7, 0x00AA00AAu), 14, 0x0000CCCCu);
+    const uint32_t t = (lo8 ^ (hi8 << 4)) & 0xF0F0F0F0u;
+    lo8 ^= t;
+    hi8 ^= t >> 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t x = ((j < 4 ? lo8 : hi8) >> (8 * (j & 3))) & 255u;
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sp_s[x]), bz, acc[j], 0, 0, 0);
+    }
+  };
+  // a pair of token blocks: scores of both, one running-max update, then the
+  // weighted value and sketch products with the same reference max
+  auto process_pair = [&](const SB &RA, const SB &RB, int tb) {
+    // stage the pair's value and sign tiles
+    uint8_t *stA = tile_s[wave][0], *stB = tile_s[wave][1];
+    *(u32x4 *)(stA + 16 * lane) = RA.vp;
+    *(u32x4 *)(stB + 16 * lane) = RB.vp;
+    if constexpr (VQ) {
+      *(u32x4 *)(stA + VT + 16 * lane) = RA.sp;
+      *(u32x4 *)(stB + VT + 16 * lane) = RB.sp;
+    }
+    const float sA = score(RA, tb);
+    const float sB = score(RB, tb + 16);
+    const float bm = row_max16(fmaxf(sA, sB));
+    if (__ballot(bm > M)) {
+      const float Mn = fmaxf(M, bm);
+      const float al = fast_exp2(M - Mn);
+      L *= al;
+      M = Mn;
+      const float alc = __shfl(al, 16 * hc, 64);   // alpha of the accumulator lane's head
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= alc;
+    }
+    weights(RA, sA, 0);
+    weights(RB, sB, 1);
+    wave_sync();
+    uint32_t vA[4], vhA[4], sgA[4], vB[4], vhB[4], sgB[4];
+    stage_bytes<VB, VQ>(stA, stA + VT, n, g, vA, vhA, sgA);
+    stage_bytes<VB, VQ>(stB, stB + VT, n, g, vB, vhB, sgB);
+    values(vA, vhA, 0);
+    values(vB, vhB, 1);
+    if constexpr (VQ) sketch(sgA, sgB);
+    wave_sync();   // the exchange and stage buffers are rewritten by the next pair
+  };
+
+  // ---- main loop: a pair of blocks per step, two pairs in flight ------------
+  SB R0, R1, R2, R3;
+  const int s0 = a.t0;
+  // issued in block order (the loop head's wait counts assume it)
+  __builtin_amdgcn_sched_barrier(0);
+  scan_load(R0, rs, s0, t_lo, n, g);
+  scan_load(R1, rs, s0, t_lo + 16, n, g);
+  __builtin_amdgcn_sched_barrier(0);
+  scan_load(R2, rs, s0, t_lo + 32, n, g);
+  scan_load(R3, rs, s0, t_lo + 48, n, g);
+  __builtin_amdgcn_sched_barrier(0);
+  // (the scheduling barriers keep each refill between the two pair steps, so
+  // a pair's data is requested a full pair step before it is used)
+  for (int ip = 0; ip < npair; ip += 2) {
+    const int tb = t_lo + 32 * ip;
+    process_pair(R0, R1, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    scan_load(R0, rs, s0, tb + 64, n, g);
+    scan_load(R1, rs, s0, tb + 80, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+    process_pair(R2, R3, tb + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    scan_load(R2, rs, s0, tb + 96, n, g);
+    scan_load(R3, rs, s0, tb + 112, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- epilogue: per-wave partials through LDS, then the block's partial ----
+  {
+    float l = L;
+    l += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(l), 0xB1, 0xF, 0xF, false));
+    l += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(l), 0x4E, 0xF, 0xF, false));
+    l += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(l), 0x141, 0xF, 0xF, false));
+    l += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(l), 0x140, 0xF, 0xF, false));
+    if (n == 0) {
+      ep_s[wave][g][0] = M;
+      ep_s[wave][g][1] = l;
+    }
+  }
+  // lanes of kind 0 (values) and 2 (sketch) combine hi + lo / 2048 of their pair
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = fmaf(quad_next(acc[j][r]), 1.0f / 2048.0f, acc[j][r]);
+      const int coord = 32 * g + 8 * r + j;
+      if (wkind == 0) ep_s[wave][hc][2 + coord] = v;
+      else if (wkind == 2 && VQ) ep_s[wave][hc][2 + D + coord] = v;
+    }
+  __syncthreads();
+  for (int idx = tid; idx < 4 * NS; idx += 256) {
+    const int h = idx / NS, kk = idx - h * NS;
+    if (h >= GT) continue;
+    float mw[4], mx = -3.0e38f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = ep_s[w][h][0];
+      mx = fmaxf(mx, mw[w]);
+    }
+    float v;
+    if (kk == 0) {
+      v = mx > -3.0e38f ? mx : -INFINITY;
+    } else if (!VQ && kk >= 2 + D) {
+      v = 0.0f;
+    } else {
+      v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v = fmaf(fast_exp2(mw[w] - mx), ep_s[w][h][kk], v);
+    }
+    a.part[(((size_t)b * a.Hq + hq0 + h) * a.splits + split) * NS + kk] = v;
+  }
+}
+
+}  // namespace kvq

@@ -222,7 +222,7 @@ def test_single_token_context():
     assert np.allclose(got, vh, rtol=1e-5, atol=1e-6)   # o = v^_1
 
 
-@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_decode_full_capacity_ragged_tail(d, splits):
     """n_ctx equal to the capacity with value records that are not 16-byte

@@ -197,20 +197,20 @@ def test_validation_status_codes(K):
 
 
 def test_auto_splits_fill_the_gpu(K):
-    """About 4096 blocks, split lengths rounded up to whole 256-token rounds
-    (at least 256), and never more tokens per split than the LDS logit buffer
-    holds (1280 tokens at four heads per block, 2560 at two, 5120 at one)."""
+    """Head dimension 128 (matrix-core scan): about 2048 blocks, with no LDS cap
+    on the split length.  Smaller heads (vector-unit scan): about 4096 blocks,
+    never more tokens per split than the LDS logit buffer holds.  Split lengths
+    are whole 256-token rounds (at least 256)."""
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)
-    assert K.kvq_decode_auto_splits(c, 32, 32768) == 32       # 1024-token splits
+    assert K.kvq_decode_auto_splits(c, 32, 32768) == 16       # 2048-token splits
     c = _fake_cache(K, d=128, B=4, H=8, cap=131136)
-    assert K.kvq_decode_auto_splits(c, 32, 131136) == 103
+    assert K.kvq_decode_auto_splits(c, 32, 131136) == 57      # 2049 -> 2304-token splits
     c = _fake_cache(K, d=64, B=1, H=1, cap=256)
     assert K.kvq_decode_auto_splits(c, 1, 256) == 1
     c = _fake_cache(K, d=128, B=1, H=32, cap=4096)
-    assert K.kvq_decode_auto_splits(c, 32, 4096) == 16        # 32 units x 16 = 512 blocks
-    c = _fake_cache(K, d=128, B=1, H=1, cap=100000)
+    assert K.kvq_decode_auto_splits(c, 32, 4096) == 16        # 256-token floor
+    c = _fake_cache(K, d=64, B=1, H=1, cap=100000)
     assert K.kvq_decode_auto_splits(c, 1, 100000) == 391      # 256-token splits
-    assert K.kvq_decode_auto_splits(c, 2, 100000) == 391
 
 
 def test_explicit_splits_below_the_lds_budget_rejected(K):
