@@ -214,8 +214,10 @@ def test_auto_splits_fill_the_gpu(K):
 
 
 def test_explicit_splits_below_the_lds_budget_rejected(K):
+    """The vector-unit scan (head dimension below 128) keeps a split's logits
+    in LDS; the matrix-core scan (128) has no such cap."""
     lib = K.lib()
-    c = _fake_cache(K, d=128, B=1, H=2, cap=6000)
+    c = _fake_cache(K, d=64, B=1, H=2, cap=6000)
     ws = C.c_size_t()
     p = C.byref(c)
     assert lib.kvq_decode_workspace(p, 8, 5120, 4, C.byref(ws)) == 0      # 1280 per split
@@ -225,6 +227,9 @@ def test_explicit_splits_below_the_lds_budget_rejected(K):
     assert lib.kvq_decode_workspace(p, 4, 5120, 2, C.byref(ws)) == 0      # two heads: 2560
     assert lib.kvq_decode_workspace(p, 4, 5121, 2, C.byref(ws)) == 10
     assert lib.kvq_decode_workspace(p, 8, 4096, 8193, C.byref(ws)) == 10
+    c = _fake_cache(K, d=128, B=1, H=2, cap=6000)
+    p = C.byref(c)
+    assert lib.kvq_decode_workspace(p, 8, 6000, 1, C.byref(ws)) == 0
 
 
 def _cell_bits(bits):
