@@ -273,7 +273,7 @@ def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_
     ks, vs = ref.scheme_sides(scheme, n_bits)
     rot = ref.Rot(rotation, rot_param)
     ok = ref.OracleCache(nb, hk, w.N, w.d, ks, w.d, rot)
-    ov = ref.OracleCache(nb, hk, w.N, w.d, vs, w.d, rot)
+    ov = ref.OracleCache(nb, hk, w.N, w.d, vs, w.d, rot, values=True)
     t0 = time.perf_counter()
     ok.quantize(host(Ks), 0, S, cores)
     ov.quantize(host(Vs), 0, S, cores)

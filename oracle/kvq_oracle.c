@@ -15,6 +15,9 @@
  *                    for b=2, d/4 bytes) followed by a 1-bit plane (the high
  *                    bit of every code, laid out as for b=1, d/8 bytes).
  *   sign bits:       bit k of the sketch at byte k/8, shift k%8.
+ * These per-slot records are what orc_encode / orc_decode exchange.  A cache
+ * side stores them per slot, or (value side at d = 128) in token groups whose
+ * bit positions orc_vgroup_code_bit / orc_vgroup_sign_bit define.
  */
 #include "kvq_oracle.h"
 
@@ -227,6 +230,108 @@ static int get_code(const uint8_t *rec, int d, int bits, int i) {
   return (rec[(i * bits) / 8] >> ((i * bits) % 8)) & ((1 << bits) - 1);
 }
 
+/* Token-group storage of the value side at d = 128 (the library's format; the
+ * pages fix none).  R = 16 b bytes per slot.
+ * Codes: slots 4q .. 4q+3 share bytes [4q R, 4q R + 4R).  Piece n = c / 8
+ * (coordinates 8n .. 8n+7) starts at 4q R + 4 b n.  With r = slot % 4 and
+ * j = c % 8, bit i of the code of (slot, c) is at
+ *   b = 4: byte 2j + r/2 of the piece, bit 4 (r%2) + i
+ *   b = 3: P = the 6-bit pair field u = 2j + r/2, bit pb = 3 (r%2) + i of P;
+ *          u < 12: byte u, bit pb; u >= 12: byte 4 (pb/2) + u - 12, bit 6 + pb%2
+ *   b = 2: byte j, bit 2r + i
+ *   b = 1: byte j/2, bit 4 (j%2) + r
+ * Sign bits: slots 8o .. 8o+7 share bytes [128 o, 128 o + 128); the sign of
+ * (slot, sketch row k) is bit slot % 8 of byte 128 o + k. */
+void orc_vgroup_code_bit(int bits, size_t slot, int c, int i, size_t *byte, int *bit) {
+  const size_t rec = (size_t)16 * bits;
+  const size_t piece = (slot / 4) * 4 * rec + (size_t)(c / 8) * (size_t)(4 * bits);
+  const int r = (int)(slot % 4), j = c % 8;
+  if (bits == 4) {
+    *byte = piece + (size_t)(2 * j + r / 2);
+    *bit = 4 * (r % 2) + i;
+  } else if (bits == 3) {
+    const int u = 2 * j + r / 2, pb = 3 * (r % 2) + i;
+    if (u < 12) {
+      *byte = piece + (size_t)u;
+      *bit = pb;
+    } else {
+      *byte = piece + (size_t)(4 * (pb / 2) + u - 12);
+      *bit = 6 + pb % 2;
+    }
+  } else if (bits == 2) {
+    *byte = piece + (size_t)j;
+    *bit = 2 * r + i;
+  } else {
+    *byte = piece + (size_t)(j / 2);
+    *bit = 4 * (j % 2) + r;
+  }
+}
+
+void orc_vgroup_sign_bit(size_t slot, int k, size_t *byte, int *bit) {
+  *byte = (slot / 8) * 128 + (size_t)k;
+  *bit = (int)(slot % 8);
+}
+
+static void set_bit(uint8_t *p, size_t byte, int bit, int v) {
+  p[byte] = (uint8_t)((p[byte] & ~(1u << bit)) | ((unsigned)(v & 1) << bit));
+}
+
+void orc_load_record(const uint8_t *codes, const uint8_t *signs, int grouped, size_t slot,
+                     int d, int bits, int qjl, int m, uint8_t *rec, uint8_t *sg) {
+  const size_t cb = (size_t)d * bits / 8, sbytes = (size_t)m / 8;
+  if (!grouped) {
+    memcpy(rec, codes + slot * cb, cb);
+    if (qjl) memcpy(sg, signs + slot * sbytes, sbytes);
+    return;
+  }
+  memset(rec, 0, cb);
+  for (int c = 0; c < d; ++c) {
+    int code = 0;
+    for (int i = 0; i < bits; ++i) {
+      size_t by;
+      int bt;
+      orc_vgroup_code_bit(bits, slot, c, i, &by, &bt);
+      code |= ((codes[by] >> bt) & 1) << i;
+    }
+    put_code(rec, d, bits, c, code);
+  }
+  if (!qjl) return;
+  memset(sg, 0, sbytes);
+  for (int k = 0; k < m; ++k) {
+    size_t by;
+    int bt;
+    orc_vgroup_sign_bit(slot, k, &by, &bt);
+    sg[k / 8] |= (uint8_t)(((signs[by] >> bt) & 1) << (k % 8));
+  }
+}
+
+/* Store one slot's record (per-slot layout in rec / sg) into either storage. */
+static void store_record(uint8_t *codes, uint8_t *signs, int grouped, size_t slot, int d,
+                         int bits, int qjl, int m, const uint8_t *rec, const uint8_t *sg) {
+  const size_t cb = (size_t)d * bits / 8, sbytes = (size_t)m / 8;
+  if (!grouped) {
+    memcpy(codes + slot * cb, rec, cb);
+    if (qjl) memcpy(signs + slot * sbytes, sg, sbytes);
+    return;
+  }
+  for (int c = 0; c < d; ++c) {
+    const int code = get_code(rec, d, bits, c);
+    for (int i = 0; i < bits; ++i) {
+      size_t by;
+      int bt;
+      orc_vgroup_code_bit(bits, slot, c, i, &by, &bt);
+      set_bit(codes, by, bt, code >> i);
+    }
+  }
+  if (!qjl) return;
+  for (int k = 0; k < m; ++k) {
+    size_t by;
+    int bt;
+    orc_vgroup_sign_bit(slot, k, &by, &bt);
+    set_bit(signs, by, bt, sg[k / 8] >> (k % 8));
+  }
+}
+
 /* Forward rotation y = R x in fp32 (kinds: see the header).  WHT and
  * randomized Hadamard: sign flips (exact) then the butterflies above.  Dense:
  * y_i = fma chain over j ascending from 0 ([KPP] "Rotation invariance
@@ -381,23 +486,23 @@ static void run_units(void (*fn)(void *, int), void *ctx, int n, int nthreads) {
 typedef struct {
   const void *src; int dtype, H, T, d; long long sb, sh, st; int t0, cap;
   int rotate; const void *rparam; int bits; const float *C, *Th; int qjl; const uint16_t *S; int m;
-  uint8_t *codes, *signs; uint16_t *norm, *rnorm;
+  uint8_t *codes, *signs; uint16_t *norm, *rnorm; int grouped;
 } qctx_t;
 
 static void quantize_unit(void *vc, int unit) {
   qctx_t *c = (qctx_t *)vc;
   int b = unit / c->H, h = unit % c->H;
-  size_t cb = (size_t)c->d * c->bits / 8, sbytes = (size_t)c->m / 8;
   float x[4096];
+  uint8_t rec[2048], sg[512];
   for (int t = 0; t < c->T; ++t) {
     long long off = b * c->sb + h * c->sh + t * c->st;
     for (int i = 0; i < c->d; ++i)
       x[i] = c->dtype == 0 ? ((const float *)c->src)[off + i]
                            : orc_bf16_to_f32(((const uint16_t *)c->src)[off + i]);
     size_t slot = ((size_t)unit * c->cap) + (size_t)(c->t0 + t);
-    orc_encode(x, c->d, c->rotate, c->rparam, c->bits, c->C, c->Th, c->qjl, c->S, c->m,
-               c->codes + slot * cb, c->qjl ? c->signs + slot * sbytes : NULL,
-               c->norm + slot, c->qjl ? c->rnorm + slot : NULL);
+    orc_encode(x, c->d, c->rotate, c->rparam, c->bits, c->C, c->Th, c->qjl, c->S, c->m, rec,
+               c->qjl ? sg : NULL, c->norm + slot, c->qjl ? c->rnorm + slot : NULL);
+    store_record(c->codes, c->signs, c->grouped, slot, c->d, c->bits, c->qjl, c->m, rec, sg);
   }
 }
 
@@ -406,27 +511,27 @@ void orc_quantize_cache(const void *src, int dtype, int B, int H, int T, int d,
                         int rotate, const void *rparam, int bits, const float *centroid,
                         const float *threshold, int qjl, const uint16_t *S, int m,
                         uint8_t *codes, uint8_t *signs, uint16_t *norm, uint16_t *rnorm,
-                        int nthreads) {
+                        int grouped, int nthreads) {
   qctx_t c = {src, dtype, H, T, d, sb, sh, st, t0, cap, rotate, rparam, bits, centroid, threshold,
-              qjl, S, m, codes, signs, norm, rnorm};
+              qjl, S, m, codes, signs, norm, rnorm, grouped};
   run_units(quantize_unit, &c, B * H, nthreads);
 }
 
 typedef struct {
   const uint8_t *codes, *signs; const uint16_t *norm, *rnorm;
   int H, cap, t0, T, d, rotate; const void *rparam; int bits; const float *C; int qjl;
-  const uint16_t *S; int m;
+  const uint16_t *S; int m; int grouped;
   double *out;
 } dctx_t;
 
 static void dequantize_unit(void *vc, int unit) {
   dctx_t *c = (dctx_t *)vc;
-  size_t cb = (size_t)c->d * c->bits / 8, sbytes = (size_t)c->m / 8;
+  uint8_t rec[2048], sg[512];
   for (int t = 0; t < c->T; ++t) {
     size_t slot = (size_t)unit * c->cap + (size_t)(c->t0 + t);
-    orc_decode(c->codes + slot * cb, c->qjl ? c->signs + slot * sbytes : NULL, c->norm[slot],
-               c->qjl ? c->rnorm[slot] : 0, c->d, c->rotate, c->rparam, c->bits, c->C, c->qjl,
-               c->S, c->m,
+    orc_load_record(c->codes, c->signs, c->grouped, slot, c->d, c->bits, c->qjl, c->m, rec, sg);
+    orc_decode(rec, c->qjl ? sg : NULL, c->norm[slot], c->qjl ? c->rnorm[slot] : 0, c->d,
+               c->rotate, c->rparam, c->bits, c->C, c->qjl, c->S, c->m,
                c->out + ((size_t)unit * c->T + t) * c->d);
   }
 }
@@ -435,9 +540,10 @@ void orc_dequantize_cache(const uint8_t *codes, const uint8_t *signs,
                           const uint16_t *norm, const uint16_t *rnorm,
                           int B, int H, int cap, int t0, int T, int d,
                           int rotate, const void *rparam, int bits, const float *centroid,
-                          int qjl, const uint16_t *S, int m, double *out, int nthreads) {
+                          int qjl, const uint16_t *S, int m, int grouped, double *out,
+                          int nthreads) {
   dctx_t c = {codes, signs, norm, rnorm, H, cap, t0, T, d, rotate, rparam, bits, centroid, qjl,
-              S, m, out};
+              S, m, grouped, out};
   run_units(dequantize_unit, &c, B * H, nthreads);
 }
 
@@ -456,10 +562,10 @@ typedef struct {
 
 static void side_decode(const orc_side *sd, size_t slot, int d, const uint16_t *S, int m,
                         double *x) {
-  size_t cb = (size_t)d * sd->bits / 8, sbytes = (size_t)m / 8;
-  orc_decode(sd->codes + slot * cb, sd->qjl ? sd->signs + slot * sbytes : NULL, sd->norm[slot],
-             sd->qjl ? sd->rnorm[slot] : 0, d, sd->rotate, sd->rparam, sd->bits, sd->centroid,
-             sd->qjl, S, m, x);
+  uint8_t rec[2048], sg[512];
+  orc_load_record(sd->codes, sd->signs, sd->grouped, slot, d, sd->bits, sd->qjl, m, rec, sg);
+  orc_decode(rec, sd->qjl ? sg : NULL, sd->norm[slot], sd->qjl ? sd->rnorm[slot] : 0, d,
+             sd->rotate, sd->rparam, sd->bits, sd->centroid, sd->qjl, S, m, x);
 }
 
 /* Plain attention over explicit fp64 keys and values (n tokens, row-major):

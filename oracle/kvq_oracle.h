@@ -28,6 +28,7 @@
  */
 #ifndef KVQ_ORACLE_H
 #define KVQ_ORACLE_H
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -72,6 +73,18 @@ void orc_decode(const uint8_t *codes, const uint8_t *signs, uint16_t norm, uint1
                 int d, int rotate, const void *rparam, int bits, const float *centroid,
                 int qjl, const uint16_t *S, int m, double *xhat);
 
+/* Storage of a cache side's records.  grouped == 0: slot s holds its own
+ * record at bytes [s R, s R + R) (R = record bytes) and its sign record at
+ * [s m/8, (s+1) m/8).  grouped == 1 (value side at d = 128, cap a multiple of
+ * 16): the codes and sign bits of neighbouring slots share bytes; the bit
+ * positions are given by orc_vgroup_code_bit / orc_vgroup_sign_bit. */
+void orc_vgroup_code_bit(int bits, size_t slot, int c, int i, size_t *byte, int *bit);
+void orc_vgroup_sign_bit(size_t slot, int k, size_t *byte, int *bit);
+
+/* Record of one slot in the per-slot layout, from either storage. */
+void orc_load_record(const uint8_t *codes, const uint8_t *signs, int grouped, size_t slot,
+                     int d, int bits, int qjl, int m, uint8_t *rec, uint8_t *sg);
+
 /* Quantize-on-write of T tokens into a cache laid out [B][H][cap][record].
  * src: fp32 (dtype 0) or bf16 bit patterns (dtype 1), element (b,h,t,i) at
  * b*sb + h*sh + t*st + i (in elements).  Tokens go to cache slots t0..t0+T-1.
@@ -82,14 +95,15 @@ void orc_quantize_cache(const void *src, int dtype, int B, int H, int T, int d,
                         const float *threshold,
                         int qjl, const uint16_t *S, int m,
                         uint8_t *codes, uint8_t *signs, uint16_t *norm, uint16_t *rnorm,
-                        int nthreads);
+                        int grouped, int nthreads);
 
 /* Dequantize cache slots t0..t0+T-1 of every (b,h) into out [B][H][T][d] fp64. */
 void orc_dequantize_cache(const uint8_t *codes, const uint8_t *signs,
                           const uint16_t *norm, const uint16_t *rnorm,
                           int B, int H, int cap, int t0, int T, int d,
                           int rotate, const void *rparam, int bits, const float *centroid,
-                          int qjl, const uint16_t *S, int m, double *out, int nthreads);
+                          int qjl, const uint16_t *S, int m, int grouped, double *out,
+                          int nthreads);
 
 /* Plain attention over explicit fp64 keys K [n][d] and values V [n][d]. */
 void orc_attention_dense(const double *q, const double *K, const double *V, int n, int d,
@@ -102,6 +116,7 @@ typedef struct {
   int rotate, bits, qjl;
   const float *centroid;
   const void *rparam;
+  int grouped;
 } orc_side;
 
 /* Decode attention over the reconstructed cache, fp64, plain definition:

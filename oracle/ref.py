@@ -54,9 +54,13 @@ def lib():
         L.orc_decode.argtypes = [vp, vp, C.c_uint16, C.c_uint16, i32, i32, vp, i32, vp, i32, vp,
                                  i32, vp]
         L.orc_quantize_cache.argtypes = [vp, i32, i32, i32, i32, i32, i64, i64, i64, i32, i32,
-                                         i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32]
+                                         i32, vp, i32, vp, vp, i32, vp, i32, vp, vp, vp, vp, i32,
+                                         i32]
         L.orc_dequantize_cache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                           i32, vp, i32, vp, i32, vp, i32, vp, i32]
+                                           i32, vp, i32, vp, i32, vp, i32, i32, vp, i32]
+        L.orc_vgroup_code_bit.argtypes = [i32, C.c_size_t, i32, i32, vp, vp]
+        L.orc_vgroup_sign_bit.argtypes = [C.c_size_t, i32, vp, vp]
+        L.orc_load_record.argtypes = [vp, vp, i32, C.c_size_t, i32, i32, i32, i32, vp, vp]
         L.orc_attention_dense.argtypes = [vp, vp, vp, i32, i32, vp]
         L.orc_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, i32, i32,
                                     vp, vp, i32, i32]
@@ -196,10 +200,16 @@ def decode(codes, signs, norm, rnorm, d, side: Side, S=None, rot: Rot = WHT) -> 
 
 # ---------------------------------------------------------------- caches
 class OracleCache:
-    """Host arrays of one side (K or V) of a cache, laid out [B][H][cap][...]."""
+    """Host arrays of one side (K or V) of a cache, laid out [B][H][cap][...].
+    values=True marks the value side: at d = 128 its codes and sign bits are
+    stored in token groups (orc_vgroup_code_bit / orc_vgroup_sign_bit), which
+    needs cap to be a multiple of 16."""
 
-    def __init__(self, B, H, cap, d, side: Side, m: int, rot: Rot = WHT):
+    def __init__(self, B, H, cap, d, side: Side, m: int, rot: Rot = WHT, values: bool = False):
         self.B, self.H, self.cap, self.d, self.side, self.m = B, H, cap, d, side, m
+        self.grouped = 1 if (values and d == 128) else 0
+        if self.grouped and cap % 16:
+            raise ValueError("value side at d = 128 needs cap % 16 == 0")
         self.rot, self.rp = rot, rot.array()
         self.codes = np.zeros((B, H, cap, d * side.bits // 8), np.uint8)
         self.signs = np.zeros((B, H, cap, m // 8), np.uint8) if side.qjl else None
@@ -225,7 +235,7 @@ class OracleCache:
                                  _p(self.centroid),
                                  _p(self.threshold), self.side.qjl, _p(Sc), self.m,
                                  _p(self.codes), _p(self.signs), _p(self.norm), _p(self.rnorm),
-                                 nthreads)
+                                 self.grouped, nthreads)
 
     def dequantize(self, t0: int, T: int, S: np.ndarray | None, nthreads: int = 1) -> np.ndarray:
         out = np.zeros((self.B, self.H, T, self.d), np.float64)
@@ -234,7 +244,7 @@ class OracleCache:
                                    self.B, self.H, self.cap, t0, T, self.d,
                                    self.rot.code(self.side), _p(self.rp), self.side.bits,
                                    _p(self.centroid), self.side.qjl, _p(Sc),
-                                   self.m, _p(out), nthreads)
+                                   self.m, self.grouped, _p(out), nthreads)
         return out
 
     def view(self, b0: int, b1: int, h0: int = 0, h1: int | None = None) -> "OracleCache":
@@ -257,13 +267,14 @@ class OracleCache:
     def _side_struct(self):
         return _OrcSide(_p(self.codes), _p(self.signs), _p(self.norm), _p(self.rnorm),
                         self.rot.code(self.side), self.side.bits, self.side.qjl,
-                        _p(self.centroid), _p(self.rp))
+                        _p(self.centroid), _p(self.rp), self.grouped)
 
 
 class _OrcSide(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("signs", C.c_void_p), ("norm", C.c_void_p),
                 ("rnorm", C.c_void_p), ("rotate", C.c_int), ("bits", C.c_int),
-                ("qjl", C.c_int), ("centroid", C.c_void_p), ("rparam", C.c_void_p)]
+                ("qjl", C.c_int), ("centroid", C.c_void_p), ("rparam", C.c_void_p),
+                ("grouped", C.c_int)]
 
 
 def attention(kc: OracleCache, vc: OracleCache, q: np.ndarray, n_ctx: int,

@@ -38,7 +38,7 @@ class Pair:
         ks, vs = ref.scheme_sides(scheme, n)
         rot = ref.Rot(rotation, param)
         self.ok = ref.OracleCache(B, Hkv, cap, d, ks, d, rot)
-        self.ov = ref.OracleCache(B, Hkv, cap, d, vs, d, rot)
+        self.ov = ref.OracleCache(B, Hkv, cap, d, vs, d, rot, values=True)
 
     def write(self, K: torch.Tensor, V: torch.Tensor, t0: int, dev="cuda", nthreads=8):
         """K, V: [B][Hkv][T][d] tensors (any strides, innermost contiguous)."""

@@ -44,7 +44,7 @@ def _caches(scheme, n, d, B, Hkv, cap):
     gpu = KVQCache(scheme, n, d, B, Hkv, cap, S_bf16=None, device=DEV)
     ks, vs = ref.scheme_sides(scheme, n)
     ok = ref.OracleCache(B, Hkv, cap, d, ks, d)
-    ov = ref.OracleCache(B, Hkv, cap, d, vs, d)
+    ov = ref.OracleCache(B, Hkv, cap, d, vs, d, values=True)
     return gpu, ok, ov, sketch.sketch_bf16_bits(7, d, d)
 
 

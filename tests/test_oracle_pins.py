@@ -416,7 +416,7 @@ def test_attention_over_cache_matches_numpy(orc, scheme):
         .view(torch.int16).numpy().view(np.uint16)
     ks, vs = orc.scheme_sides(scheme, 3)
     kc = orc.OracleCache(B, Hkv, cap, d, ks, d)
-    vc = orc.OracleCache(B, Hkv, cap, d, vs, d)
+    vc = orc.OracleCache(B, Hkv, cap, d, vs, d, values=True)
     K = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
     V = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
     q = rng.standard_normal((B, Hq, d)).astype(np.float32)
@@ -441,7 +441,7 @@ def _window_case(scheme, seed, B=2, Hkv=2, Hq=4, d=8, cap=14):
         .view(torch.int16).numpy().view(np.uint16)
     ks, vs = ref.scheme_sides(scheme, 3)
     kc = ref.OracleCache(B, Hkv, cap, d, ks, d)
-    vc = ref.OracleCache(B, Hkv, cap, d, vs, d)
+    vc = ref.OracleCache(B, Hkv, cap, d, vs, d, values=True)
     K = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32) * 2
     V = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
     kc.quantize(K, 0, S)
