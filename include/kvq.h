@@ -116,7 +116,18 @@ kvq_status kvq_sketch_init(uint64_t seed, int m, int d, uint16_t *S_bf16_host);
  * k/8, bit k%8; bit = 1 means the sketch row is >= 0.  The stored norm is
  * ||x|| (||y|| for KVQ_ROT_QR); the residual norm is ||r|| of the rotated unit
  * direction.  Pointers not used by the scheme must be NULL.  All pointers 16-B
- * aligned.  The rotation fields are set by kvq_cache_set_rotation. */
+ * aligned.  The rotation fields are set by kvq_cache_set_rotation.
+ * At d = 128 the value side is stored in token groups instead (same buffer
+ * sizes; cap must be a multiple of 16): the codes of slots 4q .. 4q+3 share
+ * bytes [4q R, 4q R + 4R) (R = d*vb/8), piece n (coordinates 8n .. 8n+7) at
+ * byte 4 vb n, holding for coordinate 8n+j and slot 4q+r:
+ *   vb 4: byte 2j + r/2, bits 4 (r%2) .. +3
+ *   vb 3: the 6-bit field u = 2j + r/2 = code(4q + 2(r/2)) | code(+1) << 3;
+ *         u < 12: bits 0..5 of byte u; u >= 12: its bit pairs (0,1), (2,3),
+ *         (4,5) in bits 6, 7 of bytes u-12, u-8, u-4
+ *   vb 2: byte j, bits 2r .. 2r+1;   vb 1: byte j/2, bit 4 (j%2) + r
+ * and the sign bits of slots 8o .. 8o+7 share bytes [128 o, 128 o + 128):
+ * bit e of byte 128 o + k = sign of slot 8o + e at sketch row k. */
 typedef struct {
   int32_t scheme, n_bits, d, m, batch, kv_heads, capacity;
   int32_t k_bits, v_bits, k_qjl, v_qjl, rotate;  /* derived by kvq_cache_init */
@@ -132,7 +143,8 @@ typedef struct {
 /* Fill the scalar fields and codebooks of `c` for a scheme at n_bits per
  * coordinate (KV: n in 1..4; KQV, QKQV: n in 2..4); leaves the pointers
  * NULL and the rotation at KVQ_ROT_WHT.  Errors: KVQ_ERR_NULL,
- * KVQ_ERR_SCHEME, KVQ_ERR_BITS, KVQ_ERR_DIM, KVQ_ERR_RANGE. */
+ * KVQ_ERR_SCHEME, KVQ_ERR_BITS, KVQ_ERR_DIM, KVQ_ERR_RANGE (also: d = 128
+ * with a capacity that is not a multiple of 16). */
 kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch,
                           int kv_heads, int capacity);
 

@@ -226,6 +226,9 @@ int rot_code(const kvq_cache *c) { return c->rotate ? kvq::RK_WHT + c->rot_kind 
 bool hadamard_kind(int rk) { return rk == kvq::RK_WHT || rk == kvq::RK_RHT; }
 
 // Structural checks shared by every device entry point.
+// The value side at d = 128 is stored in token groups (kvq_vgroup.hpp).
+bool vgrouped(const kvq_cache *c) { return c->d == 128; }
+
 kvq_status check_cache(const kvq_cache *c) {
   if (!c) return KVQ_ERR_NULL;
   Sides s;
@@ -240,6 +243,8 @@ kvq_status check_cache(const kvq_cache *c) {
     return KVQ_ERR_BITS;
   if (!codebook_usable(c->cb_k) || !codebook_usable(c->cb_v)) return KVQ_ERR_BITS;
   if (c->batch < 1 || c->kv_heads < 1 || c->capacity < 1) return KVQ_ERR_RANGE;
+  // value groups (d = 128) must not straddle two units
+  if (vgrouped(c) && c->capacity % 16) return KVQ_ERR_RANGE;
   if ((long long)c->batch * c->kv_heads * c->capacity > (1ll << 40)) return KVQ_ERR_RANGE;
   if (!c->k_codes || !c->k_norm || !c->v_codes || !c->v_norm) return KVQ_ERR_NULL;
   if (s.kq && (!c->k_signs || !c->k_rnorm)) return KVQ_ERR_NULL;
@@ -289,7 +294,8 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
   a.B = c->batch; a.H = c->kv_heads; a.T = T; a.t0 = t0; a.cap = c->capacity;
   const int rk = rot_code(c);
   const int vt = (rk == kvq::RK_QR || c->d <= 64) ? 64 : 32;  // tokens per quantize tile
-  a.tiles_per_bh = (T + vt - 1) / vt;
+  // tiles are aligned to vt slots: the first starts at t0 - t0 % vt
+  a.tiles_per_bh = (t0 % vt + T + vt - 1) / vt;
   long long tiles = (long long)a.tiles_per_bh * a.B * a.H;
   if (tiles > (1ll << 31) - 1) return KVQ_ERR_RANGE;
   a.total_tiles = (int)tiles;
@@ -308,7 +314,8 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
   const int bits = side == 0 ? c->k_bits : c->v_bits;
   hipStream_t hs = (hipStream_t)stream;
   return hip_status(by_dim(c->d, [&](auto D) {
-    return kvq::launch_quantize<decltype(D)::value>(a, bits, rk, qjl, dtype == KVQ_BF16, hs);
+    return kvq::launch_quantize<decltype(D)::value>(a, bits, rk, qjl, dtype == KVQ_BF16,
+                                                    side == 1 && vgrouped(c), hs);
   }));
 }
 
@@ -466,6 +473,7 @@ kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch
   if (st != KVQ_OK) return st;
   if (!supported_dim(d)) return KVQ_ERR_DIM;
   if (batch < 1 || kv_heads < 1 || capacity < 1) return KVQ_ERR_RANGE;
+  if (d == 128 && capacity % 16) return KVQ_ERR_RANGE;   // value token groups
   std::memset(c, 0, sizeof(*c));
   c->scheme = scheme; c->n_bits = n_bits; c->d = d; c->m = d;
   c->batch = batch; c->kv_heads = kv_heads; c->capacity = capacity;
@@ -563,6 +571,7 @@ kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *o
   a.S = c->S;
   a.out = out;
   a.H = c->kv_heads; a.cap = c->capacity; a.t0 = t0; a.T = T;
+  a.vg = !k && vgrouped(c);
   const kvq_codebook &cb = k ? c->cb_k : c->cb_v;
   for (int i = 0; i < 16; ++i) a.cent[i] = cb.centroid[i];
   a.coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
@@ -618,8 +627,9 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
     return KVQ_ERR_RANGE;
   if (t_end > c->capacity) return KVQ_ERR_CAPACITY;
   if (t_end - t_begin + n_win < 1) return KVQ_ERR_RANGE;
-  // the matrix-core scan addresses a unit's records with 32-bit byte offsets
-  if (scan_mfma(c) && (uint64_t)t_end * 64u >= (1ull << 32)) return KVQ_ERR_RANGE;
+  // the matrix-core scan addresses a unit's records with 32-bit byte offsets,
+  // up to the end of the 16-slot block holding slot t_end - 1
+  if (scan_mfma(c) && ((uint64_t)t_end + 15) * 64u >= (1ull << 32)) return KVQ_ERR_RANGE;
   if (n_win > 0) {
     if (!wk || !wv) return KVQ_ERR_NULL;
     if (w_dtype != KVQ_F32 && w_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
@@ -687,7 +697,10 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   }
   a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.Hkv = c->kv_heads; a.Hq = q_heads; a.Gtot = G; a.HG = G / gt; a.cap = c->capacity;
-  a.n_ctx = n_ctx; a.splits = splits; a.tps = n_ctx > 0 ? split_tokens(n_ctx, splits) : 0;
+  a.n_ctx = n_ctx; a.splits = splits;
+  // the matrix-core scan splits the slots from t_begin rounded down to 16
+  const int lead = scan_mfma(c) ? (t_begin & 15) : 0;
+  a.tps = n_ctx > 0 ? split_tokens(n_ctx + lead, splits) : 0;
   e = by_dim(d, [&](auto D) {
     return kvq::launch_decode<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
                                                   c->v_qjl != 0, gt, c->batch, hs);

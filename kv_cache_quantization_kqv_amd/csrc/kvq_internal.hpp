@@ -57,6 +57,7 @@ struct DequantArgs {
   float oscale;              // 1/sqrt(d) for the Hadamard kinds, else 1
   uint32_t rsign[4];         // RK_RHT
   const float *Q;            // RK_QR
+  int vg;                    // token-group storage (value side at d = 128)
 };
 
 struct PrepArgs {
@@ -134,7 +135,7 @@ struct WindowArgs {
 
 // Dispatchers: one translation unit per head dimension.
 template <int D> hipError_t launch_quantize(const QuantArgs &a, int bits, int rk, bool qjl,
-                                            bool bf16, hipStream_t s);
+                                            bool bf16, bool vg, hipStream_t s);
 template <int D> hipError_t launch_dequantize(const DequantArgs &a, int bits, int rk, bool qjl,
                                               int n_vec, hipStream_t s);
 template <int D> hipError_t launch_prep(const PrepArgs &a, int rk, bool kqjl, bool bf16,

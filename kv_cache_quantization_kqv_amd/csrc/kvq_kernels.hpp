@@ -377,10 +377,19 @@ __device__ __forceinline__ float sketch_row_norm_max(const unsigned char *S_s, i
 // 16.  A sign is taken from z when |z| exceeds a bound on the accumulation
 // error of any summation order, D * 2^-22 * ||S_k|| * ||r~|| (+2^-100 for
 // flushed denormals); the rest are settled exactly (below).
+}  // namespace kvq
+
+#include "kvq_vgroup.hpp"
+
+namespace kvq {
+
+// Rows rlo <= t < nvalid of the tile are tokens; their sign records go to
+// signs_out at slot0 + t, or (srows non-null) to srows + 16 t in LDS.
 template <int D, int NRT>
 __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const unsigned char *S_s,
-                                             const float *rn_s, float a_snmax, int nvalid,
-                                             size_t slot0, uint8_t *signs_out, int lane) {
+                                             const float *rn_s, float a_snmax, int rlo, int nvalid,
+                                             size_t slot0, uint8_t *signs_out, uint8_t *srows,
+                                             int lane) {
   constexpr int P2 = D * 2 + 16;
   constexpr int NCT = (D + 31) / 32;
 #pragma unroll 1
@@ -423,7 +432,8 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       }
       // the per-bit mask only where some entry of the wave is uncertain (rare);
       // !(zmin > bound) also catches NaN
-      if (__ballot(!(zmin > bound) && t < nvalid)) {
+      const bool trow = t >= rlo && t < nvalid;
+      if (__ballot(!(zmin > bound) && trow)) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
@@ -431,7 +441,7 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
         }
       }
       if constexpr (D < 32) unsure &= (1u << D) - 1u;                 // rows >= D do not exist
-      if (t >= nvalid) unsure = 0u;                                    // padding rows of the tile
+      if (!trow) unsure = 0u;                                          // padding rows of the tile
       // Uncertain entries, one (lane, row) at a time for the whole wave.  The
       // products s_i r~_i of two bf16 values are exact in fp32 (16-bit
       // significands; |s r~| >= 2^-126 unless tiny, covered by 2^-110
@@ -486,8 +496,13 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       }
       sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
     }
-    const bool tvalid = t < nvalid && lane < 32;
-    if (tvalid) {
+    const bool tvalid = t >= rlo && t < nvalid && lane < 32;
+    bool to_lds = false;
+    if constexpr (D == 128) {
+      to_lds = srows != nullptr;
+      if (to_lds && lane < 32) *(u32x4 *)(srows + 16 * t) = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
+    }
+    if (tvalid && !to_lds) {
       const size_t tslot = slot0 + (size_t)t;
       uint8_t *dst = signs_out + tslot * (D / 8);
       if constexpr (D == 128) {
@@ -518,12 +533,13 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
 // half sum), which is the root of the same adjacent-pair tree.  Then
 // u = y * (1/nu), bucketize, pack.  Sketch sides write the bf16 residual
 // halves back to the stage and take the signs of S r~ (sketch_signs).
+// Tiles are aligned to VT cache slots (the first one may start before t0, the
+// last end after t0 + T; those rows are padding).  VG: value side at d = 128
+// in token groups; the codes go to LDS as one nibble per coordinate and the
+// sign records to LDS, and the wave then writes whole groups (vg_emit_*).
 // ---------------------------------------------------------------------------
-#ifndef KVQ_QUANT_WPE
-#define KVQ_QUANT_WPE 2  // two waves per SIMD (registers <= 256)
-#endif
-template <int D, int BITS, int RK, bool QJL, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_QUANT_WPE)))
+template <int D, int BITS, int RK, bool QJL, bool BF16, bool VG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void quantize_kernel(const QuantArgs a) {
   constexpr int LPV = D > 64 ? 2 : 1;        // lanes per vector
   constexpr int DL = D / LPV;                // coordinates per lane
@@ -544,11 +560,15 @@ void quantize_kernel(const QuantArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
   __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
+  static_assert(!VG || D == 128, "token groups exist at d = 128 only");
+  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * 64 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t srow_all[4][VG && QJL ? VT * 16 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned char *stage = stage_all[wave];
   float *rn_s = rn_all[wave];
   const int vrow = lane / LPV;               // token row of this lane in the tile
+  const int lead = a.t0 % VT;                // padding rows before t0 in the first tile
   const int half = lane % LPV;               // which coordinate half
   build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
   if constexpr (QJL) stage_sketch<D>(S_s, a.S, tid);
@@ -571,8 +591,8 @@ void quantize_kernel(const QuantArgs a) {
     const int bh = tile / a.tiles_per_bh;
     const int tt = tile - bh * a.tiles_per_bh;
     const int b = bh / a.H, h = bh - b * a.H;
-    const int tbase = tt * VT;
-    const int nvalid = min(VT, a.T - tbase);
+    const int tbase = tt * VT - lead;
+    const int rlo = max(0, -tbase), nvalid = min(VT, a.T - tbase);
     // chunk lane + 64k is row lane/CPR + (64/CPR) k, column lane%CPR: one base
     // pointer per lane and a fixed row step (few live registers across the loop)
     const long long rstride = a.st * ESZ;
@@ -584,7 +604,7 @@ void quantize_kernel(const QuantArgs a) {
     for (int k = 0; k < NLD; ++k) {
       const int r = lane / CPR + (64 / CPR) * k;
       pf[k] = u32x4{0u, 0u, 0u, 0u};
-      if (r < nvalid) pf[k] = *(const u32x4 *)(src + k * kstep);
+      if (r >= rlo && r < nvalid) pf[k] = *(const u32x4 *)(src + k * kstep);
     }
   };
   auto stash = [&]() {
@@ -605,8 +625,8 @@ void quantize_kernel(const QuantArgs a) {
   for (int tile = tile0; tile < a.total_tiles; tile += tstride) {
     const int bh = tile / a.tiles_per_bh;
     const int tt = tile - bh * a.tiles_per_bh;
-    const int tbase = tt * VT;
-    const int nvalid = min(VT, a.T - tbase);
+    const int tbase = tt * VT - lead;
+    const int rlo = max(0, -tbase), nvalid = min(VT, a.T - tbase);
 
     float y[DL];
     const unsigned char *myrow = stage + vrow * PITCH + half * DL * ESZ;
@@ -668,7 +688,8 @@ void quantize_kernel(const QuantArgs a) {
     }
     const float nu = sqrtf(ss);
     const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
-    LocalCodes<DL, BITS> lc;
+    // VG: one nibble per coordinate (any width up to 4 fits)
+    LocalCodes<DL, VG ? 4 : BITS> lc;
     lc.clear();
 #pragma unroll
     for (int i = 0; i < DL; ++i) {
@@ -679,10 +700,15 @@ void quantize_kernel(const QuantArgs a) {
       // keep at most 16 coordinates' table lookups in flight (register pressure)
       if ((i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
     }
-    const bool valid = vrow < nvalid;
+    const bool valid = vrow >= rlo && vrow < nvalid;
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vrow);
     uint32_t rec[RECW];
-    if constexpr (LPV == 2) {
+    if constexpr (VG) {
+      // each lane writes its own half of the slot's nibble row
+      uint8_t *nr = vrow_all[wave] + vrow * 64 + half * 32;
+      *(u32x4 *)nr = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
+      *(u32x4 *)(nr + 16) = u32x4{lc.w[4], lc.w[5], lc.w[6], lc.w[7]};
+    } else if constexpr (LPV == 2) {
       // each lane packed its own half; the lower lane joins the two images
       LocalCodes<DL, BITS> oth;
 #pragma unroll
@@ -701,7 +727,7 @@ void quantize_kernel(const QuantArgs a) {
       }
     }
     if (valid && half == 0) {
-      store_bytes<RECB>(a.codes + slot * RECB, rec);
+      if constexpr (!VG) store_bytes<RECB>(a.codes + slot * RECB, rec);
       a.norm[slot] = f32_to_f16_bits(nu * a.scale);
     }
 
@@ -732,8 +758,15 @@ void quantize_kernel(const QuantArgs a) {
       if (next < a.total_tiles) fetch(next);
       wave_sync();
 
-      sketch_signs<D, NRT>(stage, S_s, rn_s, a_snmax, nvalid,
-                           (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs, lane);
+      sketch_signs<D, NRT>(stage, S_s, rn_s, a_snmax, rlo, nvalid,
+                           (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
+                           VG ? srow_all[wave] : nullptr, lane);
+    }
+    if constexpr (VG) {
+      wave_sync();
+      const size_t slot0 = (size_t)bh * a.cap + (size_t)(a.t0 + tbase);
+      vg_emit_codes<BITS, VT>(vrow_all[wave], rlo, nvalid, a.codes + slot0 * RECB, lane);
+      if constexpr (QJL) vg_emit_signs<VT>(srow_all[wave], rlo, nvalid, a.signs + slot0 * 16, lane);
     }
     wave_sync();
     if (next < a.total_tiles) stash();
@@ -780,7 +813,7 @@ __device__ __forceinline__ void dense_rows(cfloat *qb, const float *x, float *yb
 // sums over the whole vector.  Codes of a block are stored as soon as they are
 // known; sketch sides stage the bf16 residual rows for sketch_signs.
 // ---------------------------------------------------------------------------
-template <int D, int BITS, bool QJL, bool BF16>
+template <int D, int BITS, bool QJL, bool BF16, bool VG>
 __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) {
   constexpr int VT = 64;                     // vectors per wave tile (one per lane)
   constexpr int RB = 16;                     // rows of y per block
@@ -795,7 +828,11 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
   __shared__ __attribute__((aligned(16))) unsigned char res_all[4][RBYTES];
   __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
+  static_assert(!VG || D == 128, "token groups exist at d = 128 only");
+  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * 64 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t srow_all[4][VG && QJL ? VT * 16 : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lead = a.t0 % VT;                // padding rows before t0 in the first tile
   unsigned char *res = res_all[wave];
   float *rn_s = rn_all[wave];
   build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
@@ -810,9 +847,9 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
     const int bh = tile / a.tiles_per_bh;
     const int tt = tile - bh * a.tiles_per_bh;
     const int b = bh / a.H, h = bh - b * a.H;
-    const int tbase = tt * VT;
-    const int nvalid = min(VT, a.T - tbase);
-    const bool valid = lane < nvalid;
+    const int tbase = tt * VT - lead;
+    const int rlo = max(0, -tbase), nvalid = min(VT, a.T - tbase);
+    const bool valid = lane >= rlo && lane < nvalid;
     float x[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) x[i] = 0.0f;
@@ -855,7 +892,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
     for (int blk = 0; blk < NB; ++blk) {
       float yb[RB];
       dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
-      LC lc;
+      LocalCodes<RB, VG ? 4 : BITS> lc;
       lc.clear();
 #pragma unroll
       for (int ii = 0; ii < RB; ++ii) {
@@ -864,7 +901,10 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
         lc.put(ii, code);
         if constexpr (QJL) yb[ii] = u - bt.cent[code];
       }
-      if (valid) {
+      if constexpr (VG) {
+        // nibble codes of rows 16 blk .. 16 blk + 15
+        *(u32x2 *)(vrow_all[wave] + lane * 64 + blk * 8) = u32x2{lc.w[0], lc.w[1]};
+      } else if (valid) {
         // records are 2-byte aligned: halfword stores
         if constexpr (BITS == 3) {
           uint16_t *p2 = (uint16_t *)(crec + blk * 4);          // 2-bit plane: 4 bytes per block
@@ -899,8 +939,16 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
       if (valid) a.rnorm[slot] = f32_to_f16_bits(rho);
       rn_s[lane] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
       wave_sync();
-      sketch_signs<D, VT / 32>(res, S_s, rn_s, a_snmax, nvalid,
-                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs, lane);
+      sketch_signs<D, VT / 32>(res, S_s, rn_s, a_snmax, rlo, nvalid,
+                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
+                               VG ? srow_all[wave] : nullptr, lane);
+      wave_sync();
+    }
+    if constexpr (VG) {
+      wave_sync();
+      const size_t slot0 = (size_t)bh * a.cap + (size_t)(a.t0 + tbase);
+      vg_emit_codes<BITS, VT>(vrow_all[wave], rlo, nvalid, a.codes + slot0 * RECB, lane);
+      if constexpr (QJL) vg_emit_signs<VT>(srow_all[wave], rlo, nvalid, a.signs + slot0 * 16, lane);
       wave_sync();
     }
   }
@@ -954,10 +1002,15 @@ __global__ __launch_bounds__(D) void dequant_kernel(const DequantArgs a) {
   const int v = blockIdx.x, i = threadIdx.x;
   const int bh = v / a.T, t = v - bh * a.T;
   const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + t);
-  float val = a.cent[get_code<D, BITS>(a.codes + slot * (D * BITS / 8), i)];
+  bool vg = false;
+  if constexpr (D == 128) vg = a.vg != 0;
+  const uint32_t code = vg ? vg_code<BITS>(a.codes, slot, i)
+                           : (uint32_t)get_code<D, BITS>(a.codes + slot * (D * BITS / 8), i);
+  float val = a.cent[code];
   if constexpr (QJL) {
     const uint8_t *sg = a.signs + slot * (D / 8);
-    sg_s[i] = ((sg[i >> 3] >> (i & 7)) & 1) ? 1.0f : -1.0f;
+    const uint32_t bit = vg ? vg_sign(a.signs, slot, i) : (uint32_t)((sg[i >> 3] >> (i & 7)) & 1);
+    sg_s[i] = bit ? 1.0f : -1.0f;
     __syncthreads();
     float acc = 0.0f;
     for (int k = 0; k < D; ++k) acc = acc + bf16_to_f32(a.S[(size_t)k * D + i]) * sg_s[k];
@@ -2167,6 +2220,10 @@ void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) float vh_s[TT * 16 * NCB];
   __shared__ __attribute__((aligned(16))) unsigned char ks_s[KQ ? TT * SP : 16];
   __shared__ __attribute__((aligned(16))) unsigned char vs_s[VQ ? TT * SP : 16];
+  // value codes at d = 128 are stored in token groups: the tile's groups are
+  // staged raw and read with vg_code
+  constexpr bool VGR = D == 128;
+  __shared__ __attribute__((aligned(16))) uint8_t vq_s[VGR ? TT * VBYTES : 16];
   __shared__ __attribute__((aligned(16))) float kn_s[TT], kr_s[TT], vn_s[TT], vr_s[TT];
   __shared__ float kct_s[16], vct_s[16];
 
@@ -2218,6 +2275,13 @@ void prefill_kernel(const PrefillArgs a) {
     const int ntok = min(TT, tl_b - tbase);
     const size_t rec0 = unit * a.cap + tbase;
     __syncthreads();                                  // previous tile consumed
+    if constexpr (VGR) {
+      // whole 16-slot blocks of the tile (the capacity is a multiple of 16)
+      const int nb16 = (ntok + 15) / 16 * 16 * VBYTES / 16;
+      const uint8_t *src = a.vc + rec0 * VBYTES;
+      for (int k = tid; k < nb16; k += 256) *(u32x4 *)(vq_s + 16 * k) = *(const u32x4 *)(src + 16 * k);
+      __syncthreads();
+    }
     {
       // K: this thread's quarter g = dq of token dt, every kk
       const bool ok = dt < ntok;
@@ -2235,17 +2299,37 @@ void prefill_kernel(const PrefillArgs a) {
       // V: lanes j = 4 dq .. 4 dq + 3 of token dt, every cb
       uint32_t vw[VWR + 1];
       vw[VWR] = 0u;
-      if (ok) load_rec<VBYTES>(a.vc + (rec0 + dt) * VBYTES, vw);
+      if (!VGR && ok) load_rec<VBYTES>(a.vc + (rec0 + dt) * VBYTES, vw);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int jv = 4 * dq + jj;
         float *vd = vh_s + (dt * 16 + jv) * NCB;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) vd[cb] = ok ? vct_s[vcode_at<VB>(vw, cb, jv, D / 16)] : 0.0f;
+        for (int cb = 0; cb < NCB; ++cb) {
+          const uint32_t code = VGR ? vg_code<VB>(vq_s, (size_t)dt, 16 * cb + jv)
+                                    : vcode_at<VB>(vw, cb, jv, D / 16);
+          vd[cb] = ok ? vct_s[code] : 0.0f;
+        }
       }
     }
     if constexpr (KQ) stage_records(ks_s, SP, a.ks + rec0 * SBYTES, SBYTES, ntok, tid);
-    if constexpr (VQ) stage_records(vs_s, SP, a.vs + rec0 * SBYTES, SBYTES, ntok, tid);
+    if constexpr (VQ) {
+      if constexpr (VGR) {
+        // sign octets -> per-slot records (the 8 x 8 transpose is its own inverse)
+        const int nit = (ntok + 7) / 8 * 16;
+        for (int it = tid; it < nit; it += 256) {
+          const int o = it >> 4, n = it & 15;
+          const u32x2 w = *(const u32x2 *)(a.vs + rec0 * SBYTES + o * 128 + 8 * n);
+          uint32_t lo = w.x, hi = w.y;
+          vg_transpose8(lo, hi);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vs_s[(8 * o + e) * SP + n] = (uint8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 255u);
+        }
+      } else {
+        stage_records(vs_s, SP, a.vs + rec0 * SBYTES, SBYTES, ntok, tid);
+      }
+    }
     if (tid < TT) {
       const bool ok = tid < ntok;
       kn_s[tid] = ok ? f16_bits_to_f32(a.kn[rec0 + tid]) : 0.0f;
@@ -2523,7 +2607,7 @@ namespace kvq {
 // three schemes produce are instantiated.
 // ---------------------------------------------------------------------------
 template <int D, int BITS, int RK, bool QJL>
-hipError_t quantize_go(const QuantArgs &a, bool bf16, hipStream_t s) {
+hipError_t quantize_go(const QuantArgs &a, bool bf16, bool vg, hipStream_t s) {
   // persistent-style grid: each wave walks tiles with a stride of 4 * grid
   // (encoders with a bucketize table: one round of resident blocks, three per
   // CU, or two with the sketch staged as well, so each block builds its table
@@ -2531,54 +2615,67 @@ hipError_t quantize_go(const QuantArgs &a, bool bf16, hipStream_t s) {
   const int want = (a.total_tiles + 3) / 4;
   const int gmax = BucketTables<BITS>::LUT ? (QJL ? 512 : 768) : 2048;
   const int grid = want < gmax ? want : gmax;
-  if constexpr (RK == RK_QR) {
-    if (bf16)
-      hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, false>), dim3(grid), dim3(256), 0, s, a);
+  // value sides (token groups at d = 128): unrotated without sketch, or
+  // rotated with sketch
+  constexpr bool VGOK = D == 128 && ((RK == RK_NONE) != QJL);
+  if (vg && !VGOK) return hipErrorInvalidValue;
+  auto go = [&](auto V) {
+    constexpr bool VG = decltype(V)::value;
+    if constexpr (RK == RK_QR) {
+      if (bf16)
+        hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, true, VG>), dim3(grid), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, false, VG>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+      if (bf16)
+        hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, true, VG>), dim3(grid), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, false, VG>), dim3(grid), dim3(256), 0, s, a);
+    }
+  };
+  if constexpr (VGOK) {
+    if (vg) go(std::true_type{});
+    else go(std::false_type{});
   } else {
-    if (bf16)
-      hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, false>), dim3(grid), dim3(256), 0, s, a);
+    go(std::false_type{});
   }
   return hipGetLastError();
 }
 
 template <int D, int RK>
-hipError_t quantize_rot(const QuantArgs &a, int bits, bool qjl, bool bf16, hipStream_t s) {
+hipError_t quantize_rot(const QuantArgs &a, int bits, bool qjl, bool bf16, bool vg, hipStream_t s) {
   if (!qjl) {
     switch (bits) {
-      case 2: return quantize_go<D, 2, RK, false>(a, bf16, s);
-      case 3: return quantize_go<D, 3, RK, false>(a, bf16, s);
-      case 4: return quantize_go<D, 4, RK, false>(a, bf16, s);
+      case 2: return quantize_go<D, 2, RK, false>(a, bf16, vg, s);
+      case 3: return quantize_go<D, 3, RK, false>(a, bf16, vg, s);
+      case 4: return quantize_go<D, 4, RK, false>(a, bf16, vg, s);
     }
   } else {
     switch (bits) {
-      case 1: return quantize_go<D, 1, RK, true>(a, bf16, s);
-      case 2: return quantize_go<D, 2, RK, true>(a, bf16, s);
-      case 3: return quantize_go<D, 3, RK, true>(a, bf16, s);
+      case 1: return quantize_go<D, 1, RK, true>(a, bf16, vg, s);
+      case 2: return quantize_go<D, 2, RK, true>(a, bf16, vg, s);
+      case 3: return quantize_go<D, 3, RK, true>(a, bf16, vg, s);
     }
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_quantize(const QuantArgs &a, int bits, int rk, bool qjl, bool bf16,
+hipError_t launch_quantize(const QuantArgs &a, int bits, int rk, bool qjl, bool bf16, bool vg,
                            hipStream_t s) {
   switch (rk) {
     case RK_NONE:
       if (qjl) return hipErrorInvalidValue;
       switch (bits) {
-        case 1: return quantize_go<D, 1, RK_NONE, false>(a, bf16, s);
-        case 2: return quantize_go<D, 2, RK_NONE, false>(a, bf16, s);
-        case 3: return quantize_go<D, 3, RK_NONE, false>(a, bf16, s);
-        case 4: return quantize_go<D, 4, RK_NONE, false>(a, bf16, s);
+        case 1: return quantize_go<D, 1, RK_NONE, false>(a, bf16, vg, s);
+        case 2: return quantize_go<D, 2, RK_NONE, false>(a, bf16, vg, s);
+        case 3: return quantize_go<D, 3, RK_NONE, false>(a, bf16, vg, s);
+        case 4: return quantize_go<D, 4, RK_NONE, false>(a, bf16, vg, s);
       }
       return hipErrorInvalidValue;
-    case RK_WHT: return quantize_rot<D, RK_WHT>(a, bits, qjl, bf16, s);
-    case RK_RHT: return quantize_rot<D, RK_RHT>(a, bits, qjl, bf16, s);
-    case RK_QR: return quantize_rot<D, RK_QR>(a, bits, qjl, bf16, s);
+    case RK_WHT: return quantize_rot<D, RK_WHT>(a, bits, qjl, bf16, vg, s);
+    case RK_RHT: return quantize_rot<D, RK_RHT>(a, bits, qjl, bf16, vg, s);
+    case RK_QR: return quantize_rot<D, RK_QR>(a, bits, qjl, bf16, vg, s);
   }
   return hipErrorInvalidValue;
 }
@@ -2657,14 +2754,13 @@ hipError_t decode_go(const DecodeArgs &a, int gt, int B, hipStream_t s) {
   if constexpr (D == 128) {
     // matrix-core scan (every scheme and head grouping at d = 128)
     hipLaunchKernelGGL((scan_kernel<KB, KQ, VB, VQ>), grid, blk, 0, s, a);
-    hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
-    return hipGetLastError();
-  }
-  switch (gt) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 1>), grid, blk, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 2>), grid, blk, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 4>), grid, blk, 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  } else {
+    switch (gt) {
+      case 1: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 1>), grid, blk, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 2>), grid, blk, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 4>), grid, blk, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
   return hipGetLastError();
@@ -2760,7 +2856,8 @@ hipError_t launch_finish(const FinishArgs &a, bool vq, int rows, hipStream_t s) 
 }
 
 #define KVQ_INSTANTIATE(D)                                                                     \
-  template hipError_t launch_quantize<D>(const QuantArgs &, int, int, bool, bool, hipStream_t); \
+  template hipError_t launch_quantize<D>(const QuantArgs &, int, int, bool, bool, bool,           \
+                                         hipStream_t);                                          \
   template hipError_t launch_dequantize<D>(const DequantArgs &, int, int, bool, int,            \
                                            hipStream_t);                                        \
   template hipError_t launch_prep<D>(const PrepArgs &, int, bool, bool, hipStream_t);           \

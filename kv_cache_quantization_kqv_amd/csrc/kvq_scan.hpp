@@ -30,13 +30,18 @@
 //
 // Records are read in their stored layout with raw buffer loads (one
 // descriptor per array and unit; slots past the scanned range read as zero,
-// so the loads need no branch): each lane loads the bytes its operand needs (the 16-byte key quarter of its token, the value-code bytes of
-// its eight coordinates for four tokens, the sign byte of its eight sketch
-// rows), and the value codes of two tokens are merged per coordinate by
-// in-register bit shuffles into pair-table indices.
+// so the loads need no branch).  Each lane loads exactly the bytes of its
+// operand roles: the 16-byte key quarter of its token, and -- the value side
+// is stored in token groups (kvq_vgroup.hpp) -- the piece of its quad (token-
+// pair or token-quad table indices of its eight coordinates) and the eight
+// sketch-row bytes of its token octet, whose bits are the octet's tokens.
+// Blocks are aligned to 16 cache slots; slots before the scanned range in the
+// first block are masked like those past its end.
 #pragma once
 
 namespace kvq {
+
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 
 // 8 fp16 lanes of an MFMA operand from four dwords.
 __device__ __forceinline__ f16x8 op8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -88,24 +93,29 @@ struct ScanShape {
   static constexpr bool KPAIR = KB >= 3;
   static constexpr int KENT = KB == 4 ? 256 : KB == 3 ? 64 : KB == 2 ? 256 : 16;
   static constexpr int KW = KB == 4 ? 4 : KB == 3 ? 3 : KB == 2 ? 2 : 1;   // key dwords per lane
-  static constexpr int VENT = 1 << (2 * VB);                                // value token-pair table
+  // value operand table: token-pair index (VB 4, 3; a byte, the width-3 index
+  // in its low 6 bits, so the table repeats 4 times) -> 8 bytes, or token-quad
+  // index (VB 2: byte, VB 1: nibble) -> 16 bytes
+  static constexpr bool VQUAD = VB <= 2;
+  static constexpr int VENT = VB == 1 ? 16 : 256;
+  static constexpr int VTB = VENT * (VQUAD ? 16 : 8);
+  static constexpr int PB = 4 * VB;                                         // value piece bytes per lane
   static constexpr bool SPIN = KQ || VQ;
   static constexpr int NS = 2 + 2 * D;                                      // partial floats per head
 };
 
 // One token block's raw data in registers.  Keys and norms are loaded per
-// scored token (lane role above); the block's value records and value sign
-// records are contiguous (16 x VREC and 16 x 16 bytes) and are loaded as
-// 16-byte pieces (lane l: piece l), then staged in LDS, from where each lane
-// picks the bytes of its operand role.
+// scored token; the value piece is the lane's (quad g of the block,
+// coordinates 8n .. 8n+7); the value sign bytes (rows 8n .. 8n+7 of octet
+// g % 2) are loaded by the lanes g / 2 == block parity within the pair.
 template <int KB, bool KQ, int VB, bool VQ>
 struct ScanBlock {
   using SS = ScanShape<KB, KQ, VB, VQ>;
   uint32_t k[SS::KW];    // key bytes of token n for coordinates 32 g .. 32 g + 31
   uint32_t ks;           // key sign bytes 4 g .. 4 g + 3 of token n (rows 32 g .. 32 g + 31)
   uint32_t nk, rk, nv, rv;   // fp16 bits of the key norm, key residual norm, value norm, value residual norm
-  u32x4 vp;              // piece l of the block's value records (lanes l < VREC)
-  u32x4 sp;              // piece l of the block's value sign records (lanes l < 16)
+  uint32_t v[VB];        // value piece
+  u32x2 sg;              // value sign bytes (zero in lanes of the other parity)
 };
 
 // Buffer descriptors of one (batch row, KV head) unit: each covers the unit's
@@ -123,7 +133,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, si
 
 template <int KB, bool KQ, int VB, bool VQ>
 __device__ __forceinline__ void scan_load(ScanBlock<KB, KQ, VB, VQ> &R, const ScanRsrc &rs, int slot0,
-                                          int tb, int n, int g) {
+                                          int tb, int n, int g, int par) {
   using SS = ScanShape<KB, KQ, VB, VQ>;
   const uint32_t tk = (uint32_t)(slot0 + tb + n);       // slot of this lane's scored token
   const uint32_t ko = tk * SS::KREC;
@@ -146,36 +156,26 @@ __device__ __forceinline__ void scan_load(ScanBlock<KB, KQ, VB, VQ> &R, const Sc
   R.nv = __builtin_amdgcn_raw_buffer_load_b16(rs.vn, 2 * tk, 0, 0);
   R.rv = VQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.vr, 2 * tk, 0, 0) : 0u;
   const int lane = 16 * g + n;
-  const uint32_t t16 = (uint32_t)(slot0 + tb);
-  // lanes without a piece read at an offset past every descriptor's range (zero)
-  const uint32_t oor = 0xFFFFFFF0u;
-  R.vp = __builtin_amdgcn_raw_buffer_load_b128(rs.vc, lane < SS::VREC ? t16 * SS::VREC + 16 * lane : oor, 0, 0);
-  R.sp = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (VQ) R.sp = __builtin_amdgcn_raw_buffer_load_b128(rs.vs, lane < 16 ? t16 * SS::SREC + 16 * lane : oor, 0, 0);
-}
-
-// The value bytes of operand lane (n, g) for tokens 4 g + r from a staged tile:
-// v[r] = code bytes of coordinates 8 n .. 8 n + 7, vh[r] = the 1-bit plane byte
-// of width-3 codes; s[r] = value sign byte n (rows 8 n .. 8 n + 7).
-template <int VB, bool VQ>
-__device__ __forceinline__ void stage_bytes(const uint8_t *vt, const uint8_t *st, int n, int g,
-                                            uint32_t (&v)[4], uint32_t (&vh)[4], uint32_t (&sg)[4]) {
-  constexpr int D = 128, VREC = D * VB / 8;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint8_t *rec = vt + (4 * g + r) * VREC;
-    vh[r] = 0u;
-    if constexpr (VB == 4) {
-      v[r] = *(const uint32_t *)(rec + 4 * n);
-    } else if constexpr (VB == 3) {
-      v[r] = *(const uint16_t *)(rec + 2 * n);
-      vh[r] = rec[D / 4 + n];
-    } else if constexpr (VB == 2) {
-      v[r] = *(const uint16_t *)(rec + 2 * n);
-    } else {
-      v[r] = rec[n];
-    }
-    sg[r] = VQ ? st[(4 * g + r) * (D / 8) + n] : 0u;
+  const uint32_t t16 = (uint32_t)(slot0 + tb);          // a multiple of 16
+  const uint32_t vo = t16 * SS::VREC + (uint32_t)(SS::PB * lane);
+  if constexpr (VB == 4) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs.vc, vo, 0, 0);
+    R.v[0] = w.x; R.v[1] = w.y; R.v[2] = w.z; R.v[3] = w.w;
+  } else if constexpr (VB == 3) {
+    const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rs.vc, vo, 0, 0);
+    R.v[0] = w.x; R.v[1] = w.y; R.v[2] = w.z;
+  } else if constexpr (VB == 2) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.vc, vo, 0, 0);
+    R.v[0] = w.x; R.v[1] = w.y;
+  } else {
+    R.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.vc, vo, 0, 0);
+  }
+  R.sg = u32x2{0u, 0u};
+  if constexpr (VQ) {
+    // lanes of the other parity read at an offset past every range (zero)
+    const uint32_t so = (g >> 1) == par ? t16 * SS::SREC + 128u * (uint32_t)(g & 1) + 8u * (uint32_t)n
+                                        : 0xFFFFFFF0u;
+    R.sg = __builtin_amdgcn_raw_buffer_load_b64(rs.vs, so, 0, 0);
   }
 }
 
@@ -206,53 +206,31 @@ __device__ __forceinline__ f16x8 key_operand(const uint32_t *k, int j, const uin
   }
 }
 
-// Token-pair table indices of the value codes: for coordinate 8 n + j, idx01[j]
-// covers tokens 4 g, 4 g + 1 and idx23[j] tokens 4 g + 2, 4 g + 3 (index
-// convention of pair_codes: first token's code in the low field).
+// A operand of value step j (coordinate 8n + j, tokens 4g .. 4g+3 of the lane
+// group) from the lane's piece: slot order (Ch t0, Cl t0, Ch t1, Cl t1, ...).
+// hi3: width 3, fields 12..15 gathered into the bytes of one dword (once per block).
 template <int VB>
-__device__ __forceinline__ void value_indices(const uint32_t *v, const uint32_t *vh, uint32_t (&i01)[8],
-                                              uint32_t (&i23)[8]) {
-  if constexpr (VB == 4) {
-    // bytes (t0 nib, t1 nib) per coordinate: interleave nibbles of two tokens
-    const uint32_t a0 = dswap(__builtin_amdgcn_perm(v[1], v[0], 0x05010400u), 4, 0x00F000F0u);
-    const uint32_t a1 = dswap(__builtin_amdgcn_perm(v[1], v[0], 0x07030602u), 4, 0x00F000F0u);
-    const uint32_t b0 = dswap(__builtin_amdgcn_perm(v[3], v[2], 0x05010400u), 4, 0x00F000F0u);
-    const uint32_t b1 = dswap(__builtin_amdgcn_perm(v[3], v[2], 0x07030602u), 4, 0x00F000F0u);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      i01[j] = ((j < 4 ? a0 : a1) >> (8 * (j & 3))) & 255u;
-      i23[j] = ((j < 4 ? b0 : b1) >> (8 * (j & 3))) & 255u;
+__device__ __forceinline__ f16x8 value_operand(const uint32_t *v, uint32_t hi3, int j,
+                                               const uint8_t *tab) {
+  if constexpr (VB == 4 || VB == 3) {
+    // fields 2j (tokens 0, 1) and 2j + 1 (tokens 2, 3)
+    uint32_t i0, i1;
+    if (VB == 4 || j < 6) {
+      i0 = (v[j >> 1] >> (16 * (j & 1))) & 255u;
+      i1 = (v[j >> 1] >> (16 * (j & 1) + 8)) & 255u;
+    } else {
+      i0 = (hi3 >> (16 * (j - 6))) & 255u;
+      i1 = (hi3 >> (16 * (j - 6) + 8)) & 255u;
     }
-  } else if constexpr (VB == 3 || VB == 2) {
-    // nibble j = (t0 low pair, t1 low pair): interleave 2-bit units of two tokens
-    uint32_t w01 = __builtin_amdgcn_perm(v[1], v[0], 0x05010400u);
-    w01 = dswap(dswap(w01, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu);
-    uint32_t w23 = __builtin_amdgcn_perm(v[3], v[2], 0x05010400u);
-    w23 = dswap(dswap(w23, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu);
-    uint32_t h = 0u;
-    if constexpr (VB == 3) {
-      // 2-bit unit j of each half = (t0 high bit, t1 high bit) of coordinate j
-      h = vh[0] | (vh[1] << 8) | (vh[2] << 16) | (vh[3] << 24);
-      h = dswap(dswap(dswap(h, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu), 1, 0x22222222u);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      i01[j] = (w01 >> (4 * j)) & 15u;
-      i23[j] = (w23 >> (4 * j)) & 15u;
-      if constexpr (VB == 3) {
-        i01[j] |= ((h >> (2 * j)) & 3u) << 4;
-        i23[j] |= ((h >> (16 + 2 * j)) & 3u) << 4;
-      }
-    }
+    const u32x2 t0 = *(const u32x2 *)(tab + 8 * i0);
+    const u32x2 t1 = *(const u32x2 *)(tab + 8 * i1);
+    return op8(t0.x, t0.y, t1.x, t1.y);
+  } else if constexpr (VB == 2) {
+    const uint32_t q = (v[j >> 2] >> (8 * (j & 3))) & 255u;
+    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * q));
   } else {
-    // 1-bit codes: 2-bit unit j = (t0 bit, t1 bit)
-    uint32_t h = v[0] | (v[1] << 8) | (v[2] << 16) | (v[3] << 24);
-    h = dswap(dswap(dswap(h, 4, 0x00F000F0u), 2, 0x0C0C0C0Cu), 1, 0x22222222u);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      i01[j] = (h >> (2 * j)) & 3u;
-      i23[j] = (h >> (16 + 2 * j)) & 3u;
-    }
+    const uint32_t q = (v[0] >> (4 * j)) & 15u;
+    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * q));
   }
 }
 
@@ -263,16 +241,12 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   constexpr int D = SS::D, NS = SS::NS;
   constexpr int KTB = SS::KENT * (SS::KPAIR ? 8 : 16);
   __shared__ __attribute__((aligned(16))) uint8_t kt_s[KTB];
-  __shared__ __attribute__((aligned(16))) u32x2 vt_s[SS::VENT];
+  __shared__ __attribute__((aligned(16))) uint8_t vt_s[SS::VTB];
   __shared__ __attribute__((aligned(16))) u32x4 sp_s[SS::SPIN ? 256 : 1];
   // per wave: X = (ch, cl) and Z = (cqh, cql) of [block parity][head][token]
   __shared__ __attribute__((aligned(16))) uint32_t wx_s[4][2][4][16];
   __shared__ __attribute__((aligned(16))) uint32_t wz_s[4][2][4][16];
   __shared__ __attribute__((aligned(16))) float ep_s[4][4][NS];
-  // per wave: the value and sign tiles of the two blocks of a pair, one
-  // 16-byte slot per lane (slots past the records hold the zero pieces)
-  constexpr int VT = 1024, STB = VQ ? 1024 : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t tile_s[4][2][VT + STB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: a scalar loop below
@@ -285,7 +259,10 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   const size_t unit = (size_t)b * a.Hkv + hkv;
   const size_t unitg = unit * a.HG + hgrp;
   // per-unit buffer descriptors over slots [0, t0 + n_ctx)
-  const uint32_t nslot = (uint32_t)(a.t0 + a.n_ctx);
+  // scanned slots [t0, t0 + n_ctx) in blocks aligned to 16 slots from A; the
+  // descriptors reach the end of the last block (capacity is a multiple of 16)
+  const int A = a.t0 & ~15, lead = a.t0 - A, span = lead + a.n_ctx;
+  const uint32_t nslot = (uint32_t)((a.t0 + a.n_ctx + 15) & ~15);
   const size_t us = unit * (size_t)a.cap;
   ScanRsrc rs;
   rs.kc = unit_rsrc(a.kc, us * SS::KREC, nslot * SS::KREC);
@@ -328,14 +305,19 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
       *(u32x4 *)(kt_s + 16 * p) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
+  // value table entries: (Ch | Cl << 16) of each token of the index, in token
+  // order (index fields as in the token-group storage)
   for (int p = tid; p < SS::VENT; p += 256) {
-    int ca, cb;
-    pair_codes<VB>(p, ca, cb);
-    _Float16 ha, la, hb, lb;
-    split1(a.vcent[ca], ha, la);
-    split1(a.vcent[cb], hb, lb);
-    vt_s[p] = u32x2{(uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, la) << 16),
-                    (uint32_t)__builtin_bit_cast(uint16_t, hb) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16)};
+    constexpr int NT = SS::VQUAD ? 4 : 2, FW = VB == 3 ? 3 : VB;
+    uint32_t w[4];
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+      _Float16 h, l;
+      split1(a.vcent[(p >> (FW * r)) & ((1 << VB) - 1)], h, l);
+      w[r] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+    }
+    if constexpr (SS::VQUAD) *(u32x4 *)(vt_s + 16 * p) = u32x4{w[0], w[1], w[2], w[3]};
+    else *(u32x2 *)(vt_s + 8 * p) = u32x2{w[0], w[1]};
   }
   if constexpr (SS::SPIN) {
     // byte x -> 8 fp16 spins, element e = +1 when bit e is set, else -1
@@ -431,8 +413,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   // ---- this wave's token range ------------------------------------------------
   const int t_split = split * a.tps;
   const int q4 = a.tps >> 2;
-  const int t_lo = min(a.n_ctx, t_split + wave * q4);
-  const int t_hi = min(a.n_ctx, t_split + (wave + 1) * q4);
+  const int t_lo = min(span, t_split + wave * q4);     // block-aligned index from A
+  const int t_hi = min(span, t_split + (wave + 1) * q4);
   const int nblk = (t_hi - t_lo + 15) >> 4;
   const int npair = (nblk + 1) >> 1;
 
@@ -471,7 +453,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
       s = fmaf(a.kcoef * f16_bits_to_f32((uint16_t)R.rk), sk, s);
     }
     s *= f16_bits_to_f32((uint16_t)R.nk);
-    return (head_ok && tb + n < t_hi) ? s : -INFINITY;
+    return (head_ok && tb + n >= lead && tb + n < t_hi) ? s : -INFINITY;
   };
   // weights of one block into the exchange buffers of parity par
   auto weights = [&](const SB &R, float s, int par) {
@@ -485,53 +467,38 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     wx[par][g][n] = __builtin_amdgcn_perm(lo, hi, 0x05040100u);   // (ch, cl)
     if constexpr (VQ) wz[par][g][n] = __builtin_amdgcn_perm(lo, hi, 0x07060302u);   // (cqh, cql)
   };
-  // value product of one block: B = weights of head hc for tokens 4 g .. 4 g + 3
-  auto values = [&](const uint32_t (&v)[4], const uint32_t (&vh)[4], int par) {
+  // value product of one block: A = centroids of the lane's piece, B = weights
+  // of head hc for tokens 4 g .. 4 g + 3
+  auto values = [&](const SB &R, int par) {
     const u32x4 X = *(const u32x4 *)&wx[par][hc][4 * g];
     const f16x8 bv = op8(__builtin_amdgcn_perm(X.x, X.x, selV), __builtin_amdgcn_perm(X.y, X.y, selV),
                          __builtin_amdgcn_perm(X.z, X.z, selV), __builtin_amdgcn_perm(X.w, X.w, selV));
-    uint32_t i01[8], i23[8];
-    value_indices<VB>(v, vh, i01, i23);
+    uint32_t hi3 = 0u;
+    if constexpr (VB == 3)
+      hi3 = ((R.v[0] >> 6) & 0x03030303u) | ((R.v[1] >> 4) & 0x0C0C0C0Cu) | ((R.v[2] >> 2) & 0x30303030u);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x2 t0 = *(const u32x2 *)(vtab + 8 * i01[j]);
-      const u32x2 t1 = *(const u32x2 *)(vtab + 8 * i23[j]);
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(op8(t0.x, t0.y, t1.x, t1.y), bv, acc[j], 0, 0, 0);
-    }
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_operand<VB>(R.v, hi3, j, vtab), bv, acc[j],
+                                                      0, 0, 0);
   };
-  // sketch product of a block pair: slots 0..3 <- tokens 4 g + e of the first
-  // block, 4..7 <- tokens 4 g + e - 4 of the second
-  auto sketch = [&](const uint32_t (&sa)[4], const uint32_t (&sb)[4]) {
-    const u32x4 ZA = *(const u32x4 *)&wz[0][hc][4 * g];
-    const u32x4 ZB = *(const u32x4 *)&wz[1][hc][4 * g];
-    const f16x8 bz = op8(__builtin_amdgcn_perm(ZA.y, ZA.x, selS), __builtin_amdgcn_perm(ZA.w, ZA.z, selS),
-                         __builtin_amdgcn_perm(ZB.y, ZB.x, selS), __builtin_amdgcn_perm(ZB.w, ZB.z, selS));
-    // 8 x 8 bit transpose: byte e = token e's sign byte (bit j = row 8 n + j)
-    // -> byte j = row 8 n + j (bit e = token e)
-    uint32_t lo8 = sa[0] | (sa[1] << 8) | (sa[2] << 16) | (sa[3] << 24);
-    uint32_t hi8 = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
-    lo8 = dswap(dswap(lo8, 7, 0x00AA00AAu), 14, 0x0000CCCCu);
-    hi8 = dswap(dswap(hi8, 7, 0x00AA00AAu), 14, 0x0000CCCCu);
-    const uint32_t t = (lo8 ^ (hi8 << 4)) & 0xF0F0F0F0u;
-    lo8 ^= t;
-    hi8 ^= t >> 4;
+  // sketch product of a block pair: lane group g covers octet g % 2 of block
+  // g / 2 (slot e <-> token 8 (g % 2) + e of that block); A = spins of the
+  // lane's sign byte j (row 8 n + j, bit e = token e)
+  auto sketch = [&](u32x2 sg) {
+    const uint32_t(*zq)[16] = wz[g >> 1];
+    const u32x4 Z0 = *(const u32x4 *)&zq[hc][8 * (g & 1)];
+    const u32x4 Z1 = *(const u32x4 *)&zq[hc][8 * (g & 1) + 4];
+    const f16x8 bz = op8(__builtin_amdgcn_perm(Z0.y, Z0.x, selS), __builtin_amdgcn_perm(Z0.w, Z0.z, selS),
+                         __builtin_amdgcn_perm(Z1.y, Z1.x, selS), __builtin_amdgcn_perm(Z1.w, Z1.z, selS));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t x = ((j < 4 ? lo8 : hi8) >> (8 * (j & 3))) & 255u;
+      const uint32_t x = ((j < 4 ? sg.x : sg.y) >> (8 * (j & 3))) & 255u;
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sp_s[x]), bz, acc[j], 0, 0, 0);
     }
   };
   // a pair of token blocks: scores of both, one running-max update, then the
   // weighted value and sketch products with the same reference max
   auto process_pair = [&](const SB &RA, const SB &RB, int tb) {
-    // stage the pair's value and sign tiles
-    uint8_t *stA = tile_s[wave][0], *stB = tile_s[wave][1];
-    *(u32x4 *)(stA + 16 * lane) = RA.vp;
-    *(u32x4 *)(stB + 16 * lane) = RB.vp;
-    if constexpr (VQ) {
-      *(u32x4 *)(stA + VT + 16 * lane) = RA.sp;
-      *(u32x4 *)(stB + VT + 16 * lane) = RB.sp;
-    }
     const float sA = score(RA, tb);
     const float sB = score(RB, tb + 16);
     const float bm = row_max16(fmaxf(sA, sB));
@@ -547,25 +514,22 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     weights(RA, sA, 0);
     weights(RB, sB, 1);
     wave_sync();
-    uint32_t vA[4], vhA[4], sgA[4], vB[4], vhB[4], sgB[4];
-    stage_bytes<VB, VQ>(stA, stA + VT, n, g, vA, vhA, sgA);
-    stage_bytes<VB, VQ>(stB, stB + VT, n, g, vB, vhB, sgB);
-    values(vA, vhA, 0);
-    values(vB, vhB, 1);
-    if constexpr (VQ) sketch(sgA, sgB);
-    wave_sync();   // the exchange and stage buffers are rewritten by the next pair
+    values(RA, 0);
+    values(RB, 1);
+    if constexpr (VQ) sketch(RA.sg | RB.sg);
+    wave_sync();   // the exchange buffers are rewritten by the next pair
   };
 
   // ---- main loop: a pair of blocks per step, two pairs in flight ------------
   SB R0, R1, R2, R3;
-  const int s0 = a.t0;
+  const int s0 = A;
   // issued in block order (the loop head's wait counts assume it)
   __builtin_amdgcn_sched_barrier(0);
-  scan_load(R0, rs, s0, t_lo, n, g);
-  scan_load(R1, rs, s0, t_lo + 16, n, g);
+  scan_load(R0, rs, s0, t_lo, n, g, 0);
+  scan_load(R1, rs, s0, t_lo + 16, n, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  scan_load(R2, rs, s0, t_lo + 32, n, g);
-  scan_load(R3, rs, s0, t_lo + 48, n, g);
+  scan_load(R2, rs, s0, t_lo + 32, n, g, 0);
+  scan_load(R3, rs, s0, t_lo + 48, n, g, 1);
   __builtin_amdgcn_sched_barrier(0);
   // (the scheduling barriers keep each refill between the two pair steps, so
   // a pair's data is requested a full pair step before it is used)
@@ -573,13 +537,13 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     const int tb = t_lo + 32 * ip;
     process_pair(R0, R1, tb);
     __builtin_amdgcn_sched_barrier(0);
-    scan_load(R0, rs, s0, tb + 64, n, g);
-    scan_load(R1, rs, s0, tb + 80, n, g);
+    scan_load(R0, rs, s0, tb + 64, n, g, 0);
+    scan_load(R1, rs, s0, tb + 80, n, g, 1);
     __builtin_amdgcn_sched_barrier(0);
     process_pair(R2, R3, tb + 32);
     __builtin_amdgcn_sched_barrier(0);
-    scan_load(R2, rs, s0, tb + 96, n, g);
-    scan_load(R3, rs, s0, tb + 112, n, g);
+    scan_load(R2, rs, s0, tb + 96, n, g, 0);
+    scan_load(R3, rs, s0, tb + 112, n, g, 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 

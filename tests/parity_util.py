@@ -26,6 +26,8 @@ class Pair:
 
     def __init__(self, scheme, n, d, B, Hkv, cap, S=None, device="cuda", rotation="wht",
                  rot_seed=19):
+        if d == 128:
+            cap = (cap + 15) // 16 * 16        # value token groups need whole 16-slot blocks
         self.scheme, self.n, self.d, self.B, self.Hkv, self.cap = scheme, n, d, B, Hkv, cap
         self.S_t = synth.sketch_bf16(d, d, 7) if S is None else S
         self.S = synth.bits_u16(self.S_t)
@@ -88,3 +90,18 @@ def rel_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
     num = np.linalg.norm(got.astype(np.float64) - want, axis=-1)
     den = np.linalg.norm(want, axis=-1)
     return num / np.maximum(den, 1e-300)
+
+
+def v_sign_records(P):
+    """The value sign bits as per-slot records [B][Hkv][cap][d/8] (bit k of a
+    record = sketch row k), whichever storage the cache uses (token octets at
+    d = 128: bit e of byte 128 o + k = slot 8 o + e, row k)."""
+    sg = P.gpu.view("v_signs").cpu().numpy()
+    if P.d != 128:
+        return sg
+    B, H, cap, _ = sg.shape
+    g = sg.reshape(B, H, cap // 8, 128)
+    bits = (g[:, :, :, None, :] >> np.arange(8, dtype=np.uint8)[None, None, None, :, None]) & 1
+    bits = bits.reshape(B, H, cap, 128)                  # [slot][row]
+    return np.packbits(bits, axis=-1, bitorder="little")
+

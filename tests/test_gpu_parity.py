@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from kv_cache_quantization_kqv_amd import synth
-from parity_util import Pair, rel_rows
+from parity_util import Pair, rel_rows, v_sign_records
 
 pytestmark = pytest.mark.gpu
 
@@ -165,8 +165,9 @@ def test_sign_fixup_rows():
     P.write(K, V, 0)
     torch.cuda.synchronize()
     P.assert_bit_exact()
-    sg = P.gpu.view("v_signs").cpu().numpy()
+    sg = v_sign_records(P)
     assert np.all(sg[..., 0] == 0xFF)              # rows 0..7 are zero -> bit 1
+    assert np.all(P.gpu.view("k_signs").cpu().numpy()[..., 0] == 0xFF)
 
 
 def test_sign_exact_cancellation():
@@ -191,7 +192,7 @@ def test_sign_exact_cancellation():
     P.write(K, V, 0)
     torch.cuda.synchronize()
     P.assert_bit_exact()
-    sg = P.gpu.view("v_signs").cpu().numpy()
+    sg = v_sign_records(P)[:, :, :T]
     assert np.all(sg[..., : d // 16] == 0xFF)      # rows 0..63: z = 0 exactly -> bit 1
 
 
@@ -229,7 +230,7 @@ def test_decode_full_capacity_ragged_tail(d, splits):
     multiples (3-bit codes at d <= 64): the last value piece of the last split
     ends inside a 16-byte piece at the very end of the buffers."""
     print(f"case full-capacity tail d={d} splits={splits}", flush=True)
-    B, Hkv, G, N = 2, 2, 4, 301
+    B, Hkv, G, N = 2, 2, 4, (301 if d < 128 else 304)    # d = 128: whole 16-slot blocks
     P = Pair("KQV", 4, d, B, Hkv, N)
     K, V = _inputs(B, Hkv, N, d, torch.float32, 910 + d, heavy=True)
     P.write(K, V, 0)

@@ -85,10 +85,10 @@ def test_sketch_generator(K):
     ("KV", 4, (4, 4, 0, 0, 0)), ("KQV", 4, (4, 3, 0, 1, 1)), ("QKQV", 4, (3, 3, 1, 1, 1)),
     ("KV", 1, (1, 1, 0, 0, 0)), ("KQV", 2, (2, 1, 0, 1, 1)), ("QKQV", 2, (1, 1, 1, 1, 1))])
 def test_cache_init_and_layout(K, scheme, n, want):
-    c = K.kvq_cache_init(K.SCHEMES[scheme], n, 128, 2, 3, 50)
+    c = K.kvq_cache_init(K.SCHEMES[scheme], n, 128, 2, 3, 48)
     assert (c.k_bits, c.v_bits, c.k_qjl, c.v_qjl, c.rotate) == want
-    sizes = K.kvq_cache_layout(K.SCHEMES[scheme], n, 128, 2, 3, 50)
-    rec = 2 * 3 * 50
+    sizes = K.kvq_cache_layout(K.SCHEMES[scheme], n, 128, 2, 3, 48)
+    rec = 2 * 3 * 48
     kb, vb, kq, vq, _ = want
     assert sizes == [rec * 128 * kb // 8, rec * 16 * kq, rec * 2, rec * 2 * kq,
                      rec * 128 * vb // 8, rec * 16 * vq, rec * 2, rec * 2 * vq]
@@ -106,6 +106,10 @@ def test_cache_init_errors(K):
     assert lib.kvq_cache_init(C.byref(c), 1, 4, 96, 1, 1, 1) == 3
     assert lib.kvq_cache_init(C.byref(c), 1, 4, 256, 1, 1, 1) == 3
     assert lib.kvq_cache_init(C.byref(c), 1, 4, 128, 0, 1, 1) == 10
+    # d = 128: the value side's token groups need whole 16-slot blocks
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 128, 1, 1, 50) == 10
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 128, 1, 1, 48) == 0
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 64, 1, 1, 50) == 0
 
 
 def _fake_cache(K, scheme="KQV", n=4, d=64, B=1, H=2, cap=32):

@@ -38,9 +38,9 @@ def _decode_both(cache: KVQCache, q: torch.Tensor, n_ctx: int):
 
 
 @pytest.mark.parametrize("scheme,n,d,B,Hkv,G,N,dtype", [
-    ("KQV", 4, 128, 2, 4, 4, 3000, torch.bfloat16),
+    ("KQV", 4, 128, 2, 4, 4, 3008, torch.bfloat16),
     ("QKQV", 3, 64, 3, 2, 2, 777, torch.float32),
-    ("KV", 2, 128, 1, 8, 1, 5000, torch.bfloat16),
+    ("KV", 2, 128, 1, 8, 1, 5008, torch.bfloat16),
 ])
 def test_noalloc_equals_workspace_entry(scheme, n, d, B, Hkv, G, N, dtype):
     dev = torch.device("cuda", torch.cuda.current_device())
