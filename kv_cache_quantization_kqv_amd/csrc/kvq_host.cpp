@@ -436,13 +436,18 @@ kvq_status kvq_codebook_init(int d, int bits, kvq_codebook *out) {
   const int K = 1 << bits, half = K / 2;
   double c[8];
   lloyd_max_positive(d, half, c);
+  // levels are binary16 values (the fp32 level rounded to nearest even), so
+  // the matrix-core decode contracts with them exactly; the thresholds are
+  // the midpoints of the stored levels (bucketize = nearest stored level)
+  double c16[8];
+  for (int i = 0; i < half; ++i) c16[i] = (double)(float)(_Float16)(float)c[i];
   for (int i = 0; i < half; ++i) {
-    out->centroid[half + i] = (float)c[i];
-    out->centroid[half - 1 - i] = -(float)c[i];
+    out->centroid[half + i] = (float)c16[i];
+    out->centroid[half - 1 - i] = -(float)c16[i];
   }
   out->threshold[half - 1] = 0.0f;
   for (int i = 0; i + 1 < half; ++i) {
-    float t = (float)(0.5 * (c[i] + c[i + 1]));
+    float t = (float)(0.5 * (c16[i] + c16[i + 1]));
     out->threshold[half + i] = t;
     out->threshold[half - 2 - i] = -t;
   }

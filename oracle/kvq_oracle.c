@@ -159,15 +159,20 @@ int orc_codebook(int d, int bits, double *pos_c64, float *centroid, float *thres
     quiet = (dd < 1e-13 * cmax) ? quiet + 1 : 0; /* at the rounding-noise floor */
     if (quiet >= 64) break;
   }
+  /* Stored levels: the fp32 level rounded to the nearest binary16 (ties to
+   * even), held as fp32.  Thresholds: fp32 of the fp64 midpoint of two
+   * stored levels, so bucketize returns the nearest stored level. */
+  double s16[256];
   for (int i = 0; i < K2; ++i) {
     if (pos_c64) pos_c64[i] = c[i];
-    float f = (float)c[i];
+    s16[i] = orc_f16_to_f64(orc_f32_to_f16((float)c[i]));
+    float f = (float)s16[i];
     centroid[K2 + i] = f;
     centroid[K2 - 1 - i] = -f;
   }
   threshold[K2 - 1] = 0.0f;
   for (int i = 0; i + 1 < K2; ++i) {
-    float f = (float)(0.5 * (c[i] + c[i + 1]));
+    float f = (float)(0.5 * (s16[i] + s16[i + 1]));
     threshold[K2 + i] = f;
     threshold[K2 - 2 - i] = -f;
   }

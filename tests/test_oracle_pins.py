@@ -89,9 +89,12 @@ def test_codebook_is_lloyd_max_fixed_point(orc, d, bits):
     for i in range(K // 2):
         mass, mom = _beta_cell(d, edges[i], edges[i + 1])
         assert abs(c64[i] - mom / mass) < 1e-12 * max(1.0, abs(c64[i]) * math.sqrt(d)), (i, c64[i], mom / mass)
-    # thresholds are the fp32-rounded fp64 midpoints; levels are fp32-rounded fp64 levels
-    assert np.array_equal(c[K // 2:], c64.astype(np.float32))
-    assert np.array_equal(t[K // 2:], (0.5 * (c64[1:] + c64[:-1])).astype(np.float32))
+    # stored levels: the fp32 level rounded to the nearest binary16 (numpy's
+    # conversion, independent of the oracle's); thresholds: fp32 of the fp64
+    # midpoints of the stored levels (bucketize = nearest stored level)
+    s16 = c64.astype(np.float32).astype(np.float16).astype(np.float64)
+    assert np.array_equal(c[K // 2:].astype(np.float64), s16)
+    assert np.array_equal(t[K // 2:], (0.5 * (s16[1:] + s16[:-1])).astype(np.float32))
     # total mass 1 and E[t^2] = 1/d (closed forms) via the same cells
     tot = sum(_beta_cell(d, edges[i], edges[i + 1])[0] for i in range(K // 2))
     assert abs(2 * tot - 1.0) < 1e-12
@@ -163,6 +166,33 @@ def _distortion(d, bits, c64):
     edges = np.concatenate([[0.0], 0.5 * (c64[1:] + c64[:-1]), [1.0]])
     s = sum(2 * _beta_cell(d, edges[i], edges[i + 1])[0] * c64[i] ** 2 for i in range(K // 2))
     return 1.0 - d * s
+
+
+def _distortion_of(d, levels):
+    """D = E||u - Q(u)||^2 for u uniform on S^{d-1} with the given positive
+    levels and nearest-level cells (midpoint edges), any levels:
+    per cell E[(t - c)^2] = E[t^2; cell] - 2 c M + c^2 P, E[t^2] = 1/d."""
+    edges = np.concatenate([[0.0], 0.5 * (levels[1:] + levels[:-1]), [1.0]])
+    acc = 0.0
+    for i, c in enumerate(levels):
+        P, M = _beta_cell(d, edges[i], edges[i + 1])
+        acc += 2 * (2 * c * M - c * c * P)
+    return 1.0 - d * acc
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_binary16_levels_cost_no_distortion(orc, d, bits):
+    """The stored levels are binary16 values: the distortion of the stored
+    quantiser exceeds the Lloyd-Max optimum by under 1e-5 of itself (about
+    3e-6 at 4 bits), and the general formula reproduces the optimum at the
+    fixed point."""
+    c, _, c64 = orc.codebook(d, bits)
+    K = 1 << bits
+    D_opt = _distortion(d, bits, c64)
+    assert abs(_distortion_of(d, c64) - D_opt) < 1e-12
+    D16 = _distortion_of(d, c[K // 2:].astype(np.float64))
+    assert 0.0 <= D16 - D_opt < 1e-5 * D_opt
 
 
 @pytest.mark.parametrize("d", [64, 128])
