@@ -346,9 +346,10 @@ long long min_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   return ((long long)n_ctx + tmax - 1) / tmax;
 }
 
-// About KVQ_SCAN_BLOCKS scan blocks (KVQ_SCAN_BLOCKS_MFMA for the matrix-core
-// scan): the split length is rounded up to whole 256-token rounds (at least
-// 256), and for the vector-unit scan stays within the LDS logit buffer.
+// Vector-unit scan: about KVQ_SCAN_BLOCKS blocks, the split length rounded up
+// to whole 256-token rounds (at least 256) and within the LDS logit buffer.
+// Matrix-core scan (workers take interleaved 64-token chunks): about
+// KVQ_SCAN_BLOCKS_MFMA blocks, at most one chunk per worker (4 per split).
 int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   const int G = q_heads / c->kv_heads;
   const int HG = G / heads_per_block(G);
@@ -356,6 +357,12 @@ int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   const long long target = scan_mfma(c) ? KVQ_SCAN_BLOCKS_MFMA : KVQ_SCAN_BLOCKS;
   const long long want = (target + units - 1) / units;
   if (n_ctx <= 0) return 1;
+  if (scan_mfma(c)) {
+    const long long chunks = ((long long)n_ctx + 15 + 63) / 64;
+    const long long most = (chunks + 3) / 4;
+    const long long s = want < most ? want : most;
+    return s < 1 ? 1 : (int)s;
+  }
   long long tps = ((long long)n_ctx + want - 1) / want;
   tps = tps < 256 ? 256 : (tps + 255) / 256 * 256;
   if (!scan_mfma(c)) {
@@ -633,8 +640,9 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   if (t_end > c->capacity) return KVQ_ERR_CAPACITY;
   if (t_end - t_begin + n_win < 1) return KVQ_ERR_RANGE;
   // the matrix-core scan addresses a unit's records with 32-bit byte offsets,
-  // up to the end of the 16-slot block holding slot t_end - 1
-  if (scan_mfma(c) && ((uint64_t)t_end + 15) * 64u >= (1ull << 32)) return KVQ_ERR_RANGE;
+  // up to the end of the 64-slot chunk holding slot t_end - 1 (and one block
+  // past it)
+  if (scan_mfma(c) && ((uint64_t)t_end + 128) * 64u >= (1ull << 32)) return KVQ_ERR_RANGE;
   if (n_win > 0) {
     if (!wk || !wv) return KVQ_ERR_NULL;
     if (w_dtype != KVQ_F32 && w_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;

@@ -23,7 +23,7 @@ inline int scan_tokens_max(int gt) { return KVQ_SCAN_WBUF_FLOATS / (2 * gt); }
 #define KVQ_SCAN_BLOCKS 4096
 #endif
 #ifndef KVQ_SCAN_BLOCKS_MFMA
-#define KVQ_SCAN_BLOCKS_MFMA 2048
+#define KVQ_SCAN_BLOCKS_MFMA 1024
 #endif
 
 // Rotation applied by the codec (kernel template / argument code):

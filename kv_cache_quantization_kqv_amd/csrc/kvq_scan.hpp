@@ -7,24 +7,26 @@
 // so the main loop has no block barrier.  All three contractions of a token
 // block run on v_mfma_f32_16x16x32_f16 (16 x 16 output, 32-deep):
 //
-//   scores  S[row][t] = sum_k Q[row][k] K^[k][t]     rows 4h + kind, t = token
-//   values  O[c][col] = sum_k V^[c][k] W[k][col]     c = coordinate, k = (token, part)
-//   sketch  A[m][col] = sum_k Sg[m][k] W'[k][col]    m = sketch row, k = token
+//   scores  S[row][t] = sum_k Q[row][k] K^[k][t]     rows 4h + kind, t = token, k = coordinate
+//   values  O[c][col] = sum_k V^[c][k] W[k][col]     c = coordinate, k = token of a block pair
+//   sketch  A[m][col] = sum_k Sg[m][k] W'[k][col]    m = sketch row, k = token of a block pair
 //
-// fp16 has 11 significant bits, so every operand that must carry fp32-level
-// precision is split x = xh + 2^-11 xl (xh = fp16(x), xl = fp16((x - xh) 2^11)):
-// the centroids of both tables, the prepared query and S q', the softmax
-// weights c = w n_v and cq = c rho_v.  Two output columns per quantity collect
-// sum xh yh and sum (xh yl + xl yh); the dropped xl yl term is 2^-22 relative.
-// Sign bits enter as exact fp16 +-1.
+// The codebook levels are binary16 values, so the centroid tables are exact
+// in one fp16 operand, and sign bits enter as exact fp16 +-1.  The other
+// operands carry fp32-level precision as a split x = xh + 2^-11 xl (xh =
+// fp16(x), xl = fp16((x - xh) 2^11)): the prepared query and S q' (two rows
+// of the A operand), the softmax weights c = w n_v and cq = c rho_v (two
+// columns of the B operand).  Two output rows / columns per quantity collect
+// sum xh y and sum xl y, combined as hi + lo / 2048.
 //
 // Lane roles (lane = 16 g + n):
 //   scores / softmax : token n of the block, query head g (one pair per lane);
-//                      the running max is updated once per pair of blocks
-//   value A operand  : coordinate 8 n + j of value block j, tokens 4 g .. 4 g + 3
-//   sketch A operand : sketch row 8 n + j, tokens 4 g .. 4 g + 3 of two blocks
-//   weight operands  : column 4 h + kind (kind 0/1: value hh/cross, 2/3:
-//                      sketch hi/lo) of head h, tokens of lane group g
+//                      the running max is updated once per pair of blocks;
+//                      key operand of step j: coordinates 32 g + 8 j .. + 7
+//   value A operand  : coordinate 8 n + j, tokens 4 g .. 4 g + 3 of both blocks
+//   sketch A operand : sketch row 8 n + j, tokens of octet g % 2 of block g / 2
+//   weight operands  : column 4 h + kind (kind 0/1: value hi/lo, 2/3:
+//                      sketch hi/lo) of head h, the lane group's tokens
 // The softmax lane layout is turned into the weight-operand layout through a
 // small per-wave LDS buffer (one dword per (token, head) and quantity).
 //
@@ -88,17 +90,18 @@ template <int KB, bool KQ, int VB, bool VQ>
 struct ScanShape {
   static constexpr int D = 128;
   static constexpr int KREC = D * KB / 8, VREC = D * VB / 8, SREC = D / 8;
-  // key operand table: byte (KB 4) or 6-bit index (KB 3) of two codes -> 8
-  // bytes; byte (KB 2) or nibble (KB 1) of four codes -> 16 bytes
+  // key operand table: byte (KB 4) or 6-bit index (KB 3) of two codes -> 4
+  // bytes; byte (KB 2) or nibble (KB 1) of four codes -> 8 bytes
   static constexpr bool KPAIR = KB >= 3;
   static constexpr int KENT = KB == 4 ? 256 : KB == 3 ? 64 : KB == 2 ? 256 : 16;
+  static constexpr int KTB = KENT * (KPAIR ? 4 : 8);
   static constexpr int KW = KB == 4 ? 4 : KB == 3 ? 3 : KB == 2 ? 2 : 1;   // key dwords per lane
   // value operand table: token-pair index (VB 4, 3; a byte, the width-3 index
-  // in its low 6 bits, so the table repeats 4 times) -> 8 bytes, or token-quad
-  // index (VB 2: byte, VB 1: nibble) -> 16 bytes
+  // in its low 6 bits, so the table repeats 4 times) -> 4 bytes, or token-quad
+  // index (VB 2: byte, VB 1: nibble) -> 8 bytes
   static constexpr bool VQUAD = VB <= 2;
   static constexpr int VENT = VB == 1 ? 16 : 256;
-  static constexpr int VTB = VENT * (VQUAD ? 16 : 8);
+  static constexpr int VTB = VENT * (VQUAD ? 8 : 4);
   static constexpr int PB = 4 * VB;                                         // value piece bytes per lane
   static constexpr bool SPIN = KQ || VQ;
   static constexpr int NS = 2 + 2 * D;                                      // partial floats per head
@@ -131,106 +134,120 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, si
                                            (int)bytes, 0x00020000);
 }
 
+// Loads of the scan stream data that is read once per step: non-temporal
+// (cache-policy bit 1), so it does not evict what stays resident.
 template <int KB, bool KQ, int VB, bool VQ>
 __device__ __forceinline__ void scan_load(ScanBlock<KB, KQ, VB, VQ> &R, const ScanRsrc &rs, int slot0,
                                           int tb, int n, int g, int par) {
   using SS = ScanShape<KB, KQ, VB, VQ>;
+  constexpr int NT = 2;
   const uint32_t tk = (uint32_t)(slot0 + tb + n);       // slot of this lane's scored token
   const uint32_t ko = tk * SS::KREC;
   if constexpr (KB == 4) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs.kc, ko + 16 * g, 0, 0);
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs.kc, ko + 16 * g, 0, NT);
     R.k[0] = w.x; R.k[1] = w.y; R.k[2] = w.z; R.k[3] = w.w;
   } else if constexpr (KB == 3) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.kc, ko + 8 * g, 0, 0);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.kc, ko + 8 * g, 0, NT);
     R.k[0] = w.x; R.k[1] = w.y;
-    R.k[2] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, ko + SS::D / 4 + 4 * g, 0, 0);
+    R.k[2] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, ko + SS::D / 4 + 4 * g, 0, NT);
   } else if constexpr (KB == 2) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.kc, ko + 8 * g, 0, 0);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.kc, ko + 8 * g, 0, NT);
     R.k[0] = w.x; R.k[1] = w.y;
   } else {
-    R.k[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, ko + 4 * g, 0, 0);
+    R.k[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.kc, ko + 4 * g, 0, NT);
   }
-  R.ks = KQ ? __builtin_amdgcn_raw_buffer_load_b32(rs.ks, tk * SS::SREC + 4 * g, 0, 0) : 0u;
-  R.nk = __builtin_amdgcn_raw_buffer_load_b16(rs.kn, 2 * tk, 0, 0);
-  R.rk = KQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.kr, 2 * tk, 0, 0) : 0u;
-  R.nv = __builtin_amdgcn_raw_buffer_load_b16(rs.vn, 2 * tk, 0, 0);
-  R.rv = VQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.vr, 2 * tk, 0, 0) : 0u;
+  R.ks = KQ ? __builtin_amdgcn_raw_buffer_load_b32(rs.ks, tk * SS::SREC + 4 * g, 0, NT) : 0u;
+  R.nk = __builtin_amdgcn_raw_buffer_load_b16(rs.kn, 2 * tk, 0, NT);
+  R.rk = KQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.kr, 2 * tk, 0, NT) : 0u;
+  R.nv = __builtin_amdgcn_raw_buffer_load_b16(rs.vn, 2 * tk, 0, NT);
+  R.rv = VQ ? __builtin_amdgcn_raw_buffer_load_b16(rs.vr, 2 * tk, 0, NT) : 0u;
   const int lane = 16 * g + n;
   const uint32_t t16 = (uint32_t)(slot0 + tb);          // a multiple of 16
   const uint32_t vo = t16 * SS::VREC + (uint32_t)(SS::PB * lane);
   if constexpr (VB == 4) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs.vc, vo, 0, 0);
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs.vc, vo, 0, NT);
     R.v[0] = w.x; R.v[1] = w.y; R.v[2] = w.z; R.v[3] = w.w;
   } else if constexpr (VB == 3) {
-    const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rs.vc, vo, 0, 0);
+    const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rs.vc, vo, 0, NT);
     R.v[0] = w.x; R.v[1] = w.y; R.v[2] = w.z;
   } else if constexpr (VB == 2) {
-    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.vc, vo, 0, 0);
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rs.vc, vo, 0, NT);
     R.v[0] = w.x; R.v[1] = w.y;
   } else {
-    R.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.vc, vo, 0, 0);
+    R.v[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.vc, vo, 0, NT);
   }
   R.sg = u32x2{0u, 0u};
   if constexpr (VQ) {
     // lanes of the other parity read at an offset past every range (zero)
     const uint32_t so = (g >> 1) == par ? t16 * SS::SREC + 128u * (uint32_t)(g & 1) + 8u * (uint32_t)n
                                         : 0xFFFFFFF0u;
-    R.sg = __builtin_amdgcn_raw_buffer_load_b64(rs.vs, so, 0, 0);
+    R.sg = __builtin_amdgcn_raw_buffer_load_b64(rs.vs, so, 0, NT);
   }
 }
 
 // B operand of the score product for step j: key centroids of coordinates
-// 32 g + 4 j .. + 3 of token n in the slot order (Ch c0, Ch c1, Cl c0, Cl c1,
-// Ch c2, Ch c3, Cl c2, Cl c3).
+// 32 g + 8 j .. + 7 of token n (fp16, coordinate order).
 template <int KB>
 __device__ __forceinline__ f16x8 key_operand(const uint32_t *k, int j, const uint8_t *tab) {
   if constexpr (KB == 4) {
-    const uint32_t w = k[j >> 1] >> (16 * (j & 1));
-    const u32x2 t0 = *(const u32x2 *)(tab + 8 * (w & 255u));
-    const u32x2 t1 = *(const u32x2 *)(tab + 8 * ((w >> 8) & 255u));
-    return op8(t0.x, t0.y, t1.x, t1.y);
+    const uint32_t w = k[j];
+    const uint32_t t0 = *(const uint32_t *)(tab + 4 * (w & 255u));
+    const uint32_t t1 = *(const uint32_t *)(tab + 4 * ((w >> 8) & 255u));
+    const uint32_t t2 = *(const uint32_t *)(tab + 4 * ((w >> 16) & 255u));
+    const uint32_t t3 = *(const uint32_t *)(tab + 4 * (w >> 24));
+    return op8(t0, t1, t2, t3);
   } else if constexpr (KB == 3) {
-    const uint32_t by = (k[j >> 2] >> (8 * (j & 3))) & 255u;
-    const uint32_t hb = (k[2] >> (4 * j)) & 15u;
-    const uint32_t i0 = (by & 15u) | ((hb & 3u) << 4);
-    const uint32_t i1 = (by >> 4) | ((hb >> 2) << 4);
-    const u32x2 t0 = *(const u32x2 *)(tab + 8 * i0);
-    const u32x2 t1 = *(const u32x2 *)(tab + 8 * i1);
-    return op8(t0.x, t0.y, t1.x, t1.y);
+    // 2-bit plane: 16 bits of coordinates 8 j .. 8 j + 7; 1-bit plane: byte j
+    const uint32_t lo = (k[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t hb = (k[2] >> (8 * j)) & 255u;
+    uint32_t t[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t idx = ((lo >> (4 * b)) & 15u) | (((hb >> (2 * b)) & 3u) << 4);
+      t[b] = *(const uint32_t *)(tab + 4 * idx);
+    }
+    return op8(t[0], t[1], t[2], t[3]);
   } else if constexpr (KB == 2) {
-    const uint32_t by = (k[j >> 2] >> (8 * (j & 3))) & 255u;
-    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * by));
+    const uint32_t w = (k[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const u32x2 t0 = *(const u32x2 *)(tab + 8 * (w & 255u));
+    const u32x2 t1 = *(const u32x2 *)(tab + 8 * (w >> 8));
+    return op8(t0.x, t0.y, t1.x, t1.y);
   } else {
-    const uint32_t nb = (k[0] >> (4 * j)) & 15u;
-    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * nb));
+    const uint32_t by = (k[0] >> (8 * j)) & 255u;
+    const u32x2 t0 = *(const u32x2 *)(tab + 8 * (by & 15u));
+    const u32x2 t1 = *(const u32x2 *)(tab + 8 * (by >> 4));
+    return op8(t0.x, t0.y, t1.x, t1.y);
   }
 }
 
-// A operand of value step j (coordinate 8n + j, tokens 4g .. 4g+3 of the lane
-// group) from the lane's piece: slot order (Ch t0, Cl t0, Ch t1, Cl t1, ...).
-// hi3: width 3, fields 12..15 gathered into the bytes of one dword (once per block).
+// A operand of value step j (coordinate 8n + j) over a block pair: slots
+// 0..3 = tokens 4g .. 4g+3 of the first block (piece a), 4..7 = those of the
+// second (piece b).  h3a / h3b: width 3, fields 12..15 of a piece gathered
+// into the bytes of one dword (once per block).
 template <int VB>
-__device__ __forceinline__ f16x8 value_operand(const uint32_t *v, uint32_t hi3, int j,
-                                               const uint8_t *tab) {
+__device__ __forceinline__ uint32_t value_field(const uint32_t *v, uint32_t h3, int u) {
+  if constexpr (VB == 4) return (v[u >> 2] >> (8 * (u & 3))) & 255u;
+  if (u < 12) return (v[u >> 2] >> (8 * (u & 3))) & 255u;
+  return (h3 >> (8 * (u - 12))) & 255u;
+}
+
+template <int VB>
+__device__ __forceinline__ f16x8 value_operand(const uint32_t *va, uint32_t h3a, const uint32_t *vb,
+                                               uint32_t h3b, int j, const uint8_t *tab) {
   if constexpr (VB == 4 || VB == 3) {
-    // fields 2j (tokens 0, 1) and 2j + 1 (tokens 2, 3)
-    uint32_t i0, i1;
-    if (VB == 4 || j < 6) {
-      i0 = (v[j >> 1] >> (16 * (j & 1))) & 255u;
-      i1 = (v[j >> 1] >> (16 * (j & 1) + 8)) & 255u;
-    } else {
-      i0 = (hi3 >> (16 * (j - 6))) & 255u;
-      i1 = (hi3 >> (16 * (j - 6) + 8)) & 255u;
-    }
-    const u32x2 t0 = *(const u32x2 *)(tab + 8 * i0);
-    const u32x2 t1 = *(const u32x2 *)(tab + 8 * i1);
-    return op8(t0.x, t0.y, t1.x, t1.y);
+    const uint32_t t0 = *(const uint32_t *)(tab + 4 * value_field<VB>(va, h3a, 2 * j));
+    const uint32_t t1 = *(const uint32_t *)(tab + 4 * value_field<VB>(va, h3a, 2 * j + 1));
+    const uint32_t t2 = *(const uint32_t *)(tab + 4 * value_field<VB>(vb, h3b, 2 * j));
+    const uint32_t t3 = *(const uint32_t *)(tab + 4 * value_field<VB>(vb, h3b, 2 * j + 1));
+    return op8(t0, t1, t2, t3);
   } else if constexpr (VB == 2) {
-    const uint32_t q = (v[j >> 2] >> (8 * (j & 3))) & 255u;
-    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * q));
+    const u32x2 ta = *(const u32x2 *)(tab + 8 * ((va[j >> 2] >> (8 * (j & 3))) & 255u));
+    const u32x2 tb = *(const u32x2 *)(tab + 8 * ((vb[j >> 2] >> (8 * (j & 3))) & 255u));
+    return op8(ta.x, ta.y, tb.x, tb.y);
   } else {
-    const uint32_t q = (v[0] >> (4 * j)) & 15u;
-    return __builtin_bit_cast(f16x8, *(const u32x4 *)(tab + 16 * q));
+    const u32x2 ta = *(const u32x2 *)(tab + 8 * ((va[0] >> (4 * j)) & 15u));
+    const u32x2 tb = *(const u32x2 *)(tab + 8 * ((vb[0] >> (4 * j)) & 15u));
+    return op8(ta.x, ta.y, tb.x, tb.y);
   }
 }
 
@@ -239,8 +256,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   using SS = ScanShape<KB, KQ, VB, VQ>;
   using SB = ScanBlock<KB, KQ, VB, VQ>;
   constexpr int D = SS::D, NS = SS::NS;
-  constexpr int KTB = SS::KENT * (SS::KPAIR ? 8 : 16);
-  __shared__ __attribute__((aligned(16))) uint8_t kt_s[KTB];
+  __shared__ __attribute__((aligned(16))) uint8_t kt_s[SS::KTB];
   __shared__ __attribute__((aligned(16))) uint8_t vt_s[SS::VTB];
   __shared__ __attribute__((aligned(16))) u32x4 sp_s[SS::SPIN ? 256 : 1];
   // per wave: X = (ch, cl) and Z = (cqh, cql) of [block parity][head][token]
@@ -279,45 +295,27 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     rs.vr = unit_rsrc(a.vr, us * 2, nslot * 2);
   }
 
-  // ---- tables (shared by the block) ----------------------------------------
+  // ---- tables (shared by the block): fp16 levels (exact) in index order ----
+  auto h16 = [](float c) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)c); };
   for (int p = tid; p < SS::KENT; p += 256) {
     if constexpr (SS::KPAIR) {
       int ca, cb;
       pair_codes<KB>(p, ca, cb);
-      _Float16 ha, la, hb, lb;
-      split1(a.kcent[ca], ha, la);
-      split1(a.kcent[cb], hb, lb);
-      const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-      const uint32_t lw = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
-      *(u32x2 *)(kt_s + 8 * p) = u32x2{hw, lw};
+      *(uint32_t *)(kt_s + 4 * p) = h16(a.kcent[ca]) | (h16(a.kcent[cb]) << 16);
     } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c0 = (p >> (KB * 2 * q)) & ((1 << KB) - 1);
-        const int c1 = (p >> (KB * (2 * q + 1))) & ((1 << KB) - 1);
-        _Float16 h0, l0, h1, l1;
-        split1(a.kcent[c0], h0, l0);
-        split1(a.kcent[c1], h1, l1);
-        w[2 * q] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        w[2 * q + 1] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-      }
-      *(u32x4 *)(kt_s + 16 * p) = u32x4{w[0], w[1], w[2], w[3]};
+      constexpr int M = (1 << KB) - 1;
+      *(u32x2 *)(kt_s + 8 * p) = u32x2{h16(a.kcent[p & M]) | (h16(a.kcent[(p >> KB) & M]) << 16),
+                                       h16(a.kcent[(p >> (2 * KB)) & M]) |
+                                           (h16(a.kcent[(p >> (3 * KB)) & M]) << 16)};
     }
   }
-  // value table entries: (Ch | Cl << 16) of each token of the index, in token
-  // order (index fields as in the token-group storage)
+  // value table: the tokens of a pair / quad index (fields as in the
+  // token-group storage), in token order
   for (int p = tid; p < SS::VENT; p += 256) {
-    constexpr int NT = SS::VQUAD ? 4 : 2, FW = VB == 3 ? 3 : VB;
-    uint32_t w[4];
-#pragma unroll
-    for (int r = 0; r < NT; ++r) {
-      _Float16 h, l;
-      split1(a.vcent[(p >> (FW * r)) & ((1 << VB) - 1)], h, l);
-      w[r] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
-    }
-    if constexpr (SS::VQUAD) *(u32x4 *)(vt_s + 16 * p) = u32x4{w[0], w[1], w[2], w[3]};
-    else *(u32x2 *)(vt_s + 8 * p) = u32x2{w[0], w[1]};
+    constexpr int FW = VB == 3 ? 3 : VB, M = (1 << VB) - 1;
+    auto c = [&](int r) { return h16(a.vcent[(p >> (FW * r)) & M]); };
+    if constexpr (SS::VQUAD) *(u32x2 *)(vt_s + 8 * p) = u32x2{c(0) | (c(1) << 16), c(2) | (c(3) << 16)};
+    else *(uint32_t *)(vt_s + 4 * p) = c(0) | (c(1) << 16);
   }
   if constexpr (SS::SPIN) {
     // byte x -> 8 fp16 spins, element e = +1 when bit e is set, else -1
@@ -331,10 +329,10 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   }
 
   // ---- prepared query as the A operand of the score product -------------------
-  // lane (row = 4 h + kind, g); step j slot e <-> coordinate 32 g + 4 j +
-  // 2 (e / 4) + (e % 2), part (e / 2) % 2 (0: centroid hi slot, 1: lo slot).
+  // lane (row = 4 h + kind, g); step j slot e <-> coordinate 32 g + 8 j + e;
+  // kind 0: q' hi, kind 1: q' lo (kinds 2, 3: zero here)
   const int qrow = n, qh_ = qrow >> 2, qkind = qrow & 3;
-  f16x8 qa[8];
+  f16x8 qa[4];
   float unsc_q;
   {
     const float *qv = a.qt + unitg * D * GT;
@@ -354,15 +352,13 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     unsc_q = ldexpf(1.0f, -k);
     const _Float16 z = (_Float16)0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       f16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = 4 * j + 2 * (e >> 2) + (e & 1);
-        const bool lo_slot = (e & 2) != 0;
         _Float16 hi, lo;
-        split1(ldexpf(v[c], k), hi, lo);
-        o[e] = qkind == 0 ? (lo_slot ? z : hi) : (qkind == 1 ? (lo_slot ? hi : lo) : z);
+        split1(ldexpf(v[8 * j + e], k), hi, lo);
+        o[e] = qkind == 0 ? hi : (qkind == 1 ? lo : z);
       }
       qa[j] = o;
     }
@@ -407,16 +403,17 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
 
   // weight-operand lane role: column 4 hc + kind
   const int hc = n >> 2, wkind = n & 3;
-  const uint32_t selV = wkind == 0 ? 0x0C0C0100u : (wkind == 1 ? 0x01000302u : 0x0C0C0C0Cu);
+  const uint32_t selV = wkind == 0 ? 0x05040100u : (wkind == 1 ? 0x07060302u : 0x0C0C0C0Cu);
   const uint32_t selS = wkind == 2 ? 0x05040100u : (wkind == 3 ? 0x07060302u : 0x0C0C0C0Cu);
 
-  // ---- this wave's token range ------------------------------------------------
-  const int t_split = split * a.tps;
-  const int q4 = a.tps >> 2;
-  const int t_lo = min(span, t_split + wave * q4);     // block-aligned index from A
-  const int t_hi = min(span, t_split + (wave + 1) * q4);
-  const int nblk = (t_hi - t_lo + 15) >> 4;
-  const int npair = (nblk + 1) >> 1;
+  // ---- this wave's tokens ----------------------------------------------------
+  // The unit's aligned range is cut into 64-token chunks; its W = 4 splits
+  // workers take chunks worker, worker + W, ... (interleaved), so the waves
+  // resident at one time read neighbouring memory of each array (a sweep, not
+  // W separate streams).  Token order does not matter to the online softmax.
+  const int W = 4 * a.splits;
+  const int worker = 4 * split + wave;
+  const int nchunk = (span + 63) >> 6;
 
   f32x4v acc[8];
 #pragma unroll
@@ -433,7 +430,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     // two independent accumulation chains (a chain waits for each result)
     f32x4v sc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
+    for (int j = 0; j < 4; j += 2) {
       sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], key_operand<KB>(R.k, j, kt_s), sc0, 0, 0, 0);
       sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j + 1], key_operand<KB>(R.k, j + 1, kt_s), sc1, 0, 0, 0);
     }
@@ -453,7 +450,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
       s = fmaf(a.kcoef * f16_bits_to_f32((uint16_t)R.rk), sk, s);
     }
     s *= f16_bits_to_f32((uint16_t)R.nk);
-    return (head_ok && tb + n >= lead && tb + n < t_hi) ? s : -INFINITY;
+    return (head_ok && tb + n >= lead && tb + n < span) ? s : -INFINITY;
   };
   // weights of one block into the exchange buffers of parity par
   auto weights = [&](const SB &R, float s, int par) {
@@ -467,19 +464,22 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     wx[par][g][n] = __builtin_amdgcn_perm(lo, hi, 0x05040100u);   // (ch, cl)
     if constexpr (VQ) wz[par][g][n] = __builtin_amdgcn_perm(lo, hi, 0x07060302u);   // (cqh, cql)
   };
-  // value product of one block: A = centroids of the lane's piece, B = weights
-  // of head hc for tokens 4 g .. 4 g + 3
-  auto values = [&](const SB &R, int par) {
-    const u32x4 X = *(const u32x4 *)&wx[par][hc][4 * g];
-    const f16x8 bv = op8(__builtin_amdgcn_perm(X.x, X.x, selV), __builtin_amdgcn_perm(X.y, X.y, selV),
-                         __builtin_amdgcn_perm(X.z, X.z, selV), __builtin_amdgcn_perm(X.w, X.w, selV));
-    uint32_t hi3 = 0u;
-    if constexpr (VB == 3)
-      hi3 = ((R.v[0] >> 6) & 0x03030303u) | ((R.v[1] >> 4) & 0x0C0C0C0Cu) | ((R.v[2] >> 2) & 0x30303030u);
+  // value product of a block pair: A = centroids of the lanes' pieces, B =
+  // weights hi (kind 0) / lo (kind 1) of head hc for the same tokens
+  auto values = [&](const SB &RA, const SB &RB) {
+    const u32x4 XA = *(const u32x4 *)&wx[0][hc][4 * g];
+    const u32x4 XB = *(const u32x4 *)&wx[1][hc][4 * g];
+    const f16x8 bv = op8(__builtin_amdgcn_perm(XA.y, XA.x, selV), __builtin_amdgcn_perm(XA.w, XA.z, selV),
+                         __builtin_amdgcn_perm(XB.y, XB.x, selV), __builtin_amdgcn_perm(XB.w, XB.z, selV));
+    uint32_t h3a = 0u, h3b = 0u;
+    if constexpr (VB == 3) {
+      h3a = ((RA.v[0] >> 6) & 0x03030303u) | ((RA.v[1] >> 4) & 0x0C0C0C0Cu) | ((RA.v[2] >> 2) & 0x30303030u);
+      h3b = ((RB.v[0] >> 6) & 0x03030303u) | ((RB.v[1] >> 4) & 0x0C0C0C0Cu) | ((RB.v[2] >> 2) & 0x30303030u);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_operand<VB>(R.v, hi3, j, vtab), bv, acc[j],
-                                                      0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_operand<VB>(RA.v, h3a, RB.v, h3b, j, vtab),
+                                                      bv, acc[j], 0, 0, 0);
   };
   // sketch product of a block pair: lane group g covers octet g % 2 of block
   // g / 2 (slot e <-> token 8 (g % 2) + e of that block); A = spins of the
@@ -514,8 +514,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     weights(RA, sA, 0);
     weights(RB, sB, 1);
     wave_sync();
-    values(RA, 0);
-    values(RB, 1);
+    values(RA, RB);
     if constexpr (VQ) sketch(RA.sg | RB.sg);
     wave_sync();   // the exchange buffers are rewritten by the next pair
   };
@@ -524,26 +523,28 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   SB R0, R1, R2, R3;
   const int s0 = A;
   // issued in block order (the loop head's wait counts assume it)
+  const int tfirst = 64 * min(worker, nchunk);
   __builtin_amdgcn_sched_barrier(0);
-  scan_load(R0, rs, s0, t_lo, n, g, 0);
-  scan_load(R1, rs, s0, t_lo + 16, n, g, 1);
+  scan_load(R0, rs, s0, tfirst, n, g, 0);
+  scan_load(R1, rs, s0, tfirst + 16, n, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  scan_load(R2, rs, s0, t_lo + 32, n, g, 0);
-  scan_load(R3, rs, s0, t_lo + 48, n, g, 1);
+  scan_load(R2, rs, s0, tfirst + 32, n, g, 0);
+  scan_load(R3, rs, s0, tfirst + 48, n, g, 1);
   __builtin_amdgcn_sched_barrier(0);
   // (the scheduling barriers keep each refill between the two pair steps, so
   // a pair's data is requested a full pair step before it is used)
-  for (int ip = 0; ip < npair; ip += 2) {
-    const int tb = t_lo + 32 * ip;
+  for (int ci = worker; ci < nchunk; ci += W) {
+    const int tb = 64 * ci;
+    const int tn = 64 * min(ci + W, nchunk);   // next chunk (past the end: zeros, unused)
     process_pair(R0, R1, tb);
     __builtin_amdgcn_sched_barrier(0);
-    scan_load(R0, rs, s0, tb + 64, n, g, 0);
-    scan_load(R1, rs, s0, tb + 80, n, g, 1);
+    scan_load(R0, rs, s0, tn, n, g, 0);
+    scan_load(R1, rs, s0, tn + 16, n, g, 1);
     __builtin_amdgcn_sched_barrier(0);
     process_pair(R2, R3, tb + 32);
     __builtin_amdgcn_sched_barrier(0);
-    scan_load(R2, rs, s0, tb + 96, n, g, 0);
-    scan_load(R3, rs, s0, tb + 112, n, g, 1);
+    scan_load(R2, rs, s0, tn + 32, n, g, 0);
+    scan_load(R3, rs, s0, tn + 48, n, g, 1);
     __builtin_amdgcn_sched_barrier(0);
   }
 

@@ -201,20 +201,22 @@ def test_validation_status_codes(K):
 
 
 def test_auto_splits_fill_the_gpu(K):
-    """Head dimension 128 (matrix-core scan): about 2048 blocks, with no LDS cap
-    on the split length.  Smaller heads (vector-unit scan): about 4096 blocks,
-    never more tokens per split than the LDS logit buffer holds.  Split lengths
-    are whole 256-token rounds (at least 256)."""
+    """Head dimension 128 (matrix-core scan, interleaved 64-token chunks): about
+    1024 blocks, never more than one chunk per worker (4 workers per split).
+    Smaller heads (vector-unit scan): about 4096 blocks, split lengths whole
+    256-token rounds (at least 256) within the LDS logit buffer."""
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)
-    assert K.kvq_decode_auto_splits(c, 32, 32768) == 16       # 2048-token splits
+    assert K.kvq_decode_auto_splits(c, 32, 32768) == 8         # 128 units x 8
     c = _fake_cache(K, d=128, B=4, H=8, cap=131136)
-    assert K.kvq_decode_auto_splits(c, 32, 131136) == 57      # 2049 -> 2304-token splits
+    assert K.kvq_decode_auto_splits(c, 32, 131136) == 32       # 32 units x 32
+    c = _fake_cache(K, d=128, B=1, H=32, cap=4096)
+    assert K.kvq_decode_auto_splits(c, 32, 4096) == 17         # <= 65 chunks (15-slot lead) -> 17
+    c = _fake_cache(K, d=128, B=1, H=1, cap=512)
+    assert K.kvq_decode_auto_splits(c, 1, 512) == 3            # <= 9 chunks -> 3 splits
     c = _fake_cache(K, d=64, B=1, H=1, cap=256)
     assert K.kvq_decode_auto_splits(c, 1, 256) == 1
-    c = _fake_cache(K, d=128, B=1, H=32, cap=4096)
-    assert K.kvq_decode_auto_splits(c, 32, 4096) == 16        # 256-token floor
     c = _fake_cache(K, d=64, B=1, H=1, cap=100000)
-    assert K.kvq_decode_auto_splits(c, 1, 100000) == 391      # 256-token splits
+    assert K.kvq_decode_auto_splits(c, 1, 100000) == 391       # 256-token splits
 
 
 def test_explicit_splits_below_the_lds_budget_rejected(K):
