@@ -384,8 +384,8 @@ __device__ __forceinline__ float sketch_row_norm_max(const unsigned char *S_s, i
 namespace kvq {
 
 // Rows rlo <= t < nvalid of the tile are tokens; their sign records go to
-// signs_out at slot0 + t, or (srows non-null) to srows + 16 t in LDS.
-template <int D, int NRT>
+// signs_out at slot0 + t, or (TO_LDS, d = 128) to srows + 16 t in LDS.
+template <int D, int NRT, bool TO_LDS = false>
 __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const unsigned char *S_s,
                                              const float *rn_s, float a_snmax, int rlo, int nvalid,
                                              size_t slot0, uint8_t *signs_out, uint8_t *srows,
@@ -497,12 +497,10 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
     }
     const bool tvalid = t >= rlo && t < nvalid && lane < 32;
-    bool to_lds = false;
-    if constexpr (D == 128) {
-      to_lds = srows != nullptr;
-      if (to_lds && lane < 32) *(u32x4 *)(srows + 16 * t) = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
-    }
-    if (tvalid && !to_lds) {
+    if constexpr (TO_LDS) {
+      static_assert(D == 128, "LDS sign rows exist at d = 128 only");
+      if (lane < 32) *(u32x4 *)(srows + 16 * t) = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
+    } else if (tvalid) {
       const size_t tslot = slot0 + (size_t)t;
       uint8_t *dst = signs_out + tslot * (D / 8);
       if constexpr (D == 128) {
@@ -539,7 +537,7 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
 // sign records to LDS, and the wave then writes whole groups (vg_emit_*).
 // ---------------------------------------------------------------------------
 template <int D, int BITS, int RK, bool QJL, bool BF16, bool VG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256, 2)
 void quantize_kernel(const QuantArgs a) {
   constexpr int LPV = D > 64 ? 2 : 1;        // lanes per vector
   constexpr int DL = D / LPV;                // coordinates per lane
@@ -561,7 +559,7 @@ void quantize_kernel(const QuantArgs a) {
   __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
   static_assert(!VG || D == 128, "token groups exist at d = 128 only");
-  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * 64 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * RECB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t srow_all[4][VG && QJL ? VT * 16 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -688,8 +686,7 @@ void quantize_kernel(const QuantArgs a) {
     }
     const float nu = sqrtf(ss);
     const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
-    // VG: one nibble per coordinate (any width up to 4 fits)
-    LocalCodes<DL, VG ? 4 : BITS> lc;
+    LocalCodes<DL, BITS> lc;
     lc.clear();
 #pragma unroll
     for (int i = 0; i < DL; ++i) {
@@ -704,10 +701,20 @@ void quantize_kernel(const QuantArgs a) {
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vrow);
     uint32_t rec[RECW];
     if constexpr (VG) {
-      // each lane writes its own half of the slot's nibble row
-      uint8_t *nr = vrow_all[wave] + vrow * 64 + half * 32;
-      *(u32x4 *)nr = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
-      *(u32x4 *)(nr + 16) = u32x4{lc.w[4], lc.w[5], lc.w[6], lc.w[7]};
+      // each lane writes its half of the slot's record (per-slot layout) to
+      // the LDS row (offset made opaque so it is not hoisted out of the tile
+      // loop: register pressure); vg_emit_codes regroups the rows
+      using LCT = LocalCodes<DL, BITS>;
+      int off = vrow * RECB;
+      asm volatile("" : "+v"(off));
+      uint8_t *nr = vrow_all[wave] + off;
+      if constexpr (BITS == 3) {
+        *(u32x4 *)(nr + 16 * half) = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
+        *(u32x2 *)(nr + D / 4 + 8 * half) = u32x2{lc.w[LCT::NA], lc.w[LCT::NA + 1]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < LCT::NA; ++k) *(uint32_t *)(nr + half * (DL * BITS / 8) + 4 * k) = lc.w[k];
+      }
     } else if constexpr (LPV == 2) {
       // each lane packed its own half; the lower lane joins the two images
       LocalCodes<DL, BITS> oth;
@@ -758,19 +765,23 @@ void quantize_kernel(const QuantArgs a) {
       if (next < a.total_tiles) fetch(next);
       wave_sync();
 
-      sketch_signs<D, NRT>(stage, S_s, rn_s, a_snmax, rlo, nvalid,
-                           (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
-                           VG ? srow_all[wave] : nullptr, lane);
-    }
-    if constexpr (VG) {
-      wave_sync();
-      const size_t slot0 = (size_t)bh * a.cap + (size_t)(a.t0 + tbase);
-      vg_emit_codes<BITS, VT>(vrow_all[wave], rlo, nvalid, a.codes + slot0 * RECB, lane);
-      if constexpr (QJL) vg_emit_signs<VT>(srow_all[wave], rlo, nvalid, a.signs + slot0 * 16, lane);
+      sketch_signs<D, NRT, VG>(stage, S_s, rn_s, a_snmax, rlo, nvalid,
+                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
+                               srow_all[wave], lane);
     }
     wave_sync();
     if (next < a.total_tiles) stash();
     wave_sync();
+    if constexpr (VG) {
+      // after the stash, so the next tile's prefetch registers are free (the
+      // scheduling barriers keep its work from moving into earlier phases)
+      __builtin_amdgcn_sched_barrier(0);
+      const size_t slot0 = (size_t)bh * a.cap + (size_t)(a.t0 + tbase);
+      vg_emit_codes<BITS, VT>(vrow_all[wave], rlo, nvalid, a.codes + slot0 * RECB, lane);
+      if constexpr (QJL) vg_emit_signs<VT>(srow_all[wave], rlo, nvalid, a.signs + slot0 * 16, lane);
+      wave_sync();   // the rows are rewritten by the next tile
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -829,7 +840,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
   __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
   static_assert(!VG || D == 128, "token groups exist at d = 128 only");
-  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * 64 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * RECB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t srow_all[4][VG && QJL ? VT * 16 : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lead = a.t0 % VT;                // padding rows before t0 in the first tile
@@ -885,14 +896,15 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
     const float nu = sqrtf(ss);
     const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + lane);
-    uint8_t *crec = a.codes + slot * RECB;
+    // VG: the record goes to this lane's LDS row, regrouped by vg_emit_codes
+    uint8_t *crec = VG ? vrow_all[wave] + lane * RECB : a.codes + slot * RECB;
     // pass 2: codes (and residuals)
     float rl[8] = {}, rs = 0.0f;
 #pragma unroll 1
     for (int blk = 0; blk < NB; ++blk) {
       float yb[RB];
       dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
-      LocalCodes<RB, VG ? 4 : BITS> lc;
+      LC lc;
       lc.clear();
 #pragma unroll
       for (int ii = 0; ii < RB; ++ii) {
@@ -901,10 +913,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
         lc.put(ii, code);
         if constexpr (QJL) yb[ii] = u - bt.cent[code];
       }
-      if constexpr (VG) {
-        // nibble codes of rows 16 blk .. 16 blk + 15
-        *(u32x2 *)(vrow_all[wave] + lane * 64 + blk * 8) = u32x2{lc.w[0], lc.w[1]};
-      } else if (valid) {
+      if (VG || valid) {
         // records are 2-byte aligned: halfword stores
         if constexpr (BITS == 3) {
           uint16_t *p2 = (uint16_t *)(crec + blk * 4);          // 2-bit plane: 4 bytes per block
@@ -939,9 +948,9 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
       if (valid) a.rnorm[slot] = f32_to_f16_bits(rho);
       rn_s[lane] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
       wave_sync();
-      sketch_signs<D, VT / 32>(res, S_s, rn_s, a_snmax, rlo, nvalid,
-                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
-                               VG ? srow_all[wave] : nullptr, lane);
+      sketch_signs<D, VT / 32, VG>(res, S_s, rn_s, a_snmax, rlo, nvalid,
+                                   (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
+                                   srow_all[wave], lane);
       wave_sync();
     }
     if constexpr (VG) {

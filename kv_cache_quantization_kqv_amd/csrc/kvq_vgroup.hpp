@@ -121,18 +121,47 @@ __device__ __forceinline__ void vg_transpose8(uint32_t &lo, uint32_t &hi) {
   hi ^= t >> 4;
 }
 
+// Codes of coordinates 8n .. 8n+7 of one per-slot record (layout as stored at
+// d < 128: widths 1, 2, 4 packed, width 3 a 2-bit plane then a 1-bit plane)
+// as nibbles (coordinate 8n + j in bits 4j .. 4j+3).
+template <int VB>
+__device__ __forceinline__ uint32_t vg_row_nibbles(const uint8_t *row, int n) {
+  if constexpr (VB == 4) {
+    return *(const uint32_t *)(row + 4 * n);
+  } else {
+    uint32_t x = 0u;
+    if constexpr (VB == 2 || VB == 3) {
+      x = *(const uint16_t *)(row + 2 * n);                 // 2-bit units -> bits 4j, 4j+1
+      x = (x | (x << 8)) & 0x00FF00FFu;
+      x = (x | (x << 4)) & 0x0F0F0F0Fu;
+      x = (x | (x << 2)) & 0x33333333u;
+    }
+    if constexpr (VB == 3 || VB == 1) {
+      uint32_t h = row[VB == 3 ? 32 + n : n];              // bits -> bit 4j (+2 for width 3)
+      h = (h | (h << 12)) & 0x000F000Fu;
+      h = (h | (h << 6)) & 0x03030303u;
+      h = (h | (h << 3)) & 0x11111111u;
+      x |= VB == 3 ? h << 2 : h;
+    }
+    return x;
+  }
+}
+
 // Emit the code groups of one wave tile of VT slots (tile start a multiple of
-// VT, so of 4): rows = LDS nibble codes, 64 bytes per slot of the tile; slots
-// with rlo <= row < rhi are written, the others keep their stored bits.  dst =
-// the value codes at the tile's first slot.
+// VT, so of 4): rows = LDS per-slot records (16 VB bytes each) of the tile;
+// slots with rlo <= row < rhi are written, the others keep their stored bits.
+// dst = the value codes at the tile's first slot.
 template <int VB, int VT>
 __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int rhi, uint8_t *dst,
                                               int lane) {
   constexpr int PB = 4 * VB, QB = 64 * VB;
   constexpr uint32_t NM = VB == 4 ? 0xFFFFFFFFu : VB == 3 ? 0x77777777u : VB == 2 ? 0x33333333u
                                                                                   : 0x11111111u;
-#pragma unroll
-  for (int k = 0; k < VT / 16; ++k) {
+  // opaque per call: otherwise the lane-derived addresses are hoisted out of
+  // the caller's tile loop and stay live through it (register pressure)
+  asm volatile("" : "+v"(lane));
+#pragma unroll 1
+  for (int k = 0; k < VT / 16; ++k) {   // one piece at a time (few live registers)
     const int pi = lane + 64 * k;
     const int qd = pi >> 4, n = pi & 15;
     uint32_t N[4], V[4];
@@ -141,7 +170,7 @@ __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int 
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * qd + r;
       const bool ok = row >= rlo && row < rhi;
-      N[r] = *(const uint32_t *)(rows + row * 64 + 4 * n);
+      N[r] = vg_row_nibbles<VB>(rows + row * (16 * VB), n);
       V[r] = ok ? NM : 0u;
       nv += ok ? 1 : 0;
     }
@@ -173,7 +202,8 @@ __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int 
 template <int VT>
 __device__ __forceinline__ void vg_emit_signs(const uint8_t *srows, int rlo, int rhi, uint8_t *dst,
                                               int lane) {
-#pragma unroll
+  asm volatile("" : "+v"(lane));   // as in vg_emit_codes
+#pragma unroll 1
   for (int k = 0; k < (VT * 2 + 63) / 64; ++k) {
     const int it = lane + 64 * k;
     if (it >= VT * 2) break;
