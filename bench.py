@@ -5,12 +5,17 @@ quantize-on-write of K and V for the whole context (kvq_quantize_k/v), an
 Infinity-Cache flush (so the decode reads HBM, not the 256 MB last-level
 cache), then one decode-attention step over the compressed cache
 (kvq_decode_attention: query prep, split scan, merge).  Inputs are resident in
-HBM before timing starts.  Per-call durations come from HIP events recorded on
-the stream the library launches on.
+HBM before timing starts.  Every duration is taken with HIP events recorded on
+the stream the library launches on; each reported figure is the median (with
+p10 / p90) over `--steps` repetitions (at least 30).
 
-Prints ONE JSON line.  `value` is decode-attention HBM GB/s (algorithmic bytes
-of one decode call / its mean duration); quantize GB/s, KV tokens/s, the
-roofline of the dominant kernel and the CPU oracle baseline ride along.
+Prints ONE JSON line.  `value` is decode-attention HBM GB/s of the default
+workload (algorithmic bytes of one decode call / its median duration).  Along
+with it: quantize GB/s, KV tokens/s, the decode stages (prep / scan / merge),
+the roofline of the dominant kernel (the scan), the device's streaming-read
+ceiling, the other workloads (one-layer cold/warm decode, the nine-run
+bit-budget sweep, long-context chunked quantize / one-token append / decode)
+and the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -34,10 +39,60 @@ def record_bytes(d, kb, vb, kq, vq):
     return d * kb // 8 + d * vb // 8 + (d // 8) * (kq + vq) + 2 * (2 + kq + vq)
 
 
+class Timer:
+    """HIP-event timing on the launch stream; cold runs zero a 512 MiB buffer
+    first so the measured call reads HBM, not the last-level cache."""
+
+    def __init__(self, torch, dev):
+        self.torch, self.dev = torch, dev
+        self.stream = torch.cuda.current_stream(dev)
+        self.flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def run(self, fn, reps, cold=True, marks=1):
+        """fn(ev) calls ev(k) after its k-th part (k = 1..marks); returns an
+        array [reps][marks] of microseconds per part."""
+        torch = self.torch
+        import numpy as np
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(marks + 1)] for _ in range(reps)]
+        for r in range(reps):
+            if cold:
+                self.flush.zero_()
+            e = evs[r]
+            e[0].record(self.stream)
+            fn(lambda k, e=e: e[k].record(self.stream))
+        torch.cuda.synchronize(self.dev)
+        return np.array([[e[k].elapsed_time(e[k + 1]) * 1e3 for k in range(marks)] for e in evs])
+
+
+def stats(us):
+    """median / p10 / p90 of a 1-D array of microseconds."""
+    import numpy as np
+    return {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+            "p90": round(float(np.percentile(us, 90)), 2)}
+
+
+def build_cache(torch, KVQCache, synth, w, scheme, n_bits, dev, rotation="wht", cap=None):
+    S = synth.bits_u16(synth.sketch_bf16(w.d, w.d, 7))
+    rot_param = {"wht": None, "rht": synth.rotation_signs(w.d, 19),
+                 "qr": synth.rotation_qr(w.d, 19)}[rotation]
+    cache = KVQCache(scheme, n_bits, w.d, w.B, w.Hkv, cap or w.N, S_bf16=S, device=dev,
+                     rotation=rotation, rot_signs=rot_param if rotation == "rht" else None,
+                     rot_Q=rot_param if rotation == "qr" else None)
+    return cache, S, rot_param
+
+
+def quant_bytes(c, T, B, H, d, in_b):
+    """Algorithmic bytes of quantizing T tokens of K and of V (inputs read,
+    records written)."""
+    qk = B * H * T * (d * in_b + d * c.k_bits // 8 + (d // 8) * c.k_qjl + 2 * (1 + c.k_qjl))
+    qv = B * H * T * (d * in_b + d * c.v_bits // 8 + (d // 8) * c.v_qjl + 2 * (1 + c.v_qjl))
+    return qk, qv
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama_gqa_decode")
     ap.add_argument("--scheme", default=None, help="override the workload's scheme")
@@ -48,6 +103,8 @@ def main():
     ap.add_argument("--prefill-chunk", type=int, default=256,
                     help="also time multi-query attention of a chunk of this many query tokens "
                          "at the end of the context (causal); 0 skips it")
+    ap.add_argument("--no-suite", action="store_true",
+                    help="skip the other workloads (one-layer, bit-budget sweep, long context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=32,
                     help="(b, KV head) units in the CPU sample (about 20 s of oracle work "
@@ -60,42 +117,36 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    reps = max(30, args.steps)
 
     import numpy as np
     import torch
 
     from kv_cache_quantization_kqv_amd import synth
+    from kv_cache_quantization_kqv_amd import kvq as K_
     from kv_cache_quantization_kqv_amd.kvq import KVQCache
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    T_ = Timer(torch, dev)
     w = synth.WORKLOADS[args.workload]
     scheme = args.scheme or w.scheme
     n_bits = args.bits or w.n_bits
     B, Hq, Hkv, d, N = w.B, w.Hq, w.Hkv, w.d, w.N
-    print(f"[bench] workload {w.name} {scheme}{n_bits} B={B} Hq={Hq} Hkv={Hkv} d={d} N={N}",
-          file=sys.stderr, flush=True)
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    log(f"workload {w.name} {scheme}{n_bits} B={B} Hq={Hq} Hkv={Hkv} d={d} N={N}")
 
     K, V, q = synth.make_kvq(w, device=dev)
-    S = synth.bits_u16(synth.sketch_bf16(d, d, 7))
-    rot_param = {"wht": None, "rht": synth.rotation_signs(d, 19),
-                 "qr": synth.rotation_qr(d, 19)}[args.rotation]
-    cache = KVQCache(scheme, n_bits, d, B, Hkv, N, S_bf16=S, device=dev, rotation=args.rotation,
-                     rot_signs=rot_param if args.rotation == "rht" else None,
-                     rot_Q=rot_param if args.rotation == "qr" else None)
+    cache, S, rot_param = build_cache(torch, KVQCache, synth, w, scheme, n_bits, dev, args.rotation)
     c = cache.c
     rec = record_bytes(d, c.k_bits, c.v_bits, c.k_qjl, c.v_qjl)
     in_b = 2 if w.dtype == torch.bfloat16 else 4
     q_bytes = B * Hq * d * (in_b + 4)
     dec_bytes = B * Hkv * N * rec + q_bytes
-    qk_bytes = B * Hkv * N * (d * in_b + d * c.k_bits // 8 + (d // 8) * c.k_qjl + 2 * (1 + c.k_qjl))
-    qv_bytes = B * Hkv * N * (d * in_b + d * c.v_bits // 8 + (d // 8) * c.v_qjl + 2 * (1 + c.v_qjl))
-
-    from kv_cache_quantization_kqv_amd import kvq as _kvq
-    splits = _kvq.kvq_decode_auto_splits(c, Hq, N)
+    qk_bytes, qv_bytes = quant_bytes(c, N, B, Hkv, d, in_b)
+    splits = K_.kvq_decode_auto_splits(c, Hq, N)
     ws = torch.zeros(cache.workspace_bytes(Hq, N), dtype=torch.uint8, device=dev)
     out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     if args.copy_probe_mb:
         n = args.copy_probe_mb * 1024 * 1024 // 4
         a_src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -103,73 +154,73 @@ def main():
         a_dst.copy_(a_src)
         torch.cuda.synchronize(dev)
         del a_src, a_dst
-    stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(ev):
         cache.quantize_k(K, 0)
-        if ev is not None:
-            ev[1].record(stream)
+        ev(1)
         cache.quantize_v(V, 0)
-        if ev is not None:
-            ev[2].record(stream)
-        flush.zero_()
-        if ev is not None:
-            ev[3].record(stream)
+        ev(2)
+        T_.flush.zero_()
+        ev(3)
         cache.decode_attention(q, N, out=out, workspace=ws)
-        if ev is not None:
-            ev[4].record(stream)
+        ev(4)
 
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        step(lambda k: None)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize(dev)
+    tm = T_.run(step, args.steps, cold=False, marks=4)
     wall = time.perf_counter() - t0
-    tk = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    tv = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    td = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e-3
-    print(f"[bench] timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+    log(f"timed {args.steps} steps in {wall:.3f}s")
 
-    dec_t = float(td.mean())
+    # per-call statistics over `reps` repetitions (decode cold: LLC flushed first)
+    tq = T_.run(lambda ev: (cache.quantize_k(K, 0), ev(1), cache.quantize_v(V, 0), ev(2)),
+                reps, cold=True, marks=2)
+    td = T_.run(lambda ev: (cache.decode_attention(q, N, out=out, workspace=ws), ev(1)),
+                reps, cold=True)[:, 0]
+    st = T_.run(lambda ev: (cache.decode_attention(q, N, out=out, workspace=ws, stages=K_.KVQ_STAGE_PREP), ev(1),
+                            cache.decode_attention(q, N, out=out, workspace=ws, stages=K_.KVQ_STAGE_SCAN), ev(2),
+                            cache.decode_attention(q, N, out=out, workspace=ws, stages=K_.KVQ_STAGE_MERGE), ev(3)),
+                reps, cold=True, marks=3)
+    tw = T_.run(lambda ev: (cache.decode_attention(q, N, out=out, workspace=ws), ev(1)),
+                reps, cold=False)[:, 0]
+    dec_t = float(np.median(td)) * 1e-6
     dec_gbps = dec_bytes / dec_t / 1e9
-    quant_t = float((tk + tv).mean())
+    tk, tv = tq[:, 0], tq[:, 1]
+    quant_t = float(np.median(tk + tv)) * 1e-6
     quant_gbps = (qk_bytes + qv_bytes) / quant_t / 1e9
 
-    # warm decode (back-to-back, LLC-resident when the cache fits) for context
-    for _ in range(3):
-        cache.decode_attention(q, N, out=out, workspace=ws)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        cache.decode_attention(q, N, out=out, workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    warm_t = e0.elapsed_time(e1) * 1e-3 / 10
+    # the scan kernel alone: cache records + prepared queries read, split partials written
+    scan_bytes = B * Hkv * N * rec + B * Hq * d * 4 * (1 + c.k_qjl) + B * Hq * splits * (2 + 2 * d) * 4
+    scan_t = float(np.median(st[:, 1])) * 1e-6
+    roof = {"kernel": "scan_kernel (kvq_decode_attention_stages KVQ_STAGE_SCAN: split scan on fp16 MFMA)",
+            "bound": "hbm",
+            "achieved": round(scan_bytes / scan_t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(scan_bytes / scan_t / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+            "bytes_per_launch": scan_bytes, "launch_us": round(scan_t * 1e6, 2),
+            "per_record_bytes": rec}
+    if args.traffic and os.path.exists(args.traffic) and args.rotation == "wht":
+        roof["traffic"] = read_traffic(args.traffic, scheme, n_bits, w.name)
+
+    # the device's streaming-read ceiling (simplest access pattern, 1 GiB)
+    probe = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    pw = torch.zeros(4, dtype=torch.int32, device=dev)
+    sr = T_.run(lambda ev: (K_.kvq_probe_stream_read(probe.data_ptr(), probe.numel(), pw.data_ptr(),
+                                                      T_.stream.cuda_stream), ev(1)),
+                reps, cold=True)[:, 0]
+    stream_gbps = probe.numel() / float(np.median(sr)) / 1e3
+    del probe
 
     prefill = None
     if args.prefill_chunk > 0:
         C = min(args.prefill_chunk, N)
         qp = synth.gaussian((B, C, Hq, d), 31, w.dtype, device=dev)
-        from kv_cache_quantization_kqv_amd import kvq as _kq
-        wsp = torch.empty(_kq.kvq_prefill_workspace(c, Hq, C), dtype=torch.uint8, device=dev)
+        wsp = torch.empty(K_.kvq_prefill_workspace(c, Hq, C), dtype=torch.uint8, device=dev)
         outp = torch.empty(B, C, Hq, d, dtype=torch.float32, device=dev)
-        for _ in range(2):
-            cache.prefill_attention(qp, N - C, N, causal=True, out=outp, workspace=wsp)
-        reps = max(1, min(args.steps, 5))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize(dev)
-        e0.record(stream)
-        for _ in range(reps):
-            cache.prefill_attention(qp, N - C, N, causal=True, out=outp, workspace=wsp)
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-        pt = e0.elapsed_time(e1) * 1e-3 / reps
+        cache.prefill_attention(qp, N - C, N, causal=True, out=outp, workspace=wsp)
+        tp = T_.run(lambda ev: (cache.prefill_attention(qp, N - C, N, causal=True, out=outp, workspace=wsp),
+                                ev(1)), 3, cold=False)[:, 0]
+        pt = float(np.median(tp)) * 1e-6
         # MFMA work per (row, visible token): q'.k (d), the K sketch (m, QKQV),
         # P V (d) and the V sketch (m)
         per = 2 * (d + d + d * c.k_qjl + d * c.v_qjl)
@@ -181,14 +232,6 @@ def main():
                    "kernel": "prep_kernel + prefill_kernel (fp32 MFMA 16x16x4) + finish_kernel"}
         del qp, wsp, outp
 
-    roof = {"kernel": "kvq_decode_attention: query kernel + decode_kernel (split scan, key scores on fp16 MFMA) + merge_kernel (split merge)",
-            "bound": "hbm",
-            "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-            "bytes_per_launch": dec_bytes, "per_record_bytes": rec}
-    if args.traffic and os.path.exists(args.traffic) and args.rotation == "wht":
-        roof["traffic"] = read_traffic(args.traffic, scheme, n_bits, w.name)
-
     result = {
         "metric": METRIC, "value": round(dec_gbps, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -198,27 +241,134 @@ def main():
         "config": {"workload": w.name, "scheme": scheme, "n_bits": n_bits, "batch": B,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "context": N,
                    "input_dtype": str(w.dtype).replace("torch.", ""), "keys": w.keys,
-                   "splits": splits, "rotation": args.rotation},
-        "decode": {"us": round(dec_t * 1e6, 2), "GBps": round(dec_gbps, 1),
+                   "splits": splits, "rotation": args.rotation, "reps": reps},
+        "decode": {"us": stats(td), "GBps": round(dec_gbps, 1),
                    "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
                    "kv_tokens_per_s": round(B * N / dec_t, 1),
                    "records_per_s": round(B * Hkv * N / dec_t, 1),
-                   "warm_us": round(warm_t * 1e6, 2),
-                   "warm_GBps": round(dec_bytes / warm_t / 1e9, 1)},
-        "quantize": {"us_k": round(float(tk.mean()) * 1e6, 2), "us_v": round(float(tv.mean()) * 1e6, 2),
+                   "stages_us": {"prep": stats(st[:, 0]), "scan": stats(st[:, 1]),
+                                 "merge": stats(st[:, 2])},
+                   "warm_us": stats(tw),
+                   "warm_GBps": round(dec_bytes / float(np.median(tw)) / 1e3, 1)},
+        "quantize": {"us_k": stats(tk), "us_v": stats(tv),
                      "GBps": round(quant_gbps, 1),
                      "pct_hbm_peak": round(100 * quant_gbps / HBM_PEAK_GBPS, 2),
-                     "GBps_k": round(qk_bytes / float(tk.mean()) / 1e9, 1),
-                     "GBps_v": round(qv_bytes / float(tv.mean()) / 1e9, 1)},
+                     "GBps_k": round(qk_bytes / float(np.median(tk)) / 1e3, 1),
+                     "GBps_v": round(qv_bytes / float(np.median(tv)) / 1e3, 1)},
         "roofline": roof,
+        "stream_read_GBps": round(stream_gbps, 1),
     }
     if prefill is not None:
         result["prefill"] = prefill
+    del K, V, cache, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_suite:
+        result["workloads"] = suite(torch, np, synth, K_, KVQCache, T_, dev, reps, log)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, scheme, n_bits, K, V, q, S, args.cpu_units, rec,
+        Kc, Vc, qc = synth.make_kvq(w, device=dev)
+        result["cpu_baseline"] = cpu_baseline(w, scheme, n_bits, Kc, Vc, qc, S, args.cpu_units, rec,
                                               args.rotation, rot_param)
     print(json.dumps(result), flush=True)
+
+
+def decode_cold_warm(torch, np, T_, cache, q, n_ctx, reps, ws, out, nbytes):
+    td = T_.run(lambda ev: (cache.decode_attention(q, n_ctx, out=out, workspace=ws), ev(1)),
+                reps, cold=True)[:, 0]
+    tw = T_.run(lambda ev: (cache.decode_attention(q, n_ctx, out=out, workspace=ws), ev(1)),
+                reps, cold=False)[:, 0]
+    return {"cold_us": stats(td), "cold_GBps": round(nbytes / float(np.median(td)) / 1e3, 1),
+            "warm_us": stats(tw), "warm_GBps": round(nbytes / float(np.median(tw)) / 1e3, 1)}
+
+
+def suite(torch, np, synth, K_, KVQCache, T_, dev, reps, log):
+    """The other workloads, each on its own shapes."""
+    res = {}
+    # one layer, batch 1, 32 heads, N = 4096: quantize all tokens + one decode step
+    w = synth.WORKLOADS["one_layer_decode"]
+    log(f"suite: {w.name}")
+    K, V, q = synth.make_kvq(w, device=dev)
+    cache, _, _ = build_cache(torch, KVQCache, synth, w, w.scheme, w.n_bits, dev)
+    c = cache.c
+    rec = record_bytes(w.d, c.k_bits, c.v_bits, c.k_qjl, c.v_qjl)
+    in_b = 2 if w.dtype == torch.bfloat16 else 4
+    qk, qv = quant_bytes(c, w.N, w.B, w.Hkv, w.d, in_b)
+    tq = T_.run(lambda ev: (cache.quantize_k(K, 0), cache.quantize_v(V, 0), ev(1)), reps, cold=True)[:, 0]
+    ws = torch.zeros(cache.workspace_bytes(w.Hq, w.N), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+    nbytes = w.B * w.Hkv * w.N * rec + w.B * w.Hq * w.d * (in_b + 4)
+    res[w.name] = {"quantize_us": stats(tq), "quantize_GBps": round((qk + qv) / float(np.median(tq)) / 1e3, 1),
+                   "decode": decode_cold_warm(torch, np, T_, cache, q, w.N, reps, ws, out, nbytes),
+                   "decode_bytes": nbytes}
+    del K, V, q, cache, ws, out
+
+    # bit-budget sweep: KV, KQV, QKQV at n = 2, 3, 4 over the same inputs
+    w = synth.WORKLOADS["bit_budget_sweep"]
+    log(f"suite: {w.name}")
+    K, V, q = synth.make_kvq(w, device=dev)
+    in_b = 2 if w.dtype == torch.bfloat16 else 4
+    runs = []
+    for scheme in ("KV", "KQV", "QKQV"):
+        for n in (2, 3, 4):
+            cache, _, _ = build_cache(torch, KVQCache, synth, w, scheme, n, dev)
+            c = cache.c
+            rec = record_bytes(w.d, c.k_bits, c.v_bits, c.k_qjl, c.v_qjl)
+            qk, qv = quant_bytes(c, w.N, w.B, w.Hkv, w.d, in_b)
+            tq = T_.run(lambda ev: (cache.quantize_k(K, 0), cache.quantize_v(V, 0), ev(1)), reps,
+                        cold=True)[:, 0]
+            ws = torch.zeros(cache.workspace_bytes(w.Hq, w.N), dtype=torch.uint8, device=dev)
+            out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+            nbytes = w.B * w.Hkv * w.N * rec + w.B * w.Hq * w.d * (in_b + 4)
+            runs.append({"scheme": scheme, "n_bits": n, "record_bytes": rec,
+                         "quantize_GBps": round((qk + qv) / float(np.median(tq)) / 1e3, 1),
+                         **decode_cold_warm(torch, np, T_, cache, q, w.N, reps, ws, out, nbytes)})
+            del cache, ws, out
+    res[w.name] = runs
+    del K, V, q
+
+    # long context: 8192-token prefill chunks, then 64 decode steps that each
+    # append one token and decode over the grown context
+    w = synth.WORKLOADS["long_context"]
+    log(f"suite: {w.name}")
+    steps = 64
+    K, V, q = synth.make_kvq(w, device=dev, N=w.N + steps)
+    cap = (w.N + steps + 15) // 16 * 16
+    cache, _, _ = build_cache(torch, KVQCache, synth, w, w.scheme, w.n_bits, dev, cap=cap)
+    c = cache.c
+    rec = record_bytes(w.d, c.k_bits, c.v_bits, c.k_qjl, c.v_qjl)
+    in_b = 2 if w.dtype == torch.bfloat16 else 4
+    CH = 8192
+    qk, qv = quant_bytes(c, CH, w.B, w.Hkv, w.d, in_b)
+
+    def chunks(ev):
+        for i in range(w.N // CH):
+            cache.quantize_k(K[:, :, i * CH:(i + 1) * CH], i * CH)
+            cache.quantize_v(V[:, :, i * CH:(i + 1) * CH], i * CH)
+            ev(i + 1)
+    tc = T_.run(chunks, 3, cold=True, marks=w.N // CH).reshape(-1)
+    ws = torch.zeros(cache.workspace_bytes(w.Hq, w.N + steps), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.B, w.Hq, w.d, dtype=torch.float32, device=dev)
+    nbytes = w.B * w.Hkv * w.N * rec + w.B * w.Hq * w.d * (in_b + 4)
+    dec = decode_cold_warm(torch, np, T_, cache, q, w.N, reps, ws, out, nbytes)
+
+    def decode_steps(ev):
+        for s in range(steps):
+            p = w.N + s
+            cache.quantize_k(K[:, :, p:p + 1], p)
+            cache.quantize_v(V[:, :, p:p + 1], p)
+            ev(2 * s + 1)
+            cache.decode_attention(q, p + 1, out=out, workspace=ws)
+            ev(2 * s + 2)
+    ts = T_.run(decode_steps, 1, cold=False, marks=2 * steps)[0]
+    res[w.name] = {"chunk_tokens": CH,
+                   "chunk_quantize_us": stats(tc),
+                   "chunk_quantize_GBps": round((qk + qv) / float(np.median(tc)) / 1e3, 1),
+                   "decode_131k": dec, "decode_bytes": nbytes,
+                   "step_append_us": stats(ts[0::2]), "step_decode_us": stats(ts[1::2])}
+    del K, V, q, cache, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def kernel_source_digest():

@@ -267,6 +267,25 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache *c, const void *q, int q
                                         int q_heads, int n_ctx, int splits, float *out,
                                         void *stream);
 
+/* Decode stages for kvq_decode_attention_stages (bit mask). */
+enum {
+  KVQ_STAGE_PREP = 1,   /* query preparation q' = R q (and S q'); window partial */
+  KVQ_STAGE_SCAN = 2,   /* split scan over the compressed slots -> split partials */
+  KVQ_STAGE_MERGE = 4,  /* merge of the split partials -> out */
+  KVQ_STAGE_ALL = 7
+};
+
+/* kvq_decode_attention run stage by stage: the same arguments plus `stages`,
+ * a non-empty mask of KVQ_STAGE_*; only the selected stages are launched, in
+ * the order prep, scan, merge.  The stages communicate through the workspace,
+ * so calls with PREP, then SCAN, then MERGE on one stream (same arguments and
+ * workspace) give exactly the result of one kvq_decode_attention call, which
+ * equals stages = KVQ_STAGE_ALL.  For callers that time or overlap the stages
+ * separately.  Errors: as kvq_decode_attention; KVQ_ERR_RANGE for a bad mask. */
+kvq_status kvq_decode_attention_stages(const kvq_cache *c, const void *q, int q_dtype,
+                                       int q_heads, int n_ctx, int splits, int stages, float *out,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace bytes kvq_decode_attention (or kvq_decode_attention_window over
  * n_ctx compressed slots) needs for these arguments; n_ctx may be 0 here. */
 kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int splits,
@@ -305,6 +324,14 @@ const char *kvq_status_str(kvq_status s);
 
 /* Library version string. */
 const char *kvq_version(void);
+
+/* Measurement aid, not part of the codec: one streaming read of `bytes`
+ * (a multiple of 16) of device memory at buf (16-B aligned), grid-stride,
+ * non-temporal 16-byte loads; out: 4 device words that the kernel may write
+ * (its result is meaningless).  Timing it gives the read bandwidth the device
+ * reaches with the simplest access pattern, the practical ceiling for the
+ * decode scan.  Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_RANGE, KVQ_ERR_HIP. */
+kvq_status kvq_probe_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

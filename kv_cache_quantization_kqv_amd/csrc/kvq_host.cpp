@@ -390,6 +390,23 @@ int split_tokens(int n_ctx, int splits) {
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
+// Streaming-read probe (kvq_probe_stream_read): every thread reads 16-byte
+// words in a grid-stride sweep with non-temporal loads (the pattern that comes
+// closest to the HBM peak), folds them with XOR and writes one word per block
+// only when the fold hits an unlikely value (the loads stay live).
+constexpr int kStreamReadBlocks = 2048;
+typedef unsigned int probe_u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_read_kernel(const probe_u32x4 *__restrict__ p,
+                                                          size_t n16, uint32_t *out) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0u;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+    const probe_u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) out[blockIdx.x & 3] = acc;
+}
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -414,6 +431,15 @@ void *scratch_address() {
 extern "C" {
 
 const char *kvq_version(void) { return "libkvq 0.1 (gfx950)"; }
+
+kvq_status kvq_probe_stream_read(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  if (!buf || !out) return KVQ_ERR_NULL;
+  if (!aligned16(buf) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (bytes < 16 || bytes % 16) return KVQ_ERR_RANGE;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamReadBlocks), dim3(256), 0, (hipStream_t)stream,
+                     (const probe_u32x4 *)buf, bytes / 16, out);
+  return hip_status(hipGetLastError());
+}
 
 const char *kvq_status_str(kvq_status s) {
   switch (s) {
@@ -629,7 +655,8 @@ namespace {
 kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_heads, int t_begin,
                        int t_end, const void *wk, const void *wv, int w_dtype, int n_win,
                        int splits, float *out, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+                       void *stream, int stages = KVQ_STAGE_ALL) {
+  if (stages < 1 || stages > KVQ_STAGE_ALL) return KVQ_ERR_RANGE;
   kvq_status s = check_cache(c);
   if (s != KVQ_OK) return s;
   if (!q || !out) return KVQ_ERR_NULL;
@@ -674,12 +701,15 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
   for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
   p.Q = c->rot_Q;
-  hipError_t e = by_dim(d, [&](auto D) {
-    return kvq::launch_prep<decltype(D)::value>(p, rk, c->k_qjl != 0, q_dtype == KVQ_BF16, hs);
-  });
-  if (e != hipSuccess) return KVQ_ERR_HIP;
+  hipError_t e = hipSuccess;
+  if (stages & KVQ_STAGE_PREP) {
+    e = by_dim(d, [&](auto D) {
+      return kvq::launch_prep<decltype(D)::value>(p, rk, c->k_qjl != 0, q_dtype == KVQ_BF16, hs);
+    });
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
 
-  if (n_win > 0) {
+  if (n_win > 0 && (stages & KVQ_STAGE_PREP)) {
     kvq::WindowArgs w;
     std::memset(&w, 0, sizeof(w));
     w.q = q; w.wk = wk; w.wv = wv; w.wpart = wpart;
@@ -716,7 +746,8 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   a.tps = n_ctx > 0 ? split_tokens(n_ctx + lead, splits) : 0;
   e = by_dim(d, [&](auto D) {
     return kvq::launch_decode<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
-                                                  c->v_qjl != 0, gt, c->batch, hs);
+                                                  c->v_qjl != 0, gt, c->batch,
+                                                  stages & (kvq::STAGE_SCAN | kvq::STAGE_MERGE), hs);
   });
   return hip_status(e);
 }
@@ -743,6 +774,14 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache *c, const void *q, int q
   if (!ws) return KVQ_ERR_HIP;
   return decode_impl(c, q, q_dtype, q_heads, 0, n_ctx, nullptr, nullptr, KVQ_F32, 0, splits, out,
                      ws, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+kvq_status kvq_decode_attention_stages(const kvq_cache *c, const void *q, int q_dtype,
+                                       int q_heads, int n_ctx, int splits, int stages, float *out,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_ctx < 1) return c ? KVQ_ERR_RANGE : KVQ_ERR_NULL;
+  return decode_impl(c, q, q_dtype, q_heads, 0, n_ctx, nullptr, nullptr, KVQ_F32, 0, splits,
+                     out, workspace, workspace_bytes, stream, stages);
 }
 
 kvq_status kvq_decode_attention_window(const kvq_cache *c, const void *q, int q_dtype,

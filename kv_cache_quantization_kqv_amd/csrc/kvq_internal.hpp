@@ -140,8 +140,11 @@ template <int D> hipError_t launch_dequantize(const DequantArgs &a, int bits, in
                                               int n_vec, hipStream_t s);
 template <int D> hipError_t launch_prep(const PrepArgs &a, int rk, bool kqjl, bool bf16,
                                         hipStream_t s);
+// decode stages (bit mask): query preparation (and the full-precision window),
+// the split scan, the merge
+enum { STAGE_PREP = 1, STAGE_SCAN = 2, STAGE_MERGE = 4 };
 template <int D> hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq,
-                                          int gt, int B, hipStream_t s);
+                                          int gt, int B, int stages, hipStream_t s);
 template <int D> hipError_t launch_window(const WindowArgs &a, bool q_bf16, bool w_bf16, int rows,
                                           hipStream_t s);
 template <int D> hipError_t launch_prefill(const PrefillArgs &a, int kb, bool kq, int vb, bool vq,

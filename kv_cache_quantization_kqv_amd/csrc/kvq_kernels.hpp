@@ -2758,44 +2758,46 @@ hipError_t launch_prep(const PrepArgs &a, int rk, bool kq, bool bf16, hipStream_
 }
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
-hipError_t decode_go(const DecodeArgs &a, int gt, int B, hipStream_t s) {
+hipError_t decode_go(const DecodeArgs &a, int gt, int B, int stages, hipStream_t s) {
   const dim3 grid(a.splits, a.Hkv * a.HG, B), blk(256);
-  if constexpr (D == 128) {
-    // matrix-core scan (every scheme and head grouping at d = 128)
-    hipLaunchKernelGGL((scan_kernel<KB, KQ, VB, VQ>), grid, blk, 0, s, a);
-  } else {
-    switch (gt) {
-      case 1: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 1>), grid, blk, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 2>), grid, blk, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 4>), grid, blk, 0, s, a); break;
-      default: return hipErrorInvalidValue;
+  if (stages & STAGE_SCAN) {
+    if constexpr (D == 128) {
+      // matrix-core scan (every scheme and head grouping at d = 128)
+      hipLaunchKernelGGL((scan_kernel<KB, KQ, VB, VQ>), grid, blk, 0, s, a);
+    } else {
+      switch (gt) {
+        case 1: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 1>), grid, blk, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 2>), grid, blk, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<D, KB, KQ, VB, VQ, 4>), grid, blk, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+      }
     }
   }
-  hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
+  if (stages & STAGE_MERGE) hipLaunchKernelGGL((merge_kernel<D, VQ>), dim3(B * a.Hq), blk, 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_decode(const DecodeArgs &a, int kb, bool kq, int vb, bool vq, int gt, int B,
-                         hipStream_t s) {
+                         int stages, hipStream_t s) {
   if (!kq && !vq && kb == vb) {  // KV
     switch (kb) {
-      case 1: return decode_go<D, 1, false, 1, false>(a, gt, B, s);
-      case 2: return decode_go<D, 2, false, 2, false>(a, gt, B, s);
-      case 3: return decode_go<D, 3, false, 3, false>(a, gt, B, s);
-      case 4: return decode_go<D, 4, false, 4, false>(a, gt, B, s);
+      case 1: return decode_go<D, 1, false, 1, false>(a, gt, B, stages, s);
+      case 2: return decode_go<D, 2, false, 2, false>(a, gt, B, stages, s);
+      case 3: return decode_go<D, 3, false, 3, false>(a, gt, B, stages, s);
+      case 4: return decode_go<D, 4, false, 4, false>(a, gt, B, stages, s);
     }
   } else if (!kq && vq && vb == kb - 1) {  // KQV
     switch (kb) {
-      case 2: return decode_go<D, 2, false, 1, true>(a, gt, B, s);
-      case 3: return decode_go<D, 3, false, 2, true>(a, gt, B, s);
-      case 4: return decode_go<D, 4, false, 3, true>(a, gt, B, s);
+      case 2: return decode_go<D, 2, false, 1, true>(a, gt, B, stages, s);
+      case 3: return decode_go<D, 3, false, 2, true>(a, gt, B, stages, s);
+      case 4: return decode_go<D, 4, false, 3, true>(a, gt, B, stages, s);
     }
   } else if (kq && vq && kb == vb) {  // QKQV
     switch (kb) {
-      case 1: return decode_go<D, 1, true, 1, true>(a, gt, B, s);
-      case 2: return decode_go<D, 2, true, 2, true>(a, gt, B, s);
-      case 3: return decode_go<D, 3, true, 3, true>(a, gt, B, s);
+      case 1: return decode_go<D, 1, true, 1, true>(a, gt, B, stages, s);
+      case 2: return decode_go<D, 2, true, 2, true>(a, gt, B, stages, s);
+      case 3: return decode_go<D, 3, true, 3, true>(a, gt, B, stages, s);
     }
   }
   return hipErrorInvalidValue;
@@ -2870,7 +2872,7 @@ hipError_t launch_finish(const FinishArgs &a, bool vq, int rows, hipStream_t s) 
   template hipError_t launch_dequantize<D>(const DequantArgs &, int, int, bool, int,            \
                                            hipStream_t);                                        \
   template hipError_t launch_prep<D>(const PrepArgs &, int, bool, bool, hipStream_t);           \
-  template hipError_t launch_decode<D>(const DecodeArgs &, int, bool, int, bool, int, int,      \
+  template hipError_t launch_decode<D>(const DecodeArgs &, int, bool, int, bool, int, int, int, \
                                        hipStream_t);                                            \
   template hipError_t launch_window<D>(const WindowArgs &, bool, bool, int, hipStream_t);     \
   template hipError_t launch_prefill<D>(const PrefillArgs &, int, bool, int, bool, int,        \

@@ -28,6 +28,7 @@ EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_
            "kvq_rotation_signs", "kvq_rotation_qr", "kvq_cache_layout", "kvq_quantize_k",
            "kvq_quantize_v", "kvq_dequantize", "kvq_decode_attention",
            "kvq_decode_attention_window", "kvq_decode_attention_noalloc",
+           "kvq_decode_attention_stages", "kvq_probe_stream_read",
            "kvq_decode_workspace", "kvq_decode_auto_splits",
            "kvq_prefill_attention", "kvq_prefill_workspace", "kvq_status_str", "kvq_version"]
 
@@ -85,6 +86,9 @@ def lib():
             "kvq_decode_attention_window": ([cache_p, vp, i32, i32, i32, i32, vp, vp, i32, i32,
                                              i32, vp, vp, sz, vp], i32),
             "kvq_decode_attention_noalloc": ([cache_p, vp, i32, i32, i32, i32, vp, vp], i32),
+            "kvq_decode_attention_stages": ([cache_p, vp, i32, i32, i32, i32, i32, vp, vp, sz, vp],
+                                            i32),
+            "kvq_probe_stream_read": ([vp, sz, vp, vp], i32),
             "kvq_decode_workspace": ([cache_p, i32, i32, i32, C.POINTER(sz)], i32),
             "kvq_decode_auto_splits": ([cache_p, i32, i32], i32),
             "kvq_prefill_attention": ([cache_p, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp],
@@ -207,6 +211,21 @@ def kvq_decode_attention_noalloc(c: kvq_cache, q: int, q_dtype: int, q_heads: in
                                               out, stream), "kvq_decode_attention_noalloc")
 
 
+KVQ_STAGE_PREP, KVQ_STAGE_SCAN, KVQ_STAGE_MERGE, KVQ_STAGE_ALL = 1, 2, 4, 7
+
+
+def kvq_decode_attention_stages(c: kvq_cache, q: int, q_dtype: int, q_heads: int, n_ctx: int,
+                                splits: int, stages: int, out: int, workspace: int, ws_bytes: int,
+                                stream: int = 0):
+    _check(lib().kvq_decode_attention_stages(C.byref(c), q, q_dtype, q_heads, n_ctx, splits, stages,
+                                             out, workspace, ws_bytes, stream),
+           "kvq_decode_attention_stages")
+
+
+def kvq_probe_stream_read(buf: int, nbytes: int, out: int, stream: int = 0):
+    _check(lib().kvq_probe_stream_read(buf, nbytes, out, stream), "kvq_probe_stream_read")
+
+
 def kvq_prefill_workspace(c: kvq_cache, q_heads: int, n_q: int) -> int:
     n = C.c_size_t()
     _check(lib().kvq_prefill_workspace(C.byref(c), q_heads, n_q, C.byref(n)),
@@ -316,7 +335,10 @@ class KVQCache:
     def workspace_bytes(self, q_heads: int, n_ctx: int, splits: int = 0) -> int:
         return kvq_decode_workspace(self.c, q_heads, n_ctx, splits)
 
-    def decode_attention(self, q, n_ctx: int, splits: int = 0, out=None, workspace=None):
+    def decode_attention(self, q, n_ctx: int, splits: int = 0, out=None, workspace=None,
+                         stages: int = KVQ_STAGE_ALL):
+        """Decode over cache slots [0, n_ctx); stages (KVQ_STAGE_* mask) runs only
+        those stages (the workspace carries the intermediate results)."""
         torch = self.torch
         if q.dim() != 3 or q.shape[0] != self.batch or q.shape[2] != self.d or not q.is_contiguous():
             raise ValueError("q must be a contiguous [B][q_heads][d] tensor")
@@ -329,8 +351,13 @@ class KVQCache:
             workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
         if out is None:
             out = torch.empty(self.batch, Hq, self.d, dtype=torch.float32, device=self.device)
-        kvq_decode_attention(self.c, q.data_ptr(), dt, Hq, n_ctx, splits, out.data_ptr(),
-                             workspace.data_ptr(), workspace.numel(), self._stream())
+        if stages == KVQ_STAGE_ALL:
+            kvq_decode_attention(self.c, q.data_ptr(), dt, Hq, n_ctx, splits, out.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), self._stream())
+        else:
+            kvq_decode_attention_stages(self.c, q.data_ptr(), dt, Hq, n_ctx, splits, stages,
+                                        out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        self._stream())
         return out
 
     def prefill_attention(self, q, q_pos0: int, n_ctx: int, causal: bool = True, out=None,

@@ -407,3 +407,32 @@ def test_prefill_token_splits(scheme, n, causal):
     for p0 in (0, 700, N - nq):
         got = P.gpu.prefill_attention(q.cuda(), p0, N, causal=causal).cpu().numpy()
         assert rel_rows(got, P.prefill(q, p0, causal, N)).max() < 1e-5, p0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_stages_equal_one_call(d):
+    """Prep, scan and merge launched by three staged calls give the one-call
+    result bit for bit (same kernels, same workspace)."""
+    from kv_cache_quantization_kqv_amd import kvq as _kvq
+    print(f"case decode-stages d={d}", flush=True)
+    B, Hkv, G, N = 2, 2, 4, 500
+    P = Pair("KQV", 4, d, B, Hkv, N)
+    K, V = _inputs(B, Hkv, N, d, torch.bfloat16, 1500 + d, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, Hkv * G, d), 1501 + d, torch.bfloat16).cuda()
+    ws = torch.zeros(P.gpu.workspace_bytes(Hkv * G, N, 3), dtype=torch.uint8, device="cuda")
+    a = P.gpu.decode_attention(q, N, splits=3, workspace=ws).clone()
+    out = torch.full_like(a, float("nan"))
+    for st in (_kvq.KVQ_STAGE_PREP, _kvq.KVQ_STAGE_SCAN, _kvq.KVQ_STAGE_MERGE):
+        P.gpu.decode_attention(q, N, splits=3, out=out, workspace=ws, stages=st)
+    assert torch.equal(a, out)
+
+
+def test_stream_read_probe_runs():
+    from kv_cache_quantization_kqv_amd import kvq as _kvq
+    buf = torch.ones(1 << 22, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    _kvq.kvq_probe_stream_read(buf.data_ptr(), buf.numel(), out.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+

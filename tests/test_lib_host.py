@@ -431,3 +431,23 @@ def test_prefill_splits_fill_the_gpu(K):
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)  # GQA chunk: 2048 blocks, 1 split
     assert lib.kvq_prefill_workspace(C.byref(c), 32, 256, C.byref(ws)) == 0
     assert ws.value == 4 * 16 * 32 * 256 * (128 + 1 * (2 + 256))
+
+
+def test_decode_stages_and_probe_validation(K):
+    """Bad stage masks and bad probe arguments fail before any launch."""
+    lib = K.lib()
+    c = _fake_cache(K, d=128, B=1, H=2, cap=64)
+    p = C.byref(c)
+    ws = C.c_size_t()
+    assert lib.kvq_decode_workspace(p, 8, 64, 0, C.byref(ws)) == 0
+    q, out, w = 0xA00000, 0xB00000, 0xC00000
+    for mask in (0, 8, -1):
+        assert lib.kvq_decode_attention_stages(p, q, 1, 8, 64, 0, mask, out, w, ws.value, None) == 10
+    assert lib.kvq_decode_attention_stages(p, q, 1, 8, 0, 0, 7, out, w, ws.value, None) == 10
+    assert lib.kvq_decode_attention_stages(None, q, 1, 8, 64, 0, 7, out, w, ws.value, None) == 1
+    assert lib.kvq_probe_stream_read(None, 64, out, None) == 1
+    assert lib.kvq_probe_stream_read(q, 64, None, None) == 1
+    assert lib.kvq_probe_stream_read(q + 4, 64, out, None) == 2
+    assert lib.kvq_probe_stream_read(q, 40, out, None) == 10
+    assert lib.kvq_probe_stream_read(q, 0, out, None) == 10
+
