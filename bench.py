@@ -384,7 +384,7 @@ def kernel_source_digest():
 
 
 def read_traffic(path, scheme, n_bits, workload):
-    """Measured HBM bytes per decode launch from a profile summary's json block;
+    """Measured HBM bytes per scan launch from a profile summary's json block;
     None unless it was taken on this workload and on the current sources."""
     text = open(path).read()
     if "```json" not in text:
@@ -394,7 +394,7 @@ def read_traffic(path, scheme, n_bits, workload):
         return None
     if blk.get("source_sha256") != kernel_source_digest():
         return None
-    return blk.get("decode_bytes_per_launch")
+    return blk.get("scan_bytes_per_launch")
 
 
 def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_param=None):
