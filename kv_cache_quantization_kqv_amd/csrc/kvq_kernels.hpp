@@ -384,8 +384,8 @@ __device__ __forceinline__ float sketch_row_norm_max(const unsigned char *S_s, i
 namespace kvq {
 
 // Rows rlo <= t < nvalid of the tile are tokens; their sign records go to
-// signs_out at slot0 + t, or (TO_LDS, d = 128) to srows + 16 t in LDS.
-template <int D, int NRT, bool TO_LDS = false>
+// signs_out at slot0 + t, or (TO_LDS, d = 128) to srows + SP t in LDS.
+template <int D, int NRT, bool TO_LDS = false, int SP = 16>
 __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const unsigned char *S_s,
                                              const float *rn_s, float a_snmax, int rlo, int nvalid,
                                              size_t slot0, uint8_t *signs_out, uint8_t *srows,
@@ -499,7 +499,7 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
     const bool tvalid = t >= rlo && t < nvalid && lane < 32;
     if constexpr (TO_LDS) {
       static_assert(D == 128, "LDS sign rows exist at d = 128 only");
-      if (lane < 32) *(u32x4 *)(srows + 16 * t) = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
+      if (lane < 32) *(u32x4 *)(srows + SP * t) = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
     } else if (tvalid) {
       const size_t tslot = slot0 + (size_t)t;
       uint8_t *dst = signs_out + tslot * (D / 8);
@@ -559,8 +559,10 @@ void quantize_kernel(const QuantArgs a) {
   __shared__ BucketTables<BITS> bt;
   __shared__ float rn_all[4][VT];
   static_assert(!VG || D == 128, "token groups exist at d = 128 only");
-  __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * RECB : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t srow_all[4][VG && QJL ? VT * 16 : 16];
+  // VG: once the stage's residual rows are consumed, row t of the stage (pitch
+  // P2) holds slot t's per-slot code record in bytes [0, RECB) and its sign
+  // record in the row's padding, bytes [2D, 2D + 16)
+  static_assert(!VG || (RECB <= 2 * D && VT * P2 <= VT * PITCH), "group rows must fit the stage");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   unsigned char *stage = stage_all[wave];
@@ -701,20 +703,11 @@ void quantize_kernel(const QuantArgs a) {
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vrow);
     uint32_t rec[RECW];
     if constexpr (VG) {
-      // each lane writes its half of the slot's record (per-slot layout) to
-      // the LDS row (offset made opaque so it is not hoisted out of the tile
-      // loop: register pressure); vg_emit_codes regroups the rows
-      using LCT = LocalCodes<DL, BITS>;
-      int off = vrow * RECB;
-      asm volatile("" : "+v"(off));
-      uint8_t *nr = vrow_all[wave] + off;
-      if constexpr (BITS == 3) {
-        *(u32x4 *)(nr + 16 * half) = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
-        *(u32x2 *)(nr + D / 4 + 8 * half) = u32x2{lc.w[LCT::NA], lc.w[LCT::NA + 1]};
-      } else {
+      // the record halves stay in lc until the stage is free (below); packed
+      // here, or the compiler defers the packing and keeps every code live
 #pragma unroll
-        for (int k = 0; k < LCT::NA; ++k) *(uint32_t *)(nr + half * (DL * BITS / 8) + 4 * k) = lc.w[k];
-      }
+      for (int k = 0; k < LocalCodes<DL, BITS>::NA + LocalCodes<DL, BITS>::NB; ++k)
+        asm volatile("" : "+v"(lc.w[k]));
     } else if constexpr (LPV == 2) {
       // each lane packed its own half; the lower lane joins the two images
       LocalCodes<DL, BITS> oth;
@@ -765,23 +758,39 @@ void quantize_kernel(const QuantArgs a) {
       if (next < a.total_tiles) fetch(next);
       wave_sync();
 
-      sketch_signs<D, NRT, VG>(stage, S_s, rn_s, a_snmax, rlo, nvalid,
-                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
-                               srow_all[wave], lane);
+      // VG: the sign records go to the residual rows' padding
+      sketch_signs<D, NRT, VG, P2>(stage, S_s, rn_s, a_snmax, rlo, nvalid,
+                                   (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
+                                   stage + 2 * D, lane);
     }
-    wave_sync();
-    if (next < a.total_tiles) stash();
     wave_sync();
     if constexpr (VG) {
-      // after the stash, so the next tile's prefetch registers are free (the
-      // scheduling barriers keep its work from moving into earlier phases)
+      // (the scheduling barriers keep the emission's work from moving into
+      // the earlier phases: register pressure)
       __builtin_amdgcn_sched_barrier(0);
+      // each lane writes its half of the slot's record (per-slot layout) to
+      // the slot's stage row (offset made opaque so it is not hoisted out of
+      // the tile loop: register pressure); vg_emit_codes regroups the rows
+      using LCT = LocalCodes<DL, BITS>;
+      int off = vrow * P2;
+      asm volatile("" : "+v"(off));
+      uint8_t *nr = stage + off;
+      if constexpr (BITS == 3) {
+        *(u32x4 *)(nr + 16 * half) = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
+        *(u32x2 *)(nr + D / 4 + 8 * half) = u32x2{lc.w[LCT::NA], lc.w[LCT::NA + 1]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < LCT::NA; ++k) *(uint32_t *)(nr + half * (DL * BITS / 8) + 4 * k) = lc.w[k];
+      }
+      wave_sync();
       const size_t slot0 = (size_t)bh * a.cap + (size_t)(a.t0 + tbase);
-      vg_emit_codes<BITS, VT>(vrow_all[wave], rlo, nvalid, a.codes + slot0 * RECB, lane);
-      if constexpr (QJL) vg_emit_signs<VT>(srow_all[wave], rlo, nvalid, a.signs + slot0 * 16, lane);
-      wave_sync();   // the rows are rewritten by the next tile
+      vg_emit_codes<BITS, VT, P2>(stage, rlo, nvalid, a.codes + slot0 * RECB, lane);
+      if constexpr (QJL) vg_emit_signs<VT, P2>(stage + 2 * D, rlo, nvalid, a.signs + slot0 * 16, lane);
+      wave_sync();   // the stage takes the next tile
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (next < a.total_tiles) stash();
+    wave_sync();
   }
 }
 

@@ -148,10 +148,10 @@ __device__ __forceinline__ uint32_t vg_row_nibbles(const uint8_t *row, int n) {
 }
 
 // Emit the code groups of one wave tile of VT slots (tile start a multiple of
-// VT, so of 4): rows = LDS per-slot records (16 VB bytes each) of the tile;
-// slots with rlo <= row < rhi are written, the others keep their stored bits.
-// dst = the value codes at the tile's first slot.
-template <int VB, int VT>
+// VT, so of 4): rows = LDS per-slot records (16 VB bytes each, RP bytes
+// apart) of the tile; slots with rlo <= row < rhi are written, the others keep
+// their stored bits.  dst = the value codes at the tile's first slot.
+template <int VB, int VT, int RP = 16 * VB>
 __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int rhi, uint8_t *dst,
                                               int lane) {
   constexpr int PB = 4 * VB, QB = 64 * VB;
@@ -170,7 +170,7 @@ __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int 
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * qd + r;
       const bool ok = row >= rlo && row < rhi;
-      N[r] = vg_row_nibbles<VB>(rows + row * (16 * VB), n);
+      N[r] = vg_row_nibbles<VB>(rows + row * RP, n);
       V[r] = ok ? NM : 0u;
       nv += ok ? 1 : 0;
     }
@@ -197,9 +197,9 @@ __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int 
 }
 
 // Emit the sign groups of one wave tile of VT slots: srows = LDS sign records
-// (16 bytes per slot, row k at byte k / 8 bit k % 8).  dst = the value signs at
-// the tile's first slot.
-template <int VT>
+// (16 bytes per slot, SP bytes apart; row k at byte k / 8 bit k % 8).  dst =
+// the value signs at the tile's first slot.
+template <int VT, int SP = 16>
 __device__ __forceinline__ void vg_emit_signs(const uint8_t *srows, int rlo, int rhi, uint8_t *dst,
                                               int lane) {
   asm volatile("" : "+v"(lane));   // as in vg_emit_codes
@@ -212,7 +212,7 @@ __device__ __forceinline__ void vg_emit_signs(const uint8_t *srows, int rlo, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = 8 * o + e;
-      const uint32_t by = srows[row * 16 + n];
+      const uint32_t by = srows[row * SP + n];
       if (e < 4) lo |= by << (8 * e);
       else hi |= by << (8 * (e - 4));
       vm |= (row >= rlo && row < rhi ? 1u : 0u) << e;
