@@ -346,15 +346,15 @@ long long min_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   return ((long long)n_ctx + tmax - 1) / tmax;
 }
 
-// Vector-unit scan: about KVQ_SCAN_BLOCKS blocks, the split length rounded up
+// Vector-unit scan: about kvq::kScanBlocks blocks, the split length rounded up
 // to whole 256-token rounds (at least 256) and within the LDS logit buffer.
 // Matrix-core scan (workers take interleaved 64-token chunks): about
-// KVQ_SCAN_BLOCKS_MFMA blocks, at most one chunk per worker (4 per split).
+// kvq::kScanBlocksMfma blocks, at most one chunk per worker (4 per split).
 int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   const int G = q_heads / c->kv_heads;
   const int HG = G / heads_per_block(G);
   const long long units = (long long)c->batch * c->kv_heads * HG;
-  const long long target = scan_mfma(c) ? KVQ_SCAN_BLOCKS_MFMA : KVQ_SCAN_BLOCKS;
+  const long long target = scan_mfma(c) ? kvq::kScanBlocksMfma : kvq::kScanBlocks;
   const long long want = (target + units - 1) / units;
   if (n_ctx <= 0) return 1;
   if (scan_mfma(c)) {

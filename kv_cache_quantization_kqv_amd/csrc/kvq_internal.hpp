@@ -6,25 +6,18 @@
 
 #include "../../include/kvq.h"
 
-// Logits and weights of one decode split stay in LDS: 2 floats per (token,
-// query head of the block), so a split holds at most KVQ_SCAN_WBUF_FLOATS/(2 GT)
-// tokens.
-#ifndef KVQ_SCAN_WBUF_FLOATS
-#define KVQ_SCAN_WBUF_FLOATS 10240
-#endif
-
 namespace kvq {
 
-inline int scan_tokens_max(int gt) { return KVQ_SCAN_WBUF_FLOATS / (2 * gt); }
+// Vector-unit scan (d < 128): the logits and weights of one decode split stay
+// in LDS, 2 floats per (token, query head of the block), so a split holds at
+// most kScanWbufFloats / (2 GT) tokens.
+constexpr int kScanWbufFloats = 10240;
+inline int scan_tokens_max(int gt) { return kScanWbufFloats / (2 * gt); }
 
-// Target block count of the automatic decode split choice (vector-unit scan,
-// matrix-core scan).
-#ifndef KVQ_SCAN_BLOCKS
-#define KVQ_SCAN_BLOCKS 4096
-#endif
-#ifndef KVQ_SCAN_BLOCKS_MFMA
-#define KVQ_SCAN_BLOCKS_MFMA 1024
-#endif
+// Target block count of the automatic decode split choice: vector-unit scan;
+// matrix-core scan (two rounds of three resident blocks on each of 256 CUs).
+constexpr long long kScanBlocks = 4096;
+constexpr long long kScanBlocksMfma = 1536;
 
 // Rotation applied by the codec (kernel template / argument code):
 // none, Walsh-Hadamard, randomized Hadamard (signs, then WHT), dense Q.

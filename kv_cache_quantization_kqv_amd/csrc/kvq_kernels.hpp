@@ -13,11 +13,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kvq_internal.hpp"
+#include <map>
+#include <mutex>
+#include <utility>
 
-#ifndef KVQ_DECODE_E4
-#define KVQ_DECODE_E4 8  // coordinates per lane when four query heads share a KV head
-#endif
+#include "kvq_internal.hpp"
 
 namespace kvq {
 
@@ -181,12 +181,12 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 // equals #{thresholds < u} (ties go to the lower cell; -0 and +0 against the
 // zero threshold compare as IEEE floats do).
 // ---------------------------------------------------------------------------
-#ifndef KVQ_BUCKETIZE_CMP_MAXBITS
-#define KVQ_BUCKETIZE_CMP_MAXBITS 2
-#endif
+// Codes of at most kCmpMaxBits bits are found by compares against the
+// thresholds; wider ones through the cell table.
+constexpr int kCmpMaxBits = 2;
 template <int BITS>
 struct BucketTables {
-  static constexpr bool LUT = BITS > KVQ_BUCKETIZE_CMP_MAXBITS;
+  static constexpr bool LUT = BITS > kCmpMaxBits;
   static constexpr int MB = BITS >= 4 ? 2 : 1;       // mantissa bits of the cell prefix
   static constexpr int SHIFT = 23 - MB;
   static constexpr int NCELL = 1 << (9 + MB);
@@ -245,7 +245,7 @@ __device__ __forceinline__ uint32_t bucketize_cmp(float u, const float *thr) {
 
 template <int BITS>
 __device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables<BITS> &bt, const float *thr) {
-  if constexpr (BITS <= KVQ_BUCKETIZE_CMP_MAXBITS) return bucketize_cmp<BITS>(u, thr);
+  if constexpr (BITS <= kCmpMaxBits) return bucketize_cmp<BITS>(u, thr);
   else return bucketize_lut<BITS>(u, bt);
 }
 
@@ -1414,18 +1414,6 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, flo
   }
 }
 
-#ifndef KVQ_SCAN_PD
-#define KVQ_SCAN_PD 2   // value tiles in flight (registers) ahead of the one in LDS
-#endif
-#ifndef KVQ_SCAN_WPF
-#define KVQ_SCAN_WPF 4  // wave-private value slices in flight (registers)
-#endif
-
-// Three blocks per CU (LDS allows three at about 52 KB each): registers <= 168.
-#ifndef KVQ_SCAN_WAVES_PER_EU
-#define KVQ_SCAN_WAVES_PER_EU 3
-#endif
-#define KVQ_SCAN_OCC __attribute__((amdgpu_waves_per_eu(KVQ_SCAN_WAVES_PER_EU)))
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
@@ -1440,66 +1428,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   merge_splits<D, VQ, 1>(a, sm, mx, b, hq);
 }
 
-// Key scores on the matrix cores (4-bit keys, d = 128, four query heads per
-// block).  A wave scores 16 tokens per step with v_mfma_f32_16x16x32_f16:
-// row = token (lane % 16), 32 K slots (lane group g = lane / 16 holds 8 of
-// them), column = output column.  fp16 carries 11 significant bits, so both
-// operands are split: C = Ch + 2^-11 Cl (one pair-table entry holds the fp16
-// pair Ch and the fp16 pair Cl of two coordinates) and q' 2^k = qh + 2^-11 ql,
-// with k a per-head power of two that keeps q' 2^k inside fp16's range.
-// Column h < 4 collects sum Ch qh of head h, column 7 - h the sum
-// (Ch ql + Cl qh); the dropped Cl ql term is 2^-22 relative, so a score
-// carries about fp32 precision.  Lane group g covers coordinates
-// [32 g, 32 g + 32): step j (0..7) takes the code bytes 2j and 2j + 1, i.e.
-// coordinates 32 g + 4 j + {0, 1, 2, 3}, in the slot order
-// (Ch, Ch, Cl, Cl) of the first pair, then of the second.
-#ifndef KVQ_SCAN_MFMA_KEYS
-#define KVQ_SCAN_MFMA_KEYS 1
-#endif
-template <int D, int KB, bool KQ, int GT>
-struct MfmaKeys {
-  static constexpr bool on = KVQ_SCAN_MFMA_KEYS && D == 128 && KB == 4 && !KQ && GT == 4;
-};
-
-// B operands of lane (n = lane % 16, g = lane / 16) for the eight steps, from
-// the prepared query qv ([coordinate][4 heads]).  Column n serves head n
-// (n < 4) or head 7 - n (4 <= n < 8); other columns are zero.  `unscale` =
-// 2^-k of the lane's head.
-__device__ __forceinline__ void mfma_key_operands(const float *qv, int lane, f16x8 (&bq)[8],
-                                                  float &unscale) {
-  const int n = lane & 15, g = lane >> 4, h = n < 4 ? n : 7 - (n & 7);
-  float v[32];
-  float m = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    v[c] = qv[(32 * g + c) * 4 + (h & 3)];
-    m = fmaxf(m, fabsf(v[c]));
-  }
-  m = fmaxf(m, __shfl_xor(m, 16, 64));
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
-  int ex = 0;
-  const bool fin = m > 0.0f && m <= 3.0e38f;
-  if (fin) (void)frexpf(m, &ex);                      // m < 2^ex
-  const int k = fin ? 14 - ex : 0;
-  unscale = ldexpf(1.0f, -k);
-  const _Float16 z = (_Float16)0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 4 * j + 2 * (e >> 2) + (e & 1);
-      const bool lo_slot = (e & 2) != 0;
-      const float x = ldexpf(v[c], k);
-      const _Float16 hi = (_Float16)x;
-      const _Float16 lo = (_Float16)((x - (float)hi) * 2048.0f);
-      bq[j][e] = n < 4 ? (lo_slot ? z : hi) : (n < 8 ? (lo_slot ? hi : lo) : z);
-    }
-}
-
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
-__global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeArgs a) {
-  constexpr bool MFA = MfmaKeys<D, KB, KQ, GT>::on;  // key scores on the matrix cores
-  constexpr int E = (GT >= 4 && D >= 16) ? KVQ_DECODE_E4 : 16;  // value coordinates per lane
+// (three blocks per CU: registers <= 168)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(
+    const DecodeArgs a) {
+  constexpr int E = GT >= 4 ? 8 : 16;               // value coordinates per lane
   constexpr int L = D / E;                           // lanes sharing a token group in phase C
   constexpr int GPW = 64 / L;                        // token groups per wave
   constexpr int TG = 4;                              // tokens per group
@@ -1507,7 +1440,7 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   constexpr int NWA = TT / (GPW * TG);               // waves that own groups of a tile
   constexpr int NGT = TT / TG;                       // groups per tile
   constexpr int NS = 2 + 2 * D;
-  constexpr int TPS_MAX = KVQ_SCAN_WBUF_FLOATS / (2 * GT);
+  constexpr int TPS_MAX = kScanWbufFloats / (2 * GT);
   constexpr int KBYTES = D * KB / 8, KW = (KBYTES + 3) / 4;
   constexpr int SBYTES = D / 8, SW = (SBYTES + 3) / 4;
   constexpr int NPAIR = 1 << (2 * VB);
@@ -1518,10 +1451,10 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   constexpr int EPI = GT * NS;                       // epilogue floats (reuses wbuf)
   static_assert(TPS_MAX % TT == 0, "split budget must be whole tiles");
   static_assert(NWA >= 1 && NWA <= 4 && E % 8 == 0, "phase C mapping");
-  static_assert(EPI <= KVQ_SCAN_WBUF_FLOATS, "epilogue staging must fit the logit buffer");
-  static_assert(GT * (256 + NS) <= KVQ_SCAN_WBUF_FLOATS, "merge staging must fit the logit buffer");
+  static_assert(EPI <= kScanWbufFloats, "epilogue staging must fit the logit buffer");
+  static_assert(GT * (256 + NS) <= kScanWbufFloats, "merge staging must fit the logit buffer");
 
-  __shared__ __attribute__((aligned(16))) float wbuf[KVQ_SCAN_WBUF_FLOATS];
+  __shared__ __attribute__((aligned(16))) float wbuf[kScanWbufFloats];
   __shared__ __attribute__((aligned(16))) uint8_t tile[TL::BYTES];
   // sign tables of the tile's token groups: for group g and 4-bit mask m,
   // sum_i (2 m_i - 1) cq[4g + i] per head
@@ -1540,20 +1473,7 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   for (int p = tid; p < KPAIR; p += 256) {
     int ca, cb;
     pair_codes<KB>(p, ca, cb);
-    if constexpr (MFA) {
-      // fp16 pair (Ch[a], Ch[b]) and pair of scaled remainders 2^11 (C - Ch)
-      const float xa = a.kcent[ca], xb = a.kcent[cb];
-      const _Float16 ha = (_Float16)xa, hb = (_Float16)xb;
-      const _Float16 la = (_Float16)((xa - (float)ha) * 2048.0f);
-      const _Float16 lb = (_Float16)((xb - (float)hb) * 2048.0f);
-      const uint32_t hw = (uint32_t)__builtin_bit_cast(uint16_t, ha) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-      const uint32_t lw = (uint32_t)__builtin_bit_cast(uint16_t, la) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
-      kp_s[p] = f32x2{__uint_as_float(hw), __uint_as_float(lw)};
-    } else {
-      kp_s[p] = f32x2{a.kcent[ca], a.kcent[cb]};
-    }
+    kp_s[p] = f32x2{a.kcent[ca], a.kcent[cb]};
   }
   for (int p = tid; p < NPAIR; p += 256) {
     int ca, cb;
@@ -1572,9 +1492,9 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
   __syncthreads();
 
   // value tiles: thread tid copies 16-byte chunks tid + 256k of each tile;
-  // KVQ_SCAN_PD tiles are in flight in registers (the first ones requested
-  // before phase A, so they arrive while the keys are scored)
-  constexpr int PD = KVQ_SCAN_PD;
+  // PD tiles are in flight in registers (the first ones requested before
+  // phase A, so they arrive while the keys are scored)
+  constexpr int PD = 2;
   const int nround = (nloc + TT - 1) / TT * TT;
   const int ntiles = nround / TT;
   const uint8_t *cbase[NPT];
@@ -1614,34 +1534,8 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     for (int k = 0; k < NPT; ++k)
       if (cbase[k]) *(u32x4 *)(tile + (tid + 256 * k) * 16) = src[k];
   };
-  // Wave-private value slices (d = 128, one 16-byte piece per lane): wave w
-  // takes tokens [16 w, 16 w + 16) of every 64-token tile itself, with
-  // KVQ_SCAN_WPF slices in flight, so phase C needs no block barrier.
-  using TW = VTile<D, VB, VQ, 16>;
-  constexpr bool WPC = D == 128 && E == 8 && TT == 64 && TW::BYTES == 1024;
-  constexpr int WPF = WPC ? KVQ_SCAN_WPF : 1;
-  u32x4 pw[WPF];
-  auto wfetch = [&](int it, u32x4 &dst) {
-    dst = u32x4{0u, 0u, 0u, 0u};
-    if (it < ntiles) {
-      const int tb = it * TT + 16 * wave;                  // first token of the slice
-      const int byte = lane * 16;
-      if (byte < TW::VS) {
-        if (tb + byte / TW::VREC < nloc)
-          dst = __builtin_nontemporal_load((const u32x4 *)(a.vc + (rec0 + tb) * TW::VREC + byte));
-      } else if constexpr (VQ) {
-        if (tb + (byte - TW::VS) / TW::SREC < nloc)
-          dst = __builtin_nontemporal_load((const u32x4 *)(a.vs + (rec0 + tb) * TW::SREC + byte - TW::VS));
-      }
-    }
-  };
-  if constexpr (WPC) {
 #pragma unroll
-    for (int j = 0; j < WPF; ++j) wfetch(j, pw[j]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < PD; ++j) fetch(j, pf[j]);
-  }
+  for (int j = 0; j < PD; ++j) fetch(j, pf[j]);
 
   // ---- phase A: logits, one token per lane -------------------------------
   cfloat *qc = (cfloat *)(a.qt + unitg * D * GT);
@@ -1656,80 +1550,6 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) mx[hh] = -INFINITY;
 
-  if constexpr (MFA) {
-    // Lane (n, g) loads bytes [16 g, 16 g + 16) of the records of tokens
-    // base + 16 blk + n (blk < 4); lane l loads the norms of token base + l.
-    const int n = lane & 15, g = lane >> 4;
-    f16x8 bq[8];
-    float unscale;
-    mfma_key_operands((const float *)(a.qt + unitg * D * GT), lane, bq, unscale);
-    u32x4 kw4[4];
-    uint32_t kn2 = 0u, vnr2 = 0u;
-    auto kload4 = [&](int base, u32x4 (&w)[4], uint32_t &nkb, uint32_t &vv) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const int tl = base + 16 * blk + n;
-        w[blk] = tl < nloc ? *(const u32x4 *)(kc_p + (size_t)tl * KBYTES + 16 * g) : u32x4{0u, 0u, 0u, 0u};
-      }
-      const int tl = base + lane;
-      if (tl < nloc) {
-        nkb = __builtin_nontemporal_load(kn_p + tl);
-        vv = (uint32_t)__builtin_nontemporal_load(vn_p + tl) |
-             (VQ ? (uint32_t)__builtin_nontemporal_load(vr_p + tl) << 16 : 0u);
-      } else {
-        nkb = 0u;
-        vv = 0u;
-      }
-    };
-    kload4(wave * 64, kw4, kn2, vnr2);
-    for (int base = wave * 64; base < nloc; base += 256) {
-      u32x4 nw4[4];
-      uint32_t nkn, nvv;
-      kload4(base + 256, nw4, nkn, nvv);   // prefetch the next round
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        f32x4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t w = kw4[blk][j >> 1] >> (16 * (j & 1));
-          const f32x2 t0 = kp_s[w & 255u], t1 = kp_s[(w >> 8) & 255u];
-          const u32x4 av = {__float_as_uint(t0.x), __float_as_uint(t0.y), __float_as_uint(t1.x),
-                            __float_as_uint(t1.y)};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), bq[j], acc, 0, 0, 0);
-        }
-        // acc[r] = column n of token row 4 g + r; column 7 - h holds the
-        // remainder sum of head h (row_half_mirror: lane i <- lane 7 - i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float lo = __int_as_float(
-              __builtin_amdgcn_update_dpp(0, __float_as_int(acc[r]), 0x141, 0xF, 0xF, false));
-          const int tl = base + 16 * blk + 4 * g + r;
-          if (n < 4 && tl < nloc) wc[tl * GT + n] = fmaf(lo, 1.0f / 2048.0f, acc[r]) * unscale;
-        }
-      }
-      const int tl = base + lane;
-      if (tl < nloc) *(u32x2 *)(wq + tl * GT) = u32x2{vnr2, kn2};
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) kw4[blk] = nw4[blk];
-      kn2 = nkn;
-      vnr2 = nvv;
-    }
-    // scale by the key norms; the split's max per head
-    __syncthreads();
-    for (int tl = tid; tl < nloc; tl += 256) {
-      const float nkf = f16_bits_to_f32((uint16_t)(*(const uint32_t *)(wq + tl * GT + 1) & 0xFFFFu));
-      float4 s4 = *(const float4 *)(wc + tl * GT);
-      s4.x *= nkf;
-      s4.y *= nkf;
-      s4.z *= nkf;
-      s4.w *= nkf;
-      *(float4 *)(wc + tl * GT) = s4;
-      mx[0] = fmaxf(mx[0], s4.x);
-      mx[1] = fmaxf(mx[1], s4.y);
-      mx[2] = fmaxf(mx[2], s4.z);
-      mx[3] = fmaxf(mx[3], s4.w);
-    }
-  } else {
   uint32_t kw[KW], ksw[SW];
   float nk = 0.0f, rk = 0.0f;
   uint32_t vnr = 0u;   // fp16 bits of the value norm (low) and residual norm (high)
@@ -1806,7 +1626,6 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     rk = nrk;
     vnr = nvnr;
   }
-  }  // key scores on the vector units
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
     const float m = wave_max(mx[hh]);
@@ -1930,63 +1749,6 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
     }
   };
   __syncthreads();   // weights of phase B are in LDS
-  if constexpr (WPC) {
-    uint8_t *wt = tile + wave * 1024;                     // this wave's slice in LDS
-    for (int it0 = 0; it0 < ntiles; it0 += WPF) {
-#pragma unroll
-      for (int j = 0; j < WPF; ++j) {
-        const int it = it0 + j;
-        if (it >= ntiles) break;
-        *(u32x4 *)(wt + lane * 16) = pw[j];
-        wfetch(it + WPF, pw[j]);
-        if constexpr (VQ) {
-          // sign table of group grp, mask lg (tokens past the split have cq = 0)
-          const float *cqp = wq + (it * TT + grp * TG) * GT;
-          float t4[GT];
-#pragma unroll
-          for (int hh = 0; hh < GT; ++hh) t4[hh] = 0.0f;
-#pragma unroll
-          for (int i = 0; i < TG; ++i) {
-            const float sg = ((lg >> i) & 1) ? 1.0f : -1.0f;
-#pragma unroll
-            for (int hh = 0; hh < GT; ++hh) t4[hh] = fmaf(sg, cqp[i * GT + hh], t4[hh]);
-          }
-          *(float4 *)(tbl + (grp * 16 + lg) * GT) = float4{t4[0], t4[1], t4[2], t4[3]};
-        }
-        wave_sync();
-        const int tr0 = grp * TG;
-        float c[TG][GT];
-#pragma unroll
-        for (int i = 0; i < TG; ++i) {
-          const float *wsrc = wc + (it * TT + tr0 + i) * GT;
-#pragma unroll
-          for (int hh = 0; hh < GT; ++hh) c[i][hh] = wsrc[hh];
-        }
-#pragma unroll
-        for (int i = 0; i < TG; ++i) {
-          uint32_t vw0, vw1;
-          lds_codes<D, VB, E>(wt + TW::VC + (4 * gs + i) * TW::VREC, lg, vw0, vw1);
-#pragma unroll
-          for (int p = 0; p < E / 2; ++p) {
-            const f32x2 cv = vp_s[pair_index<VB>(vw0, vw1, p)];
-#pragma unroll
-            for (int hh = 0; hh < GT; ++hh) {
-              o[hh][2 * p] = fmaf(c[i][hh], cv.x, o[hh][2 * p]);
-              o[hh][2 * p + 1] = fmaf(c[i][hh], cv.y, o[hh][2 * p + 1]);
-            }
-          }
-        }
-        if constexpr (VQ) {
-          const uint8_t *sb = wt + TW::VS + 4 * gs * TW::SREC;
-          uint32_t w = 0u;
-#pragma unroll
-          for (int i = 0; i < TG; ++i) w |= (uint32_t)sb[i * TW::SREC + lg] << (8 * i);
-          sign_terms(w, 0);
-        }
-        wave_sync();   // the slice area and the tables are rewritten next
-      }
-    }
-  } else {
   if constexpr (VQ) {
     if (ntiles > 0) build_tables(0);
   }
@@ -2045,7 +1807,6 @@ __global__ __launch_bounds__(256) KVQ_SCAN_OCC void decode_kernel(const DecodeAr
       }
     }
   }
-  }  // block-staged value tiles
 
   // ---- epilogue: sum token slots (lanes), then waves; L over threads -------
 #pragma unroll
@@ -2624,40 +2385,61 @@ namespace kvq {
 // Dispatchers (host).  Only the (bits, rotation, sketch) combinations that the
 // three schemes produce are instantiated.
 // ---------------------------------------------------------------------------
+// Blocks of 256 threads of kernel `kern` that the current device holds at
+// once (every CU at the kernel's occupancy); looked up once per kernel and
+// device.  0 when the runtime cannot tell.
+inline int resident_blocks(const void *kern) {
+  static std::mutex mu;
+  static std::map<std::pair<const void *, int>, int> known;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kern, dev);
+  const auto it = known.find(key);
+  if (it != known.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess)
+    return 0;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  known[key] = n;
+  return n;
+}
+
+// Persistent-style encoder launch: each wave walks tiles with a stride of
+// 4 * grid.  Encoders with a bucketize table run one round of resident
+// blocks, so each block builds its table once for many tiles; the others two.
+inline hipError_t launch_tiles(const void *kern, const QuantArgs &a, bool lut, hipStream_t s) {
+  const int want = (a.total_tiles + 3) / 4;
+  const int r = resident_blocks(kern);
+  const int cap = (r > 0 ? r : 256) * (lut ? 1 : 2);
+  const int grid = want < cap ? want : cap;
+  QuantArgs arg = a;
+  void *args[] = {&arg};
+  return hipLaunchKernel(kern, dim3(grid), dim3(256), args, 0, s);
+}
+
 template <int D, int BITS, int RK, bool QJL>
 hipError_t quantize_go(const QuantArgs &a, bool bf16, bool vg, hipStream_t s) {
-  // persistent-style grid: each wave walks tiles with a stride of 4 * grid
-  // (encoders with a bucketize table: one round of resident blocks, three per
-  // CU, or two with the sketch staged as well, so each block builds its table
-  // once for many tiles)
-  const int want = (a.total_tiles + 3) / 4;
-  const int gmax = BucketTables<BITS>::LUT ? (QJL ? 512 : 768) : 2048;
-  const int grid = want < gmax ? want : gmax;
+  constexpr bool LUT = BucketTables<BITS>::LUT;
   // value sides (token groups at d = 128): unrotated without sketch, or
   // rotated with sketch
   constexpr bool VGOK = D == 128 && ((RK == RK_NONE) != QJL);
   if (vg && !VGOK) return hipErrorInvalidValue;
-  auto go = [&](auto V) {
+  auto go = [&](auto V) -> hipError_t {
     constexpr bool VG = decltype(V)::value;
     if constexpr (RK == RK_QR) {
-      if (bf16)
-        hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, true, VG>), dim3(grid), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((quantize_dense_kernel<D, BITS, QJL, false, VG>), dim3(grid), dim3(256), 0, s, a);
+      if (bf16) return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, true, VG>, a, LUT, s);
+      return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, false, VG>, a, LUT, s);
     } else {
-      if (bf16)
-        hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, true, VG>), dim3(grid), dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((quantize_kernel<D, BITS, RK, QJL, false, VG>), dim3(grid), dim3(256), 0, s, a);
+      if (bf16) return launch_tiles((const void *)&quantize_kernel<D, BITS, RK, QJL, true, VG>, a, LUT, s);
+      return launch_tiles((const void *)&quantize_kernel<D, BITS, RK, QJL, false, VG>, a, LUT, s);
     }
   };
   if constexpr (VGOK) {
-    if (vg) go(std::true_type{});
-    else go(std::false_type{});
-  } else {
-    go(std::false_type{});
+    if (vg) return go(std::true_type{});
   }
-  return hipGetLastError();
+  return go(std::false_type{});
 }
 
 template <int D, int RK>

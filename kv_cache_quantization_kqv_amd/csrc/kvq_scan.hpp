@@ -96,11 +96,12 @@ struct ScanShape {
   static constexpr int KENT = KB == 4 ? 256 : KB == 3 ? 64 : KB == 2 ? 256 : 16;
   static constexpr int KTB = KENT * (KPAIR ? 4 : 8);
   static constexpr int KW = KB == 4 ? 4 : KB == 3 ? 3 : KB == 2 ? 2 : 1;   // key dwords per lane
-  // value operand table: token-pair index (VB 4, 3; a byte, the width-3 index
-  // in its low 6 bits, so the table repeats 4 times) -> 4 bytes, or token-quad
-  // index (VB 2: byte, VB 1: nibble) -> 8 bytes
+  // value operand table: token-pair index (VB 4: a byte, VB 3: 6 bits) -> 4
+  // bytes, or token-quad index (VB 2: byte, VB 1: nibble) -> 8 bytes.  (Small
+  // tables matter: random reads of a 64-entry table meet fewer LDS bank
+  // conflicts than those of a 256-entry one.)
   static constexpr bool VQUAD = VB <= 2;
-  static constexpr int VENT = VB == 1 ? 16 : 256;
+  static constexpr int VENT = VB == 1 ? 16 : VB == 3 ? 64 : 256;
   static constexpr int VTB = VENT * (VQUAD ? 8 : 4);
   static constexpr int PB = 4 * VB;                                         // value piece bytes per lane
   static constexpr bool SPIN = KQ || VQ;
@@ -227,8 +228,8 @@ __device__ __forceinline__ f16x8 key_operand(const uint32_t *k, int j, const uin
 template <int VB>
 __device__ __forceinline__ uint32_t value_field(const uint32_t *v, uint32_t h3, int u) {
   if constexpr (VB == 4) return (v[u >> 2] >> (8 * (u & 3))) & 255u;
-  if (u < 12) return (v[u >> 2] >> (8 * (u & 3))) & 255u;
-  return (h3 >> (8 * (u - 12))) & 255u;
+  if (u < 12) return (v[u >> 2] >> (8 * (u & 3))) & 63u;
+  return (h3 >> (8 * (u - 12))) & 63u;
 }
 
 template <int VB>
@@ -258,7 +259,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   constexpr int D = SS::D, NS = SS::NS;
   __shared__ __attribute__((aligned(16))) uint8_t kt_s[SS::KTB];
   __shared__ __attribute__((aligned(16))) uint8_t vt_s[SS::VTB];
-  __shared__ __attribute__((aligned(16))) u32x4 sp_s[SS::SPIN ? 256 : 1];
+  // nibble -> 4 fp16 spins (+1 where the bit is set, else -1), element e = bit e
+  __shared__ __attribute__((aligned(16))) u32x2 sp_s[SS::SPIN ? 16 : 1];
   // per wave: X = (ch, cl) and Z = (cqh, cql) of [block parity][head][token]
   __shared__ __attribute__((aligned(16))) uint32_t wx_s[4][2][4][16];
   __shared__ __attribute__((aligned(16))) uint32_t wz_s[4][2][4][16];
@@ -318,15 +320,19 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     else *(uint32_t *)(vt_s + 4 * p) = c(0) | (c(1) << 16);
   }
   if constexpr (SS::SPIN) {
-    // byte x -> 8 fp16 spins, element e = +1 when bit e is set, else -1
-    for (int p = tid; p < 256; p += 256) {
-      uint32_t w[4];
+    if (tid < 16) {
+      uint32_t w[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = (((p >> (2 * q)) & 1) ? 0x3C00u : 0xBC00u) | ((((p >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
-      sp_s[p] = u32x4{w[0], w[1], w[2], w[3]};
+      for (int q = 0; q < 2; ++q)
+        w[q] = (((tid >> (2 * q)) & 1) ? 0x3C00u : 0xBC00u) | ((((tid >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+      sp_s[tid] = u32x2{w[0], w[1]};
     }
   }
+  // the 8 spins of a sign byte (element e = bit e)
+  auto spins = [&](uint32_t x) {
+    const u32x2 lo = sp_s[x & 15u], hi = sp_s[(x >> 4) & 15u];
+    return op8(lo.x, lo.y, hi.x, hi.y);
+  };
 
   // ---- prepared query as the A operand of the score product -------------------
   // lane (row = 4 h + kind, g); step j slot e <-> coordinate 32 g + 8 j + e;
@@ -437,8 +443,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     if constexpr (KQ) {
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
-        const f16x8 sg0 = __builtin_bit_cast(f16x8, sp_s[(R.ks >> (8 * j)) & 255u]);
-        const f16x8 sg1 = __builtin_bit_cast(f16x8, sp_s[(R.ks >> (8 * j + 8)) & 255u]);
+        const f16x8 sg0 = spins(R.ks >> (8 * j));
+        const f16x8 sg1 = spins(R.ks >> (8 * j + 8));
         sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qs[j], sg0, sc0, 0, 0, 0);
         sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qs[j + 1], sg1, sc1, 0, 0, 0);
       }
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t x = ((j < 4 ? sg.x : sg.y) >> (8 * (j & 3))) & 255u;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, sp_s[x]), bz, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(spins(x), bz, acc[j], 0, 0, 0);
     }
   };
   // a pair of token blocks: scores of both, one running-max update, then the

@@ -48,6 +48,34 @@ def test_quantize_bit_exact(scheme, n, d, dtype):
     P.assert_bit_exact()
 
 
+# Encoders walk tiles in a persistent-style grid (one or two rounds of resident
+# blocks), so a wave takes a second tile only past 4 waves x 256 CUs x 3 blocks
+# (the most any encoder keeps resident) = 3072 tiles.  These inputs have 6400
+# tiles (32 or 64 tokens each) and so run the prefetch / stash loop over many
+# tiles per wave, for each input type, rotation and bucketize kind.
+MULTI_TILE = [("KQV", 4, 128, torch.bfloat16, "wht"), ("KQV", 4, 128, torch.float32, "wht"),
+              ("KQV", 4, 128, torch.bfloat16, "rht"), ("KQV", 4, 128, torch.float32, "qr"),
+              ("KV", 2, 128, torch.bfloat16, "wht"), ("KV", 4, 128, torch.float32, "wht"),
+              ("QKQV", 3, 128, torch.float32, "wht"), ("KQV", 4, 64, torch.float32, "wht"),
+              ("KQV", 2, 64, torch.bfloat16, "rht"), ("QKQV", 3, 64, torch.bfloat16, "qr"),
+              ("KV", 2, 64, torch.float32, "wht")]
+
+
+@pytest.mark.parametrize("scheme,n,d,dtype,rotation", MULTI_TILE,
+                         ids=[f"{s}{n}-d{d}-{'bf16' if t == torch.bfloat16 else 'f32'}-{r}"
+                              for s, n, d, t, r in MULTI_TILE])
+def test_quantize_bit_exact_many_tiles_per_wave(scheme, n, d, dtype, rotation):
+    vt = 32 if (d == 128 and rotation != "qr") else 64
+    B, H, t0 = 4, 8, 5
+    T = 6400 // 32 * vt - t0                      # 200 tiles per (batch row, head)
+    print(f"case quantize-many-tiles {scheme}{n} d={d} {dtype} {rotation} T={T}", flush=True)
+    P = Pair(scheme, n, d, B, H, T + t0 + 11, rotation=rotation)
+    K, V = _inputs(B, H, T, d, dtype, 2100 + d + n, heavy=(scheme != "KV"))
+    P.write(K, V, t0)
+    torch.cuda.synchronize()
+    P.assert_bit_exact()
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scheme,n", [("KV", 4), ("KQV", 4), ("KQV", 2), ("QKQV", 3)])
 def test_dequantize_matches_oracle(scheme, n, d):

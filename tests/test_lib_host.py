@@ -202,13 +202,13 @@ def test_validation_status_codes(K):
 
 def test_auto_splits_fill_the_gpu(K):
     """Head dimension 128 (matrix-core scan, interleaved 64-token chunks): about
-    1024 blocks, never more than one chunk per worker (4 workers per split).
+    1536 blocks, never more than one chunk per worker (4 workers per split).
     Smaller heads (vector-unit scan): about 4096 blocks, split lengths whole
     256-token rounds (at least 256) within the LDS logit buffer."""
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)
-    assert K.kvq_decode_auto_splits(c, 32, 32768) == 8         # 128 units x 8
+    assert K.kvq_decode_auto_splits(c, 32, 32768) == 12        # 128 units x 12
     c = _fake_cache(K, d=128, B=4, H=8, cap=131136)
-    assert K.kvq_decode_auto_splits(c, 32, 131136) == 32       # 32 units x 32
+    assert K.kvq_decode_auto_splits(c, 32, 131136) == 48       # 32 units x 48
     c = _fake_cache(K, d=128, B=1, H=32, cap=4096)
     assert K.kvq_decode_auto_splits(c, 32, 4096) == 17         # <= 65 chunks (15-slot lead) -> 17
     c = _fake_cache(K, d=128, B=1, H=1, cap=512)
