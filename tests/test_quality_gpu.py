@@ -12,9 +12,18 @@ Cache Quantisations Inspired by TurboQuant", gist.science summary):
   Contribution 3: low-rank keys are the worst case for attention quality;
   Contribution 1 (unbiasedness): the sketched value side has projection
     ratio 1, the scalar side 1 - D_b.
+  Significance: the mean KL is too optimistic; the worst case (maximum over
+    queries) is far above it, and KQV still beats QKQV there;
+  Results (tail weight): as nu -> 1.05 KQV keeps a stable key direction
+    error while the unrotated KV codec degrades;
+  Contribution 1 (2 pi): the amplification (pi/2) D_{n-1} / D_n grows toward
+    its high-rate limit 2 pi, and the measured score-variance ratio follows it;
+  Evaluation metrics (6D): rank-based comparisons of the per-query scale and
+    direction errors at the key cache, value cache and output.
 The K-geometry crossover at n in {2, 3} that the summary reports is not
 asserted: with direction error = 1 - cos of the reconstructed key it does not
-appear in this setup (QKQV keys are worse at every budget).
+appear in this setup (QKQV keys are worse at every budget).  Where a claim
+holds only in part the test asserts what is measured and says so.
 """
 import math
 
@@ -111,3 +120,79 @@ def test_rotations_stay_under_the_rate_distortion_bound(bits):
     e = sum(quality.rotation_mse("hadamard", bits, "rht", H=1, N=64, seed=3000 + 7 * k)
             for k in range(32)) / 32
     assert e <= tq, e
+
+
+@pytest.mark.parametrize("keys", FAMILIES)
+def test_worst_case_kl(table, keys):
+    """The worst query is far worse than the mean on the structured families,
+    and KQV beats QKQV on the worst case too at n = 4."""
+    a, b = table[(keys, "KQV", 4)], table[(keys, "QKQV", 4)]
+    assert a.kl_max >= a.kl_p99 >= a.kl
+    assert a.kl_max < b.kl_max, (a.kl_max, b.kl_max)
+    if keys != "gaussian":
+        assert a.kl_max > 5 * a.kl, (a.kl_max, a.kl)
+
+
+@pytest.fixture(scope="module")
+def sweep():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_quantization_kqv_amd import quality
+    print("case quality tail sweep", flush=True)
+    return quality.tail_sweep(device="cuda")
+
+
+def test_tail_weight_sweep(sweep):
+    """nu from 5 down to 1.05: KQV's key direction error stays within 25% of
+    its light-tail value; KV's grows at every step and ends 20x above KQV's.
+    (The summary prints epsilon_dir ~ 0.027 for KQV; with 1 - cos at n = 4 this
+    setup gives ~0.004, so the level is not compared, only the stability.)"""
+    kqv = [r["KQV"] for r in sweep]
+    kv = [r["KV"] for r in sweep]
+    assert max(kqv) < 1.25 * min(kqv), kqv
+    assert all(x < y for x, y in zip(kv, kv[1:])), kv
+    assert kv[-1] > 20 * kqv[-1], (kv[-1], kqv[-1])
+
+
+def test_two_pi_amplification():
+    """D_{b-1} / D_b rises toward 4 (each bit quarters the distortion), so the
+    predicted amplification (pi/2) D_{n-1} / D_n rises toward 2 pi; at n = 4
+    the measured score-variance ratio of (n-1)-bit + sketch keys to n-bit keys
+    is within 10% of the prediction and above 85% of 2 pi."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_quantization_kqv_amd import quality
+    print("case quality 2pi", flush=True)
+    a = quality.amplification(device="cuda")
+    r = a["ratio_D"]
+    assert r[2] < r[3] < r[4] < 4.0, r
+    assert abs(a["measured_n4"] / a["predicted"][4] - 1) < 0.1, a
+    assert 0.85 * 2 * math.pi < a["measured_n4"] < 2 * math.pi, a
+
+
+@pytest.mark.parametrize("keys", FAMILIES)
+def test_six_d_kqv_against_qkqv_and_kv(keys):
+    """Per-query 6D errors (-SNR, angle at K, V, output), n = 4.  Against
+    QKQV: KQV's key-site errors are smaller for every query (rank-biserial -1),
+    the value sites are identical (same value codec), and the output errors
+    are smaller except for focused queries, whose output is one value token's
+    error (a tie).  Against KV the summary's claim holds only for heavy-tailed
+    keys: KV's n-bit scalar values have smaller per-vector errors than
+    (n-1)-bit + sketch values (value site +1 for KV), which carries to the
+    output on the other families at this token count."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_quantization_kqv_amd import quality
+    print(f"case quality 6d {keys}", flush=True)
+    _, comp = quality.six_d(keys, 4, device="cuda")
+    q, kv = comp["QKQV"]["rank_biserial"], comp["KV"]["rank_biserial"]
+    assert q[0] < -0.99 and q[1] < -0.99, q
+    assert q[2] == 0.0 and q[3] == 0.0, q
+    if keys == "focused":
+        assert abs(q[4]) < 0.1 and abs(q[5]) < 0.1, q
+    else:
+        assert q[4] < -0.3 and q[5] < -0.3, q
+    assert kv[2] > 0.99 and kv[3] > 0.99, kv
+    if keys == "heavytail":
+        assert kv[0] < -0.99 and kv[1] < -0.99 and kv[4] < -0.5 and kv[5] < -0.5, kv
+    assert comp["QKQV"]["energy"] > 0 and comp["KV"]["energy"] > 0
