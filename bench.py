@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "4-bit KQV decode-attn HBM GB/s (% of peak) + KV tokens/s; quantize GB/s"
 HBM_PEAK_GBPS = 8000.0
 FP32_MFMA_PEAK = 157.3  # TFLOP/s, dense fp32 matrix (MI355X)
+FP16_MFMA_PEAK = 2500.0  # TFLOP/s, dense fp16 matrix (MI355X)
 
 
 def record_bytes(d, kb, vb, kq, vq):
@@ -226,10 +227,21 @@ def main():
         per = 2 * (d + d + d * c.k_qjl + d * c.v_qjl)
         vis = sum(N - C + i + 1 for i in range(C))
         flops = B * Hq * vis * per
-        prefill = {"chunk": C, "q_pos0": N - C, "causal": True, "us": round(pt * 1e6, 2),
-                   "TFLOPs": round(flops / pt / 1e12, 2), "peak_TFLOPs": FP32_MFMA_PEAK,
-                   "pct_fp32_mfma_peak": round(100 * flops / pt / 1e12 / FP32_MFMA_PEAK, 2),
-                   "kernel": "prep_kernel + prefill_kernel (fp32 MFMA 16x16x4) + finish_kernel"}
+        tf = flops / pt / 1e12
+        if d == 128:
+            # fp16 matrix cores; every fp32 operand is split into two fp16 parts,
+            # so one algorithmic product costs two MFMA products
+            prefill = {"chunk": C, "q_pos0": N - C, "causal": True, "us": round(pt * 1e6, 2),
+                       "TFLOPs": round(tf, 2), "peak_TFLOPs": FP16_MFMA_PEAK,
+                       "pct_fp16_mfma_peak": round(100 * tf / FP16_MFMA_PEAK, 2),
+                       "pct_split_operand_peak": round(100 * tf / (FP16_MFMA_PEAK / 2), 2),
+                       "x_fp32_mfma_peak": round(tf / FP32_MFMA_PEAK, 3),
+                       "kernel": "prep_kernel + prefill16_kernel (fp16 MFMA 16x16x32, split operands) + finish_kernel"}
+        else:
+            prefill = {"chunk": C, "q_pos0": N - C, "causal": True, "us": round(pt * 1e6, 2),
+                       "TFLOPs": round(tf, 2), "peak_TFLOPs": FP32_MFMA_PEAK,
+                       "pct_fp32_mfma_peak": round(100 * tf / FP32_MFMA_PEAK, 2),
+                       "kernel": "prep_kernel + prefill_kernel (fp32 MFMA 16x16x4) + finish_kernel"}
         del qp, wsp, outp
 
     result = {

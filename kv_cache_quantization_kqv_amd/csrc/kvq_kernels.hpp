@@ -2378,6 +2378,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
 }  // namespace kvq
 
 #include "kvq_scan.hpp"
+#include "kvq_prefill16.hpp"
 
 namespace kvq {
 
@@ -2611,7 +2612,10 @@ template <int D, int KB, bool KQ, int VB, bool VQ>
 hipError_t prefill_go(const PrefillArgs &a, int B, hipStream_t s) {
   const int NR = a.nq * a.G;
   const dim3 grid((NR + 63) / 64 * a.splits, a.Hkv, B), blk(256);
-  hipLaunchKernelGGL((prefill_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((prefill16_kernel<KB, KQ, VB, VQ>), grid, blk, 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
   return hipGetLastError();
 }
 

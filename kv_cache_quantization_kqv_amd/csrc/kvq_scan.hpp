@@ -80,10 +80,20 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz((a - ah) * 2048.0f, (b - bh) * 2048.0f));
 }
 
-// fp16 split of one float (any sign): hi | lo << 16.
-__device__ __forceinline__ void split1(float x, _Float16 &h, _Float16 &l) {
-  h = (_Float16)x;
-  l = (_Float16)((x - (float)h) * 2048.0f);
+// fp16 split of two floats (any sign): words hi and lo (element 0 in the low
+// half) with x = h + l 2^-11 to about 2^-22.  h is one rounding of each x, and
+// l is taken from exactly that h: the packed word passes through an opaque
+// register, so the operand and the remainder cannot come from two separate
+// conversions (the compiler may lower one conversion to different
+// instructions, whose roundings of a near-tie need not agree).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  const f32x2 x = {x0, x1};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+  asm volatile("" : "+v"(hi));
+  const f16x2 hv = __builtin_bit_cast(f16x2, hi);
+  const f32x2 r = {(x0 - (float)hv[0]) * 2048.0f, (x1 - (float)hv[1]) * 2048.0f};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, f16x2));
 }
 
 template <int KB, bool KQ, int VB, bool VQ>
@@ -356,17 +366,16 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     if (fin) (void)frexpf(m, &ex);
     const int k = fin ? 14 - ex : 0;
     unsc_q = ldexpf(1.0f, -k);
-    const _Float16 z = (_Float16)0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f16x8 o;
+      uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        _Float16 hi, lo;
-        split1(ldexpf(v[8 * j + e], k), hi, lo);
-        o[e] = qkind == 0 ? hi : (qkind == 1 ? lo : z);
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hi, lo;
+        split_pair(ldexpf(v[8 * j + 2 * e], k), ldexpf(v[8 * j + 2 * e + 1], k), hi, lo);
+        w[e] = qkind == 0 ? hi : (qkind == 1 ? lo : 0u);
       }
-      qa[j] = o;
+      qa[j] = op8(w[0], w[1], w[2], w[3]);
     }
   }
   // K sketch (QKQV): rows 4 h + 2 / 4 h + 3 carry S q' hi / lo, slot e of step
@@ -389,17 +398,16 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     if (fin) (void)frexpf(m, &ex);
     const int k = fin ? 14 - ex : 0;
     unsc_s = ldexpf(1.0f, -k);
-    const _Float16 z = (_Float16)0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f16x8 o;
+      uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        _Float16 hi, lo;
-        split1(ldexpf(v[8 * j + e], k), hi, lo);
-        o[e] = qkind == 2 ? hi : (qkind == 3 ? lo : z);
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hi, lo;
+        split_pair(ldexpf(v[8 * j + 2 * e], k), ldexpf(v[8 * j + 2 * e + 1], k), hi, lo);
+        w[e] = qkind == 2 ? hi : (qkind == 3 ? lo : 0u);
       }
-      qs[j] = o;
+      qs[j] = op8(w[0], w[1], w[2], w[3]);
     }
   }
   // scale factors of the softmax lane's head g (row 4 g of the operand lanes)
