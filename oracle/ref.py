@@ -29,7 +29,9 @@ SCHEMES = {"KV": 0, "KQV": 1, "QKQV": 2}
 def lib():
     global _LIB
     if _LIB is None:
-        path = os.path.join(HERE, "liboracle.so")
+        # KVQ_ORACLE_LIB: a differently built copy of the same source (the
+        # sanitizer test runs the pins against an ASan / UBSan build)
+        path = os.environ.get("KVQ_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
         if not os.path.exists(path):
             from . import build as _b
             _b.build()
