@@ -349,6 +349,44 @@ def attention_window(kc: OracleCache, vc: OracleCache, q: np.ndarray, t_begin: i
     return out
 
 
+def prefill_attention_window(kc: OracleCache, vc: OracleCache, q: np.ndarray, q_pos0: int,
+                             causal: bool, t_begin: int, t_end: int, wk: np.ndarray | None,
+                             wv: np.ndarray | None, S: np.ndarray | None,
+                             nthreads: int = 1) -> np.ndarray:
+    """Multi-query attention with a full-precision window: query token i (at
+    position q_pos0 + i) attends over the reconstructed slots t in [t_begin,
+    t_end), only t <= q_pos0 + i when causal, together with every window token
+    wk, wv [B][Hkv][n_win][d] (float32 or bf16 bits; None for none).  The
+    window holds tokens that precede the chunk -- attention sinks and the most
+    recent tokens before it ("Your KV cache is not a bit problem but a geometry
+    problem", "Systems tax", "What we should do", "Frontier") -- so every query
+    of the chunk sees all of them.  One plain fp64 softmax per row over the
+    union.  Returns fp64 [B][n_q][Hq][d]."""
+    qd = _host_f64(np.ascontiguousarray(q))
+    B, nq, Hq, d = qd.shape
+    G = Hq // kc.H
+    T = t_end - t_begin
+    if T > 0:
+        Kh = kc.dequantize(t_begin, T, S, nthreads)
+        Vh = vc.dequantize(t_begin, T, S, nthreads)
+    else:
+        Kh = np.zeros((B, kc.H, 0, d))
+        Vh = np.zeros((B, kc.H, 0, d))
+    Kw = _host_f64(wk) if wk is not None else np.zeros((B, kc.H, 0, d))
+    Vw = _host_f64(wv) if wv is not None else np.zeros((B, kc.H, 0, d))
+    out = np.zeros((B, nq, Hq, d), np.float64)
+    for b in range(B):
+        for i in range(nq):
+            lim = min(t_end, q_pos0 + i + 1) if causal else t_end
+            n = max(0, lim - t_begin)
+            for hq in range(Hq):
+                h = hq // G
+                K = np.concatenate([Kh[b, h, :n], Kw[b, h]], axis=0)
+                V = np.concatenate([Vh[b, h, :n], Vw[b, h]], axis=0)
+                out[b, i, hq] = attention_dense(qd[b, i, hq], K, V)
+    return out
+
+
 def prefill_attention(kc: OracleCache, vc: OracleCache, q: np.ndarray, q_pos0: int, causal: bool,
                       n_ctx: int, S: np.ndarray | None, nthreads: int = 1) -> np.ndarray:
     """Multi-query attention of q [B][n_q][Hq][d] (float32 or bf16 bits) over

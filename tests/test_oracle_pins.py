@@ -741,3 +741,39 @@ def test_prefill_attention_reductions(orc, scheme):
     for i in range(nq):
         assert np.allclose(full[:, i], orc.attention(kc, vc, q[:, i], n_ctx, S), rtol=1e-12,
                            atol=1e-13)
+
+
+@pytest.mark.parametrize("scheme", ["KV", "KQV", "QKQV"])
+def test_prefill_attention_window_reductions(orc, scheme):
+    """Multi-query attention with a full-precision window (sinks and the recent
+    tokens before the chunk, visible to every query of it).  Checked against
+    (1) the plain multi-query oracle when the window is empty and the range
+    starts at 0, (2) for every query token i, the decode-with-window oracle
+    over [t_begin, min(t_end, q_pos0 + i + 1)) and the same window (causal)
+    and over [t_begin, t_end) (non-causal), (3) numpy attention over the
+    window alone when the compressed range is empty."""
+    B, Hkv, Hq, d, t_end, nq, p0 = 2, 2, 4, 8, 13, 5, 8
+    rng, S, kc, vc, _ = _window_case(scheme, 43)
+    G = Hq // Hkv
+    q = rng.standard_normal((B, nq, Hq, d)).astype(np.float32)
+    # (1)
+    a = orc.prefill_attention_window(kc, vc, q, p0, True, 0, t_end, None, None, S)
+    assert np.allclose(a, orc.prefill_attention(kc, vc, q, p0, True, t_end, S), rtol=1e-12,
+                       atol=1e-13)
+    # (2) sinks [0, 2) exact in the window, compressed [2, t_end)
+    wk = rng.standard_normal((B, Hkv, 4, d)).astype(np.float32)
+    wv = rng.standard_normal((B, Hkv, 4, d)).astype(np.float32)
+    for causal in (True, False):
+        a = orc.prefill_attention_window(kc, vc, q, p0, causal, 2, t_end, wk, wv, S)
+        for i in range(nq):
+            lim = min(t_end, p0 + i + 1) if causal else t_end
+            want = orc.attention_window(kc, vc, q[:, i], 2, lim, wk, wv, S)
+            assert np.allclose(a[:, i], want, rtol=1e-12, atol=1e-13)
+    # (3)
+    a = orc.prefill_attention_window(kc, vc, q, p0, True, 5, 5, wk, wv, S)
+    for b in range(B):
+        for i in range(nq):
+            for h in range(Hq):
+                want = _np_attention(q[b, i, h].astype(np.float64), wk[b, h // G].astype(np.float64),
+                                     wv[b, h // G].astype(np.float64))
+                assert np.allclose(a[b, i, h], want, rtol=1e-12, atol=1e-13)
