@@ -313,10 +313,28 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
                                  int n_q, int q_pos0, int causal, int n_ctx, float *out,
                                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes kvq_prefill_attention needs:
- * 4 * B * q_heads * n_q * (d * (1 + [K sketched]) + S * (2 + 2 d)), S the
- * token splits the library uses for this shape (more when the rows alone do
- * not fill the GPU; at most 64). */
+/* kvq_prefill_attention with a full-precision window ("Your KV cache is not a
+ * bit problem but a geometry problem", "Systems tax" and "What we should do":
+ * recent tokens kept unquantized; its frontier section: attention sinks).
+ * Query token i (position q_pos0 + i) attends over the compressed slots
+ * [t_begin, t_end) -- only slots <= q_pos0 + i when causal -- together with
+ * all n_win window tokens wk, wv [B][kv_heads][n_win][d] (w_dtype KVQ_F32 or
+ * KVQ_BF16, 16-B aligned; caller-owned, read only): the window holds tokens
+ * that precede the chunk (sinks, the most recent tokens before it), so every
+ * query of the chunk sees all of them.  One softmax over the union.
+ * 0 <= t_begin <= t_end <= capacity, 0 <= n_win <= 4096,
+ * t_end - t_begin + n_win >= 1; wk / wv may be null when n_win == 0.  Other
+ * arguments, workspace and errors as kvq_prefill_attention. */
+kvq_status kvq_prefill_attention_window(const kvq_cache *c, const void *q, int q_dtype,
+                                        int q_heads, int n_q, int q_pos0, int causal, int t_begin,
+                                        int t_end, const void *wk, const void *wv, int w_dtype,
+                                        int n_win, float *out, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kvq_prefill_attention (and kvq_prefill_attention_window)
+ * needs: 4 * B * q_heads * n_q * (d * (1 + [K sketched]) + S * (2 + 2 d) +
+ * 2 + d), S the token splits the library uses for this shape (more when the
+ * rows alone do not fill the GPU; at most 64). */
 kvq_status kvq_prefill_workspace(const kvq_cache *c, int q_heads, int n_q, size_t *bytes);
 
 /* Static text for a status code. */

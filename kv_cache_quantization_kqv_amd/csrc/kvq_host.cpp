@@ -713,7 +713,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
     kvq::WindowArgs w;
     std::memset(&w, 0, sizeof(w));
     w.q = q; w.wk = wk; w.wv = wv; w.wpart = wpart;
-    w.Hq = q_heads; w.Hkv = c->kv_heads; w.n_win = n_win;
+    w.Hq = q_heads; w.Hkv = c->kv_heads; w.n_win = n_win; w.nq = 1;
     w.qscale = (float)(kLog2e / std::sqrt((double)d));
     e = by_dim(d, [&](auto D) {
       return kvq::launch_window<decltype(D)::value>(w, q_dtype == KVQ_BF16, w_dtype == KVQ_BF16,
@@ -802,22 +802,38 @@ kvq_status kvq_prefill_workspace(const kvq_cache *c, int q_heads, int n_q, size_
   const size_t rows = (size_t)c->batch * q_heads * n_q;
   if (rows > ((size_t)1 << 31) - 1) return KVQ_ERR_RANGE;
   const size_t S = (size_t)prefill_splits(c, q_heads, n_q);
-  // prepared q' (and S q'), then per row and token split (M, L, o', a)
-  *bytes = sizeof(float) * rows * ((size_t)c->d * (1 + (c->k_qjl ? 1 : 0)) + S * (2 + 2 * (size_t)c->d));
+  // prepared q' (and S q'), then per row and token split (M, L, o', a), then
+  // the full-precision window's partial (M, L, o) per row
+  *bytes = sizeof(float) * rows * ((size_t)c->d * (1 + (c->k_qjl ? 1 : 0)) + S * (2 + 2 * (size_t)c->d) +
+                                   2 + (size_t)c->d);
   return KVQ_OK;
 }
 
-kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
-                                 int n_q, int q_pos0, int causal, int n_ctx, float *out,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Multi-query attention over slots [t_begin, t_end) plus n_win full-precision
+// window tokens (both entry points).
+kvq_status prefill_impl(const kvq_cache *c, const void *q, int q_dtype, int q_heads, int n_q,
+                        int q_pos0, int causal, int t_begin, int t_end, const void *wk,
+                        const void *wv, int w_dtype, int n_win, float *out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
   kvq_status s = check_cache(c);
   if (s != KVQ_OK) return s;
   if (!q || !out) return KVQ_ERR_NULL;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
   if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
   if (causal != 0 && causal != 1) return KVQ_ERR_RANGE;
-  if (n_q < 1 || n_ctx < 1 || q_pos0 < 0) return KVQ_ERR_RANGE;
-  if (n_ctx > c->capacity) return KVQ_ERR_CAPACITY;
+  if (n_q < 1 || q_pos0 < 0 || t_begin < 0 || t_end < t_begin) return KVQ_ERR_RANGE;
+  if (n_win < 0 || n_win > KVQ_WINDOW_MAX || t_end - t_begin + n_win < 1) return KVQ_ERR_RANGE;
+  if (t_end > c->capacity) return KVQ_ERR_CAPACITY;
+  if (n_win > 0) {
+    if (!wk || !wv) return KVQ_ERR_NULL;
+    if (w_dtype != KVQ_F32 && w_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (!aligned16(wk) || !aligned16(wv)) return KVQ_ERR_ALIGN;
+  }
+  const int n_ctx = t_end;
   size_t need = 0;
   s = kvq_prefill_workspace(c, q_heads, n_q, &need);
   if (s != KVQ_OK) return s;
@@ -829,6 +845,8 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   float *qt = (float *)workspace;
   float *sqt = qt + rows * d;
   float *part = sqt + (c->k_qjl ? rows * d : 0);
+  const size_t smax = (size_t)prefill_splits(c, q_heads, n_q);
+  float *wpart = part + rows * smax * (2 + 2 * (size_t)d);
   hipStream_t hs = (hipStream_t)stream;
   const int rk = rot_code(c);
 
@@ -845,6 +863,19 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   });
   if (e != hipSuccess) return KVQ_ERR_HIP;
 
+  if (n_win > 0) {
+    kvq::WindowArgs w;
+    std::memset(&w, 0, sizeof(w));
+    w.q = q; w.wk = wk; w.wv = wv; w.wpart = wpart;
+    w.Hq = q_heads; w.Hkv = c->kv_heads; w.n_win = n_win; w.nq = n_q;
+    w.qscale = (float)(kLog2e / std::sqrt((double)d));
+    e = by_dim(d, [&](auto D) {
+      return kvq::launch_window<decltype(D)::value>(w, q_dtype == KVQ_BF16, w_dtype == KVQ_BF16,
+                                                    (int)rows, hs);
+    });
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+
   kvq::PrefillArgs a;
   std::memset(&a, 0, sizeof(a));
   a.kc = c->k_codes; a.ks = c->k_signs; a.vc = c->v_codes; a.vs = c->v_signs;
@@ -856,12 +887,13 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   }
   a.kcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.Hkv = c->kv_heads; a.G = G; a.cap = c->capacity; a.nq = n_q; a.q_pos0 = q_pos0;
-  a.n_ctx = n_ctx; a.causal = causal;
+  a.n_ctx = n_ctx; a.causal = causal; a.t0 = t_begin;
   {
-    const int smax = prefill_splits(c, q_heads, n_q);
-    const int per = (n_ctx + smax - 1) / smax;
-    a.tps = (per + 63) / 64 * 64;
-    a.splits = (n_ctx + a.tps - 1) / a.tps;
+    // the slots [t_begin rounded down to 16, t_end) in splits of whole 64-slot tiles
+    const int span = t_end - (t_begin & ~15);
+    const int per = (span + (int)smax - 1) / (int)smax;
+    a.tps = span > 0 ? (per + 63) / 64 * 64 : 64;
+    a.splits = span > 0 ? (span + a.tps - 1) / a.tps : 1;
   }
   e = by_dim(d, [&](auto D) {
     return kvq::launch_prefill<decltype(D)::value>(a, c->k_bits, c->k_qjl != 0, c->v_bits,
@@ -879,10 +911,32 @@ kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype,
   f.Q = c->rot_Q;
   f.Hkv = c->kv_heads; f.Hq = q_heads; f.G = G; f.nq = n_q; f.rows = (int)rows;
   f.splits = a.splits;
+  f.wpart = n_win > 0 ? wpart : nullptr;
   e = by_dim(d, [&](auto D) {
     return kvq::launch_finish<decltype(D)::value>(f, c->v_qjl != 0, (int)rows, hs);
   });
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
+                                 int n_q, int q_pos0, int causal, int n_ctx, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_ctx < 1) return c ? KVQ_ERR_RANGE : KVQ_ERR_NULL;
+  return prefill_impl(c, q, q_dtype, q_heads, n_q, q_pos0, causal, 0, n_ctx, nullptr, nullptr,
+                      KVQ_F32, 0, out, workspace, workspace_bytes, stream);
+}
+
+kvq_status kvq_prefill_attention_window(const kvq_cache *c, const void *q, int q_dtype,
+                                        int q_heads, int n_q, int q_pos0, int causal, int t_begin,
+                                        int t_end, const void *wk, const void *wv, int w_dtype,
+                                        int n_win, float *out, void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  return prefill_impl(c, q, q_dtype, q_heads, n_q, q_pos0, causal, t_begin, t_end, wk, wv, w_dtype,
+                      n_win, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

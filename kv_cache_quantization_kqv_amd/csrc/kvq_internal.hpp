@@ -97,7 +97,9 @@ struct PrefillArgs {
   float kcent[16], vcent[16];
   float kcoef;               // sqrt(pi/2)/m (K sketch)
   int Hkv, G, cap, nq, q_pos0, n_ctx, causal;
-  int splits, tps;           // token splits per row tile, tokens per split (multiple of 64)
+  int t0;                    // first compressed slot (slots [t0, n_ctx) are read)
+  int splits, tps;           // token splits per row tile, tokens per split (multiple of 64),
+                             // counted from t0 rounded down to 16
 };
 
 // Finish of a multi-query call, one block per output row: o = R^T (o' + c S^T a).
@@ -112,6 +114,7 @@ struct FinishArgs {
   int Hkv, Hq, G, nq;
   int rows;                  // B * Hkv * nq * G
   int splits;
+  const float *wpart;        // full-precision window partial per output row, or null
 };
 
 // Full-precision window (sinks and recent tokens): exact partial softmax sums
@@ -120,8 +123,9 @@ struct FinishArgs {
 struct WindowArgs {
   const void *q;             // [B][Hq][d], q_dtype
   const void *wk, *wv;       // [B][Hkv][n_win][d], w_dtype
-  float *wpart;              // [B][Hq][2 + d]: max (base 2), sum, unnormalised o
+  float *wpart;              // [rows][2 + d]: max (base 2), sum, unnormalised o
   int Hq, Hkv, n_win;
+  int nq;                    // query tokens per batch row (q is [B][nq][Hq][d]; 1 for decode)
   float qscale;              // log2(e)/sqrt(d)
 };
 

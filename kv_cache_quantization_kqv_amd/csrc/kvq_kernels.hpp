@@ -1875,7 +1875,7 @@ __global__ __launch_bounds__(256) void window_kernel(const WindowArgs a) {
   __shared__ float red[4];
   __shared__ float po[2][D];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = row / a.Hq, hq = row - b * a.Hq;
+  const int b = row / (a.Hq * a.nq), hq = row % a.Hq;
   const int hkv = hq / (a.Hq / a.Hkv);
   const size_t base = ((size_t)b * a.Hkv + hkv) * a.n_win * D;
   for (int i = tid; i < D; i += 256) {
@@ -2013,7 +2013,7 @@ void prefill_kernel(const PrefillArgs a) {
   const int NR = a.nq * a.G;
   const int rt = blockIdx.x / a.splits, split = blockIdx.x - rt * a.splits;
   const int R0 = rt * 64 + wave * 16;                 // first row of this wave
-  const int t_lo = split * a.tps;                     // this block's slots [t_lo, t_lo + tps)
+  const int t_lo = (a.t0 & ~15) + split * a.tps;      // this block's slots [t_lo, t_lo + tps)
   if (tid < 16) {
     kct_s[tid] = a.kcent[tid];
     vct_s[tid] = a.vcent[tid];
@@ -2182,7 +2182,7 @@ void prefill_kernel(const PrefillArgs a) {
         float v = sc[r];
         if constexpr (KQ) v = fmaf(a.kcoef * kr4[r], sk[r], v);
         v = kn4[r] * v;
-        s[r] = (tbase + tr0 + r < tl) ? v : -INFINITY;
+        s[r] = (tbase + tr0 + r < tl && tbase + tr0 + r >= a.t0) ? v : -INFINITY;
         mloc = fmaxf(mloc, s[r]);
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
@@ -2297,6 +2297,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
   }
   // log-sum-exp merge of the row's token splits (base 2), then / L
   float v[8] = {0, 0, 0, 0, 0, 0, 0, 0}, av[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float Mc = -INFINITY, Lc = 0.0f;                    // merged max and sum of the compressed part
   {
     constexpr int NS = 2 + 2 * D;
     const float *src = a.part + (ok ? ridx : 0) * a.splits * NS;
@@ -2313,12 +2314,14 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
         if constexpr (VQ) av[e] = fmaf(w, ps[2 + D + i0 + e], av[e]);
       }
     }
-    const float inv = ok ? 1.0f / Ls : 0.0f;
+    const float inv = (ok && Ls > 0.0f) ? 1.0f / Ls : 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       v[e] *= inv;
       av[e] *= inv;
     }
+    Mc = Mx;
+    Lc = Ls;
   }
   if constexpr (VQ) {
 #pragma unroll
@@ -2369,7 +2372,19 @@ __global__ __launch_bounds__(256) void finish_kernel(const FinishArgs a) {
     const int R = (int)(ridx - unit * NR);
     const int b = (int)(unit / a.Hkv), hkv = (int)(unit - (size_t)b * a.Hkv);
     const int tq = R / a.G, g = R - tq * a.G;
-    float *dst = a.out + (((size_t)b * a.nq + tq) * a.Hq + hkv * a.G + g) * D + i0;
+    const size_t orow = ((size_t)b * a.nq + tq) * a.Hq + hkv * a.G + g;
+    if (a.wpart) {
+      // full-precision window: one more log-sum-exp step in the original
+      // space (v is the compressed part already divided by its sum)
+      const float *wp = a.wpart + orow * (2 + D);
+      const float mu = wp[0], m = fmaxf(Mc, mu);
+      const float ac = (Mc == -INFINITY) ? 0.0f : fast_exp2(Mc - m);
+      const float au = (mu == -INFINITY) ? 0.0f : fast_exp2(mu - m);
+      const float den = ac * Lc + au * wp[1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (ac * Lc * v[e] + au * wp[2 + i0 + e]) / den;
+    }
+    float *dst = a.out + orow * D + i0;
     *(float4 *)dst = float4{v[0], v[1], v[2], v[3]};
     *(float4 *)(dst + 4) = float4{v[4], v[5], v[6], v[7]};
   }

@@ -86,7 +86,7 @@ void prefill16_kernel(const PrefillArgs a) {
   const int NR = a.nq * a.G;
   const int rt = blockIdx.x / a.splits, split = blockIdx.x - rt * a.splits;
   const int R0 = rt * 64 + wave * 16;                 // first row of this wave
-  const int t_lo = split * a.tps;                     // this block's slots [t_lo, t_lo + tps)
+  const int t_lo = (a.t0 & ~15) + split * a.tps;      // this block's slots [t_lo, t_lo + tps)
   if (tid < 16) {
     kc_s[tid] = (_Float16)a.kcent[tid];
     vc_s[tid] = (_Float16)a.vcent[tid];
@@ -273,7 +273,7 @@ void prefill16_kernel(const PrefillArgs a) {
         float v = fmaf(l[r], 1.0f / 2048.0f, h[r]) * unq;
         if constexpr (KQ) v = fmaf(a.kcoef * kr4[r], fmaf(kl[r], 1.0f / 2048.0f, kh[r]) * uns, v);
         v = kn4[r] * v;
-        s[r] = (tbase + t0 + r < tl) ? v : -INFINITY;
+        s[r] = (tbase + t0 + r < tl && tbase + t0 + r >= a.t0) ? v : -INFINITY;
       }
     };
 

@@ -30,7 +30,8 @@ EXPORTS = ["kvq_codebook_init", "kvq_sketch_init", "kvq_cache_init", "kvq_cache_
            "kvq_decode_attention_window", "kvq_decode_attention_noalloc",
            "kvq_decode_attention_stages", "kvq_probe_stream_read",
            "kvq_decode_workspace", "kvq_decode_auto_splits",
-           "kvq_prefill_attention", "kvq_prefill_workspace", "kvq_status_str", "kvq_version"]
+           "kvq_prefill_attention", "kvq_prefill_attention_window", "kvq_prefill_workspace",
+           "kvq_status_str", "kvq_version"]
 
 
 class KVQError(RuntimeError):
@@ -93,6 +94,8 @@ def lib():
             "kvq_decode_auto_splits": ([cache_p, i32, i32], i32),
             "kvq_prefill_attention": ([cache_p, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp],
                                       i32),
+            "kvq_prefill_attention_window": ([cache_p, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp,
+                                              i32, i32, vp, vp, sz, vp], i32),
             "kvq_prefill_workspace": ([cache_p, i32, i32, C.POINTER(sz)], i32),
             "kvq_status_str": ([i32], C.c_char_p),
             "kvq_version": ([], C.c_char_p),
@@ -241,6 +244,16 @@ def kvq_prefill_attention(c: kvq_cache, q: int, q_dtype: int, q_heads: int, n_q:
            "kvq_prefill_attention")
 
 
+def kvq_prefill_attention_window(c: kvq_cache, q: int, q_dtype: int, q_heads: int, n_q: int,
+                                 q_pos0: int, causal: int, t_begin: int, t_end: int, wk: int,
+                                 wv: int, w_dtype: int, n_win: int, out: int, workspace: int,
+                                 ws_bytes: int, stream: int = 0):
+    _check(lib().kvq_prefill_attention_window(C.byref(c), q, q_dtype, q_heads, n_q, q_pos0, causal,
+                                              t_begin, t_end, wk, wv, w_dtype, n_win, out,
+                                              workspace, ws_bytes, stream),
+           "kvq_prefill_attention_window")
+
+
 # ------------------------------------------------------------------ torch-owned cache
 class KVQCache:
     """A compressed KV cache whose buffers are torch device tensors.
@@ -379,6 +392,41 @@ class KVQCache:
         kvq_prefill_attention(self.c, q.data_ptr(), dt, Hq, n_q, q_pos0, int(bool(causal)), n_ctx,
                               out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                               self._stream())
+        return out
+
+    def prefill_attention_window(self, q, q_pos0: int, t_begin: int, t_end: int, wk=None, wv=None,
+                                 causal: bool = True, out=None, workspace=None):
+        """Multi-query attention of q [B][n_q][q_heads][d] over cache slots
+        [t_begin, t_end) (causal: up to each query's position) plus the
+        full-precision tokens wk, wv ([B][kv_heads][n_win][d], fp32 or bf16;
+        None for none), which every query sees."""
+        torch = self.torch
+        if q.dim() != 4 or q.shape[0] != self.batch or q.shape[3] != self.d or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B][n_q][q_heads][d] tensor")
+        dts = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}
+        dt = dts.get(q.dtype)
+        if dt is None:
+            raise TypeError(f"unsupported dtype {q.dtype}")
+        n_win, wdt, pk, pv = 0, KVQ_F32, 0, 0
+        if wk is not None:
+            shape = (self.batch, self.kv_heads, wk.shape[2] if wk.dim() == 4 else -1, self.d)
+            if (wk.dim() != 4 or tuple(wk.shape) != shape or wv is None
+                    or tuple(wv.shape) != shape or wk.dtype != wv.dtype
+                    or not (wk.is_contiguous() and wv.is_contiguous())):
+                raise ValueError("wk, wv must be contiguous [B][kv_heads][n_win][d] tensors")
+            wdt = dts.get(wk.dtype)
+            if wdt is None:
+                raise TypeError(f"unsupported dtype {wk.dtype}")
+            n_win, pk, pv = wk.shape[2], wk.data_ptr(), wv.data_ptr()
+        n_q, Hq = q.shape[1], q.shape[2]
+        nbytes = kvq_prefill_workspace(self.c, Hq, n_q)
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device)
+        if out is None:
+            out = torch.empty(self.batch, n_q, Hq, self.d, dtype=torch.float32, device=self.device)
+        kvq_prefill_attention_window(self.c, q.data_ptr(), dt, Hq, n_q, q_pos0, int(bool(causal)),
+                                     t_begin, t_end, pk, pv, wdt, n_win, out.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), self._stream())
         return out
 
     def decode_attention_window(self, q, t_begin: int, t_end: int, wk=None, wv=None,

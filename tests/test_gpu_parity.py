@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from kv_cache_quantization_kqv_amd import synth
-from parity_util import Pair, rel_rows, v_sign_records
+from oracle import ref
+from parity_util import Pair, host_bits, rel_rows, v_sign_records
 
 pytestmark = pytest.mark.gpu
 
@@ -417,6 +418,58 @@ def test_prefill_rotations_and_short_chunks(rotation):
     one = P.gpu.prefill_attention(q1.cuda(), N - 1, N, causal=True)[:, 0]
     dec = P.gpu.decode_attention(q1[:, 0].contiguous().cuda(), N)
     assert rel_rows(one.cpu().numpy(), dec.cpu().numpy().astype(np.float64)).max() < 1e-5
+
+
+# (t_begin, t_end, window token runs taken from the exact inputs), over a
+# 187-slot cache: sinks and recent tokens exact next to a compressed middle, a
+# window alone, a compressed range from an offset inside a 16-slot block
+PREFILL_WINDOW_CASES = {"recent": (0, 123, [(123, 64)]),
+                        "sinks": (4, 150, [(0, 4), (150, 37)]),
+                        "window_only": (150, 150, [(0, 4), (102, 48)]),
+                        "offset": (21, 187, [])}
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("case", list(PREFILL_WINDOW_CASES))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scheme,n", [("KQV", 4), ("QKQV", 3), ("KV", 2)])
+def test_prefill_window_matches_oracle(scheme, n, d, case, dtype):
+    """Multi-query attention with a full-precision window: a chunk of 37 query
+    tokens at positions 150..186 over compressed slots [t_begin, t_end) (only
+    those up to each query's position when causal) plus window tokens that
+    every query sees, in one softmax per row."""
+    print(f"case prefill-window {scheme}{n} d={d} {case} {dtype}", flush=True)
+    B, Hkv, G, nq, p0 = 2, 2, 4, 37, 150
+    N = p0 + nq
+    t_begin, t_end, win = PREFILL_WINDOW_CASES[case]
+    P = Pair(scheme, n, d, B, Hkv, N + 5)
+    K, V = _inputs(B, Hkv, N, d, dtype, 2300 + d + n, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, nq, Hkv * G, d), 2400 + d, dtype)
+    wk = torch.cat([K[:, :, a:a + c] for a, c in win], 2).contiguous() if win else None
+    wv = torch.cat([V[:, :, a:a + c] for a, c in win], 2).contiguous() if win else None
+    for causal in (True, False):
+        want = ref.prefill_attention_window(P.ok, P.ov, host_bits(q), p0, causal, t_begin, t_end,
+                                            None if wk is None else host_bits(wk),
+                                            None if wv is None else host_bits(wv), P.S, 8)
+        got = P.gpu.prefill_attention_window(
+            q.cuda(), p0, t_begin, t_end, None if wk is None else wk.cuda(),
+            None if wv is None else wv.cuda(), causal=causal).cpu().numpy()
+        err = rel_rows(got, want)
+        assert err.max() < TOL[dtype], (causal, err.max())
+
+
+def test_prefill_window_empty_equals_plain_prefill():
+    """No window over [0, n): bit for bit the plain multi-query call."""
+    B, Hkv, G, nq, p0, d = 2, 2, 4, 37, 150, 128
+    N = p0 + nq
+    P = Pair("KQV", 4, d, B, Hkv, N + 5)
+    K, V = _inputs(B, Hkv, N, d, torch.bfloat16, 2500, heavy=True)
+    P.write(K, V, 0)
+    q = synth.gaussian((B, nq, Hkv * G, d), 2501, torch.bfloat16).cuda()
+    a = P.gpu.prefill_attention(q, p0, N, causal=True)
+    b = P.gpu.prefill_attention_window(q, p0, 0, N, causal=True)
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("causal", [True, False])

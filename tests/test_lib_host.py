@@ -397,8 +397,9 @@ def test_prefill_validation_status_codes(K):
     assert lib.kvq_prefill_workspace(p, 6, 0, C.byref(ws)) == 10
     assert lib.kvq_prefill_workspace(p, 6, 5, C.byref(ws)) == 0   # G = 3 is fine here
     # q' (no K sketch), then (M, L, o', a) per row and split: one split here
-    # (a 32-slot cache caps the splits at ceil(32 / 256) = 1)
-    assert ws.value == 4 * 1 * 6 * 5 * (64 + 1 * (2 + 2 * 64))
+    # (a 32-slot cache caps the splits at ceil(32 / 256) = 1), then the
+    # window partial (M, L, o) per row
+    assert ws.value == 4 * 1 * 6 * 5 * (64 + 1 * (2 + 2 * 64) + 2 + 64)
     need = ws.value
     q, out, w = 0xA00000, 0xB00000, 0xC00000
     f = lib.kvq_prefill_attention
@@ -415,7 +416,31 @@ def test_prefill_validation_status_codes(K):
     assert f(p, q, 1, 5, 5, 0, 1, 8, out, w, need, None) == 9
     q3 = _fake_cache(K, scheme="QKQV", n=3)
     assert lib.kvq_prefill_workspace(C.byref(q3), 2, 7, C.byref(ws)) == 0
-    assert ws.value == 4 * 1 * 2 * 7 * (2 * 64 + 1 * (2 + 2 * 64))  # + S q'
+    assert ws.value == 4 * 1 * 2 * 7 * (2 * 64 + 1 * (2 + 2 * 64) + 2 + 64)  # + S q'
+
+
+def test_prefill_window_validation_status_codes(K):
+    """kvq_prefill_attention_window checks its range, window and pointers
+    before any launch (no GPU needed for these paths)."""
+    lib = K.lib()
+    c = _fake_cache(K)                               # KQV-4, d = 64, B = 1, Hkv = 2, cap = 32
+    p = C.byref(c)
+    ws = C.c_size_t()
+    assert lib.kvq_prefill_workspace(p, 6, 5, C.byref(ws)) == 0
+    need = ws.value
+    q, out, w, wk, wv = 0xA00000, 0xB00000, 0xC00000, 0xD00000, 0xE00000
+    f = lib.kvq_prefill_attention_window
+    # (c, q, q_dtype, q_heads, n_q, q_pos0, causal, t_begin, t_end, wk, wv, w_dtype, n_win, out, ...)
+    assert f(p, q, 1, 6, 5, 0, 1, 4, 3, wk, wv, 1, 2, out, w, need, None) == 10     # t_end < t_begin
+    assert f(p, q, 1, 6, 5, 0, 1, 3, 3, None, None, 1, 0, out, w, need, None) == 10  # empty union
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 8, wk, wv, 1, 4097, out, w, need, None) == 10  # window too long
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 8, wk, wv, 1, -1, out, w, need, None) == 10
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 33, wk, wv, 1, 2, out, w, need, None) == 6     # past capacity
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 8, None, wv, 1, 2, out, w, need, None) == 1    # window pointers
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 8, wk + 4, wv, 1, 2, out, w, need, None) == 2
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 8, wk, wv, 5, 2, out, w, need, None) == 8       # window dtype
+    assert f(p, q, 1, 6, 5, 0, 1, 0, 8, wk, wv, 1, 2, out, w, need - 1, None) == 7  # workspace
+    assert f(p, q, 1, 6, 5, 0, 2, 0, 8, wk, wv, 1, 2, out, w, need, None) == 10     # causal flag
 
 
 def test_prefill_splits_fill_the_gpu(K):
@@ -427,10 +452,10 @@ def test_prefill_splits_fill_the_gpu(K):
     assert lib.kvq_prefill_workspace(C.byref(c), 32, 256, C.byref(ws)) == 0
     rows = 32 * 256
     # 4 row tiles x 32 heads = 128 blocks -> 8 splits
-    assert ws.value == 4 * rows * (128 + 8 * (2 + 256))
+    assert ws.value == 4 * rows * (128 + 8 * (2 + 256) + 2 + 128)
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)  # GQA chunk: 2048 blocks, 1 split
     assert lib.kvq_prefill_workspace(C.byref(c), 32, 256, C.byref(ws)) == 0
-    assert ws.value == 4 * 16 * 32 * 256 * (128 + 1 * (2 + 256))
+    assert ws.value == 4 * 16 * 32 * 256 * (128 + 1 * (2 + 256) + 2 + 128)
 
 
 def test_decode_stages_and_probe_validation(K):
