@@ -688,13 +688,17 @@ void quantize_kernel(const QuantArgs a) {
     }
     const float nu = sqrtf(ss);
     const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
+    // codes: the record layout (per-slot records), or one nibble per
+    // coordinate (token groups: the regrouping reads nibbles)
     LocalCodes<DL, BITS> lc;
     lc.clear();
+    uint32_t nib[VG ? DL / 8 : 1] = {};
 #pragma unroll
     for (int i = 0; i < DL; ++i) {
       const float u = y[i] * rcp;
       const uint32_t code = bucketize_code<BITS>(u, bt, a.thr);
-      lc.put(i, code);
+      if constexpr (VG) nib[i >> 3] |= code << (4 * (i & 7));
+      else lc.put(i, code);
       if constexpr (QJL) y[i] = u - bt.cent[code];
       // keep at most 16 coordinates' table lookups in flight (register pressure)
       if ((i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
@@ -703,11 +707,10 @@ void quantize_kernel(const QuantArgs a) {
     const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vrow);
     uint32_t rec[RECW];
     if constexpr (VG) {
-      // the record halves stay in lc until the stage is free (below); packed
+      // the nibbles stay in registers until the stage is free (below); packed
       // here, or the compiler defers the packing and keeps every code live
 #pragma unroll
-      for (int k = 0; k < LocalCodes<DL, BITS>::NA + LocalCodes<DL, BITS>::NB; ++k)
-        asm volatile("" : "+v"(lc.w[k]));
+      for (int k = 0; k < DL / 8; ++k) asm volatile("" : "+v"(nib[k]));
     } else if constexpr (LPV == 2) {
       // each lane packed its own half; the lower lane joins the two images
       LocalCodes<DL, BITS> oth;
@@ -768,23 +771,18 @@ void quantize_kernel(const QuantArgs a) {
       // (the scheduling barriers keep the emission's work from moving into
       // the earlier phases: register pressure)
       __builtin_amdgcn_sched_barrier(0);
-      // each lane writes its half of the slot's record (per-slot layout) to
-      // the slot's stage row (offset made opaque so it is not hoisted out of
-      // the tile loop: register pressure); vg_emit_codes regroups the rows
-      using LCT = LocalCodes<DL, BITS>;
+      // each lane writes the nibbles of its half of the slot's codes to the
+      // slot's stage row (offset made opaque so it is not hoisted out of the
+      // tile loop: register pressure); vg_emit_codes regroups the rows
       int off = vrow * P2;
       asm volatile("" : "+v"(off));
-      uint8_t *nr = stage + off;
-      if constexpr (BITS == 3) {
-        *(u32x4 *)(nr + 16 * half) = u32x4{lc.w[0], lc.w[1], lc.w[2], lc.w[3]};
-        *(u32x2 *)(nr + D / 4 + 8 * half) = u32x2{lc.w[LCT::NA], lc.w[LCT::NA + 1]};
-      } else {
+      uint8_t *nr = stage + off + (DL / 2) * half;
 #pragma unroll
-        for (int k = 0; k < LCT::NA; ++k) *(uint32_t *)(nr + half * (DL * BITS / 8) + 4 * k) = lc.w[k];
-      }
+      for (int k = 0; k < DL / 32; ++k)
+        *(u32x4 *)(nr + 16 * k) = u32x4{nib[4 * k], nib[4 * k + 1], nib[4 * k + 2], nib[4 * k + 3]};
       wave_sync();
       const size_t slot0 = (size_t)bh * a.cap + (size_t)(a.t0 + tbase);
-      vg_emit_codes<BITS, VT, P2>(stage, rlo, nvalid, a.codes + slot0 * RECB, lane);
+      vg_emit_codes<BITS, VT, P2, true>(stage, rlo, nvalid, a.codes + slot0 * RECB, lane);
       if constexpr (QJL) vg_emit_signs<VT, P2>(stage + 2 * D, rlo, nvalid, a.signs + slot0 * 16, lane);
       wave_sync();   // the stage takes the next tile
       __builtin_amdgcn_sched_barrier(0);

@@ -148,10 +148,12 @@ __device__ __forceinline__ uint32_t vg_row_nibbles(const uint8_t *row, int n) {
 }
 
 // Emit the code groups of one wave tile of VT slots (tile start a multiple of
-// VT, so of 4): rows = LDS per-slot records (16 VB bytes each, RP bytes
-// apart) of the tile; slots with rlo <= row < rhi are written, the others keep
-// their stored bits.  dst = the value codes at the tile's first slot.
-template <int VB, int VT, int RP = 16 * VB>
+// VT, so of 4): rows = LDS rows of the tile's slots, RP bytes apart, holding
+// per-slot records (16 VB bytes), or (NIB) one nibble per coordinate
+// (coordinate c in bits 4 (c % 8) of byte-aligned word c / 8: 64 bytes);
+// slots with rlo <= row < rhi are written, the others keep their stored bits.
+// dst = the value codes at the tile's first slot.
+template <int VB, int VT, int RP = 16 * VB, bool NIB = false>
 __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int rhi, uint8_t *dst,
                                               int lane) {
   constexpr int PB = 4 * VB, QB = 64 * VB;
@@ -170,7 +172,7 @@ __device__ __forceinline__ void vg_emit_codes(const uint8_t *rows, int rlo, int 
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * qd + r;
       const bool ok = row >= rlo && row < rhi;
-      N[r] = vg_row_nibbles<VB>(rows + row * RP, n);
+      N[r] = NIB ? *(const uint32_t *)(rows + row * RP + 4 * n) : vg_row_nibbles<VB>(rows + row * RP, n);
       V[r] = ok ? NM : 0u;
       nv += ok ? 1 : 0;
     }
