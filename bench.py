@@ -191,10 +191,15 @@ def main():
     quant_t = float(np.median(tk + tv)) * 1e-6
     quant_gbps = (qk_bytes + qv_bytes) / quant_t / 1e9
 
-    # the scan kernel alone: cache records + prepared queries read, split partials written
-    scan_bytes = B * Hkv * N * rec + B * Hq * d * 4 * (1 + c.k_qjl) + B * Hq * splits * (2 + 2 * d) * 4
+    # the scan kernel alone: cache records + queries read, split partials written;
+    # at d = 128 with a Hadamard rotation (or none) and no key sketch the scan
+    # prepares q' from q itself (no prep launch), else it reads q' (and S q') in fp32
+    prep_fused = d == 128 and not c.k_qjl and args.rotation != "qr"
+    q_bytes = B * Hq * d * (q.element_size() if prep_fused else 4 * (1 + c.k_qjl))
+    scan_bytes = B * Hkv * N * rec + q_bytes + B * Hq * splits * (2 + 2 * d) * 4
     scan_t = float(np.median(st[:, 1])) * 1e-6
-    roof = {"kernel": "scan_kernel (kvq_decode_attention_stages KVQ_STAGE_SCAN: split scan on fp16 MFMA)",
+    roof = {"kernel": "scan_kernel (kvq_decode_attention_stages KVQ_STAGE_SCAN: split scan on fp16 MFMA"
+                      + (", query prepared in its prologue)" if prep_fused else ")"),
             "bound": "hbm",
             "achieved": round(scan_bytes / scan_t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(scan_bytes / scan_t / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -258,8 +263,8 @@ def main():
                    "pct_hbm_peak": round(100 * dec_gbps / HBM_PEAK_GBPS, 2),
                    "kv_tokens_per_s": round(B * N / dec_t, 1),
                    "records_per_s": round(B * Hkv * N / dec_t, 1),
-                   "stages_us": {"prep": stats(st[:, 0]), "scan": stats(st[:, 1]),
-                                 "merge": stats(st[:, 2])},
+                   "stages_us": {"prep": "in scan prologue" if prep_fused else stats(st[:, 0]),
+                                 "scan": stats(st[:, 1]), "merge": stats(st[:, 2])},
                    "warm_us": stats(tw),
                    "warm_GBps": round(dec_bytes / float(np.median(tw)) / 1e3, 1)},
         "quantize": {"us_k": stats(tk), "us_v": stats(tv),

@@ -281,7 +281,11 @@ enum {
  * so calls with PREP, then SCAN, then MERGE on one stream (same arguments and
  * workspace) give exactly the result of one kvq_decode_attention call, which
  * equals stages = KVQ_STAGE_ALL.  For callers that time or overlap the stages
- * separately.  Errors: as kvq_decode_attention; KVQ_ERR_RANGE for a bad mask. */
+ * separately.  At d = 128 with a Hadamard rotation or none and no key sketch
+ * the scan prepares q' in its own prologue: there PREP launches only the
+ * window kernel (nothing without a window) and SCAN reads q itself, so q must
+ * stay unchanged until SCAN has run.
+ * Errors: as kvq_decode_attention; KVQ_ERR_RANGE for a bad mask. */
 kvq_status kvq_decode_attention_stages(const kvq_cache *c, const void *q, int q_dtype,
                                        int q_heads, int n_ctx, int splits, int stages, float *out,
                                        void *workspace, size_t workspace_bytes, void *stream);

@@ -701,8 +701,11 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
   for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
   p.Q = c->rot_Q;
+  // the matrix-core scan prepares q' itself (Hadamard kinds or none, no key
+  // sketch): no query-preparation launch
+  const bool scan_preps = scan_mfma(c) && !c->k_qjl && rk != kvq::RK_QR;
   hipError_t e = hipSuccess;
-  if (stages & KVQ_STAGE_PREP) {
+  if ((stages & KVQ_STAGE_PREP) && !scan_preps) {
     e = by_dim(d, [&](auto D) {
       return kvq::launch_prep<decltype(D)::value>(p, rk, c->k_qjl != 0, q_dtype == KVQ_BF16, hs);
     });
@@ -728,6 +731,11 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   a.kn = c->k_norm; a.kr = c->k_rnorm; a.vn = c->v_norm; a.vr = c->v_rnorm;
   a.qt = qt; a.sqt = sqt; a.part = part; a.S = c->S; a.out = out;
   a.wpart = n_win > 0 ? wpart : nullptr;
+  if (scan_preps) {
+    a.qsrc = q;
+    a.q_bf16 = q_dtype == KVQ_BF16;
+    a.qscale = p.qscale;
+  }
   a.t0 = t_begin;
   a.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;

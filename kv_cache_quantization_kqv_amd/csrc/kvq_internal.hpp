@@ -82,6 +82,12 @@ struct DecodeArgs {
   uint32_t rsign[4];         // RK_RHT
   const float *Q;            // RK_QR
   const float *wpart;        // full-precision window partial [B][Hq][2 + d] or null
+  // the query itself ([B][Hq][d], bf16 when q_bf16) when the matrix-core scan
+  // prepares q' = R q qscale in its prologue (Hadamard kinds or none, no key
+  // sketch); null: q' is read from qt
+  const void *qsrc;
+  int q_bf16;
+  float qscale;
   int t0;                    // first cache slot of the scanned range
   int Hkv, Hq, Gtot, HG, cap, n_ctx, splits, tps;
 };

@@ -1274,157 +1274,168 @@ struct VTile {
   static_assert(BYTES % 16 == 0 && VS % 16 == 0, "tile segments must be 16-byte multiples");
 };
 
-// Load of a split partial (written by the scan kernel, which completed before
-// the merge kernel started on the same stream).
-__device__ __forceinline__ float ld_part(const float *p) { return *p; }
-
-// Merge of the splits of GT query heads (run by one block of 256 threads).
-// LDS: `sm` needs GT * (MCH + NS) floats; `mx` GT floats.
-template <int D, bool VQ, int GT>
-__device__ __forceinline__ void merge_splits(const DecodeArgs &a, float *sm, float *mx, int b,
-                                             int hq0) {
-  constexpr int NS = 2 + 2 * D;
-  constexpr int MCH = 256;                           // splits per weight chunk
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Split merge of one query row (b, hq), one block of 256 threads: the
+// log-sum-exp weights of the splits, the weighted sums of their partials,
+// o' + sqrt(pi/2)/m S^T a (sketched values), the inverse rotation and the
+// division by L (and the full-precision window, if any).  Every load that does
+// not depend on another (the split maxima, the partial columns, the columns
+// of S, the window partial) is issued at the start, so the row costs about one
+// memory latency; the split weights stay in registers (lane s of the wave
+// holds split s of the current 64) and the Walsh-Hadamard transform runs
+// across the lanes of one wave.
+template <int D, bool VQ>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
+  constexpr int NS = 2 + 2 * D, NC = NS - 1;         // partial floats, columns merged
+  constexpr int NIT = (NC + 255) / 256;              // columns per thread
+  constexpr int U = 16;                              // splits per load batch
+  constexpr int KS = 256 / D, KL = D / KS;           // S^T a: KS threads per coordinate
+  __shared__ __attribute__((aligned(16))) float res[NS];    // merged L, o', a (by column)
+  __shared__ __attribute__((aligned(16))) float sta[256];   // S^T a partial sums
+  __shared__ __attribute__((aligned(16))) float wv[D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row = blockIdx.x;                        // b * Hq + hq
   const int splits = a.splits;
-  const float *pb = a.part + ((size_t)b * a.Hq + hq0) * splits * NS;   // head hh: + hh*splits*NS
-  float *al = sm;                                    // [GT][MCH]
-  float *res = sm + GT * MCH;                        // [GT][NS] merged L, o', a
-  if (wave < GT) {
-    float m = -INFINITY;
-    for (int s = lane; s < splits; s += 64) m = fmaxf(m, ld_part(pb + ((size_t)wave * splits + s) * NS));
-    m = wave_max(m);
-    if (lane == 0) mx[wave] = m;
+  const float *pb = a.part + (size_t)row * splits * NS;
+
+  // columns of S for this thread's share of S^T a
+  const int si = tid % D, sk0 = (tid / D) * KL;
+  uint16_t sv[VQ ? KL : 1];
+  if constexpr (VQ) {
+#pragma unroll
+    for (int k = 0; k < KL; ++k) sv[k] = ((const uint16_t *)a.S)[(size_t)(sk0 + k) * D + si];
   }
-  __syncthreads();
-  constexpr int NIT = (GT * (NS - 1) + 255) / 256;   // (head, column) items per thread
+  // the window partial of this thread's output coordinate
+  float wm = -INFINITY, wl = 0.0f, wo = 0.0f;
+  if (a.wpart && tid < D) {
+    const float *wp = a.wpart + (size_t)row * (2 + D);
+    wm = wp[0];
+    wl = wp[1];
+    wo = wp[2 + tid];
+  }
+  auto load_batch = [&](int s0, float (&v)[NIT][U]) {
+#pragma unroll
+    for (int j = 0; j < NIT; ++j) {
+      const int item = tid + 256 * j;
+      const bool ok = item < NC;
+      const float *src = pb + (size_t)s0 * NS + 1 + (ok ? item : 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[j][u] = (ok && s0 + u < splits) ? src[(size_t)u * NS] : 0.0f;
+    }
+  };
+  float v[NIT][U];
+  load_batch(0, v);
+  // maximum over the splits (every wave computes it: no barrier)
+  const float ms0 = lane < splits ? pb[(size_t)lane * NS] : -INFINITY;
+  float m = ms0;
+  for (int s = lane + 64; s < splits; s += 64) m = fmaxf(m, pb[(size_t)s * NS]);
+  m = wave_max(m);
+
   float acc[NIT];
 #pragma unroll
   for (int j = 0; j < NIT; ++j) acc[j] = 0.0f;
-  for (int s0 = 0; s0 < splits; s0 += MCH) {
-    for (int idx = tid; idx < GT * MCH; idx += 256) {
-      const int hh = idx / MCH, s = s0 + idx - hh * MCH;
-      float w = 0.0f;
-      if (s < splits) {
-        const float ms = ld_part(pb + ((size_t)hh * splits + s) * NS);
-        w = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - mx[hh]);
-      }
-      al[idx] = w;
+  float w = 0.0f;
+  for (int s0 = 0; s0 < splits; s0 += U) {
+    if ((s0 & 63) == 0) {
+      const int sl = s0 + lane;
+      const float ms = s0 == 0 ? ms0 : (sl < splits ? pb[(size_t)sl * NS] : -INFINITY);
+      w = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - m);
     }
-    __syncthreads();
-    const int sn = min(MCH, splits - s0);
-    // eight splits per step, all their loads issued before any is used
-    for (int u0 = 0; u0 < sn; u0 += 8) {
-      float v[NIT][8];
+    float vn[NIT][U];
+    if (s0 + U < splits) {
+      load_batch(s0 + U, vn);
+    } else {
 #pragma unroll
-      for (int j = 0; j < NIT; ++j) {
-        const int item = tid + 256 * j;
-        const bool ok = item < GT * (NS - 1);
-        const int hh = ok ? item / (NS - 1) : 0, col = ok ? 1 + item - hh * (NS - 1) : 1;
-        const float *src = pb + ((size_t)hh * splits + s0 + u0) * NS + col;
+      for (int j = 0; j < NIT; ++j)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[j][u] = (ok && u0 + u < sn) ? ld_part(src + (size_t)u * NS) : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < NIT; ++j) {
-        const int item = tid + 256 * j;
-        const int hh = item < GT * (NS - 1) ? item / (NS - 1) : 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[j] = fmaf(al[hh * MCH + u0 + u], v[j][u], acc[j]);
-      }
+        for (int u = 0; u < U; ++u) vn[j][u] = 0.0f;
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wu = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (s0 & 63) + u));
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) acc[j] = fmaf(wu, v[j][u], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NIT; ++j)
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[j][u] = vn[j][u];
   }
 #pragma unroll
-  for (int j = 0; j < NIT; ++j) {
-    const int item = tid + 256 * j;
-    if (item < GT * (NS - 1)) {
-      const int hh = item / (NS - 1), col = 1 + item - hh * (NS - 1);
-      res[hh * NS + col] = acc[j];
-    }
-  }
+  for (int j = 0; j < NIT; ++j)
+    if (tid + 256 * j < NC) res[1 + tid + 256 * j] = acc[j];
   __syncthreads();
-  // o' (+ sqrt(pi/2)/m S^T a) into al[hh][i] (reused as the WHT buffer)
-  float *wv = al;
-  if constexpr (VQ && GT * D < 256) {
-    // KS threads per output coordinate, each over D / KS rows of S, partial
-    // sums added in thread order
-    constexpr int NI = GT * D, KS = 256 / NI, KL = D / KS;
-    const int item = tid % NI, part = tid / NI;
-    const int hh = item / D, i = item - hh * D;
-    const float *av = res + hh * NS + 2 + D;
+
+  // o' (+ sqrt(pi/2)/m S^T a): KS partial sums per coordinate, added in order
+  if constexpr (VQ) {
     float t = 0.0f;
-#pragma unroll 16
-    for (int k = part * KL; k < part * KL + KL; ++k) t = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), av[k], t);
-    al[tid] = t;
-    __syncthreads();
-    if (tid < NI) {
-      float u = 0.0f;
 #pragma unroll
-      for (int p = 0; p < KS; ++p) u += al[p * NI + item];
-      wv[item] = fmaf(a.vcoef, u, res[hh * NS + 2 + i]);
-    }
-  } else {
-    for (int item = tid; item < GT * D; item += 256) {
-      const int hh = item / D, i = item - hh * D;
-      float v = res[hh * NS + 2 + i];
-      if constexpr (VQ) {
-        const float *av = res + hh * NS + 2 + D;
-        float t = 0.0f;
-#pragma unroll 16
-        for (int k = 0; k < D; ++k) t = fmaf(bf16_to_f32(a.S[(size_t)k * D + i]), av[k], t);
-        v = fmaf(a.vcoef, t, v);
+    for (int k = 0; k < KL; ++k) t = fmaf(bf16_to_f32(sv[k]), res[2 + D + sk0 + k], t);
+    sta[tid] = t;
+    __syncthreads();
+  }
+  if (tid < 64) {
+    // lane l holds coordinates l and l + 64 (D = 128) or l (D <= 64)
+    constexpr int PL = D > 64 ? 2 : 1;
+    float x[PL];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+      const int i = lane + 64 * e;
+      float val = 0.0f;
+      if (i < D) {
+        val = res[2 + i];
+        if constexpr (VQ) {
+          float u = 0.0f;
+#pragma unroll
+          for (int p = 0; p < KS; ++p) u += sta[p * D + i];
+          val = fmaf(a.vcoef, u, val);
+        }
       }
-      wv[hh * D + i] = v;
+      x[e] = val;
     }
+    if (a.rk == RK_WHT || a.rk == RK_RHT) {
+      // pairs (i, i + h): the lane with bit h clear keeps the sum, the other
+      // the difference (lower minus upper)
+#pragma unroll
+      for (int h = 1; h < (D < 64 ? D : 64); h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          const float y = __shfl_xor(x[e], h, 64);
+          x[e] = (lane & h) ? (y - x[e]) : (x[e] + y);
+        }
+      }
+      if constexpr (PL == 2) {
+        const float lo = x[0], hi = x[1];
+        x[0] = lo + hi;
+        x[1] = lo - hi;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PL; ++e)
+      if (lane + 64 * e < D) wv[lane + 64 * e] = x[e];
   }
   __syncthreads();
-  if (a.rk == RK_WHT || a.rk == RK_RHT) {
-    for (int h = 1; h < D; h <<= 1) {
-      for (int pi = tid; pi < GT * D / 2; pi += 256) {
-        const int hh = pi / (D / 2), r = pi - hh * (D / 2);
-        const int i = (r / h) * 2 * h + (r % h);     // i has bit h clear
-        const float p = wv[hh * D + i], q = wv[hh * D + i + h];
-        wv[hh * D + i] = p + q;
-        wv[hh * D + i + h] = p - q;
-      }
-      __syncthreads();
-    }
-  }
-  // with a full-precision window: one more log-sum-exp merge, in the
-  // original space (the window partial is already there)
-  for (int item = tid; item < GT * D; item += 256) {
-    const int hh = item / D, i = item - hh * D;
-    const size_t row = (size_t)b * a.Hq + hq0 + hh;
-    float num = wv[hh * D + i] * a.oscale, den = res[hh * NS + 1];
+  if (tid < D) {
+    const int i = tid;
+    float num = wv[i] * a.oscale, den = res[1];
     if (a.rk == RK_RHT && ((a.rsign[i >> 5] >> (i & 31)) & 1u)) num = -num;
-    if (a.rk == RK_QR) num = dense_rotate_back<D>(a.Q, wv + hh * D, i);
+    if (a.rk == RK_QR) num = dense_rotate_back<D>(a.Q, wv, i);
     if (a.wpart) {
-      const float *wp = a.wpart + row * (2 + D);
-      const float mc = mx[hh], mu = wp[0];
-      const float m = fmaxf(mc, mu);
-      const float ac = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - m);
-      const float au = (mu == -INFINITY) ? 0.0f : fast_exp2(mu - m);
-      num = ac * num + au * wp[2 + i];
-      den = ac * den + au * wp[1];
+      // one more log-sum-exp merge, in the original space (the window partial
+      // is already there)
+      const float mc = m, mu = wm;
+      const float mm = fmaxf(mc, mu);
+      const float ac = (mc == -INFINITY) ? 0.0f : fast_exp2(mc - mm);
+      const float au = (mu == -INFINITY) ? 0.0f : fast_exp2(mu - mm);
+      num = ac * num + au * wo;
+      den = ac * den + au * wl;
     }
-    a.out[row * D + i] = num / den;
+    a.out[(size_t)row * D + i] = num / den;
   }
 }
-
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// Split merge of one query row (b, hq): log-sum-exp weights, S^T a, inverse
-// rotation, division by L (and the full-precision window, if any).
-template <int D, bool VQ>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) float sm[256 + 2 + 2 * D];
-  __shared__ float mx[1];
-  const int row = blockIdx.x;
-  const int b = row / a.Hq, hq = row - (row / a.Hq) * a.Hq;
-  merge_splits<D, VQ, 1>(a, sm, mx, b, hq);
-}
 
 template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 // (three blocks per CU: registers <= 168)

@@ -344,6 +344,44 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
     return op8(lo.x, lo.y, hi.x, hi.y);
   };
 
+  // ---- q' = R q qscale of the block's heads, when not prepared beforehand ------
+  // wave h takes head h: lane l holds coordinates l and l + 64, the butterfly
+  // stages run in ascending h as in the query-preparation kernel (partner
+  // lane l ^ h; the last stage within the lane), with the same operations, so
+  // q' is bit for bit the one that kernel writes
+  __shared__ __attribute__((aligned(16))) float qv_s[4 * D];
+  if (a.qsrc) {
+    if (wave < GT) {
+      const size_t row = (size_t)b * a.Hq + hq0 + wave;
+      float x0, x1;
+      if (a.q_bf16) {
+        x0 = bf16_to_f32(((const uint16_t *)a.qsrc)[row * D + lane]);
+        x1 = bf16_to_f32(((const uint16_t *)a.qsrc)[row * D + lane + 64]);
+      } else {
+        x0 = ((const float *)a.qsrc)[row * D + lane];
+        x1 = ((const float *)a.qsrc)[row * D + lane + 64];
+      }
+      if (a.rk == RK_RHT) {
+        if ((a.rsign[lane >> 5] >> (lane & 31)) & 1u) x0 = -x0;
+        if ((a.rsign[2 + (lane >> 5)] >> (lane & 31)) & 1u) x1 = -x1;
+      }
+      if (a.rk == RK_WHT || a.rk == RK_RHT) {
+#pragma unroll
+        for (int h = 1; h < 64; h <<= 1) {
+          const float q0 = __shfl_xor(x0, h, 64), q1 = __shfl_xor(x1, h, 64);
+          x0 = (lane & h) ? (q0 - x0) : (x0 + q0);
+          x1 = (lane & h) ? (q1 - x1) : (x1 + q1);
+        }
+        const float lo = x0, hi = x1;
+        x0 = lo + hi;
+        x1 = lo - hi;
+      }
+      qv_s[lane * GT + wave] = x0 * a.qscale;
+      qv_s[(lane + 64) * GT + wave] = x1 * a.qscale;
+    }
+    __syncthreads();
+  }
+
   // ---- prepared query as the A operand of the score product -------------------
   // lane (row = 4 h + kind, g); step j slot e <-> coordinate 32 g + 8 j + e;
   // kind 0: q' hi, kind 1: q' lo (kinds 2, 3: zero here)
@@ -351,7 +389,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
   f16x8 qa[4];
   float unsc_q;
   {
-    const float *qv = a.qt + unitg * D * GT;
+    const float *qv = a.qsrc ? qv_s : a.qt + unitg * D * GT;
     float v[32];
     float m = 0.0f;
 #pragma unroll
