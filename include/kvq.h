@@ -123,8 +123,8 @@ kvq_status kvq_sketch_init(uint64_t seed, int m, int d, uint16_t *S_bf16_host);
  * byte 4 vb n, holding for coordinate 8n+j and slot 4q+r:
  *   vb 4: byte 2j + r/2, bits 4 (r%2) .. +3
  *   vb 3: the 6-bit field u = 2j + r/2 = code(4q + 2(r/2)) | code(+1) << 3;
- *         u < 12: bits 0..5 of byte u; u >= 12: its bit pairs (0,1), (2,3),
- *         (4,5) in bits 6, 7 of bytes u-12, u-8, u-4
+ *         u < 12: bits 2..7 of byte u; u >= 12: its bit pairs (0,1), (2,3),
+ *         (4,5) in bits 0, 1 of bytes u-12, u-8, u-4
  *   vb 2: byte j, bits 2r .. 2r+1;   vb 1: byte j/2, bit 4 (j%2) + r
  * and the sign bits of slots 8o .. 8o+7 share bytes [128 o, 128 o + 128):
  * bit e of byte 128 o + k = sign of slot 8o + e at sketch row k. */

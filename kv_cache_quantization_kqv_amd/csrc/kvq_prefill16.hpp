@@ -51,10 +51,10 @@ __device__ __forceinline__ uint32_t piece_code(const uint32_t *w, int j, int r) 
     const int u = 2 * j + (r >> 1);
     uint32_t P;
     if (u < 12) {
-      P = byte(u) & 63u;
+      P = byte(u) >> 2;
     } else {
       const int m = u - 12;
-      P = (byte(m) >> 6) | ((byte(4 + m) >> 6) << 2) | ((byte(8 + m) >> 6) << 4);
+      P = (byte(m) & 3u) | ((byte(4 + m) & 3u) << 2) | ((byte(8 + m) & 3u) << 4);
     }
     return (P >> (3 * (r & 1))) & 7u;
   } else if constexpr (VB == 2) {

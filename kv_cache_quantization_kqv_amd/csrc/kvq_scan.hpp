@@ -233,23 +233,25 @@ __device__ __forceinline__ f16x8 key_operand(const uint32_t *k, int j, const uin
 
 // A operand of value step j (coordinate 8n + j) over a block pair: slots
 // 0..3 = tokens 4g .. 4g+3 of the first block (piece a), 4..7 = those of the
-// second (piece b).  h3a / h3b: width 3, fields 12..15 of a piece gathered
-// into the bytes of one dword (once per block).
+// second (piece b).  value_field: the byte offset of field u's entry in the
+// 4-byte pair table.  Width 3 stores fields 0..11 as 4 P in their bytes (one
+// mask), and h3a / h3b gather fields 12..15 of a piece, also as 4 P, into the
+// bytes of one dword (once per block).
 template <int VB>
 __device__ __forceinline__ uint32_t value_field(const uint32_t *v, uint32_t h3, int u) {
-  if constexpr (VB == 4) return (v[u >> 2] >> (8 * (u & 3))) & 255u;
-  if (u < 12) return (v[u >> 2] >> (8 * (u & 3))) & 63u;
-  return (h3 >> (8 * (u - 12))) & 63u;
+  if constexpr (VB == 4) return 4 * ((v[u >> 2] >> (8 * (u & 3))) & 255u);
+  if (u < 12) return (v[u >> 2] >> (8 * (u & 3))) & 0xFCu;
+  return (h3 >> (8 * (u - 12))) & 255u;
 }
 
 template <int VB>
 __device__ __forceinline__ f16x8 value_operand(const uint32_t *va, uint32_t h3a, const uint32_t *vb,
                                                uint32_t h3b, int j, const uint8_t *tab) {
   if constexpr (VB == 4 || VB == 3) {
-    const uint32_t t0 = *(const uint32_t *)(tab + 4 * value_field<VB>(va, h3a, 2 * j));
-    const uint32_t t1 = *(const uint32_t *)(tab + 4 * value_field<VB>(va, h3a, 2 * j + 1));
-    const uint32_t t2 = *(const uint32_t *)(tab + 4 * value_field<VB>(vb, h3b, 2 * j));
-    const uint32_t t3 = *(const uint32_t *)(tab + 4 * value_field<VB>(vb, h3b, 2 * j + 1));
+    const uint32_t t0 = *(const uint32_t *)(tab + value_field<VB>(va, h3a, 2 * j));
+    const uint32_t t1 = *(const uint32_t *)(tab + value_field<VB>(va, h3a, 2 * j + 1));
+    const uint32_t t2 = *(const uint32_t *)(tab + value_field<VB>(vb, h3b, 2 * j));
+    const uint32_t t3 = *(const uint32_t *)(tab + value_field<VB>(vb, h3b, 2 * j + 1));
     return op8(t0, t1, t2, t3);
   } else if constexpr (VB == 2) {
     const u32x2 ta = *(const u32x2 *)(tab + 8 * ((va[j >> 2] >> (8 * (j & 3))) & 255u));
@@ -525,8 +527,8 @@ __global__ __launch_bounds__(256) void scan_kernel(const DecodeArgs a) {
                          __builtin_amdgcn_perm(XB.y, XB.x, selV), __builtin_amdgcn_perm(XB.w, XB.z, selV));
     uint32_t h3a = 0u, h3b = 0u;
     if constexpr (VB == 3) {
-      h3a = ((RA.v[0] >> 6) & 0x03030303u) | ((RA.v[1] >> 4) & 0x0C0C0C0Cu) | ((RA.v[2] >> 2) & 0x30303030u);
-      h3b = ((RB.v[0] >> 6) & 0x03030303u) | ((RB.v[1] >> 4) & 0x0C0C0C0Cu) | ((RB.v[2] >> 2) & 0x30303030u);
+      h3a = ((RA.v[0] & 0x03030303u) << 2) | ((RA.v[1] & 0x03030303u) << 4) | ((RA.v[2] & 0x03030303u) << 6);
+      h3b = ((RB.v[0] & 0x03030303u) << 2) | ((RB.v[1] & 0x03030303u) << 4) | ((RB.v[2] & 0x03030303u) << 6);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)

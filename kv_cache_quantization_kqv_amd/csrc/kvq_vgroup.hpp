@@ -12,8 +12,10 @@
 //   c_r(j) = code of slot 4q + r at coordinate 8n + j:
 //     b 4: byte 2j + p = c_{2p}(j) | c_{2p+1}(j) << 4                  (pair index)
 //     b 3: field u = 2j + p holds P = c_{2p}(j) | c_{2p+1}(j) << 3; fields
-//          0..11 are bits 0..5 of bytes 0..11, field 12 + m has its bit
-//          pairs (0,1), (2,3), (4,5) in bits 6, 7 of bytes m, 4 + m, 8 + m
+//          0..11 are bits 2..7 of bytes 0..11 (a byte with its low two bits
+//          cleared is 4 P, the byte offset of entry P in a 4-byte table),
+//          field 12 + m has its bit pairs (0,1), (2,3), (4,5) in bits 0, 1
+//          of bytes m, 4 + m, 8 + m
 //     b 2: byte j = c_0(j) | c_1(j) << 2 | c_2(j) << 4 | c_3(j) << 6   (quad index)
 //     b 1: bits 4j .. 4j+3 = c_0(j) | c_1(j) << 1 | c_2(j) << 2 | c_3(j) << 3
 //   sign bits: slots 8o .. 8o+7 own bytes [128 o, 128 o + 128); bit e of
@@ -38,10 +40,10 @@ __device__ __forceinline__ uint32_t vg_code(const uint8_t *vc, size_t slot, int 
     const int u = 2 * j + (r >> 1);
     uint32_t P;
     if (u < 12) {
-      P = piece[u] & 63u;
+      P = piece[u] >> 2;
     } else {
       const int m = u - 12;
-      P = (piece[m] >> 6) | ((piece[4 + m] >> 6) << 2) | ((piece[8 + m] >> 6) << 4);
+      P = (piece[m] & 3u) | ((piece[4 + m] & 3u) << 2) | ((piece[8 + m] & 3u) << 4);
     }
     return (P >> (3 * (r & 1))) & 7u;
   } else if constexpr (VB == 2) {
@@ -91,13 +93,12 @@ __device__ __forceinline__ void vg_piece(const uint32_t (&N)[4], uint32_t (&w)[V
         const uint32_t y = vg_nib_pairs(N[2 * p], N[2 * p + 1], h);
         q[p][h] = (y & 0x0F0F0F0Fu) | ((y >> 1) & 0x78787878u);
       }
-    w[0] = __builtin_amdgcn_perm(q[1][0], q[0][0], 0x05010400u);   // fields 0..3
-    w[1] = __builtin_amdgcn_perm(q[1][0], q[0][0], 0x07030602u);   // fields 4..7
-    w[2] = __builtin_amdgcn_perm(q[1][1], q[0][1], 0x05010400u);   // fields 8..11
+    // fields 0..11 move to bits 2..7 of their bytes (6-bit values: nothing
+    // crosses a byte), fields 12..15 fill bits 0, 1
     const uint32_t t = __builtin_amdgcn_perm(q[1][1], q[0][1], 0x07030602u);   // 12..15
-    w[0] |= (t & 0x03030303u) << 6;
-    w[1] |= ((t >> 2) & 0x03030303u) << 6;
-    w[2] |= ((t >> 4) & 0x03030303u) << 6;
+    w[0] = (__builtin_amdgcn_perm(q[1][0], q[0][0], 0x05010400u) << 2) | (t & 0x03030303u);
+    w[1] = (__builtin_amdgcn_perm(q[1][0], q[0][0], 0x07030602u) << 2) | ((t >> 2) & 0x03030303u);
+    w[2] = (__builtin_amdgcn_perm(q[1][1], q[0][1], 0x05010400u) << 2) | ((t >> 4) & 0x03030303u);
   } else if constexpr (VB == 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

@@ -242,7 +242,7 @@ static int get_code(const uint8_t *rec, int d, int bits, int i) {
  * j = c % 8, bit i of the code of (slot, c) is at
  *   b = 4: byte 2j + r/2 of the piece, bit 4 (r%2) + i
  *   b = 3: P = the 6-bit pair field u = 2j + r/2, bit pb = 3 (r%2) + i of P;
- *          u < 12: byte u, bit pb; u >= 12: byte 4 (pb/2) + u - 12, bit 6 + pb%2
+ *          u < 12: byte u, bit 2 + pb; u >= 12: byte 4 (pb/2) + u - 12, bit pb%2
  *   b = 2: byte j, bit 2r + i
  *   b = 1: byte j/2, bit 4 (j%2) + r
  * Sign bits: slots 8o .. 8o+7 share bytes [128 o, 128 o + 128); the sign of
@@ -258,10 +258,10 @@ void orc_vgroup_code_bit(int bits, size_t slot, int c, int i, size_t *byte, int 
     const int u = 2 * j + r / 2, pb = 3 * (r % 2) + i;
     if (u < 12) {
       *byte = piece + (size_t)u;
-      *bit = pb;
+      *bit = 2 + pb;
     } else {
       *byte = piece + (size_t)(4 * (pb / 2) + u - 12);
-      *bit = 6 + pb % 2;
+      *bit = pb % 2;
     }
   } else if (bits == 2) {
     *byte = piece + (size_t)j;

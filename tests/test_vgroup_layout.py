@@ -66,17 +66,17 @@ def test_sign_positions_fill_each_octet_exactly_once():
 
 def test_pair_fields_of_three_bit_codes():
     """Width 3: the codes of slots 2p and 2p + 1 of a quad form one 6-bit pair
-    field per coordinate; fields 0..11 of a piece are the low 6 bits of its
-    bytes and fields 12..15 are spread over bits 6 and 7 of three bytes."""
+    field per coordinate; fields 0..11 of a piece are the high 6 bits of its
+    bytes and fields 12..15 are spread over bits 0 and 1 of three bytes."""
     for c in range(8):                        # piece 0, j = c
         for p in range(2):
             u = 2 * c + p
             pos = [_code_bit(3, 2 * p + q, c, i) for q in range(2) for i in range(3)]
             if u < 12:
-                assert pos == [(u, b) for b in range(6)]
+                assert pos == [(u, 2 + b) for b in range(6)]
             else:
                 m = u - 12
-                assert pos == [(m, 6), (m, 7), (4 + m, 6), (4 + m, 7), (8 + m, 6), (8 + m, 7)]
+                assert pos == [(m, 0), (m, 1), (4 + m, 0), (4 + m, 1), (8 + m, 0), (8 + m, 1)]
 
 
 def _caches(scheme, n, values, cap=48):
