@@ -249,6 +249,26 @@ __device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables<B
   else return bucketize_lut<BITS>(u, bt);
 }
 
+// y[i] <- y[i] + s * (y[i] of the partner lane, lane ^ 1), for 8 coordinates,
+// one v_fmac_f32 with a DPP quad-permute source each: s = +-1 makes the
+// product exact, so each result is the one rounding of y[i] +- partner.  The
+// leading s_nop gives the DPP reads the two wait states they need after the
+// VALU writes that produced y (issued before the block).
+__device__ __forceinline__ void fmac_xor1_x8(float *y, float s) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7])
+      : "v"(s));
+}
+
 // Value of the partner lane (lane ^ 1) through a DPP quad permute (no LDS).
 __device__ __forceinline__ float xor1_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -668,17 +688,19 @@ void quantize_kernel(const QuantArgs a) {
       for (int i = 0; i < DL; ++i)
         y[i] = __uint_as_float(__float_as_uint(y[i]) ^ ((m[i >> 5] << (31 - (i & 31))) & 0x80000000u));
     }
+    // sign of this lane's coordinates as held (see the last butterfly stage)
+    float held = 1.0f;
     if constexpr (RK != RK_NONE) {
       wht_inplace<DL>(y);
       if constexpr (LPV == 2) {
-        // last stage: (y_i, y_{i+DL}) -> (y_i + y_{i+DL}, y_i - y_{i+DL}); the upper
-        // lane forms partner + (-own), which is the same rounded difference.
-        const uint32_t flip = half ? 0x80000000u : 0u;
+        // last stage: (y_i, y_{i+DL}) -> (y_i + y_{i+DL}, y_i - y_{i+DL}).  The
+        // lower lane forms own + partner; the upper lane own - partner, the
+        // exact negation of the rounded difference, and keeps that sign until
+        // the scaling below (the squares do not see it).
+        held = half ? -1.0f : 1.0f;
+        static_assert(DL % 8 == 0, "butterfly stage in groups of 8");
 #pragma unroll
-        for (int i = 0; i < DL; ++i) {
-          const float other = xor1_f(y[i]);
-          y[i] = other + __uint_as_float(__float_as_uint(y[i]) ^ flip);
-        }
+        for (int i = 0; i < DL; i += 8) fmac_xor1_x8(y + i, held);
       }
     }
     float ss = pairwise_sumsq<DL>(y);
@@ -687,7 +709,8 @@ void quantize_kernel(const QuantArgs a) {
       ss = half ? (o + ss) : (ss + o);
     }
     const float nu = sqrtf(ss);
-    const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
+    // u = y * (1/nu) with the held sign folded in (a negation is exact)
+    const float rcp = nu == 0.0f ? 0.0f : held * (1.0f / nu);
     // codes: the record layout (per-slot records), or one nibble per
     // coordinate (token groups: the regrouping reads nibbles)
     LocalCodes<DL, BITS> lc;
