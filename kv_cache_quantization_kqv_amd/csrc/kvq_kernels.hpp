@@ -441,15 +441,24 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       }
       // certified signs
       const float bound = fmaf(a_snmax, rbt, 0x1p-100f);
-      uint32_t bits = 0u, unsure = 0u;
+      uint32_t unsure = 0u;
       float zmin = INFINITY;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int bp = 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);   // bit = sketch row % 32
-        const float z = acc[j];
-        bits |= (z > 0.0f ? 1u : 0u) << bp;
-        zmin = fminf(zmin, fabsf(z));
+      for (int j = 0; j < 16; ++j) zmin = fminf(zmin, fabsf(acc[j]));
+      // bit 8 (j >> 2) + 4 (lane >> 5) + (j & 3) = sketch row % 32 of entry j.
+      // Where |z| > bound (> 0), z > 0 is exactly "sign bit clear": the sign
+      // bits enter one funnel shift each (v_alignbit), highest position
+      // first, with four zero bits between the groups of four; the other
+      // entries are settled below.
+      uint32_t neg = 0u;
+#pragma unroll
+      for (int g = 3; g >= 0; --g) {
+        if (g < 3) neg <<= 4;
+#pragma unroll
+        for (int e = 3; e >= 0; --e)
+          neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(acc[4 * g + e]), 31);
       }
+      uint32_t bits = (~neg & 0x0F0F0F0Fu) << (4 * (lane >> 5));
       // the per-bit mask only where some entry of the wave is uncertain (rare);
       // !(zmin > bound) also catches NaN
       const bool trow = t >= rlo && t < nvalid;
