@@ -53,7 +53,8 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = 1,       /* a required pointer is NULL */
   KVQ_ERR_ALIGN = 2,      /* a pointer or stride breaks the 16-byte alignment rule */
-  KVQ_ERR_DIM = 3,        /* head dimension not in {16, 32, 64, 128} */
+  KVQ_ERR_DIM = 3,        /* head dimension not in {8, 16, 32, 64, 128, 256} (or, at 8 and
+                             256, the dense rotation) */
   KVQ_ERR_BITS = 4,       /* bit width out of range for the scheme */
   KVQ_ERR_SCHEME = 5,     /* unknown scheme */
   KVQ_ERR_CAPACITY = 6,   /* t0 + T or n_ctx exceeds the cache capacity */
@@ -136,7 +137,7 @@ typedef struct {
   uint8_t *k_codes, *k_signs, *v_codes, *v_signs;
   uint16_t *k_norm, *k_rnorm, *v_norm, *v_rnorm;
   int32_t rot_kind;                              /* kvq_rotation (rotated schemes) */
-  uint32_t rot_signs[4];                         /* RHT: bit i%32 of word i/32 = negate x_i */
+  uint32_t rot_signs[8];                         /* RHT: bit i%32 of word i/32 = negate x_i */
   const float *rot_Q;                            /* QR: device, d*d fp32 row-major, else NULL */
 } kvq_cache;
 
@@ -161,9 +162,10 @@ kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
                                   const float *Q_device);
 
 /* Random diagonal of KVQ_ROT_RHT: bit i = SplitMix64 stream from `seed`, one
- * draw per coordinate, its top bit.  Host; out = 4 words (unused bits 0).
- * Errors: KVQ_ERR_NULL, KVQ_ERR_DIM (d not in {16, 32, 64, 128}). */
-kvq_status kvq_rotation_signs(uint64_t seed, int d, uint32_t out[4]);
+ * draw per coordinate, its top bit.  Host; out = 8 words (bits at and beyond
+ * d are 0).  Errors: KVQ_ERR_NULL, KVQ_ERR_DIM (d not a supported head
+ * dimension). */
+kvq_status kvq_rotation_signs(uint64_t seed, int d, uint32_t out[8]);
 
 /* Random rotation of KVQ_ROT_QR, Haar-distributed on SO(d) ("Rotation
  * invariance guarantee"): a d x d standard Gaussian matrix (SplitMix64,
@@ -310,8 +312,9 @@ int kvq_decode_auto_splits(const kvq_cache *c, int q_heads, int n_ctx);
  * Same decoded-vector semantics as kvq_decode_attention (rotated-space
  * scoring, sketch-space value term, one S^T product per row).  workspace:
  * kvq_prefill_workspace bytes.  1 <= n_ctx <= capacity, n_q >= 1,
- * q_pos0 >= 0, causal in {0, 1}.
- * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_HEADS,
+ * q_pos0 >= 0, causal in {0, 1}.  Head dimensions 16 .. 256 (the tiles are
+ * 16 coordinates wide; d = 8 gives KVQ_ERR_DIM).
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_HEADS, KVQ_ERR_DIM,
  * KVQ_ERR_CAPACITY, KVQ_ERR_RANGE, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
 kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
                                  int n_q, int q_pos0, int causal, int n_ctx, float *out,

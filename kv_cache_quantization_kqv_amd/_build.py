@@ -27,7 +27,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
          "-I", os.path.join(ROOT, "include")]
 
-SOURCES = ["kvq_host.cpp", "kvq_d16.hip", "kvq_d32.hip", "kvq_d64.hip", "kvq_d128.hip"]
+SOURCES = ["kvq_host.cpp", "kvq_d8.hip", "kvq_d16.hip", "kvq_d32.hip", "kvq_d64.hip",
+           "kvq_d128.hip", "kvq_d256.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -179,7 +179,7 @@ kvq_status scheme_sides(int scheme, int n, Sides *s) {
   }
 }
 
-bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_dim(int d) { return d == 8 || d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
 
 // The encoder's table bucketize needs a symmetric threshold table with a zero
 // middle threshold, and at most one threshold in every cell of the prefix
@@ -189,10 +189,14 @@ bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool codebook_usable(const kvq_codebook &cb) {
   const int K = 1 << cb.bits, half = K / 2;
   const int shift = 23 - (cb.bits >= 4 ? 2 : 1);
+  // the cell table serves codes of 3 and 4 bits at d >= 16; compares (which
+  // need only the symmetry) serve the others
+  const bool cells = cb.bits > 2 && cb.d >= 16;
   if (cb.threshold[half - 1] != 0.0f) return false;
   for (int k = 0; k + 1 < half; ++k) {
     const float p = cb.threshold[half + k];
     if (!(p > 0.0f) || p >= 2.0f || cb.threshold[half - 2 - k] != -p) return false;
+    if (!cells) continue;
     if (k == 0) {
       uint32_t a;
       std::memcpy(&a, &p, 4);
@@ -213,7 +217,7 @@ bool codebook_usable(const kvq_codebook &cb) {
 
 // Sign words of the randomized Hadamard rotation: no bits at or beyond d.
 bool signs_fit(const uint32_t *w, int d) {
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 8; ++k) {
     const int lo = 32 * k;
     const uint32_t allowed = d >= lo + 32 ? 0xFFFFFFFFu : (d <= lo ? 0u : ((1u << (d - lo)) - 1u));
     if (w[k] & ~allowed) return false;
@@ -253,6 +257,7 @@ kvq_status check_cache(const kvq_cache *c) {
   if (c->rot_kind < KVQ_ROT_WHT || c->rot_kind > KVQ_ROT_QR) return KVQ_ERR_SCHEME;
   if (!s.rot && c->rot_kind != KVQ_ROT_WHT) return KVQ_ERR_SCHEME;
   if (c->rot_kind == KVQ_ROT_QR && !c->rot_Q) return KVQ_ERR_NULL;
+  if (c->rot_kind == KVQ_ROT_QR && (c->d < 16 || c->d > 128)) return KVQ_ERR_DIM;
   if (c->rot_kind == KVQ_ROT_RHT && !signs_fit(c->rot_signs, c->d)) return KVQ_ERR_RANGE;
   const void *ptrs[] = {c->k_codes, c->k_norm, c->v_codes, c->v_norm, c->k_signs, c->k_rnorm,
                         c->v_signs, c->v_rnorm, c->S,
@@ -267,9 +272,11 @@ kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_
 template <typename F>
 hipError_t by_dim(int d, F &&f) {
   switch (d) {
+    case 8: return f(std::integral_constant<int, 8>{});
     case 16: return f(std::integral_constant<int, 16>{});
     case 32: return f(std::integral_constant<int, 32>{});
     case 64: return f(std::integral_constant<int, 64>{});
+    case 256: return f(std::integral_constant<int, 256>{});
     default: return f(std::integral_constant<int, 128>{});
   }
 }
@@ -293,14 +300,16 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
   a.sb = sb; a.sh = sh; a.st = st;
   a.B = c->batch; a.H = c->kv_heads; a.T = T; a.t0 = t0; a.cap = c->capacity;
   const int rk = rot_code(c);
-  const int vt = (rk == kvq::RK_QR || c->d <= 64) ? 64 : 32;  // tokens per quantize tile
+  // tokens per quantize tile (64 / lanes per vector; one lane per vector for
+  // the dense rotation)
+  const int vt = (rk == kvq::RK_QR || c->d <= 64) ? 64 : (c->d == 128 ? 32 : 16);
   // tiles are aligned to vt slots: the first starts at t0 - t0 % vt
   a.tiles_per_bh = (t0 % vt + T + vt - 1) / vt;
   long long tiles = (long long)a.tiles_per_bh * a.B * a.H;
   if (tiles > (1ll << 31) - 1) return KVQ_ERR_RANGE;
   a.total_tiles = (int)tiles;
   a.scale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
-  for (int k = 0; k < 4; ++k) a.rsign[k] = c->rot_signs[k];
+  for (int k = 0; k < 8; ++k) a.rsign[k] = c->rot_signs[k];
   a.Q = c->rot_Q;
   const kvq_codebook &cb = side == 0 ? c->cb_k : c->cb_v;
   for (int i = 0; i < 16; ++i) a.cent[i] = cb.centroid[i];
@@ -526,28 +535,29 @@ kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
   if (!c) return KVQ_ERR_NULL;
   if (kind < KVQ_ROT_WHT || kind > KVQ_ROT_QR) return KVQ_ERR_SCHEME;
   if (!c->rotate && kind != KVQ_ROT_WHT) return KVQ_ERR_SCHEME;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   if (kind == KVQ_ROT_RHT) {
     if (!signs) return KVQ_ERR_NULL;
     const int nw = (c->d + 31) / 32;
-    for (int k = 0; k < nw && k < 4; ++k) w[k] = signs[k];
+    for (int k = 0; k < nw && k < 8; ++k) w[k] = signs[k];
     if (!signs_fit(w, c->d)) return KVQ_ERR_RANGE;
   }
   if (kind == KVQ_ROT_QR) {
+    if (c->d < 16 || c->d > 128) return KVQ_ERR_DIM;   // dense rotation: 16 <= d <= 128
     if (!Q_device) return KVQ_ERR_NULL;
     if (!aligned16(Q_device)) return KVQ_ERR_ALIGN;
   }
   c->rot_kind = kind;
-  for (int k = 0; k < 4; ++k) c->rot_signs[k] = w[k];
+  for (int k = 0; k < 8; ++k) c->rot_signs[k] = w[k];
   c->rot_Q = kind == KVQ_ROT_QR ? Q_device : nullptr;
   return KVQ_OK;
 }
 
-kvq_status kvq_rotation_signs(uint64_t seed, int d, uint32_t out[4]) {
+kvq_status kvq_rotation_signs(uint64_t seed, int d, uint32_t out[8]) {
   if (!out) return KVQ_ERR_NULL;
   if (!supported_dim(d)) return KVQ_ERR_DIM;
   uint64_t state = seed;
-  for (int k = 0; k < 4; ++k) out[k] = 0u;
+  for (int k = 0; k < 8; ++k) out[k] = 0u;
   for (int i = 0; i < d; ++i)
     if (splitmix64(state) >> 63) out[i >> 5] |= 1u << (i & 31);
   return KVQ_OK;
@@ -615,7 +625,7 @@ kvq_status kvq_dequantize(const kvq_cache *c, int which, int t0, int T, float *o
   a.coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   const int rk = rot_code(c);
   a.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)c->d)) : 1.0f;
-  for (int r = 0; r < 4; ++r) a.rsign[r] = c->rot_signs[r];
+  for (int r = 0; r < 8; ++r) a.rsign[r] = c->rot_signs[r];
   a.Q = c->rot_Q;
   const int bits = k ? c->k_bits : c->v_bits;
   const bool qjl = k ? c->k_qjl : c->v_qjl;
@@ -699,7 +709,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = gt; p.HG = G / gt;
   const int rk = rot_code(c);
   p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
-  for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
+  for (int k = 0; k < 8; ++k) p.rsign[k] = c->rot_signs[k];
   p.Q = c->rot_Q;
   // the matrix-core scan prepares q' itself (Hadamard kinds or none, no key
   // sketch): no query-preparation launch
@@ -740,7 +750,7 @@ kvq_status decode_impl(const kvq_cache *c, const void *q, int q_dtype, int q_hea
   a.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   a.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
   a.rk = rk;
-  for (int k = 0; k < 4; ++k) a.rsign[k] = c->rot_signs[k];
+  for (int k = 0; k < 8; ++k) a.rsign[k] = c->rot_signs[k];
   a.Q = c->rot_Q;
   for (int i = 0; i < 16; ++i) {
     a.kcent[i] = c->cb_k.centroid[i];
@@ -829,6 +839,7 @@ kvq_status prefill_impl(const kvq_cache *c, const void *q, int q_dtype, int q_he
                         size_t workspace_bytes, void *stream) {
   kvq_status s = check_cache(c);
   if (s != KVQ_OK) return s;
+  if (c->d < 16) return KVQ_ERR_DIM;   // the multi-query tiles are 16 coordinates wide
   if (!q || !out) return KVQ_ERR_NULL;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
   if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
@@ -864,7 +875,7 @@ kvq_status prefill_impl(const kvq_cache *c, const void *q, int q_dtype, int q_he
   p.Hq = q_heads; p.Hkv = c->kv_heads; p.G = G; p.GT = 1; p.HG = G;
   p.nq = n_q;
   p.qscale = hadamard_kind(rk) ? (float)(kLog2e / d) : (float)(kLog2e / std::sqrt((double)d));
-  for (int k = 0; k < 4; ++k) p.rsign[k] = c->rot_signs[k];
+  for (int k = 0; k < 8; ++k) p.rsign[k] = c->rot_signs[k];
   p.Q = c->rot_Q;
   hipError_t e = by_dim(d, [&](auto D) {
     return kvq::launch_prep<decltype(D)::value>(p, rk, c->k_qjl != 0, q_dtype == KVQ_BF16, hs);
@@ -915,7 +926,7 @@ kvq_status prefill_impl(const kvq_cache *c, const void *q, int q_dtype, int q_he
   f.vcoef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / c->m);
   f.oscale = hadamard_kind(rk) ? (float)(1.0 / std::sqrt((double)d)) : 1.0f;
   f.rk = rk;
-  for (int k = 0; k < 4; ++k) f.rsign[k] = c->rot_signs[k];
+  for (int k = 0; k < 8; ++k) f.rsign[k] = c->rot_signs[k];
   f.Q = c->rot_Q;
   f.Hkv = c->kv_heads; f.Hq = q_heads; f.G = G; f.nq = n_q; f.rows = (int)rows;
   f.splits = a.splits;

@@ -35,7 +35,7 @@ struct QuantArgs {
   const uint16_t *S;         // m x d bf16 (sketch sides)
   uint8_t *codes, *signs;
   uint16_t *norm, *rnorm;
-  uint32_t rsign[4];         // RK_RHT: coordinate i negated when bit i is set
+  uint32_t rsign[8];         // RK_RHT: coordinate i negated when bit i is set
   const float *Q;            // RK_QR: d x d row-major
 };
 
@@ -48,7 +48,7 @@ struct DequantArgs {
   float cent[16];
   float coef;                // sqrt(pi/2)/m
   float oscale;              // 1/sqrt(d) for the Hadamard kinds, else 1
-  uint32_t rsign[4];         // RK_RHT
+  uint32_t rsign[8];         // RK_RHT
   const float *Q;            // RK_QR
   int vg;                    // token-group storage (value side at d = 128)
 };
@@ -61,7 +61,7 @@ struct PrepArgs {
   int rows;                  // B * Hq
   int Hq, Hkv, G, GT, HG;    // G = Hq / Hkv query heads per KV head, GT per block, HG = G / GT
   float qscale;              // log2(e)/d (Hadamard kinds) or log2(e)/sqrt(d)
-  uint32_t rsign[4];         // RK_RHT
+  uint32_t rsign[8];         // RK_RHT
   const float *Q;            // RK_QR
   int nq;                    // > 0: multi-query layout (rows (b, i, hq) of [B][nq][Hq][d];
                              // output [B][Hkv][nq * G][d], row i * G + g)
@@ -79,7 +79,7 @@ struct DecodeArgs {
   float vcoef;               // sqrt(pi/2)/m (V sketch)
   float oscale;              // 1/sqrt(d) for the Hadamard kinds, else 1
   int rk;                    // rotation kind (RK_*), undone in the merge
-  uint32_t rsign[4];         // RK_RHT
+  uint32_t rsign[8];         // RK_RHT
   const float *Q;            // RK_QR
   const float *wpart;        // full-precision window partial [B][Hq][2 + d] or null
   // the query itself ([B][Hq][d], bf16 when q_bf16) when the matrix-core scan
@@ -115,7 +115,7 @@ struct FinishArgs {
   float *out;                // [B][nq][Hq][d]
   float vcoef, oscale;
   int rk;
-  uint32_t rsign[4];
+  uint32_t rsign[8];
   const float *Q;
   int Hkv, Hq, G, nq;
   int rows;                  // B * Hkv * nq * G

@@ -182,11 +182,12 @@ __device__ __forceinline__ void store_bytes(uint8_t *dst, const uint32_t *w) {
 // zero threshold compare as IEEE floats do).
 // ---------------------------------------------------------------------------
 // Codes of at most kCmpMaxBits bits are found by compares against the
-// thresholds; wider ones through the cell table.
+// thresholds; wider ones through the cell table, except at d = 8, where
+// neighbouring thresholds can share a cell (compares for every width).
 constexpr int kCmpMaxBits = 2;
-template <int BITS>
+template <int BITS, bool CELLS = true>
 struct BucketTables {
-  static constexpr bool LUT = BITS > kCmpMaxBits;
+  static constexpr bool LUT = CELLS && BITS > kCmpMaxBits;
   static constexpr int MB = BITS >= 4 ? 2 : 1;       // mantissa bits of the cell prefix
   static constexpr int SHIFT = 23 - MB;
   static constexpr int NCELL = 1 << (9 + MB);
@@ -194,10 +195,10 @@ struct BucketTables {
   float cent[16];
 };
 
-template <int BITS>
-__device__ void build_bucket_tables(BucketTables<BITS> &bt, const float *thr, const float *cent,
+template <int BITS, bool CELLS>
+__device__ void build_bucket_tables(BucketTables<BITS, CELLS> &bt, const float *thr, const float *cent,
                                     int tid, int nthreads) {
-  using BT = BucketTables<BITS>;
+  using BT = BucketTables<BITS, CELLS>;
   constexpr int K = 1 << BITS;
   if constexpr (BT::LUT) {
     for (int i = tid; i < BT::NCELL; i += nthreads) {
@@ -221,8 +222,8 @@ __device__ void build_bucket_tables(BucketTables<BITS> &bt, const float *thr, co
 }
 
 template <int BITS>
-__device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables<BITS> &bt) {
-  const f32x2 e = bt.cell[__float_as_uint(u) >> BucketTables<BITS>::SHIFT];
+__device__ __forceinline__ uint32_t bucketize_lut(float u, const BucketTables<BITS, true> &bt) {
+  const f32x2 e = bt.cell[__float_as_uint(u) >> BucketTables<BITS, true>::SHIFT];
   return __float_as_uint(e.y) + (e.x < u ? 1u : 0u);
 }
 
@@ -243,9 +244,9 @@ __device__ __forceinline__ uint32_t bucketize_cmp(float u, const float *thr) {
   return n ^ (neg ? 2u * K2 - 1u : 0u);
 }
 
-template <int BITS>
-__device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables<BITS> &bt, const float *thr) {
-  if constexpr (BITS <= kCmpMaxBits) return bucketize_cmp<BITS>(u, thr);
+template <int BITS, bool CELLS>
+__device__ __forceinline__ uint32_t bucketize_code(float u, const BucketTables<BITS, CELLS> &bt, const float *thr) {
+  if constexpr (!BucketTables<BITS, CELLS>::LUT) return bucketize_cmp<BITS>(u, thr);
   else return bucketize_lut<BITS>(u, bt);
 }
 
@@ -267,6 +268,27 @@ __device__ __forceinline__ void fmac_xor1_x8(float *y, float s) {
       "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
       : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7])
       : "v"(s));
+}
+
+// As fmac_xor1_x8 with the partner lane ^ 2.
+__device__ __forceinline__ void fmac_xor2_x8(float *y, float s) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7])
+      : "v"(s));
+}
+
+// Value of the partner lane (lane ^ 2) through a DPP quad permute.
+__device__ __forceinline__ float xor2_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
 }
 
 // Value of the partner lane (lane ^ 1) through a DPP quad permute (no LDS).
@@ -296,7 +318,7 @@ __device__ __forceinline__ float lane_f(float v, int l) {
 // words) followed by a 1-bit plane image (DL/32 words, at least one).
 template <int DL, int BITS>
 struct LocalCodes {
-  static constexpr int NA = BITS == 3 ? DL / 16 : (DL * BITS + 31) / 32;
+  static constexpr int NA = BITS == 3 ? (2 * DL + 31) / 32 : (DL * BITS + 31) / 32;
   static constexpr int NB = BITS == 3 ? (DL + 31) / 32 : 0;
   uint32_t w[NA + NB];
   __device__ __forceinline__ void clear() {
@@ -339,6 +361,20 @@ __device__ __forceinline__ void join_halves(uint32_t *rec, const LocalCodes<DL, 
   }
 }
 
+// One lane's quarter of a d = 256 record (LPV = 4): codes of coordinates
+// [DL q, DL q + DL).  Widths 1, 2, 4: bytes [q DL b/8, ...); width 3: bytes
+// [q DL/4, ...) of the 2-bit plane and [D/4 + q DL/8, ...) of the 1-bit plane.
+template <int D, int DL, int BITS>
+__device__ __forceinline__ void store_quarter(uint8_t *rec, const LocalCodes<DL, BITS> &lc, int q) {
+  using LC = LocalCodes<DL, BITS>;
+  if constexpr (BITS == 3) {
+    store_bytes<DL / 4>(rec + q * (DL / 4), lc.w);
+    store_bytes<DL / 8>(rec + D / 4 + q * (DL / 8), lc.w + LC::NA);
+  } else {
+    store_bytes<DL * BITS / 8>(rec + q * (DL * BITS / 8), lc.w);
+  }
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -363,9 +399,9 @@ __device__ __forceinline__ void stage_sketch(unsigned char *S_s, const uint16_t 
 }
 
 // Largest sketch row norm (fp32, rounded up), for the sign-certification bound.
-template <int D>
+template <int D, int SP = D * 2 + 16>
 __device__ __forceinline__ float sketch_row_norm_max(const unsigned char *S_s, int lane) {
-  constexpr int P2 = D * 2 + 16;
+  constexpr int P2 = SP;
   constexpr int NCT = (D + 31) / 32;
   float mx = 0.0f;
 #pragma unroll 1
@@ -404,23 +440,53 @@ __device__ __forceinline__ float sketch_row_norm_max(const unsigned char *S_s, i
 namespace kvq {
 
 // Rows rlo <= t < nvalid of the tile are tokens; their sign records go to
-// signs_out at slot0 + t, or (TO_LDS, d = 128) to srows + SP t in LDS.
-template <int D, int NRT, bool TO_LDS = false, int SP = 16>
+// signs_out at slot0 + t, or (TO_LDS, d = 128) to srows + SP t in LDS.  S_s:
+// the sketch rows, SPITCH bytes apart (staged in LDS, or in memory at d =
+// 256); the stage holds VTR rows (a 32-row block past them reads as zero).
+// Below d = 16 (one sketch MFMA step would exceed the row) every sign is the
+// ascending fp64 sum itself, one token per lane.
+template <int D, int NRT, bool TO_LDS = false, int SP = 16, int SPITCH = D * 2 + 16,
+          int VTR = 32 * NRT>
 __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const unsigned char *S_s,
                                              const float *rn_s, float a_snmax, int rlo, int nvalid,
                                              size_t slot0, uint8_t *signs_out, uint8_t *srows,
                                              int lane) {
   constexpr int P2 = D * 2 + 16;
   constexpr int NCT = (D + 31) / 32;
+  if constexpr (D < 16) {
+    static_assert(!TO_LDS && D % 8 == 0, "direct signs: per-slot records of whole bytes");
+#pragma unroll 1
+    for (int t = lane; t < VTR; t += 64) {
+      if (t < rlo || t >= nvalid) continue;
+      const uint16_t *rr = (const uint16_t *)(stage + t * P2);
+      uint8_t *dst = signs_out + (slot0 + (size_t)t) * (D / 8);
+#pragma unroll
+      for (int kb = 0; kb < D / 8; ++kb) {
+        uint32_t by = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t *sr = (const uint16_t *)(S_s + (8 * kb + e) * SPITCH);
+          double sum = 0.0;
+          for (int i = 0; i < D; ++i)
+            sum = sum + (double)bf16_to_f32(sr[i]) * (double)bf16_to_f32(rr[i]);
+          by |= (sum >= 0.0 ? 1u : 0u) << e;
+        }
+        dst[kb] = (uint8_t)by;
+      }
+    }
+    return;
+  }
 #pragma unroll 1
   for (int rt = 0; rt < NRT; ++rt) {
     const int t = rt * 32 + (lane & 31);                  // token row in the tile
-    const float rbt = rn_s[t];
+    const bool tin = t < VTR;
+    const float rbt = tin ? rn_s[t] : 0.0f;
     // B operands (this block's residual rows), read once for all row blocks
-    u32x4 rv[D / 16];
+    u32x4 rv[D >= 16 ? D / 16 : 1];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      rv[ks] = *(const u32x4 *)(stage + t * P2 + (ks * 16 + 8 * (lane >> 5)) * 2);
+      rv[ks] = tin ? *(const u32x4 *)(stage + t * P2 + (ks * 16 + 8 * (lane >> 5)) * 2)
+                   : u32x4{0u, 0u, 0u, 0u};
     uint32_t sgw[NCT];
 #pragma unroll 1
     for (int ct = 0; ct < NCT; ++ct) {
@@ -433,7 +499,7 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const int k0 = ks * 16 + 8 * (lane >> 5);
-        u32x4 sv = *(const u32x4 *)(S_s + ks_row * P2 + k0 * 2);
+        u32x4 sv = *(const u32x4 *)(S_s + ks_row * SPITCH + k0 * 2);
         if (!kok) sv = u32x4{0u, 0u, 0u, 0u};
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sv),
                                                       __builtin_bit_cast(bf16x8, rv[ks]), acc,
@@ -461,7 +527,7 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       uint32_t bits = (~neg & 0x0F0F0F0Fu) << (4 * (lane >> 5));
       // the per-bit mask only where some entry of the wave is uncertain (rare);
       // !(zmin > bound) also catches NaN
-      const bool trow = t >= rlo && t < nvalid;
+      const bool trow = tin && t >= rlo && t < nvalid;
       if (__ballot(!(zmin > bound) && trow)) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -474,9 +540,9 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       // Uncertain entries, one (lane, row) at a time for the whole wave.  The
       // products s_i r~_i of two bf16 values are exact in fp32 (16-bit
       // significands; |s r~| >= 2^-126 unless tiny, covered by 2^-110
-      // below).  The lanes sum them in a tree of depth <= 7, so the sum T
-      // is within 7 2^-24 A of the exact sum E (A = sum |s_i r~_i|), and the
-      // oracle's ascending fp64 sum is within 127 2^-53 A of E: beyond
+      // below).  The lanes sum them in a tree of depth <= 9 (d <= 256), so
+      // the sum T is within 9 2^-24 A of the exact sum E (A = sum |s_i r~_i|),
+      // and the oracle's ascending fp64 sum is within 255 2^-53 A of E: beyond
       // 2^-20 A + 2^-110 the signs of all three agree.  Otherwise (E = 0
       // included) the ascending fp64 sum itself is formed, by every lane
       // alike from uniform addresses.
@@ -487,14 +553,18 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
         const int bp = __builtin_ctz(um);
         const int k = ct * 32 + bp;
         const unsigned char *rr = stage + (rt * 32 + (src & 31)) * P2;
-        const unsigned char *sr = S_s + k * P2;
+        const unsigned char *sr = S_s + k * SPITCH;
         float ps = 0.0f, pa = 0.0f;
-        if constexpr (D == 128) {
-          const uint32_t sw = *(const uint32_t *)(sr + 4 * lane);
-          const uint32_t rw = *(const uint32_t *)(rr + 4 * lane);
-          const float p0 = bf16_lo(sw) * bf16_lo(rw), p1 = bf16_hi(sw) * bf16_hi(rw);
-          ps = p0 + p1;
-          pa = fabsf(p0) + fabsf(p1);
+        if constexpr (D >= 128) {
+          // two products per dword, D / 128 dwords per lane
+#pragma unroll
+          for (int c = 0; c < D / 128; ++c) {
+            const uint32_t sw = *(const uint32_t *)(sr + 4 * (lane + 64 * c));
+            const uint32_t rw = *(const uint32_t *)(rr + 4 * (lane + 64 * c));
+            const float p0 = bf16_lo(sw) * bf16_lo(rw), p1 = bf16_hi(sw) * bf16_hi(rw);
+            ps = ps + (p0 + p1);
+            pa = pa + (fabsf(p0) + fabsf(p1));
+          }
         } else {
           if (lane < D) {
             const float p = bf16_to_f32(*(const uint16_t *)(sr + 2 * lane)) *
@@ -525,14 +595,17 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
       }
       sgw[ct] = bits | (uint32_t)__shfl_xor((int)bits, 32, 64);
     }
-    const bool tvalid = t >= rlo && t < nvalid && lane < 32;
+    const bool tvalid = tin && t >= rlo && t < nvalid && lane < 32;
     if constexpr (TO_LDS) {
       static_assert(D == 128, "LDS sign rows exist at d = 128 only");
       if (lane < 32) *(u32x4 *)(srows + SP * t) = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
     } else if (tvalid) {
       const size_t tslot = slot0 + (size_t)t;
       uint8_t *dst = signs_out + tslot * (D / 8);
-      if constexpr (D == 128) {
+      if constexpr (D == 256) {
+        *(u32x4 *)dst = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
+        *(u32x4 *)(dst + 16) = u32x4{sgw[4], sgw[5], sgw[6], sgw[7]};
+      } else if constexpr (D == 128) {
         *(u32x4 *)dst = u32x4{sgw[0], sgw[1], sgw[2], sgw[3]};
       } else if constexpr (D == 64) {
         *(u32x2 *)dst = u32x2{sgw[0], sgw[1]};
@@ -568,7 +641,7 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
 template <int D, int BITS, int RK, bool QJL, bool BF16, bool VG>
 __global__ __launch_bounds__(256, 2)
 void quantize_kernel(const QuantArgs a) {
-  constexpr int LPV = D > 64 ? 2 : 1;        // lanes per vector
+  constexpr int LPV = D > 128 ? 4 : (D > 64 ? 2 : 1);   // lanes per vector
   constexpr int DL = D / LPV;                // coordinates per lane
   constexpr int VT = 64 / LPV;               // vectors per tile
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -578,14 +651,18 @@ void quantize_kernel(const QuantArgs a) {
   constexpr int NLD = VT * CPR / 64;         // chunks per lane
   constexpr int RECB = D * BITS / 8;
   constexpr int RECW = (RECB + 3) / 4;
-  constexpr int NRT = VT / 32;
+  constexpr int NRT = VT >= 32 ? VT / 32 : 1;   // 32-row sketch blocks (16 valid rows at d = 256)
   constexpr int P2 = D * 2 + 16;             // bf16 row pitch (residuals, S)
-  constexpr int SBYTES = QJL ? D * P2 : 16;
+  // S staged in LDS with pitch P2, or at d = 256 (where it would not fit
+  // beside the tiles) read from memory, rows 2 d bytes apart
+  constexpr bool SMEM = D > 128;
+  constexpr int SPITCH = SMEM ? 2 * D : P2;
+  constexpr int SBYTES = (QJL && !SMEM) ? D * P2 : 16;
   static_assert(VT * P2 <= VT * PITCH, "residual rows must fit the staging buffer");
   static_assert((VT * CPR) % 64 == 0, "tile copy must split evenly over the wave");
   __shared__ __attribute__((aligned(16))) unsigned char stage_all[4][VT * PITCH];
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
-  __shared__ BucketTables<BITS> bt;
+  __shared__ BucketTables<BITS, (D >= 16)> bt;
   __shared__ float rn_all[4][VT];
   static_assert(!VG || D == 128, "token groups exist at d = 128 only");
   // VG: once the stage's residual rows are consumed, row t of the stage (pitch
@@ -598,19 +675,20 @@ void quantize_kernel(const QuantArgs a) {
   float *rn_s = rn_all[wave];
   const int vrow = lane / LPV;               // token row of this lane in the tile
   const int lead = a.t0 % VT;                // padding rows before t0 in the first tile
-  const int half = lane % LPV;               // which coordinate half
-  build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
-  if constexpr (QJL) stage_sketch<D>(S_s, a.S, tid);
+  const int half = lane % LPV;               // which part of the vector (coordinates half*DL ...)
+  build_bucket_tables(bt, a.thr, a.cent, tid, 256);
+  if constexpr (QJL && !SMEM) stage_sketch<D>(S_s, a.S, tid);
   __syncthreads();
+  const unsigned char *Ssrc = SMEM ? (const unsigned char *)a.S : S_s;
   float a_snmax = 0.0f;
-  if constexpr (QJL) a_snmax = sketch_row_norm_max<D>(S_s, lane);
+  if constexpr (QJL) a_snmax = sketch_row_norm_max<D, SPITCH>(Ssrc, lane);
   // randomized Hadamard: this lane's sign words (coordinates half*DL ...)
   constexpr int NMW = (DL + 31) / 32;
   uint32_t mw[NMW];
 #pragma unroll
   for (int w = 0; w < NMW; ++w) {
     mw[w] = 0u;
-    if constexpr (RK == RK_RHT) mw[w] = (LPV == 2 && half) ? a.rsign[NMW + w] : a.rsign[w];
+    if constexpr (RK == RK_RHT) mw[w] = a.rsign[half * NMW + w];
   }
 
   const int tile0 = blockIdx.x * 4 + wave;
@@ -701,21 +779,35 @@ void quantize_kernel(const QuantArgs a) {
     float held = 1.0f;
     if constexpr (RK != RK_NONE) {
       wht_inplace<DL>(y);
-      if constexpr (LPV == 2) {
-        // last stage: (y_i, y_{i+DL}) -> (y_i + y_{i+DL}, y_i - y_{i+DL}).  The
+      if constexpr (LPV >= 2) {
+        // stage h = DL: (y_i, y_{i+DL}) -> (y_i + y_{i+DL}, y_i - y_{i+DL}).  The
         // lower lane forms own + partner; the upper lane own - partner, the
         // exact negation of the rounded difference, and keeps that sign until
         // the scaling below (the squares do not see it).
-        held = half ? -1.0f : 1.0f;
+        held = (half & 1) ? -1.0f : 1.0f;
         static_assert(DL % 8 == 0, "butterfly stage in groups of 8");
 #pragma unroll
         for (int i = 0; i < DL; i += 8) fmac_xor1_x8(y + i, held);
       }
+      if constexpr (LPV == 4) {
+        // stage h = 2 DL between lanes q and q ^ 2, which hold the same sign:
+        // own +- partner is that sign times the true sum / the negated
+        // difference
+        const float s2 = (half & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < DL; i += 8) fmac_xor2_x8(y + i, s2);
+        held *= s2;
+      }
     }
     float ss = pairwise_sumsq<DL>(y);
-    if constexpr (LPV == 2) {
+    // the adjacent-pair tree over the lanes of the vector (lower part first)
+    if constexpr (LPV >= 2) {
       const float o = xor1_f(ss);
-      ss = half ? (o + ss) : (ss + o);
+      ss = (half & 1) ? (o + ss) : (ss + o);
+    }
+    if constexpr (LPV == 4) {
+      const float o = xor2_f(ss);
+      ss = (half & 2) ? (o + ss) : (ss + o);
     }
     const float nu = sqrtf(ss);
     // u = y * (1/nu) with the held sign folded in (a negation is exact)
@@ -743,6 +835,8 @@ void quantize_kernel(const QuantArgs a) {
       // here, or the compiler defers the packing and keeps every code live
 #pragma unroll
       for (int k = 0; k < DL / 8; ++k) asm volatile("" : "+v"(nib[k]));
+    } else if constexpr (LPV == 4) {
+      // each lane writes its quarter of the record itself (below)
     } else if constexpr (LPV == 2) {
       // each lane packed its own half; the lower lane joins the two images
       LocalCodes<DL, BITS> oth;
@@ -750,6 +844,9 @@ void quantize_kernel(const QuantArgs a) {
       for (int k = 0; k < LocalCodes<DL, BITS>::NA + LocalCodes<DL, BITS>::NB; ++k)
         oth.w[k] = xor1_u(lc.w[k]);
       join_halves<D, DL, BITS, RECW>(rec, lc, oth);
+    } else if constexpr (BITS == 3 && D == 8) {
+      // 2-bit plane (2 bytes), then the 1-bit plane (1 byte)
+      rec[0] = (lc.w[0] & 0xFFFFu) | (lc.w[1] << 16);
     } else {
 #pragma unroll
       for (int k = 0; k < RECW; ++k) rec[k] = 0u;
@@ -761,16 +858,23 @@ void quantize_kernel(const QuantArgs a) {
           rec[LocalCodes<DL, BITS>::NA + k] |= lc.w[LocalCodes<DL, BITS>::NA + k];
       }
     }
+    if constexpr (LPV == 4) {
+      if (valid) store_quarter<D, DL, BITS>(a.codes + slot * RECB, lc, half);
+    }
     if (valid && half == 0) {
-      if constexpr (!VG) store_bytes<RECB>(a.codes + slot * RECB, rec);
+      if constexpr (!VG && LPV < 4) store_bytes<RECB>(a.codes + slot * RECB, rec);
       a.norm[slot] = f32_to_f16_bits(nu * a.scale);
     }
 
     if constexpr (QJL) {
       float rs = pairwise_sumsq<DL>(y);
-      if constexpr (LPV == 2) {
+      if constexpr (LPV >= 2) {
         const float o = xor1_f(rs);
-        rs = half ? (o + rs) : (rs + o);
+        rs = (half & 1) ? (o + rs) : (rs + o);
+      }
+      if constexpr (LPV == 4) {
+        const float o = xor2_f(rs);
+        rs = (half & 2) ? (o + rs) : (rs + o);
       }
       const float rho = sqrtf(rs);
       if (valid && half == 0) a.rnorm[slot] = f32_to_f16_bits(rho);
@@ -794,7 +898,7 @@ void quantize_kernel(const QuantArgs a) {
       wave_sync();
 
       // VG: the sign records go to the residual rows' padding
-      sketch_signs<D, NRT, VG, P2>(stage, S_s, rn_s, a_snmax, rlo, nvalid,
+      sketch_signs<D, NRT, VG, P2, SPITCH, VT>(stage, Ssrc, rn_s, a_snmax, rlo, nvalid,
                                    (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
                                    stage + 2 * D, lane);
     }
@@ -876,7 +980,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
   using LC = LocalCodes<RB, BITS>;
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
   __shared__ __attribute__((aligned(16))) unsigned char res_all[4][RBYTES];
-  __shared__ BucketTables<BITS> bt;
+  __shared__ BucketTables<BITS, (D >= 16)> bt;
   __shared__ float rn_all[4][VT];
   static_assert(!VG || D == 128, "token groups exist at d = 128 only");
   __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * RECB : 16];
@@ -885,7 +989,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
   const int lead = a.t0 % VT;                // padding rows before t0 in the first tile
   unsigned char *res = res_all[wave];
   float *rn_s = rn_all[wave];
-  build_bucket_tables<BITS>(bt, a.thr, a.cent, tid, 256);
+  build_bucket_tables(bt, a.thr, a.cent, tid, 256);
   if constexpr (QJL) stage_sketch<D>(S_s, a.S, tid);
   __syncthreads();
   float a_snmax = 0.0f;
@@ -1164,6 +1268,10 @@ __device__ __forceinline__ void load_rec(const uint8_t *p, uint32_t *w) {
     const uint16_t *h = (const uint16_t *)p;
     w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
     w[1] = h[2];
+  } else if constexpr (BYTES == 3) {
+    w[0] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+  } else if constexpr (BYTES == 1) {
+    w[0] = p[0];
   } else {
     static_assert(BYTES == 2, "record size");
     w[0] = *(const uint16_t *)p;
@@ -1194,6 +1302,10 @@ __device__ __forceinline__ void lds_codes(const uint8_t *r, int g, uint32_t &w0,
     if constexpr (BITS == 4) {
       w0 = *(const uint32_t *)(r + g * 4);
       w1 = 0u;
+    } else if constexpr (BITS == 3 && D == 8) {
+      // 3-byte records: rows at odd addresses, so byte reads
+      w0 = (uint32_t)r[0] | ((uint32_t)r[1] << 8);
+      w1 = r[2];
     } else if constexpr (BITS == 3) {
       w0 = *(const uint16_t *)(r + g * 2);
       w1 = r[D / 4 + g];
@@ -1207,13 +1319,18 @@ __device__ __forceinline__ void lds_codes(const uint8_t *r, int g, uint32_t &w0,
   }
 }
 
-// The first nb bytes (even, below 16) of a 16-byte piece, zero-extended: the
-// last piece of a split's value segment may end inside the piece (records of
-// 2, 6, 8, 12 or 24 bytes), and the bytes after it may lie past the end of the
-// caller's buffer.
+// The first nb bytes (below 16) of a 16-byte piece, zero-extended: the last
+// piece of a split's value segment may end inside the piece (records of 1, 2,
+// 3, 6, 8, 12 or 24 bytes), and the bytes after it may lie past the end of
+// the caller's buffer.  Halfword reads for even nb (the records of 2-byte
+// multiples start 2-byte aligned), byte reads otherwise.
 __device__ __forceinline__ u32x4 load_piece_tail(const uint8_t *p, int nb) {
   uint32_t w[4] = {0u, 0u, 0u, 0u};
-  for (int i = 0; i < nb; i += 2) w[i >> 2] |= (uint32_t)(*(const uint16_t *)(p + i)) << (8 * (i & 2));
+  if ((nb & 1) == 0 && (((uintptr_t)p) & 1) == 0) {
+    for (int i = 0; i < nb; i += 2) w[i >> 2] |= (uint32_t)(*(const uint16_t *)(p + i)) << (8 * (i & 2));
+  } else {
+    for (int i = 0; i < nb; ++i) w[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
+  }
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
@@ -1222,8 +1339,9 @@ __device__ __forceinline__ u32x4 load_piece_tail(const uint8_t *p, int nb) {
 template <int D, int BITS>
 __device__ __forceinline__ uint32_t rec_pair(const uint32_t *w, int p) {
   if constexpr (BITS == 4) return (w[p >> 2] >> (8 * (p & 3))) & 255u;
-  if constexpr (BITS == 3)
-    return ((w[p >> 3] >> (4 * (p & 7))) & 15u) | (((w[D / 16 + (p >> 4)] >> (2 * (p & 15))) & 3u) << 4);
+  if constexpr (BITS == 3)   // the 1-bit plane starts at bit 2 D (byte D / 4)
+    return ((w[p >> 3] >> (4 * (p & 7))) & 15u) |
+           (((w[(2 * D + 2 * p) >> 5] >> ((2 * D + 2 * p) & 31)) & 3u) << 4);
   if constexpr (BITS == 2) return (w[p >> 3] >> (4 * (p & 7))) & 15u;
   return (w[p >> 4] >> (2 * (p & 15))) & 3u;
 }
@@ -1320,7 +1438,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   constexpr int NS = 2 + 2 * D, NC = NS - 1;         // partial floats, columns merged
   constexpr int NIT = (NC + 255) / 256;              // columns per thread
   constexpr int U = 16;                              // splits per load batch
-  constexpr int KS = 256 / D, KL = D / KS;           // S^T a: KS threads per coordinate
+  // S^T a: KS threads per coordinate, KL rows of S each (in registers when
+  // few, else read in the loop)
+  constexpr int KS = (256 / D) < D ? (256 / D) : D, KL = D / KS;
+  constexpr bool SREG = KL <= 64;
   __shared__ __attribute__((aligned(16))) float res[NS];    // merged L, o', a (by column)
   __shared__ __attribute__((aligned(16))) float sta[256];   // S^T a partial sums
   __shared__ __attribute__((aligned(16))) float wv[D];
@@ -1329,10 +1450,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   const int splits = a.splits;
   const float *pb = a.part + (size_t)row * splits * NS;
 
-  // columns of S for this thread's share of S^T a
-  const int si = tid % D, sk0 = (tid / D) * KL;
-  uint16_t sv[VQ ? KL : 1];
-  if constexpr (VQ) {
+  // columns of S for this thread's share of S^T a: every thread at d >= 16
+  // (KS d = 256); at d = 8 threads tid >= KS d read a valid row and drop it
+  // (no per-load branch: the loads stay in flight together)
+  const int si = tid % D;
+  const bool sthr = KS * D >= 256 || tid < KS * D;
+  const int sk0 = sthr ? (tid / D) * KL : 0;
+  uint16_t sv[VQ && SREG ? KL : 1];
+  if constexpr (VQ && SREG) {
 #pragma unroll
     for (int k = 0; k < KL; ++k) sv[k] = ((const uint16_t *)a.S)[(size_t)(sk0 + k) * D + si];
   }
@@ -1401,14 +1526,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
   // o' (+ sqrt(pi/2)/m S^T a): KS partial sums per coordinate, added in order
   if constexpr (VQ) {
     float t = 0.0f;
+    if constexpr (SREG) {
 #pragma unroll
-    for (int k = 0; k < KL; ++k) t = fmaf(bf16_to_f32(sv[k]), res[2 + D + sk0 + k], t);
-    sta[tid] = t;
+      for (int k = 0; k < KL; ++k) t = fmaf(bf16_to_f32(sv[k]), res[2 + D + sk0 + k], t);
+    } else {
+#pragma unroll 8
+      for (int k = 0; k < KL; ++k)
+        t = fmaf(bf16_to_f32(((const uint16_t *)a.S)[(size_t)(sk0 + k) * D + si]),
+                 res[2 + D + sk0 + k], t);
+    }
+    sta[tid] = sthr ? t : 0.0f;
     __syncthreads();
   }
   if (tid < 64) {
-    // lane l holds coordinates l and l + 64 (D = 128) or l (D <= 64)
-    constexpr int PL = D > 64 ? 2 : 1;
+    // lane l holds coordinates l + 64 e, e < PL
+    constexpr int PL = D > 64 ? D / 64 : 1;
     float x[PL];
 #pragma unroll
     for (int e = 0; e < PL; ++e) {
@@ -1436,10 +1568,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
           x[e] = (lane & h) ? (y - x[e]) : (x[e] + y);
         }
       }
-      if constexpr (PL == 2) {
-        const float lo = x[0], hi = x[1];
-        x[0] = lo + hi;
-        x[1] = lo - hi;
+      // stages h = 64 e' within the lane: pairs (e, e + e')
+#pragma unroll
+      for (int hs = 1; hs < PL; hs <<= 1) {
+#pragma unroll
+        for (int e = 0; e < PL; ++e) {
+          if (e & hs) continue;
+          const float lo = x[e], hi = x[e + hs];
+          x[e] = lo + hi;
+          x[e + hs] = lo - hi;
+        }
       }
     }
 #pragma unroll
@@ -1473,7 +1611,7 @@ template <int D, int KB, bool KQ, int VB, bool VQ, int GT>
 // (three blocks per CU: registers <= 168)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(
     const DecodeArgs a) {
-  constexpr int E = GT >= 4 ? 8 : 16;               // value coordinates per lane
+  constexpr int E = (GT >= 4 || D < 16) ? 8 : 16;   // value coordinates per lane
   constexpr int L = D / E;                           // lanes sharing a token group in phase C
   constexpr int GPW = 64 / L;                        // token groups per wave
   constexpr int TG = 4;                              // tokens per group
@@ -1928,12 +2066,15 @@ __global__ __launch_bounds__(256) void window_kernel(const WindowArgs a) {
   auto wval = [&](const void *p, size_t idx) {
     return WB ? bf16_to_f32(((const uint16_t *)p)[idx]) : ((const float *)p)[idx];
   };
+  // scores and weighted sums accumulate in fp64 (a window is at most
+  // KVQ_WINDOW_MAX tokens; fp32 chains of d = 256 terms would cost most of the
+  // output's 1e-5 relative budget)
   float m = -INFINITY;
   for (int j = tid; j < a.n_win; j += 256) {
-    float s = 0.0f;
-    for (int i = 0; i < D; ++i) s = fmaf(qf[i], wval(a.wk, base + (size_t)j * D + i), s);
-    sj[j] = s;
-    m = fmaxf(m, s);
+    double s = 0.0;
+    for (int i = 0; i < D; ++i) s = fma((double)qf[i], (double)wval(a.wk, base + (size_t)j * D + i), s);
+    sj[j] = (float)s;
+    m = fmaxf(m, sj[j]);
   }
   m = wave_max(m);
   if (lane == 0) red[wave] = m;
@@ -1953,9 +2094,10 @@ __global__ __launch_bounds__(256) void window_kernel(const WindowArgs a) {
   // o: two token halves per coordinate, then summed
   for (int it = tid; it < 2 * D; it += 256) {
     const int half = it / D, i = it - half * D;
-    float acc = 0.0f;
-    for (int j = half; j < a.n_win; j += 2) acc = fmaf(sj[j], wval(a.wv, base + (size_t)j * D + i), acc);
-    po[half][i] = acc;
+    double acc = 0.0;
+    for (int j = half; j < a.n_win; j += 2)
+      acc = fma((double)sj[j], (double)wval(a.wv, base + (size_t)j * D + i), acc);
+    po[half][i] = (float)acc;
   }
   __syncthreads();
   float *dst = a.wpart + (size_t)row * (2 + D);
@@ -2478,7 +2620,7 @@ inline hipError_t launch_tiles(const void *kern, const QuantArgs &a, bool lut, h
 
 template <int D, int BITS, int RK, bool QJL>
 hipError_t quantize_go(const QuantArgs &a, bool bf16, bool vg, hipStream_t s) {
-  constexpr bool LUT = BucketTables<BITS>::LUT;
+  constexpr bool LUT = BucketTables<BITS, (D >= 16)>::LUT;
   // value sides (token groups at d = 128): unrotated without sketch, or
   // rotated with sketch
   constexpr bool VGOK = D == 128 && ((RK == RK_NONE) != QJL);
@@ -2486,8 +2628,12 @@ hipError_t quantize_go(const QuantArgs &a, bool bf16, bool vg, hipStream_t s) {
   auto go = [&](auto V) -> hipError_t {
     constexpr bool VG = decltype(V)::value;
     if constexpr (RK == RK_QR) {
-      if (bf16) return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, true, VG>, a, LUT, s);
-      return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, false, VG>, a, LUT, s);
+      // the dense rotation's encoder covers 16 <= d <= 128
+      if constexpr (D < 16 || D > 128) return hipErrorInvalidValue;
+      else {
+        if (bf16) return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, true, VG>, a, LUT, s);
+        return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, false, VG>, a, LUT, s);
+      }
     } else {
       if (bf16) return launch_tiles((const void *)&quantize_kernel<D, BITS, RK, QJL, true, VG>, a, LUT, s);
       return launch_tiles((const void *)&quantize_kernel<D, BITS, RK, QJL, false, VG>, a, LUT, s);
@@ -2670,8 +2816,10 @@ hipError_t prefill_go(const PrefillArgs &a, int B, hipStream_t s) {
   const dim3 grid((NR + 63) / 64 * a.splits, a.Hkv, B), blk(256);
   if constexpr (D == 128)
     hipLaunchKernelGGL((prefill16_kernel<KB, KQ, VB, VQ>), grid, blk, 0, s, a);
-  else
+  else if constexpr (D >= 16)
     hipLaunchKernelGGL((prefill_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
+  else
+    return hipErrorInvalidValue;   // the tile kernel works in 16-coordinate blocks
   return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ class kvq_cache(C.Structure):
                 ("v_codes", C.c_void_p), ("v_signs", C.c_void_p),
                 ("k_norm", C.c_void_p), ("k_rnorm", C.c_void_p),
                 ("v_norm", C.c_void_p), ("v_rnorm", C.c_void_p),
-                ("rot_kind", C.c_int32), ("rot_signs", C.c_uint32 * 4),
+                ("rot_kind", C.c_int32), ("rot_signs", C.c_uint32 * 8),
                 ("rot_Q", C.c_void_p)]
 
 
@@ -139,7 +139,7 @@ def kvq_cache_init(scheme: int, n_bits: int, d: int, batch: int, kv_heads: int,
 
 
 def kvq_rotation_signs(seed: int, d: int) -> np.ndarray:
-    out = np.zeros(4, np.uint32)
+    out = np.zeros(8, np.uint32)
     _check(lib().kvq_rotation_signs(seed, d, out.ctypes.data), "kvq_rotation_signs")
     return out
 
@@ -269,7 +269,7 @@ class KVQCache:
     def __init__(self, scheme: str, n_bits: int, d: int, batch: int, kv_heads: int,
                  capacity: int, S_bf16=None, device="cuda", rotation: str = "wht",
                  rot_signs=None, rot_Q=None, rot_seed: int = 11):
-        """rotation (rotated schemes): "wht", "rht" (rot_signs: 4 uint32 words,
+        """rotation (rotated schemes): "wht", "rht" (rot_signs: uint32 words, d/32 used,
         default kvq_rotation_signs(rot_seed)) or "qr" (rot_Q: d x d fp32,
         default kvq_rotation_qr(rot_seed))."""
         import torch

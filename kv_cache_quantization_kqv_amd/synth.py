@@ -57,11 +57,12 @@ def sketch_bf16(m: int, d: int, seed: int = 7) -> torch.Tensor:
 
 def rotation_signs(d: int, seed: int = 13):
     """Random diagonal of the randomized Hadamard rotation: d fair coin flips
-    as 4 little-endian uint32 words (bit i set: coordinate i negated)."""
+    as 8 little-endian uint32 words (bit i set: coordinate i negated; bits at
+    and beyond d zero)."""
     import numpy as np
     g = _gen(seed, "cpu")
     bits = torch.randint(0, 2, (d,), generator=g).numpy().astype(np.uint64)
-    w = np.zeros(4, np.uint32)
+    w = np.zeros(8, np.uint32)
     for i in range(d):
         w[i // 32] |= np.uint32(int(bits[i]) << (i % 32))
     return w

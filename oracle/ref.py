@@ -139,7 +139,7 @@ class Side:
 class Rot:
     """Rotation of the rotated sides ("KVQuant++" thread, "Entropy coding",
     "Rotation invariance guarantee"): "wht" (y = H x), "rht" (y = H D x,
-    param = 4 uint32 sign words) or "qr" (y = Q x, param = fp32 [d][d])."""
+    param = uint32 sign words, bit i of word i/32) or "qr" (y = Q x, param = fp32 [d][d])."""
     kind: str = "wht"
     param: object = field(default=None, compare=False)
 

@@ -37,7 +37,7 @@ def _inputs(B, H, T, d, dtype, seed, heavy=False):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("d", [8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("scheme,n", SCHEME_BITS, ids=[f"{s}{n}" for s, n in SCHEME_BITS])
 def test_quantize_bit_exact(scheme, n, d, dtype):
     print(f"case quantize {scheme}{n} d={d} {dtype}", flush=True)
@@ -77,7 +77,7 @@ def test_quantize_bit_exact_many_tiles_per_wave(scheme, n, d, dtype, rotation):
     P.assert_bit_exact()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [8, 64, 128, 256])
 @pytest.mark.parametrize("scheme,n", [("KV", 4), ("KQV", 4), ("KQV", 2), ("QKQV", 3)])
 def test_dequantize_matches_oracle(scheme, n, d):
     print(f"case dequantize {scheme}{n} d={d}", flush=True)
@@ -93,7 +93,7 @@ def test_dequantize_matches_oracle(scheme, n, d):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [8, 32, 64, 128, 256])
 @pytest.mark.parametrize("scheme,n", [("KV", 2), ("KV", 4), ("KQV", 2), ("KQV", 3), ("KQV", 4),
                                       ("QKQV", 2), ("QKQV", 4)])
 def test_decode_matches_oracle(scheme, n, d, dtype):
@@ -252,7 +252,7 @@ def test_single_token_context():
     assert np.allclose(got, vh, rtol=1e-5, atol=1e-6)   # o = v^_1
 
 
-@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("d", [8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_decode_full_capacity_ragged_tail(d, splits):
     """n_ctx equal to the capacity with value records that are not 16-byte
@@ -279,7 +279,7 @@ WINDOW_CASES = {
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("case", list(WINDOW_CASES))
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [8, 64, 128, 256])
 @pytest.mark.parametrize("scheme,n", [("KQV", 4), ("KV", 3), ("QKQV", 2)])
 def test_decode_window_matches_oracle(scheme, n, d, case, dtype):
     """Compressed slots [t_begin, t_end) plus full-precision sink and recent
@@ -334,9 +334,12 @@ def test_decode_window_equals_plain_decode_when_empty():
 ROT_SCHEMES = [("KQV", 4), ("KQV", 2), ("QKQV", 3), ("QKQV", 2)]
 
 
-@pytest.mark.parametrize("rotation", ["rht", "qr"])
+ROT_CASES = [(d, r) for d in (8, 16, 32, 64, 128, 256) for r in ("rht", "qr")
+             if not (r == "qr" and d in (8, 256))]   # the dense rotation: 16 <= d <= 128
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("d,rotation", ROT_CASES, ids=[f"{r}-d{d}" for d, r in ROT_CASES])
 @pytest.mark.parametrize("scheme,n", ROT_SCHEMES, ids=[f"{s}{n}" for s, n in ROT_SCHEMES])
 def test_quantize_bit_exact_rotations(scheme, n, d, dtype, rotation):
     """Randomized Hadamard and dense SO(d) rotations ("KVQuant++" thread,
@@ -351,8 +354,8 @@ def test_quantize_bit_exact_rotations(scheme, n, d, dtype, rotation):
     P.assert_bit_exact()
 
 
-@pytest.mark.parametrize("rotation", ["rht", "qr"])
-@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("d,rotation", [(32, "rht"), (32, "qr"), (128, "rht"), (128, "qr"),
+                                        (8, "rht"), (256, "rht")])
 def test_dequantize_and_decode_rotations(rotation, d):
     print(f"case decode-rot {rotation} d={d}", flush=True)
     B, Hkv, G, N = 2, 2, 4, 333
@@ -382,7 +385,7 @@ PREFILL_SCHEMES = [("KV", 4), ("KV", 2), ("KQV", 4), ("KQV", 3), ("KQV", 2), ("Q
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("d,G", [(16, 2), (32, 4), (64, 1), (128, 4), (128, 8)])
+@pytest.mark.parametrize("d,G", [(16, 2), (32, 4), (64, 1), (128, 4), (128, 8), (256, 4)])
 @pytest.mark.parametrize("scheme,n", PREFILL_SCHEMES, ids=[f"{s}{n}" for s, n in PREFILL_SCHEMES])
 def test_prefill_matches_oracle(scheme, n, d, G, dtype):
     """Chunked prefill: a chunk of 37 query tokens at positions 150..186 over a
@@ -490,7 +493,7 @@ def test_prefill_token_splits(scheme, n, causal):
         assert rel_rows(got, P.prefill(q, p0, causal, N)).max() < 1e-5, p0
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [8, 64, 128, 256])
 def test_decode_stages_equal_one_call(d):
     """Prep, scan and merge launched by three staged calls give the one-call
     result bit for bit (same kernels, same workspace)."""

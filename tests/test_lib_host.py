@@ -104,7 +104,10 @@ def test_cache_init_errors(K):
     assert lib.kvq_cache_init(C.byref(c), 1, 1, 128, 1, 1, 1) == 4   # KQV needs n >= 2
     assert lib.kvq_cache_init(C.byref(c), 0, 5, 128, 1, 1, 1) == 4
     assert lib.kvq_cache_init(C.byref(c), 1, 4, 96, 1, 1, 1) == 3
-    assert lib.kvq_cache_init(C.byref(c), 1, 4, 256, 1, 1, 1) == 3
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 512, 1, 1, 1) == 3
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 4, 1, 1, 1) == 3
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 256, 1, 1, 1) == 0
+    assert lib.kvq_cache_init(C.byref(c), 1, 4, 8, 1, 1, 1) == 0
     assert lib.kvq_cache_init(C.byref(c), 1, 4, 128, 0, 1, 1) == 10
     # d = 128: the value side's token groups need whole 16-slot blocks
     assert lib.kvq_cache_init(C.byref(c), 1, 4, 128, 1, 1, 50) == 10
@@ -244,7 +247,7 @@ def _cell_bits(bits):
     return 2 if bits >= 4 else 1
 
 
-@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_table_bucketize_precondition(K, d, bits):
     """At most one threshold per prefix cell and the smallest positive one
@@ -320,7 +323,7 @@ def test_bad_codebook_rejected(K):
 
 
 # --------------------------------------------------------------------------- rotations
-@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("d", [8, 16, 32, 64, 128, 256])
 def test_rotation_signs_generator(K, d):
     """Randomized Hadamard diagonal: deterministic per seed, no bits at or
     beyond d, about half the coordinates flipped over many draws."""
@@ -328,7 +331,7 @@ def test_rotation_signs_generator(K, d):
     assert np.array_equal(a, b)
     assert not np.array_equal(a, K.kvq_rotation_signs(6, d))
     bits = np.array([[(int(K.kvq_rotation_signs(s, d)[i // 32]) >> (i % 32)) & 1
-                      for i in range(128)] for s in range(64)])
+                      for i in range(256)] for s in range(64)])
     assert not bits[:, d:].any()
     p = bits[:, :d].mean()
     assert abs(p - 0.5) < 4 * math.sqrt(0.25 / (64 * d))
@@ -366,15 +369,25 @@ def test_cache_set_rotation_validation(K):
     assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, 0x10008) == 2
     w[2] = 1                                         # beyond the d/32 words read at d = 64
     assert lib.kvq_cache_set_rotation(C.byref(c), 1, w.ctypes.data, None) == 0
-    assert list(c.rot_signs) == [0, 0, 0, 0]
+    assert list(c.rot_signs) == [0] * 8
     c16 = _fake_cache(K, d=16)
     w16 = np.array([1 << 16, 0, 0, 0], np.uint32)    # coordinate 16 of a d = 16 cache
     assert lib.kvq_cache_set_rotation(C.byref(c16), 1, w16.ctypes.data, None) == 10
     w[:] = [0xFFFFFFFF, 0x80000001, 0, 0]
     assert lib.kvq_cache_set_rotation(C.byref(c), 1, w.ctypes.data, None) == 0
-    assert c.rot_kind == 1 and list(c.rot_signs) == [0xFFFFFFFF, 0x80000001, 0, 0]
+    assert c.rot_kind == 1 and list(c.rot_signs) == [0xFFFFFFFF, 0x80000001] + [0] * 6
     assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, 0x900000) == 0
-    assert c.rot_kind == 2 and c.rot_Q == 0x900000 and list(c.rot_signs) == [0, 0, 0, 0]
+    assert c.rot_kind == 2 and c.rot_Q == 0x900000 and list(c.rot_signs) == [0] * 8
+    # d = 256: all eight sign words; the dense rotation covers 16 <= d <= 128
+    c256 = _fake_cache(K, d=256)
+    w8 = np.arange(1, 9, dtype=np.uint32)
+    assert lib.kvq_cache_set_rotation(C.byref(c256), 1, w8.ctypes.data, None) == 0
+    assert list(c256.rot_signs) == list(range(1, 9))
+    assert lib.kvq_cache_set_rotation(C.byref(c256), 2, None, 0x900000) == 3
+    c8 = _fake_cache(K, d=8)
+    assert lib.kvq_cache_set_rotation(C.byref(c8), 2, None, 0x900000) == 3
+    assert lib.kvq_cache_set_rotation(C.byref(c8), 1, np.array([1 << 8], np.uint32).ctypes.data,
+                                      None) == 10
     # the struct is validated again by every entry point
     bad = _fake_cache(K, d=64)
     bad.rot_kind = 2                                 # dense rotation without Q
@@ -414,6 +427,9 @@ def test_prefill_validation_status_codes(K):
     assert f(p, q, 1, 6, 5, 0, 1, 33, out, w, need, None) == 6
     assert f(p, q, 1, 6, 0, 0, 1, 8, out, w, need, None) == 10
     assert f(p, q, 1, 5, 5, 0, 1, 8, out, w, need, None) == 9
+    # d = 8: the multi-query tiles are 16 coordinates wide
+    c8 = _fake_cache(K, d=8)
+    assert f(C.byref(c8), q, 1, 6, 5, 0, 1, 8, out, w, 1 << 30, None) == 3
     q3 = _fake_cache(K, scheme="QKQV", n=3)
     assert lib.kvq_prefill_workspace(C.byref(q3), 2, 7, C.byref(ws)) == 0
     assert ws.value == 4 * 1 * 2 * 7 * (2 * 64 + 1 * (2 + 2 * 64) + 2 + 64)  # + S q'
