@@ -53,8 +53,8 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = 1,       /* a required pointer is NULL */
   KVQ_ERR_ALIGN = 2,      /* a pointer or stride breaks the 16-byte alignment rule */
-  KVQ_ERR_DIM = 3,        /* head dimension not in {8, 16, 32, 64, 128, 256} (or, at 8 and
-                             256, the dense rotation) */
+  KVQ_ERR_DIM = 3,        /* head dimension not in {8, 16, 32, 64, 128, 256} (or the dense
+                             rotation at 256) */
   KVQ_ERR_BITS = 4,       /* bit width out of range for the scheme */
   KVQ_ERR_SCHEME = 5,     /* unknown scheme */
   KVQ_ERR_CAPACITY = 6,   /* t0 + T or n_ctx exceeds the cache capacity */
@@ -155,8 +155,8 @@ kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch
  * d bits (d/32 words, at least one; bits at and beyond d must be 0).
  * KVQ_ROT_QR: Q = device pointer to d*d fp32 (row-major, 16-B aligned),
  * which must stay valid while the cache is used; its orthogonality is the
- * caller's (see kvq_rotation_qr).
- * Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME (KV scheme, or unknown kind),
+ * caller's (see kvq_rotation_qr); d <= 128 (KVQ_ERR_DIM at d = 256).
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME (KV scheme, or unknown kind), KVQ_ERR_DIM,
  * KVQ_ERR_ALIGN, KVQ_ERR_RANGE (sign bits beyond d). */
 kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
                                   const float *Q_device);
@@ -312,9 +312,8 @@ int kvq_decode_auto_splits(const kvq_cache *c, int q_heads, int n_ctx);
  * Same decoded-vector semantics as kvq_decode_attention (rotated-space
  * scoring, sketch-space value term, one S^T product per row).  workspace:
  * kvq_prefill_workspace bytes.  1 <= n_ctx <= capacity, n_q >= 1,
- * q_pos0 >= 0, causal in {0, 1}.  Head dimensions 16 .. 256 (the tiles are
- * 16 coordinates wide; d = 8 gives KVQ_ERR_DIM).
- * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_HEADS, KVQ_ERR_DIM,
+ * q_pos0 >= 0, causal in {0, 1}.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_ALIGN, KVQ_ERR_DTYPE, KVQ_ERR_HEADS,
  * KVQ_ERR_CAPACITY, KVQ_ERR_RANGE, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
 kvq_status kvq_prefill_attention(const kvq_cache *c, const void *q, int q_dtype, int q_heads,
                                  int n_q, int q_pos0, int causal, int n_ctx, float *out,

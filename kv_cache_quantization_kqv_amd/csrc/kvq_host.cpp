@@ -257,7 +257,7 @@ kvq_status check_cache(const kvq_cache *c) {
   if (c->rot_kind < KVQ_ROT_WHT || c->rot_kind > KVQ_ROT_QR) return KVQ_ERR_SCHEME;
   if (!s.rot && c->rot_kind != KVQ_ROT_WHT) return KVQ_ERR_SCHEME;
   if (c->rot_kind == KVQ_ROT_QR && !c->rot_Q) return KVQ_ERR_NULL;
-  if (c->rot_kind == KVQ_ROT_QR && (c->d < 16 || c->d > 128)) return KVQ_ERR_DIM;
+  if (c->rot_kind == KVQ_ROT_QR && c->d > 128) return KVQ_ERR_DIM;
   if (c->rot_kind == KVQ_ROT_RHT && !signs_fit(c->rot_signs, c->d)) return KVQ_ERR_RANGE;
   const void *ptrs[] = {c->k_codes, c->k_norm, c->v_codes, c->v_norm, c->k_signs, c->k_rnorm,
                         c->v_signs, c->v_rnorm, c->S,
@@ -543,7 +543,7 @@ kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
     if (!signs_fit(w, c->d)) return KVQ_ERR_RANGE;
   }
   if (kind == KVQ_ROT_QR) {
-    if (c->d < 16 || c->d > 128) return KVQ_ERR_DIM;   // dense rotation: 16 <= d <= 128
+    if (c->d > 128) return KVQ_ERR_DIM;   // dense rotation: d <= 128
     if (!Q_device) return KVQ_ERR_NULL;
     if (!aligned16(Q_device)) return KVQ_ERR_ALIGN;
   }
@@ -839,7 +839,6 @@ kvq_status prefill_impl(const kvq_cache *c, const void *q, int q_dtype, int q_he
                         size_t workspace_bytes, void *stream) {
   kvq_status s = check_cache(c);
   if (s != KVQ_OK) return s;
-  if (c->d < 16) return KVQ_ERR_DIM;   // the multi-query tiles are 16 coordinates wide
   if (!q || !out) return KVQ_ERR_NULL;
   if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
   if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;

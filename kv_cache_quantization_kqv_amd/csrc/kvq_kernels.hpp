@@ -970,7 +970,7 @@ __device__ __forceinline__ void dense_rows(cfloat *qb, const float *x, float *yb
 template <int D, int BITS, bool QJL, bool BF16, bool VG>
 __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) {
   constexpr int VT = 64;                     // vectors per wave tile (one per lane)
-  constexpr int RB = 16;                     // rows of y per block
+  constexpr int RB = D < 16 ? D : 16;        // rows of y per block
   constexpr int NB = D / RB;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RECB = D * BITS / 8;
@@ -1057,8 +1057,14 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
         if constexpr (QJL) yb[ii] = u - bt.cent[code];
       }
       if (VG || valid) {
-        // records are 2-byte aligned: halfword stores
-        if constexpr (BITS == 3) {
+        // records are 2-byte aligned (d >= 16): halfword stores; d = 8 records
+        // (1 to 4 bytes) are written bytewise
+        if constexpr (D < 16) {
+          uint32_t img = lc.w[0];
+          if constexpr (BITS == 3) img = (lc.w[0] & 0xFFFFu) | (lc.w[LC::NA] << 16);
+#pragma unroll
+          for (int k = 0; k < RECB; ++k) crec[k] = (uint8_t)(img >> (8 * k));
+        } else if constexpr (BITS == 3) {
           uint16_t *p2 = (uint16_t *)(crec + blk * 4);          // 2-bit plane: 4 bytes per block
           p2[0] = (uint16_t)(lc.w[0] & 0xFFFFu);
           p2[1] = (uint16_t)(lc.w[0] >> 16);
@@ -2454,6 +2460,113 @@ void prefill_kernel(const PrefillArgs a) {
   }
 }
 
+// Multi-query attention below d = 16, where the tile kernels' 16-coordinate
+// blocks do not fit: the same split partials (M, L, o', a) as prefill_kernel
+// for the same grid (64 query rows of one (b, KV head) and one token split per
+// block).  Wave w takes the slots t_lo + w, t_lo + w + 4, ... of the split,
+// one thread per row, with an online base-2 softmax over exact fp32 scores
+// from the stored codes; the four waves' partials are merged through LDS.
+template <int D, int KB, bool KQ, int VB, bool VQ>
+__global__ __launch_bounds__(256) void prefill_small_kernel(const PrefillArgs a) {
+  constexpr int NS = 2 + 2 * D;
+  constexpr int KREC = D * KB / 8, VREC = D * VB / 8, SREC = D / 8;
+  __shared__ float ps[4][64][NS];
+  __shared__ float kct_s[16], vct_s[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.z, hkv = blockIdx.y;
+  const size_t unit = (size_t)b * a.Hkv + hkv;
+  const int NR = a.nq * a.G;
+  const int rt = blockIdx.x / a.splits, split = blockIdx.x - rt * a.splits;
+  const int R = rt * 64 + lane;
+  const int t_lo = (a.t0 & ~15) + split * a.tps;
+  if (tid < 16) {
+    kct_s[tid] = a.kcent[tid];
+    vct_s[tid] = a.vcent[tid];
+  }
+  __syncthreads();
+  // visible slots of row R in this split: [max(t_lo, t0), min(limit, t_lo + tps))
+  int lim = 0;
+  if (R < NR) {
+    lim = a.n_ctx;
+    if (a.causal) lim = min(lim, a.q_pos0 + R / a.G + 1);
+    lim = min(lim, t_lo + a.tps);
+  }
+  const int t_start = max(t_lo, a.t0);
+  float q[D], sq[KQ ? D : 1];
+  {
+    const size_t r = unit * NR + (R < NR ? R : 0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      q[i] = a.qt[r * D + i];
+      if constexpr (KQ) sq[i] = a.sqt[r * D + i];
+    }
+  }
+  float M = -INFINITY, L = 0.0f, o[D], av[VQ ? D : 1];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    o[i] = 0.0f;
+    if constexpr (VQ) av[i] = 0.0f;
+  }
+  for (int t = t_start + wave; t < lim; t += 4) {
+    const size_t slot = unit * a.cap + (size_t)t;
+    const uint8_t *kr = a.kc + slot * KREC;
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc = fmaf(q[i], kct_s[get_code<D, KB>(kr, i)], acc);
+    const float nk = f16_bits_to_f32(a.kn[slot]);
+    float s;
+    if constexpr (KQ) {
+      const uint8_t *sg = a.ks + slot * SREC;
+      float sk = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) sk = fmaf(sq[i], ((sg[i >> 3] >> (i & 7)) & 1) ? 1.0f : -1.0f, sk);
+      s = nk * fmaf(a.kcoef * f16_bits_to_f32(a.kr[slot]), sk, acc);
+    } else {
+      s = nk * acc;
+    }
+    const float Mn = fmaxf(M, s);
+    const float al = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+    const float w = fast_exp2(s - Mn);
+    L = fmaf(L, al, w);
+    const float c = w * f16_bits_to_f32(a.vn[slot]);
+    const uint8_t *vr = a.vc + slot * VREC;
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] = fmaf(c, vct_s[get_code<D, VB>(vr, i)], o[i] * al);
+    if constexpr (VQ) {
+      const float cq = c * f16_bits_to_f32(a.vr[slot]);
+      const uint8_t *sg = a.vs + slot * SREC;
+#pragma unroll
+      for (int k = 0; k < D; ++k)
+        av[k] = fmaf(cq, ((sg[k >> 3] >> (k & 7)) & 1) ? 1.0f : -1.0f, av[k] * al);
+    }
+    M = Mn;
+  }
+  ps[wave][lane][0] = M;
+  ps[wave][lane][1] = L;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    ps[wave][lane][2 + i] = o[i];
+    ps[wave][lane][2 + D + i] = VQ ? av[i] : 0.0f;
+  }
+  __syncthreads();
+  if (wave == 0 && R < NR) {
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, ps[w][lane][0]);
+    float f[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) f[w] = ps[w][lane][0] == -INFINITY ? 0.0f : fast_exp2(ps[w][lane][0] - Mx);
+    float *dst = a.part + ((unit * NR + R) * a.splits + split) * NS;
+    dst[0] = Mx;
+    for (int k = 1; k < NS; ++k) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v = fmaf(f[w], ps[w][lane][k], v);
+      dst[k] = v;
+    }
+  }
+}
+
 // Finish of multi-query rows, FR rows per block of 256 threads (S staged once
 // per block in LDS):  o = R^T (o' + sqrt(pi/2)/m S^T a)  (o', a already / L).
 // Thread t owns row t / (D/8) and coordinates 8 (t % (D/8)) .. + 7.
@@ -2628,8 +2741,8 @@ hipError_t quantize_go(const QuantArgs &a, bool bf16, bool vg, hipStream_t s) {
   auto go = [&](auto V) -> hipError_t {
     constexpr bool VG = decltype(V)::value;
     if constexpr (RK == RK_QR) {
-      // the dense rotation's encoder covers 16 <= d <= 128
-      if constexpr (D < 16 || D > 128) return hipErrorInvalidValue;
+      // the dense rotation's encoder covers d <= 128
+      if constexpr (D > 128) return hipErrorInvalidValue;
       else {
         if (bf16) return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, true, VG>, a, LUT, s);
         return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, false, VG>, a, LUT, s);
@@ -2819,7 +2932,7 @@ hipError_t prefill_go(const PrefillArgs &a, int B, hipStream_t s) {
   else if constexpr (D >= 16)
     hipLaunchKernelGGL((prefill_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
   else
-    return hipErrorInvalidValue;   // the tile kernel works in 16-coordinate blocks
+    hipLaunchKernelGGL((prefill_small_kernel<D, KB, KQ, VB, VQ>), grid, blk, 0, s, a);
   return hipGetLastError();
 }
 

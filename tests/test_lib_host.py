@@ -378,14 +378,14 @@ def test_cache_set_rotation_validation(K):
     assert c.rot_kind == 1 and list(c.rot_signs) == [0xFFFFFFFF, 0x80000001] + [0] * 6
     assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, 0x900000) == 0
     assert c.rot_kind == 2 and c.rot_Q == 0x900000 and list(c.rot_signs) == [0] * 8
-    # d = 256: all eight sign words; the dense rotation covers 16 <= d <= 128
+    # d = 256: all eight sign words; the dense rotation covers d <= 128
     c256 = _fake_cache(K, d=256)
     w8 = np.arange(1, 9, dtype=np.uint32)
     assert lib.kvq_cache_set_rotation(C.byref(c256), 1, w8.ctypes.data, None) == 0
     assert list(c256.rot_signs) == list(range(1, 9))
     assert lib.kvq_cache_set_rotation(C.byref(c256), 2, None, 0x900000) == 3
     c8 = _fake_cache(K, d=8)
-    assert lib.kvq_cache_set_rotation(C.byref(c8), 2, None, 0x900000) == 3
+    assert lib.kvq_cache_set_rotation(C.byref(c8), 2, None, 0x900000) == 0
     assert lib.kvq_cache_set_rotation(C.byref(c8), 1, np.array([1 << 8], np.uint32).ctypes.data,
                                       None) == 10
     # the struct is validated again by every entry point
@@ -427,9 +427,6 @@ def test_prefill_validation_status_codes(K):
     assert f(p, q, 1, 6, 5, 0, 1, 33, out, w, need, None) == 6
     assert f(p, q, 1, 6, 0, 0, 1, 8, out, w, need, None) == 10
     assert f(p, q, 1, 5, 5, 0, 1, 8, out, w, need, None) == 9
-    # d = 8: the multi-query tiles are 16 coordinates wide
-    c8 = _fake_cache(K, d=8)
-    assert f(C.byref(c8), q, 1, 6, 5, 0, 1, 8, out, w, 1 << 30, None) == 3
     q3 = _fake_cache(K, scheme="QKQV", n=3)
     assert lib.kvq_prefill_workspace(C.byref(q3), 2, 7, C.byref(ws)) == 0
     assert ws.value == 4 * 1 * 2 * 7 * (2 * 64 + 1 * (2 + 2 * 64) + 2 + 64)  # + S q'
