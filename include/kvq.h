@@ -53,8 +53,7 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = 1,       /* a required pointer is NULL */
   KVQ_ERR_ALIGN = 2,      /* a pointer or stride breaks the 16-byte alignment rule */
-  KVQ_ERR_DIM = 3,        /* head dimension not in {8, 16, 32, 64, 128, 256} (or the dense
-                             rotation at 256) */
+  KVQ_ERR_DIM = 3,        /* head dimension not in {8, 16, 32, 64, 128, 256} */
   KVQ_ERR_BITS = 4,       /* bit width out of range for the scheme */
   KVQ_ERR_SCHEME = 5,     /* unknown scheme */
   KVQ_ERR_CAPACITY = 6,   /* t0 + T or n_ctx exceeds the cache capacity */
@@ -155,8 +154,8 @@ kvq_status kvq_cache_init(kvq_cache *c, int scheme, int n_bits, int d, int batch
  * d bits (d/32 words, at least one; bits at and beyond d must be 0).
  * KVQ_ROT_QR: Q = device pointer to d*d fp32 (row-major, 16-B aligned),
  * which must stay valid while the cache is used; its orthogonality is the
- * caller's (see kvq_rotation_qr); d <= 128 (KVQ_ERR_DIM at d = 256).
- * Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME (KV scheme, or unknown kind), KVQ_ERR_DIM,
+ * caller's (see kvq_rotation_qr).
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SCHEME (KV scheme, or unknown kind),
  * KVQ_ERR_ALIGN, KVQ_ERR_RANGE (sign bits beyond d). */
 kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
                                   const float *Q_device);

@@ -257,7 +257,6 @@ kvq_status check_cache(const kvq_cache *c) {
   if (c->rot_kind < KVQ_ROT_WHT || c->rot_kind > KVQ_ROT_QR) return KVQ_ERR_SCHEME;
   if (!s.rot && c->rot_kind != KVQ_ROT_WHT) return KVQ_ERR_SCHEME;
   if (c->rot_kind == KVQ_ROT_QR && !c->rot_Q) return KVQ_ERR_NULL;
-  if (c->rot_kind == KVQ_ROT_QR && c->d > 128) return KVQ_ERR_DIM;
   if (c->rot_kind == KVQ_ROT_RHT && !signs_fit(c->rot_signs, c->d)) return KVQ_ERR_RANGE;
   const void *ptrs[] = {c->k_codes, c->k_norm, c->v_codes, c->v_norm, c->k_signs, c->k_rnorm,
                         c->v_signs, c->v_rnorm, c->S,
@@ -301,8 +300,9 @@ kvq_status quantize_side(const kvq_cache *c, int side, const void *src, int dtyp
   a.B = c->batch; a.H = c->kv_heads; a.T = T; a.t0 = t0; a.cap = c->capacity;
   const int rk = rot_code(c);
   // tokens per quantize tile (64 / lanes per vector; one lane per vector for
-  // the dense rotation)
-  const int vt = (rk == kvq::RK_QR || c->d <= 64) ? 64 : (c->d == 128 ? 32 : 16);
+  // the dense rotation, a lane pair at d = 256)
+  const int vt = rk == kvq::RK_QR ? (c->d > 128 ? 32 : 64)
+                                  : (c->d <= 64 ? 64 : (c->d == 128 ? 32 : 16));
   // tiles are aligned to vt slots: the first starts at t0 - t0 % vt
   a.tiles_per_bh = (t0 % vt + T + vt - 1) / vt;
   long long tiles = (long long)a.tiles_per_bh * a.B * a.H;
@@ -543,7 +543,6 @@ kvq_status kvq_cache_set_rotation(kvq_cache *c, int kind, const uint32_t *signs,
     if (!signs_fit(w, c->d)) return KVQ_ERR_RANGE;
   }
   if (kind == KVQ_ROT_QR) {
-    if (c->d > 128) return KVQ_ERR_DIM;   // dense rotation: d <= 128
     if (!Q_device) return KVQ_ERR_NULL;
     if (!aligned16(Q_device)) return KVQ_ERR_ALIGN;
   }

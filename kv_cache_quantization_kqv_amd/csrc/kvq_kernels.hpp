@@ -956,11 +956,45 @@ __device__ __forceinline__ void dense_rows(cfloat *qb, const float *x, float *yb
   }
 }
 
+// The same RB rows with x split over a lane pair (d = 256): lane l < 32 holds
+// x_0 .. x_{D/2-1} of vector l, lane l + 32 the rest.  Each row's chain is
+// relayed: the lower lane runs j < D/2 from 0, hands its sum to the upper lane
+// (a cross-half shuffle), which continues over j >= D/2, so y_i is the same
+// single ascending fma chain.  Both halves work at every step (the lower on
+// row ii, the upper on row ii - 1), each reading its own half-row of Q with
+// vector loads; y ends in the upper lanes (the lower lanes' yb is scratch).
+template <int D, int RB>
+__device__ __forceinline__ void dense_rows_relay(const float *Qb, const float (&xh)[D / 2],
+                                                 float (&yb)[RB], int half, int lane) {
+  constexpr int XN = D / 2;
+  float carry = 0.0f;
+#pragma unroll
+  for (int ii = 0; ii <= RB; ++ii) {
+    // idle steps (upper at ii = 0, lower at ii = RB) recompute an in-range row
+    const int r = half ? (ii > 0 ? ii - 1 : 0) : (ii < RB ? ii : RB - 1);
+    const float *qr = Qb + (size_t)r * D + half * XN;
+    float acc = half ? carry : 0.0f;
+#pragma unroll
+    for (int c = 0; c < XN / 4; ++c) {
+      const f32x4v qv = *(const f32x4v *)(qr + 4 * c);
+      acc = fmaf(qv[0], xh[4 * c + 0], acc);
+      acc = fmaf(qv[1], xh[4 * c + 1], acc);
+      acc = fmaf(qv[2], xh[4 * c + 2], acc);
+      acc = fmaf(qv[3], xh[4 * c + 3], acc);
+    }
+    if (ii > 0) yb[ii - 1] = acc;
+    carry = __shfl_xor(acc, 32, 64);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Quantize-on-write with a dense rotation y = Q x (RK_QR; "KVQuant++" thread,
 // "Rotation invariance guarantee").  One lane per vector, 64 vectors per wave
 // tile, x in registers; Q is read with scalar loads (every lane needs the same
-// row at the same time).  y is formed twice, in blocks of 16 rows: first for
+// row at the same time).  At d = 256 (PAIR) a lane pair holds a vector
+// (dense_rows_relay), 32 vectors per wave tile, and the upper lane of the pair
+// owns everything after y; the sketch is read from memory.  y is formed twice,
+// in blocks of 16 rows: first for
 // the norm, then for the codes, so only x stays live.  A block's pairwise sum
 // of squares is a subtree of the adjacent-pair tree and the block sums are
 // combined in that tree's order (tree_push), so nu and rho equal the pairwise
@@ -969,13 +1003,16 @@ __device__ __forceinline__ void dense_rows(cfloat *qb, const float *x, float *yb
 // ---------------------------------------------------------------------------
 template <int D, int BITS, bool QJL, bool BF16, bool VG>
 __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) {
-  constexpr int VT = 64;                     // vectors per wave tile (one per lane)
+  constexpr bool PAIR = D > 128;             // a lane pair per vector
+  constexpr int VT = PAIR ? 32 : 64;         // vectors per wave tile
+  constexpr int XN = PAIR ? D / 2 : D;       // coordinates of x per lane
   constexpr int RB = D < 16 ? D : 16;        // rows of y per block
   constexpr int NB = D / RB;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RECB = D * BITS / 8;
   constexpr int P2 = D * 2 + 16;
-  constexpr int SBYTES = QJL ? D * P2 : 16;
+  constexpr int SPITCH = PAIR ? D * 2 : P2;
+  constexpr int SBYTES = (QJL && !PAIR) ? D * P2 : 16;
   constexpr int RBYTES = QJL ? VT * P2 : 16;
   using LC = LocalCodes<RB, BITS>;
   __shared__ __attribute__((aligned(16))) unsigned char S_s[SBYTES];
@@ -986,14 +1023,18 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
   __shared__ __attribute__((aligned(16))) uint8_t vrow_all[4][VG ? VT * RECB : 16];
   __shared__ __attribute__((aligned(16))) uint8_t srow_all[4][VG && QJL ? VT * 16 : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = PAIR ? lane >> 5 : 0;     // PAIR: which half of x this lane holds
+  const int vl = PAIR ? lane & 31 : lane;    // this lane's vector in the tile
+  const bool own = !PAIR || half == 1;       // the lane that finishes the vector
   const int lead = a.t0 % VT;                // padding rows before t0 in the first tile
   unsigned char *res = res_all[wave];
   float *rn_s = rn_all[wave];
   build_bucket_tables(bt, a.thr, a.cent, tid, 256);
-  if constexpr (QJL) stage_sketch<D>(S_s, a.S, tid);
+  if constexpr (QJL && !PAIR) stage_sketch<D>(S_s, a.S, tid);
   __syncthreads();
+  const unsigned char *Ssrc = PAIR ? (const unsigned char *)a.S : S_s;
   float a_snmax = 0.0f;
-  if constexpr (QJL) a_snmax = sketch_row_norm_max<D>(S_s, lane);
+  if constexpr (QJL) a_snmax = sketch_row_norm_max<D, SPITCH>(Ssrc, lane);
   cfloat *Qc = (cfloat *)a.Q;
 
 #pragma unroll 1
@@ -1003,16 +1044,18 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
     const int b = bh / a.H, h = bh - b * a.H;
     const int tbase = tt * VT - lead;
     const int rlo = max(0, -tbase), nvalid = min(VT, a.T - tbase);
-    const bool valid = lane >= rlo && lane < nvalid;
-    float x[D];
+    const bool inr = vl >= rlo && vl < nvalid;
+    const bool valid = own && inr;           // this lane stores the vector's results
+    float x[XN];
 #pragma unroll
-    for (int i = 0; i < D; ++i) x[i] = 0.0f;
-    if (valid) {
+    for (int i = 0; i < XN; ++i) x[i] = 0.0f;
+    if (inr) {
       const unsigned char *src = (const unsigned char *)a.src +
-          ((long long)b * a.sb + (long long)h * a.sh + (long long)(tbase + lane) * a.st) * ESZ;
+          ((long long)b * a.sb + (long long)h * a.sh + (long long)(tbase + vl) * a.st +
+           half * XN) * ESZ;
       if constexpr (BF16) {
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
+        for (int c = 0; c < XN / 8; ++c) {
           const u32x4 v = *(const u32x4 *)(src + c * 16);
           x[8 * c + 0] = bf16_lo(v.x); x[8 * c + 1] = bf16_hi(v.x);
           x[8 * c + 2] = bf16_lo(v.y); x[8 * c + 3] = bf16_hi(v.y);
@@ -1021,7 +1064,7 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < D / 4; ++c) {
+        for (int c = 0; c < XN / 4; ++c) {
           const u32x4 v = *(const u32x4 *)(src + c * 16);
           x[4 * c + 0] = __uint_as_float(v.x); x[4 * c + 1] = __uint_as_float(v.y);
           x[4 * c + 2] = __uint_as_float(v.z); x[4 * c + 3] = __uint_as_float(v.w);
@@ -1033,12 +1076,13 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
 #pragma unroll 1
     for (int blk = 0; blk < NB; ++blk) {
       float yb[RB];
-      dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
+      if constexpr (PAIR) dense_rows_relay<D, RB>(a.Q + (size_t)blk * RB * D, x, yb, half, lane);
+      else dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
       ss = tree_push(lvl, pairwise_sumsq<RB>(yb), blk);
     }
     const float nu = sqrtf(ss);
     const float rcp = nu == 0.0f ? 0.0f : 1.0f / nu;
-    const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + lane);
+    const size_t slot = (size_t)bh * a.cap + (size_t)(a.t0 + tbase + vl);
     // VG: the record goes to this lane's LDS row, regrouped by vg_emit_codes
     uint8_t *crec = VG ? vrow_all[wave] + lane * RECB : a.codes + slot * RECB;
     // pass 2: codes (and residuals)
@@ -1046,7 +1090,8 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
 #pragma unroll 1
     for (int blk = 0; blk < NB; ++blk) {
       float yb[RB];
-      dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
+      if constexpr (PAIR) dense_rows_relay<D, RB>(a.Q + (size_t)blk * RB * D, x, yb, half, lane);
+      else dense_rows<D, RB>(Qc + (size_t)blk * RB * D, x, yb);
       LC lc;
       lc.clear();
 #pragma unroll
@@ -1078,9 +1123,10 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
       }
       if constexpr (QJL) {
         rs = tree_push(rl, pairwise_sumsq<RB>(yb), blk);
-        unsigned char *rrow = res + lane * P2 + blk * RB * 2;
+        unsigned char *rrow = res + vl * P2 + blk * RB * 2;
 #pragma unroll
         for (int c = 0; c < RB / 8; ++c) {
+          if (!own) break;
           uint32_t wv[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -1095,11 +1141,11 @@ __global__ __launch_bounds__(256) void quantize_dense_kernel(const QuantArgs a) 
     if constexpr (QJL) {
       const float rho = sqrtf(rs);
       if (valid) a.rnorm[slot] = f32_to_f16_bits(rho);
-      rn_s[lane] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
+      if (own) rn_s[vl] = (float)D * 0x1p-22f * (rho * (1.0f + 0x1p-7f));
       wave_sync();
-      sketch_signs<D, VT / 32, VG>(res, S_s, rn_s, a_snmax, rlo, nvalid,
-                                   (size_t)bh * a.cap + (size_t)(a.t0 + tbase), a.signs,
-                                   srow_all[wave], lane);
+      sketch_signs<D, VT / 32, VG, 16, SPITCH>(res, Ssrc, rn_s, a_snmax, rlo, nvalid,
+                                               (size_t)bh * a.cap + (size_t)(a.t0 + tbase),
+                                               a.signs, srow_all[wave], lane);
       wave_sync();
     }
     if constexpr (VG) {
@@ -2741,12 +2787,8 @@ hipError_t quantize_go(const QuantArgs &a, bool bf16, bool vg, hipStream_t s) {
   auto go = [&](auto V) -> hipError_t {
     constexpr bool VG = decltype(V)::value;
     if constexpr (RK == RK_QR) {
-      // the dense rotation's encoder covers d <= 128
-      if constexpr (D > 128) return hipErrorInvalidValue;
-      else {
-        if (bf16) return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, true, VG>, a, LUT, s);
-        return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, false, VG>, a, LUT, s);
-      }
+      if (bf16) return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, true, VG>, a, LUT, s);
+      return launch_tiles((const void *)&quantize_dense_kernel<D, BITS, QJL, false, VG>, a, LUT, s);
     } else {
       if (bf16) return launch_tiles((const void *)&quantize_kernel<D, BITS, RK, QJL, true, VG>, a, LUT, s);
       return launch_tiles((const void *)&quantize_kernel<D, BITS, RK, QJL, false, VG>, a, LUT, s);

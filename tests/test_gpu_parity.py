@@ -59,14 +59,16 @@ MULTI_TILE = [("KQV", 4, 128, torch.bfloat16, "wht"), ("KQV", 4, 128, torch.floa
               ("KV", 2, 128, torch.bfloat16, "wht"), ("KV", 4, 128, torch.float32, "wht"),
               ("QKQV", 3, 128, torch.float32, "wht"), ("KQV", 4, 64, torch.float32, "wht"),
               ("KQV", 2, 64, torch.bfloat16, "rht"), ("QKQV", 3, 64, torch.bfloat16, "qr"),
-              ("KV", 2, 64, torch.float32, "wht")]
+              ("KV", 2, 64, torch.float32, "wht"), ("QKQV", 3, 256, torch.float32, "qr")]
 
 
 @pytest.mark.parametrize("scheme,n,d,dtype,rotation", MULTI_TILE,
                          ids=[f"{s}{n}-d{d}-{'bf16' if t == torch.bfloat16 else 'f32'}-{r}"
                               for s, n, d, t, r in MULTI_TILE])
 def test_quantize_bit_exact_many_tiles_per_wave(scheme, n, d, dtype, rotation):
-    vt = 32 if (d == 128 and rotation != "qr") else 64
+    # tokens per tile: 64 / lanes per vector (one lane per vector for the dense
+    # rotation below d = 256, a lane pair at 256)
+    vt = {128: 32 if rotation != "qr" else 64, 256: 32}.get(d, 64)
     B, H, t0 = 4, 8, 5
     T = 6400 // 32 * vt - t0                      # 200 tiles per (batch row, head)
     print(f"case quantize-many-tiles {scheme}{n} d={d} {dtype} {rotation} T={T}", flush=True)
@@ -334,8 +336,7 @@ def test_decode_window_equals_plain_decode_when_empty():
 ROT_SCHEMES = [("KQV", 4), ("KQV", 2), ("QKQV", 3), ("QKQV", 2)]
 
 
-ROT_CASES = [(d, r) for d in (8, 16, 32, 64, 128, 256) for r in ("rht", "qr")
-             if not (r == "qr" and d == 256)]   # the dense rotation: d <= 128
+ROT_CASES = [(d, r) for d in (8, 16, 32, 64, 128, 256) for r in ("rht", "qr")]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
@@ -355,7 +356,7 @@ def test_quantize_bit_exact_rotations(scheme, n, d, dtype, rotation):
 
 
 @pytest.mark.parametrize("d,rotation", [(32, "rht"), (32, "qr"), (128, "rht"), (128, "qr"),
-                                        (8, "rht"), (8, "qr"), (256, "rht")])
+                                        (8, "rht"), (8, "qr"), (256, "rht"), (256, "qr")])
 def test_dequantize_and_decode_rotations(rotation, d):
     print(f"case decode-rot {rotation} d={d}", flush=True)
     B, Hkv, G, N = 2, 2, 4, 333
@@ -403,6 +404,23 @@ def test_prefill_matches_oracle(scheme, n, d, G, dtype):
         got = P.gpu.prefill_attention(q.cuda(), p0, N, causal=causal).cpu().numpy()
         err = rel_rows(got, P.prefill(q, p0, causal, N))
         assert err.max() < TOL[dtype], (causal, err.max())
+
+
+@pytest.mark.parametrize("rotation", ["rht", "qr"])
+def test_prefill_rotations_d256(rotation):
+    """The multi-query path under both rotation variants at d = 256 (lane-pair
+    dense encoder, query rotation and the finish's rotation back)."""
+    print(f"case prefill-rot-d256 {rotation}", flush=True)
+    B, Hkv, G, d, nq, p0 = 1, 2, 2, 256, 21, 110
+    N = p0 + nq
+    for scheme, n in (("KQV", 4), ("QKQV", 3)):
+        P = Pair(scheme, n, d, B, Hkv, N, rotation=rotation)
+        K, V = _inputs(B, Hkv, N, d, torch.float32, 2050, heavy=True)
+        P.write(K, V, 0)
+        q = synth.gaussian((B, nq, Hkv * G, d), 2051, torch.float32)
+        for causal in (True, False):
+            got = P.gpu.prefill_attention(q.cuda(), p0, N, causal=causal).cpu().numpy()
+            assert rel_rows(got, P.prefill(q, p0, causal, N)).max() < 1e-5, (scheme, causal)
 
 
 @pytest.mark.parametrize("rotation", ["rht", "qr"])

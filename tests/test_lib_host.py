@@ -378,12 +378,14 @@ def test_cache_set_rotation_validation(K):
     assert c.rot_kind == 1 and list(c.rot_signs) == [0xFFFFFFFF, 0x80000001] + [0] * 6
     assert lib.kvq_cache_set_rotation(C.byref(c), 2, None, 0x900000) == 0
     assert c.rot_kind == 2 and c.rot_Q == 0x900000 and list(c.rot_signs) == [0] * 8
-    # d = 256: all eight sign words; the dense rotation covers d <= 128
+    # d = 256: all eight sign words; the dense rotation as at every d
     c256 = _fake_cache(K, d=256)
     w8 = np.arange(1, 9, dtype=np.uint32)
     assert lib.kvq_cache_set_rotation(C.byref(c256), 1, w8.ctypes.data, None) == 0
     assert list(c256.rot_signs) == list(range(1, 9))
-    assert lib.kvq_cache_set_rotation(C.byref(c256), 2, None, 0x900000) == 3
+    assert lib.kvq_cache_set_rotation(C.byref(c256), 2, None, 0x900000) == 0
+    assert c256.rot_kind == 2 and c256.rot_Q == 0x900000
+    assert lib.kvq_cache_set_rotation(C.byref(c256), 2, None, 0x900008) == 2
     c8 = _fake_cache(K, d=8)
     assert lib.kvq_cache_set_rotation(C.byref(c8), 2, None, 0x900000) == 0
     assert lib.kvq_cache_set_rotation(C.byref(c8), 1, np.array([1 << 8], np.uint32).ctypes.data,
