@@ -473,6 +473,16 @@ def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_
     in_b = 2 if w.dtype == torch.bfloat16 else 4
     dec_bytes = units * w.N * rec + units * G * w.d * (in_b + 4)
     q_bytes = units * w.N * (2 * w.d * in_b + rec)
+    # the first unit again on one thread (the per-core rate)
+    ok1 = ref.OracleCache(1, 1, w.N, w.d, ks, w.d, rot)
+    ov1 = ref.OracleCache(1, 1, w.N, w.d, vs, w.d, rot, values=True)
+    t0 = time.perf_counter()
+    ok1.quantize(host(Ks[:1, :1]), 0, S, 1)
+    ov1.quantize(host(Vs[:1, :1]), 0, S, 1)
+    tq1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ref.attention(ok1, ov1, host(qs[:1, :G]), w.N, S, nthreads=1)
+    ta1 = time.perf_counter() - t0
     del np
     return {"value": round(dec_bytes / ta / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
@@ -480,7 +490,11 @@ def cpu_baseline(w, scheme, n_bits, K, V, q, S, units, rec, rotation="wht", rot_
                       f"full context {w.N}: "
                       f"oracle quantize {tq:.2f}s, fp64 decode attention {ta:.2f}s",
             "quantize_GBps": round(q_bytes / tq / 1e9, 4),
-            "decode_kv_tokens_per_s": round(w.N * units / w.Hkv / ta, 1)}
+            "decode_kv_tokens_per_s": round(w.N * units / w.Hkv / ta, 1),
+            "single_thread": {"sample": f"b = 0, KV head 0 x {G} query heads, full context "
+                                        f"{w.N}: quantize {tq1:.2f}s, decode {ta1:.2f}s",
+                              "decode_GBps": round(dec_bytes / units / ta1 / 1e9, 5),
+                              "quantize_GBps": round(q_bytes / units / tq1 / 1e9, 5)}}
 
 
 def synth_bits(x):
