@@ -638,8 +638,11 @@ __device__ __forceinline__ void sketch_signs(const unsigned char *stage, const u
 // in token groups; the codes go to LDS as one nibble per coordinate and the
 // sign records to LDS, and the wave then writes whole groups (vg_emit_*).
 // ---------------------------------------------------------------------------
+// At d = 256 a lane holds 64 coordinates and the encoder does not fit two
+// blocks per CU: one block per CU lets it use the whole register file (spills
+// go to accumulator registers rather than scratch memory).
 template <int D, int BITS, int RK, bool QJL, bool BF16, bool VG>
-__global__ __launch_bounds__(256, 2)
+__global__ __launch_bounds__(256, D > 128 ? 1 : 2)
 void quantize_kernel(const QuantArgs a) {
   constexpr int LPV = D > 128 ? 4 : (D > 64 ? 2 : 1);   // lanes per vector
   constexpr int DL = D / LPV;                // coordinates per lane
@@ -2219,7 +2222,7 @@ __device__ __forceinline__ void stage_records(unsigned char *dst, int pitch, con
 }
 
 template <int D, int KB, bool KQ, int VB, bool VQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void prefill_kernel(const PrefillArgs a) {
   constexpr int TT = 64;                              // tokens per staged tile
   constexpr int KBYTES = D * KB / 8, VBYTES = D * VB / 8, SBYTES = D / 8;
