@@ -1193,6 +1193,9 @@ __device__ __forceinline__ float wht_block(float *t_s, float x) {
 template <int D>
 __device__ __forceinline__ float dense_rotate_back(const float *Q, const float *t_s, int i) {
   float acc = 0.0f;
+  // (a bounded unroll: callers forming several coordinates at once would
+  // otherwise keep every load of every chain in flight)
+#pragma unroll 8
   for (int j = 0; j < D; ++j) acc = fmaf(Q[(size_t)j * D + i], t_s[j], acc);
   return acc;
 }

@@ -406,12 +406,14 @@ def test_prefill_matches_oracle(scheme, n, d, G, dtype):
         assert err.max() < TOL[dtype], (causal, err.max())
 
 
+@pytest.mark.parametrize("d", [8, 32, 64, 256])
 @pytest.mark.parametrize("rotation", ["rht", "qr"])
-def test_prefill_rotations_d256(rotation):
-    """The multi-query path under both rotation variants at d = 256 (lane-pair
-    dense encoder, query rotation and the finish's rotation back)."""
-    print(f"case prefill-rot-d256 {rotation}", flush=True)
-    B, Hkv, G, d, nq, p0 = 1, 2, 2, 256, 21, 110
+def test_prefill_rotations_other_dims(rotation, d):
+    """The multi-query path under both rotation variants away from d = 128
+    (query rotation, the tile or small kernels, the finish's rotation back; at
+    d = 256 the lane-pair dense encoder)."""
+    print(f"case prefill-rot d={d} {rotation}", flush=True)
+    B, Hkv, G, nq, p0 = 1, 2, 2, 21, 110
     N = p0 + nq
     for scheme, n in (("KQV", 4), ("QKQV", 3)):
         P = Pair(scheme, n, d, B, Hkv, N, rotation=rotation)
