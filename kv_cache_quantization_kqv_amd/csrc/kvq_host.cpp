@@ -355,15 +355,37 @@ long long min_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   return ((long long)n_ctx + tmax - 1) / tmax;
 }
 
+// Compute units of the current device (looked up once per device; the
+// fallback where the runtime has no device, e.g. for host-only calls).
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> known;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kvq::kCusFallback;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)known.size() > dev && known[dev] > 0) return known[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return kvq::kCusFallback;
+  if ((int)known.size() <= dev) known.resize(dev + 1, 0);
+  known[dev] = cus;
+  return cus;
+}
+
 // Vector-unit scan: about kvq::kScanBlocks blocks, the split length rounded up
 // to whole 256-token rounds (at least 256) and within the LDS logit buffer.
-// Matrix-core scan (workers take interleaved 64-token chunks): about
-// kvq::kScanBlocksMfma blocks, at most one chunk per worker (4 per split).
+// Matrix-core scan (workers take interleaved 64-token chunks): one round of
+// resident blocks (every CU at the scan's occupancy), so no block waits for a
+// second round and the fewest split partials are written; at most one chunk
+// per worker (4 per split).
 int auto_splits(const kvq_cache *c, int q_heads, int n_ctx) {
   const int G = q_heads / c->kv_heads;
   const int HG = G / heads_per_block(G);
   const long long units = (long long)c->batch * c->kv_heads * HG;
-  const long long target = scan_mfma(c) ? kvq::kScanBlocksMfma : kvq::kScanBlocks;
+  const long long target =
+      scan_mfma(c) ? (long long)device_cus() *
+                         (c->k_qjl ? kvq::kScanBlocksPerCuSketch : kvq::kScanBlocksPerCu)
+                   : kvq::kScanBlocks;
   const long long want = (target + units - 1) / units;
   if (n_ctx <= 0) return 1;
   if (scan_mfma(c)) {

@@ -14,10 +14,11 @@ namespace kvq {
 constexpr int kScanWbufFloats = 10240;
 inline int scan_tokens_max(int gt) { return kScanWbufFloats / (2 * gt); }
 
-// Target block count of the automatic decode split choice: vector-unit scan;
-// matrix-core scan (two rounds of three resident blocks on each of 256 CUs).
+// Target block count of the automatic decode split choice (vector-unit scan).
 constexpr long long kScanBlocks = 4096;
-constexpr long long kScanBlocksMfma = 1536;
+// Matrix-core scan: resident blocks per CU (the key-sketch variants need more
+// registers and fit two), and the CU count assumed where no device answers.
+constexpr int kScanBlocksPerCu = 3, kScanBlocksPerCuSketch = 2, kCusFallback = 256;
 
 // Rotation applied by the codec (kernel template / argument code):
 // none, Walsh-Hadamard, randomized Hadamard (signs, then WHT), dense Q.

@@ -204,14 +204,17 @@ def test_validation_status_codes(K):
 
 
 def test_auto_splits_fill_the_gpu(K):
-    """Head dimension 128 (matrix-core scan, interleaved 64-token chunks): about
-    1536 blocks, never more than one chunk per worker (4 workers per split).
-    Smaller heads (vector-unit scan): about 4096 blocks, split lengths whole
-    256-token rounds (at least 256) within the LDS logit buffer."""
+    """Head dimension 128 (matrix-core scan, interleaved 64-token chunks): one
+    round of resident blocks (3 per CU, 2 with the key sketch; 256 CUs where no
+    device answers, as here), never more than one chunk per worker (4 workers
+    per split).  Smaller heads (vector-unit scan): about 4096 blocks, split
+    lengths whole 256-token rounds (at least 256) within the LDS logit buffer."""
     c = _fake_cache(K, d=128, B=16, H=8, cap=32768)
-    assert K.kvq_decode_auto_splits(c, 32, 32768) == 12        # 128 units x 12
+    assert K.kvq_decode_auto_splits(c, 32, 32768) == 6         # 128 units x 6 = 768
     c = _fake_cache(K, d=128, B=4, H=8, cap=131136)
-    assert K.kvq_decode_auto_splits(c, 32, 131136) == 48       # 32 units x 48
+    assert K.kvq_decode_auto_splits(c, 32, 131136) == 24       # 32 units x 24
+    c = _fake_cache(K, scheme="QKQV", n=3, d=128, B=8, H=8, cap=16384)
+    assert K.kvq_decode_auto_splits(c, 8, 16384) == 8          # QKQV: 64 units x 8 = 512
     c = _fake_cache(K, d=128, B=1, H=32, cap=4096)
     assert K.kvq_decode_auto_splits(c, 32, 4096) == 17         # <= 65 chunks (15-slot lead) -> 17
     c = _fake_cache(K, d=128, B=1, H=1, cap=512)
