@@ -296,7 +296,11 @@ kvq_status kvq_decode_attention_stages(const kvq_cache *c, const void *q, int q_
 kvq_status kvq_decode_workspace(const kvq_cache *c, int q_heads, int n_ctx, int splits,
                                 size_t *bytes);
 
-/* The split count kvq_decode_attention uses when splits == 0. */
+/* The split count kvq_decode_attention uses when splits == 0.  At d = 128 it
+ * follows the current device's compute-unit count (one round of resident scan
+ * blocks; 256 CUs assumed where no device answers), so a workspace sized with
+ * splits == 0 on one device may be too small on a larger one (the call then
+ * returns KVQ_ERR_WORKSPACE).  0 for invalid arguments. */
 int kvq_decode_auto_splits(const kvq_cache *c, int q_heads, int n_ctx);
 
 /* Multi-query (chunked-prefill) attention over the compressed cache ("Your
